@@ -1,0 +1,262 @@
+"""Lightning Attention oracle: plain, slow, fp64 CPU reference.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import this package. The HIP product
+path (``linear_attention_amd``) never imports it and shares no code with it.
+
+Three independent formulations of the same operator, all in fp64:
+
+``recurrence*``
+    The per-token recurrence ``S <- e^{-s} S + k^T v ; o = q S`` (compiled C,
+    ``lightning_oracle.c``), which is what the block form of MiniMax Signal
+    Lab · M1, §03 Lightning Attention, reduces to with a one-token block, and
+    the "cumsum" that the fishai commentary on M1 says the block split avoids.
+    This is the oracle the GPU path is checked against.
+``brute_force``
+    The quadratic masked form: the §03 intra-block formula
+    ``[(Q K^T) ⊙ D] V`` with one block spanning the whole sequence, plus the
+    decayed read of the carried-in state (a one-block ``O_inter``).
+``block_form``
+    The §03 block decomposition itself, step by step in the pages' notation
+    (``D``, ``d_q``, ``d_k``, block decay, last short block of length ``m``).
+
+Readings of points the pages leave open (each is listed in the design doc):
+positions inside a block are 1-indexed, ``d_q[i] = e^{-s i}``,
+``d_k[j] = e^{-s (m - j)}``, the state decays by ``e^{-s m}`` per block of
+``m`` tokens, ``D`` includes the diagonal, ``⊙`` with a length-``m`` vector
+scales token rows, and the operator output is ``O_intra + O_inter`` with no
+normaliser. A carried-in state ``S0`` is decayed by the first token.
+
+Parity status: pinned (see ``tests/test_oracle.py``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "lightning_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liblightning_oracle.so")
+
+# gcc flags: portable x86-64-v3 so the library built here also runs on the GPU
+# host; IEEE fp64 (no fast-math).
+GCC_CMD = ["gcc", "-O3", "-march=x86-64-v3", "-fopenmp", "-shared", "-fPIC",
+           "-Wall", "-Wextra", _SRC, "-o", _LIB_PATH]
+
+
+def build() -> str:
+    """Compile the C oracle in place and return the library path."""
+    subprocess.run(GCC_CMD, check=True)
+    return _LIB_PATH
+
+
+class _Unit(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("in_stride", ctypes.c_longlong),
+        ("len", ctypes.c_longlong),
+        ("slope", ctypes.c_double),
+        ("s0", ctypes.c_void_p),
+        ("o", ctypes.c_void_p),
+        ("o_stride", ctypes.c_longlong),
+        ("s_final", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.lto_recurrence.argtypes = [ctypes.POINTER(_Unit), ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int]
+        lib.lto_recurrence.restype = ctypes.c_int
+        lib.lto_max_threads.argtypes = []
+        lib.lto_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    """Threads the C oracle's OpenMP region uses by default."""
+    return int(_load().lto_max_threads())
+
+
+def _f32(x):
+    return np.ascontiguousarray(np.asarray(x), dtype=np.float32)
+
+
+def recurrence_packed(q, k, v, slopes, cu_seqlens, s0=None, heads=None,
+                      want_o=True, threads=0):
+    """Per-token recurrence over packed sequences, every (sequence, head) unit.
+
+    q, k, v: [T, H, d] values (cast to float32; bf16/fp32 inputs are exact).
+    slopes: [H] fp32 slopes (widened to fp64).
+    cu_seqlens: [n+1] sequence boundaries, cu[0] = 0, cu[n] = T.
+    s0: [n, H, d, d] carried-in states or None (zero).
+    heads: optional list of head indices to compute (default: all).
+    Returns (o [T, len(heads), d] fp64 or None, s_final [n, len(heads), d, d] fp64).
+    """
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    T, H, d = q.shape
+    assert k.shape == q.shape and v.shape == q.shape
+    slopes = np.asarray(slopes, dtype=np.float32)
+    cu = [int(x) for x in np.asarray(cu_seqlens).reshape(-1)]
+    n = len(cu) - 1
+    assert cu[0] == 0 and cu[-1] == T and all(b >= a for a, b in zip(cu, cu[1:]))
+    hs = list(range(H)) if heads is None else [int(h) for h in heads]
+    nh = len(hs)
+    if s0 is not None:
+        s0 = np.ascontiguousarray(s0, dtype=np.float64)
+        assert s0.shape == (n, H, d, d)
+    o = np.zeros((T, nh, d), dtype=np.float64) if want_o else None
+    sf = np.zeros((n, nh, d, d), dtype=np.float64)
+
+    units = (_Unit * (n * nh))()
+    f4, f8 = 4, 8
+    idx = 0
+    for si in range(n):
+        a, b = cu[si], cu[si + 1]
+        for hj, h in enumerate(hs):
+            u = units[idx]
+            base = (a * H + h) * d * f4
+            u.q = q.ctypes.data + base
+            u.k = k.ctypes.data + base
+            u.v = v.ctypes.data + base
+            u.in_stride = H * d
+            u.len = b - a
+            u.slope = float(slopes[h])
+            u.s0 = (s0.ctypes.data + ((si * H + h) * d * d) * f8) if s0 is not None else None
+            if want_o:
+                u.o = o.ctypes.data + ((a * nh + hj) * d) * f8
+                u.o_stride = nh * d
+            else:
+                u.o = None
+                u.o_stride = 0
+            u.s_final = sf.ctypes.data + ((si * nh + hj) * d * d) * f8
+            idx += 1
+    rc = _load().lto_recurrence(units, n * nh, d, int(threads))
+    if rc != 0:
+        raise RuntimeError("oracle recurrence failed")
+    return o, sf
+
+
+def recurrence_batch(q, k, v, slopes, s0=None, heads=None, want_o=True, threads=0):
+    """Per-token recurrence for a fixed-length batch.
+
+    q, k, v: [batch, L, H, d]; s0: [batch, H, d, d] or None.
+    Returns (o [batch, L, len(heads), d] or None, s_final [batch, len(heads), d, d]).
+    """
+    q = _f32(q)
+    bsz, L, H, d = q.shape
+    cu = np.arange(bsz + 1) * L
+    o, sf = recurrence_packed(q.reshape(bsz * L, H, d), _f32(k).reshape(bsz * L, H, d),
+                              _f32(v).reshape(bsz * L, H, d), slopes, cu, s0=s0,
+                              heads=heads, want_o=want_o, threads=threads)
+    if o is not None:
+        o = o.reshape(bsz, L, o.shape[1], d)
+    return o, sf
+
+
+def recurrence(q, k, v, s, s0=None, want_o=True):
+    """Per-token recurrence for one (sequence, head) unit: q, k, v [L, d]."""
+    q = _f32(q)
+    L, d = q.shape
+    s0b = None if s0 is None else np.asarray(s0, dtype=np.float64).reshape(1, 1, d, d)
+    o, sf = recurrence_packed(q.reshape(L, 1, d), _f32(k).reshape(L, 1, d),
+                              _f32(v).reshape(L, 1, d), np.array([s], np.float32),
+                              [0, L], s0=s0b, want_o=want_o)
+    return (None if o is None else o.reshape(L, d)), sf.reshape(d, d)
+
+
+def decode(q, k, v, slopes, state):
+    """One decode step for every (sequence, head): one iteration of the recurrence.
+
+    q, k, v: [batch, H, d]; state: [batch, H, d, d] (fp64 copy is made).
+    Returns (o [batch, H, d] fp64, new_state [batch, H, d, d] fp64).
+    """
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    bsz, H, d = q.shape
+    st = np.ascontiguousarray(state, dtype=np.float64).reshape(bsz, H, d, d)
+    cu = np.arange(bsz + 1)
+    o, sf = recurrence_packed(q.reshape(bsz, H, d), k, v, slopes, cu, s0=st)
+    return o.reshape(bsz, H, d), sf
+
+
+def recurrence_loop(q, k, v, s, s0=None):
+    """Pure NumPy per-token loop for one unit (small cases; same definition as the C code)."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    L, d = q.shape
+    lam = np.exp(-np.float64(np.float32(s)))
+    S = np.zeros((d, d)) if s0 is None else np.array(s0, np.float64)
+    o = np.zeros((L, d))
+    for i in range(L):
+        S = lam * S + np.outer(k[i], v[i])
+        o[i] = q[i] @ S
+    return o, S
+
+
+def brute_force(q, k, v, s, s0=None):
+    """Quadratic masked form for one unit: one block spanning all L tokens.
+
+    o_i = sum_{j<=i} e^{-s(i-j)} (q_i . k_j) v_j + e^{-s i} q_i S0,
+    S_L = sum_j e^{-s(L-j)} k_j^T v_j + e^{-s L} S0   (positions 1..L).
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    L, d = q.shape
+    s = np.float64(np.float32(s))
+    pos = np.arange(1, L + 1, dtype=np.float64)
+    diff = pos[:, None] - pos[None, :]
+    D = np.where(diff >= 0, np.exp(-s * np.maximum(diff, 0.0)), 0.0)
+    o = ((q @ k.T) * D) @ v
+    wk = np.exp(-s * (L - pos))
+    S = (k * wk[:, None]).T @ v
+    if s0 is not None:
+        s0 = np.asarray(s0, np.float64)
+        o = o + (q * np.exp(-s * pos)[:, None]) @ s0
+        S = S + np.exp(-s * L) * s0
+    return o, S
+
+
+def block_form(q, k, v, s, block, s0=None):
+    """The §03 block decomposition for one unit, in fp64, block length ``block``.
+
+    For each block t of m tokens (m = block, or the remainder for the last one),
+    with positions i, j = 1..m:
+        D_ij   = e^{-s(i-j)} [i >= j]
+        d_q[i] = e^{-s i},  d_k[j] = e^{-s(m-j)}
+        O_t    = [(Q_t K_t^T) ⊙ D] V_t + (Q_t ⊙ d_q) S_{t-1}
+        S_t    = e^{-s m} S_{t-1} + (K_t ⊙ d_k)^T V_t
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    L, d = q.shape
+    s = np.float64(np.float32(s))
+    S = np.zeros((d, d)) if s0 is None else np.array(s0, np.float64)
+    o = np.zeros((L, d))
+    for t0 in range(0, L, block):
+        m = min(block, L - t0)
+        Qt, Kt, Vt = q[t0:t0 + m], k[t0:t0 + m], v[t0:t0 + m]
+        i = np.arange(1, m + 1, dtype=np.float64)
+        diff = i[:, None] - i[None, :]
+        D = np.where(diff >= 0, np.exp(-s * np.maximum(diff, 0.0)), 0.0)
+        dq = np.exp(-s * i)
+        dk = np.exp(-s * (m - i))
+        o_intra = ((Qt @ Kt.T) * D) @ Vt
+        o_inter = (Qt * dq[:, None]) @ S
+        o[t0:t0 + m] = o_intra + o_inter
+        S = np.exp(-s * m) * S + (Kt * dk[:, None]).T @ Vt
+    return o, S

@@ -1,0 +1,357 @@
+"""Pins for the fp64 oracle, against things other than itself (CPU only).
+
+Every check here compares an oracle formulation with an independent fact:
+the quadratic masked form (one block spanning the sequence), the block form at
+many block sizes, closed forms for one-hot inputs, the s = 0 cumulative sum,
+the s -> infinity limit, a pure state-decay case, invariants (chunking, decode
+continuation, linearity, head permutation), and the state size the pages print.
+A mutation test shows that plausible mistakes in a recurrence fail the pins.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+SLOPES = [0.0, 2.0 ** -8, float(np.float32(2.0 ** (-1 / 8))), 5.0, 50.0]
+TOL = 1e-12
+
+
+def rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    nb = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+def rand_unit(seed, L, d, with_s0):
+    g = np.random.Generator(np.random.PCG64(seed))
+    q, k, v = (g.standard_normal((L, d)).astype(np.float32) for _ in range(3))
+    s0 = g.standard_normal((d, d)) if with_s0 else None
+    return q, k, v, s0
+
+
+def c_rec(q, k, v, s, s0=None):
+    return oracle.recurrence(q, k, v, s, s0=s0)
+
+
+# --------------------------------------------------------------------------
+# The pin suite, written against any single-unit recurrence function f.
+# --------------------------------------------------------------------------
+
+def pin_failures(f):
+    """Names of the pins that f(q, k, v, s, s0) -> (o, S) fails."""
+    bad = []
+    d = 4
+    # 1. quadratic masked form, with and without a carried-in state
+    for s in (0.0, 2.0 ** -8, 0.917, 5.0):
+        for with_s0 in (False, True):
+            q, k, v, s0 = rand_unit(7, 23, d, with_s0)
+            o, S = f(q, k, v, s, s0)
+            ob, Sb = oracle.brute_force(q, k, v, s, s0)
+            if rel(o, ob) > 1e-10 or rel(S, Sb) > 1e-10:
+                bad.append(f"brute_force s={s} s0={with_s0}")
+    # 2. one-hot closed form: q_i = e_a, k_j0 = e_a, v_j0 = e_b
+    L, a, b = 11, 1, 2
+    for s in (0.3, 1.7):
+        for j0 in (1, 4, 11):
+            q = np.zeros((L, d), np.float32)
+            k = np.zeros((L, d), np.float32)
+            v = np.zeros((L, d), np.float32)
+            q[:, a] = 1.0
+            k[j0 - 1, a] = 1.0
+            v[j0 - 1, b] = 1.0
+            o, S = f(q, k, v, s, None)
+            sf = float(np.float32(s))
+            want_o = np.zeros((L, d))
+            for i in range(j0, L + 1):
+                want_o[i - 1, b] = math.exp(-sf * (i - j0))
+            want_S = np.zeros((d, d))
+            want_S[a, b] = math.exp(-sf * (L - j0))
+            if rel(o, want_o) > 1e-12 or rel(S, want_S) > 1e-12:
+                bad.append(f"one_hot s={s} j0={j0}")
+    # 3. s = 0: plain causal cumulative sum o_i = q_i sum_{j<=i} k_j^T v_j
+    q, k, v, _ = rand_unit(11, 17, d, False)
+    o, S = f(q, k, v, 0.0, None)
+    cums = np.cumsum(np.einsum("lr,lc->lrc", k.astype(np.float64), v.astype(np.float64)), axis=0)
+    want = np.einsum("lr,lrc->lc", q.astype(np.float64), cums)
+    if rel(o, want) > 1e-12 or rel(S, cums[-1]) > 1e-12:
+        bad.append("cumsum s=0")
+    # 4. s large: only the diagonal survives, o_i = (q_i . k_i) v_i
+    o, S = f(q, k, v, 200.0, None)
+    want = np.sum(q.astype(np.float64) * k, axis=1)[:, None] * v
+    if rel(o, want) > 1e-12:
+        bad.append("diagonal s=200")
+    # 5. pure state decay: k = v = 0, q = e_a -> o_i = e^{-s i} S0[a], S_L = e^{-s L} S0
+    L = 9
+    q = np.zeros((L, d), np.float32)
+    q[:, a] = 1.0
+    z = np.zeros((L, d), np.float32)
+    s0 = np.random.Generator(np.random.PCG64(3)).standard_normal((d, d))
+    s = 0.4
+    sf = float(np.float32(s))
+    o, S = f(q, z, z, s, s0)
+    want_o = np.stack([math.exp(-sf * i) * s0[a] for i in range(1, L + 1)])
+    if rel(o, want_o) > 1e-12 or rel(S, math.exp(-sf * L) * s0) > 1e-12:
+        bad.append("state_decay")
+    return bad
+
+
+def test_c_recurrence_passes_pins():
+    assert pin_failures(c_rec) == []
+
+
+def test_numpy_loop_passes_pins():
+    assert pin_failures(oracle.recurrence_loop) == []
+
+
+@pytest.mark.parametrize("block", [1, 2, 3, 7, 16, 64])
+def test_block_form_passes_pins(block):
+    assert pin_failures(lambda q, k, v, s, s0: oracle.block_form(q, k, v, s, block, s0)) == []
+
+
+# --------------------------------------------------------------------------
+# Mutation test: plausible mistakes must fail at least one pin.
+# --------------------------------------------------------------------------
+
+def _mut_loop(q, k, v, s, s0, *, order="update_first", transpose=False, sign=-1.0,
+              decay_s0=True, diag=True, qside="left"):
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    L, d = q.shape
+    lam = math.exp(sign * float(np.float32(s)))
+    S = np.zeros((d, d)) if s0 is None else np.array(s0, np.float64)
+    o = np.zeros((L, d))
+    for i in range(L):
+        if order == "read_first":
+            o[i] = q[i] @ S
+        kv = np.outer(v[i], k[i]) if transpose else np.outer(k[i], v[i])
+        S = (lam * S if (decay_s0 or i > 0) else S) + kv
+        if order == "update_first":
+            o[i] = (q[i] @ S) if qside == "left" else (S @ q[i])
+            if not diag:
+                o[i] -= (q[i] @ k[i]) * v[i]
+    return o, S
+
+
+MUTANTS = {
+    "output_before_update": dict(order="read_first"),
+    "transposed_kv": dict(transpose=True),
+    "growth_instead_of_decay": dict(sign=+1.0),
+    "undecayed_carried_state": dict(decay_s0=False),
+    "diagonal_dropped": dict(diag=False),
+    "state_read_transposed": dict(qside="right"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutants_fail_pins(name):
+    kw = MUTANTS[name]
+    with np.errstate(all="ignore"):  # the growth mutant overflows on purpose
+        assert pin_failures(lambda q, k, v, s, s0: _mut_loop(q, k, v, s, s0, **kw)), name
+
+
+def test_unmutated_loop_passes_pins():
+    assert pin_failures(lambda q, k, v, s, s0: _mut_loop(q, k, v, s, s0)) == []
+
+
+def _mut_block(q, k, v, s, s0, block, mistake):
+    """Copy of the block form with one planted mistake."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    L, d = q.shape
+    s = float(np.float32(s))
+    S = np.zeros((d, d)) if s0 is None else np.array(s0, np.float64)
+    o = np.zeros((L, d))
+    for t0 in range(0, L, block):
+        m = min(block, L - t0)
+        Qt, Kt, Vt = q[t0:t0 + m], k[t0:t0 + m], v[t0:t0 + m]
+        i = np.arange(1, m + 1, dtype=np.float64)
+        diff = i[:, None] - i[None, :]
+        D = np.where(diff >= 0, np.exp(-s * np.maximum(diff, 0.0)), 0.0)
+        dq = np.exp(-s * (i - 1 if mistake == "dq_zero_based" else i))
+        mm = block if mistake == "full_block_for_short" else m
+        dk = np.exp(-s * (mm - i))
+        if mistake == "strict_mask":
+            D = np.where(diff > 0, D, 0.0)
+        o[t0:t0 + m] = ((Qt @ Kt.T) * D) @ Vt + (Qt * dq[:, None]) @ S
+        S = np.exp(-s * mm) * S + (Kt * dk[:, None]).T @ Vt
+    return o, S
+
+
+@pytest.mark.parametrize("mistake", ["dq_zero_based", "full_block_for_short", "strict_mask"])
+def test_block_mutants_fail_pins(mistake):
+    # block 4 over lengths 23, 11, 17, 9 leaves short last blocks
+    assert pin_failures(lambda q, k, v, s, s0: _mut_block(q, k, v, s, s0, 4, mistake))
+
+
+# --------------------------------------------------------------------------
+# Direct comparisons at the sizes the survey asks for.
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("s", SLOPES)
+@pytest.mark.parametrize("with_s0", [False, True])
+@pytest.mark.parametrize("L,d", [(1, 3), (2, 8), (37, 8), (203, 16)])
+def test_recurrence_vs_brute_force(s, with_s0, L, d):
+    q, k, v, s0 = rand_unit(L * 100 + d, L, d, with_s0)
+    o, S = c_rec(q, k, v, s, s0)
+    ob, Sb = oracle.brute_force(q, k, v, s, s0)
+    assert rel(o, ob) < TOL
+    assert rel(S, Sb) < TOL
+
+
+@pytest.mark.parametrize("s", SLOPES)
+@pytest.mark.parametrize("block", [1, 2, 3, 7, 16, 64, 203, 512])
+def test_block_size_invariance(s, block):
+    q, k, v, s0 = rand_unit(5, 203, 8, True)
+    o, S = c_rec(q, k, v, s, s0)
+    ob, Sb = oracle.block_form(q, k, v, s, block, s0)
+    assert rel(ob, o) < TOL
+    assert rel(Sb, S) < TOL
+
+
+def test_one_hot_at_block_edges():
+    """Closed form with the key at the first/last slot of a block and in a short last block."""
+    L, d, B, a, b = 70, 4, 16, 0, 3
+    s = float(np.float32(0.25))
+    for j0 in (1, 16, 17, 32, 64, 65, 70):
+        q = np.zeros((L, d), np.float32)
+        k = np.zeros((L, d), np.float32)
+        v = np.zeros((L, d), np.float32)
+        q[:, a] = 1.0
+        k[j0 - 1, a] = 1.0
+        v[j0 - 1, b] = 1.0
+        want_o = np.zeros((L, d))
+        for i in range(j0, L + 1):
+            want_o[i - 1, b] = math.exp(-s * (i - j0))
+        want_S = np.zeros((d, d))
+        want_S[a, b] = math.exp(-s * (L - j0))
+        for fn in (lambda: c_rec(q, k, v, s), lambda: oracle.block_form(q, k, v, s, B)):
+            o, S = fn()
+            assert rel(o, want_o) < 1e-13, j0
+            assert rel(S, want_S) < 1e-13, j0
+
+
+def test_chunk_invariance():
+    q, k, v, s0 = rand_unit(9, 150, 8, True)
+    s = 0.05
+    o, S = c_rec(q, k, v, s, s0)
+    for a in (1, 64, 149):
+        o1, S1 = c_rec(q[:a], k[:a], v[:a], s, s0)
+        o2, S2 = c_rec(q[a:], k[a:], v[a:], s, S1)
+        assert rel(np.concatenate([o1, o2]), o) < TOL
+        assert rel(S2, S) < TOL
+
+
+def test_decode_continuation():
+    """prefill(L) then n decode steps equals prefill(L + n)."""
+    H, d, L, n = 3, 8, 40, 5
+    g = np.random.Generator(np.random.PCG64(21))
+    q, k, v = (g.standard_normal((1, L + n, H, d)).astype(np.float32) for _ in range(3))
+    sl = workloads.slopes(H)
+    o_full, S_full = oracle.recurrence_batch(q, k, v, sl)
+    _, S = oracle.recurrence_batch(q[:, :L], k[:, :L], v[:, :L], sl)
+    for t in range(L, L + n):
+        o_t, S = oracle.decode(q[:, t], k[:, t], v[:, t], sl, S)
+        assert rel(o_t, o_full[:, t]) < TOL
+    assert rel(S, S_full) < TOL
+
+
+def test_linearity_in_q_and_v():
+    q1, k, v1, s0 = rand_unit(31, 60, 8, False)
+    q2, _, v2, _ = rand_unit(32, 60, 8, False)
+    s, al, be = 0.1, 0.7, -1.3  # (float64 combinations: NumPy keeps float32 * python float in float32)
+    oq1, _ = oracle.recurrence_loop(q1, k, v1, s)
+    oq2, _ = oracle.recurrence_loop(q2, k, v1, s)
+    oq, _ = oracle.recurrence_loop(al * q1.astype(np.float64) + be * q2.astype(np.float64), k, v1, s)
+    assert rel(oq, al * oq1 + be * oq2) < TOL
+    ov2, S2 = oracle.recurrence_loop(q1, k, v2, s)
+    ov, Sv = oracle.recurrence_loop(q1, k, al * v1.astype(np.float64) + be * v2.astype(np.float64), s)
+    _, S1 = oracle.recurrence_loop(q1, k, v1, s)
+    assert rel(ov, al * oq1 + be * ov2) < TOL
+    assert rel(Sv, al * S1 + be * S2) < TOL
+
+
+def test_heads_and_sequences_independent():
+    """Permuting heads together with their slopes permutes the outputs; packing changes nothing."""
+    H, d = 5, 8
+    lens = [13, 1, 0, 40]
+    cu = workloads.cu_seqlens(lens)
+    T = int(cu[-1])
+    g = np.random.Generator(np.random.PCG64(41))
+    q, k, v = (g.standard_normal((T, H, d)).astype(np.float32) for _ in range(3))
+    s0 = g.standard_normal((len(lens), H, d, d))
+    sl = workloads.slopes(H)
+    o, S = oracle.recurrence_packed(q, k, v, sl, cu, s0=s0)
+    perm = [3, 0, 4, 1, 2]
+    op, Sp = oracle.recurrence_packed(q[:, perm], k[:, perm], v[:, perm], sl[perm], cu,
+                                      s0=s0[:, perm])
+    assert rel(op, o[:, perm]) < TOL
+    assert rel(Sp, S[:, perm]) < TOL
+    for si, (a, b) in enumerate(zip(cu[:-1], cu[1:])):
+        for h in range(H):
+            ou, Su = oracle.recurrence_loop(q[a:b, h], k[a:b, h], v[a:b, h], sl[h], s0[si, h])
+            assert rel(o[a:b, h], ou) < TOL
+            assert rel(S[si, h], Su) < TOL
+    # a zero-length sequence returns its carried-in state untouched
+    assert np.array_equal(S[2], s0[2])
+
+
+def test_heads_subset_matches_all():
+    H, d, L = 6, 8, 33
+    g = np.random.Generator(np.random.PCG64(51))
+    q, k, v = (g.standard_normal((2, L, H, d)).astype(np.float32) for _ in range(3))
+    sl = workloads.slopes(H)
+    o, S = oracle.recurrence_batch(q, k, v, sl)
+    o2, S2 = oracle.recurrence_batch(q, k, v, sl, heads=[4, 1])
+    assert np.array_equal(o2, o[:, :, [4, 1]])
+    assert np.array_equal(S2, S[:, [4, 1]])
+
+
+def test_state_size_matches_pages():
+    """The state the oracle carries (d x d per head) reproduces the sizes printed in §04."""
+    gold = json.load(open(os.path.join(GOLDEN, "state_cache_sizes.json")))
+    H, d = 64, 128
+    q = np.zeros((1, 1, H, d), np.float32)
+    _, S = oracle.recurrence_batch(q, q, q, workloads.slopes(H), want_o=False)
+    per_layer_fp32 = S[0].size * 4
+    assert S.shape == (1, H, d, d)
+    p = gold["printed"]
+    mb = gold["lightning_layers"] * per_layer_fp32 / 1e6
+    assert round(mb, 2) == p["lightning_state_MB"]
+    # softmax layers: K and V, 8 KV heads x 128, BF16, per token
+    kv_per_layer_token = 2 * 8 * 128 * 2
+    sm_gb = gold["softmax_layers"] * kv_per_layer_token * gold["context_tokens"] / 1e9
+    all_gb = gold["all_layers"] * kv_per_layer_token * gold["context_tokens"] / 1e9
+    assert round(sm_gb, 2) == p["softmax_kv_GB"]
+    assert round(all_gb, 2) == p["all_gqa_kv_GB"]
+    assert round(sm_gb + mb / 1e3, 2) == p["hybrid_total_GB"]
+    assert round(100 * (1 - (sm_gb + mb / 1e3) / all_gb), 1) == p["saving_vs_all_gqa_percent"]
+
+
+def test_workload_slopes_exact():
+    """H = 8 slopes are 2^-1 .. 2^-8 exactly; H = 64 runs from 2^(-1/8) to 2^-8."""
+    s8 = workloads.slopes(8)
+    assert list(s8) == [2.0 ** -(h + 1) for h in range(8)]
+    s64 = workloads.slopes(64)
+    assert s64[-1] == 2.0 ** -8
+    assert abs(s64[0] - 2.0 ** (-1 / 8)) < 1e-7
+
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 1e-3], np.float32)
+    r = workloads.round_bf16(x)
+    assert r[0] == 1.0
+    assert r[1] == 1.0            # tie -> even mantissa
+    assert r[2] == 1.0 + 2 ** -6  # tie -> even (rounds up)
+    assert r[3] == -2.5
+    assert abs(r[4] - 1e-3) / 1e-3 < 2 ** -8
+    assert np.all((r.view(np.uint32) & 0xFFFF) == 0)
