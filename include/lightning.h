@@ -1,0 +1,149 @@
+/*
+ * lightning.h - C ABI of the MI355X (gfx950) Lightning Attention library.
+ *
+ * The operator is the causal linear attention with a per-head exponential
+ * decay described in MiniMax Signal Lab · M1 (ailearn.mscapital.top),
+ * §03 Lightning Attention. For a block t of B tokens (positions i, j = 1..B;
+ * a last short block uses its real length m in place of B):
+ *
+ *     D_ij    = e^{-s_h (i - j)} [i >= j]
+ *     O_intra = [(Q_t K_t^T) ⊙ D] V_t
+ *     O_inter = (Q_t ⊙ d_q) S_{t-1},          d_q[i] = e^{-s_h i}
+ *     O_t     = O_intra + O_inter              (§03 dataflow figure: the two
+ *                                              outputs are added)
+ *     S_t     = e^{-s_h B} S_{t-1} + (K_t ⊙ d_k)^T V_t,   d_k[j] = e^{-s_h (B - j)}
+ *
+ * with a fixed d x d FP32 state S per head (§03, and §04 Context Cache, whose
+ * 70-layer state total fixes d x d FP32 per head for 64 heads of d = 128).
+ * "⊙" with a length-B vector scales token rows. The value of O and of the final
+ * state does not depend on B: the block form is an exact re-association of the
+ * per-token recurrence S <- e^{-s_h} S + k^T v, o = q S (the token sees its own
+ * key). The output is the raw sum; normalisation and gating come after this
+ * operator and are not part of it.
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer argument except `stream` is a DEVICE pointer (HBM). The
+ *    caller owns every buffer; the library allocates nothing, keeps no global
+ *    state, and never synchronises.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    the call returns before it runs.
+ *  - Layouts are dense and row-major with head_dim innermost. Element offsets
+ *    are 64-bit, so a tensor may exceed 2^31 elements.
+ *  - State tensors are FP32 [units, heads, head_dim (key index), head_dim
+ *    (value index)]: S[r][c] multiplies key component r into value column c.
+ *  - Slopes are FP32 [heads], s_h >= 0 (0 = no decay). Their values are read on
+ *    the device and are not validated; NaN/Inf anywhere propagate to outputs.
+ *  - Arguments are validated on the host before any launch. A failed check
+ *    returns its status and enqueues nothing. A failed launch returns
+ *    LT_ERR_HIP. No C++ exception crosses this interface.
+ *  - Supported: head_dim == 128; in_dtype LT_BF16 or LT_F32 (bf16 inputs are
+ *    multiplied on MFMA with fp32 accumulation; fp32 inputs on fp32 MFMA);
+ *    out_dtype LT_F32 or LT_BF16.
+ *  - Overlap: `state_in == state_out` (same address) is allowed and updates the
+ *    state in place. Any other overlap between an output and any other buffer
+ *    is rejected with LT_ERR_ALIAS.
+ */
+#ifndef LIGHTNING_H
+#define LIGHTNING_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define LT_API __attribute__((visibility("default")))
+#else
+#define LT_API
+#endif
+
+typedef enum {
+    LT_OK = 0,
+    LT_ERR_NULL = 1,      /* a required pointer is NULL */
+    LT_ERR_SHAPE = 2,     /* unsupported or inconsistent sizes */
+    LT_ERR_BLOCK = 3,     /* block size out of range */
+    LT_ERR_DTYPE = 4,     /* unsupported dtype code */
+    LT_ERR_ALIAS = 5,     /* an output overlaps another buffer */
+    LT_ERR_HIP = 6        /* the HIP runtime reported an error at launch */
+} lt_status;
+
+typedef enum { LT_F32 = 0, LT_BF16 = 1 } lt_dtype;
+
+/* Largest block size accepted by the prefill entry points. */
+#define LT_MAX_BLOCK 65536
+
+/* Human-readable name of a status code (static storage; never NULL). */
+LT_API const char *lt_status_string(int status);
+
+/* Library ABI version: major * 10000 + minor * 100 + patch. */
+LT_API int lt_version(void);
+
+/*
+ * lt_prefill - block-wise prefill of `batch` sequences of equal length.
+ *
+ *   q, k, v    [batch, seqlen, heads, head_dim], in_dtype.
+ *   slopes     [heads] fp32 per-head decay slopes s_h.
+ *   o          [batch, seqlen, heads, head_dim], out_dtype: O_intra + O_inter.
+ *   state_in   [batch, heads, head_dim, head_dim] fp32 carried-in state S_0,
+ *              or NULL for a zero state. The first token decays it once
+ *              (o_1 = q_1 (e^{-s} S_0 + k_1^T v_1)), as in the per-token form.
+ *   state_out  same shape: the state after the last token, or NULL to skip.
+ *              May equal state_in.
+ *   block      the method's block length B, 1..LT_MAX_BLOCK. The result does
+ *              not depend on it (see above); the kernels schedule their own
+ *              sub-blocks.
+ *   seqlen 0 writes state_out = state_in (or zeros). batch 0 or heads 0 is a
+ *   no-op. Errors: LT_ERR_NULL, LT_ERR_SHAPE, LT_ERR_BLOCK, LT_ERR_DTYPE,
+ *   LT_ERR_ALIAS, LT_ERR_HIP.
+ */
+LT_API lt_status lt_prefill(const void *q, const void *k, const void *v, lt_dtype in_dtype,
+                            const float *slopes, void *o, lt_dtype out_dtype,
+                            const float *state_in, float *state_out,
+                            int batch, long long seqlen, int heads, int head_dim, int block,
+                            void *stream);
+
+/*
+ * lt_prefill_varlen - prefill of `num_seqs` packed sequences of different
+ * lengths, each with its own carried-in state (chunked prefill / resume).
+ *
+ *   q, k, v     [total_tokens, heads, head_dim], in_dtype; sequence n owns rows
+ *               cu_seqlens[n] .. cu_seqlens[n+1]-1.
+ *   cu_seqlens  [num_seqs + 1] int32 on the device: cu[0] = 0, non-decreasing,
+ *               cu[num_seqs] = total_tokens. Contents are not checked on the
+ *               host; the kernels clamp every boundary into [0, total_tokens],
+ *               so malformed boundaries give wrong results, never stray memory
+ *               accesses.
+ *   slopes, o, state_in, state_out, block: as lt_prefill, with state tensors
+ *               [num_seqs, heads, head_dim, head_dim]. Blocks restart at each
+ *               sequence start; zero-length sequences pass their state through.
+ *   Errors: as lt_prefill.
+ */
+LT_API lt_status lt_prefill_varlen(const void *q, const void *k, const void *v, lt_dtype in_dtype,
+                                   const int *cu_seqlens, int num_seqs, long long total_tokens,
+                                   const float *slopes, void *o, lt_dtype out_dtype,
+                                   const float *state_in, float *state_out,
+                                   int heads, int head_dim, int block, void *stream);
+
+/*
+ * lt_decode - one decode step for `batch` sequences: each reads and writes its
+ * fixed-size state in place (§03: the next block reads the carried state
+ * directly instead of rescanning history; §04: that state does not grow):
+ *
+ *     S <- e^{-s_h} S + k^T v ;   o = q S   (o reads the updated state)
+ *
+ *   q, k, v  [batch, heads, head_dim], in_dtype (one token per sequence).
+ *   state    [batch, heads, head_dim, head_dim] fp32, updated IN PLACE.
+ *   o        [batch, heads, head_dim], out_dtype.
+ *   A single token has no block, so there is no block argument.
+ *   Errors: LT_ERR_NULL, LT_ERR_SHAPE, LT_ERR_DTYPE, LT_ERR_ALIAS, LT_ERR_HIP.
+ */
+LT_API lt_status lt_decode(const void *q, const void *k, const void *v, lt_dtype in_dtype,
+                           const float *slopes, float *state, void *o, lt_dtype out_dtype,
+                           int batch, int heads, int head_dim, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIGHTNING_H */

@@ -1,0 +1,19 @@
+"""Lightning Attention for MI355X (gfx950): HIP kernels behind a C ABI.
+
+The operator (MiniMax Signal Lab · M1, §03 Lightning Attention) is causal
+linear attention with a per-head exponential decay, evaluated block by block
+with a fixed d x d fp32 state per head, plus its one-token decode step.
+
+``lt_prefill``, ``lt_prefill_varlen`` and ``lt_decode`` mirror the C entry
+points of ``include/lightning.h`` one to one.
+"""
+
+from ._native import (EXPORTS, HEAD_DIM, LIB_PATH, LT_BF16, LT_ERR_ALIAS, LT_ERR_BLOCK,
+                      LT_ERR_DTYPE, LT_ERR_HIP, LT_ERR_NULL, LT_ERR_SHAPE, LT_F32, LT_MAX_BLOCK,
+                      LT_OK, LightningError, lib, lt_decode, lt_prefill, lt_prefill_varlen,
+                      status_string)
+
+__all__ = ["lt_prefill", "lt_prefill_varlen", "lt_decode", "LightningError", "lib",
+           "status_string", "EXPORTS", "LIB_PATH", "HEAD_DIM", "LT_OK", "LT_ERR_NULL",
+           "LT_ERR_SHAPE", "LT_ERR_BLOCK", "LT_ERR_DTYPE", "LT_ERR_ALIAS", "LT_ERR_HIP",
+           "LT_F32", "LT_BF16", "LT_MAX_BLOCK"]

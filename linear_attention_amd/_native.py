@@ -1,0 +1,173 @@
+"""ctypes binding of ``liblightning.so`` (the C ABI in ``include/lightning.h``).
+
+Argument marshalling only: shapes and dtypes are read off torch tensors, raw
+device pointers and the current HIP stream are passed to the C entry points,
+and every step of the computation runs in the library's HIP kernels. There is
+no fallback: if the library is missing, importing this module fails.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "liblightning.so")
+
+LT_OK, LT_ERR_NULL, LT_ERR_SHAPE, LT_ERR_BLOCK, LT_ERR_DTYPE, LT_ERR_ALIAS, LT_ERR_HIP = range(7)
+LT_F32, LT_BF16 = 0, 1
+LT_MAX_BLOCK = 65536
+HEAD_DIM = 128
+
+EXPORTS = ("lt_status_string", "lt_version", "lt_prefill", "lt_prefill_varlen", "lt_decode")
+
+_vp, _i, _ll = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong
+
+
+class LightningError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m linear_attention_amd.build` "
+            "(the Lightning kernels have no fallback path)")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.lt_status_string.argtypes = [_i]
+    lib.lt_status_string.restype = ctypes.c_char_p
+    lib.lt_version.argtypes = []
+    lib.lt_version.restype = _i
+    lib.lt_prefill.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp,
+                               _i, _ll, _i, _i, _i, _vp]
+    lib.lt_prefill.restype = _i
+    lib.lt_prefill_varlen.argtypes = [_vp, _vp, _vp, _i, _vp, _i, _ll, _vp, _vp, _i,
+                                      _vp, _vp, _i, _i, _i, _vp]
+    lib.lt_prefill_varlen.restype = _i
+    lib.lt_decode.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _vp]
+    lib.lt_decode.restype = _i
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.lt_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != LT_OK:
+        raise LightningError(status, where)
+
+
+# ---------------------------------------------------------------------------
+# torch-facing wrappers (same names as the C entry points)
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t == torch.float32:
+        return LT_F32
+    if t == torch.bfloat16:
+        return LT_BF16
+    raise TypeError(f"unsupported dtype {t}; Lightning kernels take float32 or bfloat16")
+
+
+def _dev_ptr(t, name):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def lt_prefill(q, k, v, slopes, block, state_in=None, *, o=None, state_out=None,
+               want_state=True, out_dtype=None, stream=None):
+    """Fixed-length prefill. q, k, v: [batch, L, H, 128]; slopes: fp32 [H].
+
+    Returns (o [batch, L, H, 128], state_out [batch, H, 128, 128] fp32 or None).
+    ``state_out`` may be given (it may be ``state_in`` itself for an in-place
+    update); otherwise one is allocated when ``want_state``.
+    """
+    torch = _torch()
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [batch, L, H, d] shape")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    batch, L, H, d = q.shape
+    out_dtype = out_dtype or torch.float32
+    if o is None:
+        o = torch.empty((batch, L, H, d), device=q.device, dtype=out_dtype)
+    if state_out is None and want_state:
+        state_out = torch.empty((batch, H, d, d), device=q.device, dtype=torch.float32)
+    st = lib.lt_prefill(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dtype_code(q.dtype),
+                        _dev_ptr(slopes, "slopes"), _dev_ptr(o, "o"), _dtype_code(o.dtype),
+                        _dev_ptr(state_in, "state_in"), _dev_ptr(state_out, "state_out"),
+                        batch, L, H, d, int(block), _stream(stream, q.device))
+    _check(st, "lt_prefill")
+    return o, state_out
+
+
+def lt_prefill_varlen(q, k, v, cu_seqlens, slopes, block, state_in=None, *, o=None,
+                      state_out=None, want_state=True, out_dtype=None, stream=None):
+    """Packed variable-length prefill. q, k, v: [T, H, 128]; cu_seqlens: int32 [n+1] on device.
+
+    Returns (o [T, H, 128], state_out [n, H, 128, 128] fp32 or None).
+    """
+    torch = _torch()
+    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [T, H, d] shape")
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    T, H, d = q.shape
+    n = cu_seqlens.numel() - 1
+    out_dtype = out_dtype or torch.float32
+    if o is None:
+        o = torch.empty((T, H, d), device=q.device, dtype=out_dtype)
+    if state_out is None and want_state:
+        state_out = torch.empty((n, H, d, d), device=q.device, dtype=torch.float32)
+    st = lib.lt_prefill_varlen(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                               _dtype_code(q.dtype), _dev_ptr(cu_seqlens, "cu_seqlens"), n, T,
+                               _dev_ptr(slopes, "slopes"), _dev_ptr(o, "o"), _dtype_code(o.dtype),
+                               _dev_ptr(state_in, "state_in"), _dev_ptr(state_out, "state_out"),
+                               H, d, int(block), _stream(stream, q.device))
+    _check(st, "lt_prefill_varlen")
+    return o, state_out
+
+
+def lt_decode(q, k, v, slopes, state, *, o=None, out_dtype=None, stream=None):
+    """One decode step. q, k, v: [batch, H, 128]; state: [batch, H, 128, 128] fp32, updated in place.
+
+    Returns o [batch, H, 128].
+    """
+    torch = _torch()
+    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [batch, H, d] shape")
+    batch, H, d = q.shape
+    if state.dtype != torch.float32 or tuple(state.shape) != (batch, H, d, d):
+        raise ValueError("state must be float32 [batch, H, d, d]")
+    out_dtype = out_dtype or torch.float32
+    if o is None:
+        o = torch.empty((batch, H, d), device=q.device, dtype=out_dtype)
+    st = lib.lt_decode(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dtype_code(q.dtype),
+                       _dev_ptr(slopes, "slopes"), _dev_ptr(state, "state"), _dev_ptr(o, "o"),
+                       _dtype_code(o.dtype), batch, H, d, _stream(stream, q.device))
+    _check(st, "lt_decode")
+    return o

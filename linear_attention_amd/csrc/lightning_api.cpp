@@ -1,0 +1,159 @@
+// C-ABI front end: host-side argument checks, then one launch on the caller's
+// stream. Every check runs before any HIP call, so the error paths need no GPU.
+#include <cstdint>
+
+#include "internal.h"
+#include "lightning.h"
+
+namespace {
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+    bool empty() const { return hi <= lo; }
+};
+
+Range range_of(const void *p, long long bytes) {
+    uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, bytes > 0 ? lo + static_cast<uintptr_t>(bytes) : lo};
+}
+
+bool overlaps(Range a, Range b) {
+    if (a.empty() || b.empty()) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool dtype_ok(int d) { return d == LT_F32 || d == LT_BF16; }
+long long dtype_size(int d) { return d == LT_F32 ? 4 : 2; }
+
+// a * b * c * d as 64-bit with overflow detection (all operands >= 0).
+bool mul4(long long a, long long b, long long c, long long d, long long *out) {
+    long long t;
+    if (__builtin_mul_overflow(a, b, &t)) return false;
+    if (__builtin_mul_overflow(t, c, &t)) return false;
+    if (__builtin_mul_overflow(t, d, &t)) return false;
+    *out = t;
+    return true;
+}
+
+lt_status map_hip(hipError_t e) { return e == hipSuccess ? LT_OK : LT_ERR_HIP; }
+
+// Shared checks of the two prefill entry points. `tokens` = rows of q/k/v/o.
+lt_status check_prefill(const void *q, const void *k, const void *v, int in_dtype,
+                        const float *slopes, void *o, int out_dtype,
+                        const float *state_in, float *state_out,
+                        long long units, long long tokens, int heads, int head_dim,
+                        int block) {
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return LT_ERR_DTYPE;
+    if (head_dim != lt::kHeadDim || heads < 0 || units < 0 || tokens < 0) return LT_ERR_SHAPE;
+    if (block < 1 || block > LT_MAX_BLOCK) return LT_ERR_BLOCK;
+    if (units == 0 || heads == 0) return LT_OK;
+    if (!slopes) return LT_ERR_NULL;
+    if (tokens > 0 && (!q || !k || !v || !o)) return LT_ERR_NULL;
+
+    long long in_bytes, out_bytes, st_bytes, grid;
+    if (!mul4(tokens, heads, head_dim, dtype_size(in_dtype), &in_bytes) ||
+        !mul4(tokens, heads, head_dim, dtype_size(out_dtype), &out_bytes) ||
+        !mul4(units, heads, (long long)head_dim * head_dim, 4, &st_bytes) ||
+        !mul4(units, heads, lt::kValueSlices, 1, &grid) || grid > 0x7fffffffLL)
+        return LT_ERR_SHAPE;
+
+    const Range rq = range_of(q, in_bytes), rk = range_of(k, in_bytes),
+                rv = range_of(v, in_bytes), ro = range_of(o, out_bytes),
+                rs = range_of(slopes, (long long)heads * 4),
+                rsi = range_of(state_in, state_in ? st_bytes : 0),
+                rso = range_of(state_out, state_out ? st_bytes : 0);
+    if (overlaps(ro, rq) || overlaps(ro, rk) || overlaps(ro, rv) || overlaps(ro, rs) ||
+        overlaps(ro, rsi) || overlaps(ro, rso))
+        return LT_ERR_ALIAS;
+    if (overlaps(rso, rq) || overlaps(rso, rk) || overlaps(rso, rv) || overlaps(rso, rs))
+        return LT_ERR_ALIAS;
+    if (state_in && state_out && state_in != state_out && overlaps(rsi, rso))
+        return LT_ERR_ALIAS;
+    return LT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+LT_API const char *lt_status_string(int status) {
+    switch (status) {
+        case LT_OK: return "LT_OK";
+        case LT_ERR_NULL: return "LT_ERR_NULL: a required pointer is NULL";
+        case LT_ERR_SHAPE: return "LT_ERR_SHAPE: unsupported or inconsistent sizes";
+        case LT_ERR_BLOCK: return "LT_ERR_BLOCK: block size out of range";
+        case LT_ERR_DTYPE: return "LT_ERR_DTYPE: unsupported dtype";
+        case LT_ERR_ALIAS: return "LT_ERR_ALIAS: an output overlaps another buffer";
+        case LT_ERR_HIP: return "LT_ERR_HIP: HIP runtime error at launch";
+        default: return "unknown lt_status";
+    }
+}
+
+LT_API int lt_version(void) { return 10000; }
+
+LT_API lt_status lt_prefill(const void *q, const void *k, const void *v, lt_dtype in_dtype,
+                            const float *slopes, void *o, lt_dtype out_dtype,
+                            const float *state_in, float *state_out,
+                            int batch, long long seqlen, int heads, int head_dim, int block,
+                            void *stream) {
+    if (batch < 0 || seqlen < 0) return LT_ERR_SHAPE;
+    long long tokens;
+    if (__builtin_mul_overflow((long long)batch, seqlen, &tokens)) return LT_ERR_SHAPE;
+    lt_status st = check_prefill(q, k, v, in_dtype, slopes, o, out_dtype, state_in, state_out,
+                                 batch, tokens, heads, head_dim, block);
+    if (st != LT_OK || batch == 0 || heads == 0) return st;
+    if (tokens == 0 && !state_out) return LT_OK;
+    lt::PrefillArgs a{q, k, v, slopes, o, state_in, state_out, nullptr, seqlen, tokens,
+                      batch, heads};
+    return map_hip(lt::launch_prefill(a, in_dtype, out_dtype,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+LT_API lt_status lt_prefill_varlen(const void *q, const void *k, const void *v, lt_dtype in_dtype,
+                                   const int *cu_seqlens, int num_seqs, long long total_tokens,
+                                   const float *slopes, void *o, lt_dtype out_dtype,
+                                   const float *state_in, float *state_out,
+                                   int heads, int head_dim, int block, void *stream) {
+    if (num_seqs < 0 || total_tokens < 0) return LT_ERR_SHAPE;
+    if (total_tokens > 0x7fffffffLL) return LT_ERR_SHAPE;  // int32 sequence boundaries
+    lt_status st = check_prefill(q, k, v, in_dtype, slopes, o, out_dtype, state_in, state_out,
+                                 num_seqs, total_tokens, heads, head_dim, block);
+    if (st != LT_OK || num_seqs == 0 || heads == 0) return st;
+    if (!cu_seqlens) return LT_ERR_NULL;
+    if (overlaps(range_of(cu_seqlens, (long long)(num_seqs + 1) * 4),
+                 range_of(o, total_tokens * heads * head_dim * dtype_size(out_dtype))) ||
+        (state_out && overlaps(range_of(cu_seqlens, (long long)(num_seqs + 1) * 4),
+                               range_of(state_out, (long long)num_seqs * heads * head_dim *
+                                                       head_dim * 4))))
+        return LT_ERR_ALIAS;
+    if (total_tokens == 0 && !state_out) return LT_OK;
+    lt::PrefillArgs a{q, k, v, slopes, o, state_in, state_out, cu_seqlens, 0, total_tokens,
+                      num_seqs, heads};
+    return map_hip(lt::launch_prefill(a, in_dtype, out_dtype,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+LT_API lt_status lt_decode(const void *q, const void *k, const void *v, lt_dtype in_dtype,
+                           const float *slopes, float *state, void *o, lt_dtype out_dtype,
+                           int batch, int heads, int head_dim, void *stream) {
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return LT_ERR_DTYPE;
+    if (head_dim != lt::kHeadDim || heads < 0 || batch < 0) return LT_ERR_SHAPE;
+    if (batch == 0 || heads == 0) return LT_OK;
+    if (!q || !k || !v || !slopes || !state || !o) return LT_ERR_NULL;
+    long long units = (long long)batch * heads;
+    if (units > 0x7fffffffLL) return LT_ERR_SHAPE;
+    const long long in_bytes = units * head_dim * dtype_size(in_dtype);
+    const long long out_bytes = units * head_dim * dtype_size(out_dtype);
+    const long long st_bytes = units * head_dim * head_dim * 4;
+    const Range rq = range_of(q, in_bytes), rk = range_of(k, in_bytes),
+                rv = range_of(v, in_bytes), ro = range_of(o, out_bytes),
+                rs = range_of(slopes, (long long)heads * 4), rst = range_of(state, st_bytes);
+    if (overlaps(ro, rq) || overlaps(ro, rk) || overlaps(ro, rv) || overlaps(ro, rs) ||
+        overlaps(ro, rst) || overlaps(rst, rq) || overlaps(rst, rk) || overlaps(rst, rv) ||
+        overlaps(rst, rs))
+        return LT_ERR_ALIAS;
+    lt::DecodeArgs a{q, k, v, slopes, state, o, batch, heads};
+    return map_hip(lt::launch_decode(a, in_dtype, out_dtype, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

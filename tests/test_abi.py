@@ -1,0 +1,143 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and its
+host-side argument checks return the documented status codes before any HIP
+call (no compute is launched here)."""
+
+import os
+import re
+
+import pytest
+
+from parity_util import ensure_built
+
+ensure_built()
+
+import linear_attention_amd as la  # noqa: E402
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lightning.h")
+
+# Fake, never-dereferenced device addresses: every call below fails validation
+# (or is a documented no-op) before the library touches HIP.
+A = 0x10_0000_0000
+MB = 1 << 20
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"LT_API\s+[\w\s\*]+?\b(lt_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_symbols() == sorted(la.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    for name in declared_symbols():
+        assert hasattr(la.lib, name), name
+
+
+def test_only_the_abi_is_exported():
+    import subprocess
+
+    out = subprocess.run(["nm", "-D", "--defined-only", la.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert {s for s in syms if s.startswith("lt_")} == set(la.EXPORTS)
+
+
+def test_status_strings():
+    for code in range(7):
+        assert la.status_string(code).startswith(
+            ["LT_OK", "LT_ERR_NULL", "LT_ERR_SHAPE", "LT_ERR_BLOCK", "LT_ERR_DTYPE",
+             "LT_ERR_ALIAS", "LT_ERR_HIP"][code])
+    assert la.status_string(99) == "unknown lt_status"
+    assert la.lib.lt_version() == 10000
+
+
+def prefill(**kw):
+    args = dict(q=A, k=A + 100 * MB, v=A + 200 * MB, in_dtype=la.LT_BF16, slopes=A + 300 * MB,
+                o=A + 400 * MB, out_dtype=la.LT_F32, state_in=None, state_out=A + 900 * MB,
+                batch=1, seqlen=64, heads=2, head_dim=128, block=64, stream=None)
+    args.update(kw)
+    return la.lib.lt_prefill(*args.values())
+
+
+def varlen(**kw):
+    args = dict(q=A, k=A + 100 * MB, v=A + 200 * MB, in_dtype=la.LT_BF16,
+                cu=A + 290 * MB, num_seqs=2, total=64, slopes=A + 300 * MB, o=A + 400 * MB,
+                out_dtype=la.LT_F32, state_in=None, state_out=A + 900 * MB, heads=2,
+                head_dim=128, block=64, stream=None)
+    args.update(kw)
+    return la.lib.lt_prefill_varlen(*args.values())
+
+
+def decode(**kw):
+    args = dict(q=A, k=A + MB, v=A + 2 * MB, in_dtype=la.LT_BF16, slopes=A + 3 * MB,
+                state=A + 4 * MB, o=A + 100 * MB, out_dtype=la.LT_F32, batch=2, heads=2,
+                head_dim=128, stream=None)
+    args.update(kw)
+    return la.lib.lt_decode(*args.values())
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "slopes", "o"])
+def test_prefill_null_pointers(field):
+    assert prefill(**{field: None}) == la.LT_ERR_NULL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=64), la.LT_ERR_SHAPE),
+    (dict(head_dim=256), la.LT_ERR_SHAPE),
+    (dict(heads=-1), la.LT_ERR_SHAPE),
+    (dict(batch=-1), la.LT_ERR_SHAPE),
+    (dict(seqlen=-5), la.LT_ERR_SHAPE),
+    (dict(seqlen=1 << 50, heads=64), la.LT_ERR_SHAPE),  # byte count overflows int64
+    (dict(block=0), la.LT_ERR_BLOCK),
+    (dict(block=la.LT_MAX_BLOCK + 1), la.LT_ERR_BLOCK),
+    (dict(in_dtype=7), la.LT_ERR_DTYPE),
+    (dict(out_dtype=-1), la.LT_ERR_DTYPE),
+])
+def test_prefill_bad_arguments(kw, code):
+    assert prefill(**kw) == code
+
+
+def test_prefill_alias_checks():
+    assert prefill(o=A + 16384) == la.LT_ERR_ALIAS               # o inside q (32 KiB)
+    assert prefill(state_out=A + 400 * MB) == la.LT_ERR_ALIAS    # state_out on o
+    assert prefill(state_out=A + 10) == la.LT_ERR_ALIAS          # state_out inside q
+    s = A + 900 * MB
+    assert prefill(state_in=s, state_out=s + 4096) == la.LT_ERR_ALIAS  # partial overlap
+    assert prefill(state_in=s, state_out=s + 8 * MB, batch=0) == la.LT_OK
+
+
+def test_prefill_noops_need_no_gpu():
+    assert prefill(batch=0) == la.LT_OK
+    assert prefill(heads=0) == la.LT_OK
+    # zero tokens with no state to write: nothing to launch; q/k/v/o may be NULL
+    assert prefill(seqlen=0, state_out=None, q=None, k=None, v=None, o=None) == la.LT_OK
+
+
+def test_varlen_checks():
+    assert varlen(cu=None) == la.LT_ERR_NULL
+    assert varlen(num_seqs=-1) == la.LT_ERR_SHAPE
+    assert varlen(total=-1) == la.LT_ERR_SHAPE
+    assert varlen(total=1 << 31, heads=1) == la.LT_ERR_SHAPE     # int32 boundaries
+    assert varlen(head_dim=96) == la.LT_ERR_SHAPE
+    assert varlen(block=0) == la.LT_ERR_BLOCK
+    assert varlen(cu=A + 400 * MB) == la.LT_ERR_ALIAS            # cu_seqlens inside o
+    assert varlen(num_seqs=0) == la.LT_OK
+    assert varlen(total=0, state_out=None, q=None, k=None, v=None, o=None) == la.LT_OK
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "slopes", "state", "o"])
+def test_decode_null_pointers(field):
+    assert decode(**{field: None}) == la.LT_ERR_NULL
+
+
+def test_decode_checks():
+    assert decode(head_dim=64) == la.LT_ERR_SHAPE
+    assert decode(batch=-1) == la.LT_ERR_SHAPE
+    assert decode(in_dtype=3) == la.LT_ERR_DTYPE
+    assert decode(o=A + 4 * MB + 1000) == la.LT_ERR_ALIAS        # o inside the state
+    assert decode(state=A + 512) == la.LT_ERR_ALIAS              # state over q
+    assert decode(batch=0) == la.LT_OK
+    assert decode(heads=0) == la.LT_OK

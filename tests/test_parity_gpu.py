@@ -1,0 +1,266 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Small and medium shapes that span several 64-token sub-blocks, ragged tails,
+empty inputs, carried-in states, in-place state updates, both input dtypes and
+both output dtypes. Tolerance: relative L2 per (sequence, head) of O and of
+the final state, <= 1e-5 for fp32 inputs and <= 1e-2 for bf16 inputs.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from parity_util import (TOL_BF16, TOL_F32, ensure_built, max_rel_per_head, max_rel_states,
+                         rel_l2, to_device, to_host_f32)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def la():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm device")
+    ensure_built()
+    import linear_attention_amd
+
+    return linear_attention_amd
+
+
+def tol(dtype):
+    return TOL_F32 if dtype == "f32" else TOL_BF16
+
+
+def run_prefill_case(la, batch, L, H, dtype, seed, block=256, with_s0=False, out_dtype="f32"):
+    import torch
+
+    print(f"[case] prefill batch={batch} L={L} H={H} dtype={dtype} seed={seed} s0={with_s0}",
+          flush=True)
+    q, k, v = workloads.qkv_host(seed, (batch, L, H, 128), dtype)
+    sl = workloads.slopes(H)
+    s0 = workloads.state_host(seed + 7, (batch, H, 128, 128)) if with_s0 else None
+    od = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    o, st = la.lt_prefill(to_device(q, dtype), to_device(k, dtype), to_device(v, dtype),
+                          torch.from_numpy(sl).cuda(), block,
+                          None if s0 is None else torch.from_numpy(s0).cuda(), out_dtype=od)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.recurrence_batch(q, k, v, sl, s0=s0)
+    o_g, s_g = to_host_f32(o), to_host_f32(st)
+    cu = np.arange(batch + 1) * L
+    eo = max_rel_per_head(o_g.reshape(batch * L, H, 128), o_ref.reshape(batch * L, H, 128), cu)
+    es = max_rel_states(s_g, s_ref)
+    return eo, es
+
+
+@pytest.mark.parametrize("L", [1, 2, 63, 64, 65, 128, 200, 1000])
+def test_prefill_bf16_lengths(la, L):
+    eo, es = run_prefill_case(la, 1, L, 4, "bf16", 100 + L)
+    assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)
+
+
+@pytest.mark.parametrize("L", [1, 63, 64, 65, 300])
+def test_prefill_f32_lengths(la, L):
+    eo, es = run_prefill_case(la, 1, L, 4, "f32", 200 + L)
+    assert eo <= TOL_F32 and es <= TOL_F32, (eo, es)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_batch_and_carried_state(la, dtype):
+    eo, es = run_prefill_case(la, 3, 190, 5, dtype, 301, with_s0=True)
+    assert eo <= tol(dtype) and es <= tol(dtype), (eo, es)
+
+
+def test_prefill_tiny_f32_config(la):
+    """Tiny fp32 prefill: batch 1, 8 heads, L = 1024, block 64, seed 1001; checked
+    against the recurrence and against brute-force quadratic masked attention."""
+    import torch
+
+    w = workloads.TINY_F32
+    q, k, v = workloads.qkv_host(w.seed, (1, w.seqlen, w.heads, 128), "f32")
+    sl = workloads.slopes(w.heads)
+    o, st = la.lt_prefill(to_device(q, "f32"), to_device(k, "f32"), to_device(v, "f32"),
+                          torch.from_numpy(sl).cuda(), w.block)
+    torch.cuda.synchronize()
+    o_g, s_g = to_host_f32(o), to_host_f32(st)
+    o_ref, s_ref = oracle.recurrence_batch(q, k, v, sl)
+    for h in range(w.heads):
+        ob, sb = oracle.brute_force(q[0, :, h], k[0, :, h], v[0, :, h], sl[h])
+        assert rel_l2(o_ref[0, :, h], ob) < 1e-12
+        assert rel_l2(o_g[0, :, h], ob) <= TOL_F32
+        assert rel_l2(o_g[0, :, h], o_ref[0, :, h]) <= TOL_F32
+        assert rel_l2(s_g[0, h], sb) <= TOL_F32
+        assert rel_l2(s_g[0, h], s_ref[0, h]) <= TOL_F32
+
+
+@pytest.mark.parametrize("block", [1, 16, 64, 100, 256, 4096])
+def test_prefill_block_argument_does_not_change_value(la, block):
+    eo, es = run_prefill_case(la, 1, 333, 2, "bf16", 401, block=block)
+    assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)
+
+
+def test_prefill_bf16_output(la):
+    eo, es = run_prefill_case(la, 1, 257, 3, "bf16", 501, out_dtype="bf16")
+    assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)
+
+
+def test_prefill_extreme_slopes(la):
+    """s = 0 (plain cumsum), tiny and huge slopes (decay underflows to exactly 0)."""
+    import torch
+
+    L, H = 300, 4
+    q, k, v = workloads.qkv_host(601, (1, L, H, 128), "bf16")
+    sl = np.array([0.0, 1e-6, 30.0, 500.0], np.float32)
+    o, st = la.lt_prefill(to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16"),
+                          torch.from_numpy(sl).cuda(), 256)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.recurrence_batch(q, k, v, sl)
+    o_g, s_g = to_host_f32(o), to_host_f32(st)
+    assert np.isfinite(o_g).all() and np.isfinite(s_g).all()
+    for h in range(H):
+        assert rel_l2(o_g[0, :, h], o_ref[0, :, h]) <= TOL_BF16, h
+        assert rel_l2(s_g[0, h], s_ref[0, h]) <= TOL_BF16, h
+
+
+def test_prefill_state_in_place(la):
+    """state_out == state_in updates the carried state in place."""
+    import torch
+
+    L, H = 150, 3
+    q, k, v = workloads.qkv_host(701, (2, L, H, 128), "bf16")
+    sl = workloads.slopes(H)
+    s0 = workloads.state_host(702, (2, H, 128, 128))
+    st = torch.from_numpy(s0).cuda()
+    o, st2 = la.lt_prefill(to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16"),
+                           torch.from_numpy(sl).cuda(), 64, st, state_out=st)
+    torch.cuda.synchronize()
+    assert st2.data_ptr() == st.data_ptr()
+    o_ref, s_ref = oracle.recurrence_batch(q, k, v, sl, s0=s0)
+    assert max_rel_states(to_host_f32(st), s_ref) <= TOL_BF16
+
+
+def test_prefill_zero_length_passes_state_through(la):
+    import torch
+
+    H = 3
+    s0 = workloads.state_host(801, (2, H, 128, 128))
+    q = torch.empty((2, 0, H, 128), device="cuda", dtype=torch.bfloat16)
+    sl = torch.from_numpy(workloads.slopes(H)).cuda()
+    _, st = la.lt_prefill(q, q, q, sl, 256, torch.from_numpy(s0).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host_f32(st), s0)
+    _, st = la.lt_prefill(q, q, q, sl, 256)
+    torch.cuda.synchronize()
+    assert not to_host_f32(st).any()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_varlen_ragged_with_empty_sequences(la, dtype):
+    import torch
+
+    H = 4
+    lens = [0, 1, 64, 65, 200, 0, 7, 130]
+    cu = workloads.cu_seqlens(lens)
+    T = int(cu[-1])
+    print(f"[case] varlen lens={lens} dtype={dtype}", flush=True)
+    q, k, v = workloads.qkv_host(901, (T, H, 128), dtype)
+    sl = workloads.slopes(H)
+    s0 = workloads.state_host(902, (len(lens), H, 128, 128))
+    o, st = la.lt_prefill_varlen(to_device(q, dtype), to_device(k, dtype), to_device(v, dtype),
+                                 torch.from_numpy(cu).cuda(), torch.from_numpy(sl).cuda(), 256,
+                                 torch.from_numpy(s0).cuda())
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.recurrence_packed(q, k, v, sl, cu, s0=s0)
+    assert max_rel_per_head(to_host_f32(o), o_ref, cu) <= tol(dtype)
+    assert max_rel_states(to_host_f32(st), s_ref) <= tol(dtype)
+
+
+def test_chunked_prefill_equals_one_shot(la):
+    """prefill(x[:a]) -> state -> prefill(x[a:], state) against the oracle over all of x."""
+    import torch
+
+    L, H, a = 777, 4, 321
+    q, k, v = workloads.qkv_host(1101, (1, L, H, 128), "bf16")
+    sl = workloads.slopes(H)
+    dq, dk, dv = (to_device(x, "bf16") for x in (q, k, v))
+    s_t = torch.from_numpy(sl).cuda()
+    o1, st1 = la.lt_prefill(dq[:, :a].contiguous(), dk[:, :a].contiguous(),
+                            dv[:, :a].contiguous(), s_t, 256)
+    o2, st2 = la.lt_prefill(dq[:, a:].contiguous(), dk[:, a:].contiguous(),
+                            dv[:, a:].contiguous(), s_t, 256, st1)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.recurrence_batch(q, k, v, sl)
+    o_g = np.concatenate([to_host_f32(o1), to_host_f32(o2)], axis=1)
+    cu = np.array([0, L])
+    assert max_rel_per_head(o_g[0], o_ref[0], cu) <= TOL_BF16
+    assert max_rel_states(to_host_f32(st2), s_ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_steps_continue_prefill(la, dtype):
+    """prefill(L) then n decode steps against the oracle recurrence over L + n tokens."""
+    import torch
+
+    B, H, L, n = 3, 5, 100, 6
+    q, k, v = workloads.qkv_host(1201, (B, L + n, H, 128), dtype)
+    sl = workloads.slopes(H)
+    s_t = torch.from_numpy(sl).cuda()
+    dq, dk, dv = (to_device(x, dtype) for x in (q, k, v))
+    _, st = la.lt_prefill(dq[:, :L].contiguous(), dk[:, :L].contiguous(),
+                          dv[:, :L].contiguous(), s_t, 64)
+    outs = []
+    for t in range(L, L + n):
+        outs.append(la.lt_decode(dq[:, t].contiguous(), dk[:, t].contiguous(),
+                                 dv[:, t].contiguous(), s_t, st))
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.recurrence_batch(q, k, v, sl)
+    for i, t in enumerate(range(L, L + n)):
+        og = to_host_f32(outs[i])
+        for b in range(B):
+            for h in range(H):
+                assert rel_l2(og[b, h], o_ref[b, t, h]) <= tol(dtype), (t, b, h)
+    assert max_rel_states(to_host_f32(st), s_ref) <= tol(dtype)
+
+
+def test_decode_single_step_exact_inputs(la):
+    """One decode step from a random fp32 state against the oracle's decode."""
+    import torch
+
+    B, H = 7, 6
+    q, k, v = workloads.qkv_host(1301, (B, H, 128), "bf16")
+    sl = workloads.slopes(H)
+    s0 = workloads.state_host(1302, (B, H, 128, 128))
+    st = torch.from_numpy(s0).cuda()
+    o = la.lt_decode(to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16"),
+                     torch.from_numpy(sl).cuda(), st, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.decode(q, k, v, sl, s0)
+    og, sg = to_host_f32(o), to_host_f32(st)
+    for b in range(B):
+        for h in range(H):
+            assert rel_l2(og[b, h], o_ref[b, h]) <= TOL_BF16
+            # fp32 state update: a few ulps
+            assert rel_l2(sg[b, h], s_ref[b, h]) <= 1e-6
+
+
+def test_prefill_is_deterministic(la):
+    import torch
+
+    q, k, v = workloads.qkv_host(1401, (1, 500, 8, 128), "bf16")
+    sl = torch.from_numpy(workloads.slopes(8)).cuda()
+    args = [to_device(x, "bf16") for x in (q, k, v)]
+    o1, s1 = la.lt_prefill(*args, sl, 256)
+    o2, s2 = la.lt_prefill(*args, sl, 256)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_launch_error_reports_status(la):
+    """Argument errors surface as LightningError with the status code."""
+    import torch
+
+    q = torch.zeros((1, 8, 2, 64), device="cuda", dtype=torch.bfloat16)
+    with pytest.raises(la.LightningError) as e:
+        la.lt_prefill(q, q, q, torch.zeros(2, device="cuda"), 64)
+    assert e.value.status == la.LT_ERR_SHAPE
