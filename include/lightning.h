@@ -36,7 +36,7 @@
  *  - Arguments are validated on the host before any launch. A failed check
  *    returns its status and enqueues nothing. A failed launch returns
  *    LT_ERR_HIP. No C++ exception crosses this interface.
- *  - Supported: head_dim == 128; in_dtype LT_BF16 or LT_F32 (bf16 inputs are
+ *  - Supported: head_dim == 128; 0 <= heads <= LT_MAX_HEADS; in_dtype LT_BF16 or LT_F32 (bf16 inputs are
  *    multiplied on MFMA with fp32 accumulation; fp32 inputs on fp32 MFMA);
  *    out_dtype LT_F32 or LT_BF16.
  *  - Overlap: `state_in == state_out` (same address) is allowed and updates the
@@ -72,6 +72,8 @@ typedef enum { LT_F32 = 0, LT_BF16 = 1 } lt_dtype;
 
 /* Largest block size accepted by the prefill entry points. */
 #define LT_MAX_BLOCK 65536
+/* Largest head count accepted (keeps in-kernel token strides in 32 bits). */
+#define LT_MAX_HEADS 65536
 
 /* Human-readable name of a status code (static storage; never NULL). */
 LT_API const char *lt_status_string(int status);
@@ -93,6 +95,9 @@ LT_API int lt_version(void);
  *   block      the method's block length B, 1..LT_MAX_BLOCK. The result does
  *              not depend on it (see above); the kernels schedule their own
  *              sub-blocks.
+ *   workspace  device scratch of workspace_bytes bytes owned by the caller (see
+ *              lt_prefill_workspace_bytes), or NULL. Its contents on entry do
+ *              not matter; it must not overlap any other argument.
  *   seqlen 0 writes state_out = state_in (or zeros). batch 0 or heads 0 is a
  *   no-op. Errors: LT_ERR_NULL, LT_ERR_SHAPE, LT_ERR_BLOCK, LT_ERR_DTYPE,
  *   LT_ERR_ALIAS, LT_ERR_HIP.
@@ -101,7 +106,18 @@ LT_API lt_status lt_prefill(const void *q, const void *k, const void *v, lt_dtyp
                             const float *slopes, void *o, lt_dtype out_dtype,
                             const float *state_in, float *state_out,
                             int batch, long long seqlen, int heads, int head_dim, int block,
-                            void *stream);
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * lt_prefill_workspace_bytes - device workspace that lets lt_prefill split long
+ * sequences across workgroups (used when batch * heads is too small to occupy
+ * the GPU with one workgroup per sequence and head; holds one fp32 d x d state
+ * per sequence, head and sequence piece). Returns 0 when no workspace helps or
+ * the arguments are invalid. lt_prefill given a NULL or smaller workspace still
+ * computes the same result, with one workgroup per (sequence, head).
+ */
+LT_API size_t lt_prefill_workspace_bytes(int batch, long long seqlen, int heads, int head_dim,
+                                         lt_dtype in_dtype);
 
 /*
  * lt_prefill_varlen - prefill of `num_seqs` packed sequences of different

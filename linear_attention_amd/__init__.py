@@ -4,16 +4,26 @@ The operator (MiniMax Signal Lab · M1, §03 Lightning Attention) is causal
 linear attention with a per-head exponential decay, evaluated block by block
 with a fixed d x d fp32 state per head, plus its one-token decode step.
 
-``lt_prefill``, ``lt_prefill_varlen`` and ``lt_decode`` mirror the C entry
-points of ``include/lightning.h`` one to one.
+``lt_prefill``, ``lt_prefill_workspace_bytes``, ``lt_prefill_varlen`` and
+``lt_decode`` mirror the C entry points of ``include/lightning.h`` one to one.
+The shared library is loaded on first use of any of these names (so the build
+module can be imported before the library exists); a missing library raises
+ImportError there, and there is no fallback path.
 """
 
-from ._native import (EXPORTS, HEAD_DIM, LIB_PATH, LT_BF16, LT_ERR_ALIAS, LT_ERR_BLOCK,
-                      LT_ERR_DTYPE, LT_ERR_HIP, LT_ERR_NULL, LT_ERR_SHAPE, LT_F32, LT_MAX_BLOCK,
-                      LT_OK, LightningError, lib, lt_decode, lt_prefill, lt_prefill_varlen,
-                      status_string)
+_NATIVE_NAMES = (
+    "lt_prefill", "lt_prefill_workspace_bytes", "lt_prefill_varlen", "lt_decode",
+    "LightningError", "lib", "status_string", "EXPORTS", "LIB_PATH", "HEAD_DIM", "LT_OK",
+    "LT_ERR_NULL", "LT_ERR_SHAPE", "LT_ERR_BLOCK", "LT_ERR_DTYPE", "LT_ERR_ALIAS", "LT_ERR_HIP",
+    "LT_F32", "LT_BF16", "LT_MAX_BLOCK",
+)
 
-__all__ = ["lt_prefill", "lt_prefill_varlen", "lt_decode", "LightningError", "lib",
-           "status_string", "EXPORTS", "LIB_PATH", "HEAD_DIM", "LT_OK", "LT_ERR_NULL",
-           "LT_ERR_SHAPE", "LT_ERR_BLOCK", "LT_ERR_DTYPE", "LT_ERR_ALIAS", "LT_ERR_HIP",
-           "LT_F32", "LT_BF16", "LT_MAX_BLOCK"]
+__all__ = list(_NATIVE_NAMES)
+
+
+def __getattr__(name):
+    if name in _NATIVE_NAMES:
+        from . import _native
+
+        return getattr(_native, name)
+    raise AttributeError(f"module {__name__!r} has no attribute {name!r}")

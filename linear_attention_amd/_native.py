@@ -19,7 +19,8 @@ LT_F32, LT_BF16 = 0, 1
 LT_MAX_BLOCK = 65536
 HEAD_DIM = 128
 
-EXPORTS = ("lt_status_string", "lt_version", "lt_prefill", "lt_prefill_varlen", "lt_decode")
+EXPORTS = ("lt_status_string", "lt_version", "lt_prefill", "lt_prefill_workspace_bytes",
+           "lt_prefill_varlen", "lt_decode")
 
 _vp, _i, _ll = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong
 
@@ -41,8 +42,10 @@ def _load() -> ctypes.CDLL:
     lib.lt_version.argtypes = []
     lib.lt_version.restype = _i
     lib.lt_prefill.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp,
-                               _i, _ll, _i, _i, _i, _vp]
+                               _i, _ll, _i, _i, _i, _vp, ctypes.c_size_t, _vp]
     lib.lt_prefill.restype = _i
+    lib.lt_prefill_workspace_bytes.argtypes = [_i, _ll, _i, _i, _i]
+    lib.lt_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.lt_prefill_varlen.argtypes = [_vp, _vp, _vp, _i, _vp, _i, _ll, _vp, _vp, _i,
                                       _vp, _vp, _i, _i, _i, _vp]
     lib.lt_prefill_varlen.restype = _i
@@ -98,13 +101,20 @@ def _stream(stream, device):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def lt_prefill_workspace_bytes(batch, seqlen, heads, head_dim=HEAD_DIM, in_dtype=LT_BF16) -> int:
+    return int(lib.lt_prefill_workspace_bytes(int(batch), int(seqlen), int(heads), int(head_dim),
+                                              int(in_dtype)))
+
+
 def lt_prefill(q, k, v, slopes, block, state_in=None, *, o=None, state_out=None,
-               want_state=True, out_dtype=None, stream=None):
+               want_state=True, out_dtype=None, workspace=None, stream=None):
     """Fixed-length prefill. q, k, v: [batch, L, H, 128]; slopes: fp32 [H].
 
     Returns (o [batch, L, H, 128], state_out [batch, H, 128, 128] fp32 or None).
     ``state_out`` may be given (it may be ``state_in`` itself for an in-place
-    update); otherwise one is allocated when ``want_state``.
+    update); otherwise one is allocated when ``want_state``. ``workspace`` is a
+    uint8 device tensor of at least ``lt_prefill_workspace_bytes`` bytes; one
+    is allocated when it is None and the plan wants one.
     """
     torch = _torch()
     if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
@@ -117,10 +127,16 @@ def lt_prefill(q, k, v, slopes, block, state_in=None, *, o=None, state_out=None,
         o = torch.empty((batch, L, H, d), device=q.device, dtype=out_dtype)
     if state_out is None and want_state:
         state_out = torch.empty((batch, H, d, d), device=q.device, dtype=torch.float32)
+    if workspace is None:
+        nbytes = lt_prefill_workspace_bytes(batch, L, H, d, _dtype_code(q.dtype))
+        if nbytes:
+            workspace = torch.empty(nbytes, device=q.device, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.lt_prefill(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dtype_code(q.dtype),
                         _dev_ptr(slopes, "slopes"), _dev_ptr(o, "o"), _dtype_code(o.dtype),
                         _dev_ptr(state_in, "state_in"), _dev_ptr(state_out, "state_out"),
-                        batch, L, H, d, int(block), _stream(stream, q.device))
+                        batch, L, H, d, int(block), _dev_ptr(workspace, "workspace"), ws_bytes,
+                        _stream(stream, q.device))
     _check(st, "lt_prefill")
     return o, state_out
 

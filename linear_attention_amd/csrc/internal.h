@@ -39,8 +39,28 @@ constexpr int kHeadDim = 128;
 // independent workgroups.
 constexpr int kValueSlices = 4;
 
-hipError_t launch_prefill(const PrefillArgs &a, lt_dtype in_dtype, lt_dtype out_dtype,
-                          hipStream_t stream);
+// How a bf16 prefill is cut into workgroups. Each (unit, head) sequence is
+// split into `segments` consecutive pieces of `seg_len` tokens (the last may be
+// shorter), one workgroup each. With more than one segment, a pre-pass over
+// `sub` equal pieces of every segment but the last computes the state each
+// piece contributes; segment g then starts from the decayed sum of everything
+// before it. All lengths are multiples of the 64-token sub-block.
+struct PrefillPlan {
+    int segments;
+    int sub;
+    long long seg_len;
+    size_t workspace;  // bytes: per (unit, head), (1 + (segments-1)*sub) fp32 d x d states
+};
+
+PrefillPlan plan_prefill(long long units, long long seqlen, int heads, lt_dtype in_dtype,
+                         bool varlen);
+
+// fp32 inputs: one workgroup per (unit, head, 32-column value slice).
+hipError_t launch_prefill_slices(const PrefillArgs &a, lt_dtype in_dtype, lt_dtype out_dtype,
+                                 hipStream_t stream);
+// bf16 inputs: one 8-wave workgroup per (unit, head, segment).
+hipError_t launch_prefill_heads(const PrefillArgs &a, const PrefillPlan &plan, void *workspace,
+                                lt_dtype out_dtype, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, lt_dtype in_dtype, lt_dtype out_dtype,
                          hipStream_t stream);
 

@@ -37,6 +37,25 @@ bool mul4(long long a, long long b, long long c, long long d, long long *out) {
 
 lt_status map_hip(hipError_t e) { return e == hipSuccess ? LT_OK : LT_ERR_HIP; }
 
+// Workgroups a prefill launch should reach to occupy MI355X (256 CUs; the
+// whole-head kernel runs one 8-wave workgroup per CU).
+constexpr long long kTargetWorkgroups = 256;
+// Shortest segment worth a workgroup of its own, and pre-pass pieces per segment.
+constexpr long long kMinSegment = 2048;
+constexpr int kPieces = 4;
+
+lt_status launch(const lt::PrefillArgs &a, int in_dtype, int out_dtype, bool varlen,
+                 void *workspace, size_t workspace_bytes, void *stream) {
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (in_dtype != LT_BF16)
+        return map_hip(lt::launch_prefill_slices(a, (lt_dtype)in_dtype, (lt_dtype)out_dtype, st));
+    lt::PrefillPlan p = lt::plan_prefill(a.units, varlen ? a.total_tokens : a.seqlen, a.heads,
+                                         (lt_dtype)in_dtype, varlen);
+    if (p.workspace > 0 && (!workspace || workspace_bytes < p.workspace))
+        p = lt::PrefillPlan{1, 1, varlen ? a.total_tokens : a.seqlen, 0};
+    return map_hip(lt::launch_prefill_heads(a, p, workspace, (lt_dtype)out_dtype, st));
+}
+
 // Shared checks of the two prefill entry points. `tokens` = rows of q/k/v/o.
 lt_status check_prefill(const void *q, const void *k, const void *v, int in_dtype,
                         const float *slopes, void *o, int out_dtype,
@@ -44,7 +63,8 @@ lt_status check_prefill(const void *q, const void *k, const void *v, int in_dtyp
                         long long units, long long tokens, int heads, int head_dim,
                         int block) {
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return LT_ERR_DTYPE;
-    if (head_dim != lt::kHeadDim || heads < 0 || units < 0 || tokens < 0) return LT_ERR_SHAPE;
+    if (head_dim != lt::kHeadDim || heads < 0 || heads > LT_MAX_HEADS || units < 0 || tokens < 0)
+        return LT_ERR_SHAPE;
     if (block < 1 || block > LT_MAX_BLOCK) return LT_ERR_BLOCK;
     if (units == 0 || heads == 0) return LT_OK;
     if (!slopes) return LT_ERR_NULL;
@@ -74,7 +94,40 @@ lt_status check_prefill(const void *q, const void *k, const void *v, int in_dtyp
 
 }  // namespace
 
+namespace lt {
+
+PrefillPlan plan_prefill(long long units, long long seqlen, int heads, lt_dtype in_dtype,
+                         bool varlen) {
+    PrefillPlan p{1, 1, seqlen, 0};
+    if (in_dtype != LT_BF16 || varlen || units <= 0 || heads <= 0) return p;
+    const long long uh = units * heads;
+    if (uh >= kTargetWorkgroups) return p;
+    long long g = (kTargetWorkgroups + uh - 1) / uh;
+    if (g > seqlen / kMinSegment) g = seqlen / kMinSegment;
+    if (g < 2) return p;
+    const long long quantum = 64LL * kPieces;
+    long long seg = (seqlen + g - 1) / g;
+    seg = (seg + quantum - 1) / quantum * quantum;
+    g = (seqlen + seg - 1) / seg;
+    if (g < 2) return p;
+    p.segments = (int)g;
+    p.sub = kPieces;
+    p.seg_len = seg;
+    p.workspace = (size_t)uh * (size_t)(1 + (g - 1) * kPieces) * kHeadDim * kHeadDim * sizeof(float);
+    return p;
+}
+
+}  // namespace lt
+
 extern "C" {
+
+LT_API size_t lt_prefill_workspace_bytes(int batch, long long seqlen, int heads, int head_dim,
+                                         lt_dtype in_dtype) {
+    if (batch <= 0 || seqlen <= 0 || heads <= 0 || heads > LT_MAX_HEADS ||
+        head_dim != lt::kHeadDim || !dtype_ok(in_dtype))
+        return 0;
+    return lt::plan_prefill(batch, seqlen, heads, in_dtype, false).workspace;
+}
 
 LT_API const char *lt_status_string(int status) {
     switch (status) {
@@ -95,18 +148,28 @@ LT_API lt_status lt_prefill(const void *q, const void *k, const void *v, lt_dtyp
                             const float *slopes, void *o, lt_dtype out_dtype,
                             const float *state_in, float *state_out,
                             int batch, long long seqlen, int heads, int head_dim, int block,
-                            void *stream) {
+                            void *workspace, size_t workspace_bytes, void *stream) {
     if (batch < 0 || seqlen < 0) return LT_ERR_SHAPE;
     long long tokens;
     if (__builtin_mul_overflow((long long)batch, seqlen, &tokens)) return LT_ERR_SHAPE;
     lt_status st = check_prefill(q, k, v, in_dtype, slopes, o, out_dtype, state_in, state_out,
                                  batch, tokens, heads, head_dim, block);
     if (st != LT_OK || batch == 0 || heads == 0) return st;
+    if (workspace && workspace_bytes > 0) {
+        const Range rw = range_of(workspace, (long long)workspace_bytes);
+        const long long in_b = tokens * heads * head_dim * dtype_size(in_dtype);
+        const long long st_b = (long long)batch * heads * head_dim * head_dim * 4;
+        if (overlaps(rw, range_of(q, in_b)) || overlaps(rw, range_of(k, in_b)) ||
+            overlaps(rw, range_of(v, in_b)) || overlaps(rw, range_of(slopes, heads * 4LL)) ||
+            overlaps(rw, range_of(o, tokens * heads * head_dim * dtype_size(out_dtype))) ||
+            (state_in && overlaps(rw, range_of(state_in, st_b))) ||
+            (state_out && overlaps(rw, range_of(state_out, st_b))))
+            return LT_ERR_ALIAS;
+    }
     if (tokens == 0 && !state_out) return LT_OK;
     lt::PrefillArgs a{q, k, v, slopes, o, state_in, state_out, nullptr, seqlen, tokens,
                       batch, heads};
-    return map_hip(lt::launch_prefill(a, in_dtype, out_dtype,
-                                      static_cast<hipStream_t>(stream)));
+    return launch(a, in_dtype, out_dtype, false, workspace, workspace_bytes, stream);
 }
 
 LT_API lt_status lt_prefill_varlen(const void *q, const void *k, const void *v, lt_dtype in_dtype,
@@ -129,15 +192,15 @@ LT_API lt_status lt_prefill_varlen(const void *q, const void *k, const void *v, 
     if (total_tokens == 0 && !state_out) return LT_OK;
     lt::PrefillArgs a{q, k, v, slopes, o, state_in, state_out, cu_seqlens, 0, total_tokens,
                       num_seqs, heads};
-    return map_hip(lt::launch_prefill(a, in_dtype, out_dtype,
-                                      static_cast<hipStream_t>(stream)));
+    return launch(a, in_dtype, out_dtype, true, nullptr, 0, stream);
 }
 
 LT_API lt_status lt_decode(const void *q, const void *k, const void *v, lt_dtype in_dtype,
                            const float *slopes, float *state, void *o, lt_dtype out_dtype,
                            int batch, int heads, int head_dim, void *stream) {
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return LT_ERR_DTYPE;
-    if (head_dim != lt::kHeadDim || heads < 0 || batch < 0) return LT_ERR_SHAPE;
+    if (head_dim != lt::kHeadDim || heads < 0 || heads > LT_MAX_HEADS || batch < 0)
+        return LT_ERR_SHAPE;
     if (batch == 0 || heads == 0) return LT_OK;
     if (!q || !k || !v || !slopes || !state || !o) return LT_ERR_NULL;
     long long units = (long long)batch * heads;

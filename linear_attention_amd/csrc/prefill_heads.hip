@@ -1,0 +1,448 @@
+// Lightning Attention prefill for bf16 inputs on gfx950 (MI355X): one 8-wave
+// workgroup per (sequence, head, segment of the sequence).
+//
+// Operator (MiniMax Signal Lab · M1, §03 Lightning Attention), per head with a
+// d x d fp32 state S carried across blocks of m tokens (positions 1..m):
+//   O_t = [(Q_t K_t^T) ⊙ D] V_t + (Q_t ⊙ d_q) S_{t-1}
+//   S_t = e^{-s m} S_{t-1} + (K_t ⊙ d_k)^T V_t
+//   D_ij = e^{-s(i-j)}[i>=j],  d_q[i] = e^{-s i},  d_k[j] = e^{-s(m-j)}.
+// The result does not depend on the block length, so the kernel walks each
+// sequence in 64-token sub-blocks.
+//
+// gfx950 design:
+//  * A workgroup owns a whole head (all 128 value columns), so the 64x64 score
+//    tile of a sub-block is computed once, and one loop iteration moves 80 KiB
+//    of HBM traffic (q, k, v in bf16, o in fp32) against ~44 MFMA issue slots
+//    per SIMD. Eight waves give two waves per SIMD to hide latency.
+//  * All products use v_mfma_f32_32x32x16_bf16 (fp32 accumulation). Wave w owns
+//    output block (queries 32*(w/4).., value columns 32*(w%4)..) and state
+//    blocks (keys 64*(w/4).., the same 32 columns); waves 0..2 also compute the
+//    three causal 32x32 score blocks and share P through LDS.
+//  * Q, K, V stay row-major in LDS. The transposed operands (V^T for P V, K^T
+//    and (V ⊙ d_k)^T for the state update) are read with ds_read_b64_tr_b16,
+//    which returns a 4x16 block transposed across each 16-lane group, so no
+//    VALU transposes are needed. Only V ⊙ d_k is formed by VALU.
+//  * The state lives in the MFMA accumulators of the eight waves for the whole
+//    segment; each sub-block it is also written to LDS once as bf16 S^T, the
+//    operand of the next sub-block's inter-block product.
+//  * Batch-1 prefill has only 64 (sequence, head) pairs for 256 CUs, so long
+//    sequences are cut into segments. A pre-pass kernel computes the state
+//    contributed by fixed pieces of every segment but the last (the same state
+//    update without outputs) into a workspace; segment g starts from
+//    e^{-s*start_g} S_0 plus each piece's state decayed to start_g.
+//  * Output stores are deferred one iteration so the prefetch loads of the next
+//    sub-block are always the newest memory operations in flight.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "internal.h"
+
+namespace lt {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+constexpr int D = kHeadDim;  // 128
+constexpr int C = 64;        // tokens per sub-block
+constexpr int NT = 512;      // 8 waves
+constexpr int QP = D + 8;    // LDS row pitch (elements) of the 128-wide tiles
+constexpr int PP = C + 8;    // LDS row pitch of the P tile
+constexpr float LOG2E = 1.4426950408889634f;
+
+static_assert(D == 128 && C == 64, "tile shapes are fixed below");
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// MFMA operand (32x32x16, bf16) from a row-major LDS tile whose rows are the
+// operand rows: lane l reads row row0 + (l % 32), contraction slots
+// k0 + 8*(l / 32) .. +7.
+__device__ __forceinline__ bf16x8 ld_op(const __bf16 *t, int pitch, int row0, int k0, int lane) {
+    return *reinterpret_cast<const bf16x8 *>(t + (row0 + (lane & 31)) * pitch + k0 + 8 * (lane >> 5));
+}
+
+// MFMA operand whose rows are the COLUMNS of a row-major LDS tile and whose
+// contraction runs down the tile rows: lane l gets tile[k0 + 8*(l/32) + e]
+// [c0 + (l % 32)], e = 0..7. ds_read_b64_tr_b16 lets each 16-lane group load a
+// 4x16 block (lanes 4r..4r+3 give row r) and hands lane i column i.
+__device__ __forceinline__ bf16x8 ld_op_t(const __bf16 *t, int pitch, int c0, int k0, int lane) {
+    const int li = lane & 15, grp = lane >> 4;
+    const __bf16 *p = t + (k0 + 8 * (grp >> 1) + (li >> 2)) * pitch + c0 + 16 * (grp & 1) + 4 * (li & 3);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p);
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p + 4 * pitch));
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ __forceinline__ uint4 keep_if(bool keep, uint4 x) {
+    return make_uint4(keep ? x.x : 0u, keep ? x.y : 0u, keep ? x.z : 0u, keep ? x.w : 0u);
+}
+
+// 8 bf16 (in a uint4) scaled by f, rounded back to bf16.
+__device__ __forceinline__ uint4 scale_bf16x8(uint4 x, float f) {
+    uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float lo = __uint_as_float(w[i] << 16) * f;
+        const float hi = __uint_as_float(w[i] & 0xffff0000u) * f;
+        const __bf16 blo = static_cast<__bf16>(lo), bhi = static_cast<__bf16>(hi);
+        uint16_t ulo, uhi;
+        __builtin_memcpy(&ulo, &blo, 2);
+        __builtin_memcpy(&uhi, &bhi, 2);
+        r[i] = (uint32_t)ulo | ((uint32_t)uhi << 16);
+    }
+    return make_uint4(r[0], r[1], r[2], r[3]);
+}
+
+// Register staging of one sub-block: thread t holds tokens (t/16) + 32i,
+// i = 0, 1, elements 8*(t%16)..+7 of q, k and v. Loads are unconditional with
+// rows clamped into [0, m), so their number never depends on m; rows >= m are
+// zeroed when written to LDS.
+template <bool WITH_Q>
+struct Stage {
+    uint4 q[2], k[2], v[2];
+
+    __device__ void load(const uint16_t *qg, const uint16_t *kg, const uint16_t *vg, int ts, int m,
+                         int tid) {
+        const int seg = tid & 15;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int t = (tid >> 4) + 32 * i;
+            const int row = (t < m ? t : m - 1) * ts + 8 * seg;
+            if (WITH_Q) q[i] = *reinterpret_cast<const uint4 *>(qg + row);
+            k[i] = *reinterpret_cast<const uint4 *>(kg + row);
+            v[i] = *reinterpret_cast<const uint4 *>(vg + row);
+        }
+    }
+
+    // Writes Q, K, V row-major and V ⊙ d_k (d_k[t] = e^{-s(m-1-t)}, 0 for t >= m).
+    __device__ void store(__bf16 *Qs, __bf16 *Ks, __bf16 *Vs, __bf16 *Vds, int m, float s2,
+                          int tid) {
+        const int seg = tid & 15;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int t = (tid >> 4) + 32 * i;
+            const bool in = t < m;
+            const int off = t * QP + 8 * seg;
+            if (WITH_Q) *reinterpret_cast<uint4 *>(Qs + off) = keep_if(in, q[i]);
+            *reinterpret_cast<uint4 *>(Ks + off) = keep_if(in, k[i]);
+            const uint4 vv = keep_if(in, v[i]);
+            *reinterpret_cast<uint4 *>(Vs + off) = vv;
+            const float dk = in ? fast_exp2(-s2 * (float)(m - 1 - t)) : 0.f;
+            *reinterpret_cast<uint4 *>(Vds + off) = scale_bf16x8(vv, dk);
+        }
+    }
+};
+
+// Wave roles (w = wave index, h = lane / 32, r32 = lane % 32):
+//   qh = w / 4, cq = w % 4
+//   output block   O[32qh + r32][32cq + 8(v/4) + 4h + v%4]           (as O^T)
+//   state blocks   S[64qh + 32db + 8(v/4) + 4h + v%4][32cq + r32], db = 0, 1
+// so the state block layout equals the accumulator layout of
+// mma(K^T rows, (V ⊙ d_k)^T rows).
+
+// S <- e^{-s m} S + K^T (V ⊙ d_k) for this wave's two state blocks.
+__device__ __forceinline__ void state_update(f32x16 (&S)[2], const __bf16 *Ks, const __bf16 *Vds,
+                                             float bd, int qh, int cq, int lane) {
+#pragma unroll
+    for (int db = 0; db < 2; ++db) S[db] *= bd;
+#pragma unroll
+    for (int ks = 0; ks < C / 16; ++ks) {
+        const bf16x8 b = ld_op_t(Vds, QP, 32 * cq, 16 * ks, lane);
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+            S[db] = mma(ld_op_t(Ks, QP, 64 * qh + 32 * db, 16 * ks, lane), b, S[db]);
+    }
+}
+
+// Writes the wave's state blocks as bf16 S^T rows (value column major).
+__device__ __forceinline__ void write_state_t(__bf16 *Sts, const f32x16 (&S)[2], int qh, int cq,
+                                              int lane) {
+    const int r32 = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int gv = 0; gv < 4; ++gv) {
+            bf16x4 x;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[r] = static_cast<__bf16>(S[db][4 * gv + r]);
+            *reinterpret_cast<bf16x4 *>(Sts + (32 * cq + r32) * QP + 64 * qh + 32 * db + 8 * gv + 4 * h) = x;
+        }
+}
+
+__device__ __forceinline__ void store_out4(float *p, const f32x16 &o, int gv) {
+    *reinterpret_cast<float4 *>(p) = make_float4(o[4 * gv], o[4 * gv + 1], o[4 * gv + 2], o[4 * gv + 3]);
+}
+__device__ __forceinline__ void store_out4(__bf16 *p, const f32x16 &o, int gv) {
+    bf16x4 y;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) y[r] = static_cast<__bf16>(o[4 * gv + r]);
+    *reinterpret_cast<bf16x4 *>(p) = y;
+}
+
+struct SeqRange {
+    long long start, len;
+};
+
+__device__ __forceinline__ SeqRange sequence_of(const PrefillArgs &a, int n) {
+    if (a.cu_seqlens) {
+        const long long T = a.total_tokens;
+        long long lo = a.cu_seqlens[n], hi = a.cu_seqlens[n + 1];
+        lo = lo < 0 ? 0 : (lo > T ? T : lo);
+        hi = hi < lo ? lo : (hi > T ? T : hi);
+        return {lo, hi - lo};
+    }
+    return {(long long)n * a.seqlen, a.seqlen};
+}
+
+// ---------------------------------------------------------------------------
+// Pre-pass: the state one piece of a sequence contributes, from a zero state:
+//   S_piece = sum_t e^{-s(end-1-t)} k_t^T v_t  over the piece's tokens.
+// Workgroup (unit, head, piece j) covers tokens [j*piece_len, (j+1)*piece_len),
+// all full 64-token sub-blocks. Piece 0 also copies the carried-in state S_0
+// (or zeros) to the workspace, so the main kernel never reads state_in and an
+// in-place state update cannot race.
+// Workspace per (unit, head): [S_0][S_piece 0 .. npieces-1], fp32 d x d each.
+__global__ __launch_bounds__(NT) void piece_state_kernel(PrefillArgs a, int npieces,
+                                                         long long piece_len, float *ws) {
+    __shared__ __attribute__((aligned(16))) __bf16 Ks[C * QP];
+    __shared__ __attribute__((aligned(16))) __bf16 Vs[C * QP];
+    __shared__ __attribute__((aligned(16))) __bf16 Vds[C * QP];
+
+    const int j = blockIdx.x % npieces;
+    const int uh = blockIdx.x / npieces;
+    const int h = uh % a.heads, n = uh / a.heads;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qh = w >> 2, cq = w & 3, r32 = lane & 31, hf = lane >> 5;
+
+    const SeqRange sr = sequence_of(a, n);
+    const int ts = a.heads * D;
+    const long long base = ((sr.start + j * piece_len) * a.heads + h) * (long long)D;
+    const uint16_t *kg = static_cast<const uint16_t *>(a.k) + base;
+    const uint16_t *vg = static_cast<const uint16_t *>(a.v) + base;
+    const float s2 = a.slopes[h] * LOG2E;
+    float *wsu = ws + (size_t)uh * (1 + npieces) * D * D;
+
+    if (j == 0) {
+        const long long sb = (long long)uh * D * D;
+        for (int e = tid; e < D * D; e += NT) wsu[e] = a.state_in ? a.state_in[sb + e] : 0.f;
+    }
+
+    f32x16 S[2];
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) S[db][v] = 0.f;
+
+    Stage<false> stage;
+    const long long nch = piece_len / C;
+    const float bd = fast_exp2(-s2 * (float)C);
+    stage.load(nullptr, kg, vg, ts, C, tid);
+    for (long long c = 0; c < nch; ++c) {
+        __syncthreads();
+        stage.store(nullptr, Ks, Vs, Vds, C, s2, tid);
+        const long long cn = (c + 1 < nch) ? c + 1 : c;
+        stage.load(nullptr, kg + cn * C * (long long)ts, vg + cn * C * (long long)ts, ts, C, tid);
+        __syncthreads();
+        state_update(S, Ks, Vds, bd, qh, cq, lane);
+    }
+
+    float *dst = wsu + (size_t)(1 + j) * D * D;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            dst[(64 * qh + 32 * db + 8 * (v >> 2) + 4 * hf + (v & 3)) * D + 32 * cq + r32] = S[db][v];
+}
+
+// ---------------------------------------------------------------------------
+template <typename OutT>
+__global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, int segments, long long seg_len,
+                                                  int sub, const float *ws) {
+    __shared__ __attribute__((aligned(16))) __bf16 Qs[C * QP];
+    __shared__ __attribute__((aligned(16))) __bf16 Ks[C * QP];
+    __shared__ __attribute__((aligned(16))) __bf16 Vs[C * QP];
+    __shared__ __attribute__((aligned(16))) __bf16 Vds[C * QP];
+    __shared__ __attribute__((aligned(16))) __bf16 Sts[2][D * QP];
+    __shared__ __attribute__((aligned(16))) __bf16 Ps[C * PP];
+
+    const int g = blockIdx.x % segments;
+    const int uh = blockIdx.x / segments;
+    const int h = uh % a.heads, n = uh / a.heads;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qh = w >> 2, cq = w & 3, r32 = lane & 31, hf = lane >> 5;
+
+    const SeqRange sr = sequence_of(a, n);
+    const long long seg0 = (long long)g * seg_len;
+    long long len = sr.len - seg0;
+    len = len < 0 ? 0 : (len > seg_len ? seg_len : len);
+    const int ts = a.heads * D;
+    const long long base = ((sr.start + seg0) * a.heads + h) * (long long)D;
+    const uint16_t *qg = static_cast<const uint16_t *>(a.q) + base;
+    const uint16_t *kg = static_cast<const uint16_t *>(a.k) + base;
+    const uint16_t *vg = static_cast<const uint16_t *>(a.v) + base;
+    OutT *og = static_cast<OutT *>(a.o) + base;
+    const float s2 = a.slopes[h] * LOG2E;
+
+    // ---- carried-in state of this segment
+    f32x16 S[2];
+    auto sidx = [&](int db, int v) {
+        return (64 * qh + 32 * db + 8 * (v >> 2) + 4 * hf + (v & 3)) * D + 32 * cq + r32;
+    };
+    if (segments == 1) {
+        const long long sb = (long long)uh * D * D;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) S[db][v] = a.state_in ? a.state_in[sb + sidx(db, v)] : 0.f;
+    } else {
+        const int npieces = (segments - 1) * sub;
+        const long long piece_len = seg_len / sub;
+        const float *wsu = ws + (size_t)uh * (1 + npieces) * D * D;
+        const float f0 = fast_exp2(-s2 * (float)seg0);
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) S[db][v] = f0 * wsu[sidx(db, v)];
+        for (int j = 0; j < g * sub; ++j) {
+            const float fj = fast_exp2(-s2 * (float)(seg0 - (j + 1) * piece_len));
+            const float *src = wsu + (size_t)(1 + j) * D * D;
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) S[db][v] += fj * src[sidx(db, v)];
+        }
+    }
+    write_state_t(Sts[0], S, qh, cq, lane);
+
+    // loop-invariant decay factors
+    const int qpos = 32 * qh + r32;                       // query row of this lane's outputs
+    const float dq = fast_exp2(-s2 * (float)(qpos + 1));  // d_q for that row
+    const bool scorer = w < 3;                            // waves 0..2 own one score block each
+    const int qb = w == 0 ? 0 : 1, kb = w == 2 ? 1 : 0;   // (query block, key block)
+    float dscore[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int diff = (32 * qb + r32) - (32 * kb + 8 * (v >> 2) + 4 * hf + (v & 3));
+        dscore[v] = diff >= 0 ? fast_exp2(-s2 * (float)diff) : 0.f;
+    }
+
+    Stage<true> stage;
+    const long long nfull = len / C;
+    const int tail = (int)(len - nfull * C);
+    const long long nchunks = nfull + (tail > 0);
+    auto chunk_len = [&](long long c) { return c < nfull ? C : tail; };
+    if (nchunks > 0) stage.load(qg, kg, vg, ts, chunk_len(0), tid);
+
+    int cur = 0;
+    f32x16 o;
+    OutT *orow = og;
+    auto flush = [&]() {
+#pragma unroll
+        for (int gv = 0; gv < 4; ++gv) store_out4(orow + 32 * cq + 8 * gv + 4 * hf, o, gv);
+    };
+
+    auto step = [&](long long c, int m, bool have_prev, auto full) {
+        constexpr bool FULL = decltype(full)::value;
+        __syncthreads();  // (A) readers of the previous tiles are done
+        stage.store(Qs, Ks, Vs, Vds, m, s2, tid);
+        if (have_prev) flush();
+        if (FULL) {
+            const long long cn = (c + 1 < nchunks) ? c + 1 : c;
+            const long long off = cn * C * (long long)ts;
+            stage.load(qg + off, kg + off, vg + off, ts, chunk_len(cn), tid);
+        }
+        __syncthreads();  // (B) tiles and S^T of the previous sub-block are visible
+
+        if (scorer) {
+            // scores^T block: keys 32kb.., queries 32qb.. ; masked, decayed, to LDS as P
+            f32x16 sc;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) sc[v] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks)
+                sc = mma(ld_op(Ks, QP, 32 * kb, 16 * ks, lane), ld_op(Qs, QP, 32 * qb, 16 * ks, lane), sc);
+#pragma unroll
+            for (int gv = 0; gv < 4; ++gv) {
+                bf16x4 p;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) p[r] = static_cast<__bf16>(sc[4 * gv + r] * dscore[4 * gv + r]);
+                *reinterpret_cast<bf16x4 *>(Ps + (32 * qb + r32) * PP + 32 * kb + 8 * gv + 4 * hf) = p;
+            }
+        }
+
+        // inter-block part: O^T = S^T (Q ⊙ d_q)^T
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[v] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            o = mma(ld_op(Sts[cur], QP, 32 * cq, 16 * ks, lane), ld_op(Qs, QP, 32 * qh, 16 * ks, lane), o);
+        o *= dq;
+
+        // state: S = e^{-s m} S + K^T (V ⊙ d_k), then S^T (bf16) for the next sub-block
+        state_update(S, Ks, Vds, fast_exp2(-s2 * (float)m), qh, cq, lane);
+        write_state_t(Sts[cur ^ 1], S, qh, cq, lane);
+        __syncthreads();  // (C) P is visible
+
+        // intra-block part: O^T += V^T P^T over the causal key range
+#pragma unroll
+        for (int ks = 0; ks < C / 16; ++ks) {
+            if (ks >= 2 * (qh + 1)) break;
+            o = mma(ld_op_t(Vs, QP, 32 * cq, 16 * ks, lane), ld_op(Ps, PP, 32 * qh, 16 * ks, lane), o);
+        }
+        orow = og + (c * C + qpos) * (long long)ts;
+        if (!FULL && qpos < m) flush();
+        cur ^= 1;
+    };
+    if (nfull > 0) step(0, C, false, std::true_type{});
+    for (long long c = 1; c < nfull; ++c) step(c, C, true, std::true_type{});
+    if (tail > 0)
+        step(nfull, tail, nfull > 0, std::false_type{});
+    else if (nfull > 0)
+        flush();
+
+    if (a.state_out && g == segments - 1) {
+        const long long sb = (long long)uh * D * D;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) a.state_out[sb + sidx(db, v)] = S[db][v];
+    }
+}
+
+template <typename OutT>
+hipError_t launch(const PrefillArgs &a, const PrefillPlan &p, void *workspace, hipStream_t stream) {
+    const long long uh = (long long)a.units * a.heads;
+    float *ws = static_cast<float *>(workspace);
+    if (p.segments > 1) {
+        const int npieces = (p.segments - 1) * p.sub;
+        hipLaunchKernelGGL(piece_state_kernel, dim3((unsigned)(uh * npieces)), dim3(NT), 0, stream,
+                           a, npieces, p.seg_len / p.sub, ws);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((head_kernel<OutT>), dim3((unsigned)(uh * p.segments)), dim3(NT), 0, stream,
+                       a, p.segments, p.seg_len, p.sub, ws);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_heads(const PrefillArgs &a, const PrefillPlan &plan, void *workspace,
+                                lt_dtype out_dtype, hipStream_t stream) {
+    return out_dtype == LT_F32 ? launch<float>(a, plan, workspace, stream)
+                               : launch<__bf16>(a, plan, workspace, stream);
+}
+
+}  // namespace lt

@@ -34,6 +34,8 @@
 
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace lt {
@@ -53,6 +55,19 @@ constexpr float LOG2E = 1.4426950408889634f;
 static_assert(SL == 32 && C == 64 && D == 128, "tile shapes are fixed below");
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Component-wise select (keeps vector selects in registers).
+__device__ __forceinline__ uint4 keep_if(bool keep, uint4 x) {
+    return make_uint4(keep ? x.x : 0u, keep ? x.y : 0u, keep ? x.z : 0u, keep ? x.w : 0u);
+}
+__device__ __forceinline__ float4 keep_if(bool keep, float4 x) {
+    return make_float4(keep ? x.x : 0.f, keep ? x.y : 0.f, keep ? x.z : 0.f, keep ? x.w : 0.f);
+}
+
+// 2^x with the hardware exp2 (v_exp_f32, about 1 ulp). Arguments here are
+// never positive; results below the fp32 normal range may flush to zero, which
+// changes a decay product by less than 2^-126 relative.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Per-input-type MFMA policy. Operands are read from LDS rows in which the
 // contraction index is contiguous; lane l reads row (l % 16), contraction
@@ -98,24 +113,40 @@ __device__ __forceinline__ f32x4 contract(f32x4 acc, const typename M::E *a, int
     return acc;
 }
 
-// O^T[cols][queries] += V^T[cols][keys] P^T[keys][queries] for the causal key
-// tiles 0..w of wave w. sc[kt] holds scores^T tile kt in accumulator layout:
+// acc[j] += A_j[16 rows][K] * B_j[K][16 cols] for N independent tiles; the
+// contraction loop is outermost so the N MFMA chains interleave.
+// a(j) and b(j) return the first row of tile j's A and B operands.
+template <typename M, int K, int N, typename FA, typename FB>
+__device__ __forceinline__ void contract_n(f32x4 (&acc)[N], FA a, FB b, int a_pitch, int b_pitch,
+                                           int lane) {
+    const int oa = (lane & 15) * a_pitch + (lane >> 4) * M::KPL;
+    const int ob = (lane & 15) * b_pitch + (lane >> 4) * M::KPL;
+#pragma unroll
+    for (int ks = 0; ks < K / M::KSTEP; ++ks)
+#pragma unroll
+        for (int j = 0; j < N; ++j)
+            acc[j] = M::mma(M::ld(a(j) + oa + ks * M::KSTEP), M::ld(b(j) + ob + ks * M::KSTEP),
+                            acc[j]);
+}
+
+// O^T[cols][queries] += V^T[cols][keys] P^T[keys][queries] over the sub-block's
+// four key tiles (P is zero above the diagonal). sc[kt] holds scores^T tile kt
+// in accumulator layout:
 // lane l has keys 16kt + 4(l/16) + r, r = 0..3, for query (l % 16).
 template <typename M>
 __device__ __forceinline__ void intra(f32x4 (&o)[2], const f32x4 (&sc)[4],
-                                      const typename M::E *vts, int tp, int w, int lane);
+                                      const typename M::E *vts, int tp, int lane);
 
 template <>
 __device__ __forceinline__ void intra<Mma<__bf16>>(f32x4 (&o)[2], const f32x4 (&sc)[4],
-                                                   const __bf16 *vts, int tp, int w, int lane) {
+                                                   const __bf16 *vts, int tp, int lane) {
     const int li = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-        if (2 * ks > w) break;
         // contraction slots 0..3 -> keys 32ks + 4g + r, slots 4..7 -> keys 32ks + 16 + 4g + r
         bf16x8 b;
         const f32x4 lo = sc[2 * ks];
-        const f32x4 hi = (2 * ks + 1 <= w) ? sc[2 * ks + 1] : f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 hi = sc[2 * ks + 1];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             b[r] = static_cast<__bf16>(lo[r]);
@@ -139,11 +170,10 @@ __device__ __forceinline__ void intra<Mma<__bf16>>(f32x4 (&o)[2], const f32x4 (&
 
 template <>
 __device__ __forceinline__ void intra<Mma<float>>(f32x4 (&o)[2], const f32x4 (&sc)[4],
-                                                  const float *vts, int tp, int w, int lane) {
+                                                  const float *vts, int tp, int lane) {
     const int li = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-        if (kt > w) break;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -166,39 +196,42 @@ template <> struct Stage<__bf16> {
     static constexpr int TPT = 4, NV = 1;
     uint4 q[TPT], k[TPT], v[NV];
 
-    __device__ void load(const uint16_t *qg, const uint16_t *kg, const uint16_t *vg, long long ts,
-                         int m, int tid) {
+    // Every thread issues the same loads on every call (row indices clamped
+    // into [0, m)), so the number of memory operations in flight never depends
+    // on m and the compiler can count them exactly. Rows t >= m are zeroed in
+    // store(), not here, so nothing waits on these loads before the data is
+    // needed. `ts` (elements between tokens) times 63 fits in 32 bits.
+    __device__ void load(const uint16_t *qg, const uint16_t *kg, const uint16_t *vg, int ts, int m,
+                         int tid) {
         const int seg = tid & 15, t0 = 4 * (tid >> 4);
 #pragma unroll
         for (int i = 0; i < TPT; ++i) {
             const int t = t0 + i;
-            if (t < m) {
-                q[i] = *reinterpret_cast<const uint4 *>(qg + t * ts + 8 * seg);
-                k[i] = *reinterpret_cast<const uint4 *>(kg + t * ts + 8 * seg);
-            } else {
-                q[i] = make_uint4(0, 0, 0, 0);
-                k[i] = make_uint4(0, 0, 0, 0);
-            }
+            const int row = (t < m ? t : m - 1) * ts + 8 * seg;
+            q[i] = *reinterpret_cast<const uint4 *>(qg + row);
+            k[i] = *reinterpret_cast<const uint4 *>(kg + row);
         }
         const int vt = tid >> 2, vs = tid & 3;
-        v[0] = (vt < m) ? *reinterpret_cast<const uint4 *>(vg + vt * ts + 8 * vs)
-                        : make_uint4(0, 0, 0, 0);
+        v[0] = *reinterpret_cast<const uint4 *>(vg + (vt < m ? vt : m - 1) * ts + 8 * vs);
     }
 
     // Writes Q, K (row-major), K ⊙ d_k transposed, and V transposed into LDS.
     __device__ void store(__bf16 *Qs, __bf16 *Ks, __bf16 *Kts, __bf16 *Vts, int qp, int tp, int m,
-                          float s2, int tid) const {
+                          float s2, int tid) {
         const int seg = tid & 15, t0 = 4 * (tid >> 4);
 #pragma unroll
         for (int i = 0; i < TPT; ++i) {
+            q[i] = keep_if(t0 + i < m, q[i]);
+            k[i] = keep_if(t0 + i < m, k[i]);
             *reinterpret_cast<uint4 *>(Qs + (t0 + i) * qp + 8 * seg) = q[i];
             *reinterpret_cast<uint4 *>(Ks + (t0 + i) * qp + 8 * seg) = k[i];
         }
+        v[0] = keep_if((tid >> 2) < m, v[0]);
         float dk[TPT];
 #pragma unroll
         for (int i = 0; i < TPT; ++i) {
             const int t = t0 + i;
-            dk[i] = (t < m) ? exp2f(-s2 * (float)(m - 1 - t)) : 0.f;
+            dk[i] = (t < m) ? fast_exp2(-s2 * (float)(m - 1 - t)) : 0.f;
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -225,42 +258,40 @@ template <> struct Stage<float> {
     static constexpr int TPT = 8, NV = 2;
     float4 q[TPT], k[TPT], v[NV];
 
-    __device__ void load(const float *qg, const float *kg, const float *vg, long long ts, int m,
-                         int tid) {
+    __device__ void load(const float *qg, const float *kg, const float *vg, int ts, int m, int tid) {
         const int seg = tid & 31, t0 = 8 * (tid >> 5);
 #pragma unroll
         for (int i = 0; i < TPT; ++i) {
             const int t = t0 + i;
-            if (t < m) {
-                q[i] = *reinterpret_cast<const float4 *>(qg + t * ts + 4 * seg);
-                k[i] = *reinterpret_cast<const float4 *>(kg + t * ts + 4 * seg);
-            } else {
-                q[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-                k[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-            }
+            const int row = (t < m ? t : m - 1) * ts + 4 * seg;
+            q[i] = *reinterpret_cast<const float4 *>(qg + row);
+            k[i] = *reinterpret_cast<const float4 *>(kg + row);
         }
         const int vs = tid & 7;
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
             const int vt = (tid >> 3) + 32 * j;
-            v[j] = (vt < m) ? *reinterpret_cast<const float4 *>(vg + vt * ts + 4 * vs)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
+            v[j] = *reinterpret_cast<const float4 *>(vg + (vt < m ? vt : m - 1) * ts + 4 * vs);
         }
     }
 
     __device__ void store(float *Qs, float *Ks, float *Kts, float *Vts, int qp, int tp, int m,
-                          float s2, int tid) const {
+                          float s2, int tid) {
         const int seg = tid & 31, t0 = 8 * (tid >> 5);
 #pragma unroll
         for (int i = 0; i < TPT; ++i) {
+            q[i] = keep_if(t0 + i < m, q[i]);
+            k[i] = keep_if(t0 + i < m, k[i]);
             *reinterpret_cast<float4 *>(Qs + (t0 + i) * qp + 4 * seg) = q[i];
             *reinterpret_cast<float4 *>(Ks + (t0 + i) * qp + 4 * seg) = k[i];
         }
+#pragma unroll
+        for (int j = 0; j < NV; ++j) v[j] = keep_if((tid >> 3) + 32 * j < m, v[j]);
         float dk[TPT];
 #pragma unroll
         for (int i = 0; i < TPT; ++i) {
             const int t = t0 + i;
-            dk[i] = (t < m) ? exp2f(-s2 * (float)(m - 1 - t)) : 0.f;
+            dk[i] = (t < m) ? fast_exp2(-s2 * (float)(m - 1 - t)) : 0.f;
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -330,7 +361,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs a) {
         len = a.seqlen;
     }
 
-    const long long ts = (long long)a.heads * D;  // elements between consecutive tokens
+    const int ts = a.heads * D;  // elements between consecutive tokens (checked < 2^24)
     const long long base = (start * a.heads + h) * D;
     const G *qg = static_cast<const G *>(a.q) + base;
     const G *kg = static_cast<const G *>(a.k) + base;
@@ -366,69 +397,87 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs a) {
     write_state_operand(Sts[0]);
 
     Stage<InT> stage;
-    const long long nchunks = (len + C - 1) / C;
-    if (nchunks > 0) stage.load(qg, kg, vg, ts, (int)(len < C ? len : C), tid);
+    const long long nfull = len / C;               // full sub-blocks
+    const int tail = (int)(len - nfull * C);        // tokens in a last short one
+    const long long nchunks = nfull + (tail > 0);
+    auto chunk_len = [&](long long c) { return c < nfull ? C : tail; };
+    if (nchunks > 0) stage.load(qg, kg, vg, ts, chunk_len(0), tid);
 
+    const int qpos = 16 * w + li;  // query row (in the sub-block) of this lane's outputs
     int cur = 0;
-    for (long long c = 0; c < nchunks; ++c) {
-        const long long rem = len - c * C;
-        const int m = (int)(rem < C ? rem : C);
+    // Outputs of a full sub-block are stored one step late, after the wait for
+    // the next tiles and before the next prefetch is issued: the prefetch loads
+    // are then always the newest memory operations in flight, so waiting for
+    // them never waits on output stores issued after them.
+    f32x4 o_prev[2];
+    OutT *orow_prev = og;
+    auto flush = [&]() {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) store_out(orow_prev + 16 * ct + 4 * g, o_prev[ct]);
+    };
+    // One sub-block of m tokens. FULL sub-blocks (m == C) have no data-dependent
+    // branch around any memory operation.
+    auto step = [&](long long c, int m, bool have_prev, auto full) {
+        constexpr bool FULL = decltype(full)::value;
         __syncthreads();  // previous sub-block's readers of the tiles are done
         stage.store(Qs, Ks, Kts, Vts, QP, TP, m, s2, tid);
-        if (c + 1 < nchunks) {
-            const long long rem2 = rem - C;
-            const long long off = (c + 1) * C * ts;
-            stage.load(qg + off, kg + off, vg + off, ts, (int)(rem2 < C ? rem2 : C), tid);
+        if (have_prev) flush();
+        if (FULL) {
+            // prefetch the next sub-block (after the last one, re-read this one)
+            const long long cn = (c + 1 < nchunks) ? c + 1 : c;
+            const long long off = cn * C * (long long)ts;
+            stage.load(qg + off, kg + off, vg + off, ts, chunk_len(cn), tid);
         }
         __syncthreads();  // tiles and the previous state operand are visible
 
-        // scores^T tiles (keys 16kt.., queries 16w..), causal: kt <= w
+        // scores^T tiles (keys 16kt.., queries 16w..) and the inter-block product
+        // S^T Q^T share the B operand (this wave's 16 queries): six independent
+        // MFMA chains, interleaved.
+        f32x4 acc[6];
+        const E *sts = Sts[cur];
+        const E *qrow = Qs + 16 * w * QP;
+#pragma unroll
+        for (int j = 0; j < 6; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        contract_n<M, D, 6>(
+            acc, [&](int j) { return j < 4 ? Ks + 16 * j * QP : sts + 16 * (j - 4) * QP; },
+            [&](int) { return qrow; }, QP, QP, lane);
+
         f32x4 sc[4];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (kt <= w) sc[kt] = contract<M, D>(sc[kt], Ks + 16 * kt * QP, QP, Qs + 16 * w * QP, QP, lane);
-        }
-        const int qpos = 16 * w + li;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            if (kt > w) break;
+        for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int diff = qpos - (16 * kt + 4 * g + r);
-                sc[kt][r] = diff >= 0 ? sc[kt][r] * exp2f(-s2 * (float)diff) : 0.f;
+                sc[kt][r] = diff >= 0 ? acc[kt][r] * fast_exp2(-s2 * (float)diff) : 0.f;
             }
-        }
 
         // O^T = S^T (Q ⊙ d_q)^T + V^T P^T for value columns 16ct.., queries 16w..
-        f32x4 o[2];
-        const float dq = exp2f(-s2 * (float)(qpos + 1));
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            o[ct] = contract<M, D>(f32x4{0.f, 0.f, 0.f, 0.f}, Sts[cur] + 16 * ct * QP, QP,
-                                   Qs + 16 * w * QP, QP, lane);
-            o[ct] *= dq;
-        }
-        intra<M>(o, sc, Vts, TP, w, lane);
-        if (qpos < m) {
-            OutT *orow = og + (c * C + qpos) * ts;
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) store_out(orow + 16 * ct + 4 * g, o[ct]);
-        }
+        const float dq = fast_exp2(-s2 * (float)(qpos + 1));
+        o_prev[0] = acc[4] * dq;
+        o_prev[1] = acc[5] * dq;
+        intra<M>(o_prev, sc, Vts, TP, lane);
+        orow_prev = og + (c * C + qpos) * (long long)ts;
+        if (!FULL && qpos < m) flush();
 
         // S = e^{-s m} S + (K ⊙ d_k)^T V   (keys 32w.., all 32 columns)
-        const float bd = exp2f(-s2 * (float)m);
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                S[rt][ct] *= bd;
-                S[rt][ct] = contract<M, C>(S[rt][ct], Kts + (32 * w + 16 * rt) * TP, TP,
-                                           Vts + 16 * ct * TP, TP, lane);
-            }
+        const float bd = fast_exp2(-s2 * (float)m);
+        f32x4 sacc[4] = {S[0][0] * bd, S[0][1] * bd, S[1][0] * bd, S[1][1] * bd};
+        contract_n<M, C, 4>(
+            sacc, [&](int j) { return Kts + (32 * w + 16 * (j >> 1)) * TP; },
+            [&](int j) { return Vts + 16 * (j & 1) * TP; }, TP, TP, lane);
+        S[0][0] = sacc[0];
+        S[0][1] = sacc[1];
+        S[1][0] = sacc[2];
+        S[1][1] = sacc[3];
         cur ^= 1;
         write_state_operand(Sts[cur]);
-    }
+    };
+    if (nfull > 0) step(0, C, false, std::true_type{});
+    for (long long c = 1; c < nfull; ++c) step(c, C, true, std::true_type{});
+    if (tail > 0)
+        step(nfull, tail, nfull > 0, std::false_type{});
+    else if (nfull > 0)
+        flush();
 
     if (a.state_out) {
 #pragma unroll
@@ -451,7 +500,7 @@ hipError_t launch(const PrefillArgs &a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs &a, lt_dtype in_dtype, lt_dtype out_dtype,
+hipError_t launch_prefill_slices(const PrefillArgs &a, lt_dtype in_dtype, lt_dtype out_dtype,
                           hipStream_t stream) {
     if (in_dtype == LT_BF16)
         return out_dtype == LT_F32 ? launch<__bf16, float>(a, stream) : launch<__bf16, __bf16>(a, stream);

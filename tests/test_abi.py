@@ -57,7 +57,8 @@ def test_status_strings():
 def prefill(**kw):
     args = dict(q=A, k=A + 100 * MB, v=A + 200 * MB, in_dtype=la.LT_BF16, slopes=A + 300 * MB,
                 o=A + 400 * MB, out_dtype=la.LT_F32, state_in=None, state_out=A + 900 * MB,
-                batch=1, seqlen=64, heads=2, head_dim=128, block=64, stream=None)
+                batch=1, seqlen=64, heads=2, head_dim=128, block=64, workspace=None,
+                workspace_bytes=0, stream=None)
     args.update(kw)
     return la.lib.lt_prefill(*args.values())
 
@@ -107,6 +108,23 @@ def test_prefill_alias_checks():
     s = A + 900 * MB
     assert prefill(state_in=s, state_out=s + 4096) == la.LT_ERR_ALIAS  # partial overlap
     assert prefill(state_in=s, state_out=s + 8 * MB, batch=0) == la.LT_OK
+
+
+def test_prefill_workspace_alias():
+    assert prefill(workspace=A + 100, workspace_bytes=4096) == la.LT_ERR_ALIAS   # inside q
+    assert prefill(workspace=A + 900 * MB - 16, workspace_bytes=64) == la.LT_ERR_ALIAS  # state_out
+
+
+def test_workspace_query():
+    ws = la.lt_prefill_workspace_bytes
+    # batch 1, 64 heads, 32K tokens: four segments of 8192 tokens, four pieces each
+    assert ws(1, 32768, 64) == 64 * (1 + 3 * 4) * 128 * 128 * 4
+    assert ws(1, 1 << 20, 64) == 64 * (1 + 3 * 4) * 128 * 128 * 4
+    assert ws(4, 32768, 64) == 0          # 256 (sequence, head) pairs already fill the GPU
+    assert ws(1, 2048, 64) == 0           # too short to split
+    assert ws(1, 32768, 64, in_dtype=la.LT_F32) == 0
+    assert ws(1, 32768, 64, head_dim=64) == 0
+    assert ws(0, 32768, 64) == 0
 
 
 def test_prefill_noops_need_no_gpu():

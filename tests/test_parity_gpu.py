@@ -264,3 +264,52 @@ def test_launch_error_reports_status(la):
     with pytest.raises(la.LightningError) as e:
         la.lt_prefill(q, q, q, torch.zeros(2, device="cuda"), 64)
     assert e.value.status == la.LT_ERR_SHAPE
+
+
+@pytest.mark.parametrize("L,H,with_s0", [(5000, 2, False), (9000, 1, True), (20000, 3, True),
+                                         (16384, 4, False)])
+def test_prefill_segmented_long_sequences(la, L, H, with_s0):
+    """Few (sequence, head) pairs and long sequences take the segmented plan:
+    a pre-pass over sequence pieces plus one workgroup per segment."""
+    assert la.lt_prefill_workspace_bytes(1, L, H) > 0
+    eo, es = run_prefill_case(la, 1, L, H, "bf16", 2000 + L, with_s0=with_s0)
+    assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)
+
+
+def test_prefill_segmented_matches_unsegmented(la):
+    """The same inputs with and without a workspace (segmented vs one workgroup
+    per sequence and head) both match the oracle."""
+    import torch
+
+    L, H = 12000, 2
+    q, k, v = workloads.qkv_host(2101, (1, L, H, 128), "bf16")
+    sl = workloads.slopes(H)
+    s0 = workloads.state_host(2102, (1, H, 128, 128))
+    args = [to_device(x, "bf16") for x in (q, k, v)]
+    s_t = torch.from_numpy(sl).cuda()
+    o_seg, st_seg = la.lt_prefill(*args, s_t, 256, torch.from_numpy(s0).cuda())
+    o_one, st_one = la.lt_prefill(*args, s_t, 256, torch.from_numpy(s0).cuda(),
+                                  workspace=torch.empty(0, device="cuda", dtype=torch.uint8))
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.recurrence_batch(q, k, v, sl, s0=s0)
+    cu = np.array([0, L])
+    for o_g, s_g in ((o_seg, st_seg), (o_one, st_one)):
+        assert max_rel_per_head(to_host_f32(o_g)[0], o_ref[0], cu) <= TOL_BF16
+        assert max_rel_states(to_host_f32(s_g), s_ref) <= TOL_BF16
+
+
+def test_prefill_segmented_state_in_place(la):
+    """Segmented plan with state_out == state_in: the pre-pass snapshots the
+    carried-in state, so the in-place update cannot race."""
+    import torch
+
+    L, H = 10000, 2
+    q, k, v = workloads.qkv_host(2201, (1, L, H, 128), "bf16")
+    sl = workloads.slopes(H)
+    s0 = workloads.state_host(2202, (1, H, 128, 128))
+    st = torch.from_numpy(s0).cuda()
+    la.lt_prefill(*(to_device(x, "bf16") for x in (q, k, v)), torch.from_numpy(sl).cuda(), 256,
+                  st, state_out=st)
+    torch.cuda.synchronize()
+    _, s_ref = oracle.recurrence_batch(q, k, v, sl, s0=s0, want_o=False)
+    assert max_rel_states(to_host_f32(st), s_ref) <= TOL_BF16
