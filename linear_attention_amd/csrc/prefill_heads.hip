@@ -124,7 +124,8 @@ struct Stage {
         }
     }
 
-    // Writes Q, K, V row-major and V ⊙ d_k (d_k[t] = e^{-s(m-1-t)}, 0 for t >= m).
+    // Writes Q, K, V row-major and V ⊙ d_k (d_k[t] = e^{-s(m-1-t)}, 0 for t >= m);
+    // without Q (the pre-pass) only K and V ⊙ d_k.
     __device__ void store(__bf16 *Qs, __bf16 *Ks, __bf16 *Vs, __bf16 *Vds, int m, float s2,
                           int tid) {
         const int seg = tid & 15;
@@ -136,7 +137,7 @@ struct Stage {
             if (WITH_Q) *reinterpret_cast<uint4 *>(Qs + off) = keep_if(in, q[i]);
             *reinterpret_cast<uint4 *>(Ks + off) = keep_if(in, k[i]);
             const uint4 vv = keep_if(in, v[i]);
-            *reinterpret_cast<uint4 *>(Vs + off) = vv;
+            if (WITH_Q) *reinterpret_cast<uint4 *>(Vs + off) = vv;  // the pre-pass needs only V ⊙ d_k
             const float dk = in ? fast_exp2(-s2 * (float)(m - 1 - t)) : 0.f;
             *reinterpret_cast<uint4 *>(Vds + off) = scale_bf16x8(vv, dk);
         }
@@ -179,14 +180,44 @@ __device__ __forceinline__ void write_state_t(__bf16 *Sts, const f32x16 (&S)[2],
         }
 }
 
-__device__ __forceinline__ void store_out4(float *p, const f32x16 &o, int gv) {
-    *reinterpret_cast<float4 *>(p) = make_float4(o[4 * gv], o[4 * gv + 1], o[4 * gv + 2], o[4 * gv + 3]);
-}
-__device__ __forceinline__ void store_out4(__bf16 *p, const f32x16 &o, int gv) {
-    bf16x4 y;
+// Output tile staging. Each wave writes its 32x32 fp32 output block into an
+// LDS tile Os[64][OSP]; the workgroup then stores whole output rows (512 B in
+// fp32) with consecutive lanes on consecutive addresses. Stored straight from
+// the MFMA accumulator layout, a row would arrive in 32-byte pieces from four
+// instructions, which measured at under 60% of the HBM throughput of full-row
+// stores for this access pattern.
+constexpr int OSP = D + 4;  // fp32 row pitch of the staged output tile
+
+__device__ __forceinline__ void stage_out(float *Os, const f32x16 &o, int qh, int cq, int lane) {
+    const int r32 = lane & 31, hf = lane >> 5;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) y[r] = static_cast<__bf16>(o[4 * gv + r]);
-    *reinterpret_cast<bf16x4 *>(p) = y;
+    for (int gv = 0; gv < 4; ++gv)
+        *reinterpret_cast<float4 *>(Os + (32 * qh + r32) * OSP + 32 * cq + 8 * gv + 4 * hf) =
+            make_float4(o[4 * gv], o[4 * gv + 1], o[4 * gv + 2], o[4 * gv + 3]);
+}
+
+// Stores rows [0, m) of the staged tile to out (row r at out + r * ts).
+template <bool FULL>
+__device__ __forceinline__ void store_rows(float *out, long long ts, const float *Os, int m, int tid) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = (tid >> 5) + 16 * j, col = 4 * (tid & 31);
+        const float4 x = *reinterpret_cast<const float4 *>(Os + row * OSP + col);
+        if (FULL || row < m) *reinterpret_cast<float4 *>(out + row * ts + col) = x;
+    }
+}
+template <bool FULL>
+__device__ __forceinline__ void store_rows(__bf16 *out, long long ts, const float *Os, int m, int tid) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int row = (tid >> 4) + 32 * j, col = 8 * (tid & 15);
+        const float4 x0 = *reinterpret_cast<const float4 *>(Os + row * OSP + col);
+        const float4 x1 = *reinterpret_cast<const float4 *>(Os + row * OSP + col + 4);
+        const bf16x8 y = {static_cast<__bf16>(x0.x), static_cast<__bf16>(x0.y), static_cast<__bf16>(x0.z),
+                          static_cast<__bf16>(x0.w), static_cast<__bf16>(x1.x), static_cast<__bf16>(x1.y),
+                          static_cast<__bf16>(x1.z), static_cast<__bf16>(x1.w)};
+        if (FULL || row < m) *reinterpret_cast<bf16x8 *>(out + row * ts + col) = y;
+    }
 }
 
 struct SeqRange {
@@ -215,7 +246,6 @@ __device__ __forceinline__ SeqRange sequence_of(const PrefillArgs &a, int n) {
 __global__ __launch_bounds__(NT) void piece_state_kernel(PrefillArgs a, int npieces,
                                                          long long piece_len, float *ws) {
     __shared__ __attribute__((aligned(16))) __bf16 Ks[C * QP];
-    __shared__ __attribute__((aligned(16))) __bf16 Vs[C * QP];
     __shared__ __attribute__((aligned(16))) __bf16 Vds[C * QP];
 
     const int j = blockIdx.x % npieces;
@@ -244,18 +274,28 @@ __global__ __launch_bounds__(NT) void piece_state_kernel(PrefillArgs a, int npie
 #pragma unroll
         for (int v = 0; v < 16; ++v) S[db][v] = 0.f;
 
-    Stage<false> stage;
-    const long long nch = piece_len / C;
+    Stage<false> st0, st1;
+    const long long nch = piece_len / C;  // >= 2, all full sub-blocks
     const float bd = fast_exp2(-s2 * (float)C);
-    stage.load(nullptr, kg, vg, ts, C, tid);
-    for (long long c = 0; c < nch; ++c) {
+    auto prefetch = [&](Stage<false> &st, long long c) {
+        const long long off = (c < nch ? c : nch - 1) * C * (long long)ts;
+        st.load(nullptr, kg + off, vg + off, ts, C, tid);
+    };
+    auto step = [&](long long c, Stage<false> &st) {
         __syncthreads();
-        stage.store(nullptr, Ks, Vs, Vds, C, s2, tid);
-        const long long cn = (c + 1 < nch) ? c + 1 : c;
-        stage.load(nullptr, kg + cn * C * (long long)ts, vg + cn * C * (long long)ts, ts, C, tid);
+        st.store(nullptr, Ks, nullptr, Vds, C, s2, tid);
+        prefetch(st, c + 2);
         __syncthreads();
         state_update(S, Ks, Vds, bd, qh, cq, lane);
+    };
+    prefetch(st0, 0);
+    prefetch(st1, 1);
+    long long c = 0;
+    for (; c + 1 < nch; c += 2) {
+        step(c, st0);
+        step(c + 1, st1);
     }
+    if (c < nch) step(c, st0);
 
     float *dst = wsu + (size_t)(1 + j) * D * D;
 #pragma unroll
@@ -338,33 +378,37 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, int segments, l
         dscore[v] = diff >= 0 ? fast_exp2(-s2 * (float)diff) : 0.f;
     }
 
-    Stage<true> stage;
+    // Two register stages: sub-block c is staged in st[c % 2] and its loads are
+    // issued two sub-blocks ahead, so about 96 KiB of loads are in flight per CU.
+    Stage<true> st0, st1;
     const long long nfull = len / C;
     const int tail = (int)(len - nfull * C);
     const long long nchunks = nfull + (tail > 0);
     auto chunk_len = [&](long long c) { return c < nfull ? C : tail; };
-    if (nchunks > 0) stage.load(qg, kg, vg, ts, chunk_len(0), tid);
+    auto prefetch = [&](Stage<true> &st, long long c) {
+        // past the end, re-read the last sub-block (ignored) to keep the count fixed
+        const long long cn = c < nchunks ? c : nchunks - 1;
+        const long long off = cn * C * (long long)ts;
+        st.load(qg + off, kg + off, vg + off, ts, chunk_len(cn), tid);
+    };
+    if (nchunks > 0) {
+        prefetch(st0, 0);
+        prefetch(st1, 1);
+    }
 
     int cur = 0;
-    f32x16 o;
-    OutT *orow = og;
-    auto flush = [&]() {
-#pragma unroll
-        for (int gv = 0; gv < 4; ++gv) store_out4(orow + 32 * cq + 8 * gv + 4 * hf, o, gv);
-    };
-
-    auto step = [&](long long c, int m, bool have_prev, auto full) {
+    // Per sub-block: (B) tiles visible -> scores, inter-block product, state
+    // update -> (C) P visible -> intra-block product, output block to LDS ->
+    // (D) output tile visible and every read of this sub-block's tiles done ->
+    // full-row output stores. Barrier D of one sub-block also guards the tile
+    // writes of the next. The output tile reuses the S^T buffer that the
+    // inter-block product just finished reading (it is rewritten only after the
+    // next barrier B).
+    auto step = [&](long long c, int m, auto full, Stage<true> &st) {
         constexpr bool FULL = decltype(full)::value;
-        __syncthreads();  // (A) readers of the previous tiles are done
-        stage.store(Qs, Ks, Vs, Vds, m, s2, tid);
-        if (have_prev) flush();
-        if (FULL) {
-            const long long cn = (c + 1 < nchunks) ? c + 1 : c;
-            const long long off = cn * C * (long long)ts;
-            stage.load(qg + off, kg + off, vg + off, ts, chunk_len(cn), tid);
-        }
+        st.store(Qs, Ks, Vs, Vds, m, s2, tid);
+        if (FULL) prefetch(st, c + 2);
         __syncthreads();  // (B) tiles and S^T of the previous sub-block are visible
-
         if (scorer) {
             // scores^T block: keys 32kb.., queries 32qb.. ; masked, decayed, to LDS as P
             f32x16 sc;
@@ -383,6 +427,7 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, int segments, l
         }
 
         // inter-block part: O^T = S^T (Q ⊙ d_q)^T
+        f32x16 o;
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[v] = 0.f;
 #pragma unroll
@@ -401,16 +446,24 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, int segments, l
             if (ks >= 2 * (qh + 1)) break;
             o = mma(ld_op_t(Vs, QP, 32 * cq, 16 * ks, lane), ld_op(Ps, PP, 32 * qh, 16 * ks, lane), o);
         }
-        orow = og + (c * C + qpos) * (long long)ts;
-        if (!FULL && qpos < m) flush();
+        float *Os = reinterpret_cast<float *>(Sts[cur]);
+        stage_out(Os, o, qh, cq, lane);
+        __syncthreads();  // (D)
+        store_rows<FULL>(og + c * C * (long long)ts, ts, Os, m, tid);
         cur ^= 1;
     };
-    if (nfull > 0) step(0, C, false, std::true_type{});
-    for (long long c = 1; c < nfull; ++c) step(c, C, true, std::true_type{});
-    if (tail > 0)
-        step(nfull, tail, nfull > 0, std::false_type{});
-    else if (nfull > 0)
-        flush();
+    long long c = 0;
+    for (; c + 1 < nfull; c += 2) {
+        step(c, C, std::true_type{}, st0);
+        step(c + 1, C, std::true_type{}, st1);
+    }
+    if (c < nfull) step(c, C, std::true_type{}, st0);
+    if (tail > 0) {  // sub-block nfull is staged in st[nfull % 2]
+        if (nfull & 1)
+            step(nfull, tail, std::false_type{}, st1);
+        else
+            step(nfull, tail, std::false_type{}, st0);
+    }
 
     if (a.state_out && g == segments - 1) {
         const long long sb = (long long)uh * D * D;
