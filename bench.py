@@ -19,6 +19,12 @@ Prints ONE JSON line. Besides the driver's fields it carries:
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps N]
                        [--no-cpu] [--no-decode]
+       python bench.py --workload long_1m|varlen|tiny_f32   (one extra workload)
+       python bench.py --copy-calibration BYTES            (plain device copy, for
+                                                            rocprofv3 counter scaling)
+       python bench.py --traffic-from COPY_DIR FETCH_DIR WRITE_DIR
+                       (turn three rocprofv3 --pmc CSV runs into the per-launch
+                        HBM traffic summary under profiles/)
 """
 
 from __future__ import annotations
@@ -37,7 +43,7 @@ METRIC = "Lightning prefill tokens/s (H=64,d=128) + decode state GB/s, % of roof
 HBM_PEAK_GBS = 8000.0
 D = 128
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_m1_layer_L32768_traffic.json")
-PREFILL_SRC = os.path.join(ROOT, "linear_attention_amd", "csrc", "prefill.hip")
+PREFILL_SRC = os.path.join(ROOT, "linear_attention_amd", "csrc", "prefill_heads.hip")
 
 
 def log(msg):
@@ -117,7 +123,7 @@ def run_prefill(la, torch, steps, warmup):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "bytes_per_launch": bytes_alg,
-                     "kernel": "prefill_kernel<bf16, f32>"},
+                     "kernel": "lt_prefill call: piece_state_kernel + head_kernel<f32 out>"},
     }
 
 
@@ -173,6 +179,129 @@ def run_decode(la, torch, nsteps, warmup=5):
     }
 
 
+def run_other(la, torch, name, steps, warmup):
+    """Times one of the other workloads (prefill) and returns its JSON line."""
+    import numpy as np
+
+    import workloads
+
+    w = {"long_1m": workloads.LONG_1M, "varlen": workloads.VARLEN,
+         "tiny_f32": workloads.TINY_F32}[name]
+    H = w.heads
+    slopes = torch.from_numpy(workloads.slopes(H)).cuda()
+    stream = torch.cuda.current_stream()
+    if name == "varlen":
+        lens = workloads.varlen_lengths(w.seed, w.batch, w.extra["min_len"], w.extra["max_len"])
+        cu_h = workloads.cu_seqlens(lens)
+        T = int(cu_h[-1])
+        q, k, v = workloads.qkv_device(w.seed, (T, H, D), "bf16")
+        cu = torch.from_numpy(cu_h).cuda()
+        s0 = workloads.state_device(w.seed + 1, (len(lens), H, D, D), std=0.1)
+        o = torch.empty((T, H, D), device="cuda", dtype=torch.float32)
+        st = torch.empty_like(s0)
+        call = lambda: la.lt_prefill_varlen(q, k, v, cu, slopes, w.block, s0, o=o, state_out=st,
+                                            stream=stream)
+        tokens, nbytes = T, prefill_bytes(T, H, states_out=len(lens), states_in=len(lens))
+        cfg = {"num_seqs": len(lens), "total_tokens": T, "min_len": int(lens.min()),
+               "max_len": int(lens.max())}
+    else:
+        dt = "f32" if name == "tiny_f32" else "bf16"
+        shape = (w.batch, w.seqlen, H, D)
+        if dt == "f32":
+            q, k, v = (torch.from_numpy(x).cuda() for x in workloads.qkv_host(w.seed, shape, "f32"))
+        else:
+            q, k, v = workloads.qkv_device(w.seed, shape, "bf16")
+        o = torch.empty(shape, device="cuda", dtype=torch.float32)
+        st = torch.empty((w.batch, H, D, D), device="cuda", dtype=torch.float32)
+        ws_bytes = la.lt_prefill_workspace_bytes(w.batch, w.seqlen, H, D,
+                                                 la.LT_F32 if dt == "f32" else la.LT_BF16)
+        ws = torch.empty(max(ws_bytes, 1), device="cuda", dtype=torch.uint8)
+        call = lambda: la.lt_prefill(q, k, v, slopes, w.block, o=o, state_out=st, workspace=ws,
+                                     stream=stream)
+        tokens = w.batch * w.seqlen
+        nbytes = prefill_bytes(tokens, H, in_bytes=4 if dt == "f32" else 2)
+        cfg = {"batch": w.batch, "seq_len": w.seqlen}
+    for _ in range(warmup):
+        call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    gbs = nbytes / (ms / 1e3) / 1e9
+    return {"metric": METRIC, "value": round(tokens * steps / wall, 1), "unit": "tokens/s",
+            "n_gpus": 1, "steps": steps, "warmup": warmup,
+            "ms_per_step": round(wall * 1e3 / steps, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32" if name == "tiny_f32" else "bf16",
+            "data": "synthetic",
+            "config": dict({"workload": w.name, "heads": H, "head_dim": D, "block": w.block}, **cfg),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "bytes_per_launch": nbytes, "kernel": "lt_prefill call"},
+            "kernel_ms_mean": round(ms, 5)}
+
+
+def copy_calibration(torch, nbytes):
+    """A plain copy kernel of nbytes (reads nbytes, writes nbytes): torch's
+    elementwise kernel for dst = src * 1 (a same-dtype copy_ could go to the
+    DMA engine, which the shader counters do not see)."""
+    src = torch.ones(nbytes // 4, device="cuda", dtype=torch.float32)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes}))
+
+
+def traffic_from(copy_dir, fetch_dir, write_dir, copy_bytes):
+    """Per-launch HBM traffic of lt_prefill on the M1 layer from rocprofv3 runs.
+
+    copy_dir holds FETCH_SIZE and WRITE_SIZE of the calibration copy (two runs'
+    CSVs may be concatenated there as copy_fetch.csv / copy_write.csv); fetch_dir
+    and write_dir hold FETCH_SIZE and WRITE_SIZE of a bench run. Each counter is
+    scaled by (bytes the copy moved) / (what the counter read for the copy).
+    """
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter:
+                    vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    cf = per_kernel(os.path.join(copy_dir, "fetch"), "FETCH_SIZE")
+    cw = per_kernel(os.path.join(copy_dir, "write"), "WRITE_SIZE")
+    ck = [k for k in cf if "copy" in k.lower() or "elementwise" in k.lower()]
+    copy_fetch_kib = max(max(cf[k]) for k in ck)
+    copy_write_kib = max(max(cw[k]) for k in cw if k in ck)
+    f_scale = copy_bytes / (copy_fetch_kib * 1024)
+    w_scale = copy_bytes / (copy_write_kib * 1024)
+    kf = per_kernel(fetch_dir, "FETCH_SIZE")
+    kw = per_kernel(write_dir, "WRITE_SIZE")
+    kernels = [k for k in kf if "prefill" in k or "head_kernel" in k or "piece_state" in k]
+    import numpy as np
+
+    fetch = sum(float(np.median(kf[k])) for k in kernels) * 1024 * f_scale
+    write = sum(float(np.median(kw[k])) for k in kernels) * 1024 * w_scale
+    out = {"kernel_source_sha256": source_sha(PREFILL_SRC),
+           "kernels": kernels, "fetch_scale": f_scale, "write_scale": w_scale,
+           "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
+           "traffic_bytes_per_launch": round(fetch + write),
+           "algorithmic_bytes_per_launch": prefill_bytes(32768, 64)}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 def run_cpu_baseline(w, dev_inputs, tokens):
     """The fp64 oracle (as it stands) on the host cores, on the first `tokens`
     tokens of the same prefill inputs, all heads."""
@@ -201,7 +330,15 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=32768)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--workload", default="m1_layer",
+                    choices=["m1_layer", "long_1m", "varlen", "tiny_f32"])
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--traffic-from", nargs=3, metavar=("COPY_DIR", "FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from, args.copy_bytes)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -216,6 +353,14 @@ def main():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(1)
     import linear_attention_amd as la
+
+    if args.copy_calibration:
+        copy_calibration(torch, args.copy_calibration)
+        return
+    if args.workload != "m1_layer":
+        log(f"[bench] {args.workload}")
+        print(json.dumps(run_other(la, torch, args.workload, args.steps, args.warmup)), flush=True)
+        return
 
     log("[bench] prefill m1_layer L=32768 H=64 d=128 block=256")
     w, dev_inputs, pre = run_prefill(la, torch, args.steps, args.warmup)
