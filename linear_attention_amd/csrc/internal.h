@@ -45,11 +45,14 @@ constexpr int kValueSlices = 4;
 // `sub` equal pieces of every segment but the last computes the state each
 // piece contributes; segment g then starts from the decayed sum of everything
 // before it. All lengths are multiples of the 64-token sub-block.
+// With value_slices == 4 the head is instead split into four 32-column value
+// slices (one workgroup each, no segments, no workspace).
 struct PrefillPlan {
     int segments;
     int sub;
     long long seg_len;
     size_t workspace;  // bytes: per (unit, head), (1 + (segments-1)*sub) fp32 d x d states
+    int value_slices;  // 1 = whole head per workgroup, 4 = value-slice workgroups
 };
 
 PrefillPlan plan_prefill(long long units, long long seqlen, int heads, lt_dtype in_dtype,
@@ -58,7 +61,8 @@ PrefillPlan plan_prefill(long long units, long long seqlen, int heads, lt_dtype 
 // fp32 inputs: one workgroup per (unit, head, 32-column value slice).
 hipError_t launch_prefill_slices(const PrefillArgs &a, lt_dtype in_dtype, lt_dtype out_dtype,
                                  hipStream_t stream);
-// bf16 inputs: one 8-wave workgroup per (unit, head, segment).
+// bf16 inputs: one 8-wave workgroup per (unit, head, segment) or per
+// (unit, head, value slice).
 hipError_t launch_prefill_heads(const PrefillArgs &a, const PrefillPlan &plan, void *workspace,
                                 lt_dtype out_dtype, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, lt_dtype in_dtype, lt_dtype out_dtype,

@@ -51,8 +51,7 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 constexpr int D = kHeadDim;  // 128
 constexpr int C = 64;        // tokens per sub-block
 constexpr int NT = 512;      // 8 waves
-constexpr int QP = D + 8;    // LDS row pitch (elements) of the 128-wide tiles
-constexpr int PP = C + 8;    // LDS row pitch of the P tile
+constexpr int PW = C;        // width of the P tile
 constexpr float LOG2E = 1.4426950408889634f;
 
 static_assert(D == 128 && C == 64, "tile shapes are fixed below");
@@ -63,22 +62,48 @@ __device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// MFMA operand (32x32x16, bf16) from a row-major LDS tile whose rows are the
-// operand rows: lane l reads row row0 + (l % 32), contraction slots
-// k0 + 8*(l / 32) .. +7.
-__device__ __forceinline__ bf16x8 ld_op(const __bf16 *t, int pitch, int row0, int k0, int lane) {
-    return *reinterpret_cast<const bf16x8 *>(t + (row0 + (lane & 31)) * pitch + k0 + 8 * (lane >> 5));
+// LDS tile layouts. Tiles are row-major without padding; bank conflicts are
+// avoided by permuting the 16-byte chunks of each row. For a 128-wide bf16 tile
+// (16 chunks per 256-byte row) chunk c of row r is stored at c ^ swz(r) with
+// swz(r) = ((r & 3) << 2) | ((r >> 2) & 3), a bijection on the 16 rows of any
+// aligned 16-row group (16-byte operand reads of 16 consecutive rows hit 64
+// distinct banks) that also sends the chunk pairs read by one transposing read
+// (4 consecutive rows x 2 adjacent chunks) to 4 disjoint pairs (8-byte reads of
+// a 32-lane half-wave hit 64 distinct banks).
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+struct L128 {  // [rows][128] bf16
+    __device__ static int off(int row, int col) {
+        return row * 128 + ((((col >> 3) ^ swz(row)) << 3) | (col & 7));
+    }
+};
+struct LP {  // P tile [64][64] bf16: 8 chunks per 128-byte row, two rows per bank line
+    __device__ static int off(int row, int col) {
+        return row * PW + ((((col >> 3) ^ ((row >> 1) & 7)) << 3) | (col & 7));
+    }
+};
+template <int PITCH>
+struct LPad {  // narrow tiles: plain padded rows
+    __device__ static int off(int row, int col) { return row * PITCH + col; }
+};
+
+// MFMA operand (32x32x16, bf16) from an LDS tile whose rows are the operand
+// rows: lane l reads row row0 + (l % 32), contraction slots k0 + 8*(l / 32)..+7.
+template <class L>
+__device__ __forceinline__ bf16x8 ld_op(const __bf16 *t, int row0, int k0, int lane) {
+    return *reinterpret_cast<const bf16x8 *>(t + L::off(row0 + (lane & 31), k0 + 8 * (lane >> 5)));
 }
 
-// MFMA operand whose rows are the COLUMNS of a row-major LDS tile and whose
-// contraction runs down the tile rows: lane l gets tile[k0 + 8*(l/32) + e]
-// [c0 + (l % 32)], e = 0..7. ds_read_b64_tr_b16 lets each 16-lane group load a
-// 4x16 block (lanes 4r..4r+3 give row r) and hands lane i column i.
-__device__ __forceinline__ bf16x8 ld_op_t(const __bf16 *t, int pitch, int c0, int k0, int lane) {
+// MFMA operand whose rows are the COLUMNS of an LDS tile and whose contraction
+// runs down the tile rows: lane l gets tile[k0 + 8*(l/32) + e][c0 + (l % 32)],
+// e = 0..7. ds_read_b64_tr_b16 lets each 16-lane group load a 4x16 block (lanes
+// 4r..4r+3 give row r) and hands lane i column i.
+template <class L>
+__device__ __forceinline__ bf16x8 ld_op_t(const __bf16 *t, int c0, int k0, int lane) {
     const int li = lane & 15, grp = lane >> 4;
-    const __bf16 *p = t + (k0 + 8 * (grp >> 1) + (li >> 2)) * pitch + c0 + 16 * (grp & 1) + 4 * (li & 3);
-    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p);
-    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p + 4 * pitch));
+    const int row = k0 + 8 * (grp >> 1) + (li >> 2), col = c0 + 16 * (grp & 1) + 4 * (li & 3);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(t + L::off(row, col)));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(t + L::off(row + 4, col)));
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
@@ -133,7 +158,7 @@ struct Stage {
         for (int i = 0; i < 2; ++i) {
             const int t = (tid >> 4) + 32 * i;
             const bool in = t < m;
-            const int off = t * QP + 8 * seg;
+            const int off = L128::off(t, 8 * seg);
             if (WITH_Q) *reinterpret_cast<uint4 *>(Qs + off) = keep_if(in, q[i]);
             *reinterpret_cast<uint4 *>(Ks + off) = keep_if(in, k[i]);
             const uint4 vv = keep_if(in, v[i]);
@@ -158,10 +183,10 @@ __device__ __forceinline__ void state_update(f32x16 (&S)[2], const __bf16 *Ks, c
     for (int db = 0; db < 2; ++db) S[db] *= bd;
 #pragma unroll
     for (int ks = 0; ks < C / 16; ++ks) {
-        const bf16x8 b = ld_op_t(Vds, QP, 32 * cq, 16 * ks, lane);
+        const bf16x8 b = ld_op_t<L128>(Vds, 32 * cq, 16 * ks, lane);
 #pragma unroll
         for (int db = 0; db < 2; ++db)
-            S[db] = mma(ld_op_t(Ks, QP, 64 * qh + 32 * db, 16 * ks, lane), b, S[db]);
+            S[db] = mma(ld_op_t<L128>(Ks, 64 * qh + 32 * db, 16 * ks, lane), b, S[db]);
     }
 }
 
@@ -176,23 +201,28 @@ __device__ __forceinline__ void write_state_t(__bf16 *Sts, const f32x16 (&S)[2],
             bf16x4 x;
 #pragma unroll
             for (int r = 0; r < 4; ++r) x[r] = static_cast<__bf16>(S[db][4 * gv + r]);
-            *reinterpret_cast<bf16x4 *>(Sts + (32 * cq + r32) * QP + 64 * qh + 32 * db + 8 * gv + 4 * h) = x;
+            *reinterpret_cast<bf16x4 *>(Sts + L128::off(32 * cq + r32, 64 * qh + 32 * db + 8 * gv + 4 * h)) = x;
         }
 }
 
 // Output tile staging. Each wave writes its 32x32 fp32 output block into an
-// LDS tile Os[64][OSP]; the workgroup then stores whole output rows (512 B in
+// LDS tile Os[64][128]; the workgroup then stores whole output rows (512 B in
 // fp32) with consecutive lanes on consecutive addresses. Stored straight from
 // the MFMA accumulator layout, a row would arrive in 32-byte pieces from four
 // instructions, which measured at under 60% of the HBM throughput of full-row
 // stores for this access pattern.
-constexpr int OSP = D + 4;  // fp32 row pitch of the staged output tile
+// Staged output tile: fp32 [64][128], 4-float chunks of row r permuted by
+// r & 15 (writes of 16 rows of one chunk and reads of one whole row are both
+// conflict-free).
+__device__ __forceinline__ int ooff(int row, int col) {
+    return row * D + ((((col >> 2) ^ (row & 15)) << 2) | (col & 3));
+}
 
 __device__ __forceinline__ void stage_out(float *Os, const f32x16 &o, int qh, int cq, int lane) {
     const int r32 = lane & 31, hf = lane >> 5;
 #pragma unroll
     for (int gv = 0; gv < 4; ++gv)
-        *reinterpret_cast<float4 *>(Os + (32 * qh + r32) * OSP + 32 * cq + 8 * gv + 4 * hf) =
+        *reinterpret_cast<float4 *>(Os + ooff(32 * qh + r32, 32 * cq + 8 * gv + 4 * hf)) =
             make_float4(o[4 * gv], o[4 * gv + 1], o[4 * gv + 2], o[4 * gv + 3]);
 }
 
@@ -202,7 +232,7 @@ __device__ __forceinline__ void store_rows(float *out, long long ts, const float
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int row = (tid >> 5) + 16 * j, col = 4 * (tid & 31);
-        const float4 x = *reinterpret_cast<const float4 *>(Os + row * OSP + col);
+        const float4 x = *reinterpret_cast<const float4 *>(Os + ooff(row, col));
         if (FULL || row < m) *reinterpret_cast<float4 *>(out + row * ts + col) = x;
     }
 }
@@ -211,8 +241,8 @@ __device__ __forceinline__ void store_rows(__bf16 *out, long long ts, const floa
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int row = (tid >> 4) + 32 * j, col = 8 * (tid & 15);
-        const float4 x0 = *reinterpret_cast<const float4 *>(Os + row * OSP + col);
-        const float4 x1 = *reinterpret_cast<const float4 *>(Os + row * OSP + col + 4);
+        const float4 x0 = *reinterpret_cast<const float4 *>(Os + ooff(row, col));
+        const float4 x1 = *reinterpret_cast<const float4 *>(Os + ooff(row, col + 4));
         const bf16x8 y = {static_cast<__bf16>(x0.x), static_cast<__bf16>(x0.y), static_cast<__bf16>(x0.z),
                           static_cast<__bf16>(x0.w), static_cast<__bf16>(x1.x), static_cast<__bf16>(x1.y),
                           static_cast<__bf16>(x1.z), static_cast<__bf16>(x1.w)};
@@ -245,8 +275,8 @@ __device__ __forceinline__ SeqRange sequence_of(const PrefillArgs &a, int n) {
 // Workspace per (unit, head): [S_0][S_piece 0 .. npieces-1], fp32 d x d each.
 __global__ __launch_bounds__(NT) void piece_state_kernel(PrefillArgs a, int npieces,
                                                          long long piece_len, float *ws) {
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[C * QP];
-    __shared__ __attribute__((aligned(16))) __bf16 Vds[C * QP];
+    __shared__ __attribute__((aligned(16))) __bf16 Ks[C * D];
+    __shared__ __attribute__((aligned(16))) __bf16 Vds[C * D];
 
     const int j = blockIdx.x % npieces;
     const int uh = blockIdx.x / npieces;
@@ -309,12 +339,12 @@ __global__ __launch_bounds__(NT) void piece_state_kernel(PrefillArgs a, int npie
 template <typename OutT>
 __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, int segments, long long seg_len,
                                                   int sub, const float *ws) {
-    __shared__ __attribute__((aligned(16))) __bf16 Qs[C * QP];
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[C * QP];
-    __shared__ __attribute__((aligned(16))) __bf16 Vs[C * QP];
-    __shared__ __attribute__((aligned(16))) __bf16 Vds[C * QP];
-    __shared__ __attribute__((aligned(16))) __bf16 Sts[2][D * QP];
-    __shared__ __attribute__((aligned(16))) __bf16 Ps[C * PP];
+    __shared__ __attribute__((aligned(16))) __bf16 Qs[C * D];
+    __shared__ __attribute__((aligned(16))) __bf16 Ks[C * D];
+    __shared__ __attribute__((aligned(16))) __bf16 Vs[C * D];
+    __shared__ __attribute__((aligned(16))) __bf16 Vds[C * D];
+    __shared__ __attribute__((aligned(16))) __bf16 Sts[2][D * D];
+    __shared__ __attribute__((aligned(16))) __bf16 Ps[C * PW];
 
     const int g = blockIdx.x % segments;
     const int uh = blockIdx.x / segments;
@@ -416,13 +446,13 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, int segments, l
             for (int v = 0; v < 16; ++v) sc[v] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks)
-                sc = mma(ld_op(Ks, QP, 32 * kb, 16 * ks, lane), ld_op(Qs, QP, 32 * qb, 16 * ks, lane), sc);
+                sc = mma(ld_op<L128>(Ks, 32 * kb, 16 * ks, lane), ld_op<L128>(Qs, 32 * qb, 16 * ks, lane), sc);
 #pragma unroll
             for (int gv = 0; gv < 4; ++gv) {
                 bf16x4 p;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) p[r] = static_cast<__bf16>(sc[4 * gv + r] * dscore[4 * gv + r]);
-                *reinterpret_cast<bf16x4 *>(Ps + (32 * qb + r32) * PP + 32 * kb + 8 * gv + 4 * hf) = p;
+                *reinterpret_cast<bf16x4 *>(Ps + LP::off(32 * qb + r32, 32 * kb + 8 * gv + 4 * hf)) = p;
             }
         }
 
@@ -432,7 +462,7 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, int segments, l
         for (int v = 0; v < 16; ++v) o[v] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks)
-            o = mma(ld_op(Sts[cur], QP, 32 * cq, 16 * ks, lane), ld_op(Qs, QP, 32 * qh, 16 * ks, lane), o);
+            o = mma(ld_op<L128>(Sts[cur], 32 * cq, 16 * ks, lane), ld_op<L128>(Qs, 32 * qh, 16 * ks, lane), o);
         o *= dq;
 
         // state: S = e^{-s m} S + K^T (V ⊙ d_k), then S^T (bf16) for the next sub-block
@@ -444,7 +474,7 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, int segments, l
 #pragma unroll
         for (int ks = 0; ks < C / 16; ++ks) {
             if (ks >= 2 * (qh + 1)) break;
-            o = mma(ld_op_t(Vs, QP, 32 * cq, 16 * ks, lane), ld_op(Ps, PP, 32 * qh, 16 * ks, lane), o);
+            o = mma(ld_op_t<L128>(Vs, 32 * cq, 16 * ks, lane), ld_op<LP>(Ps, 32 * qh, 16 * ks, lane), o);
         }
         float *Os = reinterpret_cast<float *>(Sts[cur]);
         stage_out(Os, o, qh, cq, lane);
@@ -474,9 +504,238 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, int segments, l
     }
 }
 
+// ---------------------------------------------------------------------------
+// Value-slice variant, for launches with too few (sequence, head) pairs to fill
+// the GPU with whole heads (batch-1 prefill: 64 pairs for 256 CUs). Output
+// columns J depend only on V[:, J] and S[:, J], so a head's 128 value columns
+// split into 4 independent 32-column workgroups with no pre-pass and no extra
+// HBM traffic: the four workgroups of a head read the same q and k tiles, and
+// the launch places them on one XCD so the repeats hit that XCD's L2.
+// Per 64-token sub-block the 8 waves split: waves 0..2 one causal 32x32 score
+// block each; waves 3, 4 the two 32x32 output blocks (inter then intra part);
+// waves 5, 6, 7 and 0 one 32x32 state block each (keys 32*db.., 32 columns).
+constexpr int NSL = 4;          // value slices per head
+constexpr int SW = D / NSL;     // 32 value columns per workgroup
+constexpr int VP = SW + 8;      // LDS pitch (elements) of the V slice tiles
+constexpr int OSS = SW + 4;     // fp32 pitch of the staged output slice
+
+// Register staging for a slice workgroup: q, k as in Stage (tokens (t/16) + 32i,
+// elements 8(t%16)..), v slice 8 bytes per thread (token t/8, columns 4(t%8)..).
+struct SliceStage {
+    uint4 q[2], k[2];
+    uint2 v;
+
+    __device__ void load(const uint16_t *qg, const uint16_t *kg, const uint16_t *vg, int ts, int m,
+                         int tid) {
+        const int seg = tid & 15;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int t = (tid >> 4) + 32 * i;
+            const int row = (t < m ? t : m - 1) * ts + 8 * seg;
+            q[i] = *reinterpret_cast<const uint4 *>(qg + row);
+            k[i] = *reinterpret_cast<const uint4 *>(kg + row);
+        }
+        const int vt = tid >> 3;
+        v = *reinterpret_cast<const uint2 *>(vg + (vt < m ? vt : m - 1) * ts + 4 * (tid & 7));
+    }
+
+    __device__ void store(__bf16 *Qs, __bf16 *Ks, __bf16 *Vs, __bf16 *Vds, int m, float s2, int tid) {
+        const int seg = tid & 15;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int t = (tid >> 4) + 32 * i;
+            const bool in = t < m;
+            *reinterpret_cast<uint4 *>(Qs + L128::off(t, 8 * seg)) = keep_if(in, q[i]);
+            *reinterpret_cast<uint4 *>(Ks + L128::off(t, 8 * seg)) = keep_if(in, k[i]);
+        }
+        const int vt = tid >> 3;
+        const bool in = vt < m;
+        const uint2 vv = make_uint2(in ? v.x : 0u, in ? v.y : 0u);
+        *reinterpret_cast<uint2 *>(Vs + vt * VP + 4 * (tid & 7)) = vv;
+        const float dk = in ? fast_exp2(-s2 * (float)(m - 1 - vt)) : 0.f;
+        const uint4 sc = scale_bf16x8(make_uint4(vv.x, vv.y, 0u, 0u), dk);
+        *reinterpret_cast<uint2 *>(Vds + vt * VP + 4 * (tid & 7)) = make_uint2(sc.x, sc.y);
+    }
+};
+
+template <bool FULL>
+__device__ __forceinline__ void store_slice_rows(float *out, long long ts, const float *Os, int m,
+                                                 int tid) {
+    const int row = tid >> 3, col = 4 * (tid & 7);
+    const float4 x = *reinterpret_cast<const float4 *>(Os + row * OSS + col);
+    if (FULL || row < m) *reinterpret_cast<float4 *>(out + row * ts + col) = x;
+}
+template <bool FULL>
+__device__ __forceinline__ void store_slice_rows(__bf16 *out, long long ts, const float *Os, int m,
+                                                 int tid) {
+    const int row = tid >> 3, col = 4 * (tid & 7);
+    const float4 x = *reinterpret_cast<const float4 *>(Os + row * OSS + col);
+    const bf16x4 y = {static_cast<__bf16>(x.x), static_cast<__bf16>(x.y), static_cast<__bf16>(x.z),
+                      static_cast<__bf16>(x.w)};
+    if (FULL || row < m) *reinterpret_cast<bf16x4 *>(out + row * ts + col) = y;
+}
+
+template <typename OutT>
+__global__ __launch_bounds__(NT) void slice_kernel(PrefillArgs a) {
+    __shared__ __attribute__((aligned(16))) __bf16 Qs[C * D];
+    __shared__ __attribute__((aligned(16))) __bf16 Ks[C * D];
+    __shared__ __attribute__((aligned(16))) __bf16 Vs[C * VP];
+    __shared__ __attribute__((aligned(16))) __bf16 Vds[C * VP];
+    __shared__ __attribute__((aligned(16))) __bf16 Sts[2][SW * D];
+    __shared__ __attribute__((aligned(16))) __bf16 Ps[C * PW];
+    __shared__ __attribute__((aligned(16))) float Os[C * OSS];
+
+    // XCD-aware mapping: workgroups are dealt round-robin over the 8 XCDs, so
+    // v = (bid % 8) * (nwg / 8) + bid / 8 gives each XCD a contiguous run of v,
+    // and the 4 slices of a head share one XCD.
+    const int nwg = gridDim.x, bid = blockIdx.x;
+    const int vid = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
+    const int slice = vid % NSL, uh = vid / NSL;
+    const int h = uh % a.heads, n = uh / a.heads;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r32 = lane & 31, hf = lane >> 5;
+
+    const SeqRange sr = sequence_of(a, n);
+    const long long len = sr.len;
+    const int ts = a.heads * D;
+    const long long base = (sr.start * a.heads + h) * (long long)D;
+    const uint16_t *qg = static_cast<const uint16_t *>(a.q) + base;
+    const uint16_t *kg = static_cast<const uint16_t *>(a.k) + base;
+    const uint16_t *vg = static_cast<const uint16_t *>(a.v) + base + slice * SW;
+    OutT *og = static_cast<OutT *>(a.o) + base + slice * SW;
+    const float s2 = a.slopes[h] * LOG2E;
+
+    // roles
+    const bool scorer = w < 3;
+    const int qb = w == 0 ? 0 : 1, kb = w == 2 ? 1 : 0;
+    const bool outw = (w == 3 || w == 4);
+    const int qh = w - 3;                       // output block of waves 3, 4
+    const bool stw = (w == 0 || w >= 5);        // state block owners
+    const int db = w == 0 ? 3 : w - 5;          // their key block
+
+    // state block S[32db + 8(v/4) + 4hf + v%4][slice*32 + r32]
+    f32x16 S;
+    const long long sb = (long long)uh * D * D + slice * SW;
+    auto sidx = [&](int v) { return (32 * db + 8 * (v >> 2) + 4 * hf + (v & 3)) * D + r32; };
+#pragma unroll
+    for (int v = 0; v < 16; ++v) S[v] = (stw && a.state_in) ? a.state_in[sb + sidx(v)] : 0.f;
+    auto write_st = [&](__bf16 *dst) {
+#pragma unroll
+        for (int gv = 0; gv < 4; ++gv) {
+            bf16x4 x;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[r] = static_cast<__bf16>(S[4 * gv + r]);
+            *reinterpret_cast<bf16x4 *>(dst + L128::off(r32, 32 * db + 8 * gv + 4 * hf)) = x;
+        }
+    };
+    if (stw) write_st(Sts[0]);
+
+    const int qpos = 32 * qh + r32;
+    const float dq = fast_exp2(-s2 * (float)(qpos + 1));
+    float dscore[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int diff = (32 * qb + r32) - (32 * kb + 8 * (v >> 2) + 4 * hf + (v & 3));
+        dscore[v] = diff >= 0 ? fast_exp2(-s2 * (float)diff) : 0.f;
+    }
+
+    SliceStage st0, st1;
+    const long long nfull = len / C;
+    const int tail = (int)(len - nfull * C);
+    const long long nchunks = nfull + (tail > 0);
+    auto chunk_len = [&](long long c) { return c < nfull ? C : tail; };
+    auto prefetch = [&](SliceStage &st, long long c) {
+        const long long cn = c < nchunks ? c : nchunks - 1;
+        const long long off = cn * C * (long long)ts;
+        st.load(qg + off, kg + off, vg + off, ts, chunk_len(cn), tid);
+    };
+    if (nchunks > 0) {
+        prefetch(st0, 0);
+        prefetch(st1, 1);
+    }
+
+    int cur = 0;
+    auto step = [&](long long c, int m, auto full, SliceStage &st) {
+        constexpr bool FULL = decltype(full)::value;
+        st.store(Qs, Ks, Vs, Vds, m, s2, tid);
+        if (FULL) prefetch(st, c + 2);
+        __syncthreads();  // (B) tiles and S^T of the previous sub-block are visible
+
+        f32x16 o;
+        if (scorer) {
+            f32x16 sc;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) sc[v] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks)
+                sc = mma(ld_op<L128>(Ks, 32 * kb, 16 * ks, lane), ld_op<L128>(Qs, 32 * qb, 16 * ks, lane), sc);
+#pragma unroll
+            for (int gv = 0; gv < 4; ++gv) {
+                bf16x4 p;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) p[r] = static_cast<__bf16>(sc[4 * gv + r] * dscore[4 * gv + r]);
+                *reinterpret_cast<bf16x4 *>(Ps + LP::off(32 * qb + r32, 32 * kb + 8 * gv + 4 * hf)) = p;
+            }
+        }
+        if (outw) {  // inter-block part O^T = S^T (Q ⊙ d_q)^T
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[v] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks)
+                o = mma(ld_op<L128>(Sts[cur], 0, 16 * ks, lane), ld_op<L128>(Qs, 32 * qh, 16 * ks, lane), o);
+            o *= dq;
+        }
+        if (stw) {  // S = e^{-s m} S + K^T (V ⊙ d_k) for keys 32db..
+            S *= fast_exp2(-s2 * (float)m);
+#pragma unroll
+            for (int ks = 0; ks < C / 16; ++ks)
+                S = mma(ld_op_t<L128>(Ks, 32 * db, 16 * ks, lane), ld_op_t<LPad<VP>>(Vds, 0, 16 * ks, lane), S);
+            write_st(Sts[cur ^ 1]);
+        }
+        __syncthreads();  // (C) P and the new S^T are visible
+
+        if (outw) {  // intra-block part O^T += V^T P^T, then stage the block
+#pragma unroll
+            for (int ks = 0; ks < C / 16; ++ks) {
+                if (ks >= 2 * (qh + 1)) break;
+                o = mma(ld_op_t<LPad<VP>>(Vs, 0, 16 * ks, lane), ld_op<LP>(Ps, 32 * qh, 16 * ks, lane), o);
+            }
+#pragma unroll
+            for (int gv = 0; gv < 4; ++gv)
+                *reinterpret_cast<float4 *>(Os + (32 * qh + r32) * OSS + 8 * gv + 4 * hf) =
+                    make_float4(o[4 * gv], o[4 * gv + 1], o[4 * gv + 2], o[4 * gv + 3]);
+        }
+        __syncthreads();  // (D) output slice staged; every tile read of this sub-block done
+        store_slice_rows<FULL>(og + c * C * (long long)ts, ts, Os, m, tid);
+        cur ^= 1;
+    };
+    long long c = 0;
+    for (; c + 1 < nfull; c += 2) {
+        step(c, C, std::true_type{}, st0);
+        step(c + 1, C, std::true_type{}, st1);
+    }
+    if (c < nfull) step(c, C, std::true_type{}, st0);
+    if (tail > 0) {
+        if (nfull & 1)
+            step(nfull, tail, std::false_type{}, st1);
+        else
+            step(nfull, tail, std::false_type{}, st0);
+    }
+
+    if (a.state_out && stw) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) a.state_out[sb + sidx(v)] = S[v];
+    }
+}
+
 template <typename OutT>
 hipError_t launch(const PrefillArgs &a, const PrefillPlan &p, void *workspace, hipStream_t stream) {
     const long long uh = (long long)a.units * a.heads;
+    if (p.value_slices == NSL) {
+        hipLaunchKernelGGL((slice_kernel<OutT>), dim3((unsigned)(uh * NSL)), dim3(NT), 0, stream, a);
+        return hipGetLastError();
+    }
     float *ws = static_cast<float *>(workspace);
     if (p.segments > 1) {
         const int npieces = (p.segments - 1) * p.sub;

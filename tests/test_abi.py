@@ -119,7 +119,11 @@ def test_workspace_query():
     ws = la.lt_prefill_workspace_bytes
     # batch 1, 64 heads, 32K tokens: four segments of 8192 tokens, four pieces each
     assert ws(1, 32768, 64) == 64 * (1 + 3 * 4) * 128 * 128 * 4
-    assert ws(1, 1 << 20, 64) == 64 * (1 + 3 * 4) * 128 * 128 * 4
+    # batch 1, 8 heads, 32K tokens: 16 segments of 2048 tokens
+    assert ws(1, 32768, 8) == 8 * (1 + 15 * 4) * 128 * 128 * 4
+    # batch 1, 2 heads, 1M tokens: 128 segments of 8192 tokens
+    assert ws(1, 1 << 20, 2) == 2 * (1 + 127 * 4) * 128 * 128 * 4
+    assert ws(1, 3000, 64) == 0           # short: value slices, no workspace
     assert ws(4, 32768, 64) == 0          # 256 (sequence, head) pairs already fill the GPU
     assert ws(1, 2048, 64) == 0           # too short to split
     assert ws(1, 32768, 64, in_dtype=la.LT_F32) == 0

@@ -313,3 +313,51 @@ def test_prefill_segmented_state_in_place(la):
     torch.cuda.synchronize()
     _, s_ref = oracle.recurrence_batch(q, k, v, sl, s0=s0, want_o=False)
     assert max_rel_states(to_host_f32(st), s_ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("batch,L,H,with_s0", [(1, 1, 64, True), (1, 65, 64, False),
+                                               (1, 1000, 64, True), (2, 333, 40, True),
+                                               (1, 200, 3, True)])
+def test_prefill_value_slice_plan(la, batch, L, H, with_s0):
+    """Short sequences with fewer than 256 (sequence, head) pairs take the
+    value-slice kernel (4 workgroups of 32 value columns per head)."""
+    assert la.lt_prefill_workspace_bytes(batch, L, H) == 0
+    eo, es = run_prefill_case(la, batch, L, H, "bf16", 3000 + L + H, with_s0=with_s0)
+    assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)
+
+
+def test_prefill_value_slices_without_workspace(la):
+    """A long sequence whose plan wants a workspace, called without one, falls
+    back to value slices and still matches the oracle."""
+    import torch
+
+    L, H = 6000, 64
+    assert la.lt_prefill_workspace_bytes(1, L, H) > 0
+    q, k, v = workloads.qkv_host(3201, (1, L, H, 128), "bf16")
+    sl = workloads.slopes(H)
+    s0 = workloads.state_host(3202, (1, H, 128, 128))
+    o, st = la.lt_prefill(*(to_device(x, "bf16") for x in (q, k, v)), torch.from_numpy(sl).cuda(),
+                          256, torch.from_numpy(s0).cuda(),
+                          workspace=torch.empty(0, device="cuda", dtype=torch.uint8))
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.recurrence_batch(q, k, v, sl, s0=s0)
+    cu = np.array([0, L])
+    assert max_rel_per_head(to_host_f32(o)[0], o_ref[0], cu) <= TOL_BF16
+    assert max_rel_states(to_host_f32(st), s_ref) <= TOL_BF16
+
+
+def test_prefill_value_slice_bf16_output_in_place(la):
+    import torch
+
+    L, H = 700, 64
+    q, k, v = workloads.qkv_host(3101, (1, L, H, 128), "bf16")
+    sl = workloads.slopes(H)
+    s0 = workloads.state_host(3102, (1, H, 128, 128))
+    st = torch.from_numpy(s0).cuda()
+    o, _ = la.lt_prefill(*(to_device(x, "bf16") for x in (q, k, v)), torch.from_numpy(sl).cuda(),
+                         256, st, state_out=st, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.recurrence_batch(q, k, v, sl, s0=s0)
+    cu = np.array([0, L])
+    assert max_rel_per_head(to_host_f32(o)[0], o_ref[0], cu) <= TOL_BF16
+    assert max_rel_states(to_host_f32(st), s_ref) <= TOL_BF16
