@@ -14,6 +14,8 @@
 //    fully coalesced 512-byte transaction of float4 loads/stores;
 //  * all 16 state loads of a thread are issued before anything waits on them
 //    (64 KiB in flight per workgroup);
+//  * state loads and stores carry the non-temporal hint: a batch's states
+//    (1 GiB at 256 sequences x 64 heads) are streamed once per step;
 //  * q.S is reduced in registers, across the two row groups of a wave with a
 //    lane shuffle, then across the four waves through 2 KiB of LDS.
 #include <hip/hip_runtime.h>
@@ -33,6 +35,16 @@ constexpr float LOG2E = 1.4426950408889634f;
 __device__ __forceinline__ float load_in(const float *p, long long i) { return p[i]; }
 __device__ __forceinline__ float load_in(const uint16_t *p, long long i) {
     return __uint_as_float((uint32_t)p[i] << 16);
+}
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 stream_load(const float *p) {
+    const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+    return make_float4(x.x, x.y, x.z, x.w);
+}
+__device__ __forceinline__ void stream_store(float *p, float4 x) {
+    __builtin_nontemporal_store(f32x4{x.x, x.y, x.z, x.w}, reinterpret_cast<f32x4 *>(p));
 }
 
 __device__ __forceinline__ void store4(float *p, float4 x) { *reinterpret_cast<float4 *>(p) = x; }
@@ -59,7 +71,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     float4 s[ROWS_PER_THREAD];
 #pragma unroll
     for (int i = 0; i < ROWS_PER_THREAD; ++i)
-        s[i] = *reinterpret_cast<const float4 *>(st + (rg + 8 * i) * D + 4 * cg);
+        s[i] = stream_load(st + (rg + 8 * i) * D + 4 * cg);
 
     const G *q = static_cast<const G *>(a.q) + (long long)unit * D;
     const G *k = static_cast<const G *>(a.k) + (long long)unit * D;
@@ -83,7 +95,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
         x.y = lam * x.y + kr * v4.y;
         x.z = lam * x.z + kr * v4.z;
         x.w = lam * x.w + kr * v4.w;
-        *reinterpret_cast<float4 *>(st + r * D + 4 * cg) = x;
+        stream_store(st + r * D + 4 * cg, x);
         acc.x += qr * x.x;
         acc.y += qr * x.y;
         acc.z += qr * x.z;

@@ -41,19 +41,28 @@ constexpr int kValueSlices = 4;
 
 // How a bf16 prefill is cut into workgroups. Each (unit, head) sequence is
 // split into `segments` consecutive pieces of `seg_len` tokens (the last may be
-// shorter), one workgroup each. With more than one segment, a pre-pass over
-// `sub` equal pieces of every segment but the last computes the state each
-// piece contributes; segment g then starts from the decayed sum of everything
-// before it. All lengths are multiples of the 64-token sub-block.
+// shorter), one workgroup each. With more than one segment, the first
+// (segments-1)*seg_len tokens are also cut into `pieces` pre-pass pieces of
+// `piece_len` tokens (the last may be shorter); the pre-pass computes the state
+// each piece contributes (and, for a piece that straddles a segment boundary,
+// the part before the boundary), a combine pass sums them into the state at
+// every segment start, and segment g starts from that. seg_len and piece_len
+// are multiples of 128 tokens (two 64-token sub-blocks).
 // With value_slices == 4 the head is instead split into four 32-column value
 // slices (one workgroup each, no segments, no workspace).
 struct PrefillPlan {
-    int segments;
-    int sub;
-    long long seg_len;
-    size_t workspace;  // bytes: per (unit, head), (1 + (segments-1)*sub) fp32 d x d states
-    int value_slices;  // 1 = whole head per workgroup, 4 = value-slice workgroups
+    int segments = 1;
+    long long seg_len = 0;
+    int pieces = 0;
+    long long piece_len = 0;
+    size_t workspace = 0;  // bytes: per (unit, head), prefill_states(...) fp32 d x d states
+    int value_slices = 1;  // 1 = whole head per workgroup, 4 = value-slice workgroups
 };
+
+// fp32 d x d states per (unit, head) in the workspace of a segmented plan:
+// one per piece, one partial state per segment boundary, one carried-in state
+// per segment.
+constexpr long long prefill_states(int segments, int pieces) { return pieces + 2LL * segments - 1; }
 
 PrefillPlan plan_prefill(long long units, long long seqlen, int heads, lt_dtype in_dtype,
                          bool varlen);

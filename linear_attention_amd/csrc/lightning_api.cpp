@@ -40,9 +40,13 @@ lt_status map_hip(hipError_t e) { return e == hipSuccess ? LT_OK : LT_ERR_HIP; }
 // Workgroups a prefill launch should reach to occupy MI355X (256 CUs; the
 // whole-head kernel runs one 8-wave workgroup per CU).
 constexpr long long kTargetWorkgroups = 256;
-// Shortest segment worth a workgroup of its own, and pre-pass pieces per segment.
+// Shortest segment worth a workgroup of its own.
 constexpr long long kMinSegment = 2048;
-constexpr int kPieces = 4;
+// Pre-pass workgroups to aim for: two per CU is what its registers allow, so
+// the whole pre-pass grid is resident at once.
+constexpr long long kPrepassWorkgroups = 512;
+// Shortest pre-pass piece.
+constexpr long long kMinPiece = 512;
 
 lt_status launch(const lt::PrefillArgs &a, int in_dtype, int out_dtype, bool varlen,
                  void *workspace, size_t workspace_bytes, void *stream) {
@@ -52,8 +56,11 @@ lt_status launch(const lt::PrefillArgs &a, int in_dtype, int out_dtype, bool var
     lt::PrefillPlan p = lt::plan_prefill(a.units, varlen ? a.total_tokens : a.seqlen, a.heads,
                                          (lt_dtype)in_dtype, varlen);
     // Without the workspace the segmented plan needs, split value columns instead.
-    if (p.workspace > 0 && (!workspace || workspace_bytes < p.workspace))
-        p = lt::PrefillPlan{1, 1, varlen ? a.total_tokens : a.seqlen, 0, 4};
+    if (p.workspace > 0 && (!workspace || workspace_bytes < p.workspace)) {
+        p = lt::PrefillPlan{};
+        p.seg_len = varlen ? a.total_tokens : a.seqlen;
+        p.value_slices = lt::kValueSlices;
+    }
     return map_hip(lt::launch_prefill_heads(a, p, workspace, (lt_dtype)out_dtype, st));
 }
 
@@ -102,28 +109,39 @@ PrefillPlan plan_prefill(long long units, long long seqlen, int heads, lt_dtype 
     // bf16 plans, by the number of (sequence, head) pairs uh:
     //   uh >= 256: one whole-head workgroup per pair;
     //   long fixed-length sequences: whole heads cut into segments, with the
-    //     pre-pass (its extra k, v reads cost less than re-reading q, k per
-    //     value slice, which measured 4.05 TB/s memory-only against 5.2 TB/s);
+    //     pre-pass and combine pass (its extra k, v reads cost less than
+    //     re-reading q, k per value slice, which measured 4.05 TB/s memory-only
+    //     against 5.2 TB/s);
     //   otherwise (varlen, short sequences): four value-slice workgroups per pair.
-    PrefillPlan p{1, 1, seqlen, 0, 1};
+    PrefillPlan p;
+    p.seg_len = seqlen;
     if (in_dtype != LT_BF16 || units <= 0 || heads <= 0) return p;
     const long long uh = units * heads;
     if (uh >= kTargetWorkgroups) return p;
-    p.value_slices = 4;
+    p.value_slices = kValueSlices;
     if (varlen) return p;
     long long g = (kTargetWorkgroups + uh - 1) / uh;
     if (g > seqlen / kMinSegment) g = seqlen / kMinSegment;
     if (g < 2) return p;
-    const long long quantum = 64LL * kPieces;
     long long seg = (seqlen + g - 1) / g;
-    seg = (seg + quantum - 1) / quantum * quantum;
+    seg = (seg + 127) / 128 * 128;  // segmented kernels step two sub-blocks at a time
     g = (seqlen + seg - 1) / seg;
     if (g < 2) return p;
+    // Pre-pass pieces over the first (g-1) segments. piece <= seg, so a piece
+    // holds at most one segment boundary strictly inside it.
+    const long long covered = (g - 1) * seg;
+    const long long want = (kPrepassWorkgroups + uh - 1) / uh;
+    long long piece = (covered + want - 1) / want;
+    piece = (piece + 127) / 128 * 128;
+    if (piece < kMinPiece) piece = kMinPiece;
+    if (piece > seg) piece = seg;
     p.value_slices = 1;
     p.segments = (int)g;
-    p.sub = kPieces;
     p.seg_len = seg;
-    p.workspace = (size_t)uh * (size_t)(1 + (g - 1) * kPieces) * kHeadDim * kHeadDim * sizeof(float);
+    p.piece_len = piece;
+    p.pieces = (int)((covered + piece - 1) / piece);
+    p.workspace = (size_t)uh * (size_t)prefill_states(p.segments, p.pieces) * kHeadDim * kHeadDim *
+                  sizeof(float);
     return p;
 }
 

@@ -107,6 +107,40 @@ __device__ __forceinline__ bf16x8 ld_op_t(const __bf16 *t, int c0, int k0, int l
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// Streaming HBM access. q, k, v are read once and o is written once, so loads
+// and stores carry the non-temporal hint; measured on this kernel's access
+// pattern (256-byte row pieces at a 16 KiB token stride) it lifts the k, v
+// read rate from 2.4 to 5.7 TB/s and the q, k, v + o pattern from 5.2 to
+// 5.8 TB/s. State and workspace traffic keeps the default policy.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 stream_load16(const uint16_t *p) {
+    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(x.x, x.y, x.z, x.w);
+}
+__device__ __forceinline__ uint2 stream_load8(const uint16_t *p) {
+    const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+    return make_uint2(x.x, x.y);
+}
+__device__ __forceinline__ void stream_store(float *p, float4 x) {
+    __builtin_nontemporal_store(f32x4{x.x, x.y, x.z, x.w}, reinterpret_cast<f32x4 *>(p));
+}
+template <class V>
+__device__ __forceinline__ void stream_store_bits(__bf16 *p, const V &x) {
+    static_assert(sizeof(V) == 16 || sizeof(V) == 8, "16- or 8-byte stores");
+    if constexpr (sizeof(V) == 16) {
+        u32x4 b;
+        __builtin_memcpy(&b, &x, 16);
+        __builtin_nontemporal_store(b, reinterpret_cast<u32x4 *>(p));
+    } else {
+        u32x2 b;
+        __builtin_memcpy(&b, &x, 8);
+        __builtin_nontemporal_store(b, reinterpret_cast<u32x2 *>(p));
+    }
+}
+
 __device__ __forceinline__ uint4 keep_if(bool keep, uint4 x) {
     return make_uint4(keep ? x.x : 0u, keep ? x.y : 0u, keep ? x.z : 0u, keep ? x.w : 0u);
 }
@@ -143,27 +177,28 @@ struct Stage {
         for (int i = 0; i < 2; ++i) {
             const int t = (tid >> 4) + 32 * i;
             const int row = (t < m ? t : m - 1) * ts + 8 * seg;
-            if (WITH_Q) q[i] = *reinterpret_cast<const uint4 *>(qg + row);
-            k[i] = *reinterpret_cast<const uint4 *>(kg + row);
-            v[i] = *reinterpret_cast<const uint4 *>(vg + row);
+            if (WITH_Q) q[i] = stream_load16(qg + row);
+            k[i] = stream_load16(kg + row);
+            v[i] = stream_load16(vg + row);
         }
     }
 
     // Writes Q, K, V row-major and V ⊙ d_k (d_k[t] = e^{-s(m-1-t)}, 0 for t >= m);
-    // without Q (the pre-pass) only K and V ⊙ d_k.
+    // without Q (the pre-pass) only K and V ⊙ d_k. FULL: m == C (no masking).
+    template <bool FULL>
     __device__ void store(__bf16 *Qs, __bf16 *Ks, __bf16 *Vs, __bf16 *Vds, int m, float s2,
                           int tid) {
         const int seg = tid & 15;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int t = (tid >> 4) + 32 * i;
-            const bool in = t < m;
+            const bool in = FULL || t < m;
             const int off = L128::off(t, 8 * seg);
             if (WITH_Q) *reinterpret_cast<uint4 *>(Qs + off) = keep_if(in, q[i]);
             *reinterpret_cast<uint4 *>(Ks + off) = keep_if(in, k[i]);
             const uint4 vv = keep_if(in, v[i]);
             if (WITH_Q) *reinterpret_cast<uint4 *>(Vs + off) = vv;  // the pre-pass needs only V ⊙ d_k
-            const float dk = in ? fast_exp2(-s2 * (float)(m - 1 - t)) : 0.f;
+            const float dk = in ? fast_exp2(-s2 * (float)((FULL ? C : m) - 1 - t)) : 0.f;
             *reinterpret_cast<uint4 *>(Vds + off) = scale_bf16x8(vv, dk);
         }
     }
@@ -233,7 +268,7 @@ __device__ __forceinline__ void store_rows(float *out, long long ts, const float
     for (int j = 0; j < 4; ++j) {
         const int row = (tid >> 5) + 16 * j, col = 4 * (tid & 31);
         const float4 x = *reinterpret_cast<const float4 *>(Os + ooff(row, col));
-        if (FULL || row < m) *reinterpret_cast<float4 *>(out + row * ts + col) = x;
+        if (FULL || row < m) stream_store(out + row * ts + col, x);
     }
 }
 template <bool FULL>
@@ -246,7 +281,7 @@ __device__ __forceinline__ void store_rows(__bf16 *out, long long ts, const floa
         const bf16x8 y = {static_cast<__bf16>(x0.x), static_cast<__bf16>(x0.y), static_cast<__bf16>(x0.z),
                           static_cast<__bf16>(x0.w), static_cast<__bf16>(x1.x), static_cast<__bf16>(x1.y),
                           static_cast<__bf16>(x1.z), static_cast<__bf16>(x1.w)};
-        if (FULL || row < m) *reinterpret_cast<bf16x8 *>(out + row * ts + col) = y;
+        if (FULL || row < m) stream_store_bits(out + row * ts + col, y);
     }
 }
 
@@ -266,79 +301,154 @@ __device__ __forceinline__ SeqRange sequence_of(const PrefillArgs &a, int n) {
 }
 
 // ---------------------------------------------------------------------------
-// Pre-pass: the state one piece of a sequence contributes, from a zero state:
-//   S_piece = sum_t e^{-s(end-1-t)} k_t^T v_t  over the piece's tokens.
-// Workgroup (unit, head, piece j) covers tokens [j*piece_len, (j+1)*piece_len),
-// all full 64-token sub-blocks. Piece 0 also copies the carried-in state S_0
-// (or zeros) to the workspace, so the main kernel never reads state_in and an
-// in-place state update cannot race.
-// Workspace per (unit, head): [S_0][S_piece 0 .. npieces-1], fp32 d x d each.
-__global__ __launch_bounds__(NT) void piece_state_kernel(PrefillArgs a, int npieces,
-                                                         long long piece_len, float *ws) {
+// Segmented plans. Sequence (unit, head) is cut into `segments` segments of
+// seg_len tokens; the first covered = (segments-1)*seg_len tokens are cut again
+// into `pieces` pre-pass pieces of piece_len tokens (piece_len <= seg_len; both
+// multiples of 128, so every piece and part of a piece is an even number of
+// 64-token sub-blocks). Workspace per (unit, head), fp32 d x d states:
+//   [P_0 .. P_{pieces-1}]       state of each piece's tokens from a zero state
+//   [B_1 .. B_{segments-1}]     for a boundary inside a piece: the state of that
+//                               piece's tokens before the boundary
+//   [S_0 .. S_{segments-1}]     state at the start of each segment
+// A state of tokens [t0, t1) from zero is sum_t e^{-s(t1-1-t)} k_t^T v_t, and
+// states compose as S(t2) = e^{-s(t2-t1)} S(t1) + state of [t1, t2).
+struct Segmented {
+    int segments, pieces;
+    long long seg_len, piece_len;
+    __device__ long long covered() const { return (segments - 1) * seg_len; }
+    __device__ float *unit(float *ws, int uh) const {
+        return ws + (size_t)uh * (size_t)(pieces + 2 * segments - 1) * D * D;
+    }
+    __device__ static float *slot(float *u, long long i) { return u + (size_t)i * D * D; }
+    __device__ float *piece_state(float *u, int j) const { return slot(u, j); }
+    __device__ int partial_slot(int g) const { return pieces + g - 1; }
+    __device__ float *partial(float *u, int g) const { return slot(u, partial_slot(g)); }
+    __device__ float *start_state(float *u, int g) const { return slot(u, pieces + segments - 1 + g); }
+};
+
+// Pre-pass: workgroup (unit, head, piece j) runs the state update over the
+// piece's full 64-token sub-blocks without outputs, writing P_j and, if a
+// segment boundary falls strictly inside the piece, B_g on the way.
+__global__ __launch_bounds__(NT, 4) void piece_state_kernel(PrefillArgs a, Segmented sp, float *ws) {
     __shared__ __attribute__((aligned(16))) __bf16 Ks[C * D];
     __shared__ __attribute__((aligned(16))) __bf16 Vds[C * D];
 
-    const int j = blockIdx.x % npieces;
-    const int uh = blockIdx.x / npieces;
+    const int j = blockIdx.x % sp.pieces;
+    const int uh = blockIdx.x / sp.pieces;
     const int h = uh % a.heads, n = uh / a.heads;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int qh = w >> 2, cq = w & 3, r32 = lane & 31, hf = lane >> 5;
 
+    const long long t0 = j * sp.piece_len;
+    const long long t1 = t0 + sp.piece_len < sp.covered() ? t0 + sp.piece_len : sp.covered();
     const SeqRange sr = sequence_of(a, n);
     const int ts = a.heads * D;
-    const long long base = ((sr.start + j * piece_len) * a.heads + h) * (long long)D;
+    const long long base = ((sr.start + t0) * a.heads + h) * (long long)D;
     const uint16_t *kg = static_cast<const uint16_t *>(a.k) + base;
     const uint16_t *vg = static_cast<const uint16_t *>(a.v) + base;
     const float s2 = a.slopes[h] * LOG2E;
-    float *wsu = ws + (size_t)uh * (1 + npieces) * D * D;
-
-    if (j == 0) {
-        const long long sb = (long long)uh * D * D;
-        for (int e = tid; e < D * D; e += NT) wsu[e] = a.state_in ? a.state_in[sb + e] : 0.f;
-    }
+    float *u = sp.unit(ws, uh);
 
     f32x16 S[2];
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
         for (int v = 0; v < 16; ++v) S[db][v] = 0.f;
+    // Writes S to workspace slot `slot` of this (unit, head). The empty asm
+    // keeps the compiler from computing the addresses of both stores before
+    // the loops (which costs ~50 registers and spills).
+    auto store_state = [&](int slot) {
+        asm volatile("" : "+s"(slot));
+        float *dst = Segmented::slot(u, slot);
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                dst[(64 * qh + 32 * db + 8 * (v >> 2) + 4 * hf + (v & 3)) * D + 32 * cq + r32] = S[db][v];
+    };
 
     Stage<false> st0, st1;
-    const long long nch = piece_len / C;  // >= 2, all full sub-blocks
+    const long long nch = (t1 - t0) / C;  // even, >= 2: all full sub-blocks
     const float bd = fast_exp2(-s2 * (float)C);
     auto prefetch = [&](Stage<false> &st, long long c) {
         const long long off = (c < nch ? c : nch - 1) * C * (long long)ts;
         st.load(nullptr, kg + off, vg + off, ts, C, tid);
     };
     auto step = [&](long long c, Stage<false> &st) {
+        // Nothing of this sub-block may be scheduled into the previous one:
+        // touching its registers there waits for its loads one sub-block early.
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
-        st.store(nullptr, Ks, nullptr, Vds, C, s2, tid);
+        st.template store<true>(nullptr, Ks, nullptr, Vds, C, s2, tid);
         prefetch(st, c + 2);
         __syncthreads();
         state_update(S, Ks, Vds, bd, qh, cq, lane);
     };
+    // sub-blocks [c0, c1), both even; sub-block c is staged in st[c % 2]
+    auto run = [&](long long c0, long long c1) {
+        for (long long c = c0; c < c1; c += 2) {
+            step(c, st0);
+            step(c + 1, st1);
+        }
+    };
     prefetch(st0, 0);
     prefetch(st1, 1);
-    long long c = 0;
-    for (; c + 1 < nch; c += 2) {
-        step(c, st0);
-        step(c + 1, st1);
-    }
-    if (c < nch) step(c, st0);
+    // Up to the segment boundary inside the piece (if any: B_g), then the rest.
+    // Without one the first part is the whole piece, the second is empty, and
+    // P_j is written twice with the same values (a branch around either store
+    // costs the loop ~50 registers).
+    const int gb = (int)(t0 / sp.seg_len) + 1;  // first segment boundary after t0
+    const long long b = gb * sp.seg_len;
+    const long long cb = b < t1 ? (b - t0) / C : nch;
+    run(0, cb);
+    store_state(b < t1 ? sp.partial_slot(gb) : j);
+    run(cb, nch);
+    store_state(j);
+}
 
-    float *dst = wsu + (size_t)(1 + j) * D * D;
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-            dst[(64 * qh + 32 * db + 8 * (v >> 2) + 4 * hf + (v & 3)) * D + 32 * cq + r32] = S[db][v];
+// Combine pass: the state at every segment start, S_0 being the carried-in
+// state (or zero). Workgroup (unit, head, 1024-element slice) walks the pieces
+// in order with 4 elements per thread:
+//   acc <- e^{-s len_j} acc + P_j,
+// and at each boundary b_g: S_g = acc if b_g ends piece j, or
+// e^{-s(b_g - start_j)} acc + B_g if it falls inside piece j.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineSlices = D * D / (4 * kCombineThreads);
+
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(PrefillArgs a, Segmented sp,
+                                                                   float *ws) {
+    const int uh = blockIdx.x / kCombineSlices;
+    const int e = 4 * ((blockIdx.x % kCombineSlices) * kCombineThreads + threadIdx.x);
+    const int h = uh % a.heads;
+    const float s2 = a.slopes[h] * LOG2E;
+    float *u = sp.unit(ws, uh);
+    float4 acc = a.state_in ? *reinterpret_cast<const float4 *>(a.state_in + (size_t)uh * D * D + e)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4 *>(sp.start_state(u, 0) + e) = acc;
+    const long long covered = sp.covered();
+    for (int j = 0; j < sp.pieces; ++j) {
+        const long long t0 = j * sp.piece_len;
+        const long long t1 = t0 + sp.piece_len < covered ? t0 + sp.piece_len : covered;
+        const int gb = (int)(t0 / sp.seg_len) + 1;
+        const long long b = gb * sp.seg_len;
+        if (b < t1) {
+            const float f = fast_exp2(-s2 * (float)(b - t0));
+            const float4 p = *reinterpret_cast<const float4 *>(sp.partial(u, gb) + e);
+            *reinterpret_cast<float4 *>(sp.start_state(u, gb) + e) =
+                make_float4(f * acc.x + p.x, f * acc.y + p.y, f * acc.z + p.z, f * acc.w + p.w);
+        }
+        const float f = fast_exp2(-s2 * (float)(t1 - t0));
+        const float4 p = *reinterpret_cast<const float4 *>(sp.piece_state(u, j) + e);
+        acc = make_float4(f * acc.x + p.x, f * acc.y + p.y, f * acc.z + p.z, f * acc.w + p.w);
+        if (t1 % sp.seg_len == 0)
+            *reinterpret_cast<float4 *>(sp.start_state(u, (int)(t1 / sp.seg_len)) + e) = acc;
+    }
 }
 
 // ---------------------------------------------------------------------------
 template <typename OutT>
-__global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, int segments, long long seg_len,
-                                                  int sub, const float *ws) {
+__global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, float *ws) {
     __shared__ __attribute__((aligned(16))) __bf16 Qs[C * D];
     __shared__ __attribute__((aligned(16))) __bf16 Ks[C * D];
     __shared__ __attribute__((aligned(16))) __bf16 Vs[C * D];
@@ -346,6 +456,8 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, int segments, l
     __shared__ __attribute__((aligned(16))) __bf16 Sts[2][D * D];
     __shared__ __attribute__((aligned(16))) __bf16 Ps[C * PW];
 
+    const int segments = sp.segments;
+    const long long seg_len = sp.seg_len;
     const int g = blockIdx.x % segments;
     const int uh = blockIdx.x / segments;
     const int h = uh % a.heads, n = uh / a.heads;
@@ -365,34 +477,24 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, int segments, l
     OutT *og = static_cast<OutT *>(a.o) + base;
     const float s2 = a.slopes[h] * LOG2E;
 
-    // ---- carried-in state of this segment
+    // ---- carried-in state of this segment (the combine pass wrote it for
+    // segmented plans, so an in-place state update never races with it)
     f32x16 S[2];
     auto sidx = [&](int db, int v) {
         return (64 * qh + 32 * db + 8 * (v >> 2) + 4 * hf + (v & 3)) * D + 32 * cq + r32;
     };
-    if (segments == 1) {
-        const long long sb = (long long)uh * D * D;
+    const float *s_in = segments > 1 ? sp.start_state(sp.unit(ws, uh), g)
+                                     : (a.state_in ? a.state_in + (size_t)uh * D * D : nullptr);
+    if (s_in) {
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) S[db][v] = a.state_in ? a.state_in[sb + sidx(db, v)] : 0.f;
+            for (int v = 0; v < 16; ++v) S[db][v] = s_in[sidx(db, v)];
     } else {
-        const int npieces = (segments - 1) * sub;
-        const long long piece_len = seg_len / sub;
-        const float *wsu = ws + (size_t)uh * (1 + npieces) * D * D;
-        const float f0 = fast_exp2(-s2 * (float)seg0);
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) S[db][v] = f0 * wsu[sidx(db, v)];
-        for (int j = 0; j < g * sub; ++j) {
-            const float fj = fast_exp2(-s2 * (float)(seg0 - (j + 1) * piece_len));
-            const float *src = wsu + (size_t)(1 + j) * D * D;
-#pragma unroll
-            for (int db = 0; db < 2; ++db)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) S[db][v] += fj * src[sidx(db, v)];
-        }
+            for (int v = 0; v < 16; ++v) S[db][v] = 0.f;
     }
     write_state_t(Sts[0], S, qh, cq, lane);
 
@@ -436,7 +538,7 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, int segments, l
     // next barrier B).
     auto step = [&](long long c, int m, auto full, Stage<true> &st) {
         constexpr bool FULL = decltype(full)::value;
-        st.store(Qs, Ks, Vs, Vds, m, s2, tid);
+        st.template store<FULL>(Qs, Ks, Vs, Vds, m, s2, tid);
         if (FULL) prefetch(st, c + 2);
         __syncthreads();  // (B) tiles and S^T of the previous sub-block are visible
         if (scorer) {
@@ -532,11 +634,11 @@ struct SliceStage {
         for (int i = 0; i < 2; ++i) {
             const int t = (tid >> 4) + 32 * i;
             const int row = (t < m ? t : m - 1) * ts + 8 * seg;
-            q[i] = *reinterpret_cast<const uint4 *>(qg + row);
-            k[i] = *reinterpret_cast<const uint4 *>(kg + row);
+            q[i] = stream_load16(qg + row);
+            k[i] = stream_load16(kg + row);
         }
         const int vt = tid >> 3;
-        v = *reinterpret_cast<const uint2 *>(vg + (vt < m ? vt : m - 1) * ts + 4 * (tid & 7));
+        v = stream_load8(vg + (vt < m ? vt : m - 1) * ts + 4 * (tid & 7));
     }
 
     __device__ void store(__bf16 *Qs, __bf16 *Ks, __bf16 *Vs, __bf16 *Vds, int m, float s2, int tid) {
@@ -563,7 +665,7 @@ __device__ __forceinline__ void store_slice_rows(float *out, long long ts, const
                                                  int tid) {
     const int row = tid >> 3, col = 4 * (tid & 7);
     const float4 x = *reinterpret_cast<const float4 *>(Os + row * OSS + col);
-    if (FULL || row < m) *reinterpret_cast<float4 *>(out + row * ts + col) = x;
+    if (FULL || row < m) stream_store(out + row * ts + col, x);
 }
 template <bool FULL>
 __device__ __forceinline__ void store_slice_rows(__bf16 *out, long long ts, const float *Os, int m,
@@ -572,7 +674,7 @@ __device__ __forceinline__ void store_slice_rows(__bf16 *out, long long ts, cons
     const float4 x = *reinterpret_cast<const float4 *>(Os + row * OSS + col);
     const bf16x4 y = {static_cast<__bf16>(x.x), static_cast<__bf16>(x.y), static_cast<__bf16>(x.z),
                       static_cast<__bf16>(x.w)};
-    if (FULL || row < m) *reinterpret_cast<bf16x4 *>(out + row * ts + col) = y;
+    if (FULL || row < m) stream_store_bits(out + row * ts + col, y);
 }
 
 template <typename OutT>
@@ -737,15 +839,19 @@ hipError_t launch(const PrefillArgs &a, const PrefillPlan &p, void *workspace, h
         return hipGetLastError();
     }
     float *ws = static_cast<float *>(workspace);
+    const Segmented sp{p.segments, p.pieces, p.seg_len, p.piece_len};
     if (p.segments > 1) {
-        const int npieces = (p.segments - 1) * p.sub;
-        hipLaunchKernelGGL(piece_state_kernel, dim3((unsigned)(uh * npieces)), dim3(NT), 0, stream,
-                           a, npieces, p.seg_len / p.sub, ws);
-        const hipError_t e = hipGetLastError();
+        hipLaunchKernelGGL(piece_state_kernel, dim3((unsigned)(uh * p.pieces)), dim3(NT), 0, stream,
+                           a, sp, ws);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(uh * kCombineSlices)), dim3(kCombineThreads),
+                           0, stream, a, sp, ws);
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL((head_kernel<OutT>), dim3((unsigned)(uh * p.segments)), dim3(NT), 0, stream,
-                       a, p.segments, p.seg_len, p.sub, ws);
+                       a, sp, ws);
     return hipGetLastError();
 }
 

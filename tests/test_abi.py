@@ -117,12 +117,18 @@ def test_prefill_workspace_alias():
 
 def test_workspace_query():
     ws = la.lt_prefill_workspace_bytes
-    # batch 1, 64 heads, 32K tokens: four segments of 8192 tokens, four pieces each
-    assert ws(1, 32768, 64) == 64 * (1 + 3 * 4) * 128 * 128 * 4
-    # batch 1, 8 heads, 32K tokens: 16 segments of 2048 tokens
-    assert ws(1, 32768, 8) == 8 * (1 + 15 * 4) * 128 * 128 * 4
-    # batch 1, 2 heads, 1M tokens: 128 segments of 8192 tokens
-    assert ws(1, 1 << 20, 2) == 2 * (1 + 127 * 4) * 128 * 128 * 4
+    st = 128 * 128 * 4  # one fp32 state
+    # Segmented plan: per (sequence, head) one state per pre-pass piece, one
+    # partial state per segment boundary and one start state per segment.
+    # batch 1, 64 heads, 32K tokens: 4 segments of 8192; 24576 covered tokens
+    # in 8 pieces of 3072 (512 pre-pass workgroups)
+    assert ws(1, 32768, 64) == 64 * (8 + 2 * 4 - 1) * st
+    # batch 1, 8 heads, 32K tokens: 16 segments of 2048; 30720 covered tokens
+    # in 60 pieces of 512 (the shortest piece)
+    assert ws(1, 32768, 8) == 8 * (60 + 2 * 16 - 1) * st
+    # batch 1, 2 heads, 1M tokens: 128 segments of 8192; 127 * 8192 covered
+    # tokens in 254 pieces of 4096
+    assert ws(1, 1 << 20, 2) == 2 * (254 + 2 * 128 - 1) * st
     assert ws(1, 3000, 64) == 0           # short: value slices, no workspace
     assert ws(4, 32768, 64) == 0          # 256 (sequence, head) pairs already fill the GPU
     assert ws(1, 2048, 64) == 0           # too short to split
