@@ -123,7 +123,7 @@ def run_prefill(la, torch, steps, warmup):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "bytes_per_launch": bytes_alg,
-                     "kernel": "lt_prefill call: piece_state_kernel + head_kernel<f32 out>"},
+                     "kernel": "lt_prefill call: piece_state_kernel + combine_kernel + head_kernel<float>"},
     }
 
 
@@ -287,7 +287,7 @@ def traffic_from(copy_dir, fetch_dir, write_dir, copy_bytes):
     w_scale = copy_bytes / (copy_write_kib * 1024)
     kf = per_kernel(fetch_dir, "FETCH_SIZE")
     kw = per_kernel(write_dir, "WRITE_SIZE")
-    kernels = [k for k in kf if "prefill" in k or "head_kernel" in k or "piece_state" in k]
+    kernels = [k for k in kf if any(n in k for n in ("head_kernel", "piece_state_kernel", "combine_kernel", "slice_kernel"))]
     import numpy as np
 
     fetch = sum(float(np.median(kf[k])) for k in kernels) * 1024 * f_scale
@@ -302,22 +302,26 @@ def traffic_from(copy_dir, fetch_dir, write_dir, copy_bytes):
     print(json.dumps(out))
 
 
-def run_cpu_baseline(w, dev_inputs, tokens):
+def run_cpu_baseline(w, dev_inputs, tokens, min_seconds=10.0, max_reps=50):
     """The fp64 oracle (as it stands) on the host cores, on the first `tokens`
-    tokens of the same prefill inputs, all heads."""
+    tokens of the same prefill inputs, all heads; repeated until `min_seconds`
+    of CPU work have been timed."""
     import oracle
 
     q, k, v, slopes = dev_inputs
     hq, hk, hv = (x[:, :tokens].float().cpu().numpy() for x in (q, k, v))
     sl = slopes.cpu().numpy()
     threads = oracle.max_threads()
-    t0 = time.perf_counter()
-    oracle.recurrence_batch(hq, hk, hv, sl)
-    dt = time.perf_counter() - t0
-    return {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": threads,
+    reps, dt = 0, 0.0
+    while reps < max_reps and (reps == 0 or dt < min_seconds):
+        t0 = time.perf_counter()
+        oracle.recurrence_batch(hq, hk, hv, sl)
+        dt += time.perf_counter() - t0
+        reps += 1
+    return {"value": round(tokens * reps / dt, 1), "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"first {tokens} of {w.seqlen} tokens, all {w.heads} heads "
-                      f"({tokens * w.heads} (token, head) pairs, {dt:.2f} s, fp64)",
+            "sample": f"first {tokens} of {w.seqlen} tokens, all {w.heads} heads, {reps} runs "
+                      f"({reps * tokens * w.heads} (token, head) pairs, {dt:.2f} s, fp64)",
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
