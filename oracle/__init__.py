@@ -19,6 +19,10 @@ Three independent formulations of the same operator, all in fp64:
 ``block_form``
     The §03 block decomposition itself, step by step in the pages' notation
     (``D``, ``d_q``, ``d_k``, block decay, last short block of length ``m``).
+``norm_gate``
+    The step after the operator in the §03 data-flow figure: the summed output
+    is normalised and gated (RMS normalisation per (token, head), a weight per
+    (head, feature), a logistic-sigmoid gate; the pages name neither form).
 
 Readings of points the pages leave open (each is listed in the design doc):
 positions inside a block are 1-indexed, ``d_q[i] = e^{-s i}``,
@@ -260,3 +264,22 @@ def block_form(q, k, v, s, block, s0=None):
         o[t0:t0 + m] = o_intra + o_inter
         S = np.exp(-s * m) * S + (Kt * dk[:, None]).T @ Vt
     return o, S
+
+
+def norm_gate(o, gate, weight, eps):
+    """Post-sum normalisation and gating, in fp64.
+
+    MiniMax Signal Lab · M1, §03 (data-flow figure): after the intra- and
+    inter-block outputs are added, the result passes through a normalisation
+    and a gate. The pages name neither; the reading used here: each (token,
+    head) vector of d features is divided by its root mean square,
+    sqrt(mean(o^2) + eps), multiplied by a weight per (head, feature), and
+    multiplied by the logistic sigmoid of a gate tensor of the same shape as o.
+
+    o, gate: [..., H, d]; weight: [H, d]; eps >= 0. Returns fp64 [..., H, d].
+    """
+    o = np.asarray(o, np.float64)
+    g = np.asarray(gate, np.float64)
+    w = np.asarray(weight, np.float64)
+    ms = np.mean(o * o, axis=-1, keepdims=True)
+    return o / np.sqrt(ms + np.float64(eps)) * w * (1.0 / (1.0 + np.exp(-g)))

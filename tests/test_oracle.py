@@ -355,3 +355,129 @@ def test_bf16_rounding_is_nearest_even():
     assert r[3] == -2.5
     assert abs(r[4] - 1e-3) / 1e-3 < 2 ** -8
     assert np.all((r.view(np.uint32) & 0xFFFF) == 0)
+
+
+# --------------------------------------------------------------------------
+# Post-sum normalisation and gating (oracle.norm_gate)
+# --------------------------------------------------------------------------
+
+def _ng_inputs(seed, T=5, H=3, d=8):
+    g = np.random.Generator(np.random.PCG64(seed))
+    o = g.standard_normal((T, H, d)) * g.uniform(0.1, 10.0, (T, H, 1))
+    gate = g.standard_normal((T, H, d))
+    w = g.uniform(0.5, 2.0, (H, d))
+    return o, gate, w
+
+
+def norm_gate_pin_failures(f):
+    """Names of the pins that f(o, gate, weight, eps) fails."""
+    bad = []
+    o, gate, w = _ng_inputs(11)
+    T, H, d = o.shape
+    ones = np.ones((H, d))
+    big = np.full_like(gate, 40.0)  # sigmoid(40) rounds to 1 in fp64
+    # 1. unit root mean square with weight 1, gate -> 1, eps = 0
+    y = f(o, big, ones, 0.0)
+    if np.max(np.abs(np.sqrt(np.mean(y * y, axis=-1)) - 1.0)) > 1e-12:
+        bad.append("unit rms")
+    # 2. with eps: rms(y) = sqrt(ms / (ms + eps))
+    eps = 0.37
+    ms = np.mean(o * o, axis=-1)
+    y = f(o, big, ones, eps)
+    if np.max(np.abs(np.sqrt(np.mean(y * y, axis=-1)) - np.sqrt(ms / (ms + eps)))) > 1e-12:
+        bad.append("rms with eps")
+    # 3. scale invariance and odd symmetry (eps = 0)
+    y0 = f(o, gate, w, 0.0)
+    if rel(f(3.7 * o, gate, w, 0.0), y0) > 1e-13 or rel(f(-o, gate, w, 0.0), -y0) > 1e-13:
+        bad.append("scale invariance")
+    # 4. one-hot closed form, every head with its own hot feature b_h:
+    #    o_h = a e_{b_h} -> y_{h, b_h} = a / sqrt(a^2/d + eps) w[h, b_h] sigmoid(g_{h, b_h})
+    a = 2.5
+    oh = np.zeros((1, H, d))
+    for hh in range(H):
+        oh[0, hh, (3 + 2 * hh) % d] = a
+    y = f(oh, gate[:1], w, eps)
+    for hh in range(H):
+        b = (3 + 2 * hh) % d
+        want = a / math.sqrt(a * a / d + eps) * w[hh, b] / (1.0 + math.exp(-gate[0, hh, b]))
+        others = np.delete(y[0, hh], b)
+        if abs(y[0, hh, b] - want) > 1e-12 * abs(want) or np.max(np.abs(others)) > 0.0:
+            bad.append(f"one-hot head {hh}")
+    # 5. gate values with exact sigmoids: 0 -> 1/2, ln 3 -> 3/4
+    yb = f(o, big, w, eps)
+    if rel(f(o, np.zeros_like(gate), w, eps), 0.5 * yb) > 1e-13:
+        bad.append("gate 0")
+    if rel(f(o, np.full_like(gate, math.log(3.0)), w, eps), 0.75 * yb) > 1e-13:
+        bad.append("gate ln 3")
+    # 6. linear in the weight
+    if rel(f(o, gate, 2.0 * w, eps), 2.0 * f(o, gate, w, eps)) > 1e-13:
+        bad.append("weight linearity")
+    # 7. heads are normalised independently
+    o2 = o.copy()
+    o2[:, 0] *= 100.0
+    o2[:, 2] = np.random.Generator(np.random.PCG64(3)).standard_normal((T, d))
+    if rel(f(o2, gate, w, eps)[:, 1], f(o, gate, w, eps)[:, 1]) > 1e-13:
+        bad.append("per-head")
+    # 8. feature permutation equivariance
+    perm = np.random.Generator(np.random.PCG64(5)).permutation(d)
+    if rel(f(o[..., perm], gate[..., perm], w[:, perm], eps), f(o, gate, w, eps)[..., perm]) > 1e-13:
+        bad.append("permutation")
+    return bad
+
+
+def test_norm_gate_passes_pins():
+    assert norm_gate_pin_failures(oracle.norm_gate) == []
+
+
+def _ng_mutant(mistake):
+    def f(o, gate, weight, eps):
+        o = np.asarray(o, np.float64)
+        g = np.asarray(gate, np.float64)
+        w = np.asarray(weight, np.float64)
+        x = o - o.mean(axis=-1, keepdims=True) if mistake == "layernorm" else o
+        if mistake == "l2":
+            den = np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+        elif mistake == "all_heads":
+            den = np.sqrt(np.mean(x * x, axis=(-2, -1), keepdims=True) + eps)
+        elif mistake == "no_eps":
+            den = np.sqrt(np.mean(x * x, axis=-1, keepdims=True))
+        elif mistake == "eps_outside":
+            den = np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) + eps
+        else:
+            den = np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+        if mistake == "tanh":
+            act = np.tanh(g)
+        elif mistake == "gate_sign":
+            act = 1.0 / (1.0 + np.exp(g))
+        else:
+            act = 1.0 / (1.0 + np.exp(-g))
+        wt = w[::-1] if mistake == "weight_heads_reversed" else w
+        return x / den * wt * act
+    return f
+
+
+@pytest.mark.parametrize("mistake", ["layernorm", "l2", "all_heads", "no_eps", "eps_outside",
+                                     "tanh", "gate_sign", "weight_heads_reversed"])
+def test_norm_gate_mutants_fail_pins(mistake):
+    with np.errstate(all="ignore"):
+        assert norm_gate_pin_failures(_ng_mutant(mistake)), mistake
+
+
+def test_norm_gate_unmutated_mutant_passes():
+    assert norm_gate_pin_failures(_ng_mutant(None)) == []
+
+
+def test_norm_gate_of_decode_matches_prefill_rows():
+    """The epilogue of a decode step equals the epilogue of the matching prefill row."""
+    g = np.random.Generator(np.random.PCG64(21))
+    L, H, d = 9, 2, 8
+    q, k, v = (g.standard_normal((1, L, H, d)).astype(np.float32) for _ in range(3))
+    sl = np.array([0.3, 0.01], np.float32)
+    gate = g.standard_normal((L, H, d))
+    w = g.uniform(0.5, 2.0, (H, d))
+    o, _ = oracle.recurrence_batch(q, k, v, sl)
+    y_pre = oracle.norm_gate(o[0], gate, w, 1e-6)
+    st = np.zeros((1, H, d, d))
+    for t in range(L):
+        ot, st = oracle.decode(q[:, t], k[:, t], v[:, t], sl, st)
+        assert rel(oracle.norm_gate(ot[0], gate[t], w, 1e-6), y_pre[t]) < 1e-12
