@@ -14,6 +14,8 @@ Prints ONE JSON line. Besides the driver's fields it carries:
   decode        the batched decode step (256 sequences x 64 heads, 1 GiB fp32
                 state updated in place), per-step HIP-event times over the run,
                 state-stream GB/s against 8 TB/s;
+  norm_gate     the same prefill and decode with the normalisation and gate
+                fused into the epilogue (bf16 gate, bf16 y);
   cpu_baseline  the fp64 oracle on the host cores, timed on the same prefill
                 workload (reported baseline, not a target).
 
@@ -127,7 +129,53 @@ def run_prefill(la, torch, steps, warmup):
     }
 
 
-def run_decode(la, torch, nsteps, warmup=5):
+def run_prefill_norm_gate(la, torch, steps, warmup):
+    """lt_prefill_norm_gate on the M1 layer: bf16 q, k, v and gate, bf16 y, fp32
+    final state; algorithmic bytes 3*256 + 256 + 256 = 1,280 B per token-head."""
+    import numpy as np
+
+    import workloads
+
+    w = workloads.M1_LAYER
+    shape = (w.batch, w.seqlen, w.heads, w.head_dim)
+    q, k, v = workloads.qkv_device(w.seed, shape, "bf16")
+    gate = workloads.gate_device(w.seed + 10, shape, "bf16")
+    nw = torch.from_numpy(workloads.norm_weight_host(w.seed + 11, w.heads)).cuda()
+    slopes = torch.from_numpy(workloads.slopes(w.heads)).cuda()
+    y = torch.empty(shape, device="cuda", dtype=torch.bfloat16)
+    st = torch.empty((w.batch, w.heads, D, D), device="cuda", dtype=torch.float32)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        la.lt_prefill_norm_gate(q, k, v, slopes, gate, nw, workloads.NORM_EPS, w.block, y=y,
+                                state_out=st, stream=stream)
+    for _ in range(warmup):
+        call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    assert bool(torch.isfinite(y[0, -1].float()).all()), "non-finite norm-gate output"
+    tokens = w.batch * w.seqlen
+    nbytes = tokens * w.heads * D * (3 * 2 + 2 + 2) + w.batch * w.heads * D * D * 4
+    gbs = nbytes / (ms / 1e3) / 1e9
+    return {"workload": w.name + " + norm_gate", "gate_dtype": "bf16", "out_dtype": "bf16",
+            "tokens_per_s": round(tokens / (ms / 1e3), 1), "kernel_ms_mean": round(ms, 5),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "bytes_per_launch": nbytes,
+                         "kernel": "lt_prefill_norm_gate call: piece_state_kernel + combine_kernel "
+                                   "+ head_kernel<bf16, norm-gate>"}}
+
+
+def run_decode(la, torch, nsteps, warmup=5, norm_gate=False):
+    """Batched decode steps (norm_gate: lt_decode_norm_gate with bf16 gate and
+    bf16 y, the same algorithmic bytes as the plain step with fp32 o)."""
     import numpy as np
 
     import workloads
@@ -148,23 +196,36 @@ def run_decode(la, torch, nsteps, warmup=5):
     qkv = (torch.randn((nsteps + warmup, 3, B, H, D), generator=g, device="cuda")
            .mul_(workloads.INPUT_SCALE).to(torch.bfloat16))
     slopes = torch.from_numpy(workloads.slopes(H)).cuda()
-    o = torch.empty((B, H, D), device="cuda", dtype=torch.float32)
     stream = torch.cuda.current_stream()
+    if norm_gate:
+        gates = workloads.gate_device(w.seed + 2, (nsteps + warmup, B, H, D), "bf16")
+        nw = torch.from_numpy(workloads.norm_weight_host(w.seed + 3, H)).cuda()
+        o = torch.empty((B, H, D), device="cuda", dtype=torch.bfloat16)
+
+        def step(i):
+            x = qkv[i]
+            la.lt_decode_norm_gate(x[0], x[1], x[2], slopes, state, gates[i], nw,
+                                   workloads.NORM_EPS, y=o, stream=stream)
+    else:
+        o = torch.empty((B, H, D), device="cuda", dtype=torch.float32)
+
+        def step(i):
+            x = qkv[i]
+            la.lt_decode(x[0], x[1], x[2], slopes, state, o=o, stream=stream)
     for i in range(warmup):
-        la.lt_decode(qkv[i, 0], qkv[i, 1], qkv[i, 2], slopes, state, o=o, stream=stream)
+        step(i)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(nsteps)]
     for i, (a, b) in enumerate(ev):
-        x = qkv[warmup + i]
         a.record(stream)
-        la.lt_decode(x[0], x[1], x[2], slopes, state, o=o, stream=stream)
+        step(warmup + i)
         b.record(stream)
     torch.cuda.synchronize()
     ms = np.array([a.elapsed_time(b) for a, b in ev])
     assert bool(torch.isfinite(o).all()), "non-finite decode output"
     med = float(np.median(ms))
-    nbytes = decode_bytes(B, H)
+    nbytes = decode_bytes(B, H) if not norm_gate else B * H * (2 * D * D * 4 + 4 * D * 2 + D * 2)
     gbs = nbytes / (med / 1e3) / 1e9
     return {
         "workload": w.name, "batch": B, "heads": H, "head_dim": D, "steps": nsteps,
@@ -174,7 +235,8 @@ def run_decode(la, torch, nsteps, warmup=5):
         "ms_per_step_p90": round(float(np.percentile(ms, 90)), 5),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "bytes_per_launch": nbytes, "kernel": "decode_kernel<bf16, f32>"},
+                     "bytes_per_launch": nbytes,
+                     "kernel": "decode_kernel<bf16, bf16, norm-gate>" if norm_gate else "decode_kernel<bf16, f32>"},
         "state": "Gaussian stand-in with the per-head scale of a 4096-token prefill state",
     }
 
@@ -334,6 +396,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=32768)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-norm-gate", action="store_true")
+    ap.add_argument("--norm-gate-decode-steps", type=int, default=200)
     ap.add_argument("--workload", default="m1_layer",
                     choices=["m1_layer", "long_1m", "varlen", "tiny_f32"])
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
@@ -374,6 +438,14 @@ def main():
         log(f"[bench] decode batch=256 H=64, {args.decode_steps} steps")
         dec = run_decode(la, torch, args.decode_steps)
         log(f"[bench] decode {dec['ms_per_step_median']:.4f} ms/step")
+    ng = None
+    if not args.no_norm_gate:
+        log("[bench] prefill + norm_gate m1_layer (bf16 gate, bf16 y)")
+        ng = {"prefill": run_prefill_norm_gate(la, torch, args.steps, args.warmup)}
+        log(f"[bench] prefill + norm_gate {ng['prefill']['kernel_ms_mean']:.3f} ms/launch")
+        if not args.no_decode:
+            ng["decode"] = run_decode(la, torch, args.norm_gate_decode_steps, norm_gate=True)
+            log(f"[bench] decode + norm_gate {ng['decode']['ms_per_step_median']:.4f} ms/step")
     cpu = None
     if not args.no_cpu:
         log(f"[bench] cpu oracle on {args.cpu_tokens} tokens")
@@ -398,6 +470,7 @@ def main():
         "roofline": pre["roofline"],
         "kernel_ms_mean": round(pre["kernel_ms_mean"], 5),
         "decode": dec,
+        "norm_gate": ng,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -18,8 +18,9 @@
  * "⊙" with a length-B vector scales token rows. The value of O and of the final
  * state does not depend on B: the block form is an exact re-association of the
  * per-token recurrence S <- e^{-s_h} S + k^T v, o = q S (the token sees its own
- * key). The output is the raw sum; normalisation and gating come after this
- * operator and are not part of it.
+ * key). lt_prefill, lt_prefill_varlen and lt_decode write the raw sum; the
+ * *_norm_gate variants also apply the normalisation and gate that follow the
+ * sum in the §03 data-flow figure before anything is stored.
  *
  * Conventions shared by every entry point
  *  - Every pointer argument except `stream` is a DEVICE pointer (HBM). The
@@ -65,7 +66,8 @@ typedef enum {
     LT_ERR_BLOCK = 3,     /* block size out of range */
     LT_ERR_DTYPE = 4,     /* unsupported dtype code */
     LT_ERR_ALIAS = 5,     /* an output overlaps another buffer */
-    LT_ERR_HIP = 6        /* the HIP runtime reported an error at launch */
+    LT_ERR_HIP = 6,       /* the HIP runtime reported an error at launch */
+    LT_ERR_VALUE = 7      /* a scalar argument is out of range (eps of the norm-gate variants) */
 } lt_status;
 
 typedef enum { LT_F32 = 0, LT_BF16 = 1 } lt_dtype;
@@ -157,6 +159,53 @@ LT_API lt_status lt_prefill_varlen(const void *q, const void *k, const void *v, 
 LT_API lt_status lt_decode(const void *q, const void *k, const void *v, lt_dtype in_dtype,
                            const float *slopes, float *state, void *o, lt_dtype out_dtype,
                            int batch, int heads, int head_dim, void *stream);
+
+/*
+ * lt_prefill_norm_gate, lt_prefill_varlen_norm_gate, lt_decode_norm_gate -
+ * the operator above followed, inside the same kernels, by the step the §03
+ * data-flow figure places after the sum (the summed output is normalised and
+ * gated). The pages give no formula; this library's reading, per (token, head):
+ *
+ *     y = o / sqrt(mean_d(o^2) + eps) * norm_weight[h] * sigmoid(gate)
+ *
+ * where o = O_intra + O_inter (never written to memory), the mean runs over
+ * the head_dim features, sigmoid(x) = 1 / (1 + e^{-x}), and
+ *
+ *   gate         o's shape ([batch, seqlen, heads, head_dim], [total_tokens,
+ *                heads, head_dim] or [batch, heads, head_dim]) in in_dtype.
+ *   norm_weight  [heads, head_dim] fp32.
+ *   eps          finite, >= 0; otherwise LT_ERR_VALUE. With eps = 0 a zero
+ *                output row gives NaN, as the formula does.
+ *   y            takes the place of o (same shape, out_dtype).
+ *
+ * Every other argument, the state handling and the workspace are those of
+ * lt_prefill / lt_prefill_varlen / lt_decode. The prefill variants take bf16
+ * inputs only (LT_ERR_DTYPE for LT_F32); the decode variant takes both. y must
+ * not overlap gate or norm_weight, nor may state_out / state (LT_ERR_ALIAS).
+ * Errors: those of the base entry point, plus LT_ERR_VALUE.
+ */
+LT_API lt_status lt_prefill_norm_gate(const void *q, const void *k, const void *v,
+                                      lt_dtype in_dtype, const float *slopes, const void *gate,
+                                      const float *norm_weight, float eps, void *y,
+                                      lt_dtype out_dtype, const float *state_in, float *state_out,
+                                      int batch, long long seqlen, int heads, int head_dim,
+                                      int block, void *workspace, size_t workspace_bytes,
+                                      void *stream);
+
+LT_API lt_status lt_prefill_varlen_norm_gate(const void *q, const void *k, const void *v,
+                                             lt_dtype in_dtype, const int *cu_seqlens,
+                                             int num_seqs, long long total_tokens,
+                                             const float *slopes, const void *gate,
+                                             const float *norm_weight, float eps, void *y,
+                                             lt_dtype out_dtype, const float *state_in,
+                                             float *state_out, int heads, int head_dim, int block,
+                                             void *stream);
+
+LT_API lt_status lt_decode_norm_gate(const void *q, const void *k, const void *v,
+                                     lt_dtype in_dtype, const float *slopes, float *state,
+                                     const void *gate, const float *norm_weight, float eps,
+                                     void *y, lt_dtype out_dtype, int batch, int heads,
+                                     int head_dim, void *stream);
 
 #ifdef __cplusplus
 }

@@ -14,15 +14,16 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "liblightning.so")
 
-LT_OK, LT_ERR_NULL, LT_ERR_SHAPE, LT_ERR_BLOCK, LT_ERR_DTYPE, LT_ERR_ALIAS, LT_ERR_HIP = range(7)
+LT_OK, LT_ERR_NULL, LT_ERR_SHAPE, LT_ERR_BLOCK, LT_ERR_DTYPE, LT_ERR_ALIAS, LT_ERR_HIP, LT_ERR_VALUE = range(8)
 LT_F32, LT_BF16 = 0, 1
 LT_MAX_BLOCK = 65536
 HEAD_DIM = 128
 
 EXPORTS = ("lt_status_string", "lt_version", "lt_prefill", "lt_prefill_workspace_bytes",
-           "lt_prefill_varlen", "lt_decode")
+           "lt_prefill_varlen", "lt_decode", "lt_prefill_norm_gate", "lt_prefill_varlen_norm_gate",
+           "lt_decode_norm_gate")
 
-_vp, _i, _ll = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong
+_vp, _i, _ll, _f = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_float
 
 
 class LightningError(RuntimeError):
@@ -51,6 +52,15 @@ def _load() -> ctypes.CDLL:
     lib.lt_prefill_varlen.restype = _i
     lib.lt_decode.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _vp]
     lib.lt_decode.restype = _i
+    lib.lt_prefill_norm_gate.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _f, _vp, _i, _vp, _vp,
+                                         _i, _ll, _i, _i, _i, _vp, ctypes.c_size_t, _vp]
+    lib.lt_prefill_norm_gate.restype = _i
+    lib.lt_prefill_varlen_norm_gate.argtypes = [_vp, _vp, _vp, _i, _vp, _i, _ll, _vp, _vp, _vp, _f,
+                                                _vp, _i, _vp, _vp, _i, _i, _i, _vp]
+    lib.lt_prefill_varlen_norm_gate.restype = _i
+    lib.lt_decode_norm_gate.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _f, _vp, _i, _i, _i,
+                                        _i, _vp]
+    lib.lt_decode_norm_gate.restype = _i
     return lib
 
 
@@ -187,3 +197,102 @@ def lt_decode(q, k, v, slopes, state, *, o=None, out_dtype=None, stream=None):
                        _dtype_code(o.dtype), batch, H, d, _stream(stream, q.device))
     _check(st, "lt_decode")
     return o
+
+
+def _check_gate(gate, like, norm_weight, heads):
+    torch = _torch()
+    if tuple(gate.shape) != tuple(like.shape) or gate.dtype != like.dtype:
+        raise ValueError("gate must have the shape and dtype of q")
+    if norm_weight.dtype != torch.float32 or tuple(norm_weight.shape) != (heads, HEAD_DIM):
+        raise ValueError("norm_weight must be float32 [heads, 128]")
+
+
+def lt_prefill_norm_gate(q, k, v, slopes, gate, norm_weight, eps, block, state_in=None, *, y=None,
+                         state_out=None, want_state=True, out_dtype=None, workspace=None,
+                         stream=None):
+    """Fixed-length prefill followed by y = rmsnorm(o) * norm_weight * sigmoid(gate) per
+    (token, head). q, k, v, gate: bf16 [batch, L, H, 128]; norm_weight: fp32 [H, 128].
+
+    Returns (y [batch, L, H, 128], state_out or None); other arguments as lt_prefill.
+    """
+    torch = _torch()
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [batch, L, H, d] shape")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    batch, L, H, d = q.shape
+    _check_gate(gate, q, norm_weight, H)
+    out_dtype = out_dtype or torch.float32
+    if y is None:
+        y = torch.empty((batch, L, H, d), device=q.device, dtype=out_dtype)
+    if state_out is None and want_state:
+        state_out = torch.empty((batch, H, d, d), device=q.device, dtype=torch.float32)
+    if workspace is None:
+        nbytes = lt_prefill_workspace_bytes(batch, L, H, d, _dtype_code(q.dtype))
+        if nbytes:
+            workspace = torch.empty(nbytes, device=q.device, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.lt_prefill_norm_gate(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                                  _dtype_code(q.dtype), _dev_ptr(slopes, "slopes"),
+                                  _dev_ptr(gate, "gate"), _dev_ptr(norm_weight, "norm_weight"),
+                                  float(eps), _dev_ptr(y, "y"), _dtype_code(y.dtype),
+                                  _dev_ptr(state_in, "state_in"), _dev_ptr(state_out, "state_out"),
+                                  batch, L, H, d, int(block), _dev_ptr(workspace, "workspace"),
+                                  ws_bytes, _stream(stream, q.device))
+    _check(st, "lt_prefill_norm_gate")
+    return y, state_out
+
+
+def lt_prefill_varlen_norm_gate(q, k, v, cu_seqlens, slopes, gate, norm_weight, eps, block,
+                                state_in=None, *, y=None, state_out=None, want_state=True,
+                                out_dtype=None, stream=None):
+    """Packed variable-length prefill followed by the norm-gate epilogue.
+    q, k, v, gate: bf16 [T, H, 128]; other arguments as lt_prefill_varlen.
+
+    Returns (y [T, H, 128], state_out [n, H, 128, 128] or None).
+    """
+    torch = _torch()
+    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [T, H, d] shape")
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    T, H, d = q.shape
+    _check_gate(gate, q, norm_weight, H)
+    n = cu_seqlens.numel() - 1
+    out_dtype = out_dtype or torch.float32
+    if y is None:
+        y = torch.empty((T, H, d), device=q.device, dtype=out_dtype)
+    if state_out is None and want_state:
+        state_out = torch.empty((n, H, d, d), device=q.device, dtype=torch.float32)
+    st = lib.lt_prefill_varlen_norm_gate(
+        _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dtype_code(q.dtype),
+        _dev_ptr(cu_seqlens, "cu_seqlens"), n, T, _dev_ptr(slopes, "slopes"),
+        _dev_ptr(gate, "gate"), _dev_ptr(norm_weight, "norm_weight"), float(eps),
+        _dev_ptr(y, "y"), _dtype_code(y.dtype), _dev_ptr(state_in, "state_in"),
+        _dev_ptr(state_out, "state_out"), H, d, int(block), _stream(stream, q.device))
+    _check(st, "lt_prefill_varlen_norm_gate")
+    return y, state_out
+
+
+def lt_decode_norm_gate(q, k, v, slopes, state, gate, norm_weight, eps, *, y=None, out_dtype=None,
+                        stream=None):
+    """One decode step followed by the norm-gate epilogue. q, k, v, gate: [batch, H, 128];
+    state: [batch, H, 128, 128] fp32, updated in place. Returns y [batch, H, 128].
+    """
+    torch = _torch()
+    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [batch, H, d] shape")
+    batch, H, d = q.shape
+    _check_gate(gate, q, norm_weight, H)
+    if state.dtype != torch.float32 or tuple(state.shape) != (batch, H, d, d):
+        raise ValueError("state must be float32 [batch, H, d, d]")
+    out_dtype = out_dtype or torch.float32
+    if y is None:
+        y = torch.empty((batch, H, d), device=q.device, dtype=out_dtype)
+    st = lib.lt_decode_norm_gate(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                                 _dtype_code(q.dtype), _dev_ptr(slopes, "slopes"),
+                                 _dev_ptr(state, "state"), _dev_ptr(gate, "gate"),
+                                 _dev_ptr(norm_weight, "norm_weight"), float(eps), _dev_ptr(y, "y"),
+                                 _dtype_code(y.dtype), batch, H, d, _stream(stream, q.device))
+    _check(st, "lt_decode_norm_gate")
+    return y

@@ -5,7 +5,9 @@
 // state directly instead of rescanning history; §04: the state does not grow):
 //     S <- e^{-s} S + k^T v ;   o = q S
 // The output reads the updated state, as the per-token form of §03 does (the
-// block diagonal D_ii = 1 lets a token see its own key).
+// block diagonal D_ii = 1 lets a token see its own key). Optionally the output
+// is normalised and gated before it is stored (the step after the sum in the
+// §03 data-flow figure).
 //
 // The step is a pure HBM stream: 64 KiB of state read and 64 KiB written per
 // (sequence, head) for about 5 * 128^2 flops, 0.62 flop per byte. Design:
@@ -58,7 +60,18 @@ __device__ __forceinline__ void store4(__bf16 *p, float4 x) {
     *reinterpret_cast<bf16x4 *>(p) = y;
 }
 
-template <typename G, typename OutT>
+__device__ __forceinline__ float4 load4_in(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+__device__ __forceinline__ float4 load4_in(const uint16_t *p) {
+    const uint2 w = *reinterpret_cast<const uint2 *>(p);
+    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+}
+__device__ __forceinline__ float sigmoid(float g) {
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-g * LOG2E));
+}
+
+// NG: write y = o / sqrt(mean(o^2) + eps) * w * sigmoid(g) instead of o.
+template <typename G, typename OutT, bool NG>
 __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     __shared__ float qs[D], ks[D];
     __shared__ float4 part[4][D / 4];
@@ -83,6 +96,11 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     const float4 v4 = make_float4(load_in(v, 4 * cg), load_in(v, 4 * cg + 1),
                                   load_in(v, 4 * cg + 2), load_in(v, 4 * cg + 3));
     const float lam = exp2f(-a.slopes[h] * LOG2E);
+    float4 gate4 = make_float4(0.f, 0.f, 0.f, 0.f), w4 = gate4;
+    if (NG && tid < 32) {
+        gate4 = load4_in(static_cast<const G *>(a.ng.gate) + (long long)unit * D + 4 * tid);
+        w4 = *reinterpret_cast<const float4 *>(a.ng.norm_weight + h * D + 4 * tid);
+    }
     __syncthreads();
 
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -118,6 +136,14 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
             o.z += part[j][tid].z;
             o.w += part[j][tid].w;
         }
+        if constexpr (NG) {
+            float ss = o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
+#pragma unroll
+            for (int m = 16; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+            const float inv = __builtin_amdgcn_rsqf(ss * (1.f / D) + a.ng.eps);
+            o = make_float4(o.x * inv * w4.x * sigmoid(gate4.x), o.y * inv * w4.y * sigmoid(gate4.y),
+                            o.z * inv * w4.z * sigmoid(gate4.z), o.w * inv * w4.w * sigmoid(gate4.w));
+        }
         store4(static_cast<OutT *>(a.o) + (long long)unit * D + 4 * tid, o);
     }
 }
@@ -125,7 +151,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
 template <typename G, typename OutT>
 hipError_t launch(const DecodeArgs &a, hipStream_t stream) {
     const long long units = (long long)a.batch * a.heads;
-    hipLaunchKernelGGL((decode_kernel<G, OutT>), dim3((unsigned)units), dim3(NT), 0, stream, a);
+    if (a.ng.gate)
+        hipLaunchKernelGGL((decode_kernel<G, OutT, true>), dim3((unsigned)units), dim3(NT), 0, stream, a);
+    else
+        hipLaunchKernelGGL((decode_kernel<G, OutT, false>), dim3((unsigned)units), dim3(NT), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -11,6 +11,16 @@ namespace lt {
 // One prefill launch: `units` independent sequences x `heads` heads.
 // Fixed-length batches leave cu_seqlens NULL and use seqlen; packed batches
 // pass cu_seqlens (device int32, units + 1 entries) and total_tokens.
+// Optional epilogue after O = O_intra + O_inter: with gate != nullptr the
+// kernels write y = o / sqrt(mean_d(o^2) + eps) * norm_weight[h] * sigmoid(g)
+// per (token, head) instead of o; gate has o's shape in the input dtype,
+// norm_weight is fp32 [heads, d].
+struct NormGate {
+    const void *gate = nullptr;
+    const float *norm_weight = nullptr;
+    float eps = 0.f;
+};
+
 struct PrefillArgs {
     const void *q, *k, *v;
     const float *slopes;
@@ -22,6 +32,7 @@ struct PrefillArgs {
     long long total_tokens;
     int units;
     int heads;
+    NormGate ng;
 };
 
 struct DecodeArgs {
@@ -31,6 +42,7 @@ struct DecodeArgs {
     void *o;
     int batch;
     int heads;
+    NormGate ng;
 };
 
 // Head dimension the kernels are built for.

@@ -55,11 +55,14 @@ lt_status launch(const lt::PrefillArgs &a, int in_dtype, int out_dtype, bool var
         return map_hip(lt::launch_prefill_slices(a, (lt_dtype)in_dtype, (lt_dtype)out_dtype, st));
     lt::PrefillPlan p = lt::plan_prefill(a.units, varlen ? a.total_tokens : a.seqlen, a.heads,
                                          (lt_dtype)in_dtype, varlen);
-    // Without the workspace the segmented plan needs, split value columns instead.
-    if (p.workspace > 0 && (!workspace || workspace_bytes < p.workspace)) {
+    // Without the workspace the segmented plan needs, split value columns instead;
+    // the norm-gate epilogue needs whole output rows, so it keeps one workgroup
+    // per (sequence, head) rather than value slices.
+    const bool no_ws = p.workspace > 0 && (!workspace || workspace_bytes < p.workspace);
+    if (no_ws || (a.ng.gate && p.value_slices != 1)) {
         p = lt::PrefillPlan{};
         p.seg_len = varlen ? a.total_tokens : a.seqlen;
-        p.value_slices = lt::kValueSlices;
+        if (!a.ng.gate) p.value_slices = lt::kValueSlices;
     }
     return map_hip(lt::launch_prefill_heads(a, p, workspace, (lt_dtype)out_dtype, st));
 }
@@ -96,6 +99,21 @@ lt_status check_prefill(const void *q, const void *k, const void *v, int in_dtyp
     if (overlaps(rso, rq) || overlaps(rso, rk) || overlaps(rso, rv) || overlaps(rso, rs))
         return LT_ERR_ALIAS;
     if (state_in && state_out && state_in != state_out && overlaps(rsi, rso))
+        return LT_ERR_ALIAS;
+    return LT_OK;
+}
+
+// Checks of the norm-gate variants: eps, the gate and weight pointers (needed
+// when there are tokens), and overlap of the outputs with them.
+lt_status check_norm_gate(const void *gate, long long gate_bytes, const float *norm_weight,
+                          float eps, int heads, int head_dim, const void *y, long long y_bytes,
+                          const float *state_out, long long st_bytes) {
+    if (!(eps >= 0.f) || eps == __builtin_inff()) return LT_ERR_VALUE;  // NaN fails eps >= 0
+    if (gate_bytes > 0 && (!gate || !norm_weight)) return LT_ERR_NULL;
+    const Range rg = range_of(gate, gate_bytes),
+                rw = range_of(norm_weight, norm_weight ? (long long)heads * head_dim * 4 : 0),
+                ry = range_of(y, y_bytes), rs = range_of(state_out, state_out ? st_bytes : 0);
+    if (overlaps(ry, rg) || overlaps(ry, rw) || overlaps(rs, rg) || overlaps(rs, rw))
         return LT_ERR_ALIAS;
     return LT_OK;
 }
@@ -166,50 +184,74 @@ LT_API const char *lt_status_string(int status) {
         case LT_ERR_DTYPE: return "LT_ERR_DTYPE: unsupported dtype";
         case LT_ERR_ALIAS: return "LT_ERR_ALIAS: an output overlaps another buffer";
         case LT_ERR_HIP: return "LT_ERR_HIP: HIP runtime error at launch";
+        case LT_ERR_VALUE: return "LT_ERR_VALUE: a scalar argument is out of range";
         default: return "unknown lt_status";
     }
 }
 
-LT_API int lt_version(void) { return 10000; }
+LT_API int lt_version(void) { return 10100; }
 
-LT_API lt_status lt_prefill(const void *q, const void *k, const void *v, lt_dtype in_dtype,
-                            const float *slopes, void *o, lt_dtype out_dtype,
-                            const float *state_in, float *state_out,
-                            int batch, long long seqlen, int heads, int head_dim, int block,
-                            void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+lt_status prefill_impl(const void *q, const void *k, const void *v, lt_dtype in_dtype,
+                       const float *slopes, void *o, lt_dtype out_dtype, const float *state_in,
+                       float *state_out, int batch, long long seqlen, int heads, int head_dim,
+                       int block, void *workspace, size_t workspace_bytes, void *stream,
+                       const lt::NormGate *ng) {
     if (batch < 0 || seqlen < 0) return LT_ERR_SHAPE;
     long long tokens;
     if (__builtin_mul_overflow((long long)batch, seqlen, &tokens)) return LT_ERR_SHAPE;
     lt_status st = check_prefill(q, k, v, in_dtype, slopes, o, out_dtype, state_in, state_out,
                                  batch, tokens, heads, head_dim, block);
-    if (st != LT_OK || batch == 0 || heads == 0) return st;
+    if (st != LT_OK) return st;
+    const long long in_b = tokens * heads * head_dim * dtype_size(in_dtype);
+    const long long st_b = (long long)batch * heads * head_dim * head_dim * 4;
+    if (ng) {
+        if (in_dtype != LT_BF16) return LT_ERR_DTYPE;
+        st = check_norm_gate(ng->gate, in_b, ng->norm_weight, ng->eps, heads, head_dim, o,
+                             tokens * heads * head_dim * dtype_size(out_dtype), state_out, st_b);
+        if (st != LT_OK) return st;
+    }
+    if (batch == 0 || heads == 0) return LT_OK;
     if (workspace && workspace_bytes > 0) {
         const Range rw = range_of(workspace, (long long)workspace_bytes);
-        const long long in_b = tokens * heads * head_dim * dtype_size(in_dtype);
-        const long long st_b = (long long)batch * heads * head_dim * head_dim * 4;
         if (overlaps(rw, range_of(q, in_b)) || overlaps(rw, range_of(k, in_b)) ||
             overlaps(rw, range_of(v, in_b)) || overlaps(rw, range_of(slopes, heads * 4LL)) ||
             overlaps(rw, range_of(o, tokens * heads * head_dim * dtype_size(out_dtype))) ||
             (state_in && overlaps(rw, range_of(state_in, st_b))) ||
-            (state_out && overlaps(rw, range_of(state_out, st_b))))
+            (state_out && overlaps(rw, range_of(state_out, st_b))) ||
+            (ng && (overlaps(rw, range_of(ng->gate, in_b)) ||
+                    overlaps(rw, range_of(ng->norm_weight, (long long)heads * head_dim * 4)))))
             return LT_ERR_ALIAS;
     }
     if (tokens == 0 && !state_out) return LT_OK;
     lt::PrefillArgs a{q, k, v, slopes, o, state_in, state_out, nullptr, seqlen, tokens,
                       batch, heads};
+    if (ng) a.ng = *ng;
     return launch(a, in_dtype, out_dtype, false, workspace, workspace_bytes, stream);
 }
 
-LT_API lt_status lt_prefill_varlen(const void *q, const void *k, const void *v, lt_dtype in_dtype,
-                                   const int *cu_seqlens, int num_seqs, long long total_tokens,
-                                   const float *slopes, void *o, lt_dtype out_dtype,
-                                   const float *state_in, float *state_out,
-                                   int heads, int head_dim, int block, void *stream) {
+lt_status varlen_impl(const void *q, const void *k, const void *v, lt_dtype in_dtype,
+                      const int *cu_seqlens, int num_seqs, long long total_tokens,
+                      const float *slopes, void *o, lt_dtype out_dtype, const float *state_in,
+                      float *state_out, int heads, int head_dim, int block, void *stream,
+                      const lt::NormGate *ng) {
     if (num_seqs < 0 || total_tokens < 0) return LT_ERR_SHAPE;
     if (total_tokens > 0x7fffffffLL) return LT_ERR_SHAPE;  // int32 sequence boundaries
     lt_status st = check_prefill(q, k, v, in_dtype, slopes, o, out_dtype, state_in, state_out,
                                  num_seqs, total_tokens, heads, head_dim, block);
-    if (st != LT_OK || num_seqs == 0 || heads == 0) return st;
+    if (st != LT_OK) return st;
+    if (ng) {
+        if (in_dtype != LT_BF16) return LT_ERR_DTYPE;
+        st = check_norm_gate(ng->gate, total_tokens * heads * head_dim * dtype_size(in_dtype),
+                             ng->norm_weight, ng->eps, heads, head_dim, o,
+                             total_tokens * heads * head_dim * dtype_size(out_dtype), state_out,
+                             (long long)num_seqs * heads * head_dim * head_dim * 4);
+        if (st != LT_OK) return st;
+    }
+    if (num_seqs == 0 || heads == 0) return LT_OK;
     if (!cu_seqlens) return LT_ERR_NULL;
     if (overlaps(range_of(cu_seqlens, (long long)(num_seqs + 1) * 4),
                  range_of(o, total_tokens * heads * head_dim * dtype_size(out_dtype))) ||
@@ -220,22 +262,28 @@ LT_API lt_status lt_prefill_varlen(const void *q, const void *k, const void *v, 
     if (total_tokens == 0 && !state_out) return LT_OK;
     lt::PrefillArgs a{q, k, v, slopes, o, state_in, state_out, cu_seqlens, 0, total_tokens,
                       num_seqs, heads};
+    if (ng) a.ng = *ng;
     return launch(a, in_dtype, out_dtype, true, nullptr, 0, stream);
 }
 
-LT_API lt_status lt_decode(const void *q, const void *k, const void *v, lt_dtype in_dtype,
-                           const float *slopes, float *state, void *o, lt_dtype out_dtype,
-                           int batch, int heads, int head_dim, void *stream) {
+lt_status decode_impl(const void *q, const void *k, const void *v, lt_dtype in_dtype,
+                      const float *slopes, float *state, void *o, lt_dtype out_dtype, int batch,
+                      int heads, int head_dim, void *stream, const lt::NormGate *ng) {
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return LT_ERR_DTYPE;
     if (head_dim != lt::kHeadDim || heads < 0 || heads > LT_MAX_HEADS || batch < 0)
         return LT_ERR_SHAPE;
-    if (batch == 0 || heads == 0) return LT_OK;
-    if (!q || !k || !v || !slopes || !state || !o) return LT_ERR_NULL;
     long long units = (long long)batch * heads;
     if (units > 0x7fffffffLL) return LT_ERR_SHAPE;
     const long long in_bytes = units * head_dim * dtype_size(in_dtype);
     const long long out_bytes = units * head_dim * dtype_size(out_dtype);
     const long long st_bytes = units * head_dim * head_dim * 4;
+    if (ng) {
+        const lt_status st = check_norm_gate(ng->gate, in_bytes, ng->norm_weight, ng->eps, heads,
+                                             head_dim, o, out_bytes, state, st_bytes);
+        if (st != LT_OK) return st;
+    }
+    if (batch == 0 || heads == 0) return LT_OK;
+    if (!q || !k || !v || !slopes || !state || !o) return LT_ERR_NULL;
     const Range rq = range_of(q, in_bytes), rk = range_of(k, in_bytes),
                 rv = range_of(v, in_bytes), ro = range_of(o, out_bytes),
                 rs = range_of(slopes, (long long)heads * 4), rst = range_of(state, st_bytes);
@@ -244,7 +292,72 @@ LT_API lt_status lt_decode(const void *q, const void *k, const void *v, lt_dtype
         overlaps(rst, rs))
         return LT_ERR_ALIAS;
     lt::DecodeArgs a{q, k, v, slopes, state, o, batch, heads};
+    if (ng) a.ng = *ng;
     return map_hip(lt::launch_decode(a, in_dtype, out_dtype, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+LT_API lt_status lt_prefill(const void *q, const void *k, const void *v, lt_dtype in_dtype,
+                            const float *slopes, void *o, lt_dtype out_dtype,
+                            const float *state_in, float *state_out,
+                            int batch, long long seqlen, int heads, int head_dim, int block,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+    return prefill_impl(q, k, v, in_dtype, slopes, o, out_dtype, state_in, state_out, batch, seqlen,
+                        heads, head_dim, block, workspace, workspace_bytes, stream, nullptr);
+}
+
+LT_API lt_status lt_prefill_norm_gate(const void *q, const void *k, const void *v,
+                                      lt_dtype in_dtype, const float *slopes, const void *gate,
+                                      const float *norm_weight, float eps, void *y,
+                                      lt_dtype out_dtype, const float *state_in, float *state_out,
+                                      int batch, long long seqlen, int heads, int head_dim,
+                                      int block, void *workspace, size_t workspace_bytes,
+                                      void *stream) {
+    const lt::NormGate ng{gate, norm_weight, eps};
+    return prefill_impl(q, k, v, in_dtype, slopes, y, out_dtype, state_in, state_out, batch, seqlen,
+                        heads, head_dim, block, workspace, workspace_bytes, stream, &ng);
+}
+
+LT_API lt_status lt_prefill_varlen(const void *q, const void *k, const void *v, lt_dtype in_dtype,
+                                   const int *cu_seqlens, int num_seqs, long long total_tokens,
+                                   const float *slopes, void *o, lt_dtype out_dtype,
+                                   const float *state_in, float *state_out,
+                                   int heads, int head_dim, int block, void *stream) {
+    return varlen_impl(q, k, v, in_dtype, cu_seqlens, num_seqs, total_tokens, slopes, o, out_dtype,
+                       state_in, state_out, heads, head_dim, block, stream, nullptr);
+}
+
+LT_API lt_status lt_prefill_varlen_norm_gate(const void *q, const void *k, const void *v,
+                                             lt_dtype in_dtype, const int *cu_seqlens,
+                                             int num_seqs, long long total_tokens,
+                                             const float *slopes, const void *gate,
+                                             const float *norm_weight, float eps, void *y,
+                                             lt_dtype out_dtype, const float *state_in,
+                                             float *state_out, int heads, int head_dim, int block,
+                                             void *stream) {
+    const lt::NormGate ng{gate, norm_weight, eps};
+    return varlen_impl(q, k, v, in_dtype, cu_seqlens, num_seqs, total_tokens, slopes, y, out_dtype,
+                       state_in, state_out, heads, head_dim, block, stream, &ng);
+}
+
+LT_API lt_status lt_decode(const void *q, const void *k, const void *v, lt_dtype in_dtype,
+                           const float *slopes, float *state, void *o, lt_dtype out_dtype,
+                           int batch, int heads, int head_dim, void *stream) {
+    return decode_impl(q, k, v, in_dtype, slopes, state, o, out_dtype, batch, heads, head_dim,
+                       stream, nullptr);
+}
+
+LT_API lt_status lt_decode_norm_gate(const void *q, const void *k, const void *v,
+                                     lt_dtype in_dtype, const float *slopes, float *state,
+                                     const void *gate, const float *norm_weight, float eps,
+                                     void *y, lt_dtype out_dtype, int batch, int heads,
+                                     int head_dim, void *stream) {
+    const lt::NormGate ng{gate, norm_weight, eps};
+    return decode_impl(q, k, v, in_dtype, slopes, state, y, out_dtype, batch, heads, head_dim,
+                       stream, &ng);
 }
 
 }  // extern "C"

@@ -285,6 +285,50 @@ __device__ __forceinline__ void store_rows(__bf16 *out, long long ts, const floa
     }
 }
 
+// Rows [0, m) of the staged tile with the post-sum normalisation and gate:
+// y = o / sqrt(mean(o^2) + eps) * w * sigmoid(g). Thread layout as the fp32
+// store_rows (rows (tid/32) + 16j, columns 4(tid%32)..+3). Each row's sum of
+// squares comes from rss[row][0..3], the partial sums of its four 32-column
+// blocks that the waves wrote from their accumulators (row_sumsq). gr[j] holds
+// the four bf16 gate values of row j, w the four weights of the thread's columns.
+__device__ __forceinline__ void put4(float *p, float4 y) { stream_store(p, y); }
+__device__ __forceinline__ void put4(__bf16 *p, float4 y) {
+    const bf16x4 b = {static_cast<__bf16>(y.x), static_cast<__bf16>(y.y), static_cast<__bf16>(y.z),
+                      static_cast<__bf16>(y.w)};
+    stream_store_bits(p, b);
+}
+__device__ __forceinline__ float sigmoid(float g) {
+    return __builtin_amdgcn_rcpf(1.f + fast_exp2(-g * LOG2E));
+}
+
+// The wave's output block holds, per lane, 16 of the 32 columns (value block
+// 32cq..) of query row 32qh + lane%32; lanes l and l^32 hold the other 16.
+__device__ __forceinline__ void row_sumsq(float *rss, const f32x16 &o, int qh, int cq, int lane) {
+    float ss = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) ss += o[v] * o[v];
+    ss += __shfl_xor(ss, 32);
+    if (lane < 32) rss[(32 * qh + lane) * 4 + cq] = ss;
+}
+
+template <bool FULL, typename OutT>
+__device__ __forceinline__ void store_rows_norm_gate(OutT *out, long long ts, const float *Os,
+                                                     const float *rss, int m, int tid,
+                                                     const uint2 (&gr)[4], float4 w, float eps) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = (tid >> 5) + 16 * j, col = 4 * (tid & 31);
+        const float4 x = *reinterpret_cast<const float4 *>(Os + ooff(row, col));
+        const float4 p = *reinterpret_cast<const float4 *>(rss + 4 * row);
+        const float inv = __builtin_amdgcn_rsqf((p.x + p.y + p.z + p.w) * (1.f / D) + eps);
+        const float g0 = __uint_as_float(gr[j].x << 16), g1 = __uint_as_float(gr[j].x & 0xffff0000u);
+        const float g2 = __uint_as_float(gr[j].y << 16), g3 = __uint_as_float(gr[j].y & 0xffff0000u);
+        const float4 y = make_float4(x.x * inv * w.x * sigmoid(g0), x.y * inv * w.y * sigmoid(g1),
+                                     x.z * inv * w.z * sigmoid(g2), x.w * inv * w.w * sigmoid(g3));
+        if (FULL || row < m) put4(out + row * ts + col, y);
+    }
+}
+
 struct SeqRange {
     long long start, len;
 };
@@ -447,7 +491,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(PrefillArgs a,
 }
 
 // ---------------------------------------------------------------------------
-template <typename OutT>
+template <typename OutT, bool NG>
 __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, float *ws) {
     __shared__ __attribute__((aligned(16))) __bf16 Qs[C * D];
     __shared__ __attribute__((aligned(16))) __bf16 Ks[C * D];
@@ -476,6 +520,13 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
     const uint16_t *vg = static_cast<const uint16_t *>(a.v) + base;
     OutT *og = static_cast<OutT *>(a.o) + base;
     const float s2 = a.slopes[h] * LOG2E;
+    // epilogue: gate rows of this (sequence, head) and the head's normalisation
+    // weights, kept in LDS (read after the first barrier B)
+    __shared__ __attribute__((aligned(16))) float Wn[NG ? D : 1];
+    __shared__ __attribute__((aligned(16))) float Rss[NG ? C * 4 : 1];  // per-row partial sums of o^2
+    const uint16_t *gg = NG ? static_cast<const uint16_t *>(a.ng.gate) + base : nullptr;
+    if (NG && tid < D / 4)
+        *reinterpret_cast<float4 *>(Wn + 4 * tid) = *reinterpret_cast<const float4 *>(a.ng.norm_weight + h * D + 4 * tid);
 
     // ---- carried-in state of this segment (the combine pass wrote it for
     // segmented plans, so an in-place state update never races with it)
@@ -540,6 +591,16 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
         constexpr bool FULL = decltype(full)::value;
         st.template store<FULL>(Qs, Ks, Vs, Vds, m, s2, tid);
         if (FULL) prefetch(st, c + 2);
+        // gate rows of this sub-block, consumed by the epilogue at its end
+        uint2 gr[4];
+        if constexpr (NG) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = (tid >> 5) + 16 * j;
+                const int rr = FULL || row < m ? row : m - 1;
+                gr[j] = stream_load8(gg + (c * C + rr) * (long long)ts + 4 * (tid & 31));
+            }
+        }
         __syncthreads();  // (B) tiles and S^T of the previous sub-block are visible
         if (scorer) {
             // scores^T block: keys 32kb.., queries 32qb.. ; masked, decayed, to LDS as P
@@ -580,8 +641,13 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
         }
         float *Os = reinterpret_cast<float *>(Sts[cur]);
         stage_out(Os, o, qh, cq, lane);
+        if constexpr (NG) row_sumsq(Rss, o, qh, cq, lane);
         __syncthreads();  // (D)
-        store_rows<FULL>(og + c * C * (long long)ts, ts, Os, m, tid);
+        if constexpr (NG)
+            store_rows_norm_gate<FULL>(og + c * C * (long long)ts, ts, Os, Rss, m, tid, gr,
+                                       *reinterpret_cast<const float4 *>(Wn + 4 * (tid & 31)), a.ng.eps);
+        else
+            store_rows<FULL>(og + c * C * (long long)ts, ts, Os, m, tid);
         cur ^= 1;
     };
     long long c = 0;
@@ -834,6 +900,8 @@ __global__ __launch_bounds__(NT) void slice_kernel(PrefillArgs a) {
 template <typename OutT>
 hipError_t launch(const PrefillArgs &a, const PrefillPlan &p, void *workspace, hipStream_t stream) {
     const long long uh = (long long)a.units * a.heads;
+    // a value-slice workgroup sees 32 of a row's 128 columns: no row epilogue
+    if (p.value_slices == NSL && a.ng.gate) return hipErrorInvalidValue;
     if (p.value_slices == NSL) {
         hipLaunchKernelGGL((slice_kernel<OutT>), dim3((unsigned)(uh * NSL)), dim3(NT), 0, stream, a);
         return hipGetLastError();
@@ -850,8 +918,12 @@ hipError_t launch(const PrefillArgs &a, const PrefillPlan &p, void *workspace, h
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((head_kernel<OutT>), dim3((unsigned)(uh * p.segments)), dim3(NT), 0, stream,
-                       a, sp, ws);
+    if (a.ng.gate)
+        hipLaunchKernelGGL((head_kernel<OutT, true>), dim3((unsigned)(uh * p.segments)), dim3(NT), 0,
+                           stream, a, sp, ws);
+    else
+        hipLaunchKernelGGL((head_kernel<OutT, false>), dim3((unsigned)(uh * p.segments)), dim3(NT), 0,
+                           stream, a, sp, ws);
     return hipGetLastError();
 }
 

@@ -46,12 +46,13 @@ def test_only_the_abi_is_exported():
 
 
 def test_status_strings():
-    for code in range(7):
-        assert la.status_string(code).startswith(
-            ["LT_OK", "LT_ERR_NULL", "LT_ERR_SHAPE", "LT_ERR_BLOCK", "LT_ERR_DTYPE",
-             "LT_ERR_ALIAS", "LT_ERR_HIP"][code])
+    names = ["LT_OK", "LT_ERR_NULL", "LT_ERR_SHAPE", "LT_ERR_BLOCK", "LT_ERR_DTYPE",
+             "LT_ERR_ALIAS", "LT_ERR_HIP", "LT_ERR_VALUE"]
+    for code, name in enumerate(names):
+        assert la.status_string(code).startswith(name)
+        assert getattr(la, name) == code
     assert la.status_string(99) == "unknown lt_status"
-    assert la.lib.lt_version() == 10000
+    assert la.lib.lt_version() == 10100
 
 
 def prefill(**kw):
@@ -169,3 +170,78 @@ def test_decode_checks():
     assert decode(state=A + 512) == la.LT_ERR_ALIAS              # state over q
     assert decode(batch=0) == la.LT_OK
     assert decode(heads=0) == la.LT_OK
+
+
+# --------------------------------------------------------------------------
+# norm-gate variants: the base checks plus eps, gate / weight pointers, overlap
+# --------------------------------------------------------------------------
+
+def prefill_ng(**kw):
+    args = dict(q=A, k=A + 100 * MB, v=A + 200 * MB, in_dtype=la.LT_BF16, slopes=A + 300 * MB,
+                gate=A + 310 * MB, weight=A + 350 * MB, eps=1e-6, y=A + 400 * MB,
+                out_dtype=la.LT_F32, state_in=None, state_out=A + 900 * MB, batch=1, seqlen=64,
+                heads=2, head_dim=128, block=64, workspace=None, workspace_bytes=0, stream=None)
+    args.update(kw)
+    return la.lib.lt_prefill_norm_gate(*args.values())
+
+
+def varlen_ng(**kw):
+    args = dict(q=A, k=A + 100 * MB, v=A + 200 * MB, in_dtype=la.LT_BF16, cu=A + 290 * MB,
+                num_seqs=2, total=64, slopes=A + 300 * MB, gate=A + 310 * MB, weight=A + 350 * MB,
+                eps=1e-6, y=A + 400 * MB, out_dtype=la.LT_F32, state_in=None,
+                state_out=A + 900 * MB, heads=2, head_dim=128, block=64, stream=None)
+    args.update(kw)
+    return la.lib.lt_prefill_varlen_norm_gate(*args.values())
+
+
+def decode_ng(**kw):
+    args = dict(q=A, k=A + MB, v=A + 2 * MB, in_dtype=la.LT_BF16, slopes=A + 3 * MB,
+                state=A + 4 * MB, gate=A + 20 * MB, weight=A + 30 * MB, eps=1e-6,
+                y=A + 100 * MB, out_dtype=la.LT_F32, batch=2, heads=2, head_dim=128, stream=None)
+    args.update(kw)
+    return la.lib.lt_decode_norm_gate(*args.values())
+
+
+@pytest.mark.parametrize("call", [prefill_ng, varlen_ng, decode_ng])
+@pytest.mark.parametrize("eps", [-1e-6, float("nan"), float("inf")])
+def test_norm_gate_bad_eps(call, eps):
+    assert call(eps=eps) == la.LT_ERR_VALUE
+
+
+@pytest.mark.parametrize("call", [prefill_ng, varlen_ng, decode_ng])
+@pytest.mark.parametrize("field", ["gate", "weight"])
+def test_norm_gate_null_pointers(call, field):
+    assert call(**{field: None}) == la.LT_ERR_NULL
+
+
+@pytest.mark.parametrize("call", [prefill_ng, varlen_ng])
+def test_norm_gate_prefill_takes_bf16_only(call):
+    assert call(in_dtype=la.LT_F32) == la.LT_ERR_DTYPE
+    assert call(in_dtype=9) == la.LT_ERR_DTYPE
+
+
+def test_norm_gate_alias_checks():
+    assert prefill_ng(y=A + 310 * MB + 64) == la.LT_ERR_ALIAS          # y inside gate (32 KiB)
+    assert prefill_ng(weight=A + 400 * MB) == la.LT_ERR_ALIAS          # weight on y
+    assert prefill_ng(state_out=A + 350 * MB) == la.LT_ERR_ALIAS       # state_out on weight
+    assert prefill_ng(workspace=A + 310 * MB, workspace_bytes=64) == la.LT_ERR_ALIAS  # on gate
+    assert varlen_ng(y=A + 310 * MB) == la.LT_ERR_ALIAS
+    assert decode_ng(y=A + 20 * MB) == la.LT_ERR_ALIAS                 # y on gate
+    assert decode_ng(state=A + 30 * MB) == la.LT_ERR_ALIAS             # state on weight
+
+
+def test_norm_gate_base_checks_still_apply():
+    assert prefill_ng(q=None) == la.LT_ERR_NULL
+    assert prefill_ng(block=0) == la.LT_ERR_BLOCK
+    assert prefill_ng(head_dim=64) == la.LT_ERR_SHAPE
+    assert varlen_ng(cu=None) == la.LT_ERR_NULL
+    assert decode_ng(state=None) == la.LT_ERR_NULL
+    assert decode_ng(out_dtype=5) == la.LT_ERR_DTYPE
+
+
+def test_norm_gate_noops_need_no_gpu():
+    assert prefill_ng(batch=0) == la.LT_OK
+    assert prefill_ng(heads=0) == la.LT_OK
+    assert prefill_ng(seqlen=0, state_out=None, gate=None, weight=None) == la.LT_OK
+    assert varlen_ng(num_seqs=0, total=0) == la.LT_OK
+    assert decode_ng(batch=0, gate=None, weight=None) == la.LT_OK

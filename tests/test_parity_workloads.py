@@ -62,6 +62,31 @@ def test_m1_layer_all_heads(la):
     assert worst_o <= TOL_BF16 and worst_s <= TOL_BF16
 
 
+def test_m1_layer_norm_gate_all_heads(la):
+    """The M1 layer through lt_prefill_norm_gate (bf16 gate and y), every head."""
+    import torch
+
+    w = workloads.M1_LAYER
+    print(f"[case] {w.name} norm_gate L={w.seqlen} H={w.heads}", flush=True)
+    shape = (1, w.seqlen, w.heads, 128)
+    q, k, v = workloads.qkv_device(w.seed, shape, "bf16")
+    gate = workloads.gate_device(w.seed + 10, shape, "bf16")
+    nw = workloads.norm_weight_host(w.seed + 11, w.heads)
+    sl = workloads.slopes(w.heads)
+    y, st = la.lt_prefill_norm_gate(q, k, v, torch.from_numpy(sl).cuda(), gate,
+                                    torch.from_numpy(nw).cuda(), workloads.NORM_EPS, w.block,
+                                    out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    hq, hk, hv = (to_host_f32(x) for x in (q, k, v))
+    o_ref, s_ref = oracle.recurrence_batch(hq, hk, hv, sl)
+    y_ref = oracle.norm_gate(o_ref, to_host_f32(gate), nw, workloads.NORM_EPS)
+    y_g, s_g = to_host_f32(y), to_host_f32(st)
+    worst_y = max(rel_l2(y_g[0, :, h], y_ref[0, :, h]) for h in range(w.heads))
+    worst_s = max(rel_l2(s_g[0, h], s_ref[0, h]) for h in range(w.heads))
+    print(f"[result] worst rel L2: y {worst_y:.3e} state {worst_s:.3e}", flush=True)
+    assert worst_y <= TOL_BF16 and worst_s <= TOL_BF16
+
+
 def test_long_context_1m_sampled_heads(la):
     import torch
 

@@ -131,3 +131,27 @@ def state_device(seed: int, shape, std: float = 0.1, device="cuda"):
     g.manual_seed(seed)
     x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
     return x.mul_(std)
+
+
+# Inputs of the norm-gate epilogue (normalisation and gate after the sum): gate
+# pre-activations N(0, 1) in the input dtype, weights U[0.5, 1.5] fp32 [H, d],
+# eps 1e-6.
+NORM_EPS = 1e-6
+
+
+def gate_host(seed: int, shape, dtype: str = "bf16") -> np.ndarray:
+    x = rng(seed).standard_normal(shape, dtype=np.float32)
+    return round_bf16(x) if dtype == "bf16" else x
+
+
+def norm_weight_host(seed: int, heads: int, d: int = HEAD_DIM) -> np.ndarray:
+    return rng(seed).uniform(0.5, 1.5, (heads, d)).astype(np.float32)
+
+
+def gate_device(seed: int, shape, dtype: str = "bf16", device="cuda"):
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    return x.to(torch.bfloat16) if dtype == "bf16" else x
