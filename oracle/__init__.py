@@ -19,6 +19,9 @@ Three independent formulations of the same operator, all in fp64:
 ``block_form``
     The §03 block decomposition itself, step by step in the pages' notation
     (``D``, ``d_q``, ``d_k``, block decay, last short block of length ``m``).
+``decode_slots``
+    One decode step over a pool of per-sequence states addressed by slot ids
+    (concurrent sequences, each with the fixed-size state of §04).
 ``norm_gate``
     The step after the operator in the §03 data-flow figure: the summed output
     is normalised and gated (RMS normalisation per (token, head), a weight per
@@ -283,3 +286,29 @@ def norm_gate(o, gate, weight, eps):
     w = np.asarray(weight, np.float64)
     ms = np.mean(o * o, axis=-1, keepdims=True)
     return o / np.sqrt(ms + np.float64(eps)) * w * (1.0 / (1.0 + np.exp(-g)))
+
+
+def decode_slots(q, k, v, slopes, pool, slot_ids):
+    """One decode step of `batch` sequences whose states live in a pool.
+
+    MiniMax Signal Lab · M1, §04: every concurrent sequence keeps its own
+    fixed-size state (d x d fp32 per head), so a serving batch addresses a pool
+    of such states. Sequence b reads and updates pool[slot_ids[b]] with one
+    step of the recurrence; an id outside [0, num_slots) marks a padding row:
+    its output is zero and the pool is untouched.
+
+    q, k, v: [batch, H, d]; pool: [num_slots, H, d, d]; slot_ids: [batch] int.
+    Returns (o [batch, H, d] fp64, new_pool [num_slots, H, d, d] fp64).
+    """
+    pool = np.array(pool, dtype=np.float64)
+    ids = np.asarray(slot_ids, np.int64)
+    bsz, H, d = np.shape(q)
+    o = np.zeros((bsz, H, d))
+    live = [b for b in range(bsz) if 0 <= ids[b] < pool.shape[0]]
+    if live:
+        sl = ids[live]
+        ob, sb = decode(np.asarray(q)[live], np.asarray(k)[live], np.asarray(v)[live], slopes,
+                        pool[sl])
+        o[live] = ob
+        pool[sl] = sb
+    return o, pool

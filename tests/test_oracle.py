@@ -481,3 +481,49 @@ def test_norm_gate_of_decode_matches_prefill_rows():
     for t in range(L):
         ot, st = oracle.decode(q[:, t], k[:, t], v[:, t], sl, st)
         assert rel(oracle.norm_gate(ot[0], gate[t], w, 1e-6), y_pre[t]) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# Decode over a state pool (oracle.decode_slots)
+# --------------------------------------------------------------------------
+
+def _slot_inputs(seed, B=4, H=2, d=8, slots=6):
+    g = np.random.Generator(np.random.PCG64(seed))
+    q, k, v = (g.standard_normal((B, H, d)).astype(np.float32) for _ in range(3))
+    pool = g.standard_normal((slots, H, d, d))
+    sl = np.array([0.2, 0.01], np.float32)[:H]
+    return q, k, v, sl, pool
+
+
+def test_decode_slots_identity_equals_decode():
+    q, k, v, sl, pool = _slot_inputs(31, slots=4)
+    o, new = oracle.decode_slots(q, k, v, sl, pool, np.arange(4))
+    o2, st2 = oracle.decode(q, k, v, sl, pool)
+    assert rel(o, o2) < 1e-14 and rel(new, st2) < 1e-14
+
+
+def test_decode_slots_padding_and_untouched_slots():
+    q, k, v, sl, pool = _slot_inputs(32)
+    ids = np.array([4, -1, 1, 6])           # -1 and 6 (= num_slots) are padding
+    o, new = oracle.decode_slots(q, k, v, sl, pool, ids)
+    assert np.all(o[1] == 0.0) and np.all(o[3] == 0.0)
+    for s_ in (0, 2, 3, 5):                 # slots nobody addressed
+        assert np.array_equal(new[s_], pool[s_])
+    # the live rows: one step of the recurrence on their own slot (brute-force one-token form)
+    for b, s_ in ((0, 4), (2, 1)):
+        for h in range(q.shape[1]):
+            S = (np.exp(-np.float64(sl[h])) * pool[s_, h]
+                 + np.outer(k[b, h].astype(np.float64), v[b, h].astype(np.float64)))
+            assert rel(new[s_, h], S) < 1e-13
+            assert rel(o[b, h], q[b, h].astype(np.float64) @ S) < 1e-13
+
+
+def test_decode_slots_relabelling_invariance():
+    """Permuting the pool and the ids the same way permutes the result."""
+    q, k, v, sl, pool = _slot_inputs(33)
+    ids = np.array([5, 0, 3, 2])
+    perm = np.random.Generator(np.random.PCG64(34)).permutation(pool.shape[0])
+    inv = np.argsort(perm)
+    o1, p1 = oracle.decode_slots(q, k, v, sl, pool, ids)
+    o2, p2 = oracle.decode_slots(q, k, v, sl, pool[perm], inv[ids])
+    assert rel(o1, o2) < 1e-14 and rel(p1, p2[inv]) < 1e-14
