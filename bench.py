@@ -173,9 +173,11 @@ def run_prefill_norm_gate(la, torch, steps, warmup):
                                    "+ head_kernel<bf16, norm-gate>"}}
 
 
-def run_decode(la, torch, nsteps, warmup=5, norm_gate=False):
+def run_decode(la, torch, nsteps, warmup=5, norm_gate=False, slots=0):
     """Batched decode steps (norm_gate: lt_decode_norm_gate with bf16 gate and
-    bf16 y, the same algorithmic bytes as the plain step with fp32 o)."""
+    bf16 y, the same algorithmic bytes as the plain step with fp32 o; slots > 0:
+    lt_decode_slots with the batch's states scattered over a pool of that many
+    slots, same algorithmic bytes plus 4 B of slot id per sequence)."""
     import numpy as np
 
     import workloads
@@ -189,7 +191,7 @@ def run_decode(la, torch, nsteps, warmup=5, norm_gate=False):
     s = torch.from_numpy(workloads.slopes(H)).double()
     lam2 = torch.exp(-2 * s)
     std = torch.sqrt((1 - lam2 ** w.extra["history"]) / (1 - lam2)) / D
-    state = workloads.state_device(w.seed, (B, H, D, D), std=1.0)
+    state = workloads.state_device(w.seed, (max(B, slots), H, D, D), std=1.0)
     state.mul_(std.float().cuda().view(1, H, 1, 1))
     g = torch.Generator(device="cuda")
     g.manual_seed(w.seed + 1)
@@ -197,7 +199,16 @@ def run_decode(la, torch, nsteps, warmup=5, norm_gate=False):
            .mul_(workloads.INPUT_SCALE).to(torch.bfloat16))
     slopes = torch.from_numpy(workloads.slopes(H)).cuda()
     stream = torch.cuda.current_stream()
-    if norm_gate:
+    if slots:
+        import numpy as _np
+        ids = torch.from_numpy(_np.random.Generator(_np.random.PCG64(w.seed + 4))
+                               .permutation(slots)[:B].astype(_np.int32)).cuda()
+        o = torch.empty((B, H, D), device="cuda", dtype=torch.float32)
+
+        def step(i):
+            x = qkv[i]
+            la.lt_decode_slots(x[0], x[1], x[2], slopes, state, ids, o=o, stream=stream)
+    elif norm_gate:
         gates = workloads.gate_device(w.seed + 2, (nsteps + warmup, B, H, D), "bf16")
         nw = torch.from_numpy(workloads.norm_weight_host(w.seed + 3, H)).cuda()
         o = torch.empty((B, H, D), device="cuda", dtype=torch.bfloat16)
@@ -226,9 +237,11 @@ def run_decode(la, torch, nsteps, warmup=5, norm_gate=False):
     assert bool(torch.isfinite(o).all()), "non-finite decode output"
     med = float(np.median(ms))
     nbytes = decode_bytes(B, H) if not norm_gate else B * H * (2 * D * D * 4 + 4 * D * 2 + D * 2)
+    nbytes += 4 * B if slots else 0
     gbs = nbytes / (med / 1e3) / 1e9
     return {
-        "workload": w.name, "batch": B, "heads": H, "head_dim": D, "steps": nsteps,
+        "workload": w.name + (f" over a {slots}-slot state pool" if slots else ""),
+        "batch": B, "heads": H, "head_dim": D, "steps": nsteps,
         "steps_per_s": round(1e3 / med, 1),
         "ms_per_step_median": round(med, 5),
         "ms_per_step_p10": round(float(np.percentile(ms, 10)), 5),
@@ -236,7 +249,8 @@ def run_decode(la, torch, nsteps, warmup=5, norm_gate=False):
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "bytes_per_launch": nbytes,
-                     "kernel": "decode_kernel<bf16, bf16, norm-gate>" if norm_gate else "decode_kernel<bf16, f32>"},
+                     "kernel": ("decode_kernel<bf16, bf16, norm-gate>" if norm_gate else
+                                "decode_kernel<bf16, f32, slots>" if slots else "decode_kernel<bf16, f32>")},
         "state": "Gaussian stand-in with the per-head scale of a 4096-token prefill state",
     }
 
@@ -438,6 +452,8 @@ def main():
         log(f"[bench] decode batch=256 H=64, {args.decode_steps} steps")
         dec = run_decode(la, torch, args.decode_steps)
         log(f"[bench] decode {dec['ms_per_step_median']:.4f} ms/step")
+        dec["slots"] = run_decode(la, torch, args.norm_gate_decode_steps, slots=512)
+        log(f"[bench] decode over 512 slots {dec['slots']['ms_per_step_median']:.4f} ms/step")
     ng = None
     if not args.no_norm_gate:
         log("[bench] prefill + norm_gate m1_layer (bf16 gate, bf16 y)")

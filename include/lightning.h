@@ -161,6 +161,26 @@ LT_API lt_status lt_decode(const void *q, const void *k, const void *v, lt_dtype
                            int batch, int heads, int head_dim, void *stream);
 
 /*
+ * lt_decode_slots - lt_decode for sequences whose states live in a pool, as a
+ * server holding many concurrent sequences keeps them (§04: each sequence
+ * carries its own fixed d x d fp32 state per head, whatever its length).
+ *
+ *   state_pool  [num_slots, heads, head_dim, head_dim] fp32, updated in place.
+ *   slot_ids    [batch] int32 on the device: sequence b reads and updates
+ *               state_pool[slot_ids[b]]. An id < 0 or >= num_slots marks a
+ *               padding row: its o is zero and no state is touched. Valid ids
+ *               must be distinct within one call (two rows on one slot race).
+ *               Ids are read on the device only.
+ *   q, k, v, o, slopes, dtypes: as lt_decode.
+ *   Errors: as lt_decode (LT_ERR_SHAPE also for num_slots < 0; LT_ERR_NULL for
+ *   a NULL slot_ids with batch > 0, or a NULL pool with num_slots > 0).
+ */
+LT_API lt_status lt_decode_slots(const void *q, const void *k, const void *v, lt_dtype in_dtype,
+                                 const float *slopes, float *state_pool, int num_slots,
+                                 const int *slot_ids, void *o, lt_dtype out_dtype, int batch,
+                                 int heads, int head_dim, void *stream);
+
+/*
  * lt_prefill_norm_gate, lt_prefill_varlen_norm_gate, lt_decode_norm_gate -
  * the operator above followed, inside the same kernels, by the step the §03
  * data-flow figure places after the sum (the summed output is normalised and

@@ -21,7 +21,7 @@ HEAD_DIM = 128
 
 EXPORTS = ("lt_status_string", "lt_version", "lt_prefill", "lt_prefill_workspace_bytes",
            "lt_prefill_varlen", "lt_decode", "lt_prefill_norm_gate", "lt_prefill_varlen_norm_gate",
-           "lt_decode_norm_gate")
+           "lt_decode_norm_gate", "lt_decode_slots")
 
 _vp, _i, _ll, _f = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_float
 
@@ -37,6 +37,14 @@ def _load() -> ctypes.CDLL:
         raise ImportError(
             f"{LIB_PATH} is not built; run `python -m linear_attention_amd.build` "
             "(the Lightning kernels have no fallback path)")
+    # PyTorch for ROCm ships its own HIP runtime. Loading torch first lets the
+    # library's libamdhip64.so.7 dependency resolve to that same runtime; loaded
+    # the other way round, the process would hold two HIP runtimes, and the one
+    # the library uses reports no device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     lib.lt_status_string.argtypes = [_i]
     lib.lt_status_string.restype = ctypes.c_char_p
@@ -61,6 +69,8 @@ def _load() -> ctypes.CDLL:
     lib.lt_decode_norm_gate.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _f, _vp, _i, _i, _i,
                                         _i, _vp]
     lib.lt_decode_norm_gate.restype = _i
+    lib.lt_decode_slots.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _vp]
+    lib.lt_decode_slots.restype = _i
     return lib
 
 
@@ -296,3 +306,27 @@ def lt_decode_norm_gate(q, k, v, slopes, state, gate, norm_weight, eps, *, y=Non
                                  _dtype_code(y.dtype), batch, H, d, _stream(stream, q.device))
     _check(st, "lt_decode_norm_gate")
     return y
+
+
+def lt_decode_slots(q, k, v, slopes, state_pool, slot_ids, *, o=None, out_dtype=None, stream=None):
+    """One decode step over a state pool. q, k, v: [batch, H, 128]; state_pool:
+    [num_slots, H, 128, 128] fp32, updated in place; slot_ids: int32 [batch] on the
+    device (out-of-range ids are padding rows with zero output). Returns o [batch, H, 128].
+    """
+    torch = _torch()
+    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [batch, H, d] shape")
+    batch, H, d = q.shape
+    if state_pool.dtype != torch.float32 or state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H, d, d):
+        raise ValueError("state_pool must be float32 [num_slots, H, d, d]")
+    if slot_ids.dtype != torch.int32 or tuple(slot_ids.shape) != (batch,):
+        raise ValueError("slot_ids must be int32 [batch]")
+    out_dtype = out_dtype or torch.float32
+    if o is None:
+        o = torch.empty((batch, H, d), device=q.device, dtype=out_dtype)
+    st = lib.lt_decode_slots(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dtype_code(q.dtype),
+                             _dev_ptr(slopes, "slopes"), _dev_ptr(state_pool, "state_pool"),
+                             int(state_pool.shape[0]), _dev_ptr(slot_ids, "slot_ids"), _dev_ptr(o, "o"),
+                             _dtype_code(o.dtype), batch, H, d, _stream(stream, q.device))
+    _check(st, "lt_decode_slots")
+    return o

@@ -35,6 +35,9 @@ struct PrefillArgs {
     NormGate ng;
 };
 
+// Decode: state is [batch, heads, d, d], or with slot_ids != nullptr a pool
+// [num_slots, heads, d, d] in which sequence b uses entry slot_ids[b] (an id
+// outside [0, num_slots) marks a padding row: zero output, no state access).
 struct DecodeArgs {
     const void *q, *k, *v;
     const float *slopes;
@@ -43,6 +46,12 @@ struct DecodeArgs {
     int batch;
     int heads;
     NormGate ng;
+    const int *slot_ids = nullptr;
+    int num_slots = 0;
+    // Workgroup order: workgroup (b, h) serves sequence (b * seq_stride) % batch,
+    // a bijection (seq_stride is coprime with batch) that keeps the states of
+    // workgroups running at the same time far apart in memory.
+    int seq_stride = 1;
 };
 
 // Head dimension the kernels are built for.
@@ -75,6 +84,11 @@ struct PrefillPlan {
 // one per piece, one partial state per segment boundary, one carried-in state
 // per segment.
 constexpr long long prefill_states(int segments, int pieces) { return pieces + 2LL * segments - 1; }
+
+// HIP keeps the last error of any runtime call until it is read. Launchers
+// clear it first, so the check after a launch reports that launch only and not
+// an error some earlier call (the caller's, say) left behind.
+inline void clear_pending_error() { (void)hipGetLastError(); }
 
 PrefillPlan plan_prefill(long long units, long long seqlen, int heads, lt_dtype in_dtype,
                          bool varlen);

@@ -1,6 +1,8 @@
 // C-ABI front end: host-side argument checks, then one launch on the caller's
 // stream. Every check runs before any HIP call, so the error paths need no GPU.
 #include <cstdint>
+#include <cstdio>
+#include <numeric>
 
 #include "internal.h"
 #include "lightning.h"
@@ -35,7 +37,13 @@ bool mul4(long long a, long long b, long long c, long long d, long long *out) {
     return true;
 }
 
-lt_status map_hip(hipError_t e) { return e == hipSuccess ? LT_OK : LT_ERR_HIP; }
+// A failed launch is reported as LT_ERR_HIP; the HIP error itself goes to
+// stderr, the only place the status code cannot carry it.
+lt_status map_hip(hipError_t e) {
+    if (e == hipSuccess) return LT_OK;
+    std::fprintf(stderr, "liblightning: kernel launch failed: %s (%d)\n", hipGetErrorName(e), (int)e);
+    return LT_ERR_HIP;
+}
 
 // Workgroups a prefill launch should reach to occupy MI355X (256 CUs; the
 // whole-head kernel runs one 8-wave workgroup per CU).
@@ -101,6 +109,18 @@ lt_status check_prefill(const void *q, const void *k, const void *v, int in_dtyp
     if (state_in && state_out && state_in != state_out && overlaps(rsi, rso))
         return LT_ERR_ALIAS;
     return LT_OK;
+}
+
+// Stride of the decode workgroup order: the integer nearest 0.618 * batch
+// that is coprime with batch (so b -> b * stride mod batch is a bijection),
+// the golden-ratio step that keeps consecutive workgroups' states far apart.
+// Measured on the 256 x 64 batch: most strides give 0.357-0.361 ms per step,
+// sequence order 0.380 ms, and strides = +-1 mod 32 (31, 33) only 0.370 ms.
+int decode_seq_stride(int batch) {
+    if (batch < 8) return 1;
+    int p = (int)(0.6180339887 * batch + 0.5);
+    while (std::gcd(p, batch) != 1) ++p;
+    return p % batch;
 }
 
 // Checks of the norm-gate variants: eps, the gate and weight pointers (needed
@@ -266,33 +286,49 @@ lt_status varlen_impl(const void *q, const void *k, const void *v, lt_dtype in_d
     return launch(a, in_dtype, out_dtype, true, nullptr, 0, stream);
 }
 
+// Decode. With slot_ids, `state` is a pool of num_slots entries of
+// [heads, d, d] and sequence b uses entry slot_ids[b] (ids are read on the
+// device only; out-of-range ids are padding rows).
 lt_status decode_impl(const void *q, const void *k, const void *v, lt_dtype in_dtype,
                       const float *slopes, float *state, void *o, lt_dtype out_dtype, int batch,
-                      int heads, int head_dim, void *stream, const lt::NormGate *ng) {
+                      int heads, int head_dim, void *stream, const lt::NormGate *ng,
+                      const int *slot_ids = nullptr, int num_slots = -1) {
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return LT_ERR_DTYPE;
     if (head_dim != lt::kHeadDim || heads < 0 || heads > LT_MAX_HEADS || batch < 0)
         return LT_ERR_SHAPE;
+    const bool slots = num_slots >= 0;
     long long units = (long long)batch * heads;
     if (units > 0x7fffffffLL) return LT_ERR_SHAPE;
+    long long pool_units = units;
+    if (slots && __builtin_mul_overflow((long long)num_slots, (long long)heads, &pool_units))
+        return LT_ERR_SHAPE;
+    if (pool_units > 0x7fffffffLL) return LT_ERR_SHAPE;
     const long long in_bytes = units * head_dim * dtype_size(in_dtype);
     const long long out_bytes = units * head_dim * dtype_size(out_dtype);
-    const long long st_bytes = units * head_dim * head_dim * 4;
+    const long long st_bytes = pool_units * head_dim * head_dim * 4;
     if (ng) {
         const lt_status st = check_norm_gate(ng->gate, in_bytes, ng->norm_weight, ng->eps, heads,
                                              head_dim, o, out_bytes, state, st_bytes);
         if (st != LT_OK) return st;
     }
     if (batch == 0 || heads == 0) return LT_OK;
-    if (!q || !k || !v || !slopes || !state || !o) return LT_ERR_NULL;
+    if (!q || !k || !v || !slopes || !o || (!state && pool_units > 0) || (slots && !slot_ids))
+        return LT_ERR_NULL;
     const Range rq = range_of(q, in_bytes), rk = range_of(k, in_bytes),
                 rv = range_of(v, in_bytes), ro = range_of(o, out_bytes),
-                rs = range_of(slopes, (long long)heads * 4), rst = range_of(state, st_bytes);
+                rs = range_of(slopes, (long long)heads * 4), rst = range_of(state, st_bytes),
+                rid = range_of(slot_ids, slots ? (long long)batch * 4 : 0);
     if (overlaps(ro, rq) || overlaps(ro, rk) || overlaps(ro, rv) || overlaps(ro, rs) ||
         overlaps(ro, rst) || overlaps(rst, rq) || overlaps(rst, rk) || overlaps(rst, rv) ||
-        overlaps(rst, rs))
+        overlaps(rst, rs) || overlaps(ro, rid) || overlaps(rst, rid))
         return LT_ERR_ALIAS;
     lt::DecodeArgs a{q, k, v, slopes, state, o, batch, heads};
+    a.seq_stride = decode_seq_stride(batch);
     if (ng) a.ng = *ng;
+    if (slots) {
+        a.slot_ids = slot_ids;
+        a.num_slots = num_slots;
+    }
     return map_hip(lt::launch_decode(a, in_dtype, out_dtype, static_cast<hipStream_t>(stream)));
 }
 
@@ -348,6 +384,15 @@ LT_API lt_status lt_decode(const void *q, const void *k, const void *v, lt_dtype
                            int batch, int heads, int head_dim, void *stream) {
     return decode_impl(q, k, v, in_dtype, slopes, state, o, out_dtype, batch, heads, head_dim,
                        stream, nullptr);
+}
+
+LT_API lt_status lt_decode_slots(const void *q, const void *k, const void *v, lt_dtype in_dtype,
+                                 const float *slopes, float *state_pool, int num_slots,
+                                 const int *slot_ids, void *o, lt_dtype out_dtype, int batch,
+                                 int heads, int head_dim, void *stream) {
+    if (num_slots < 0) return LT_ERR_SHAPE;
+    return decode_impl(q, k, v, in_dtype, slopes, state_pool, o, out_dtype, batch, heads, head_dim,
+                       stream, nullptr, slot_ids, num_slots);
 }
 
 LT_API lt_status lt_decode_norm_gate(const void *q, const void *k, const void *v,

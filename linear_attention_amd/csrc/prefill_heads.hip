@@ -899,6 +899,7 @@ __global__ __launch_bounds__(NT) void slice_kernel(PrefillArgs a) {
 
 template <typename OutT>
 hipError_t launch(const PrefillArgs &a, const PrefillPlan &p, void *workspace, hipStream_t stream) {
+    clear_pending_error();
     const long long uh = (long long)a.units * a.heads;
     // a value-slice workgroup sees 32 of a row's 128 columns: no row epilogue
     if (p.value_slices == NSL && a.ng.gate) return hipErrorInvalidValue;

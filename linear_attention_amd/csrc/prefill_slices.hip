@@ -493,6 +493,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs a) {
 
 template <typename InT, typename OutT>
 hipError_t launch(const PrefillArgs &a, hipStream_t stream) {
+    clear_pending_error();
     const long long nwg = (long long)a.units * a.heads * NSL;
     hipLaunchKernelGGL((prefill_kernel<InT, OutT>), dim3((unsigned)nwg), dim3(NT), 0, stream, a);
     return hipGetLastError();

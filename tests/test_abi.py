@@ -245,3 +245,44 @@ def test_norm_gate_noops_need_no_gpu():
     assert prefill_ng(seqlen=0, state_out=None, gate=None, weight=None) == la.LT_OK
     assert varlen_ng(num_seqs=0, total=0) == la.LT_OK
     assert decode_ng(batch=0, gate=None, weight=None) == la.LT_OK
+
+
+# --------------------------------------------------------------------------
+# decode over a state pool
+# --------------------------------------------------------------------------
+
+def decode_slots(**kw):
+    args = dict(q=A, k=A + MB, v=A + 2 * MB, in_dtype=la.LT_BF16, slopes=A + 3 * MB,
+                pool=A + 10 * MB, num_slots=8, ids=A + 5 * MB, o=A + 200 * MB,
+                out_dtype=la.LT_F32, batch=4, heads=2, head_dim=128, stream=None)
+    args.update(kw)
+    return la.lib.lt_decode_slots(*args.values())
+
+
+def test_decode_slots_checks():
+    assert decode_slots(num_slots=-1) == la.LT_ERR_SHAPE
+    assert decode_slots(ids=None) == la.LT_ERR_NULL
+    assert decode_slots(pool=None) == la.LT_ERR_NULL
+    assert decode_slots(head_dim=64) == la.LT_ERR_SHAPE
+    assert decode_slots(in_dtype=3) == la.LT_ERR_DTYPE
+    assert decode_slots(o=A + 5 * MB) == la.LT_ERR_ALIAS            # o on slot_ids
+    assert decode_slots(ids=A + 10 * MB + 64) == la.LT_ERR_ALIAS     # ids inside the pool
+    assert decode_slots(o=A + 10 * MB + 4096) == la.LT_ERR_ALIAS     # o inside the pool (1 MiB)
+    assert decode_slots(batch=0) == la.LT_OK
+    assert decode_slots(heads=0) == la.LT_OK
+
+
+def test_one_hip_runtime_per_process():
+    """Touching the package before torch (as test collection does) must not
+    leave two HIP runtimes in the process (torch ships its own)."""
+    import subprocess
+    import sys
+
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import linear_attention_amd as la\n"
+            "la.LT_OK; la.lib\n"
+            "import torch\n"
+            "maps = open('/proc/self/maps').read()\n"
+            "print(len({l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l}))\n") % ROOT
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True)
+    assert out.stdout.strip().splitlines()[-1] == "1", out.stdout + out.stderr

@@ -361,3 +361,25 @@ def test_prefill_value_slice_bf16_output_in_place(la):
     cu = np.array([0, L])
     assert max_rel_per_head(to_host_f32(o)[0], o_ref[0], cu) <= TOL_BF16
     assert max_rel_states(to_host_f32(st), s_ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("B", [9, 37, 210])
+def test_decode_batches_with_strided_order(la, B):
+    """Decode visits sequences in a strided order for batch >= 8; every
+    (sequence, head) output and state against the oracle."""
+    import torch
+
+    H = 3
+    print(f"[case] decode B={B} H={H}", flush=True)
+    q, k, v = workloads.qkv_host(1100 + B, (B, H, 128), "bf16")
+    s0 = workloads.state_host(1200 + B, (B, H, 128, 128))
+    sl = workloads.slopes(H)
+    state = torch.from_numpy(s0).cuda()
+    o = la.lt_decode(to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16"),
+                     torch.from_numpy(sl).cuda(), state)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.decode(q, k, v, sl, s0)
+    og = to_host_f32(o)
+    eo = max(rel_l2(og[b, h], o_ref[b, h]) for b in range(B) for h in range(H))
+    es = max_rel_states(to_host_f32(state), s_ref)
+    assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)
