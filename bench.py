@@ -363,7 +363,10 @@ def traffic_from(copy_dir, fetch_dir, write_dir, copy_bytes):
     w_scale = copy_bytes / (copy_write_kib * 1024)
     kf = per_kernel(fetch_dir, "FETCH_SIZE")
     kw = per_kernel(write_dir, "WRITE_SIZE")
-    kernels = [k for k in kf if any(n in k for n in ("head_kernel", "piece_state_kernel", "combine_kernel", "slice_kernel"))]
+    # the plain call's kernels (the fused norm-gate call shares the pre-pass and
+    # combine, whose work is the same, but has its own main kernel)
+    kernels = [k for k in kf if any(n in k for n in ("head_kernel<float, false>", "piece_state_kernel",
+                                                      "combine_kernel"))]
     import numpy as np
 
     fetch = sum(float(np.median(kf[k])) for k in kernels) * 1024 * f_scale
