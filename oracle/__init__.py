@@ -19,6 +19,10 @@ Three independent formulations of the same operator, all in fp64:
 ``block_form``
     The §03 block decomposition itself, step by step in the pages' notation
     (``D``, ``d_q``, ``d_k``, block decay, last short block of length ``m``).
+``backward*``
+    Gradients of ``sum(dO * O) + <dS, S_final>`` with respect to q, k, v and
+    S0: the reverse-mode derivative of the per-token recurrence (compiled C;
+    the pages give no backward).
 ``decode_slots``
     One decode step over a pool of per-sequence states addressed by slot ids
     (concurrent sequences, each with the fixed-size state of §04).
@@ -74,18 +78,37 @@ class _Unit(ctypes.Structure):
     ]
 
 
+class _BwdUnit(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("dout", ctypes.c_void_p),
+        ("in_stride", ctypes.c_longlong),
+        ("len", ctypes.c_longlong),
+        ("slope", ctypes.c_double),
+        ("s0", ctypes.c_void_p),
+        ("ds", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+        ("o_stride", ctypes.c_longlong),
+        ("ds0", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
+        if (not os.path.exists(_LIB_PATH)
+                or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
             build()
         lib = ctypes.CDLL(_LIB_PATH)
         lib.lto_recurrence.argtypes = [ctypes.POINTER(_Unit), ctypes.c_int,
                                        ctypes.c_int, ctypes.c_int]
         lib.lto_recurrence.restype = ctypes.c_int
+        lib.lto_backward.argtypes = [ctypes.POINTER(_BwdUnit), ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_int]
+        lib.lto_backward.restype = ctypes.c_int
         lib.lto_max_threads.argtypes = []
         lib.lto_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -312,3 +335,66 @@ def decode_slots(q, k, v, slopes, pool, slot_ids):
         o[live] = ob
         pool[sl] = sb
     return o, pool
+
+
+def backward_packed(q, k, v, dout, slopes, cu_seqlens, s0=None, ds=None, threads=0):
+    """Gradients of the operator over packed sequences, every (sequence, head).
+
+    The loss is l = sum_t dout_t . o_t + <ds, S_final> per (sequence, head);
+    returns (dq, dk, dv [T, H, d] fp64, ds0 [n, H, d, d] fp64) with
+      dq_t = dout_t S_t^T,  G_t = q_t^T dout_t + e^{-s} G_{t+1} (G_L adds ds),
+      dk_t = G_t v_t,  dv_t = G_t^T k_t,  ds0 = e^{-s} G_1
+    (reverse-mode derivative of the per-token recurrence; the pages give no
+    backward). q, k, v, dout: [T, H, d] (read as float32); s0, ds: [n, H, d, d]
+    or None (zero).
+    """
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    T, H, d = q.shape
+    assert k.shape == q.shape and v.shape == q.shape and dout.shape == q.shape
+    slopes = np.asarray(slopes, dtype=np.float32)
+    cu = [int(x) for x in np.asarray(cu_seqlens).reshape(-1)]
+    n = len(cu) - 1
+    assert cu[0] == 0 and cu[-1] == T and all(b >= a for a, b in zip(cu, cu[1:]))
+    if s0 is not None:
+        s0 = np.ascontiguousarray(s0, dtype=np.float64)
+        assert s0.shape == (n, H, d, d)
+    if ds is not None:
+        ds = np.ascontiguousarray(ds, dtype=np.float64)
+        assert ds.shape == (n, H, d, d)
+    dq, dk, dv = (np.zeros((T, H, d), dtype=np.float64) for _ in range(3))
+    ds0 = np.zeros((n, H, d, d), dtype=np.float64)
+    units = (_BwdUnit * (n * H))()
+    f4, f8 = 4, 8
+    idx = 0
+    for si in range(n):
+        a, b = cu[si], cu[si + 1]
+        for h in range(H):
+            u = units[idx]
+            base = (a * H + h) * d * f4
+            u.q, u.k, u.v, u.dout = (x.ctypes.data + base for x in (q, k, v, dout))
+            u.in_stride = H * d
+            u.len = b - a
+            u.slope = float(slopes[h])
+            st = ((si * H + h) * d * d) * f8
+            u.s0 = (s0.ctypes.data + st) if s0 is not None else None
+            u.ds = (ds.ctypes.data + st) if ds is not None else None
+            ob = ((a * H + h) * d) * f8
+            u.dq, u.dk, u.dv = (x.ctypes.data + ob for x in (dq, dk, dv))
+            u.o_stride = H * d
+            u.ds0 = ds0.ctypes.data + st
+            idx += 1
+    if _load().lto_backward(units, n * H, d, int(threads)) != 0:
+        raise RuntimeError("lto_backward failed")
+    return dq, dk, dv, ds0
+
+
+def backward_batch(q, k, v, dout, slopes, s0=None, ds=None, threads=0):
+    """backward_packed for [batch, L, H, d] inputs; returns [batch, L, H, d]
+    gradients and [batch, H, d, d] ds0."""
+    q = np.asarray(q)
+    B, L, H, d = q.shape
+    cu = np.arange(B + 1) * L
+    flat = lambda x: np.asarray(x).reshape(B * L, H, d)
+    dq, dk, dv, ds0 = backward_packed(flat(q), flat(k), flat(v), flat(dout), slopes, cu,
+                                      s0=s0, ds=ds, threads=threads)
+    return dq.reshape(B, L, H, d), dk.reshape(B, L, H, d), dv.reshape(B, L, H, d), ds0

@@ -124,3 +124,111 @@ int lto_max_threads(void)
     return 1;
 #endif
 }
+
+/*
+ * Backward of the recurrence above (gradients of a scalar loss
+ *   l = sum_i dout_i . o_i + <ds, S_L>
+ * with respect to q, k, v and S_0). The pages give no backward; this is the
+ * plain reverse-mode derivative of the per-token recurrence:
+ *   dq_t = dout_t S_t^T                 (S_t: state after token t)
+ *   G_t  = q_t^T dout_t + e^{-s} G_{t+1},  G_L = q_L^T dout_L + ds
+ *   dk_t = G_t v_t,  dv_t = G_t^T k_t,  dS_0 = e^{-s} G_1
+ * dout rows follow the q/k/v layout; dq/dk/dv rows the o layout of
+ * lto_unit; ds and ds0 are d*d (NULL = zero / not written).
+ */
+typedef struct {
+    const float *q, *k, *v, *dout;
+    long long in_stride;
+    long long len;
+    double slope;
+    const double *s0;
+    const double *ds;
+    double *dq, *dk, *dv;
+    long long o_stride;
+    double *ds0;
+} lto_bwd_unit;
+
+static void run_bwd_unit(const lto_bwd_unit *u, int d, double *S)
+{
+    const double lam = exp(-u->slope);
+    const size_t dd = (size_t)d * (size_t)d;
+    /* forward sweep: S_t and dq_t */
+    if (u->s0)
+        memcpy(S, u->s0, sizeof(double) * dd);
+    else
+        memset(S, 0, sizeof(double) * dd);
+    for (long long i = 0; i < u->len; ++i) {
+        const float *ki = u->k + i * u->in_stride;
+        const float *vi = u->v + i * u->in_stride;
+        const float *gi = u->dout + i * u->in_stride;
+        for (int r = 0; r < d; ++r)
+            for (int c = 0; c < d; ++c)
+                S[(size_t)r * d + c] = lam * S[(size_t)r * d + c] + (double)ki[r] * (double)vi[c];
+        double *dqi = u->dq + i * u->o_stride;
+        for (int r = 0; r < d; ++r) {
+            double acc = 0.0;
+            for (int c = 0; c < d; ++c)
+                acc += S[(size_t)r * d + c] * (double)gi[c];
+            dqi[r] = acc;
+        }
+    }
+    /* reverse sweep: S now holds R = e^{-s} G_{t+1} (ds for the last token) */
+    if (u->ds)
+        memcpy(S, u->ds, sizeof(double) * dd);
+    else
+        memset(S, 0, sizeof(double) * dd);
+    for (long long i = u->len - 1; i >= 0; --i) {
+        const float *qi = u->q + i * u->in_stride;
+        const float *ki = u->k + i * u->in_stride;
+        const float *vi = u->v + i * u->in_stride;
+        const float *gi = u->dout + i * u->in_stride;
+        /* G_t = q_t^T dout_t + R */
+        for (int r = 0; r < d; ++r)
+            for (int c = 0; c < d; ++c)
+                S[(size_t)r * d + c] += (double)qi[r] * (double)gi[c];
+        double *dki = u->dk + i * u->o_stride;
+        double *dvi = u->dv + i * u->o_stride;
+        for (int c = 0; c < d; ++c)
+            dvi[c] = 0.0;
+        for (int r = 0; r < d; ++r) {
+            double acc = 0.0;
+            const double kr = (double)ki[r];
+            for (int c = 0; c < d; ++c) {
+                acc += S[(size_t)r * d + c] * (double)vi[c];
+                dvi[c] += S[(size_t)r * d + c] * kr;
+            }
+            dki[r] = acc;
+        }
+        for (size_t e = 0; e < dd; ++e)
+            S[e] *= lam;
+    }
+    if (u->ds0)
+        memcpy(u->ds0, S, sizeof(double) * dd);
+}
+
+int lto_backward(const lto_bwd_unit *units, int n_units, int d, int n_threads)
+{
+    if (!units || n_units < 0 || d <= 0)
+        return -1;
+    int failed = 0;
+#ifdef _OPENMP
+    if (n_threads > 0)
+        omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+#pragma omp parallel
+    {
+        double *S = (double *)malloc(sizeof(double) * (size_t)d * (size_t)d);
+        if (!S) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int n = 0; n < n_units; ++n)
+            if (S)
+                run_bwd_unit(&units[n], d, S);
+        free(S);
+    }
+    return failed ? -1 : 0;
+}

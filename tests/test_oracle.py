@@ -527,3 +527,139 @@ def test_decode_slots_relabelling_invariance():
     o1, p1 = oracle.decode_slots(q, k, v, sl, pool, ids)
     o2, p2 = oracle.decode_slots(q, k, v, sl, pool[perm], inv[ids])
     assert rel(o1, o2) < 1e-14 and rel(p1, p2[inv]) < 1e-14
+
+
+# --------------------------------------------------------------------------
+# Backward (oracle.backward_*): gradients of l = sum dO . O + <dS, S_L>
+# --------------------------------------------------------------------------
+
+def c_bwd(q, k, v, do, s, s0=None, ds=None):
+    """Single-unit adapter of oracle.backward_packed: [L, d] rows."""
+    L, d = q.shape
+    r = lambda x: np.asarray(x, np.float32).reshape(L, 1, d)
+    rs = lambda x: None if x is None else np.asarray(x, np.float64).reshape(1, 1, d, d)
+    dq, dk, dv, ds0 = oracle.backward_packed(r(q), r(k), r(v), r(do), np.array([s], np.float32),
+                                             [0, L], s0=rs(s0), ds=rs(ds))
+    return dq[:, 0], dk[:, 0], dv[:, 0], ds0[0, 0]
+
+
+def _loss_bf(q, k, v, s, s0, do, ds):
+    o, S = oracle.brute_force(q, k, v, s, s0)
+    return float(np.sum(o * do) + (0.0 if ds is None else np.sum(S * ds)))
+
+
+def backward_pin_failures(f):
+    """Names of the pins that f(q, k, v, do, s, s0, ds) -> (dq, dk, dv, ds0) fails."""
+    bad = []
+    d, L = 4, 11
+    g = np.random.Generator(np.random.PCG64(41))
+    for s in (0.0, 0.3, 2.0):
+        for with_state in (False, True):
+            q, k, v, do = (g.standard_normal((L, d)).astype(np.float32).astype(np.float64)
+                           for _ in range(4))
+            s0 = g.standard_normal((d, d)) if with_state else None
+            ds = g.standard_normal((d, d)) if with_state else None
+            dq, dk, dv, ds0 = f(q, k, v, do, s, s0, ds)
+            # 1. central finite differences of the fp64 quadratic form, one input at a time
+            eps = 1e-6
+            base_s0 = s0 if s0 is not None else np.zeros((d, d))
+            for name, grad in (("q", dq), ("k", dk), ("v", dv), ("s0", ds0)):
+                delta = g.standard_normal(grad.shape)
+                args = dict(q=q, k=k, v=v, s0=base_s0)
+                plus, minus = dict(args), dict(args)
+                plus[name] = args[name] + eps * delta
+                minus[name] = args[name] - eps * delta
+                fd = (_loss_bf(plus["q"], plus["k"], plus["v"], s, plus["s0"], do, ds)
+                      - _loss_bf(minus["q"], minus["k"], minus["v"], s, minus["s0"], do, ds)) / (2 * eps)
+                an = float(np.sum(grad * delta))
+                if abs(fd - an) > 1e-6 * max(1.0, abs(fd)):
+                    bad.append(f"finite difference d{name} s={s} state={with_state}")
+            # 2. closed forms from the quadratic masked form
+            sf = np.float64(np.float32(s))
+            pos = np.arange(1, L + 1, dtype=np.float64)
+            diff = pos[:, None] - pos[None, :]
+            M = np.where(diff >= 0, np.exp(-sf * np.maximum(diff, 0.0)), 0.0)
+            lq, lk = np.exp(-sf * pos), np.exp(-sf * (L - pos))
+            S0 = base_s0
+            dS = ds if ds is not None else np.zeros((d, d))
+            dq_w = ((do @ v.T) * M) @ k + lq[:, None] * (do @ S0.T)
+            dk_w = ((do @ v.T) * M).T @ q + lk[:, None] * (v @ dS.T)
+            dv_w = ((q @ k.T) * M).T @ do + lk[:, None] * (k @ dS)
+            ds0_w = (q * lq[:, None]).T @ do + np.exp(-sf * L) * dS
+            for name, a, b in (("dq", dq, dq_w), ("dk", dk, dk_w), ("dv", dv, dv_w),
+                               ("ds0", ds0, ds0_w)):
+                if rel(a, b) > 1e-10:
+                    bad.append(f"closed form {name} s={s} state={with_state}")
+    # 3. s = 200: only the diagonal (and the final-state term of the last token) survives
+    q, k, v, do = (g.standard_normal((L, d)) for _ in range(4))
+    q, k, v, do = (x.astype(np.float32).astype(np.float64) for x in (q, k, v, do))
+    dS = g.standard_normal((d, d))
+    dq, dk, dv, ds0 = f(q, k, v, do, 200.0, None, dS)
+    dots = np.sum(do * v, axis=1)
+    dk_w = dots[:, None] * q
+    dk_w[-1] += dS @ v[-1]
+    dv_w = np.sum(q * k, axis=1)[:, None] * do
+    dv_w[-1] += k[-1] @ dS
+    if (rel(dq, dots[:, None] * k) > 1e-12 or rel(dk, dk_w) > 1e-12 or rel(dv, dv_w) > 1e-12
+            or np.max(np.abs(ds0)) > 1e-80):
+        bad.append("s=200 diagonal")
+    # 4. linear in dO (eighths, so that dO1 + dO2 is exact in float32 too)
+    do1 = g.integers(-16, 17, (L, d)) / 8.0
+    do2 = g.integers(-16, 17, (L, d)) / 8.0
+    r1, r2, r12 = (f(q, k, v, x, 0.3, None, None) for x in (do1, do2, do1 + do2))
+    if any(rel(c, a + b) > 1e-12 for a, b, c in zip(r1, r2, r12)):
+        bad.append("linear in dO")
+    return bad
+
+
+def test_backward_passes_pins():
+    assert backward_pin_failures(c_bwd) == []
+
+
+def _bwd_loop(q, k, v, do, s, s0=None, ds=None, mistake=None):
+    """Per-token reverse-mode loop with switchable mistakes (mutation tests)."""
+    L, d = q.shape
+    lam = np.exp(-np.float64(np.float32(s)))
+    S = np.zeros((d, d)) if s0 is None else np.array(s0, np.float64)
+    dq = np.zeros((L, d))
+    for t in range(L):
+        prev = S.copy()
+        S = lam * S + np.outer(k[t], v[t])
+        dq[t] = (prev if mistake == "dq_prev_state" else S) @ do[t]
+    R = np.zeros((d, d)) if (ds is None or mistake == "ds_ignored") else np.array(ds, np.float64)
+    dk, dv = np.zeros((L, d)), np.zeros((L, d))
+    for t in range(L - 1, -1, -1):
+        G = np.outer(q[t], do[t]) + R
+        dk[t] = (G.T if mistake == "dk_transposed" else G) @ v[t]
+        dv[t] = G.T @ (q[t] if mistake == "dv_from_q" else k[t])
+        R = G if mistake == "no_decay_carry" else lam * G
+    ds0 = R / lam if mistake == "ds0_undecayed" else R
+    return dq, dk, dv, ds0
+
+
+def test_backward_numpy_loop_passes_pins():
+    assert backward_pin_failures(_bwd_loop) == []
+
+
+@pytest.mark.parametrize("mistake", ["dq_prev_state", "ds_ignored", "dk_transposed", "dv_from_q",
+                                     "no_decay_carry", "ds0_undecayed"])
+def test_backward_mutants_fail_pins(mistake):
+    f = lambda q, k, v, do, s, s0, ds: _bwd_loop(q, k, v, do, s, s0, ds, mistake=mistake)
+    with np.errstate(all="ignore"):
+        assert backward_pin_failures(f), mistake
+
+
+def test_backward_batch_matches_units():
+    """Packed and batched entry points agree with the single-unit one."""
+    g = np.random.Generator(np.random.PCG64(43))
+    B, L, H, d = 2, 9, 3, 4
+    q, k, v, do = (g.standard_normal((B, L, H, d)).astype(np.float32) for _ in range(4))
+    sl = np.array([0.5, 0.05, 0.0], np.float32)
+    s0 = g.standard_normal((B, H, d, d))
+    ds = g.standard_normal((B, H, d, d))
+    dq, dk, dv, ds0 = oracle.backward_batch(q, k, v, do, sl, s0=s0, ds=ds)
+    for b in range(B):
+        for h in range(H):
+            r = c_bwd(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h], float(sl[h]), s0[b, h], ds[b, h])
+            for got, want in zip((dq[b, :, h], dk[b, :, h], dv[b, :, h], ds0[b, h]), r):
+                assert rel(got, want) < 1e-14
