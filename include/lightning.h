@@ -161,6 +161,38 @@ LT_API lt_status lt_decode(const void *q, const void *k, const void *v, lt_dtype
                            int batch, int heads, int head_dim, void *stream);
 
 /*
+ * lt_prefill_backward - gradients of a fixed-length prefill. For the loss
+ *     l = sum_t dout_t . o_t + <d_state_out, S_final>   per (sequence, head)
+ * it writes dq, dk, dv (= dl/dq, dl/dk, dl/dv) and d_state_in (= dl/dS_0).
+ * The pages give no backward; this is the reverse-mode derivative of the
+ * operator above. With G_t = q_t^T dout_t + e^{-s_h} G_{t+1} and
+ * G_L = q_L^T dout_L + d_state_out:
+ *     dq_t = dout_t S_t^T,  dk_t = G_t v_t,  dv_t = G_t^T k_t,
+ *     d_state_in = e^{-s_h} G_1.
+ * The slopes get no gradient.
+ *
+ *   q, k, v, dout  [batch, seqlen, heads, head_dim] bf16 (in_dtype must be
+ *                  LT_BF16), the forward's inputs and the output gradient.
+ *   state_in       the forward's S_0, or NULL for zero.
+ *   d_state_out    [batch, heads, head_dim, head_dim] fp32 gradient of the
+ *                  final state, or NULL for zero.
+ *   dq, dk, dv     [batch, seqlen, heads, head_dim], grad_dtype (LT_F32 or
+ *                  LT_BF16).
+ *   d_state_in     [batch, heads, head_dim, head_dim] fp32, or NULL to skip.
+ *   block, workspace: as lt_prefill (the workspace serves the dq pass; query
+ *                  it with lt_prefill_workspace_bytes).
+ *   No output may overlap an input or another output (LT_ERR_ALIAS).
+ *   Errors: LT_ERR_NULL, LT_ERR_SHAPE, LT_ERR_BLOCK, LT_ERR_DTYPE,
+ *   LT_ERR_ALIAS, LT_ERR_HIP.
+ */
+LT_API lt_status lt_prefill_backward(const void *q, const void *k, const void *v, const void *dout,
+                                     lt_dtype in_dtype, const float *slopes, const float *state_in,
+                                     const float *d_state_out, void *dq, void *dk, void *dv,
+                                     lt_dtype grad_dtype, float *d_state_in, int batch,
+                                     long long seqlen, int heads, int head_dim, int block,
+                                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * lt_decode_slots - lt_decode for sequences whose states live in a pool, as a
  * server holding many concurrent sequences keeps them (§04: each sequence
  * carries its own fixed d x d fp32 state per head, whatever its length).

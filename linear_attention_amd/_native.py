@@ -21,7 +21,7 @@ HEAD_DIM = 128
 
 EXPORTS = ("lt_status_string", "lt_version", "lt_prefill", "lt_prefill_workspace_bytes",
            "lt_prefill_varlen", "lt_decode", "lt_prefill_norm_gate", "lt_prefill_varlen_norm_gate",
-           "lt_decode_norm_gate", "lt_decode_slots")
+           "lt_decode_norm_gate", "lt_decode_slots", "lt_prefill_backward")
 
 _vp, _i, _ll, _f = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_float
 
@@ -71,6 +71,9 @@ def _load() -> ctypes.CDLL:
     lib.lt_decode_norm_gate.restype = _i
     lib.lt_decode_slots.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _vp]
     lib.lt_decode_slots.restype = _i
+    lib.lt_prefill_backward.argtypes = [_vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp,
+                                        _i, _ll, _i, _i, _i, _vp, ctypes.c_size_t, _vp]
+    lib.lt_prefill_backward.restype = _i
     return lib
 
 
@@ -330,3 +333,40 @@ def lt_decode_slots(q, k, v, slopes, state_pool, slot_ids, *, o=None, out_dtype=
                              _dtype_code(o.dtype), batch, H, d, _stream(stream, q.device))
     _check(st, "lt_decode_slots")
     return o
+
+
+def lt_prefill_backward(q, k, v, dout, slopes, block, state_in=None, d_state_out=None, *, dq=None,
+                        dk=None, dv=None, d_state_in=None, want_d_state_in=True, grad_dtype=None,
+                        workspace=None, stream=None):
+    """Gradients of sum(dout * o) + <d_state_out, S_final> for a fixed-length prefill.
+    q, k, v, dout: bf16 [batch, L, H, 128]; state_in, d_state_out: fp32 [batch, H, 128, 128]
+    or None. Returns (dq, dk, dv [batch, L, H, 128] in grad_dtype (default fp32),
+    d_state_in [batch, H, 128, 128] fp32 or None).
+    """
+    torch = _torch()
+    if q.dim() != 4 or any(x.shape != q.shape for x in (k, v, dout)):
+        raise ValueError("q, k, v, dout must share one [batch, L, H, d] shape")
+    if any(x.dtype != q.dtype for x in (k, v, dout)):
+        raise TypeError("q, k, v, dout must share one dtype")
+    batch, L, H, d = q.shape
+    grad_dtype = grad_dtype or torch.float32
+    mk = lambda: torch.empty((batch, L, H, d), device=q.device, dtype=grad_dtype)
+    dq = mk() if dq is None else dq
+    dk = mk() if dk is None else dk
+    dv = mk() if dv is None else dv
+    if d_state_in is None and want_d_state_in:
+        d_state_in = torch.empty((batch, H, d, d), device=q.device, dtype=torch.float32)
+    if workspace is None:
+        nbytes = lt_prefill_workspace_bytes(batch, L, H, d, _dtype_code(q.dtype))
+        if nbytes:
+            workspace = torch.empty(nbytes, device=q.device, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.lt_prefill_backward(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                                 _dev_ptr(dout, "dout"), _dtype_code(q.dtype),
+                                 _dev_ptr(slopes, "slopes"), _dev_ptr(state_in, "state_in"),
+                                 _dev_ptr(d_state_out, "d_state_out"), _dev_ptr(dq, "dq"),
+                                 _dev_ptr(dk, "dk"), _dev_ptr(dv, "dv"), _dtype_code(dq.dtype),
+                                 _dev_ptr(d_state_in, "d_state_in"), batch, L, H, d, int(block),
+                                 _dev_ptr(workspace, "workspace"), ws_bytes, _stream(stream, q.device))
+    _check(st, "lt_prefill_backward")
+    return dq, dk, dv, d_state_in

@@ -1,0 +1,336 @@
+// Lightning Attention backward for bf16 inputs on gfx950 (MI355X): dK, dV and
+// the gradient of the carried-in state, in one reverse pass per (sequence, head).
+//
+// Gradients of l = sum_t dO_t . o_t + <dS, S_final> (the reverse-mode
+// derivative of the per-token form of MiniMax Signal Lab · M1, §03; the pages
+// give no backward). With G_t = q_t^T dO_t + e^{-s} G_{t+1} (G_L adds dS):
+//   dk_t = G_t v_t,  dv_t = G_t^T k_t,  dS_0 = e^{-s} G_1.
+// In blocks of m tokens (positions i = 1..m) walked from the last to the
+// first, with R the carry from the right (R = dS for the last block):
+//   dV = [(K Q^T) ⊙ D^T] dO + diag(d_r) K R,     d_r[i] = e^{-s(m-i)}
+//   dK = [(V dO^T) ⊙ D^T] Q + diag(d_r) V R^T
+//   R <- e^{-s m} R + (Q ⊙ d_q)^T dO,            d_q[i] = e^{-s i}
+// (D as in the forward; D^T keeps i' >= i). dQ is the forward operator on
+// (dO, V, K) with S_0^T and is computed by the forward kernels.
+//
+// gfx950 design, mirroring the forward kernel (tiles.h):
+//  * one 8-wave workgroup per (sequence, head); R lives in the MFMA
+//    accumulators of the eight waves (wave w: rows 64(w/4).., columns
+//    32(w%4)..) and, once per sub-block, in LDS as bf16 R^T;
+//  * waves 0..5 compute the six nonzero 32x32 blocks of A = (K Q^T) ⊙ D^T and
+//    B = (V dO^T) ⊙ D^T, stored transposed; wave w then produces the dV^T and
+//    dK^T blocks (rows 32(w%4).., tokens 32(w/4)..): the inter product
+//    (R^T K^T, R V^T) scaled by d_r, plus the intra product (dO^T A^T, Q^T B^T);
+//  * the R update is the forward state update with (Q ⊙ d_q, dO) in place of
+//    (K, V ⊙ d_k);
+//  * sub-blocks are anchored at the end of the sequence (a short block, if
+//    any, comes last and covers the first tokens);
+//  * dV and dK are staged through LDS (in the R^T buffer and the K, V tiles,
+//    free by then) and leave as whole rows; four barriers per sub-block.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "internal.h"
+#include "tiles.h"
+
+namespace lt {
+namespace {
+
+// Padded row-major LDS tiles (pitch 136 for 128-wide tiles, 72 for the 64-wide
+// score tiles): 16 consecutive rows start 4 banks apart, so 16-byte operand
+// reads are conflict-free, and addresses stay affine in the contraction step
+// (the XOR-swizzled layouts of the forward would need an address register per
+// unrolled read, more than this kernel's register budget allows).
+constexpr int PT = D + 8;   // pitch of the 128-wide tiles
+constexpr int PS = PW + 8;  // pitch of the score tiles
+using LT = LPad<PT>;
+using LS = LPad<PS>;
+
+// R^T (bf16) as the forward writes S^T, in the padded layout.
+__device__ __forceinline__ void write_rt(__bf16 *Rts, const f32x16 (&R)[2], int qh, int cq, int lane) {
+    const int r32 = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int gv = 0; gv < 4; ++gv) {
+            bf16x4 x;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[r] = static_cast<__bf16>(R[db][4 * gv + r]);
+            *reinterpret_cast<bf16x4 *>(Rts + LT::off(32 * cq + r32, 64 * qh + 32 * db + 8 * gv + 4 * h)) = x;
+        }
+}
+
+// R <- bd R + X^T Y over the sub-block (the forward's state_update, padded layout).
+__device__ __forceinline__ void carry_update(f32x16 (&R)[2], const __bf16 *X, const __bf16 *Y, float bd,
+                                             int qh, int cq, int lane) {
+#pragma unroll
+    for (int db = 0; db < 2; ++db) R[db] *= bd;
+#pragma unroll
+    for (int ks = 0; ks < C / 16; ++ks) {
+        const bf16x8 b = ld_op_t<LT>(Y, 32 * cq, 16 * ks, lane);
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+            R[db] = mma(ld_op_t<LT>(X, 64 * qh + 32 * db, 16 * ks, lane), b, R[db]);
+    }
+}
+
+// Staged fp32 output tile [64][128] (pitch 132 floats) and its full-row stores.
+constexpr int PO = D + 4;
+__device__ __forceinline__ void stage_rows(float *Os, const f32x16 &o, int qh, int cq, int lane) {
+    const int r32 = lane & 31, hf = lane >> 5;
+#pragma unroll
+    for (int gv = 0; gv < 4; ++gv)
+        *reinterpret_cast<float4 *>(Os + (32 * qh + r32) * PO + 32 * cq + 8 * gv + 4 * hf) =
+            make_float4(o[4 * gv], o[4 * gv + 1], o[4 * gv + 2], o[4 * gv + 3]);
+}
+template <bool FULL>
+__device__ __forceinline__ void put_rows(float *out, long long ts, const float *Os, int m, int tid) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = (tid >> 5) + 16 * j, col = 4 * (tid & 31);
+        const float4 x = *reinterpret_cast<const float4 *>(Os + row * PO + col);
+        if (FULL || row < m) stream_store(out + row * ts + col, x);
+    }
+}
+template <bool FULL>
+__device__ __forceinline__ void put_rows(__bf16 *out, long long ts, const float *Os, int m, int tid) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int row = (tid >> 4) + 32 * j, col = 8 * (tid & 15);
+        const float4 x0 = *reinterpret_cast<const float4 *>(Os + row * PO + col);
+        const float4 x1 = *reinterpret_cast<const float4 *>(Os + row * PO + col + 4);
+        const bf16x8 y = {static_cast<__bf16>(x0.x), static_cast<__bf16>(x0.y), static_cast<__bf16>(x0.z),
+                          static_cast<__bf16>(x0.w), static_cast<__bf16>(x1.x), static_cast<__bf16>(x1.y),
+                          static_cast<__bf16>(x1.z), static_cast<__bf16>(x1.w)};
+        if (FULL || row < m) stream_store_bits(out + row * ts + col, y);
+    }
+}
+
+// Register staging of one sub-block for the backward: q, k, v and dO (layout
+// as Stage: tokens (t/16) + 32i, elements 8(t%16)..; rows clamped into [0, m)).
+struct BwdStage {
+    uint4 q[2], k[2], v[2], g[2];
+
+    __device__ void load(const uint16_t *qg, const uint16_t *kg, const uint16_t *vg,
+                         const uint16_t *gg, int ts, int m, int tid) {
+        const int seg = tid & 15;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int t = (tid >> 4) + 32 * i;
+            const int row = (t < m ? t : m - 1) * ts + 8 * seg;
+            q[i] = stream_load16(qg + row);
+            k[i] = stream_load16(kg + row);
+            v[i] = stream_load16(vg + row);
+            g[i] = stream_load16(gg + row);
+        }
+    }
+
+    // Q, K, V, dO row-major, and Q ⊙ d_q with d_q[t] = e^{-s(t+1)} (0 for t >= m).
+    template <bool FULL>
+    __device__ void store(__bf16 *Qs, __bf16 *Ks, __bf16 *Vs, __bf16 *Gs, __bf16 *Qds, int m,
+                          float s2, int tid) {
+        const int seg = tid & 15;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int t = (tid >> 4) + 32 * i;
+            const bool in = FULL || t < m;
+            const int off = LT::off(t, 8 * seg);
+            const uint4 qq = keep_if(in, q[i]);
+            *reinterpret_cast<uint4 *>(Qs + off) = qq;
+            *reinterpret_cast<uint4 *>(Ks + off) = keep_if(in, k[i]);
+            *reinterpret_cast<uint4 *>(Vs + off) = keep_if(in, v[i]);
+            *reinterpret_cast<uint4 *>(Gs + off) = keep_if(in, g[i]);
+            const float dq = in ? fast_exp2(-s2 * (float)(t + 1)) : 0.f;
+            *reinterpret_cast<uint4 *>(Qds + off) = scale_bf16x8(qq, dq);
+        }
+    }
+};
+
+template <typename OutT>
+__global__ __launch_bounds__(NT) void bwd_kv_kernel(BackwardArgs a) {
+    __shared__ __attribute__((aligned(16))) __bf16 Qs[C * PT];
+    __shared__ __attribute__((aligned(16))) __bf16 KVs[2][C * PT];  // K, V; dK staging (fp32)
+    __shared__ __attribute__((aligned(16))) __bf16 Gs[C * PT];      // dO
+    __shared__ __attribute__((aligned(16))) __bf16 Qds[C * PT];     // Q ⊙ d_q
+    __shared__ __attribute__((aligned(16))) __bf16 Rts[D * PT];     // R^T; dV staging (fp32)
+    __shared__ __attribute__((aligned(16))) __bf16 Ats[C * PS];     // A^T: [i'][i]
+    __shared__ __attribute__((aligned(16))) __bf16 Bts[C * PS];     // B^T: [i'][i]
+    static_assert(sizeof(float) * C * PO <= sizeof(__bf16) * D * PT, "dV staging fits R^T");
+    static_assert(sizeof(float) * C * PO <= 2 * sizeof(__bf16) * C * PT, "dK staging fits K, V");
+    __bf16 *Ks = KVs[0], *Vs = KVs[1];
+
+    const int uh = blockIdx.x;
+    const int h = uh % a.heads, n = uh / a.heads;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qh = w >> 2, cq = w & 3, r32 = lane & 31, hf = lane >> 5;
+
+    const long long len = a.seqlen;
+    const int ts = a.heads * D;
+    const long long base = ((long long)n * len * a.heads + h) * (long long)D;
+    const uint16_t *qg = static_cast<const uint16_t *>(a.q) + base;
+    const uint16_t *kg = static_cast<const uint16_t *>(a.k) + base;
+    const uint16_t *vg = static_cast<const uint16_t *>(a.v) + base;
+    const uint16_t *gg = static_cast<const uint16_t *>(a.dout) + base;
+    OutT *dkg = static_cast<OutT *>(a.dk) + base;
+    OutT *dvg = static_cast<OutT *>(a.dv) + base;
+    const float s2 = a.slopes[h] * LOG2E;
+
+    // ---- carry from the right of the sequence: dS (or zero)
+    f32x16 R[2];
+    auto sidx = [&](int db, int v) {
+        return (64 * qh + 32 * db + 8 * (v >> 2) + 4 * hf + (v & 3)) * D + 32 * cq + r32;
+    };
+    if (a.d_state_out) {
+        const float *src = a.d_state_out + (size_t)uh * D * D;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) R[db][v] = src[sidx(db, v)];
+    } else {
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) R[db][v] = 0.f;
+    }
+    write_rt(Rts, R, qh, cq, lane);
+
+    // score blocks: waves 0..2 A, waves 3..5 B; block (I, I') in {(0,0), (0,1), (1,1)}
+    const bool scorer = w < 6;
+    const int blk = w % 3;
+    const int sI = blk == 2 ? 1 : 0, sJ = blk == 0 ? 0 : 1;  // rows i in 32sI.., columns i' in 32sJ..
+    float dscore[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int diff = (32 * sJ + r32) - (32 * sI + 8 * (v >> 2) + 4 * hf + (v & 3));
+        dscore[v] = diff >= 0 ? fast_exp2(-s2 * (float)diff) : 0.f;
+    }
+
+    // Sub-blocks are anchored at the end of the sequence: step p < nfull covers
+    // tokens [len - 64(p+1), len - 64p); a short first block [0, len mod 64),
+    // if any, is the last step (the block form holds for any partition).
+    const long long nfull = len / C;
+    const int head_len = (int)(len - nfull * C);
+    const long long nsteps = nfull + (head_len > 0);
+    auto step_start = [&](long long p) { return p < nfull ? len - C * (p + 1) : 0; };
+    auto step_len = [&](long long p) { return p < nfull ? C : head_len; };
+    // sub-block of step p is staged in st[p % 2], loaded two steps ahead
+    BwdStage st0, st1;
+    auto prefetch = [&](BwdStage &st, long long p) {
+        const long long pp = p < nsteps ? p : nsteps - 1;  // past the start: reload (ignored)
+        const long long off = step_start(pp) * (long long)ts;
+        st.load(qg + off, kg + off, vg + off, gg + off, ts, step_len(pp), tid);
+    };
+    if (nsteps > 0) {
+        prefetch(st0, 0);
+        prefetch(st1, 1);
+    }
+
+    auto step = [&](long long p, int m, auto full, BwdStage &st) {
+        constexpr bool FULL = decltype(full)::value;
+        const long long t0 = step_start(p);
+        st.template store<FULL>(Qs, Ks, Vs, Gs, Qds, m, s2, tid);
+        prefetch(st, p + 2);
+        __syncthreads();  // (B) tiles and R^T visible
+
+        if (scorer) {
+            // A^T or B^T block: C[i][i'] = x_i . y_i' masked to i' >= i and decayed,
+            // stored as [i'][i]
+            const __bf16 *X = w < 3 ? Ks : Vs;
+            const __bf16 *Y = w < 3 ? Qs : Gs;
+            __bf16 *T = w < 3 ? Ats : Bts;
+            f32x16 sc;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) sc[v] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks)
+                sc = mma(ld_op<LT>(X, 32 * sI, 16 * ks, lane), ld_op<LT>(Y, 32 * sJ, 16 * ks, lane), sc);
+#pragma unroll
+            for (int gv = 0; gv < 4; ++gv) {
+                bf16x4 pv;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) pv[r] = static_cast<__bf16>(sc[4 * gv + r] * dscore[4 * gv + r]);
+                *reinterpret_cast<bf16x4 *>(T + LS::off(32 * sJ + r32, 32 * sI + 8 * gv + 4 * hf)) = pv;
+            }
+        }
+
+        // inter products, scaled per token i = 32 qh + r32 by d_r[i] = e^{-s(m-1-i)}
+        f32x16 dv, dk;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dv[v] = dk[v] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            dv = mma(ld_op<LT>(Rts, 32 * cq, 16 * ks, lane), ld_op<LT>(Ks, 32 * qh, 16 * ks, lane), dv);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            dk = mma(ld_op_t<LT>(Rts, 32 * cq, 16 * ks, lane), ld_op<LT>(Vs, 32 * qh, 16 * ks, lane), dk);
+        const int ti = 32 * qh + r32;
+        const float dr = ti < m ? fast_exp2(-s2 * (float)(m - 1 - ti)) : 0.f;
+        dv *= dr;
+        dk *= dr;
+
+        // R <- e^{-s m} R + (Q ⊙ d_q)^T dO
+        carry_update(R, Qds, Gs, fast_exp2(-s2 * (float)m), qh, cq, lane);
+        __syncthreads();  // (C) A^T, B^T visible; reads of R^T, K, V, Q ⊙ d_q done
+
+        // intra products over i' >= 32 qh
+#pragma unroll
+        for (int ks = 0; ks < C / 16; ++ks) {
+            if (ks < 2 * qh) continue;
+            dv = mma(ld_op_t<LT>(Gs, 32 * cq, 16 * ks, lane), ld_op_t<LS>(Ats, 32 * qh, 16 * ks, lane), dv);
+        }
+#pragma unroll
+        for (int ks = 0; ks < C / 16; ++ks) {
+            if (ks < 2 * qh) continue;
+            dk = mma(ld_op_t<LT>(Qs, 32 * cq, 16 * ks, lane), ld_op_t<LS>(Bts, 32 * qh, 16 * ks, lane), dk);
+        }
+        float *dVs = reinterpret_cast<float *>(Rts);
+        float *dKs = reinterpret_cast<float *>(KVs[0]);
+        stage_rows(dVs, dv, qh, cq, lane);
+        stage_rows(dKs, dk, qh, cq, lane);
+        __syncthreads();  // (D) dV, dK staged
+        put_rows<FULL>(dvg + t0 * (long long)ts, ts, dVs, m, tid);
+        put_rows<FULL>(dkg + t0 * (long long)ts, ts, dKs, m, tid);
+        __syncthreads();  // (E) staging read; R^T and the next tiles may be written
+        write_rt(Rts, R, qh, cq, lane);
+    };
+    long long p = 0;
+    for (; p + 1 < nfull; p += 2) {
+        step(p, C, std::true_type{}, st0);
+        step(p + 1, C, std::true_type{}, st1);
+    }
+    if (p < nfull) step(p++, C, std::true_type{}, st0);
+    if (head_len > 0) {  // staged in st[nfull % 2]
+        if (nfull & 1)
+            step(p, head_len, std::false_type{}, st1);
+        else
+            step(p, head_len, std::false_type{}, st0);
+    }
+
+    if (a.d_state_in) {
+        float *dst = a.d_state_in + (size_t)uh * D * D;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) dst[sidx(db, v)] = R[db][v];
+    }
+}
+
+template <typename OutT>
+hipError_t launch(const BackwardArgs &a, hipStream_t stream) {
+    clear_pending_error();
+    const long long uh = (long long)a.units * a.heads;
+    hipLaunchKernelGGL((bwd_kv_kernel<OutT>), dim3((unsigned)uh), dim3(NT), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward_kv(const BackwardArgs &a, lt_dtype out_dtype, hipStream_t stream) {
+    return out_dtype == LT_F32 ? launch<float>(a, stream) : launch<__bf16>(a, stream);
+}
+
+}  // namespace lt

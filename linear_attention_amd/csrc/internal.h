@@ -33,6 +33,9 @@ struct PrefillArgs {
     int units;
     int heads;
     NormGate ng;
+    // state_in holds S_0 transposed ([units, heads, d_value, d_key]); the
+    // backward pass's dQ = forward(dO, V, K) carries S_0^T.
+    bool state_in_t = false;
 };
 
 // Decode: state is [batch, heads, d, d], or with slot_ids != nullptr a pool
@@ -92,6 +95,21 @@ inline void clear_pending_error() { (void)hipGetLastError(); }
 
 PrefillPlan plan_prefill(long long units, long long seqlen, int heads, lt_dtype in_dtype,
                          bool varlen);
+
+// Backward of a fixed-length bf16 prefill (gradients of
+// l = sum dout . o + <d_state_out, S_final>): dk, dv and d_state_in from one
+// reverse pass; dq is the forward operator on (dout, v, k) with S_0^T.
+struct BackwardArgs {
+    const void *q, *k, *v, *dout;  // [units * seqlen, heads, d] bf16
+    const float *slopes;
+    const float *d_state_out;      // [units, heads, d, d] or null (zero)
+    void *dk, *dv;                 // [units * seqlen, heads, d], OutT
+    float *d_state_in;             // [units, heads, d, d] or null (not written)
+    long long seqlen;
+    int units;
+    int heads;
+};
+hipError_t launch_backward_kv(const BackwardArgs &a, lt_dtype out_dtype, hipStream_t stream);
 
 // fp32 inputs: one workgroup per (unit, head, 32-column value slice).
 hipError_t launch_prefill_slices(const PrefillArgs &a, lt_dtype in_dtype, lt_dtype out_dtype,

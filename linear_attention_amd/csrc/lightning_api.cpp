@@ -67,10 +67,11 @@ lt_status launch(const lt::PrefillArgs &a, int in_dtype, int out_dtype, bool var
     // the norm-gate epilogue needs whole output rows, so it keeps one workgroup
     // per (sequence, head) rather than value slices.
     const bool no_ws = p.workspace > 0 && (!workspace || workspace_bytes < p.workspace);
-    if (no_ws || (a.ng.gate && p.value_slices != 1)) {
+    const bool whole_rows = a.ng.gate || a.state_in_t;  // epilogue or transposed S_0
+    if (no_ws || (whole_rows && p.value_slices != 1)) {
         p = lt::PrefillPlan{};
         p.seg_len = varlen ? a.total_tokens : a.seqlen;
-        if (!a.ng.gate) p.value_slices = lt::kValueSlices;
+        if (!whole_rows) p.value_slices = lt::kValueSlices;
     }
     return map_hip(lt::launch_prefill_heads(a, p, workspace, (lt_dtype)out_dtype, st));
 }
@@ -384,6 +385,56 @@ LT_API lt_status lt_decode(const void *q, const void *k, const void *v, lt_dtype
                            int batch, int heads, int head_dim, void *stream) {
     return decode_impl(q, k, v, in_dtype, slopes, state, o, out_dtype, batch, heads, head_dim,
                        stream, nullptr);
+}
+
+LT_API lt_status lt_prefill_backward(const void *q, const void *k, const void *v, const void *dout,
+                                     lt_dtype in_dtype, const float *slopes, const float *state_in,
+                                     const float *d_state_out, void *dq, void *dk, void *dv,
+                                     lt_dtype grad_dtype, float *d_state_in, int batch,
+                                     long long seqlen, int heads, int head_dim, int block,
+                                     void *workspace, size_t workspace_bytes, void *stream) {
+    if (!dtype_ok(in_dtype) || !dtype_ok(grad_dtype)) return LT_ERR_DTYPE;
+    if (in_dtype != LT_BF16) return LT_ERR_DTYPE;
+    if (batch < 0 || seqlen < 0 || head_dim != lt::kHeadDim || heads < 0 || heads > LT_MAX_HEADS)
+        return LT_ERR_SHAPE;
+    if (block < 1 || block > LT_MAX_BLOCK) return LT_ERR_BLOCK;
+    long long tokens, in_b, g_b, st_b, grid;
+    if (__builtin_mul_overflow((long long)batch, seqlen, &tokens) ||
+        !mul4(tokens, heads, head_dim, 2, &in_b) ||
+        !mul4(tokens, heads, head_dim, dtype_size(grad_dtype), &g_b) ||
+        !mul4(batch, heads, (long long)head_dim * head_dim, 4, &st_b) ||
+        !mul4(batch, heads, lt::kValueSlices, 1, &grid) || grid > 0x7fffffffLL)
+        return LT_ERR_SHAPE;
+    if (batch == 0 || heads == 0) return LT_OK;
+    if (!slopes) return LT_ERR_NULL;
+    if (tokens > 0 && (!q || !k || !v || !dout || !dq || !dk || !dv)) return LT_ERR_NULL;
+    const Range ins[] = {range_of(q, in_b), range_of(k, in_b), range_of(v, in_b),
+                         range_of(dout, in_b), range_of(slopes, heads * 4LL),
+                         range_of(state_in, state_in ? st_b : 0),
+                         range_of(d_state_out, d_state_out ? st_b : 0)};
+    const Range outs[] = {range_of(dq, g_b), range_of(dk, g_b), range_of(dv, g_b),
+                          range_of(d_state_in, d_state_in ? st_b : 0),
+                          range_of(workspace, workspace ? (long long)workspace_bytes : 0)};
+    for (const Range &o : outs) {
+        for (const Range &i : ins)
+            if (overlaps(o, i)) return LT_ERR_ALIAS;
+    }
+    for (int x = 0; x < 5; ++x)
+        for (int y = x + 1; y < 5; ++y)
+            if (overlaps(outs[x], outs[y])) return LT_ERR_ALIAS;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (tokens > 0) {
+        // dQ = forward(dO, V, K) carrying S_0^T
+        lt::PrefillArgs a{dout, v, k, slopes, dq, state_in, nullptr, nullptr, seqlen, tokens,
+                          batch, heads};
+        a.state_in_t = true;
+        const lt_status s1 = launch(a, LT_BF16, grad_dtype, false, workspace, workspace_bytes, stream);
+        if (s1 != LT_OK) return s1;
+    }
+    if (tokens == 0 && !d_state_in) return LT_OK;
+    const lt::BackwardArgs b{q, k, v, dout, slopes, d_state_out, dk, dv, d_state_in, seqlen,
+                             batch, heads};
+    return map_hip(lt::launch_backward_kv(b, grad_dtype, st));
 }
 
 LT_API lt_status lt_decode_slots(const void *q, const void *k, const void *v, lt_dtype in_dtype,

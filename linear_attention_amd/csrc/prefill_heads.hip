@@ -30,8 +30,10 @@
 //    contributed by fixed pieces of every segment but the last (the same state
 //    update without outputs) into a workspace; segment g starts from
 //    e^{-s*start_g} S_0 plus each piece's state decayed to start_g.
-//  * Output stores are deferred one iteration so the prefetch loads of the next
-//    sub-block are always the newest memory operations in flight.
+//  * Outputs go through LDS and leave as whole rows (full 512-byte fp32 rows
+//    stream far better than the 32-byte pieces of the accumulator layout).
+//  * Shared building blocks (layouts, operand loads, staging, state update)
+//    are in tiles.h.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -39,251 +41,10 @@
 #include <type_traits>
 
 #include "internal.h"
+#include "tiles.h"
 
 namespace lt {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-
-constexpr int D = kHeadDim;  // 128
-constexpr int C = 64;        // tokens per sub-block
-constexpr int NT = 512;      // 8 waves
-constexpr int PW = C;        // width of the P tile
-constexpr float LOG2E = 1.4426950408889634f;
-
-static_assert(D == 128 && C == 64, "tile shapes are fixed below");
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// LDS tile layouts. Tiles are row-major without padding; bank conflicts are
-// avoided by permuting the 16-byte chunks of each row. For a 128-wide bf16 tile
-// (16 chunks per 256-byte row) chunk c of row r is stored at c ^ swz(r) with
-// swz(r) = ((r & 3) << 2) | ((r >> 2) & 3), a bijection on the 16 rows of any
-// aligned 16-row group (16-byte operand reads of 16 consecutive rows hit 64
-// distinct banks) that also sends the chunk pairs read by one transposing read
-// (4 consecutive rows x 2 adjacent chunks) to 4 disjoint pairs (8-byte reads of
-// a 32-lane half-wave hit 64 distinct banks).
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-
-struct L128 {  // [rows][128] bf16
-    __device__ static int off(int row, int col) {
-        return row * 128 + ((((col >> 3) ^ swz(row)) << 3) | (col & 7));
-    }
-};
-struct LP {  // P tile [64][64] bf16: 8 chunks per 128-byte row, two rows per bank line
-    __device__ static int off(int row, int col) {
-        return row * PW + ((((col >> 3) ^ ((row >> 1) & 7)) << 3) | (col & 7));
-    }
-};
-template <int PITCH>
-struct LPad {  // narrow tiles: plain padded rows
-    __device__ static int off(int row, int col) { return row * PITCH + col; }
-};
-
-// MFMA operand (32x32x16, bf16) from an LDS tile whose rows are the operand
-// rows: lane l reads row row0 + (l % 32), contraction slots k0 + 8*(l / 32)..+7.
-template <class L>
-__device__ __forceinline__ bf16x8 ld_op(const __bf16 *t, int row0, int k0, int lane) {
-    return *reinterpret_cast<const bf16x8 *>(t + L::off(row0 + (lane & 31), k0 + 8 * (lane >> 5)));
-}
-
-// MFMA operand whose rows are the COLUMNS of an LDS tile and whose contraction
-// runs down the tile rows: lane l gets tile[k0 + 8*(l/32) + e][c0 + (l % 32)],
-// e = 0..7. ds_read_b64_tr_b16 lets each 16-lane group load a 4x16 block (lanes
-// 4r..4r+3 give row r) and hands lane i column i.
-template <class L>
-__device__ __forceinline__ bf16x8 ld_op_t(const __bf16 *t, int c0, int k0, int lane) {
-    const int li = lane & 15, grp = lane >> 4;
-    const int row = k0 + 8 * (grp >> 1) + (li >> 2), col = c0 + 16 * (grp & 1) + 4 * (li & 3);
-    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(t + L::off(row, col)));
-    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(t + L::off(row + 4, col)));
-    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
-// Streaming HBM access. q, k, v are read once and o is written once, so loads
-// and stores carry the non-temporal hint; measured on this kernel's access
-// pattern (256-byte row pieces at a 16 KiB token stride) it lifts the k, v
-// read rate from 2.4 to 5.7 TB/s and the q, k, v + o pattern from 5.2 to
-// 5.8 TB/s. State and workspace traffic keeps the default policy.
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint4 stream_load16(const uint16_t *p) {
-    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-    return make_uint4(x.x, x.y, x.z, x.w);
-}
-__device__ __forceinline__ uint2 stream_load8(const uint16_t *p) {
-    const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
-    return make_uint2(x.x, x.y);
-}
-__device__ __forceinline__ void stream_store(float *p, float4 x) {
-    __builtin_nontemporal_store(f32x4{x.x, x.y, x.z, x.w}, reinterpret_cast<f32x4 *>(p));
-}
-template <class V>
-__device__ __forceinline__ void stream_store_bits(__bf16 *p, const V &x) {
-    static_assert(sizeof(V) == 16 || sizeof(V) == 8, "16- or 8-byte stores");
-    if constexpr (sizeof(V) == 16) {
-        u32x4 b;
-        __builtin_memcpy(&b, &x, 16);
-        __builtin_nontemporal_store(b, reinterpret_cast<u32x4 *>(p));
-    } else {
-        u32x2 b;
-        __builtin_memcpy(&b, &x, 8);
-        __builtin_nontemporal_store(b, reinterpret_cast<u32x2 *>(p));
-    }
-}
-
-__device__ __forceinline__ uint4 keep_if(bool keep, uint4 x) {
-    return make_uint4(keep ? x.x : 0u, keep ? x.y : 0u, keep ? x.z : 0u, keep ? x.w : 0u);
-}
-
-// 8 bf16 (in a uint4) scaled by f, rounded back to bf16.
-__device__ __forceinline__ uint4 scale_bf16x8(uint4 x, float f) {
-    uint32_t w[4] = {x.x, x.y, x.z, x.w};
-    uint32_t r[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float lo = __uint_as_float(w[i] << 16) * f;
-        const float hi = __uint_as_float(w[i] & 0xffff0000u) * f;
-        const __bf16 blo = static_cast<__bf16>(lo), bhi = static_cast<__bf16>(hi);
-        uint16_t ulo, uhi;
-        __builtin_memcpy(&ulo, &blo, 2);
-        __builtin_memcpy(&uhi, &bhi, 2);
-        r[i] = (uint32_t)ulo | ((uint32_t)uhi << 16);
-    }
-    return make_uint4(r[0], r[1], r[2], r[3]);
-}
-
-// Register staging of one sub-block: thread t holds tokens (t/16) + 32i,
-// i = 0, 1, elements 8*(t%16)..+7 of q, k and v. Loads are unconditional with
-// rows clamped into [0, m), so their number never depends on m; rows >= m are
-// zeroed when written to LDS.
-template <bool WITH_Q>
-struct Stage {
-    uint4 q[2], k[2], v[2];
-
-    __device__ void load(const uint16_t *qg, const uint16_t *kg, const uint16_t *vg, int ts, int m,
-                         int tid) {
-        const int seg = tid & 15;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int t = (tid >> 4) + 32 * i;
-            const int row = (t < m ? t : m - 1) * ts + 8 * seg;
-            if (WITH_Q) q[i] = stream_load16(qg + row);
-            k[i] = stream_load16(kg + row);
-            v[i] = stream_load16(vg + row);
-        }
-    }
-
-    // Writes Q, K, V row-major and V ⊙ d_k (d_k[t] = e^{-s(m-1-t)}, 0 for t >= m);
-    // without Q (the pre-pass) only K and V ⊙ d_k. FULL: m == C (no masking).
-    template <bool FULL>
-    __device__ void store(__bf16 *Qs, __bf16 *Ks, __bf16 *Vs, __bf16 *Vds, int m, float s2,
-                          int tid) {
-        const int seg = tid & 15;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int t = (tid >> 4) + 32 * i;
-            const bool in = FULL || t < m;
-            const int off = L128::off(t, 8 * seg);
-            if (WITH_Q) *reinterpret_cast<uint4 *>(Qs + off) = keep_if(in, q[i]);
-            *reinterpret_cast<uint4 *>(Ks + off) = keep_if(in, k[i]);
-            const uint4 vv = keep_if(in, v[i]);
-            if (WITH_Q) *reinterpret_cast<uint4 *>(Vs + off) = vv;  // the pre-pass needs only V ⊙ d_k
-            const float dk = in ? fast_exp2(-s2 * (float)((FULL ? C : m) - 1 - t)) : 0.f;
-            *reinterpret_cast<uint4 *>(Vds + off) = scale_bf16x8(vv, dk);
-        }
-    }
-};
-
-// Wave roles (w = wave index, h = lane / 32, r32 = lane % 32):
-//   qh = w / 4, cq = w % 4
-//   output block   O[32qh + r32][32cq + 8(v/4) + 4h + v%4]           (as O^T)
-//   state blocks   S[64qh + 32db + 8(v/4) + 4h + v%4][32cq + r32], db = 0, 1
-// so the state block layout equals the accumulator layout of
-// mma(K^T rows, (V ⊙ d_k)^T rows).
-
-// S <- e^{-s m} S + K^T (V ⊙ d_k) for this wave's two state blocks.
-__device__ __forceinline__ void state_update(f32x16 (&S)[2], const __bf16 *Ks, const __bf16 *Vds,
-                                             float bd, int qh, int cq, int lane) {
-#pragma unroll
-    for (int db = 0; db < 2; ++db) S[db] *= bd;
-#pragma unroll
-    for (int ks = 0; ks < C / 16; ++ks) {
-        const bf16x8 b = ld_op_t<L128>(Vds, 32 * cq, 16 * ks, lane);
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-            S[db] = mma(ld_op_t<L128>(Ks, 64 * qh + 32 * db, 16 * ks, lane), b, S[db]);
-    }
-}
-
-// Writes the wave's state blocks as bf16 S^T rows (value column major).
-__device__ __forceinline__ void write_state_t(__bf16 *Sts, const f32x16 (&S)[2], int qh, int cq,
-                                              int lane) {
-    const int r32 = lane & 31, h = lane >> 5;
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int gv = 0; gv < 4; ++gv) {
-            bf16x4 x;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) x[r] = static_cast<__bf16>(S[db][4 * gv + r]);
-            *reinterpret_cast<bf16x4 *>(Sts + L128::off(32 * cq + r32, 64 * qh + 32 * db + 8 * gv + 4 * h)) = x;
-        }
-}
-
-// Output tile staging. Each wave writes its 32x32 fp32 output block into an
-// LDS tile Os[64][128]; the workgroup then stores whole output rows (512 B in
-// fp32) with consecutive lanes on consecutive addresses. Stored straight from
-// the MFMA accumulator layout, a row would arrive in 32-byte pieces from four
-// instructions, which measured at under 60% of the HBM throughput of full-row
-// stores for this access pattern.
-// Staged output tile: fp32 [64][128], 4-float chunks of row r permuted by
-// r & 15 (writes of 16 rows of one chunk and reads of one whole row are both
-// conflict-free).
-__device__ __forceinline__ int ooff(int row, int col) {
-    return row * D + ((((col >> 2) ^ (row & 15)) << 2) | (col & 3));
-}
-
-__device__ __forceinline__ void stage_out(float *Os, const f32x16 &o, int qh, int cq, int lane) {
-    const int r32 = lane & 31, hf = lane >> 5;
-#pragma unroll
-    for (int gv = 0; gv < 4; ++gv)
-        *reinterpret_cast<float4 *>(Os + ooff(32 * qh + r32, 32 * cq + 8 * gv + 4 * hf)) =
-            make_float4(o[4 * gv], o[4 * gv + 1], o[4 * gv + 2], o[4 * gv + 3]);
-}
-
-// Stores rows [0, m) of the staged tile to out (row r at out + r * ts).
-template <bool FULL>
-__device__ __forceinline__ void store_rows(float *out, long long ts, const float *Os, int m, int tid) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int row = (tid >> 5) + 16 * j, col = 4 * (tid & 31);
-        const float4 x = *reinterpret_cast<const float4 *>(Os + ooff(row, col));
-        if (FULL || row < m) stream_store(out + row * ts + col, x);
-    }
-}
-template <bool FULL>
-__device__ __forceinline__ void store_rows(__bf16 *out, long long ts, const float *Os, int m, int tid) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int row = (tid >> 4) + 32 * j, col = 8 * (tid & 15);
-        const float4 x0 = *reinterpret_cast<const float4 *>(Os + ooff(row, col));
-        const float4 x1 = *reinterpret_cast<const float4 *>(Os + ooff(row, col + 4));
-        const bf16x8 y = {static_cast<__bf16>(x0.x), static_cast<__bf16>(x0.y), static_cast<__bf16>(x0.z),
-                          static_cast<__bf16>(x0.w), static_cast<__bf16>(x1.x), static_cast<__bf16>(x1.y),
-                          static_cast<__bf16>(x1.z), static_cast<__bf16>(x1.w)};
-        if (FULL || row < m) stream_store_bits(out + row * ts + col, y);
-    }
-}
 
 // Rows [0, m) of the staged tile with the post-sum normalisation and gate:
 // y = o / sqrt(mean(o^2) + eps) * w * sigmoid(g). Thread layout as the fp32
@@ -327,21 +88,6 @@ __device__ __forceinline__ void store_rows_norm_gate(OutT *out, long long ts, co
                                      x.z * inv * w.z * sigmoid(g2), x.w * inv * w.w * sigmoid(g3));
         if (FULL || row < m) put4(out + row * ts + col, y);
     }
-}
-
-struct SeqRange {
-    long long start, len;
-};
-
-__device__ __forceinline__ SeqRange sequence_of(const PrefillArgs &a, int n) {
-    if (a.cu_seqlens) {
-        const long long T = a.total_tokens;
-        long long lo = a.cu_seqlens[n], hi = a.cu_seqlens[n + 1];
-        lo = lo < 0 ? 0 : (lo > T ? T : lo);
-        hi = hi < lo ? lo : (hi > T ? T : hi);
-        return {lo, hi - lo};
-    }
-    return {(long long)n * a.seqlen, a.seqlen};
 }
 
 // ---------------------------------------------------------------------------
@@ -467,8 +213,16 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(PrefillArgs a,
     const int h = uh % a.heads;
     const float s2 = a.slopes[h] * LOG2E;
     float *u = sp.unit(ws, uh);
-    float4 acc = a.state_in ? *reinterpret_cast<const float4 *>(a.state_in + (size_t)uh * D * D + e)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (a.state_in) {
+        const float *si = a.state_in + (size_t)uh * D * D;
+        if (a.state_in_t) {  // element (r, c) at c * D + r
+            const int r = e / D, c = e % D;
+            acc = make_float4(si[c * D + r], si[(c + 1) * D + r], si[(c + 2) * D + r], si[(c + 3) * D + r]);
+        } else {
+            acc = *reinterpret_cast<const float4 *>(si + e);
+        }
+    }
     *reinterpret_cast<float4 *>(sp.start_state(u, 0) + e) = acc;
     const long long covered = sp.covered();
     for (int j = 0; j < sp.pieces; ++j) {
@@ -536,7 +290,16 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
     };
     const float *s_in = segments > 1 ? sp.start_state(sp.unit(ws, uh), g)
                                      : (a.state_in ? a.state_in + (size_t)uh * D * D : nullptr);
-    if (s_in) {
+    if (s_in && segments == 1 && a.state_in_t) {
+        // S_0 given transposed: element (r, c) at c * D + r
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = 64 * qh + 32 * db + 8 * (v >> 2) + 4 * hf + (v & 3), c = 32 * cq + r32;
+                S[db][v] = s_in[c * D + r];
+            }
+    } else if (s_in) {
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -902,7 +665,7 @@ hipError_t launch(const PrefillArgs &a, const PrefillPlan &p, void *workspace, h
     clear_pending_error();
     const long long uh = (long long)a.units * a.heads;
     // a value-slice workgroup sees 32 of a row's 128 columns: no row epilogue
-    if (p.value_slices == NSL && a.ng.gate) return hipErrorInvalidValue;
+    if (p.value_slices == NSL && (a.ng.gate || a.state_in_t)) return hipErrorInvalidValue;
     if (p.value_slices == NSL) {
         hipLaunchKernelGGL((slice_kernel<OutT>), dim3((unsigned)(uh * NSL)), dim3(NT), 0, stream, a);
         return hipGetLastError();

@@ -286,3 +286,39 @@ def test_one_hip_runtime_per_process():
             "print(len({l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l}))\n") % ROOT
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True)
     assert out.stdout.strip().splitlines()[-1] == "1", out.stdout + out.stderr
+
+
+# --------------------------------------------------------------------------
+# backward
+# --------------------------------------------------------------------------
+
+def backward(**kw):
+    args = dict(q=A, k=A + 100 * MB, v=A + 200 * MB, dout=A + 300 * MB, in_dtype=la.LT_BF16,
+                slopes=A + 399 * MB, state_in=None, d_state_out=None, dq=A + 400 * MB,
+                dk=A + 500 * MB, dv=A + 600 * MB, grad_dtype=la.LT_F32, d_state_in=A + 900 * MB,
+                batch=1, seqlen=64, heads=2, head_dim=128, block=64, workspace=None,
+                workspace_bytes=0, stream=None)
+    args.update(kw)
+    return la.lib.lt_prefill_backward(*args.values())
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "dout", "slopes", "dq", "dk", "dv"])
+def test_backward_null_pointers(field):
+    assert backward(**{field: None}) == la.LT_ERR_NULL
+
+
+def test_backward_checks():
+    assert backward(in_dtype=la.LT_F32) == la.LT_ERR_DTYPE
+    assert backward(grad_dtype=4) == la.LT_ERR_DTYPE
+    assert backward(head_dim=64) == la.LT_ERR_SHAPE
+    assert backward(seqlen=-1) == la.LT_ERR_SHAPE
+    assert backward(block=0) == la.LT_ERR_BLOCK
+    assert backward(dq=A + 16) == la.LT_ERR_ALIAS                       # dq inside q
+    assert backward(dk=A + 400 * MB + 64) == la.LT_ERR_ALIAS            # dk inside dq (64 KiB)
+    assert backward(dv=A + 300 * MB) == la.LT_ERR_ALIAS                 # dv on dout
+    assert backward(state_in=A + 900 * MB) == la.LT_ERR_ALIAS           # d_state_in on state_in
+    assert backward(d_state_out=A + 900 * MB + 8) == la.LT_ERR_ALIAS
+    assert backward(workspace=A + 500 * MB, workspace_bytes=64) == la.LT_ERR_ALIAS
+    assert backward(batch=0) == la.LT_OK
+    assert backward(heads=0) == la.LT_OK
+    assert backward(seqlen=0, d_state_in=None) == la.LT_OK
