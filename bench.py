@@ -16,6 +16,8 @@ Prints ONE JSON line. Besides the driver's fields it carries:
                 state-stream GB/s against 8 TB/s;
   norm_gate     the same prefill and decode with the normalisation and gate
                 fused into the epilogue (bf16 gate, bf16 y);
+  backward      lt_prefill_backward (dq, dk, dv, dS0) on the M1 layer and on a
+                4 x 8192-token batch of the same heads;
   cpu_baseline  the fp64 oracle on the host cores, timed on the same prefill
                 workload (reported baseline, not a target).
 
@@ -171,6 +173,50 @@ def run_prefill_norm_gate(la, torch, steps, warmup):
                          "bytes_per_launch": nbytes,
                          "kernel": "lt_prefill_norm_gate call: piece_state_kernel + combine_kernel "
                                    "+ head_kernel<bf16, norm-gate>"}}
+
+
+def run_backward(la, torch, steps, warmup, batch, seqlen):
+    """lt_prefill_backward on [batch, seqlen, 64, 128] bf16 with fp32 gradients and a
+    final-state gradient. Algorithmic bytes: q, k, v, dO read once and dq, dk, dv
+    written once (3 * 256 + 256 + 3 * 512 = 2,560 B per token-head) plus the states."""
+    import numpy as np
+
+    import workloads
+
+    H = 64
+    shape = (batch, seqlen, H, D)
+    q, k, v = workloads.qkv_device(1002, shape, "bf16")
+    do = workloads.gate_device(1020, shape, "bf16")
+    slopes = torch.from_numpy(workloads.slopes(H)).cuda()
+    ds = workloads.state_device(1021, (batch, H, D, D), std=0.1)
+    dq, dk, dv = (torch.empty(shape, device="cuda", dtype=torch.float32) for _ in range(3))
+    dsi = torch.empty((batch, H, D, D), device="cuda", dtype=torch.float32)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        la.lt_prefill_backward(q, k, v, do, slopes, 256, None, ds, dq=dq, dk=dk, dv=dv,
+                               d_state_in=dsi, stream=stream)
+    for _ in range(warmup):
+        call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    assert bool(torch.isfinite(dk[0, 0]).all()), "non-finite backward output"
+    tokens = batch * seqlen
+    nbytes = tokens * H * D * (4 * 2 + 3 * 4) + 2 * batch * H * D * D * 4
+    gbs = nbytes / (ms / 1e3) / 1e9
+    return {"workload": f"backward [{batch}, {seqlen}, {H}, {D}] bf16 -> fp32 grads",
+            "tokens_per_s": round(tokens / (ms / 1e3), 1), "kernel_ms_mean": round(ms, 5),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "bytes_per_launch": nbytes,
+                         "kernel": "lt_prefill_backward call: dq forward pass + bwd_kv_kernel"}}
 
 
 def run_decode(la, torch, nsteps, warmup=5, norm_gate=False, slots=0):
@@ -414,6 +460,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-norm-gate", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--norm-gate-decode-steps", type=int, default=200)
     ap.add_argument("--workload", default="m1_layer",
                     choices=["m1_layer", "long_1m", "varlen", "tiny_f32"])
@@ -465,6 +512,13 @@ def main():
         if not args.no_decode:
             ng["decode"] = run_decode(la, torch, args.norm_gate_decode_steps, norm_gate=True)
             log(f"[bench] decode + norm_gate {ng['decode']['ms_per_step_median']:.4f} ms/step")
+    bwd = None
+    if not args.no_backward:
+        bwd = {}
+        for b_, l_ in ((1, 32768), (4, 8192)):
+            log(f"[bench] backward batch={b_} L={l_} H=64")
+            bwd[f"b{b_}_L{l_}"] = run_backward(la, torch, 10, 2, b_, l_)
+            log(f"[bench] backward {bwd[f'b{b_}_L{l_}']['kernel_ms_mean']:.3f} ms/call")
     cpu = None
     if not args.no_cpu:
         log(f"[bench] cpu oracle on {args.cpu_tokens} tokens")
@@ -490,6 +544,7 @@ def main():
         "kernel_ms_mean": round(pre["kernel_ms_mean"], 5),
         "decode": dec,
         "norm_gate": ng,
+        "backward": bwd,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

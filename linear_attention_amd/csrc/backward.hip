@@ -25,6 +25,9 @@
 //    (K, V ⊙ d_k);
 //  * sub-blocks are anchored at the end of the sequence (a short block, if
 //    any, comes last and covers the first tokens);
+//  * long sequences with few (sequence, head) pairs are cut into segments
+//    counted from the end, with a reverse pre-pass and the forward's combine
+//    kernel (see rev_piece_kernel);
 //  * dV and dK are staged through LDS (in the R^T buffer and the K, V tiles,
 //    free by then) and leave as whole rows; four barriers per sub-block.
 #include <hip/hip_runtime.h>
@@ -149,8 +152,113 @@ struct BwdStage {
     }
 };
 
+// ---------------------------------------------------------------------------
+// Long sequences with few (sequence, head) pairs are split as in the forward,
+// in mirrored token order (position t' = L - 1 - t): segment g covers real
+// tokens [L - (g+1) seg_len, L - g seg_len) (the last one starts at 0), and the
+// first (segments-1) segments from the end are cut into pre-pass pieces. In
+// these coordinates the carry R composes exactly like the forward state, with
+// dS in place of S_0, so the forward's combine kernel gives every segment its
+// starting carry. A piece's contribution, from zero at its real end p1 back to
+// its real start p0, is sum_i e^{-s(i - p0 + 1)} q_i^T dO_i: the carry update
+// over the piece's sub-blocks walked backward.
+struct RevStage {
+    uint4 q[2], g[2];
+
+    __device__ void load(const uint16_t *qg, const uint16_t *gg, int ts, int tid) {
+        const int seg = tid & 15;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int row = ((tid >> 4) + 32 * i) * ts + 8 * seg;
+            q[i] = stream_load16(qg + row);
+            g[i] = stream_load16(gg + row);
+        }
+    }
+    // Q ⊙ d_q (d_q[t] = e^{-s(t+1)}) and dO, full sub-blocks only
+    __device__ void store(__bf16 *Qds, __bf16 *Gs, float s2, int tid) {
+        const int seg = tid & 15;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int t = (tid >> 4) + 32 * i;
+            const int off = L128::off(t, 8 * seg);
+            *reinterpret_cast<uint4 *>(Qds + off) = scale_bf16x8(q[i], fast_exp2(-s2 * (float)(t + 1)));
+            *reinterpret_cast<uint4 *>(Gs + off) = g[i];
+        }
+    }
+};
+
+__global__ __launch_bounds__(NT, 4) void rev_piece_kernel(BackwardArgs a, Segmented sp, float *ws) {
+    __shared__ __attribute__((aligned(16))) __bf16 Qds[C * D];
+    __shared__ __attribute__((aligned(16))) __bf16 Gs[C * D];
+
+    const int j = blockIdx.x % sp.pieces;
+    const int uh = blockIdx.x / sp.pieces;
+    const int h = uh % a.heads, n = uh / a.heads;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qh = w >> 2, cq = w & 3, r32 = lane & 31, hf = lane >> 5;
+
+    // mirrored range [t0, t1) = real tokens [L - t1, L - t0)
+    const long long L = a.seqlen;
+    const long long t0 = j * sp.piece_len;
+    const long long t1 = t0 + sp.piece_len < sp.covered() ? t0 + sp.piece_len : sp.covered();
+    const int ts = a.heads * D;
+    const long long seq = (long long)n * L * a.heads;
+    const uint16_t *qg = static_cast<const uint16_t *>(a.q) + (seq + h) * (long long)D;
+    const uint16_t *gg = static_cast<const uint16_t *>(a.dout) + (seq + h) * (long long)D;
+    const float s2 = a.slopes[h] * LOG2E;
+    float *u = sp.unit(ws, uh);
+
+    f32x16 R[2];
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) R[db][v] = 0.f;
+    auto store_state = [&](int slot) {
+        asm volatile("" : "+s"(slot));
+        float *dst = Segmented::slot(u, slot);
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                dst[(64 * qh + 32 * db + 8 * (v >> 2) + 4 * hf + (v & 3)) * D + 32 * cq + r32] = R[db][v];
+    };
+
+    // sub-block k covers real tokens [L - t0 - 64(k+1), L - t0 - 64k)
+    const long long nch = (t1 - t0) / C;  // even, >= 2
+    const float bd = fast_exp2(-s2 * (float)C);
+    RevStage st0, st1;
+    auto prefetch = [&](RevStage &st, long long k) {
+        const long long kk = k < nch ? k : nch - 1;
+        const long long off = (L - t0 - C * (kk + 1)) * (long long)ts;
+        st.load(qg + off, gg + off, ts, tid);
+    };
+    auto step = [&](long long k, RevStage &st) {
+        __syncthreads();
+        st.store(Qds, Gs, s2, tid);
+        prefetch(st, k + 2);
+        __syncthreads();
+        state_update(R, Qds, Gs, bd, qh, cq, lane);
+    };
+    auto run = [&](long long k0, long long k1) {
+        for (long long k = k0; k < k1; k += 2) {
+            step(k, st0);
+            step(k + 1, st1);
+        }
+    };
+    prefetch(st0, 0);
+    prefetch(st1, 1);
+    const int gb = (int)(t0 / sp.seg_len) + 1;  // first mirrored segment boundary after t0
+    const long long b = gb * sp.seg_len;
+    const long long cb = b < t1 ? (b - t0) / C : nch;
+    run(0, cb);
+    store_state(b < t1 ? sp.partial_slot(gb) : j);
+    run(cb, nch);
+    store_state(j);
+}
+
 template <typename OutT>
-__global__ __launch_bounds__(NT) void bwd_kv_kernel(BackwardArgs a) {
+__global__ __launch_bounds__(NT) void bwd_kv_kernel(BackwardArgs a, Segmented sp, float *ws) {
     __shared__ __attribute__((aligned(16))) __bf16 Qs[C * PT];
     __shared__ __attribute__((aligned(16))) __bf16 KVs[2][C * PT];  // K, V; dK staging (fp32)
     __shared__ __attribute__((aligned(16))) __bf16 Gs[C * PT];      // dO
@@ -162,15 +270,20 @@ __global__ __launch_bounds__(NT) void bwd_kv_kernel(BackwardArgs a) {
     static_assert(sizeof(float) * C * PO <= 2 * sizeof(__bf16) * C * PT, "dK staging fits K, V");
     __bf16 *Ks = KVs[0], *Vs = KVs[1];
 
-    const int uh = blockIdx.x;
+    const int g = blockIdx.x % sp.segments;  // mirrored segment (0 = the end of the sequence)
+    const int uh = blockIdx.x / sp.segments;
     const int h = uh % a.heads, n = uh / a.heads;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int qh = w >> 2, cq = w & 3, r32 = lane & 31, hf = lane >> 5;
 
-    const long long len = a.seqlen;
+    // real tokens [seg_lo, seg_hi) of this segment
+    const long long L = a.seqlen;
+    const long long seg_hi = L - g * sp.seg_len;
+    const long long seg_lo = seg_hi - sp.seg_len > 0 && g + 1 < sp.segments ? seg_hi - sp.seg_len : 0;
+    const long long len = seg_hi - seg_lo;
     const int ts = a.heads * D;
-    const long long base = ((long long)n * len * a.heads + h) * (long long)D;
+    const long long base = (((long long)n * L + seg_lo) * a.heads + h) * (long long)D;
     const uint16_t *qg = static_cast<const uint16_t *>(a.q) + base;
     const uint16_t *kg = static_cast<const uint16_t *>(a.k) + base;
     const uint16_t *vg = static_cast<const uint16_t *>(a.v) + base;
@@ -184,12 +297,13 @@ __global__ __launch_bounds__(NT) void bwd_kv_kernel(BackwardArgs a) {
     auto sidx = [&](int db, int v) {
         return (64 * qh + 32 * db + 8 * (v >> 2) + 4 * hf + (v & 3)) * D + 32 * cq + r32;
     };
-    if (a.d_state_out) {
-        const float *src = a.d_state_out + (size_t)uh * D * D;
+    const float *r_in = sp.segments > 1 ? sp.start_state(sp.unit(ws, uh), g)
+                                        : (a.d_state_out ? a.d_state_out + (size_t)uh * D * D : nullptr);
+    if (r_in) {
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) R[db][v] = src[sidx(db, v)];
+            for (int v = 0; v < 16; ++v) R[db][v] = r_in[sidx(db, v)];
     } else {
 #pragma unroll
         for (int db = 0; db < 2; ++db)
@@ -310,7 +424,7 @@ __global__ __launch_bounds__(NT) void bwd_kv_kernel(BackwardArgs a) {
             step(p, head_len, std::false_type{}, st0);
     }
 
-    if (a.d_state_in) {
+    if (a.d_state_in && g == sp.segments - 1) {  // the segment holding token 0
         float *dst = a.d_state_in + (size_t)uh * D * D;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
@@ -320,17 +434,34 @@ __global__ __launch_bounds__(NT) void bwd_kv_kernel(BackwardArgs a) {
 }
 
 template <typename OutT>
-hipError_t launch(const BackwardArgs &a, hipStream_t stream) {
+hipError_t launch(const BackwardArgs &a, const PrefillPlan &p, void *workspace, hipStream_t stream) {
     clear_pending_error();
     const long long uh = (long long)a.units * a.heads;
-    hipLaunchKernelGGL((bwd_kv_kernel<OutT>), dim3((unsigned)uh), dim3(NT), 0, stream, a);
+    float *ws = static_cast<float *>(workspace);
+    const bool seg = p.segments > 1 && p.value_slices == 1;
+    const Segmented sp = seg ? Segmented{p.segments, p.pieces, p.seg_len, p.piece_len}
+                             : Segmented{1, 0, a.seqlen, 0};
+    if (seg) {
+        hipLaunchKernelGGL(rev_piece_kernel, dim3((unsigned)(uh * p.pieces)), dim3(NT), 0, stream, a,
+                           sp, ws);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(uh * kCombineSlices)), dim3(kCombineThreads),
+                           0, stream, a.slopes, a.heads, a.d_state_out, false, sp, ws);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((bwd_kv_kernel<OutT>), dim3((unsigned)(uh * sp.segments)), dim3(NT), 0, stream,
+                       a, sp, ws);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_backward_kv(const BackwardArgs &a, lt_dtype out_dtype, hipStream_t stream) {
-    return out_dtype == LT_F32 ? launch<float>(a, stream) : launch<__bf16>(a, stream);
+hipError_t launch_backward_kv(const BackwardArgs &a, const PrefillPlan &plan, void *workspace,
+                              lt_dtype out_dtype, hipStream_t stream) {
+    return out_dtype == LT_F32 ? launch<float>(a, plan, workspace, stream)
+                               : launch<__bf16>(a, plan, workspace, stream);
 }
 
 }  // namespace lt

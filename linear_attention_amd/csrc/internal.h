@@ -109,7 +109,11 @@ struct BackwardArgs {
     int units;
     int heads;
 };
-hipError_t launch_backward_kv(const BackwardArgs &a, lt_dtype out_dtype, hipStream_t stream);
+// With a segmented plan (segments > 1, workspace of plan.workspace bytes) the
+// reverse pass is split like the forward, in mirrored token order: segments
+// and pre-pass pieces are counted from the end of each sequence.
+hipError_t launch_backward_kv(const BackwardArgs &a, const PrefillPlan &plan, void *workspace,
+                              lt_dtype out_dtype, hipStream_t stream);
 
 // fp32 inputs: one workgroup per (unit, head, 32-column value slice).
 hipError_t launch_prefill_slices(const PrefillArgs &a, lt_dtype in_dtype, lt_dtype out_dtype,

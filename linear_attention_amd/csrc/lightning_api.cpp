@@ -434,7 +434,14 @@ LT_API lt_status lt_prefill_backward(const void *q, const void *k, const void *v
     if (tokens == 0 && !d_state_in) return LT_OK;
     const lt::BackwardArgs b{q, k, v, dout, slopes, d_state_out, dk, dv, d_state_in, seqlen,
                              batch, heads};
-    return map_hip(lt::launch_backward_kv(b, grad_dtype, st));
+    // the reverse pass splits long sequences like the forward when the
+    // workspace allows (the dq pass above has finished with it by then)
+    lt::PrefillPlan p = lt::plan_prefill(batch, seqlen, heads, LT_BF16, false);
+    if (p.value_slices != 1 || (p.workspace > 0 && (!workspace || workspace_bytes < p.workspace))) {
+        p = lt::PrefillPlan{};
+        p.seg_len = seqlen;
+    }
+    return map_hip(lt::launch_backward_kv(b, p, workspace, grad_dtype, st));
 }
 
 LT_API lt_status lt_decode_slots(const void *q, const void *k, const void *v, lt_dtype in_dtype,

@@ -270,5 +270,80 @@ __device__ __forceinline__ SeqRange sequence_of(const PrefillArgs &a, int n) {
     return {(long long)n * a.seqlen, a.seqlen};
 }
 
+// ---------------------------------------------------------------------------
+// Segmented plans. Sequence (unit, head) is cut into `segments` segments of
+// seg_len tokens; the first covered = (segments-1)*seg_len tokens are cut again
+// into `pieces` pre-pass pieces of piece_len tokens (piece_len <= seg_len; both
+// multiples of 128, so every piece and part of a piece is an even number of
+// 64-token sub-blocks). Workspace per (unit, head), fp32 d x d states:
+//   [P_0 .. P_{pieces-1}]       state of each piece's tokens from a zero state
+//   [B_1 .. B_{segments-1}]     for a boundary inside a piece: the state of that
+//                               piece's tokens before the boundary
+//   [S_0 .. S_{segments-1}]     state at the start of each segment
+// A state of tokens [t0, t1) from zero is sum_t e^{-s(t1-1-t)} k_t^T v_t, and
+// states compose as S(t2) = e^{-s(t2-t1)} S(t1) + state of [t1, t2).
+struct Segmented {
+    int segments, pieces;
+    long long seg_len, piece_len;
+    __device__ long long covered() const { return (segments - 1) * seg_len; }
+    __device__ float *unit(float *ws, int uh) const {
+        return ws + (size_t)uh * (size_t)(pieces + 2 * segments - 1) * D * D;
+    }
+    __device__ static float *slot(float *u, long long i) { return u + (size_t)i * D * D; }
+    __device__ float *piece_state(float *u, int j) const { return slot(u, j); }
+    __device__ int partial_slot(int g) const { return pieces + g - 1; }
+    __device__ float *partial(float *u, int g) const { return slot(u, partial_slot(g)); }
+    __device__ float *start_state(float *u, int g) const { return slot(u, pieces + segments - 1 + g); }
+};
+
+// Combine pass: the state at every segment start, S_0 being the first state
+// (the carried-in state, or zero). Workgroup (unit, head, 1024-element slice) walks the pieces
+// in order with 4 elements per thread:
+//   acc <- e^{-s len_j} acc + P_j,
+// and at each boundary b_g: S_g = acc if b_g ends piece j, or
+// e^{-s(b_g - start_j)} acc + B_g if it falls inside piece j.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineSlices = D * D / (4 * kCombineThreads);
+
+// s0: [units, heads, d, d] first state (null: zero); s0_t: given transposed.
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float *slopes, int heads,
+                                                                   const float *s0, bool s0_t,
+                                                                   Segmented sp, float *ws) {
+    const int uh = blockIdx.x / kCombineSlices;
+    const int e = 4 * ((blockIdx.x % kCombineSlices) * kCombineThreads + threadIdx.x);
+    const int h = uh % heads;
+    const float s2 = slopes[h] * LOG2E;
+    float *u = sp.unit(ws, uh);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (s0) {
+        const float *si = s0 + (size_t)uh * D * D;
+        if (s0_t) {  // element (r, c) at c * D + r
+            const int r = e / D, c = e % D;
+            acc = make_float4(si[c * D + r], si[(c + 1) * D + r], si[(c + 2) * D + r], si[(c + 3) * D + r]);
+        } else {
+            acc = *reinterpret_cast<const float4 *>(si + e);
+        }
+    }
+    *reinterpret_cast<float4 *>(sp.start_state(u, 0) + e) = acc;
+    const long long covered = sp.covered();
+    for (int j = 0; j < sp.pieces; ++j) {
+        const long long t0 = j * sp.piece_len;
+        const long long t1 = t0 + sp.piece_len < covered ? t0 + sp.piece_len : covered;
+        const int gb = (int)(t0 / sp.seg_len) + 1;
+        const long long b = gb * sp.seg_len;
+        if (b < t1) {
+            const float f = fast_exp2(-s2 * (float)(b - t0));
+            const float4 p = *reinterpret_cast<const float4 *>(sp.partial(u, gb) + e);
+            *reinterpret_cast<float4 *>(sp.start_state(u, gb) + e) =
+                make_float4(f * acc.x + p.x, f * acc.y + p.y, f * acc.z + p.z, f * acc.w + p.w);
+        }
+        const float f = fast_exp2(-s2 * (float)(t1 - t0));
+        const float4 p = *reinterpret_cast<const float4 *>(sp.piece_state(u, j) + e);
+        acc = make_float4(f * acc.x + p.x, f * acc.y + p.y, f * acc.z + p.z, f * acc.w + p.w);
+        if (t1 % sp.seg_len == 0)
+            *reinterpret_cast<float4 *>(sp.start_state(u, (int)(t1 / sp.seg_len)) + e) = acc;
+    }
+}
+
 }  // namespace
 }  // namespace lt

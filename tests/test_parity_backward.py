@@ -24,11 +24,11 @@ def la():
     return linear_attention_amd
 
 
-def backward_case(la, batch, L, H, seed, with_state=False, grad_dtype="f32"):
+def backward_case(la, batch, L, H, seed, with_state=False, grad_dtype="f32", workspace="auto"):
     import torch
 
     print(f"[case] backward batch={batch} L={L} H={H} seed={seed} state={with_state} "
-          f"grad={grad_dtype}", flush=True)
+          f"grad={grad_dtype} ws={workspace}", flush=True)
     q, k, v = workloads.qkv_host(seed, (batch, L, H, 128), "bf16")
     do = workloads.gate_host(seed + 1, (batch, L, H, 128), "bf16")  # N(0, 1) bf16
     sl = workloads.slopes(H)
@@ -38,7 +38,8 @@ def backward_case(la, batch, L, H, seed, with_state=False, grad_dtype="f32"):
     dq, dk, dv, dsi = la.lt_prefill_backward(
         to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16"), to_device(do, "bf16"),
         torch.from_numpy(sl).cuda(), 256, None if s0 is None else torch.from_numpy(s0).cuda(),
-        None if ds is None else torch.from_numpy(ds).cuda(), grad_dtype=gd)
+        None if ds is None else torch.from_numpy(ds).cuda(), grad_dtype=gd,
+        **({"workspace": torch.empty(0, device="cuda", dtype=torch.uint8)} if workspace == "none" else {}))
     torch.cuda.synchronize()
     rq, rk, rv, rs = oracle.backward_batch(q, k, v, do, sl, s0=s0, ds=ds)
     errs = {}
@@ -61,9 +62,11 @@ def test_backward_batch_and_state(la):
     assert max(errs.values()) <= TOL_BF16, errs
 
 
-@pytest.mark.parametrize("L,H", [(9000, 1), (5000, 2)])
+@pytest.mark.parametrize("L,H", [(9000, 1), (5000, 2), (20000, 3), (16384, 4)])
 def test_backward_long_sequences(la, L, H):
-    """Long sequences: the dq pass takes the segmented forward plan."""
+    """Long sequences with few heads: the dq pass takes the segmented forward
+    plan and the reverse pass its mirrored segments (pieces with boundaries
+    inside and at their ends)."""
     errs = backward_case(la, 1, L, H, 1500 + L, with_state=True)
     assert max(errs.values()) <= TOL_BF16, errs
 
@@ -88,3 +91,9 @@ def test_backward_zero_length_passes_state_gradient(la):
                                           64, None, torch.from_numpy(ds).cuda())
     torch.cuda.synchronize()
     assert np.array_equal(to_host_f32(dsi), ds)
+
+
+def test_backward_long_sequence_without_workspace(la):
+    """No workspace: one workgroup per (sequence, head) in both passes."""
+    errs = backward_case(la, 1, 9000, 2, 1901, with_state=True, workspace="none")
+    assert max(errs.values()) <= TOL_BF16, errs
