@@ -87,6 +87,33 @@ def test_m1_layer_norm_gate_all_heads(la):
     assert worst_y <= TOL_BF16 and worst_s <= TOL_BF16
 
 
+def test_m1_layer_backward_all_heads(la):
+    """lt_prefill_backward on the M1 layer (batch 1, 32768 tokens, 64 heads, fp32
+    gradients, with a final-state gradient), every head against the oracle."""
+    import torch
+
+    w = workloads.M1_LAYER
+    print(f"[case] {w.name} backward L={w.seqlen} H={w.heads}", flush=True)
+    shape = (1, w.seqlen, w.heads, 128)
+    q, k, v = workloads.qkv_device(w.seed, shape, "bf16")
+    do = workloads.gate_device(w.seed + 20, shape, "bf16")
+    ds = workloads.state_device(w.seed + 21, (1, w.heads, 128, 128), std=0.1)
+    sl = workloads.slopes(w.heads)
+    dq, dk, dv, dsi = la.lt_prefill_backward(q, k, v, do, torch.from_numpy(sl).cuda(), w.block,
+                                             None, ds)
+    torch.cuda.synchronize()
+    hq, hk, hv, hdo = (to_host_f32(x) for x in (q, k, v, do))
+    rq, rk, rv, rs = oracle.backward_batch(hq, hk, hv, hdo, sl, ds=to_host_f32(ds))
+    worst = {}
+    for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        gh = to_host_f32(g)
+        worst[name] = max(rel_l2(gh[0, :, h], r[0, :, h]) for h in range(w.heads))
+    sg = to_host_f32(dsi)
+    worst["ds0"] = max(rel_l2(sg[0, h], rs[0, h]) for h in range(w.heads))
+    print(f"[result] worst rel L2 {worst}", flush=True)
+    assert max(worst.values()) <= TOL_BF16
+
+
 def test_long_context_1m_sampled_heads(la):
     import torch
 
