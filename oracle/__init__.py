@@ -23,6 +23,11 @@ Three independent formulations of the same operator, all in fp64:
     Gradients of ``sum(dO * O) + <dS, S_final>`` with respect to q, k, v and
     S0: the reverse-mode derivative of the per-token recurrence (compiled C;
     the pages give no backward).
+``softmax_attention`` / ``softmax_decode``
+    The hybrid's other attention type (MiniMax Signal Lab · M1, §02: 64 query
+    heads of 128, K/V 8 x 128, RoPE on 64 of 128 dims in the softmax layers
+    only): causal softmax attention with grouped K/V heads and partial
+    rotary position embedding, and its one-token decode over a KV cache.
 ``decode_slots``
     One decode step over a pool of per-sequence states addressed by slot ids
     (concurrent sequences, each with the fixed-size state of §04).
@@ -398,3 +403,91 @@ def backward_batch(q, k, v, dout, slopes, s0=None, ds=None, threads=0):
     dq, dk, dv, ds0 = backward_packed(flat(q), flat(k), flat(v), flat(dout), slopes, cu,
                                       s0=s0, ds=ds, threads=threads)
     return dq.reshape(B, L, H, d), dk.reshape(B, L, H, d), dv.reshape(B, L, H, d), ds0
+
+
+def rope(x, positions, rope_dims, base):
+    """Rotary position embedding on the first ``rope_dims`` features, rotate-half
+    pairing: feature m and m + rope_dims/2 (m < rope_dims/2) rotate by the angle
+    position * base^(-2m/rope_dims); features past rope_dims are unchanged.
+
+    x: [..., T, H, d] (T = token axis -3); positions: [T] absolute positions.
+    """
+    x = np.asarray(x, np.float64)
+    out = x.copy()
+    if rope_dims == 0:
+        return out
+    half = rope_dims // 2
+    m = np.arange(half, dtype=np.float64)
+    theta = np.float64(base) ** (-2.0 * m / rope_dims)
+    ang = np.asarray(positions, np.float64)[:, None] * theta[None, :]  # [T, half]
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    x1, x2 = x[..., :half], x[..., half:rope_dims]
+    out[..., :half] = x1 * c - x2 * s
+    out[..., half:rope_dims] = x1 * s + x2 * c
+    return out
+
+
+def softmax_attention(q, k, v, rope_dims=64, base=10000.0, scale=None, pos0=0):
+    """Causal softmax attention with grouped K/V heads and partial RoPE, fp64.
+
+    q: [B, L, Hq, d]; k, v: [B, L, Hkv, d] with Hq a multiple of Hkv: query head
+    h reads K/V head h // (Hq / Hkv). Token t sits at position pos0 + t.
+    o_t = sum_{j <= t} softmax_j(scale * rope(q_t) . rope(k_j)) v_j, scale
+    1/sqrt(d) by default. Returns o [B, L, Hq, d] fp64.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    B, L, Hq, d = q.shape
+    Hkv = k.shape[2]
+    grp = Hq // Hkv
+    sc = 1.0 / np.sqrt(d) if scale is None else np.float64(scale)
+    pos = pos0 + np.arange(L)
+    qr, kr = rope(q, pos, rope_dims, base), rope(k, pos, rope_dims, base)
+    o = np.zeros((B, L, Hq, d))
+    mask = np.tril(np.ones((L, L), bool))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // grp
+            s = sc * (qr[b, :, h] @ kr[b, :, g].T)
+            s = np.where(mask, s, -np.inf)
+            s = s - s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            p /= p.sum(axis=1, keepdims=True)
+            o[b, :, h] = p @ v[b, :, g]
+    return o
+
+
+def softmax_decode(q, k_new, v_new, k_cache, v_cache, lengths, rope_dims=64, base=10000.0,
+                   scale=None):
+    """One decode step over a KV cache, fp64.
+
+    Sequence b's new token sits at position lengths[b]: rope(k_new) and v_new are
+    appended at that position and rope(q) attends over positions 0..lengths[b].
+    q: [B, Hq, d]; k_new, v_new: [B, Hkv, d]; k_cache, v_cache: [B, cap, Hkv, d]
+    holding rope-applied keys and values at positions < lengths[b]. A length
+    outside [0, cap) marks a padding row: zero output, cache untouched.
+    Returns (o [B, Hq, d], k_cache, v_cache) with the new entries written.
+    """
+    q = np.asarray(q, np.float64)
+    kc = np.array(k_cache, np.float64)
+    vc = np.array(v_cache, np.float64)
+    B, Hq, d = q.shape
+    Hkv = kc.shape[2]
+    grp = Hq // Hkv
+    sc = 1.0 / np.sqrt(d) if scale is None else np.float64(scale)
+    o = np.zeros((B, Hq, d))
+    for b in range(B):
+        n = int(lengths[b])
+        if n < 0 or n >= kc.shape[1]:
+            continue
+        kc[b, n] = rope(np.asarray(k_new, np.float64)[b][None], [n], rope_dims, base)[0]
+        vc[b, n] = np.asarray(v_new, np.float64)[b]
+        qr = rope(q[b][None], [n], rope_dims, base)[0]
+        for h in range(Hq):
+            g = h // grp
+            s = sc * (kc[b, :n + 1, g] @ qr[h])
+            p = np.exp(s - s.max())
+            o[b, h] = (p / p.sum()) @ vc[b, :n + 1, g]
+    return o, kc, vc

@@ -663,3 +663,177 @@ def test_backward_batch_matches_units():
             r = c_bwd(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h], float(sl[h]), s0[b, h], ds[b, h])
             for got, want in zip((dq[b, :, h], dk[b, :, h], dv[b, :, h], ds0[b, h]), r):
                 assert rel(got, want) < 1e-14
+
+
+# --------------------------------------------------------------------------
+# Softmax GQA attention with partial RoPE (oracle.rope / softmax_attention /
+# softmax_decode)
+# --------------------------------------------------------------------------
+
+def rope_pin_failures(f):
+    """Pins of a rope(x, positions, rope_dims, base) function."""
+    bad = []
+    g = np.random.Generator(np.random.PCG64(51))
+    d, R = 8, 4
+    # explicit rotation: position 1, pair m = 0 (theta = 1), pair m = 1 (theta = base^-1/2)
+    x = g.standard_normal((1, 1, d))
+    y = f(x, [1], R, 100.0)
+    for m, th in ((0, 1.0), (1, 100.0 ** -0.5)):
+        a, b = x[0, 0, m], x[0, 0, m + R // 2]
+        want = (a * math.cos(th) - b * math.sin(th), a * math.sin(th) + b * math.cos(th))
+        if abs(y[0, 0, m] - want[0]) > 1e-12 or abs(y[0, 0, m + R // 2] - want[1]) > 1e-12:
+            bad.append(f"rotation pair {m}")
+    if not np.array_equal(y[0, 0, R:], x[0, 0, R:]):
+        bad.append("unrotated features changed")
+    # norm of every rotated pair preserved; rope_dims = 0 is the identity
+    xs = g.standard_normal((7, 3, d))
+    ys = f(xs, np.arange(7) * 13 + 5, R, 10000.0)
+    for m in range(R // 2):
+        if np.max(np.abs(np.hypot(ys[..., m], ys[..., m + R // 2]) - np.hypot(xs[..., m], xs[..., m + R // 2]))) > 1e-12:
+            bad.append("pair norm")
+    if not np.array_equal(f(xs, np.arange(7), 0, 10000.0), xs):
+        bad.append("rope_dims 0")
+    # relative position: rope(q, p1) . rope(k, p2) depends on p1 - p2 only
+    q1, k1 = g.standard_normal((1, 1, d)), g.standard_normal((1, 1, d))
+    dots = [float(np.sum(f(q1, [p + 9], R, 10000.0) * f(k1, [p], R, 10000.0))) for p in (0, 5, 1234)]
+    if max(dots) - min(dots) > 1e-10:
+        bad.append("relative position")
+    return bad
+
+
+def test_rope_passes_pins():
+    assert rope_pin_failures(oracle.rope) == []
+
+
+def _rope_interleaved(x, positions, rope_dims, base):
+    x = np.asarray(x, np.float64)
+    out = x.copy()
+    half = rope_dims // 2
+    th = np.float64(base) ** (-2.0 * np.arange(half) / rope_dims)
+    ang = np.asarray(positions, np.float64)[:, None] * th[None, :]
+    c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    a, b = x[..., 0:rope_dims:2], x[..., 1:rope_dims:2]
+    out[..., 0:rope_dims:2] = a * c - b * s
+    out[..., 1:rope_dims:2] = a * s + b * c
+    return out
+
+
+def _rope_last_half(x, positions, rope_dims, base):
+    x = np.asarray(x, np.float64)
+    d = x.shape[-1]
+    y = oracle.rope(x[..., ::-1], positions, rope_dims, base)  # rotates the last features
+    return y[..., ::-1]
+
+
+@pytest.mark.parametrize("mutant", [_rope_interleaved, _rope_last_half])
+def test_rope_mutants_fail_pins(mutant):
+    assert rope_pin_failures(mutant)
+
+
+def softmax_pin_failures(f):
+    """Pins of f(q, k, v, rope_dims, base, scale, pos0) -> o (causal GQA attention)."""
+    import torch
+
+    bad = []
+    g = np.random.Generator(np.random.PCG64(52))
+    B, L, Hq, Hkv, d, R = 2, 13, 4, 2, 8, 4
+    q, k, v = g.standard_normal((B, L, Hq, d)), g.standard_normal((B, L, Hkv, d)), g.standard_normal((B, L, Hkv, d))
+    # 1. torch's scaled_dot_product_attention (fp64, CPU) on pre-rotated inputs
+    for pos0, scale in ((0, None), (7, 0.3)):
+        o = f(q, k, v, R, 10000.0, scale, pos0)
+        pos = pos0 + np.arange(L)
+        qr, kr = oracle.rope(q, pos, R, 10000.0), oracle.rope(k, pos, R, 10000.0)
+        tq = torch.from_numpy(qr).permute(0, 2, 1, 3)
+        tk = torch.from_numpy(kr).permute(0, 2, 1, 3).repeat_interleave(Hq // Hkv, dim=1)
+        tv = torch.from_numpy(v).permute(0, 2, 1, 3).repeat_interleave(Hq // Hkv, dim=1)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            tq, tk, tv, is_causal=True, scale=(1 / math.sqrt(d) if scale is None else scale))
+        if not (rel(o, ref.permute(0, 2, 1, 3).numpy()) <= 1e-12):
+            bad.append(f"sdpa pos0={pos0}")
+    # 2. q = 0: uniform weights, o_t = mean(v_0..v_t)
+    o = f(np.zeros_like(q), k, v, R, 10000.0, None, 0)
+    want = np.cumsum(v, axis=1) / np.arange(1, L + 1)[None, :, None, None]
+    if not (rel(o[:, :, ::Hq // Hkv], want) <= 1e-12) or not (rel(o[:, :, 1::Hq // Hkv], want) <= 1e-12):
+        bad.append("uniform")
+    # 3. one token: o = v_0 of the head's group
+    o = f(q[:, :1], k[:, :1], v[:, :1], R, 10000.0, None, 3)
+    if not (rel(o, np.repeat(v[:, :1], Hq // Hkv, axis=2)) <= 1e-12):
+        bad.append("single key")
+    # 4. absolute shift invariance (RoPE is relative)
+    if not (rel(f(q, k, v, R, 10000.0, None, 0), f(q, k, v, R, 10000.0, None, 1000)) <= 1e-10):
+        bad.append("shift invariance")
+    # 5. grouped heads: equal queries in one group give equal outputs; another
+    #    group's K/V do not matter
+    q2 = q.copy()
+    q2[:, :, 1] = q2[:, :, 0]
+    o = f(q2, k, v, R, 10000.0, None, 0)
+    k3 = k.copy()
+    k3[:, :, 1] += 5.0
+    o3 = f(q2, k3, v, R, 10000.0, None, 0)
+    if not (rel(o[:, :, 1], o[:, :, 0]) <= 1e-14) or not (rel(o3[:, :, :2], o[:, :, :2]) <= 1e-14):
+        bad.append("grouped heads")
+    return bad
+
+
+def _sm(q, k, v, R, base, scale, pos0):
+    return oracle.softmax_attention(q, k, v, rope_dims=R, base=base, scale=scale, pos0=pos0)
+
+
+def test_softmax_attention_passes_pins():
+    assert softmax_pin_failures(_sm) == []
+
+
+def _sm_mutant(mistake):
+    def f(q, k, v, R, base, scale, pos0):
+        q = np.asarray(q, np.float64)
+        k = np.asarray(k, np.float64)
+        v = np.asarray(v, np.float64)
+        B, L, Hq, d = q.shape
+        Hkv = k.shape[2]
+        sc = 1.0 / np.sqrt(d) if scale is None else scale
+        if mistake == "no_scale":
+            sc = 1.0
+        pos = pos0 + np.arange(L)
+        qr, kr = oracle.rope(q, pos, R, base), oracle.rope(k, pos, R, base)
+        if mistake == "rope_q_only":
+            kr = k
+        mask = np.tril(np.ones((L, L), bool), k=-1 if mistake == "strict_mask" else 0)
+        o = np.zeros((B, L, Hq, d))
+        for b in range(B):
+            for h in range(Hq):
+                gh = h % Hkv if mistake == "head_modulo" else h // (Hq // Hkv)
+                s = sc * (qr[b, :, h] @ kr[b, :, gh].T)
+                s = np.where(mask, s, -np.inf)
+                p = np.exp(s - s.max(axis=1, keepdims=True))
+                o[b, :, h] = (p / p.sum(axis=1, keepdims=True)) @ v[b, :, gh]
+        return o
+    return f
+
+
+@pytest.mark.parametrize("mistake", ["no_scale", "strict_mask", "head_modulo", "rope_q_only"])
+def test_softmax_mutants_fail_pins(mistake):
+    with np.errstate(all="ignore"):
+        assert softmax_pin_failures(_sm_mutant(mistake)), mistake
+
+
+def test_softmax_unmutated_mutant_passes():
+    assert softmax_pin_failures(_sm_mutant(None)) == []
+
+
+def test_softmax_decode_matches_last_prefill_row():
+    """Decode over a cache of the first n tokens (rope applied) equals row n of the
+    prefill; the cache gains the new entries; padding rows stay zero."""
+    g = np.random.Generator(np.random.PCG64(53))
+    B, L, Hq, Hkv, d, R, cap = 3, 10, 4, 2, 8, 4, 16
+    q, k, v = g.standard_normal((B, L, Hq, d)), g.standard_normal((B, L, Hkv, d)), g.standard_normal((B, L, Hkv, d))
+    o_full = oracle.softmax_attention(q, k, v, rope_dims=R)
+    n = L - 1
+    kc = np.zeros((B, cap, Hkv, d))
+    vc = np.zeros((B, cap, Hkv, d))
+    kc[:, :n] = oracle.rope(k[:, :n], np.arange(n), R, 10000.0)
+    vc[:, :n] = v[:, :n]
+    lengths = np.array([n, n, cap])  # the last row is padding (length == capacity)
+    o, kc2, vc2 = oracle.softmax_decode(q[:, n], k[:, n], v[:, n], kc, vc, lengths, rope_dims=R)
+    assert rel(o[:2], o_full[:2, n]) < 1e-12
+    assert np.all(o[2] == 0) and np.array_equal(kc2[2], kc[2]) and np.array_equal(vc2[2], vc[2])
+    assert rel(kc2[:2, n], oracle.rope(k[:2, n][:, None], [n], R, 10000.0)[:, 0]) < 1e-14
