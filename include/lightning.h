@@ -259,6 +259,39 @@ LT_API lt_status lt_decode_norm_gate(const void *q, const void *k, const void *v
                                      void *y, lt_dtype out_dtype, int batch, int heads,
                                      int head_dim, void *stream);
 
+/*
+ * lt_softmax_prefill - causal softmax attention of the hybrid's softmax layers
+ * (MiniMax Signal Lab · M1, §02 Architecture: 64 query heads and 8 K/V heads
+ * of 128, rotary position embedding on 64 of the 128 dimensions). Query head h
+ * reads K/V head h / (q_heads / kv_heads). Token t sits at position pos0 + t:
+ *
+ *     o_t = sum_{j <= t} softmax_j(scale * rope(q_t) . rope(k_j)) v_j
+ *
+ * rope rotates feature pairs (m, m + rope_dims/2), m < rope_dims/2, by the
+ * angle position * rope_base^(-2m/rope_dims) (rotate-half pairing); features
+ * at or past rope_dims are not rotated. Angles are formed in double precision.
+ * Scores, softmax and sums run in fp32 (products on bf16 MFMA; the
+ * probabilities enter the value product as bf16).
+ *
+ *   q         [batch, seqlen, q_heads, head_dim] bf16.
+ *   k, v      [batch, seqlen, kv_heads, head_dim] bf16.
+ *   o         [batch, seqlen, q_heads, head_dim], out_dtype (LT_F32 or LT_BF16).
+ *   k_rope    [batch, seqlen, kv_heads, head_dim] bf16 output: rope(k), the
+ *             key rows a KV cache holds (lt_softmax_decode reads that form).
+ *   head_dim  128; q_heads a multiple of kv_heads (both 0 = nothing to do).
+ *   rope_dims a multiple of 32 in [0, head_dim].
+ *   rope_base > 1 (LT_ERR_VALUE otherwise); scale > 0 and finite
+ *             (LT_ERR_VALUE), usually 1/sqrt(head_dim).
+ *   pos0      >= 0, position of token 0.
+ *   No output may overlap an input or the other output (LT_ERR_ALIAS).
+ *   Errors: LT_ERR_NULL, LT_ERR_SHAPE, LT_ERR_DTYPE, LT_ERR_VALUE,
+ *   LT_ERR_ALIAS, LT_ERR_HIP.
+ */
+LT_API lt_status lt_softmax_prefill(const void *q, const void *k, const void *v, void *o,
+                                    lt_dtype out_dtype, void *k_rope, int batch, long long seqlen,
+                                    int q_heads, int kv_heads, int head_dim, int rope_dims,
+                                    double rope_base, float scale, long long pos0, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

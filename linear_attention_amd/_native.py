@@ -9,6 +9,7 @@ no fallback: if the library is missing, importing this module fails.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -21,9 +22,9 @@ HEAD_DIM = 128
 
 EXPORTS = ("lt_status_string", "lt_version", "lt_prefill", "lt_prefill_workspace_bytes",
            "lt_prefill_varlen", "lt_decode", "lt_prefill_norm_gate", "lt_prefill_varlen_norm_gate",
-           "lt_decode_norm_gate", "lt_decode_slots", "lt_prefill_backward")
+           "lt_decode_norm_gate", "lt_decode_slots", "lt_prefill_backward", "lt_softmax_prefill")
 
-_vp, _i, _ll, _f = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_float
+_vp, _i, _ll, _f, _d = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_float, ctypes.c_double
 
 
 class LightningError(RuntimeError):
@@ -74,6 +75,9 @@ def _load() -> ctypes.CDLL:
     lib.lt_prefill_backward.argtypes = [_vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp,
                                         _i, _ll, _i, _i, _i, _vp, ctypes.c_size_t, _vp]
     lib.lt_prefill_backward.restype = _i
+    lib.lt_softmax_prefill.argtypes = [_vp, _vp, _vp, _vp, _i, _vp, _i, _ll, _i, _i, _i, _i, _d, _f,
+                                       _ll, _vp]
+    lib.lt_softmax_prefill.restype = _i
     return lib
 
 
@@ -370,3 +374,29 @@ def lt_prefill_backward(q, k, v, dout, slopes, block, state_in=None, d_state_out
                                  _dev_ptr(workspace, "workspace"), ws_bytes, _stream(stream, q.device))
     _check(st, "lt_prefill_backward")
     return dq, dk, dv, d_state_in
+
+
+def lt_softmax_prefill(q, k, v, *, rope_dims=64, rope_base=10000.0, scale=None, pos0=0, o=None,
+                       out_dtype=None, k_rope=None, stream=None):
+    """Causal softmax attention with grouped K/V heads and partial RoPE.
+    q: bf16 [batch, L, Hq, 128]; k, v: bf16 [batch, L, Hkv, 128]. Returns
+    (o [batch, L, Hq, 128] in out_dtype (default fp32), k_rope = rope(k) bf16).
+    """
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]:
+        raise ValueError("q must be [batch, L, Hq, d] and k, v [batch, L, Hkv, d]")
+    if any(x.dtype != torch.bfloat16 for x in (q, k, v)):
+        raise TypeError("q, k, v must be bfloat16")
+    batch, L, Hq, d = q.shape
+    Hkv = k.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out_dtype = out_dtype or torch.float32
+    if o is None:
+        o = torch.empty((batch, L, Hq, d), device=q.device, dtype=out_dtype)
+    if k_rope is None:
+        k_rope = torch.empty_like(k)
+    st = lib.lt_softmax_prefill(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dev_ptr(o, "o"),
+                                _dtype_code(o.dtype), _dev_ptr(k_rope, "k_rope"), batch, L, Hq, Hkv, d,
+                                int(rope_dims), float(rope_base), scale, int(pos0), _stream(stream, q.device))
+    _check(st, "lt_softmax_prefill")
+    return o, k_rope

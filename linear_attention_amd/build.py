@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblightning.so")
 
-SOURCES = ["prefill_heads.hip", "prefill_slices.hip", "decode.hip", "backward.hip", "lightning_api.cpp"]
+SOURCES = ["prefill_heads.hip", "prefill_slices.hip", "decode.hip", "backward.hip", "softmax.hip",
+           "lightning_api.cpp"]
 
 HIPCC_FLAGS = [
     "-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-shared",

@@ -115,6 +115,25 @@ struct BackwardArgs {
 hipError_t launch_backward_kv(const BackwardArgs &a, const PrefillPlan &plan, void *workspace,
                               lt_dtype out_dtype, hipStream_t stream);
 
+// Softmax attention with grouped K/V heads and partial RoPE (the hybrid's
+// other layer type). q [batch, seqlen, q_heads, d], k, v [batch, seqlen,
+// kv_heads, d] bf16; o [batch, seqlen, q_heads, d]. Token t at position
+// pos0 + t; rope on the first rope_dims features (a multiple of 32).
+struct SoftmaxArgs {
+    const void *q, *k, *v;
+    void *o;
+    int batch;
+    long long seqlen;
+    long long pos0;
+    int q_heads, kv_heads;
+    int rope_dims;
+    double log2_base;
+    float scale;
+};
+// workspace: rope(k), batch * seqlen * kv_heads * d bf16
+hipError_t launch_softmax_prefill(const SoftmaxArgs &a, void *workspace, lt_dtype out_dtype,
+                                  hipStream_t stream);
+
 // fp32 inputs: one workgroup per (unit, head, 32-column value slice).
 hipError_t launch_prefill_slices(const PrefillArgs &a, lt_dtype in_dtype, lt_dtype out_dtype,
                                  hipStream_t stream);

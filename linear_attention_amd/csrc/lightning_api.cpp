@@ -464,3 +464,56 @@ LT_API lt_status lt_decode_norm_gate(const void *q, const void *k, const void *v
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Softmax attention (grouped K/V heads, partial RoPE)
+
+namespace {
+
+lt_status check_softmax_common(int q_heads, int kv_heads, int head_dim, int rope_dims,
+                               double rope_base, float scale) {
+    if (head_dim != lt::kHeadDim || q_heads < 0 || kv_heads < 0 || q_heads > LT_MAX_HEADS ||
+        kv_heads > LT_MAX_HEADS)
+        return LT_ERR_SHAPE;
+    if ((q_heads == 0) != (kv_heads == 0)) return LT_ERR_SHAPE;
+    if (kv_heads > 0 && q_heads % kv_heads != 0) return LT_ERR_SHAPE;
+    if (rope_dims < 0 || rope_dims > head_dim || rope_dims % 32 != 0) return LT_ERR_SHAPE;
+    if (!(rope_base > 1.0) || rope_base > 1e300) return LT_ERR_VALUE;
+    if (!(scale > 0.f) || scale > 3.0e38f) return LT_ERR_VALUE;
+    return LT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+LT_API lt_status lt_softmax_prefill(const void *q, const void *k, const void *v, void *o,
+                                    lt_dtype out_dtype, void *k_rope, int batch, long long seqlen,
+                                    int q_heads, int kv_heads, int head_dim, int rope_dims,
+                                    double rope_base, float scale, long long pos0, void *stream) {
+    if (!dtype_ok(out_dtype)) return LT_ERR_DTYPE;
+    if (batch < 0 || seqlen < 0 || pos0 < 0) return LT_ERR_SHAPE;
+    const lt_status c = check_softmax_common(q_heads, kv_heads, head_dim, rope_dims, rope_base, scale);
+    if (c != LT_OK) return c;
+    long long tokens, q_b, kv_b, o_b, grid, last_pos;
+    if (__builtin_mul_overflow((long long)batch, seqlen, &tokens) ||
+        !mul4(tokens, q_heads, head_dim, 2, &q_b) || !mul4(tokens, kv_heads, head_dim, 2, &kv_b) ||
+        !mul4(tokens, q_heads, head_dim, dtype_size(out_dtype), &o_b) ||
+        !mul4((seqlen + 127) / 128, batch, q_heads, 1, &grid) || grid > 0x7fffffffLL ||
+        __builtin_add_overflow(pos0, seqlen, &last_pos) ||
+        (long long)kv_heads * head_dim * 64 > 0x7fffffffLL)
+        return LT_ERR_SHAPE;
+    if (tokens == 0 || q_heads == 0) return LT_OK;
+    if (!q || !k || !v || !o || !k_rope) return LT_ERR_NULL;
+    const Range ins[] = {range_of(q, q_b), range_of(k, kv_b), range_of(v, kv_b)};
+    const Range outs[] = {range_of(o, o_b), range_of(k_rope, kv_b)};
+    for (const Range &x : outs)
+        for (const Range &i : ins)
+            if (overlaps(x, i)) return LT_ERR_ALIAS;
+    if (overlaps(outs[0], outs[1])) return LT_ERR_ALIAS;
+    lt::SoftmaxArgs a{q, k, v, o, batch, seqlen, pos0, q_heads, kv_heads, rope_dims,
+                      __builtin_log2(rope_base), scale};
+    return map_hip(lt::launch_softmax_prefill(a, k_rope, out_dtype, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

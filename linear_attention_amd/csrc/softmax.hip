@@ -1,0 +1,313 @@
+// Softmax attention of the hybrid's other layers on gfx950 (MI355X): causal,
+// grouped K/V heads, rotary position embedding on part of the head.
+//
+// MiniMax Signal Lab · M1, §02: the softmax layers project 64 query heads of
+// 128 and 8 K/V heads of 128, and only they apply RoPE, on 64 of the 128
+// dimensions. Per query head h (K/V head g = h / (Hq / Hkv)), token t at
+// position pos0 + t:
+//   o_t = sum_{j <= t} softmax_j(scale * rope(q_t) . rope(k_j)) v_j
+// RoPE pairs feature m with m + R/2 (m < R/2, R = rope dims) and rotates the
+// pair by position * base^(-2m/R); angles are formed in fp64 and reduced mod
+// 2 pi before the fp32 sine and cosine, so they stay exact at 1M positions.
+//
+// Prefill (flash-attention forward):
+//  * rope_rows_kernel writes rope(k) once (bf16, workspace);
+//  * one 4-wave workgroup per (sequence, query head, 128 queries); wave w owns
+//    queries 32w.., held as MFMA operands in registers (rope applied, scaled
+//    by scale * log2(e)); per 64-key block S^T = K Q^T on
+//    v_mfma_f32_32x32x16_bf16 (a lane owns one query and 32 keys, so the
+//    running max and sum are lane-local plus one xor-32 shuffle); the
+//    probabilities stay in registers as the B operand of O^T += V^T P^T;
+//    blocks past a wave's last query are skipped; heavy (late) query blocks
+//    are launched first.
+// Decode: rope_append_kernel writes rope(k_new), v_new into the KV cache; one
+// 4-wave workgroup per (sequence, K/V head) serves its query heads; each wave
+// takes a quarter of the positions (S^T = K Q^T on MFMA with the group's
+// heads as columns), and the waves' partial softmax states merge in LDS.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "internal.h"
+#include "tiles.h"
+
+namespace lt {
+namespace {
+
+constexpr int SQB = 128;      // queries per prefill workgroup
+constexpr int SKB = 64;       // keys per block
+constexpr int SNT = 256;      // 4 waves
+constexpr int SPT = D + 8;    // pitch of the K, V tiles
+using LK = LPad<SPT>;
+
+__device__ __forceinline__ float bf2f(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+__device__ __forceinline__ uint16_t f2bf(float f) {
+    const __bf16 b = static_cast<__bf16>(f);
+    uint16_t u;
+    __builtin_memcpy(&u, &b, 2);
+    return u;
+}
+
+// V^T operand for O^T += V^T P^T with P^T taken straight from the S^T
+// accumulators: lane l gets V[k0 + 4(l/32) + e][c0 + l%32] for e = 0..3 and
+// V[k0 + 8 + 4(l/32) + e - 4][c0 + l%32] for e = 4..7 (the key order in which
+// the accumulator layout holds a lane's scores; the contraction does not care
+// about the order as long as both operands share it).
+__device__ __forceinline__ bf16x8 ld_vt(const __bf16 *t, int c0, int k0, int lane) {
+    const int li = lane & 15, grp = lane >> 4;
+    const int row = k0 + 4 * (grp >> 1) + (li >> 2), col = c0 + 16 * (grp & 1) + 4 * (li & 3);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(t + LK::off(row, col)));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(t + LK::off(row + 8, col)));
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// sin and cos of position * base^(-2m/R): the angle is formed in fp64 as a
+// fraction of a turn and reduced to [0, 1) before the hardware sine and
+// cosine (which take turns), so it stays exact at any position.
+__device__ __forceinline__ void rope_sincos(long long pos, int m, int R, double log2_base, float &s,
+                                            float &c) {
+    const double th = exp2(-(2.0 * m / R) * log2_base) * 0.15915494309189535;
+    double t = (double)pos * th;
+    t -= floor(t);
+    s = __builtin_amdgcn_sinf((float)t);
+    c = __builtin_amdgcn_cosf((float)t);
+}
+
+// rope(x) of one row of d bf16 features into y: thread j < 16 handles features
+// 8j..8j+7; a thread in the first half of the rotated span also writes the
+// partner features.
+__device__ __forceinline__ void rope_row(const uint16_t *x, uint16_t *y, long long pos, int R,
+                                         double log2_base, int j) {
+    const int f0 = 8 * j;
+    const int half = R / 2;
+    if (f0 >= half && f0 < R) return;  // written by the partner thread
+    uint16_t a[8];
+    *reinterpret_cast<uint4 *>(a) = *reinterpret_cast<const uint4 *>(x + f0);
+    if (f0 >= R) {  // not rotated
+        *reinterpret_cast<uint4 *>(y + f0) = *reinterpret_cast<const uint4 *>(a);
+        return;
+    }
+    uint16_t b[8], ra[8], rb[8];
+    *reinterpret_cast<uint4 *>(b) = *reinterpret_cast<const uint4 *>(x + f0 + half);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float s, c;
+        rope_sincos(pos, f0 + e, R, log2_base, s, c);
+        const float u = bf2f(a[e]), w = bf2f(b[e]);
+        ra[e] = f2bf(u * c - w * s);
+        rb[e] = f2bf(u * s + w * c);
+    }
+    *reinterpret_cast<uint4 *>(y + f0) = *reinterpret_cast<const uint4 *>(ra);
+    *reinterpret_cast<uint4 *>(y + f0 + half) = *reinterpret_cast<const uint4 *>(rb);
+}
+
+// rope of every k row: [B, L, Hkv, d] -> same shape. 16 threads per row.
+__global__ __launch_bounds__(SNT) void rope_rows_kernel(SoftmaxArgs a, uint16_t *kr) {
+    const long long row = (long long)blockIdx.x * (SNT / 16) + threadIdx.x / 16;
+    const long long rows = (long long)a.batch * a.seqlen * a.kv_heads;
+    if (row >= rows) return;
+    const long long t = (row / a.kv_heads) % a.seqlen;
+    rope_row(static_cast<const uint16_t *>(a.k) + row * D, kr + row * D, a.pos0 + t, a.rope_dims,
+             a.log2_base, threadIdx.x % 16);
+}
+
+template <typename OutT>
+__device__ __forceinline__ void put_out4(OutT *p, float x, float y, float z, float w);
+template <>
+__device__ __forceinline__ void put_out4<float>(float *p, float x, float y, float z, float w) {
+    stream_store(p, make_float4(x, y, z, w));
+}
+template <>
+__device__ __forceinline__ void put_out4<__bf16>(__bf16 *p, float x, float y, float z, float w) {
+    const bf16x4 b = {static_cast<__bf16>(x), static_cast<__bf16>(y), static_cast<__bf16>(z),
+                      static_cast<__bf16>(w)};
+    stream_store_bits(p, b);
+}
+
+template <typename OutT>
+__global__ __launch_bounds__(SNT) void fa_prefill_kernel(SoftmaxArgs a, const uint16_t *kr) {
+    __shared__ __attribute__((aligned(16))) __bf16 Ks[SKB * SPT];
+    __shared__ __attribute__((aligned(16))) __bf16 Vs[SKB * SPT];
+
+    const int nqb = (int)((a.seqlen + SQB - 1) / SQB);
+    const int bh = blockIdx.x % (a.batch * a.q_heads);
+    const int qb = nqb - 1 - (int)(blockIdx.x / (a.batch * a.q_heads));  // late blocks first
+    const int h = bh % a.q_heads, b = bh / a.q_heads;
+    const int g = h / (a.q_heads / a.kv_heads);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r32 = lane & 31, hf = lane >> 5;
+    const long long L = a.seqlen;
+    const long long q0 = (long long)qb * SQB;
+    const long long qrow = q0 + 32 * w + r32;  // this lane's query
+    const long long qlast = q0 + 32 * w + 31 < L - 1 ? q0 + 32 * w + 31 : L - 1;  // wave's last query
+
+    // ---- the lane's query as 8 MFMA operands: features 16ks + 8hf + e
+    bf16x8 qop[D / 16];
+    {
+        const long long qr = qrow < L ? qrow : L - 1;
+        const uint16_t *qg = static_cast<const uint16_t *>(a.q) + ((b * L + qr) * a.q_heads + h) * (long long)D;
+        float x[D / 16][8];
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            uint16_t u[8];
+            *reinterpret_cast<uint4 *>(u) = *reinterpret_cast<const uint4 *>(qg + 16 * ks + 8 * hf);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[ks][e] = bf2f(u[e]);
+        }
+        // rotate-half pairs lie hs = rope_dims/32 operand steps apart; feature
+        // 16ks + 8hf + e is in the first half of the rotated span iff ks < hs
+        const int hs = a.rope_dims / 32;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+            for (int dd = 1; dd <= D / 32; ++dd)
+                if (ks + dd < D / 16 && dd == hs && ks < hs) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        float s, c;
+                        rope_sincos(a.pos0 + qr, 16 * ks + 8 * hf + e, a.rope_dims, a.log2_base, s, c);
+                        const float u = x[ks][e], v = x[ks + dd][e];
+                        x[ks][e] = u * c - v * s;
+                        x[ks + dd][e] = u * s + v * c;
+                    }
+                }
+        const float qs = a.scale * 1.4426950408889634f;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qop[ks][e] = static_cast<__bf16>(x[ks][e] * qs);
+    }
+
+    f32x16 o[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[c][v] = 0.f;
+    float mrun = -__builtin_inff(), lsum = 0.f;
+
+    const long long kvh = (long long)b * L * a.kv_heads + g;  // row of token 0, K/V head g
+    const uint16_t *kg = kr + kvh * D;
+    const uint16_t *vg = static_cast<const uint16_t *>(a.v) + kvh * D;
+    const int ts = a.kv_heads * D;                             // token stride (elements)
+    const long long kend = q0 + SQB < L ? q0 + SQB : L;        // keys [0, kend)
+    const int nkb = (int)((kend + SKB - 1) / SKB);
+    // staging: thread t holds block rows (t/16) + 16i, i = 0..3, features
+    // 8(t%16)..; rows past the end repeat the last key (masked later)
+    const int srow = tid >> 4, scol = 8 * (tid & 15);
+    uint4 sk0, sk1, sk2, sk3, sv0, sv1, sv2, sv3;
+#define LT_FA_LOAD(KB)                                                                      \
+    {                                                                                       \
+        const long long k0_ = (long long)(KB) * SKB;                                        \
+        const uint16_t *kb_ = kg + k0_ * ts, *vb_ = vg + k0_ * ts;                          \
+        const int last_ = L - 1 - k0_ < SKB - 1 ? (int)(L - 1 - k0_) : SKB - 1;             \
+        const int o0_ = min(srow, last_) * ts + scol, o1_ = min(srow + 16, last_) * ts + scol; \
+        const int o2_ = min(srow + 32, last_) * ts + scol, o3_ = min(srow + 48, last_) * ts + scol; \
+        sk0 = *reinterpret_cast<const uint4 *>(kb_ + o0_);                                  \
+        sk1 = *reinterpret_cast<const uint4 *>(kb_ + o1_);                                  \
+        sk2 = *reinterpret_cast<const uint4 *>(kb_ + o2_);                                  \
+        sk3 = *reinterpret_cast<const uint4 *>(kb_ + o3_);                                  \
+        sv0 = stream_load16(vb_ + o0_);                                                     \
+        sv1 = stream_load16(vb_ + o1_);                                                     \
+        sv2 = stream_load16(vb_ + o2_);                                                     \
+        sv3 = stream_load16(vb_ + o3_);                                                     \
+    }
+    if (nkb > 0) LT_FA_LOAD(0)
+    for (int kb = 0; kb < nkb; ++kb) {
+        __syncthreads();  // previous block's tiles fully read
+        *reinterpret_cast<uint4 *>(Ks + LK::off(srow, scol)) = sk0;
+        *reinterpret_cast<uint4 *>(Ks + LK::off(srow + 16, scol)) = sk1;
+        *reinterpret_cast<uint4 *>(Ks + LK::off(srow + 32, scol)) = sk2;
+        *reinterpret_cast<uint4 *>(Ks + LK::off(srow + 48, scol)) = sk3;
+        *reinterpret_cast<uint4 *>(Vs + LK::off(srow, scol)) = sv0;
+        *reinterpret_cast<uint4 *>(Vs + LK::off(srow + 16, scol)) = sv1;
+        *reinterpret_cast<uint4 *>(Vs + LK::off(srow + 32, scol)) = sv2;
+        *reinterpret_cast<uint4 *>(Vs + LK::off(srow + 48, scol)) = sv3;
+        if (kb + 1 < nkb) LT_FA_LOAD(kb + 1)
+        __syncthreads();  // tiles visible
+        const long long k0 = (long long)kb * SKB;
+        if (k0 > qlast) continue;  // every key of this block is after the wave's queries
+
+        // S^T blocks: keys k0 + 32kk.., this lane's query column
+        f32x16 sc[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) sc[kk][v] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks)
+                sc[kk] = mma(ld_op<LK>(Ks, 32 * kk, 16 * ks, lane), qop[ks], sc[kk]);
+        }
+        // causal mask (and keys past the end) on blocks that reach the diagonal
+        const bool diag = k0 + SKB - 1 > q0 + 32 * w || k0 + SKB > L;
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const long long key = k0 + 32 * kk + 8 * (v >> 2) + 4 * hf + (v & 3);
+                if (diag && (key > qrow || key >= L)) sc[kk][v] = -__builtin_inff();
+                mx = fmaxf(mx, sc[kk][v]);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(mrun, mx);
+        const float alpha = mnew == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(mrun - mnew);
+        mrun = mnew;
+        float ps = 0.f;
+        bf16x8 pb[SKB / 16];  // P^T operands: step j holds keys 16j + 4hf + 0..3, 16j + 8 + 4hf + 0..3
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float p = __builtin_amdgcn_exp2f(sc[kk][v] - mnew);  // exp2(-inf) = 0
+                ps += p;
+                pb[2 * kk + v / 8][v % 8] = static_cast<__bf16>(p);
+            }
+        lsum = lsum * alpha + ps;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) o[c] *= alpha;
+        }
+#pragma unroll
+        for (int j = 0; j < SKB / 16; ++j)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) o[c] = mma(ld_vt(Vs, 32 * c, 16 * j, lane), pb[j], o[c]);
+    }
+
+#undef LT_FA_LOAD
+
+    // ---- normalise and store this lane's query row (value dims 32c + 8gv + 4hf..)
+    lsum += __shfl_xor(lsum, 32);
+    if (qrow < L) {
+        const float inv = 1.f / lsum;
+        OutT *og = static_cast<OutT *>(a.o) + ((b * L + qrow) * a.q_heads + h) * (long long)D;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int gv = 0; gv < 4; ++gv)
+                put_out4<OutT>(og + 32 * c + 8 * gv + 4 * hf, o[c][4 * gv] * inv, o[c][4 * gv + 1] * inv,
+                               o[c][4 * gv + 2] * inv, o[c][4 * gv + 3] * inv);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_softmax_prefill(const SoftmaxArgs &a, void *workspace, lt_dtype out_dtype,
+                                  hipStream_t stream) {
+    clear_pending_error();
+    uint16_t *kr = static_cast<uint16_t *>(workspace);
+    const long long rows = (long long)a.batch * a.seqlen * a.kv_heads;
+    hipLaunchKernelGGL(rope_rows_kernel, dim3((unsigned)((rows + SNT / 16 - 1) / (SNT / 16))), dim3(SNT),
+                       0, stream, a, kr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long long nqb = (a.seqlen + SQB - 1) / SQB;
+    const dim3 grid((unsigned)(nqb * a.batch * a.q_heads));
+    if (out_dtype == LT_F32)
+        hipLaunchKernelGGL((fa_prefill_kernel<float>), grid, dim3(SNT), 0, stream, a, kr);
+    else
+        hipLaunchKernelGGL((fa_prefill_kernel<__bf16>), grid, dim3(SNT), 0, stream, a, kr);
+    return hipGetLastError();
+}
+
+}  // namespace lt

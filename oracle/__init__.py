@@ -459,6 +459,32 @@ def softmax_attention(q, k, v, rope_dims=64, base=10000.0, scale=None, pos0=0):
     return o
 
 
+def softmax_attention_rows(q, k, v, rows, rope_dims=64, base=10000.0, scale=None, pos0=0):
+    """softmax_attention evaluated at the query rows ``rows`` only (for sequences
+    too long for the full quadratic form): row t attends over keys 0..t.
+    Returns [B, len(rows), Hq, d] fp64.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    B, L, Hq, d = q.shape
+    Hkv = k.shape[2]
+    grp = Hq // Hkv
+    sc = 1.0 / np.sqrt(d) if scale is None else np.float64(scale)
+    rows = np.asarray(rows, np.int64)
+    qr = rope(q[:, rows], pos0 + rows, rope_dims, base)
+    kr = rope(k, pos0 + np.arange(L), rope_dims, base)
+    o = np.zeros((B, len(rows), Hq, d))
+    for b in range(B):
+        for i, t in enumerate(rows):
+            for h in range(Hq):
+                g = h // grp
+                s = sc * (kr[b, :t + 1, g] @ qr[b, i, h])
+                p = np.exp(s - s.max())
+                o[b, i, h] = (p / p.sum()) @ v[b, :t + 1, g]
+    return o
+
+
 def softmax_decode(q, k_new, v_new, k_cache, v_cache, lengths, rope_dims=64, base=10000.0,
                    scale=None):
     """One decode step over a KV cache, fp64.

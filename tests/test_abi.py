@@ -322,3 +322,57 @@ def test_backward_checks():
     assert backward(batch=0) == la.LT_OK
     assert backward(heads=0) == la.LT_OK
     assert backward(seqlen=0, d_state_in=None) == la.LT_OK
+
+
+# --------------------------------------------------------------------------
+# softmax attention (grouped K/V heads, partial RoPE)
+# --------------------------------------------------------------------------
+
+def softmax_prefill(**kw):
+    args = dict(q=A, k=A + 100 * MB, v=A + 200 * MB, o=A + 300 * MB, out_dtype=la.LT_F32,
+                k_rope=A + 500 * MB, batch=1, seqlen=64, q_heads=8, kv_heads=2, head_dim=128,
+                rope_dims=64, rope_base=10000.0, scale=0.088, pos0=0, stream=None)
+    args.update(kw)
+    return la.lib.lt_softmax_prefill(*args.values())
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "o", "k_rope"])
+def test_softmax_prefill_null_pointers(field):
+    assert softmax_prefill(**{field: None}) == la.LT_ERR_NULL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(out_dtype=3), la.LT_ERR_DTYPE),
+    (dict(head_dim=64), la.LT_ERR_SHAPE),
+    (dict(q_heads=6, kv_heads=4), la.LT_ERR_SHAPE),      # not a multiple
+    (dict(q_heads=8, kv_heads=0), la.LT_ERR_SHAPE),
+    (dict(rope_dims=48), la.LT_ERR_SHAPE),               # not a multiple of 32
+    (dict(rope_dims=160), la.LT_ERR_SHAPE),
+    (dict(rope_dims=-32), la.LT_ERR_SHAPE),
+    (dict(seqlen=-1), la.LT_ERR_SHAPE),
+    (dict(batch=-1), la.LT_ERR_SHAPE),
+    (dict(pos0=-5), la.LT_ERR_SHAPE),
+    (dict(pos0=(1 << 63) - 10), la.LT_ERR_SHAPE),        # last position overflows
+    (dict(seqlen=1 << 40, q_heads=64, kv_heads=8), la.LT_ERR_SHAPE),
+    (dict(rope_base=1.0), la.LT_ERR_VALUE),
+    (dict(rope_base=float("nan")), la.LT_ERR_VALUE),
+    (dict(rope_base=float("inf")), la.LT_ERR_VALUE),
+    (dict(scale=0.0), la.LT_ERR_VALUE),
+    (dict(scale=float("nan")), la.LT_ERR_VALUE),
+    (dict(scale=float("inf")), la.LT_ERR_VALUE),
+])
+def test_softmax_prefill_bad_arguments(kw, code):
+    assert softmax_prefill(**kw) == code
+
+
+def test_softmax_prefill_alias_checks():
+    assert softmax_prefill(o=A + 16) == la.LT_ERR_ALIAS                # o inside q (8 heads, 64 tokens)
+    assert softmax_prefill(k_rope=A + 100 * MB + 32) == la.LT_ERR_ALIAS  # k_rope on k
+    assert softmax_prefill(k_rope=A + 300 * MB + 64) == la.LT_ERR_ALIAS  # k_rope inside o
+    assert softmax_prefill(o=A + 200 * MB + 8) == la.LT_ERR_ALIAS      # o on v
+
+
+def test_softmax_prefill_noops_need_no_gpu():
+    assert softmax_prefill(seqlen=0, q=None) == la.LT_OK
+    assert softmax_prefill(batch=0, k=None) == la.LT_OK
+    assert softmax_prefill(q_heads=0, kv_heads=0, o=None) == la.LT_OK

@@ -837,3 +837,15 @@ def test_softmax_decode_matches_last_prefill_row():
     assert rel(o[:2], o_full[:2, n]) < 1e-12
     assert np.all(o[2] == 0) and np.array_equal(kc2[2], kc[2]) and np.array_equal(vc2[2], vc[2])
     assert rel(kc2[:2, n], oracle.rope(k[:2, n][:, None], [n], R, 10000.0)[:, 0]) < 1e-14
+
+
+def test_softmax_rows_match_full_form():
+    """The row-sampled form agrees with the full form at every sampled row (first,
+    last, a middle row, a repeated row), with a position offset and GQA groups."""
+    g = np.random.Generator(np.random.PCG64(59))
+    B, L, Hq, Hkv, d, R = 2, 11, 6, 2, 8, 4
+    q, k, v = g.standard_normal((B, L, Hq, d)), g.standard_normal((B, L, Hkv, d)), g.standard_normal((B, L, Hkv, d))
+    rows = [0, 5, 10, 5]
+    full = oracle.softmax_attention(q, k, v, rope_dims=R, base=500.0, scale=0.3, pos0=77)
+    part = oracle.softmax_attention_rows(q, k, v, rows, rope_dims=R, base=500.0, scale=0.3, pos0=77)
+    assert rel(part, full[:, rows]) < 1e-13

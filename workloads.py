@@ -16,6 +16,10 @@ Recipe (stated once more in the design doc):
     rounded values, so input quantisation never counts as kernel error.
   * carried-in states ~ N(0, 0.01) read as variance 0.01 (std 0.1), fp32.
   * varlen lengths: 16 integers uniform on [1024, 65536], packed by cu_seqlens.
+  * softmax layers (the hybrid's other attention type, §02: 64 query heads,
+    8 K/V heads of 128, RoPE on 64 dims): q, k, v ~ N(0, std^2), std 1 by
+    default so the scaled scores are O(1) like real attention logits, rounded
+    to bf16; RoPE base 10000 (the pages give none).
 """
 
 from __future__ import annotations
@@ -50,7 +54,12 @@ DECODE = Workload("batched_decode", 256, 1, 64, 128, 0, "bf16", 1004,
 VARLEN = Workload("varlen_carried_state_prefill", 16, 0, 64, 128, 256, "bf16", 1005,
                   {"min_len": 1024, "max_len": 65536})
 
-ALL = [TINY_F32, M1_LAYER, LONG_1M, DECODE, VARLEN]
+SOFTMAX_PREFILL = Workload("m1_softmax_layer_bf16_prefill", 1, 32768, 64, 128, 0, "bf16", 1006,
+                           {"kv_heads": 8, "rope_dims": 64, "rope_base": 10000.0})
+SOFTMAX_DECODE = Workload("m1_softmax_layer_bf16_decode", 16, 1, 64, 128, 0, "bf16", 1007,
+                          {"kv_heads": 8, "rope_dims": 64, "rope_base": 10000.0, "context": 32768})
+
+ALL = [TINY_F32, M1_LAYER, LONG_1M, DECODE, VARLEN, SOFTMAX_PREFILL, SOFTMAX_DECODE]
 
 
 def slopes(heads: int) -> np.ndarray:
@@ -155,3 +164,24 @@ def gate_device(seed: int, shape, dtype: str = "bf16", device="cuda"):
     g.manual_seed(seed)
     x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
     return x.to(torch.bfloat16) if dtype == "bf16" else x
+
+
+def softmax_qkv_host(seed: int, batch: int, seqlen: int, q_heads: int, kv_heads: int,
+                     d: int = HEAD_DIM, std: float = 1.0):
+    """q [batch, L, Hq, d], k, v [batch, L, Hkv, d]: N(0, std^2) rounded to bf16
+    (fp32 arrays holding bf16 values)."""
+    g = rng(seed)
+    shapes = [(batch, seqlen, q_heads, d), (batch, seqlen, kv_heads, d), (batch, seqlen, kv_heads, d)]
+    return tuple(round_bf16(g.standard_normal(sh, dtype=np.float32) * np.float32(std)) for sh in shapes)
+
+
+def softmax_qkv_device(seed: int, batch: int, seqlen: int, q_heads: int, kv_heads: int,
+                       d: int = HEAD_DIM, std: float = 1.0, device="cuda"):
+    """Device-drawn softmax-layer inputs (bf16 tensors) for the large workloads."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    shapes = [(batch, seqlen, q_heads, d), (batch, seqlen, kv_heads, d), (batch, seqlen, kv_heads, d)]
+    return tuple((torch.randn(sh, generator=g, device=device, dtype=torch.float32) * std).to(torch.bfloat16)
+                 for sh in shapes)
