@@ -292,6 +292,47 @@ LT_API lt_status lt_softmax_prefill(const void *q, const void *k, const void *v,
                                     int q_heads, int kv_heads, int head_dim, int rope_dims,
                                     double rope_base, float scale, long long pos0, void *stream);
 
+/*
+ * lt_softmax_decode - one decode step of the softmax layer over a KV cache.
+ * Sequence b's new token sits at position n = lengths[b]: rope(k_new) (at
+ * position n) and v_new are written into row n of the caches, then rope(q)
+ * attends over cache rows 0..n of its K/V head:
+ *
+ *     o[b, h] = sum_{j <= n} softmax_j(scale * rope(q[b, h]) . k_cache[b, j, g]) v_cache[b, j, g]
+ *
+ * with g = h / (q_heads / kv_heads). The same layer and conventions as
+ * lt_softmax_prefill, whose k_rope rows are this cache's key rows.
+ *
+ *   q             [batch, q_heads, head_dim] bf16.
+ *   k_new, v_new  [batch, kv_heads, head_dim] bf16.
+ *   k_cache, v_cache  [batch, capacity, kv_heads, head_dim] bf16, updated in
+ *                 place at row lengths[b] only.
+ *   lengths       [batch] int32 on the device. A value outside [0, capacity)
+ *                 marks a padding row: its o is zero and no cache row changes.
+ *   o             [batch, q_heads, head_dim], out_dtype.
+ *   q_heads / kv_heads at most 32.
+ *   workspace     device scratch of lt_softmax_decode_workspace_bytes(...)
+ *                 bytes, or NULL / smaller: then each (sequence, K/V head) is
+ *                 served by one wave over all its keys (correct, much slower
+ *                 at long contexts). The key range is split on `capacity`, so
+ *                 a capacity near the longest length keeps every wave busy.
+ *   rope_dims, rope_base, scale: as lt_softmax_prefill.
+ *   No output (o, caches, workspace) may overlap an input or another output.
+ *   Errors: LT_ERR_NULL, LT_ERR_SHAPE (also capacity 0 with batch > 0),
+ *   LT_ERR_DTYPE, LT_ERR_VALUE, LT_ERR_ALIAS, LT_ERR_HIP.
+ */
+LT_API lt_status lt_softmax_decode(const void *q, const void *k_new, const void *v_new,
+                                   void *k_cache, void *v_cache, const int *lengths, void *o,
+                                   lt_dtype out_dtype, int batch, long long capacity, int q_heads,
+                                   int kv_heads, int head_dim, int rope_dims, double rope_base,
+                                   float scale, void *workspace, size_t workspace_bytes,
+                                   void *stream);
+
+/* Workspace bytes lt_softmax_decode uses for these sizes (0 = none needed or
+ * invalid sizes). */
+LT_API size_t lt_softmax_decode_workspace_bytes(int batch, long long capacity, int q_heads,
+                                                int kv_heads, int head_dim);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,9 +9,10 @@ with a fixed d x d fp32 state per head, plus its one-token decode step.
 ``lt_prefill_backward`` (gradients of a prefill) and the ``*_norm_gate``
 variants (the operator followed by the
 normalisation and gate of the §03 data-flow figure) mirror the C entry points
-of ``include/lightning.h`` one to one, as does ``lt_softmax_prefill`` (the
-hybrid's other layer type: causal softmax attention with grouped K/V heads and
-partial RoPE, §02 of the same pages).
+of ``include/lightning.h`` one to one, as do ``lt_softmax_prefill`` and
+``lt_softmax_decode`` (the hybrid's other layer type: causal softmax attention
+with grouped K/V heads and partial RoPE, §02 of the same pages, and its decode
+step over a KV cache).
 The shared library is loaded on first use of any of these names (so the build
 module can be imported before the library exists); a missing library raises
 ImportError there, and there is no fallback path.
@@ -20,7 +21,7 @@ ImportError there, and there is no fallback path.
 _NATIVE_NAMES = (
     "lt_prefill", "lt_prefill_workspace_bytes", "lt_prefill_varlen", "lt_decode",
     "lt_prefill_norm_gate", "lt_prefill_varlen_norm_gate", "lt_decode_norm_gate", "lt_decode_slots",
-    "lt_prefill_backward", "lt_softmax_prefill",
+    "lt_prefill_backward", "lt_softmax_prefill", "lt_softmax_decode", "lt_softmax_decode_workspace_bytes",
     "LightningError", "lib", "status_string", "EXPORTS", "LIB_PATH", "HEAD_DIM", "LT_OK",
     "LT_ERR_NULL", "LT_ERR_SHAPE", "LT_ERR_BLOCK", "LT_ERR_DTYPE", "LT_ERR_ALIAS", "LT_ERR_HIP",
     "LT_ERR_VALUE",

@@ -22,7 +22,8 @@ HEAD_DIM = 128
 
 EXPORTS = ("lt_status_string", "lt_version", "lt_prefill", "lt_prefill_workspace_bytes",
            "lt_prefill_varlen", "lt_decode", "lt_prefill_norm_gate", "lt_prefill_varlen_norm_gate",
-           "lt_decode_norm_gate", "lt_decode_slots", "lt_prefill_backward", "lt_softmax_prefill")
+           "lt_decode_norm_gate", "lt_decode_slots", "lt_prefill_backward", "lt_softmax_prefill",
+           "lt_softmax_decode", "lt_softmax_decode_workspace_bytes")
 
 _vp, _i, _ll, _f, _d = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_float, ctypes.c_double
 
@@ -78,6 +79,11 @@ def _load() -> ctypes.CDLL:
     lib.lt_softmax_prefill.argtypes = [_vp, _vp, _vp, _vp, _i, _vp, _i, _ll, _i, _i, _i, _i, _d, _f,
                                        _ll, _vp]
     lib.lt_softmax_prefill.restype = _i
+    lib.lt_softmax_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i, _i, _i, _d,
+                                      _f, _vp, ctypes.c_size_t, _vp]
+    lib.lt_softmax_decode.restype = _i
+    lib.lt_softmax_decode_workspace_bytes.argtypes = [_i, _ll, _i, _i, _i]
+    lib.lt_softmax_decode_workspace_bytes.restype = ctypes.c_size_t
     return lib
 
 
@@ -400,3 +406,45 @@ def lt_softmax_prefill(q, k, v, *, rope_dims=64, rope_base=10000.0, scale=None, 
                                 int(rope_dims), float(rope_base), scale, int(pos0), _stream(stream, q.device))
     _check(st, "lt_softmax_prefill")
     return o, k_rope
+
+
+def lt_softmax_decode_workspace_bytes(batch, capacity, q_heads, kv_heads, head_dim=128):
+    return int(lib.lt_softmax_decode_workspace_bytes(batch, capacity, q_heads, kv_heads, head_dim))
+
+
+def lt_softmax_decode(q, k_new, v_new, k_cache, v_cache, lengths, *, rope_dims=64, rope_base=10000.0,
+                      scale=None, o=None, out_dtype=None, workspace=None, stream=None):
+    """One decode step of the softmax layer. q: bf16 [batch, Hq, 128]; k_new, v_new:
+    bf16 [batch, Hkv, 128]; k_cache, v_cache: bf16 [batch, capacity, Hkv, 128],
+    updated in place at row lengths[b]; lengths: int32 [batch] on the device.
+    Returns o [batch, Hq, 128] in out_dtype (default fp32). A workspace is
+    allocated here when none is given.
+    """
+    torch = _torch()
+    if q.dim() != 3 or k_new.dim() != 3 or v_new.shape != k_new.shape or k_new.shape[0] != q.shape[0]:
+        raise ValueError("q must be [batch, Hq, d] and k_new, v_new [batch, Hkv, d]")
+    batch, Hq, d = q.shape
+    Hkv = k_new.shape[1]
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape or k_cache.shape[0] != batch or \
+            tuple(k_cache.shape[2:]) != (Hkv, d):
+        raise ValueError("caches must be [batch, capacity, Hkv, d]")
+    if any(x.dtype != torch.bfloat16 for x in (q, k_new, v_new, k_cache, v_cache)):
+        raise TypeError("q, k_new, v_new and the caches must be bfloat16")
+    if lengths.dtype != torch.int32 or tuple(lengths.shape) != (batch,):
+        raise ValueError("lengths must be int32 [batch]")
+    cap = k_cache.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out_dtype = out_dtype or torch.float32
+    if o is None:
+        o = torch.empty((batch, Hq, d), device=q.device, dtype=out_dtype)
+    if workspace is None:
+        nb = lt_softmax_decode_workspace_bytes(batch, cap, Hq, Hkv, d)
+        workspace = torch.empty(max(nb, 1), device=q.device, dtype=torch.uint8) if nb else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.lt_softmax_decode(_dev_ptr(q, "q"), _dev_ptr(k_new, "k_new"), _dev_ptr(v_new, "v_new"),
+                               _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
+                               _dev_ptr(lengths, "lengths"), _dev_ptr(o, "o"), _dtype_code(o.dtype), batch,
+                               cap, Hq, Hkv, d, int(rope_dims), float(rope_base), scale,
+                               _dev_ptr(workspace, "workspace"), wbytes, _stream(stream, q.device))
+    _check(st, "lt_softmax_decode")
+    return o

@@ -134,6 +134,35 @@ struct SoftmaxArgs {
 hipError_t launch_softmax_prefill(const SoftmaxArgs &a, void *workspace, lt_dtype out_dtype,
                                   hipStream_t stream);
 
+// One decode step of the softmax layer over a KV cache. q [batch, q_heads, d],
+// k_new, v_new [batch, kv_heads, d], caches [batch, capacity, kv_heads, d]
+// holding rope(k) and v, lengths [batch] int32 on the device (the new token's
+// position; outside [0, capacity) marks a padding row).
+struct SoftmaxDecodeArgs {
+    const void *q, *k_new, *v_new;
+    void *k_cache, *v_cache;
+    const int *lengths;
+    void *o;
+    int batch;
+    long long capacity;
+    int q_heads, kv_heads;
+    int rope_dims;
+    double log2_base;
+    float scale;
+};
+// Key splits per (sequence, K/V head): each split is one wave's range of
+// chunk keys (a multiple of 32); splits > 1 needs a workspace of
+// softmax_decode_workspace(batch, q_heads, splits) bytes.
+struct SoftmaxDecodePlan {
+    int splits = 1;
+    long long chunk = 0;
+};
+inline long long softmax_decode_workspace(int batch, int q_heads, int splits) {
+    return splits > 1 ? (long long)batch * q_heads * splits * 132 * 4 : 0;
+}
+hipError_t launch_softmax_decode(const SoftmaxDecodeArgs &a, const SoftmaxDecodePlan &plan,
+                                 float *workspace, lt_dtype out_dtype, hipStream_t stream);
+
 // fp32 inputs: one workgroup per (unit, head, 32-column value slice).
 hipError_t launch_prefill_slices(const PrefillArgs &a, lt_dtype in_dtype, lt_dtype out_dtype,
                                  hipStream_t stream);

@@ -517,3 +517,101 @@ LT_API lt_status lt_softmax_prefill(const void *q, const void *k, const void *v,
 }
 
 }  // extern "C"
+
+namespace {
+
+// Waves a softmax decode launch should reach: eight per CU keeps enough
+// cache reads in flight to cover HBM latency.
+constexpr long long kDecodeWaves = 2048;
+// Fewest keys worth a split of their own.
+constexpr long long kMinDecodeChunk = 256;
+
+// Splits are planned on the capacity (the lengths live on the device): each
+// (sequence, K/V head) gets `splits` waves of `chunk` keys; splits that start
+// past a sequence's length exit at once.
+lt::SoftmaxDecodePlan plan_softmax_decode(int batch, long long capacity, int kv_heads) {
+    lt::SoftmaxDecodePlan p;
+    const long long units = (long long)batch * kv_heads;
+    long long splits = (kDecodeWaves + units - 1) / units;
+    const long long max_splits = (capacity + kMinDecodeChunk - 1) / kMinDecodeChunk;
+    if (splits > max_splits) splits = max_splits;
+    if (splits < 1) splits = 1;
+    long long chunk = (capacity + splits - 1) / splits;
+    chunk = (chunk + 31) / 32 * 32;
+    p.chunk = chunk;
+    p.splits = (int)((capacity + chunk - 1) / chunk);
+    return p;
+}
+
+lt_status check_softmax_decode(int batch, long long capacity, int q_heads, int kv_heads,
+                               int head_dim, long long *tokens_out) {
+    if (batch < 0 || capacity < 0 || capacity > 0x7fffffffLL || head_dim != lt::kHeadDim)
+        return LT_ERR_SHAPE;
+    if (kv_heads > 0 && q_heads / kv_heads > 32) return LT_ERR_SHAPE;
+    long long tokens;
+    if (__builtin_mul_overflow((long long)batch, capacity, &tokens)) return LT_ERR_SHAPE;
+    *tokens_out = tokens;
+    return LT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+LT_API size_t lt_softmax_decode_workspace_bytes(int batch, long long capacity, int q_heads,
+                                                int kv_heads, int head_dim) {
+    long long tokens;
+    if (batch <= 0 || capacity <= 0 || q_heads <= 0 || kv_heads <= 0 || q_heads > LT_MAX_HEADS ||
+        q_heads % kv_heads != 0 ||
+        check_softmax_decode(batch, capacity, q_heads, kv_heads, head_dim, &tokens) != LT_OK)
+        return 0;
+    const lt::SoftmaxDecodePlan p = plan_softmax_decode(batch, capacity, kv_heads);
+    return (size_t)lt::softmax_decode_workspace(batch, q_heads, p.splits);
+}
+
+LT_API lt_status lt_softmax_decode(const void *q, const void *k_new, const void *v_new,
+                                   void *k_cache, void *v_cache, const int *lengths, void *o,
+                                   lt_dtype out_dtype, int batch, long long capacity, int q_heads,
+                                   int kv_heads, int head_dim, int rope_dims, double rope_base,
+                                   float scale, void *workspace, size_t workspace_bytes,
+                                   void *stream) {
+    if (!dtype_ok(out_dtype)) return LT_ERR_DTYPE;
+    const lt_status c = check_softmax_common(q_heads, kv_heads, head_dim, rope_dims, rope_base, scale);
+    if (c != LT_OK) return c;
+    long long tokens;
+    const lt_status c2 = check_softmax_decode(batch, capacity, q_heads, kv_heads, head_dim, &tokens);
+    if (c2 != LT_OK) return c2;
+    long long q_b, kv_b, cache_b, o_b, waves;
+    if (!mul4(batch, q_heads, head_dim, 2, &q_b) || !mul4(batch, kv_heads, head_dim, 2, &kv_b) ||
+        !mul4(tokens, kv_heads, head_dim, 2, &cache_b) ||
+        !mul4(batch, q_heads, head_dim, dtype_size(out_dtype), &o_b) ||
+        !mul4(batch, kv_heads, 1, 1, &waves) || waves > 0x7fffffffLL / 64 ||
+        (long long)batch * q_heads > 0x7fffffffLL)
+        return LT_ERR_SHAPE;
+    if (batch == 0 || q_heads == 0) return LT_OK;
+    if (capacity == 0) return LT_ERR_SHAPE;  // no room for the new token
+    if (!q || !k_new || !v_new || !k_cache || !v_cache || !lengths || !o) return LT_ERR_NULL;
+    lt::SoftmaxDecodePlan p = plan_softmax_decode(batch, capacity, kv_heads);
+    const long long ws_need = lt::softmax_decode_workspace(batch, q_heads, p.splits);
+    const bool use_ws = ws_need > 0 && workspace && (long long)workspace_bytes >= ws_need;
+    if (!use_ws) {
+        p.splits = 1;
+        p.chunk = (capacity + 31) / 32 * 32;
+    }
+    const Range ins[] = {range_of(q, q_b), range_of(k_new, kv_b), range_of(v_new, kv_b),
+                         range_of(lengths, batch * 4LL)};
+    const Range outs[] = {range_of(o, o_b), range_of(k_cache, cache_b), range_of(v_cache, cache_b),
+                          range_of(workspace, use_ws ? ws_need : 0)};
+    for (const Range &x : outs)
+        for (const Range &i : ins)
+            if (overlaps(x, i)) return LT_ERR_ALIAS;
+    for (int x = 0; x < 4; ++x)
+        for (int y = x + 1; y < 4; ++y)
+            if (overlaps(outs[x], outs[y])) return LT_ERR_ALIAS;
+    const lt::SoftmaxDecodeArgs a{q, k_new, v_new, k_cache, v_cache, lengths, o, batch, capacity,
+                                  q_heads, kv_heads, rope_dims, __builtin_log2(rope_base), scale};
+    return map_hip(lt::launch_softmax_decode(a, p, use_ws ? static_cast<float *>(workspace) : nullptr,
+                                             out_dtype, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

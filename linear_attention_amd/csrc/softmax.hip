@@ -20,10 +20,11 @@
 //    probabilities stay in registers as the B operand of O^T += V^T P^T;
 //    blocks past a wave's last query are skipped; heavy (late) query blocks
 //    are launched first.
-// Decode: rope_append_kernel writes rope(k_new), v_new into the KV cache; one
-// 4-wave workgroup per (sequence, K/V head) serves its query heads; each wave
-// takes a quarter of the positions (S^T = K Q^T on MFMA with the group's
-// heads as columns), and the waves' partial softmax states merge in LDS.
+// Decode: rope_append_kernel writes rope(k_new), v_new into the KV cache; then
+// one wave per (sequence, K/V head, key split) serves the group's query heads
+// as MFMA columns (S^T = K Q^T, O^T += V^T P^T over 32-key blocks staged in
+// the wave's own LDS tiles), and a combine kernel merges the splits' partial
+// softmax states (flash-decoding).
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -101,6 +102,43 @@ __device__ __forceinline__ void rope_row(const uint16_t *x, uint16_t *y, long lo
     *reinterpret_cast<uint4 *>(y + f0 + half) = *reinterpret_cast<const uint4 *>(rb);
 }
 
+// One query row as the 8 B operands of S^T = K Q^T: operand ks of lane half hf
+// holds features 16ks + 8hf + e, e = 0..7, after rope at position pos, times
+// qs (the score scale with log2(e) folded in, so softmax runs on exp2).
+__device__ __forceinline__ void load_q_operand(const uint16_t *qg, long long pos, int rope_dims,
+                                               double log2_base, float qs, int hf,
+                                               bf16x8 (&qop)[D / 16]) {
+    float x[D / 16][8];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        uint16_t u[8];
+        *reinterpret_cast<uint4 *>(u) = *reinterpret_cast<const uint4 *>(qg + 16 * ks + 8 * hf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[ks][e] = bf2f(u[e]);
+    }
+    // rotate-half pairs lie hs = rope_dims/32 operand steps apart; feature
+    // 16ks + 8hf + e is in the first half of the rotated span iff ks < hs
+    const int hs = rope_dims / 32;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+        for (int dd = 1; dd <= D / 32; ++dd)
+            if (ks + dd < D / 16 && dd == hs && ks < hs) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float s, c;
+                    rope_sincos(pos, 16 * ks + 8 * hf + e, rope_dims, log2_base, s, c);
+                    const float u = x[ks][e], v = x[ks + dd][e];
+                    x[ks][e] = u * c - v * s;
+                    x[ks + dd][e] = u * s + v * c;
+                }
+            }
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qop[ks][e] = static_cast<__bf16>(x[ks][e] * qs);
+}
+
 // rope of every k row: [B, L, Hkv, d] -> same shape. 16 threads per row.
 __global__ __launch_bounds__(SNT) void rope_rows_kernel(SoftmaxArgs a, uint16_t *kr) {
     const long long row = (long long)blockIdx.x * (SNT / 16) + threadIdx.x / 16;
@@ -142,41 +180,12 @@ __global__ __launch_bounds__(SNT) void fa_prefill_kernel(SoftmaxArgs a, const ui
     const long long qrow = q0 + 32 * w + r32;  // this lane's query
     const long long qlast = q0 + 32 * w + 31 < L - 1 ? q0 + 32 * w + 31 : L - 1;  // wave's last query
 
-    // ---- the lane's query as 8 MFMA operands: features 16ks + 8hf + e
+    // ---- the lane's query as 8 MFMA operands
     bf16x8 qop[D / 16];
     {
         const long long qr = qrow < L ? qrow : L - 1;
-        const uint16_t *qg = static_cast<const uint16_t *>(a.q) + ((b * L + qr) * a.q_heads + h) * (long long)D;
-        float x[D / 16][8];
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            uint16_t u[8];
-            *reinterpret_cast<uint4 *>(u) = *reinterpret_cast<const uint4 *>(qg + 16 * ks + 8 * hf);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[ks][e] = bf2f(u[e]);
-        }
-        // rotate-half pairs lie hs = rope_dims/32 operand steps apart; feature
-        // 16ks + 8hf + e is in the first half of the rotated span iff ks < hs
-        const int hs = a.rope_dims / 32;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-            for (int dd = 1; dd <= D / 32; ++dd)
-                if (ks + dd < D / 16 && dd == hs && ks < hs) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        float s, c;
-                        rope_sincos(a.pos0 + qr, 16 * ks + 8 * hf + e, a.rope_dims, a.log2_base, s, c);
-                        const float u = x[ks][e], v = x[ks + dd][e];
-                        x[ks][e] = u * c - v * s;
-                        x[ks + dd][e] = u * s + v * c;
-                    }
-                }
-        const float qs = a.scale * 1.4426950408889634f;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qop[ks][e] = static_cast<__bf16>(x[ks][e] * qs);
+        load_q_operand(static_cast<const uint16_t *>(a.q) + ((b * L + qr) * a.q_heads + h) * (long long)D,
+                       a.pos0 + qr, a.rope_dims, a.log2_base, a.scale * 1.4426950408889634f, hf, qop);
     }
 
     f32x16 o[4];
@@ -290,6 +299,194 @@ __global__ __launch_bounds__(SNT) void fa_prefill_kernel(SoftmaxArgs a, const ui
     }
 }
 
+// ---------------------------------------------------------------------------
+// Decode
+
+constexpr int DKB = 32;  // keys per decode block (one wave)
+constexpr int kDecodeRec = 132;  // floats per partial record: O[128], m, l, 2 pad
+
+// rope(k_new) into the key cache and v_new into the value cache at each
+// sequence's position; 16 threads per (sequence, K/V head).
+__global__ __launch_bounds__(SNT) void rope_append_kernel(SoftmaxDecodeArgs a) {
+    const int row = blockIdx.x * (SNT / 16) + threadIdx.x / 16;
+    if (row >= a.batch * a.kv_heads) return;
+    const int b = row / a.kv_heads, g = row % a.kv_heads;
+    const int n = a.lengths[b];
+    if (n < 0 || n >= a.capacity) return;  // padding row
+    const long long dst = (((long long)b * a.capacity + n) * a.kv_heads + g) * D;
+    const int j = threadIdx.x % 16;
+    *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.v_cache) + dst + 8 * j) =
+        *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.v_new) + (long long)row * D + 8 * j);
+    rope_row(static_cast<const uint16_t *>(a.k_new) + (long long)row * D,
+             static_cast<uint16_t *>(a.k_cache) + dst, n, a.rope_dims, a.log2_base, j);
+}
+
+// One wave per (sequence b, K/V head g, key split s): keys
+// [s * chunk, min((s + 1) * chunk, n + 1)) with n = lengths[b], for the
+// q_heads / kv_heads query heads of the group as MFMA columns. With one split
+// the wave writes o; otherwise it writes its unnormalised partial (O, running
+// max m in log2 units, sum l) for the combine kernel.
+template <typename OutT>
+__global__ __launch_bounds__(SNT) void fd_kernel(SoftmaxDecodeArgs a, int splits, long long chunk,
+                                                 float *ws) {
+    __shared__ __attribute__((aligned(16))) __bf16 Kw[4][DKB * SPT];
+    __shared__ __attribute__((aligned(16))) __bf16 Vw[4][DKB * SPT];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const long long unit = (long long)blockIdx.x * 4 + w;
+    if (unit >= (long long)a.batch * a.kv_heads * splits) return;
+    const int s = (int)(unit % splits);
+    const int bg = (int)(unit / splits);
+    const int b = bg / a.kv_heads, g = bg % a.kv_heads;
+    const int G = a.q_heads / a.kv_heads;
+    const int r32 = lane & 31, hf = lane >> 5;
+    const bool col = r32 < G;
+    const int h = g * G + (col ? r32 : 0);
+    const int n = a.lengths[b];
+    const long long kbeg = (long long)s * chunk;
+    if (n < 0 || n >= a.capacity) {  // padding row: zero output
+        if (splits == 1 && col) {
+            OutT *og = static_cast<OutT *>(a.o) + ((long long)b * a.q_heads + h) * D;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int gv = 0; gv < 4; ++gv) put_out4<OutT>(og + 32 * c + 8 * gv + 4 * hf, 0.f, 0.f, 0.f, 0.f);
+        }
+        return;
+    }
+    if (kbeg > n) return;  // split past the sequence: the combine reads only live splits
+    const long long kend = kbeg + chunk < (long long)n + 1 ? kbeg + chunk : (long long)n + 1;
+
+    bf16x8 qop[D / 16];
+    load_q_operand(static_cast<const uint16_t *>(a.q) + ((long long)b * a.q_heads + h) * D, n,
+                   a.rope_dims, a.log2_base, a.scale * 1.4426950408889634f, hf, qop);
+    if (!col) {
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qop[ks][e] = static_cast<__bf16>(0.f);
+    }
+
+    const int ts = a.kv_heads * D;
+    const long long base = ((long long)b * a.capacity * a.kv_heads + g) * D;  // token 0, head g
+    const uint16_t *kc = static_cast<const uint16_t *>(a.k_cache) + base;
+    const uint16_t *vc = static_cast<const uint16_t *>(a.v_cache) + base;
+    __bf16 *Kt = Kw[w], *Vt = Vw[w];
+    // staging: lane holds block rows (lane/16) + 4i, i = 0..7, features 8(lane%16)..
+    const int srow = lane >> 4, scol = 8 * (lane & 15);
+    uint4 sk[8], sv[8];
+#define LT_FD_LOAD(K0)                                                                  \
+    {                                                                                   \
+        const long long k0_ = (K0);                                                     \
+        const int last_ = kend - 1 - k0_ < DKB - 1 ? (int)(kend - 1 - k0_) : DKB - 1;   \
+        const uint16_t *kb_ = kc + k0_ * ts, *vb_ = vc + k0_ * ts;                      \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                 \
+            const int off_ = min(srow + 4 * i, last_) * ts + scol;                      \
+            sk[i] = stream_load16(kb_ + off_);                                          \
+            sv[i] = stream_load16(vb_ + off_);                                          \
+        }                                                                               \
+    }
+    LT_FD_LOAD(kbeg)
+    f32x16 o[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[c][v] = 0.f;
+    float mrun = -__builtin_inff(), lsum = 0.f;
+    for (long long k0 = kbeg; k0 < kend; k0 += DKB) {
+        // the wave's own tiles: DS instructions of one wave run in order, so
+        // the previous block's reads are done before these writes land
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            *reinterpret_cast<uint4 *>(Kt + LK::off(srow + 4 * i, scol)) = sk[i];
+            *reinterpret_cast<uint4 *>(Vt + LK::off(srow + 4 * i, scol)) = sv[i];
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (k0 + DKB < kend) LT_FD_LOAD(k0 + DKB)
+        f32x16 sc;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sc[v] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) sc = mma(ld_op<LK>(Kt, 0, 16 * ks, lane), qop[ks], sc);
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            if (k0 + 8 * (v >> 2) + 4 * hf + (v & 3) >= kend) sc[v] = -__builtin_inff();
+            mx = fmaxf(mx, sc[v]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(mrun, mx);  // finite: key k0 is live for every lane
+        const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+        mrun = mnew;
+        float ps = 0.f;
+        bf16x8 pb[2];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const float p = __builtin_amdgcn_exp2f(sc[v] - mnew);
+            ps += p;
+            pb[v / 8][v % 8] = static_cast<__bf16>(p);
+        }
+        lsum = lsum * alpha + ps;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) o[c] *= alpha;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) o[c] = mma(ld_vt(Vt, 32 * c, 16 * j, lane), pb[j], o[c]);
+        __builtin_amdgcn_wave_barrier();
+    }
+#undef LT_FD_LOAD
+    lsum += __shfl_xor(lsum, 32);
+    if (!col) return;
+    if (splits == 1) {
+        const float inv = 1.f / lsum;
+        OutT *og = static_cast<OutT *>(a.o) + ((long long)b * a.q_heads + h) * D;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int gv = 0; gv < 4; ++gv)
+                put_out4<OutT>(og + 32 * c + 8 * gv + 4 * hf, o[c][4 * gv] * inv, o[c][4 * gv + 1] * inv,
+                               o[c][4 * gv + 2] * inv, o[c][4 * gv + 3] * inv);
+    } else {
+        float *rec = ws + (((long long)b * a.q_heads + h) * splits + s) * kDecodeRec;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int gv = 0; gv < 4; ++gv)
+                *reinterpret_cast<float4 *>(rec + 32 * c + 8 * gv + 4 * hf) =
+                    make_float4(o[c][4 * gv], o[c][4 * gv + 1], o[c][4 * gv + 2], o[c][4 * gv + 3]);
+        if (hf == 0) *reinterpret_cast<float2 *>(rec + D) = make_float2(mrun, lsum);
+    }
+}
+
+// Merges the live splits of each (sequence, query head): one thread per
+// feature, o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+template <typename OutT>
+__global__ __launch_bounds__(D) void fd_combine_kernel(SoftmaxDecodeArgs a, int splits, long long chunk,
+                                                       const float *ws) {
+    const int bh = blockIdx.x;
+    const int b = bh / a.q_heads;
+    const int t = threadIdx.x;
+    OutT *og = static_cast<OutT *>(a.o) + (long long)bh * D + t;
+    const int n = a.lengths[b];
+    if (n < 0 || n >= a.capacity) {
+        *og = static_cast<OutT>(0.f);
+        return;
+    }
+    const int live = (int)(((long long)n + chunk) / chunk);  // splits holding keys 0..n
+    const float *rec = ws + (long long)bh * splits * kDecodeRec;
+    float M = -__builtin_inff();
+    for (int s = 0; s < live; ++s) M = fmaxf(M, rec[(long long)s * kDecodeRec + D]);
+    float l = 0.f, acc = 0.f;
+    for (int s = 0; s < live; ++s) {
+        const float *r = rec + (long long)s * kDecodeRec;
+        const float e = __builtin_amdgcn_exp2f(r[D] - M);
+        l += e * r[D + 1];
+        acc += e * r[t];
+    }
+    *og = static_cast<OutT>(acc / l);
+}
+
 }  // namespace
 
 hipError_t launch_softmax_prefill(const SoftmaxArgs &a, void *workspace, lt_dtype out_dtype,
@@ -307,6 +504,31 @@ hipError_t launch_softmax_prefill(const SoftmaxArgs &a, void *workspace, lt_dtyp
         hipLaunchKernelGGL((fa_prefill_kernel<float>), grid, dim3(SNT), 0, stream, a, kr);
     else
         hipLaunchKernelGGL((fa_prefill_kernel<__bf16>), grid, dim3(SNT), 0, stream, a, kr);
+    return hipGetLastError();
+}
+
+hipError_t launch_softmax_decode(const SoftmaxDecodeArgs &a, const SoftmaxDecodePlan &plan,
+                                 float *workspace, lt_dtype out_dtype, hipStream_t stream) {
+    clear_pending_error();
+    const int rows = a.batch * a.kv_heads;
+    hipLaunchKernelGGL(rope_append_kernel, dim3((rows + SNT / 16 - 1) / (SNT / 16)), dim3(SNT), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long long waves = (long long)rows * plan.splits;
+    const dim3 grid((unsigned)((waves + 3) / 4));
+    if (out_dtype == LT_F32)
+        hipLaunchKernelGGL((fd_kernel<float>), grid, dim3(SNT), 0, stream, a, plan.splits, plan.chunk, workspace);
+    else
+        hipLaunchKernelGGL((fd_kernel<__bf16>), grid, dim3(SNT), 0, stream, a, plan.splits, plan.chunk, workspace);
+    e = hipGetLastError();
+    if (e != hipSuccess || plan.splits == 1) return e;
+    const dim3 cgrid((unsigned)(a.batch * a.q_heads));
+    if (out_dtype == LT_F32)
+        hipLaunchKernelGGL((fd_combine_kernel<float>), cgrid, dim3(D), 0, stream, a, plan.splits, plan.chunk,
+                           workspace);
+    else
+        hipLaunchKernelGGL((fd_combine_kernel<__bf16>), cgrid, dim3(D), 0, stream, a, plan.splits, plan.chunk,
+                           workspace);
     return hipGetLastError();
 }
 

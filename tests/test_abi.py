@@ -376,3 +376,56 @@ def test_softmax_prefill_noops_need_no_gpu():
     assert softmax_prefill(seqlen=0, q=None) == la.LT_OK
     assert softmax_prefill(batch=0, k=None) == la.LT_OK
     assert softmax_prefill(q_heads=0, kv_heads=0, o=None) == la.LT_OK
+
+
+def softmax_decode(**kw):
+    args = dict(q=A, k_new=A + 10 * MB, v_new=A + 20 * MB, k_cache=A + 100 * MB,
+                v_cache=A + 300 * MB, lengths=A + 30 * MB, o=A + 40 * MB, out_dtype=la.LT_F32,
+                batch=2, capacity=1000, q_heads=8, kv_heads=2, head_dim=128, rope_dims=64,
+                rope_base=10000.0, scale=0.088, workspace=None, workspace_bytes=0, stream=None)
+    args.update(kw)
+    return la.lib.lt_softmax_decode(*args.values())
+
+
+@pytest.mark.parametrize("field", ["q", "k_new", "v_new", "k_cache", "v_cache", "lengths", "o"])
+def test_softmax_decode_null_pointers(field):
+    assert softmax_decode(**{field: None}) == la.LT_ERR_NULL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(out_dtype=2), la.LT_ERR_DTYPE),
+    (dict(head_dim=256), la.LT_ERR_SHAPE),
+    (dict(q_heads=66, kv_heads=2), la.LT_ERR_SHAPE),     # 33 query heads per K/V head
+    (dict(q_heads=9, kv_heads=2), la.LT_ERR_SHAPE),
+    (dict(capacity=-1), la.LT_ERR_SHAPE),
+    (dict(capacity=1 << 31), la.LT_ERR_SHAPE),           # positions are int32
+    (dict(capacity=0), la.LT_ERR_SHAPE),                 # no row for the new token
+    (dict(batch=-2), la.LT_ERR_SHAPE),
+    (dict(rope_dims=40), la.LT_ERR_SHAPE),
+    (dict(rope_base=0.5), la.LT_ERR_VALUE),
+    (dict(scale=-1.0), la.LT_ERR_VALUE),
+])
+def test_softmax_decode_bad_arguments(kw, code):
+    assert softmax_decode(**kw) == code
+
+
+def test_softmax_decode_alias_checks():
+    assert softmax_decode(o=A + 8) == la.LT_ERR_ALIAS                    # o on q
+    assert softmax_decode(k_cache=A + 10 * MB) == la.LT_ERR_ALIAS        # k_cache on k_new
+    assert softmax_decode(v_cache=A + 100 * MB + 4096) == la.LT_ERR_ALIAS  # v_cache inside k_cache
+    assert softmax_decode(o=A + 30 * MB) == la.LT_ERR_ALIAS              # o on lengths
+    n = la.lt_softmax_decode_workspace_bytes(64, 100000, 8, 2)
+    assert n > 0
+    big = dict(batch=64, capacity=100000, k_cache=A + 1000 * MB, v_cache=A + 5000 * MB)
+    assert softmax_decode(**big, workspace=A + 40 * MB, workspace_bytes=n) == la.LT_ERR_ALIAS  # on o
+    assert softmax_decode(**big, workspace=A + 5000 * MB + 64,
+                          workspace_bytes=n) == la.LT_ERR_ALIAS            # inside v_cache
+
+
+def test_softmax_decode_noops_and_workspace_query():
+    assert softmax_decode(batch=0, q=None) == la.LT_OK
+    assert softmax_decode(q_heads=0, kv_heads=0, o=None) == la.LT_OK
+    assert la.lt_softmax_decode_workspace_bytes(16, 33792, 64, 8) == 16 * 64 * 16 * 132 * 4
+    assert la.lt_softmax_decode_workspace_bytes(1, 200, 8, 1) == 0       # one split: none needed
+    assert la.lt_softmax_decode_workspace_bytes(0, 200, 8, 1) == 0
+    assert la.lt_softmax_decode_workspace_bytes(1, 200, 8, 3) == 0       # invalid sizes
