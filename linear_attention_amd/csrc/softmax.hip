@@ -29,17 +29,27 @@
 
 #include <stdint.h>
 
+#include <numeric>
+
 #include "internal.h"
 #include "tiles.h"
 
 namespace lt {
 namespace {
 
-constexpr int SQB = 128;      // queries per prefill workgroup
 constexpr int SKB = 64;       // keys per block
-constexpr int SNT = 256;      // 4 waves
-constexpr int SPT = D + 8;    // pitch of the K, V tiles
+constexpr int SNT = 256;      // 4 waves (RoPE and decode kernels)
+constexpr int FNT = 512;      // 8 waves (prefill)
+constexpr int FW = FNT / 64;
+// LDS tile pitches (bf16). K rows are read whole (ds_read_b128 per lane, a lane
+// per row): a pitch of 68 dwords puts 16 consecutive rows on distinct banks. V
+// is read with ds_read_b64_tr_b16 (four rows per 16-lane group): a pitch of
+// 80 dwords (16 mod 64) keeps the four rows of both 16-lane groups of a half
+// wave on distinct banks.
+constexpr int SPT = D + 8;
+constexpr int SPV = D + 32;
 using LK = LPad<SPT>;
+using LV = LPad<SPV>;
 
 __device__ __forceinline__ float bf2f(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
 __device__ __forceinline__ uint16_t f2bf(float f) {
@@ -57,8 +67,8 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 __device__ __forceinline__ bf16x8 ld_vt(const __bf16 *t, int c0, int k0, int lane) {
     const int li = lane & 15, grp = lane >> 4;
     const int row = k0 + 4 * (grp >> 1) + (li >> 2), col = c0 + 16 * (grp & 1) + 4 * (li & 3);
-    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(t + LK::off(row, col)));
-    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(t + LK::off(row + 8, col)));
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(t + LV::off(row, col)));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(t + LV::off(row + 8, col)));
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
@@ -162,23 +172,43 @@ __device__ __forceinline__ void put_out4<__bf16>(__bf16 *p, float x, float y, fl
     stream_store_bits(p, b);
 }
 
-template <typename OutT>
-__global__ __launch_bounds__(SNT) void fa_prefill_kernel(SoftmaxArgs a, const uint16_t *kr) {
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[SKB * SPT];
-    __shared__ __attribute__((aligned(16))) __bf16 Vs[SKB * SPT];
+// Workgroup geometry of the prefill kernel: FW waves of 32 queries each cover
+// hpw query heads of one K/V group (hpw = gcd(group size, FW)) and
+// FW / hpw consecutive 32-query blocks, so every K/V tile staged in LDS feeds
+// FW waves. Workgroups are numbered so that the ones of one (sequence, K/V
+// head) run on one XCD (the hardware deals workgroups to the 8 XCDs in turn),
+// where that head's K and V stay in the XCD's L2; within a group the late
+// (long) query blocks come first.
+struct FaGeom {
+    int hpw;         // query heads per workgroup
+    int qpw;         // queries per workgroup (32 * FW / hpw)
+    int nqb;         // query blocks per head
+    int per_group;   // workgroups per (sequence, K/V head)
+    long long real;  // workgroups with work (grid is this rounded up to 8)
+};
 
-    const int nqb = (int)((a.seqlen + SQB - 1) / SQB);
-    const int bh = blockIdx.x % (a.batch * a.q_heads);
-    const int qb = nqb - 1 - (int)(blockIdx.x / (a.batch * a.q_heads));  // late blocks first
-    const int h = bh % a.q_heads, b = bh / a.q_heads;
-    const int g = h / (a.q_heads / a.kv_heads);
+template <typename OutT>
+__global__ __launch_bounds__(FNT) void fa_prefill_kernel(SoftmaxArgs a, const uint16_t *kr, FaGeom geo) {
+    __shared__ __attribute__((aligned(16))) __bf16 Ks[2][SKB * SPT];
+    __shared__ __attribute__((aligned(16))) __bf16 Vs[2][SKB * SPV];
+
+    const long long per_xcd = gridDim.x / 8;
+    const long long u = (long long)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (u >= geo.real) return;  // padding workgroup
+    const int G = a.q_heads / a.kv_heads;
+    const int bg = (int)(u / geo.per_group), rem = (int)(u % geo.per_group);
+    const int hsubs = G / geo.hpw;
+    const int qb = geo.nqb - 1 - rem / hsubs;  // late blocks first
+    const int b = bg / a.kv_heads, g = bg % a.kv_heads;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = g * G + (rem % hsubs) * geo.hpw + w % geo.hpw;
     const int r32 = lane & 31, hf = lane >> 5;
     const long long L = a.seqlen;
-    const long long q0 = (long long)qb * SQB;
-    const long long qrow = q0 + 32 * w + r32;  // this lane's query
-    const long long qlast = q0 + 32 * w + 31 < L - 1 ? q0 + 32 * w + 31 : L - 1;  // wave's last query
+    const long long q0 = (long long)qb * geo.qpw;
+    const long long qw0 = q0 + 32 * (w / geo.hpw);                     // wave's first query
+    const long long qrow = qw0 + r32;                                   // this lane's query
+    const long long qlast = qw0 + 31 < L - 1 ? qw0 + 31 : L - 1;        // wave's last query
 
     // ---- the lane's query as 8 MFMA operands
     bf16x8 qop[D / 16];
@@ -199,65 +229,76 @@ __global__ __launch_bounds__(SNT) void fa_prefill_kernel(SoftmaxArgs a, const ui
     const uint16_t *kg = kr + kvh * D;
     const uint16_t *vg = static_cast<const uint16_t *>(a.v) + kvh * D;
     const int ts = a.kv_heads * D;                             // token stride (elements)
-    const long long kend = q0 + SQB < L ? q0 + SQB : L;        // keys [0, kend)
+    const long long kend = q0 + geo.qpw < L ? q0 + geo.qpw : L; // keys [0, kend)
     const int nkb = (int)((kend + SKB - 1) / SKB);
-    // staging: thread t holds block rows (t/16) + 16i, i = 0..3, features
+    // staging: thread t holds block rows t/16 and t/16 + 32, features
     // 8(t%16)..; rows past the end repeat the last key (masked later)
     const int srow = tid >> 4, scol = 8 * (tid & 15);
-    uint4 sk0, sk1, sk2, sk3, sv0, sv1, sv2, sv3;
+    uint4 sk0, sk1, sv0, sv1;
 #define LT_FA_LOAD(KB)                                                                      \
     {                                                                                       \
         const long long k0_ = (long long)(KB) * SKB;                                        \
         const uint16_t *kb_ = kg + k0_ * ts, *vb_ = vg + k0_ * ts;                          \
         const int last_ = L - 1 - k0_ < SKB - 1 ? (int)(L - 1 - k0_) : SKB - 1;             \
-        const int o0_ = min(srow, last_) * ts + scol, o1_ = min(srow + 16, last_) * ts + scol; \
-        const int o2_ = min(srow + 32, last_) * ts + scol, o3_ = min(srow + 48, last_) * ts + scol; \
+        const int o0_ = min(srow, last_) * ts + scol, o1_ = min(srow + 32, last_) * ts + scol; \
         sk0 = *reinterpret_cast<const uint4 *>(kb_ + o0_);                                  \
         sk1 = *reinterpret_cast<const uint4 *>(kb_ + o1_);                                  \
-        sk2 = *reinterpret_cast<const uint4 *>(kb_ + o2_);                                  \
-        sk3 = *reinterpret_cast<const uint4 *>(kb_ + o3_);                                  \
-        sv0 = stream_load16(vb_ + o0_);                                                     \
-        sv1 = stream_load16(vb_ + o1_);                                                     \
-        sv2 = stream_load16(vb_ + o2_);                                                     \
-        sv3 = stream_load16(vb_ + o3_);                                                     \
+        sv0 = *reinterpret_cast<const uint4 *>(vb_ + o0_);                                  \
+        sv1 = *reinterpret_cast<const uint4 *>(vb_ + o1_);                                  \
     }
     if (nkb > 0) LT_FA_LOAD(0)
     for (int kb = 0; kb < nkb; ++kb) {
-        __syncthreads();  // previous block's tiles fully read
-        *reinterpret_cast<uint4 *>(Ks + LK::off(srow, scol)) = sk0;
-        *reinterpret_cast<uint4 *>(Ks + LK::off(srow + 16, scol)) = sk1;
-        *reinterpret_cast<uint4 *>(Ks + LK::off(srow + 32, scol)) = sk2;
-        *reinterpret_cast<uint4 *>(Ks + LK::off(srow + 48, scol)) = sk3;
-        *reinterpret_cast<uint4 *>(Vs + LK::off(srow, scol)) = sv0;
-        *reinterpret_cast<uint4 *>(Vs + LK::off(srow + 16, scol)) = sv1;
-        *reinterpret_cast<uint4 *>(Vs + LK::off(srow + 32, scol)) = sv2;
-        *reinterpret_cast<uint4 *>(Vs + LK::off(srow + 48, scol)) = sv3;
+        // double-buffered tiles: buffer kb&1 was last read in block kb-2, which
+        // every wave finished before the barrier of block kb-1
+        __bf16 *Kb = Ks[kb & 1], *Vb = Vs[kb & 1];
+        *reinterpret_cast<uint4 *>(Kb + LK::off(srow, scol)) = sk0;
+        *reinterpret_cast<uint4 *>(Kb + LK::off(srow + 32, scol)) = sk1;
+        *reinterpret_cast<uint4 *>(Vb + LV::off(srow, scol)) = sv0;
+        *reinterpret_cast<uint4 *>(Vb + LV::off(srow + 32, scol)) = sv1;
         if (kb + 1 < nkb) LT_FA_LOAD(kb + 1)
         __syncthreads();  // tiles visible
         const long long k0 = (long long)kb * SKB;
         if (k0 > qlast) continue;  // every key of this block is after the wave's queries
 
-        // S^T blocks: keys k0 + 32kk.., this lane's query column
+        // S^T blocks: keys k0 + 32kk.., this lane's query column; the two
+        // halves interleave and each step's K operands load one step ahead
         f32x16 sc[2];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int v = 0; v < 16; ++v) sc[kk][v] = 0.f;
+        {
+            bf16x8 ka0 = ld_op<LK>(Kb, 0, 0, lane), ka1 = ld_op<LK>(Kb, 32, 0, lane);
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks)
-                sc[kk] = mma(ld_op<LK>(Ks, 32 * kk, 16 * ks, lane), qop[ks], sc[kk]);
+            for (int ks = 0; ks < D / 16; ++ks) {
+                bf16x8 kn0, kn1;
+                if (ks + 1 < D / 16) {
+                    kn0 = ld_op<LK>(Kb, 0, 16 * (ks + 1), lane);
+                    kn1 = ld_op<LK>(Kb, 32, 16 * (ks + 1), lane);
+                }
+                sc[0] = mma(ka0, qop[ks], sc[0]);
+                sc[1] = mma(ka1, qop[ks], sc[1]);
+                ka0 = kn0;
+                ka1 = kn1;
+            }
         }
         // causal mask (and keys past the end) on blocks that reach the diagonal
-        const bool diag = k0 + SKB - 1 > q0 + 32 * w || k0 + SKB > L;
+        // (a wave-uniform test); key 32kk + 8(v/4) + 4hf + v%4 of the block
+        if (k0 + SKB - 1 > qw0 || k0 + SKB > L) {
+            const int lim_q = (int)(qrow - k0);  // last key of this lane's query
+            const int lim_l = (int)(L - 1 - k0 < SKB ? L - 1 - k0 : SKB);
+            const int lim = lim_q < lim_l ? lim_q : lim_l;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    if (32 * kk + 8 * (v >> 2) + 4 * hf + (v & 3) > lim) sc[kk][v] = -__builtin_inff();
+        }
         float mx = -__builtin_inff();
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const long long key = k0 + 32 * kk + 8 * (v >> 2) + 4 * hf + (v & 3);
-                if (diag && (key > qrow || key >= L)) sc[kk][v] = -__builtin_inff();
-                mx = fmaxf(mx, sc[kk][v]);
-            }
+            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[kk][v]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float mnew = fmaxf(mrun, mx);
         const float alpha = mnew == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(mrun - mnew);
@@ -277,10 +318,22 @@ __global__ __launch_bounds__(SNT) void fa_prefill_kernel(SoftmaxArgs a, const ui
 #pragma unroll
             for (int c = 0; c < 4; ++c) o[c] *= alpha;
         }
+        {
+            bf16x8 va[4];
 #pragma unroll
-        for (int j = 0; j < SKB / 16; ++j)
+            for (int c = 0; c < 4; ++c) va[c] = ld_vt(Vb, 32 * c, 0, lane);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) o[c] = mma(ld_vt(Vs, 32 * c, 16 * j, lane), pb[j], o[c]);
+            for (int j = 0; j < SKB / 16; ++j) {
+                bf16x8 vn[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    if (j + 1 < SKB / 16) vn[c] = ld_vt(Vb, 32 * c, 16 * (j + 1), lane);
+                    o[c] = mma(va[c], pb[j], o[c]);
+                }
+#pragma unroll
+                for (int c = 0; c < 4; ++c) va[c] = vn[c];
+            }
+        }
     }
 
 #undef LT_FA_LOAD
@@ -330,7 +383,7 @@ template <typename OutT>
 __global__ __launch_bounds__(SNT) void fd_kernel(SoftmaxDecodeArgs a, int splits, long long chunk,
                                                  float *ws) {
     __shared__ __attribute__((aligned(16))) __bf16 Kw[4][DKB * SPT];
-    __shared__ __attribute__((aligned(16))) __bf16 Vw[4][DKB * SPT];
+    __shared__ __attribute__((aligned(16))) __bf16 Vw[4][DKB * SPV];
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const long long unit = (long long)blockIdx.x * 4 + w;
@@ -399,7 +452,7 @@ __global__ __launch_bounds__(SNT) void fd_kernel(SoftmaxDecodeArgs a, int splits
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             *reinterpret_cast<uint4 *>(Kt + LK::off(srow + 4 * i, scol)) = sk[i];
-            *reinterpret_cast<uint4 *>(Vt + LK::off(srow + 4 * i, scol)) = sv[i];
+            *reinterpret_cast<uint4 *>(Vt + LV::off(srow + 4 * i, scol)) = sv[i];
         }
         __builtin_amdgcn_wave_barrier();
         if (k0 + DKB < kend) LT_FD_LOAD(k0 + DKB)
@@ -498,12 +551,18 @@ hipError_t launch_softmax_prefill(const SoftmaxArgs &a, void *workspace, lt_dtyp
                        0, stream, a, kr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const long long nqb = (a.seqlen + SQB - 1) / SQB;
-    const dim3 grid((unsigned)(nqb * a.batch * a.q_heads));
+    FaGeom geo;
+    const int G = a.q_heads / a.kv_heads;
+    geo.hpw = std::gcd(G, FW);
+    geo.qpw = 32 * FW / geo.hpw;
+    geo.nqb = (int)((a.seqlen + geo.qpw - 1) / geo.qpw);
+    geo.per_group = geo.nqb * (G / geo.hpw);
+    geo.real = (long long)a.batch * a.kv_heads * geo.per_group;
+    const dim3 grid((unsigned)((geo.real + 7) / 8 * 8));
     if (out_dtype == LT_F32)
-        hipLaunchKernelGGL((fa_prefill_kernel<float>), grid, dim3(SNT), 0, stream, a, kr);
+        hipLaunchKernelGGL((fa_prefill_kernel<float>), grid, dim3(FNT), 0, stream, a, kr, geo);
     else
-        hipLaunchKernelGGL((fa_prefill_kernel<__bf16>), grid, dim3(SNT), 0, stream, a, kr);
+        hipLaunchKernelGGL((fa_prefill_kernel<__bf16>), grid, dim3(FNT), 0, stream, a, kr, geo);
     return hipGetLastError();
 }
 
