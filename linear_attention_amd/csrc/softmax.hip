@@ -51,6 +51,12 @@ constexpr int SPV = D + 32;
 using LK = LPad<SPT>;
 using LV = LPad<SPV>;
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr bf16x2 kOnes2 = {(__bf16)1.f, (__bf16)1.f};
+// Growth of a score over the running reference maximum (log2 units) that is
+// let pass before O and l are rescaled.
+constexpr float kStale = 8.f;
+
 __device__ __forceinline__ float bf2f(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
 __device__ __forceinline__ uint16_t f2bf(float f) {
     const __bf16 b = static_cast<__bf16>(f);
@@ -223,7 +229,7 @@ __global__ __launch_bounds__(FNT) void fa_prefill_kernel(SoftmaxArgs a, const ui
     for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[c][v] = 0.f;
-    float mrun = -__builtin_inff(), lsum = 0.f;
+    float mrun = 0.f, lsum = 0.f;  // lane's reference maximum (log2 units) and sum
 
     const long long kvh = (long long)b * L * a.kv_heads + g;  // row of token 0, K/V head g
     const uint16_t *kg = kr + kvh * D;
@@ -299,25 +305,34 @@ __global__ __launch_bounds__(FNT) void fa_prefill_kernel(SoftmaxArgs a, const ui
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[kk][v]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(mrun, mx);
-        const float alpha = mnew == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(mrun - mnew);
-        mrun = mnew;
-        float ps = 0.f;
-        bf16x8 pb[SKB / 16];  // P^T operands: step j holds keys 16j + 4hf + 0..3, 16j + 8 + 4hf + 0..3
+        mx = fmaxf(mx, __shfl_xor(mx, 32));  // finite: key k0 is live for every lane
+        // The reference maximum m is the first block's maximum and afterwards
+        // moves only when a score exceeds it by more than kStale (log2 units):
+        // the probabilities stay below 2^kStale, and the rescale of O and l (a
+        // wave-uniform branch) is rare after the first blocks.
+        if (kb == 0) {
+            mrun = mx;
+        } else if (__builtin_amdgcn_ballot_w64(mx > mrun + kStale)) {
+            const float mnew = fmaxf(mx, mrun);
+            const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+            mrun = mnew;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) o[c] *= alpha;
+            lsum *= alpha;
+        }
+        // P^T operands: step j holds keys 16j + 4hf + 0..3, 16j + 8 + 4hf + 0..3;
+        // l sums the bf16 probabilities that enter the product
+        bf16x8 pb[SKB / 16];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const float p = __builtin_amdgcn_exp2f(sc[kk][v] - mnew);  // exp2(-inf) = 0
-                ps += p;
-                pb[2 * kk + v / 8][v % 8] = static_cast<__bf16>(p);
-            }
-        lsum = lsum * alpha + ps;
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+            for (int v = 0; v < 16; ++v)
+                pb[2 * kk + v / 8][v % 8] = static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[kk][v] - mrun));
 #pragma unroll
-            for (int c = 0; c < 4; ++c) o[c] *= alpha;
-        }
+        for (int j = 0; j < SKB / 16; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; e += 2)
+                lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[j][e], pb[j][e + 1]}, kOnes2, lsum, false);
         {
             bf16x8 va[4];
 #pragma unroll
