@@ -18,11 +18,16 @@ Prints ONE JSON line. Besides the driver's fields it carries:
                 fused into the epilogue (bf16 gate, bf16 y);
   backward      lt_prefill_backward (dq, dk, dv, dS0) on the M1 layer and on a
                 4 x 8192-token batch of the same heads;
+  softmax       the hybrid's softmax attention layer (§02: 64 query / 8 K/V
+                heads, partial RoPE): causal prefill of 32768 tokens against the
+                bf16 MFMA peak, and a 16 x 32768-token KV-cache decode step
+                against HBM;
   cpu_baseline  the fp64 oracle on the host cores, timed on the same prefill
                 workload (reported baseline, not a target).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps N]
-                       [--no-cpu] [--no-decode]
+                       [--no-cpu] [--no-decode] [--no-norm-gate] [--no-backward]
+                       [--no-softmax]
        python bench.py --workload long_1m|varlen|tiny_f32   (one extra workload)
        python bench.py --copy-calibration BYTES            (plain device copy, for
                                                             rocprofv3 counter scaling)
@@ -217,6 +222,76 @@ def run_backward(la, torch, steps, warmup, batch, seqlen):
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "bytes_per_launch": nbytes,
                          "kernel": "lt_prefill_backward call: dq forward pass + bwd_kv_kernel"}}
+
+
+MFMA_BF16_PEAK_TFS = 2500.0
+
+
+def _event_times(torch, call, steps, warmup, stream):
+    import numpy as np
+
+    for _ in range(warmup):
+        call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = [a.elapsed_time(b) for a, b in ev]
+    return float(np.mean(t)), float(np.median(t))
+
+
+def run_softmax(la, torch, steps, warmup, decode_steps):
+    """The hybrid's softmax attention layer (64 query heads, 8 K/V heads of 128,
+    RoPE on 64 dims): causal prefill of 32768 tokens (bf16 in, bf16 out) against
+    the bf16 MFMA peak (algorithmic FLOPs 2 * Hq * L^2 * d, the causal half of
+    the two products), and a decode step of 16 sequences over 32768 cached tokens
+    each against HBM (algorithmic bytes: the K and V cache rows read, 0..n)."""
+    import workloads
+
+    wl = workloads.SOFTMAX_PREFILL
+    B, L, Hq, Hkv = wl.batch, wl.seqlen, wl.heads, wl.extra["kv_heads"]
+    R, base = wl.extra["rope_dims"], wl.extra["rope_base"]
+    q, k, v = workloads.softmax_qkv_device(wl.seed, B, L, Hq, Hkv)
+    o = torch.empty((B, L, Hq, D), device="cuda", dtype=torch.bfloat16)
+    kr = torch.empty_like(k)
+    stream = torch.cuda.current_stream()
+    call = lambda: la.lt_softmax_prefill(q, k, v, rope_dims=R, rope_base=base, o=o, k_rope=kr, stream=stream)
+    ms, _ = _event_times(torch, call, steps, warmup, stream)
+    assert bool(torch.isfinite(o[0, -1]).all()), "non-finite softmax output"
+    flops = 2.0 * B * Hq * L * L * D
+    tfs = flops / (ms / 1e3) / 1e12
+    pre = {"workload": f"{wl.name}: [{B}, {L}] x {Hq} query / {Hkv} K/V heads x {D}, rope {R}",
+           "tokens_per_s": round(B * L / (ms / 1e3), 1), "call_ms_mean": round(ms, 4),
+           "roofline": {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS,
+                        "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "flops_per_launch": flops,
+                        "kernel": "lt_softmax_prefill call: rope_rows_kernel + fa_prefill_kernel<bf16>"}}
+    del q, k, v, o, kr
+    wd = workloads.SOFTMAX_DECODE
+    Bd, ctx = wd.batch, wd.extra["context"]
+    cap = ctx + 1024
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wd.seed)
+    rnd = lambda *sh: torch.randn(sh, generator=g, device="cuda").to(torch.bfloat16)
+    dq, kn, vn = rnd(Bd, Hq, D), rnd(Bd, Hkv, D), rnd(Bd, Hkv, D)
+    kc, vc = rnd(Bd, cap, Hkv, D), rnd(Bd, cap, Hkv, D)
+    lens = torch.full((Bd,), ctx, dtype=torch.int32, device="cuda")
+    do = torch.empty((Bd, Hq, D), device="cuda", dtype=torch.bfloat16)
+    ws = torch.empty(max(la.lt_softmax_decode_workspace_bytes(Bd, cap, Hq, Hkv), 1), dtype=torch.uint8,
+                     device="cuda")
+    dcall = lambda: la.lt_softmax_decode(dq, kn, vn, kc, vc, lens, rope_dims=R, rope_base=base, o=do,
+                                         workspace=ws, stream=stream)
+    dms, dmed = _event_times(torch, dcall, decode_steps, 5, stream)
+    nbytes = Bd * (ctx + 1) * Hkv * D * 2 * 2
+    gbs = nbytes / (dms / 1e3) / 1e9
+    dec = {"workload": f"{wd.name}: {Bd} sequences x {ctx} cached tokens, {Hq} / {Hkv} heads, bf16 cache",
+           "ms_per_step_mean": round(dms, 5), "ms_per_step_median": round(dmed, 5),
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes,
+                        "kernel": "lt_softmax_decode call: rope_append + fd_kernel + fd_combine"}}
+    return {"prefill": pre, "decode": dec}
 
 
 def run_decode(la, torch, nsteps, warmup=5, norm_gate=False, slots=0):
@@ -461,6 +536,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-norm-gate", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-softmax", action="store_true")
     ap.add_argument("--norm-gate-decode-steps", type=int, default=200)
     ap.add_argument("--workload", default="m1_layer",
                     choices=["m1_layer", "long_1m", "varlen", "tiny_f32"])
@@ -519,6 +595,12 @@ def main():
             log(f"[bench] backward batch={b_} L={l_} H=64")
             bwd[f"b{b_}_L{l_}"] = run_backward(la, torch, 10, 2, b_, l_)
             log(f"[bench] backward {bwd[f'b{b_}_L{l_}']['kernel_ms_mean']:.3f} ms/call")
+    smx = None
+    if not args.no_softmax:
+        log("[bench] softmax layer: prefill L=32768 64/8 heads, decode 16 x 32768")
+        smx = run_softmax(la, torch, 5, 1, 100)
+        log(f"[bench] softmax prefill {smx['prefill']['call_ms_mean']:.3f} ms, decode "
+            f"{smx['decode']['ms_per_step_median'] * 1e3:.1f} us")
     cpu = None
     if not args.no_cpu:
         log(f"[bench] cpu oracle on {args.cpu_tokens} tokens")
@@ -545,6 +627,7 @@ def main():
         "decode": dec,
         "norm_gate": ng,
         "backward": bwd,
+        "softmax": smx,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
