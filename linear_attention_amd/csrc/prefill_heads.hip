@@ -112,6 +112,7 @@ __global__ __launch_bounds__(NT, 4) void piece_state_kernel(PrefillArgs a, Segme
     const uint16_t *kg = static_cast<const uint16_t *>(a.k) + base;
     const uint16_t *vg = static_cast<const uint16_t *>(a.v) + base;
     const float s2 = a.slopes[h] * LOG2E;
+    if (fix_head(s2, sp.seg_len, sp.fix_osz)) return;  // local-start segments: no pre-pass
     float *u = sp.unit(ws, uh);
 
     f32x16 S[2];
@@ -215,8 +216,12 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
     auto sidx = [&](int db, int v) {
         return (64 * qh + 32 * db + 8 * (v >> 2) + 4 * hf + (v & 3)) * D + 32 * cq + r32;
     };
-    const float *s_in = segments > 1 ? sp.start_state(sp.unit(ws, uh), g)
-                                     : (a.state_in ? a.state_in + (size_t)uh * D * D : nullptr);
+    // local-start segments: segment 0 starts from S_0, the others from zero
+    // (the correction pass adds their carried-in term afterwards)
+    const bool fix = segments > 1 && fix_head(s2, seg_len, sp.fix_osz);
+    const float *s_in = segments > 1 && !fix
+                            ? sp.start_state(sp.unit(ws, uh), g)
+                            : ((segments == 1 || g == 0) && a.state_in ? a.state_in + (size_t)uh * D * D : nullptr);
     if (s_in && segments == 1 && a.state_in_t) {
         // S_0 given transposed: element (r, c) at c * D + r
 #pragma unroll
@@ -353,7 +358,13 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
             step(nfull, tail, std::false_type{}, st0);
     }
 
-    if (a.state_out && g == segments - 1) {
+    if (fix) {  // end state of this local-start segment, for the correction pass
+        float *dst = sp.start_state(sp.unit(ws, uh), g);
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) dst[sidx(db, v)] = S[db][v];
+    } else if (a.state_out && g == segments - 1) {
         const long long sb = (long long)uh * D * D;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
@@ -590,6 +601,128 @@ __global__ __launch_bounds__(NT) void slice_kernel(PrefillArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Local-start segments (heads with fix_head): after the main kernel, the true
+// start state of every segment g >= 1 (into boundary slot B_g) and the final
+// state, from the end states E_g the main kernel left in slots S_g (segment 0
+// started from S_0, the others from zero):
+//   S_in(1) = E_0,   S_in(g+1) = e^{-s len_g} S_in(g) + E_g,
+//   S_final = e^{-s len_{G-1}} S_in(G-1) + E_{G-1}.
+__global__ __launch_bounds__(kCombineThreads) void fix_combine_kernel(PrefillArgs a, Segmented sp, float *ws) {
+    const int uh = blockIdx.x / kCombineSlices;
+    const int e = 4 * ((blockIdx.x % kCombineSlices) * kCombineThreads + threadIdx.x);
+    const float s2 = a.slopes[uh % a.heads] * LOG2E;
+    if (!fix_head(s2, sp.seg_len, sp.fix_osz)) return;
+    float *u = sp.unit(ws, uh);
+    float4 acc = *reinterpret_cast<const float4 *>(sp.start_state(u, 0) + e);
+    for (int g = 1; g < sp.segments; ++g) {
+        *reinterpret_cast<float4 *>(sp.partial(u, g) + e) = acc;
+        const long long rest = a.seqlen - (long long)g * sp.seg_len;
+        const float f = fast_exp2(-s2 * (float)(rest < sp.seg_len ? rest : sp.seg_len));
+        const float4 p = *reinterpret_cast<const float4 *>(sp.start_state(u, g) + e);
+        acc = make_float4(f * acc.x + p.x, f * acc.y + p.y, f * acc.z + p.z, f * acc.w + p.w);
+    }
+    if (a.state_out) *reinterpret_cast<float4 *>(a.state_out + (size_t)uh * D * D + e) = acc;
+}
+
+// o[t] += e^{-s(t+1)} q[t] S_in(g) for the first fix_len tokens t of segment g
+// (g >= 1), 64-token chunks; kFixParts workgroups per (unit, head, segment)
+// take every kFixParts-th chunk. The product is the main kernel's inter-block
+// one (S^T in bf16 on MFMA, Q from an LDS tile).
+constexpr int kFixParts = 8;
+
+__device__ __forceinline__ void add_rows(float *out, long long ts, const float *Os, int m, int tid) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = (tid >> 5) + 16 * j, col = 4 * (tid & 31);
+        if (row < m) {
+            const float4 x = *reinterpret_cast<const float4 *>(Os + ooff(row, col));
+            float4 *dst = reinterpret_cast<float4 *>(out + row * ts + col);
+            const float4 y = *dst;
+            *dst = make_float4(y.x + x.x, y.y + x.y, y.z + x.z, y.w + x.w);
+        }
+    }
+}
+__device__ __forceinline__ void add_rows(__bf16 *out, long long ts, const float *Os, int m, int tid) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int row = (tid >> 4) + 32 * j, col = 8 * (tid & 15);
+        if (row < m) {
+            const float4 x0 = *reinterpret_cast<const float4 *>(Os + ooff(row, col));
+            const float4 x1 = *reinterpret_cast<const float4 *>(Os + ooff(row, col + 4));
+            bf16x8 *dst = reinterpret_cast<bf16x8 *>(out + row * ts + col);
+            const bf16x8 y = *dst;
+            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            bf16x8 r;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) r[i] = static_cast<__bf16>(static_cast<float>(y[i]) + xs[i]);
+            *dst = r;
+        }
+    }
+}
+
+template <typename OutT>
+__global__ __launch_bounds__(NT) void fix_kernel(PrefillArgs a, Segmented sp, float *ws) {
+    __shared__ __attribute__((aligned(16))) __bf16 Sts[D * D];
+    __shared__ __attribute__((aligned(16))) __bf16 Qs[C * D];
+    __shared__ __attribute__((aligned(16))) float Os[C * D];
+
+    const int part = blockIdx.x % kFixParts;
+    const int gi = blockIdx.x / kFixParts;
+    const int g = 1 + gi % (sp.segments - 1);
+    const int uh = gi / (sp.segments - 1);
+    const int h = uh % a.heads, n = uh / a.heads;
+    const float s2 = a.slopes[h] * LOG2E;
+    if (!fix_head(s2, sp.seg_len, sp.fix_osz)) return;
+    const long long seg0 = (long long)g * sp.seg_len;
+    const long long len = a.seqlen - seg0 < sp.seg_len ? a.seqlen - seg0 : sp.seg_len;
+    const long long T = fix_len(s2, sp.seg_len) < len ? fix_len(s2, sp.seg_len) : len;
+    const long long nch = (T + C - 1) / C;
+    if (part >= nch) return;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qh = w >> 2, cq = w & 3, r32 = lane & 31, hf = lane >> 5;
+    {
+        const float *si = sp.partial(sp.unit(ws, uh), g);
+        f32x16 S[2];
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                S[db][v] = si[(64 * qh + 32 * db + 8 * (v >> 2) + 4 * hf + (v & 3)) * D + 32 * cq + r32];
+        write_state_t(Sts, S, qh, cq, lane);
+    }
+    const int ts = a.heads * D;
+    const long long base = (((long long)n * a.seqlen + seg0) * a.heads + h) * (long long)D;
+    const uint16_t *qg = static_cast<const uint16_t *>(a.q) + base;
+    OutT *og = static_cast<OutT *>(a.o) + base;
+    const int seg = tid & 15;
+    for (long long c = part; c < nch; c += kFixParts) {
+        const int m = (int)(T - c * C < C ? T - c * C : C);
+        // q rows of this chunk (rows past m read row m-1 and are zeroed); the
+        // previous chunk's reads of Qs and Os ended before its last barrier
+        // for the MFMA reads, and before this chunk's first barrier for Os
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int t = (tid >> 4) + 32 * i;
+            const uint4 x = stream_load16(qg + (c * C + (t < m ? t : m - 1)) * (long long)ts + 8 * seg);
+            *reinterpret_cast<uint4 *>(Qs + L128::off(t, 8 * seg)) = keep_if(t < m, x);
+        }
+        __syncthreads();  // Q tile (and S^T) visible; Os free
+        f32x16 o;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[v] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            o = mma(ld_op<L128>(Sts, 32 * cq, 16 * ks, lane), ld_op<L128>(Qs, 32 * qh, 16 * ks, lane), o);
+        o *= fast_exp2(-s2 * (float)(c * C + 32 * qh + r32 + 1));
+        stage_out(Os, o, qh, cq, lane);
+        __syncthreads();  // Os visible; every read of Qs done
+        add_rows(og + c * C * (long long)ts, ts, Os, m, tid);
+    }
+}
+
 template <typename OutT>
 hipError_t launch(const PrefillArgs &a, const PrefillPlan &p, void *workspace, hipStream_t stream) {
     clear_pending_error();
@@ -601,7 +734,10 @@ hipError_t launch(const PrefillArgs &a, const PrefillPlan &p, void *workspace, h
         return hipGetLastError();
     }
     float *ws = static_cast<float *>(workspace);
-    const Segmented sp{p.segments, p.pieces, p.seg_len, p.piece_len};
+    // heads may take local-start segments unless the epilogue needs the whole
+    // output (norm-gate) or S_0 comes transposed (the backward's dq pass)
+    const int fix_osz = p.segments > 1 && !a.ng.gate && !a.state_in_t ? (int)sizeof(OutT) : 0;
+    const Segmented sp{p.segments, p.pieces, p.seg_len, p.piece_len, fix_osz};
     if (p.segments > 1) {
         hipLaunchKernelGGL(piece_state_kernel, dim3((unsigned)(uh * p.pieces)), dim3(NT), 0, stream,
                            a, sp, ws);
@@ -618,6 +754,15 @@ hipError_t launch(const PrefillArgs &a, const PrefillPlan &p, void *workspace, h
     else
         hipLaunchKernelGGL((head_kernel<OutT, false>), dim3((unsigned)(uh * p.segments)), dim3(NT), 0,
                            stream, a, sp, ws);
+    if (!fix_osz) return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fix_combine_kernel, dim3((unsigned)(uh * kCombineSlices)), dim3(kCombineThreads), 0, stream,
+                       a, sp, ws);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((fix_kernel<OutT>), dim3((unsigned)(uh * (p.segments - 1) * kFixParts)), dim3(NT), 0, stream,
+                       a, sp, ws);
     return hipGetLastError();
 }
 

@@ -282,9 +282,29 @@ __device__ __forceinline__ SeqRange sequence_of(const PrefillArgs &a, int n) {
 //   [S_0 .. S_{segments-1}]     state at the start of each segment
 // A state of tokens [t0, t1) from zero is sum_t e^{-s(t1-1-t)} k_t^T v_t, and
 // states compose as S(t2) = e^{-s(t2-t1)} S(t1) + state of [t1, t2).
+// Local-start segments. A segment that starts from a zero state instead of
+// its true start state S_in misses, at its token t (t = 0, 1, ...), the term
+// e^{-s(t+1)} q_t S_in. With s2 = s log2(e) that factor is below 2^-kFixExp once
+// t + 1 > kFixExp / s2: a correction pass adds the term to the first
+// fix_len = min(segment, kFixExp / s2) tokens and leaves the rest (2^-32 of the
+// term's own scale is below fp32 resolution of the output). A head takes this
+// route when re-reading q and o for fix_len tokens costs less HBM traffic than
+// the pre-pass re-read of the whole segment's k and v:
+//   fix_len (256 + 256 osz) <= 512 seg_len    (osz: bytes per output element;
+// q read once, o read and written).
+constexpr float kFixExp = 32.f;
+__device__ __forceinline__ long long fix_len(float s2, long long seg_len) {
+    const float t = kFixExp / s2;
+    return t >= (float)seg_len ? seg_len : (long long)t;
+}
+__device__ __forceinline__ bool fix_head(float s2, long long seg_len, int osz) {
+    return osz > 0 && s2 > 0.f && fix_len(s2, seg_len) * (1 + osz) <= 2 * seg_len;
+}
+
 struct Segmented {
     int segments, pieces;
     long long seg_len, piece_len;
+    int fix_osz = 0;  // output element size when heads may take local-start segments, else 0
     __device__ long long covered() const { return (segments - 1) * seg_len; }
     __device__ float *unit(float *ws, int uh) const {
         return ws + (size_t)uh * (size_t)(pieces + 2 * segments - 1) * D * D;
@@ -313,6 +333,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float *s
     const int e = 4 * ((blockIdx.x % kCombineSlices) * kCombineThreads + threadIdx.x);
     const int h = uh % heads;
     const float s2 = slopes[h] * LOG2E;
+    if (fix_head(s2, sp.seg_len, sp.fix_osz)) return;  // local-start segments: no pre-pass states
     float *u = sp.unit(ws, uh);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (s0) {

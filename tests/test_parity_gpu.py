@@ -383,3 +383,31 @@ def test_decode_batches_with_strided_order(la, B):
     eo = max(rel_l2(og[b, h], o_ref[b, h]) for b in range(B) for h in range(H))
     es = max_rel_states(to_host_f32(state), s_ref)
     assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_prefill_segmented_slope_mix(la, out_dtype):
+    """Segmented plan over heads whose decay sends them down both routes: heads
+    with a short memory start every segment from zero and get the carried-in
+    term added to their first tokens afterwards (slopes 0.2, 1, 30; 30 needs no
+    correction at all), heads with a long one (0, 1e-6, 0.02) take the pre-pass;
+    with a carried-in state updated in place."""
+    import torch
+
+    L, H = 9000, 6
+    sl = np.array([0.0, 1e-6, 0.02, 0.2, 1.0, 30.0], np.float32)
+    print(f"[case] segmented slope mix L={L} slopes={list(sl)} out={out_dtype}", flush=True)
+    assert la.lt_prefill_workspace_bytes(1, L, H) > 0
+    q, k, v = workloads.qkv_host(2301, (1, L, H, 128), "bf16")
+    s0 = workloads.state_host(2302, (1, H, 128, 128))
+    st = torch.from_numpy(s0).cuda()
+    od = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    o, _ = la.lt_prefill(*(to_device(x, "bf16") for x in (q, k, v)), torch.from_numpy(sl).cuda(), 256,
+                         st, state_out=st, out_dtype=od)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.recurrence_batch(q, k, v, sl, s0=s0)
+    o_g = to_host_f32(o)
+    eo = max(rel_l2(o_g[0, :, h], o_ref[0, :, h]) for h in range(H))
+    es = max_rel_states(to_host_f32(st), s_ref)
+    print(f"[result] o {eo:.3e} state {es:.3e}", flush=True)
+    assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)
