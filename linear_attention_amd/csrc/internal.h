@@ -93,8 +93,9 @@ constexpr long long prefill_states(int segments, int pieces) { return pieces + 2
 // an error some earlier call (the caller's, say) left behind.
 inline void clear_pending_error() { (void)hipGetLastError(); }
 
+// prepass_wgs: pre-pass workgroups to aim for (sets the piece length).
 PrefillPlan plan_prefill(long long units, long long seqlen, int heads, lt_dtype in_dtype,
-                         bool varlen);
+                         bool varlen, long long prepass_wgs = 512);
 
 // Backward of a fixed-length bf16 prefill (gradients of
 // l = sum dout . o + <d_state_out, S_final>): dk, dv and d_state_in from one

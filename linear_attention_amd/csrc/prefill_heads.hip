@@ -629,37 +629,60 @@ __global__ __launch_bounds__(kCombineThreads) void fix_combine_kernel(PrefillArg
 // (g >= 1), 64-token chunks; kFixParts workgroups per (unit, head, segment)
 // take every kFixParts-th chunk. The product is the main kernel's inter-block
 // one (S^T in bf16 on MFMA, Q from an LDS tile).
-constexpr int kFixParts = 8;
+constexpr int kFixParts = 12;
 
-__device__ __forceinline__ void add_rows(float *out, long long ts, const float *Os, int m, int tid) {
+// The rows of o a thread adds to (loaded before the product, so their latency
+// overlaps it): fp32 rows (t/32) + 16j, 4 columns at 4(t%32); bf16 rows
+// (t/16) + 32j, 8 columns at 8(t%16). Rows >= m read row m-1 and are not stored.
+struct OutRows {
+    uint4 y[4];
+    __device__ void load(const float *out, long long ts, int m, int tid) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int row = (tid >> 5) + 16 * j, col = 4 * (tid & 31);
-        if (row < m) {
-            const float4 x = *reinterpret_cast<const float4 *>(Os + ooff(row, col));
-            float4 *dst = reinterpret_cast<float4 *>(out + row * ts + col);
-            const float4 y = *dst;
-            *dst = make_float4(y.x + x.x, y.y + x.y, y.z + x.z, y.w + x.w);
+        for (int j = 0; j < 4; ++j) {
+            const int row = (tid >> 5) + 16 * j;
+            y[j] = *reinterpret_cast<const uint4 *>(out + (row < m ? row : m - 1) * ts + 4 * (tid & 31));
         }
     }
-}
-__device__ __forceinline__ void add_rows(__bf16 *out, long long ts, const float *Os, int m, int tid) {
+    __device__ void load(const __bf16 *out, long long ts, int m, int tid) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int row = (tid >> 4) + 32 * j, col = 8 * (tid & 15);
-        if (row < m) {
+        for (int j = 0; j < 2; ++j) {
+            const int row = (tid >> 4) + 32 * j;
+            y[j] = *reinterpret_cast<const uint4 *>(out + (row < m ? row : m - 1) * ts + 8 * (tid & 15));
+        }
+    }
+    __device__ void add_store(float *out, long long ts, const float *Os, int m, int tid) const {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = (tid >> 5) + 16 * j, col = 4 * (tid & 31);
+            const float4 x = *reinterpret_cast<const float4 *>(Os + ooff(row, col));
+            if (row < m)
+                *reinterpret_cast<float4 *>(out + row * ts + col) =
+                    make_float4(__uint_as_float(y[j].x) + x.x, __uint_as_float(y[j].y) + x.y,
+                                __uint_as_float(y[j].z) + x.z, __uint_as_float(y[j].w) + x.w);
+        }
+    }
+    __device__ void add_store(__bf16 *out, long long ts, const float *Os, int m, int tid) const {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int row = (tid >> 4) + 32 * j, col = 8 * (tid & 15);
             const float4 x0 = *reinterpret_cast<const float4 *>(Os + ooff(row, col));
             const float4 x1 = *reinterpret_cast<const float4 *>(Os + ooff(row, col + 4));
-            bf16x8 *dst = reinterpret_cast<bf16x8 *>(out + row * ts + col);
-            const bf16x8 y = *dst;
             const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-            bf16x8 r;
+            const uint32_t w[4] = {y[j].x, y[j].y, y[j].z, y[j].w};
+            uint32_t r[4];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) r[i] = static_cast<__bf16>(static_cast<float>(y[i]) + xs[i]);
-            *dst = r;
+            for (int i = 0; i < 4; ++i) {
+                const __bf16 lo = static_cast<__bf16>(__uint_as_float(w[i] << 16) + xs[2 * i]);
+                const __bf16 hi = static_cast<__bf16>(__uint_as_float(w[i] & 0xffff0000u) + xs[2 * i + 1]);
+                uint16_t ulo, uhi;
+                __builtin_memcpy(&ulo, &lo, 2);
+                __builtin_memcpy(&uhi, &hi, 2);
+                r[i] = (uint32_t)ulo | ((uint32_t)uhi << 16);
+            }
+            if (row < m) *reinterpret_cast<uint4 *>(out + row * ts + col) = make_uint4(r[0], r[1], r[2], r[3]);
         }
     }
-}
+};
 
 template <typename OutT>
 __global__ __launch_bounds__(NT) void fix_kernel(PrefillArgs a, Segmented sp, float *ws) {
@@ -703,11 +726,19 @@ __global__ __launch_bounds__(NT) void fix_kernel(PrefillArgs a, Segmented sp, fl
         // q rows of this chunk (rows past m read row m-1 and are zeroed); the
         // previous chunk's reads of Qs and Os ended before its last barrier
         // for the MFMA reads, and before this chunk's first barrier for Os
+        OutT *oc = og + c * C * (long long)ts;
+        uint4 qx[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int t = (tid >> 4) + 32 * i;
-            const uint4 x = stream_load16(qg + (c * C + (t < m ? t : m - 1)) * (long long)ts + 8 * seg);
-            *reinterpret_cast<uint4 *>(Qs + L128::off(t, 8 * seg)) = keep_if(t < m, x);
+            qx[i] = stream_load16(qg + (c * C + (t < m ? t : m - 1)) * (long long)ts + 8 * seg);
+        }
+        OutRows rows;
+        rows.load(oc, ts, m, tid);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int t = (tid >> 4) + 32 * i;
+            *reinterpret_cast<uint4 *>(Qs + L128::off(t, 8 * seg)) = keep_if(t < m, qx[i]);
         }
         __syncthreads();  // Q tile (and S^T) visible; Os free
         f32x16 o;
@@ -719,7 +750,7 @@ __global__ __launch_bounds__(NT) void fix_kernel(PrefillArgs a, Segmented sp, fl
         o *= fast_exp2(-s2 * (float)(c * C + 32 * qh + r32 + 1));
         stage_out(Os, o, qh, cq, lane);
         __syncthreads();  // Os visible; every read of Qs done
-        add_rows(og + c * C * (long long)ts, ts, Os, m, tid);
+        rows.add_store(oc, ts, Os, m, tid);
     }
 }
 

@@ -347,22 +347,34 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float *s
     }
     *reinterpret_cast<float4 *>(sp.start_state(u, 0) + e) = acc;
     const long long covered = sp.covered();
-    for (int j = 0; j < sp.pieces; ++j) {
-        const long long t0 = j * sp.piece_len;
-        const long long t1 = t0 + sp.piece_len < covered ? t0 + sp.piece_len : covered;
-        const int gb = (int)(t0 / sp.seg_len) + 1;
-        const long long b = gb * sp.seg_len;
-        if (b < t1) {
-            const float f = fast_exp2(-s2 * (float)(b - t0));
-            const float4 p = *reinterpret_cast<const float4 *>(sp.partial(u, gb) + e);
-            *reinterpret_cast<float4 *>(sp.start_state(u, gb) + e) =
-                make_float4(f * acc.x + p.x, f * acc.y + p.y, f * acc.z + p.z, f * acc.w + p.w);
+    // the piece states are independent loads: issue a batch of them ahead of
+    // the sequential accumulation (this kernel never writes piece slots)
+    constexpr int kBatch = 8;
+    for (int j0 = 0; j0 < sp.pieces; j0 += kBatch) {
+        float4 pj[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+            if (j0 + i < sp.pieces) pj[i] = *reinterpret_cast<const float4 *>(sp.piece_state(u, j0 + i) + e);
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            const int j = j0 + i;
+            if (j >= sp.pieces) break;
+            const long long t0 = j * sp.piece_len;
+            const long long t1 = t0 + sp.piece_len < covered ? t0 + sp.piece_len : covered;
+            const int gb = (int)(t0 / sp.seg_len) + 1;
+            const long long b = gb * sp.seg_len;
+            if (b < t1) {
+                const float f = fast_exp2(-s2 * (float)(b - t0));
+                const float4 p = *reinterpret_cast<const float4 *>(sp.partial(u, gb) + e);
+                *reinterpret_cast<float4 *>(sp.start_state(u, gb) + e) =
+                    make_float4(f * acc.x + p.x, f * acc.y + p.y, f * acc.z + p.z, f * acc.w + p.w);
+            }
+            const float f = fast_exp2(-s2 * (float)(t1 - t0));
+            const float4 p = pj[i];
+            acc = make_float4(f * acc.x + p.x, f * acc.y + p.y, f * acc.z + p.z, f * acc.w + p.w);
+            if (t1 % sp.seg_len == 0)
+                *reinterpret_cast<float4 *>(sp.start_state(u, (int)(t1 / sp.seg_len)) + e) = acc;
         }
-        const float f = fast_exp2(-s2 * (float)(t1 - t0));
-        const float4 p = *reinterpret_cast<const float4 *>(sp.piece_state(u, j) + e);
-        acc = make_float4(f * acc.x + p.x, f * acc.y + p.y, f * acc.z + p.z, f * acc.w + p.w);
-        if (t1 % sp.seg_len == 0)
-            *reinterpret_cast<float4 *>(sp.start_state(u, (int)(t1 / sp.seg_len)) + e) = acc;
     }
 }
 
