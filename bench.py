@@ -52,7 +52,10 @@ METRIC = "Lightning prefill tokens/s (H=64,d=128) + decode state GB/s, % of roof
 HBM_PEAK_GBS = 8000.0
 D = 128
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_m1_layer_L32768_traffic.json")
-PREFILL_SRC = os.path.join(ROOT, "linear_attention_amd", "csrc", "prefill_heads.hip")
+# the prefill kernels and their launch plan: the committed traffic summary is
+# valid while these sources are unchanged
+PREFILL_SRCS = [os.path.join(ROOT, "linear_attention_amd", "csrc", f)
+                for f in ("prefill_heads.hip", "tiles.h", "lightning_api.cpp")]
 
 
 def log(msg):
@@ -70,9 +73,12 @@ def decode_bytes(batch, heads, in_bytes=2, out_bytes=4):
     return batch * heads * (2 * D * D * 4 + 3 * D * in_bytes + D * out_bytes)
 
 
-def source_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def committed_traffic(bytes_alg):
@@ -83,7 +89,7 @@ def committed_traffic(bytes_alg):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256") != source_sha(PREFILL_SRC):
+    if t.get("kernel_source_sha256") != source_sha(PREFILL_SRCS):
         return None
     return t.get("traffic_bytes_per_launch")
 
@@ -132,7 +138,8 @@ def run_prefill(la, torch, steps, warmup):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "bytes_per_launch": bytes_alg,
-                     "kernel": "lt_prefill call: piece_state_kernel + combine_kernel + head_kernel<float>"},
+                     "kernel": "lt_prefill call: piece_state_kernel + combine_kernel + head_kernel<float> "
+                               "+ fix_combine_kernel + fix_kernel<float>"},
     }
 
 
@@ -484,15 +491,16 @@ def traffic_from(copy_dir, fetch_dir, write_dir, copy_bytes):
     w_scale = copy_bytes / (copy_write_kib * 1024)
     kf = per_kernel(fetch_dir, "FETCH_SIZE")
     kw = per_kernel(write_dir, "WRITE_SIZE")
-    # the plain call's kernels (the fused norm-gate call shares the pre-pass and
-    # combine, whose work is the same, but has its own main kernel)
+    # the plain call's kernels (the counter runs time only plain lt_prefill
+    # calls: the norm-gate call and the backward's dq pass plan their pre-pass
+    # differently)
     kernels = [k for k in kf if any(n in k for n in ("head_kernel<float, false>", "piece_state_kernel",
-                                                      "combine_kernel"))]
+                                                      "combine_kernel", "fix_kernel<float>"))]
     import numpy as np
 
     fetch = sum(float(np.median(kf[k])) for k in kernels) * 1024 * f_scale
     write = sum(float(np.median(kw[k])) for k in kernels) * 1024 * w_scale
-    out = {"kernel_source_sha256": source_sha(PREFILL_SRC),
+    out = {"kernel_source_sha256": source_sha(PREFILL_SRCS),
            "kernels": kernels, "fetch_scale": f_scale, "write_scale": w_scale,
            "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
            "traffic_bytes_per_launch": round(fetch + write),
