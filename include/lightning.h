@@ -18,7 +18,9 @@
  * "⊙" with a length-B vector scales token rows. The value of O and of the final
  * state does not depend on B: the block form is an exact re-association of the
  * per-token recurrence S <- e^{-s_h} S + k^T v, o = q S (the token sees its own
- * key). lt_prefill, lt_prefill_varlen and lt_decode write the raw sum; the
+ * key). The kernels may leave out a carried-state term once its decay factor
+ * e^{-s t} is below 2^-32 (far below fp32 resolution of the output).
+ * lt_prefill, lt_prefill_varlen and lt_decode write the raw sum; the
  * *_norm_gate variants also apply the normalisation and gate that follow the
  * sum in the §03 data-flow figure before anything is stored.
  *
