@@ -53,9 +53,10 @@ constexpr long long kMinSegment = 2048;
 // Pre-pass workgroups to aim for: two per CU is what its registers allow, so
 // the whole pre-pass grid is resident at once.
 constexpr long long kPrepassWorkgroups = 512;
-// Pre-pass workgroups when heads may take local-start segments (plain
-// prefill): the heads with a short memory skip the pre-pass, and the few that
-// remain (7 of 64 in the M1 layer's slope schedule) get more, shorter pieces.
+// Pre-pass workgroups when heads may take local-start segments (every call but
+// the norm-gate ones): the heads with a short memory skip the pre-pass, and the
+// few that remain (7 of 64 in the M1 layer's slope schedule) get more, shorter
+// pieces.
 // Measured on the M1 layer: 512 -> 661 us, 1024 -> 643 us, 2048 -> 608 us.
 constexpr long long kPrepassWide = 2048;
 // Shortest pre-pass piece.
@@ -69,7 +70,7 @@ lt_status launch(const lt::PrefillArgs &a, int in_dtype, int out_dtype, bool var
     const bool whole_rows = a.ng.gate || a.state_in_t;  // epilogue or transposed S_0
     lt::PrefillPlan p = lt::plan_prefill(a.units, varlen ? a.total_tokens : a.seqlen, a.heads,
                                          (lt_dtype)in_dtype, varlen,
-                                         whole_rows ? kPrepassWorkgroups : kPrepassWide);
+                                         a.ng.gate ? kPrepassWorkgroups : kPrepassWide);
     // Without the workspace the segmented plan needs, split value columns instead;
     // the norm-gate epilogue needs whole output rows, so it keeps one workgroup
     // per (sequence, head) rather than value slices.

@@ -211,7 +211,9 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
         *reinterpret_cast<float4 *>(Wn + 4 * tid) = *reinterpret_cast<const float4 *>(a.ng.norm_weight + h * D + 4 * tid);
 
     // ---- carried-in state of this segment (the combine pass wrote it for
-    // segmented plans, so an in-place state update never races with it)
+    // segmented plans; on local-start segments segment 0 reads S_0 itself and
+    // the final state is written by a later kernel; either way an in-place
+    // state update never races with this read)
     f32x16 S[2];
     auto sidx = [&](int db, int v) {
         return (64 * qh + 32 * db + 8 * (v >> 2) + 4 * hf + (v & 3)) * D + 32 * cq + r32;
@@ -222,7 +224,7 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
     const float *s_in = segments > 1 && !fix
                             ? sp.start_state(sp.unit(ws, uh), g)
                             : ((segments == 1 || g == 0) && a.state_in ? a.state_in + (size_t)uh * D * D : nullptr);
-    if (s_in && segments == 1 && a.state_in_t) {
+    if (s_in && (segments == 1 || fix) && a.state_in_t) {
         // S_0 given transposed: element (r, c) at c * D + r
 #pragma unroll
         for (int db = 0; db < 2; ++db)
@@ -766,8 +768,8 @@ hipError_t launch(const PrefillArgs &a, const PrefillPlan &p, void *workspace, h
     }
     float *ws = static_cast<float *>(workspace);
     // heads may take local-start segments unless the epilogue needs the whole
-    // output (norm-gate) or S_0 comes transposed (the backward's dq pass)
-    const int fix_osz = p.segments > 1 && !a.ng.gate && !a.state_in_t ? (int)sizeof(OutT) : 0;
+    // output (norm-gate)
+    const int fix_osz = p.segments > 1 && !a.ng.gate ? (int)sizeof(OutT) : 0;
     const Segmented sp{p.segments, p.pieces, p.seg_len, p.piece_len, fix_osz};
     if (p.segments > 1) {
         hipLaunchKernelGGL(piece_state_kernel, dim3((unsigned)(uh * p.pieces)), dim3(NT), 0, stream,
