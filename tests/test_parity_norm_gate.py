@@ -176,3 +176,34 @@ def test_decode_norm_gate_bf16_output(la):
     y_ref = oracle.norm_gate(o_ref, gate, w, EPS)
     yg = to_host_f32(y)
     assert max(rel_l2(yg[b, h], y_ref[b, h]) for b in range(B) for h in range(H)) <= TOL_BF16
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_prefill_norm_gate_segmented_slope_mix(la, out_dtype):
+    """Norm-gate prefill over heads on both routes of the segmented plan: the
+    short-memory heads (slopes 0.2, 1, 30) start every segment from zero, leave
+    the raw output of their first rows for the correction pass, which adds the
+    carried-in term and applies the normalisation and gate; the others (0,
+    1e-6, 0.02) take the pre-pass. Carried-in state updated in place."""
+    import torch
+
+    L, H = 9000, 6
+    sl = np.array([0.0, 1e-6, 0.02, 0.2, 1.0, 30.0], np.float32)
+    print(f"[case] norm-gate segmented slope mix L={L} slopes={list(sl)} out={out_dtype}", flush=True)
+    q, k, v = workloads.qkv_host(2401, (1, L, H, 128), "bf16")
+    gate = workloads.gate_host(2402, (1, L, H, 128), "bf16")
+    w = workloads.norm_weight_host(2403, H)
+    s0 = workloads.state_host(2404, (1, H, 128, 128))
+    st = torch.from_numpy(s0).cuda()
+    od = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    y, _ = la.lt_prefill_norm_gate(to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16"),
+                                   torch.from_numpy(sl).cuda(), to_device(gate, "bf16"),
+                                   torch.from_numpy(w).cuda(), EPS, 256, st, state_out=st, out_dtype=od)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.recurrence_batch(q, k, v, sl, s0=s0)
+    y_ref = oracle.norm_gate(o_ref, gate, w, EPS)
+    yg = to_host_f32(y)
+    ey = max(rel_l2(yg[0, :, h], y_ref[0, :, h]) for h in range(H))
+    es = max_rel_states(to_host_f32(st), s_ref)
+    print(f"[result] y {ey:.3e} state {es:.3e}", flush=True)
+    assert ey <= TOL_BF16 and es <= TOL_BF16, (ey, es)
