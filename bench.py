@@ -301,6 +301,59 @@ def run_softmax(la, torch, steps, warmup, decode_steps):
     return {"prefill": pre, "decode": dec}
 
 
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+
+        return max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # noqa: BLE001 - the count is informational
+        return None
+
+
+def run_softmax_cpu_baseline(la, torch, min_seconds=5.0):
+    """The fp64 softmax oracle on the host, beside the GPU softmax rows: query
+    rows of the same 32768-token layer spread evenly over [0, L) (so their mean
+    cost is that of an average row), and decode steps of single sequences over
+    the same 32768-token context. Reported baseline, not a target."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    wl = workloads.SOFTMAX_PREFILL
+    B, L, Hq, Hkv = wl.batch, wl.seqlen, wl.heads, wl.extra["kv_heads"]
+    R, base = wl.extra["rope_dims"], wl.extra["rope_base"]
+    q, k, v = workloads.softmax_qkv_device(wl.seed, B, L, Hq, Hkv)
+    hq, hk, hv = (x.float().cpu().numpy() for x in (q, k, v))
+    del q, k, v
+    rows_done, dt, passes = 0, 0.0, 0
+    while dt < min_seconds and passes < 64:
+        rows = np.arange((509 * passes) % 4096, L, 4096)[:8]  # 8 rows 4096 apart, offset per pass
+        t0 = time.perf_counter()
+        oracle.softmax_attention_rows(hq, hk, hv, rows, rope_dims=R, base=base)
+        dt += time.perf_counter() - t0
+        rows_done += len(rows)
+        passes += 1
+    pre = {"value": round(rows_done / dt, 2), "unit": "tokens/s", "cores": _blas_threads(), "kind": "oracle",
+           "sample": f"{rows_done} query rows x {Hq} heads spread over [0, {L}), {dt:.2f} s, fp64"}
+    wd = workloads.SOFTMAX_DECODE
+    ctx = wd.extra["context"]
+    g = np.random.Generator(np.random.PCG64(wd.seed))
+    kc = g.standard_normal((1, ctx + 1, Hkv, D))
+    vc = g.standard_normal((1, ctx + 1, Hkv, D))
+    qd, kn, vn = g.standard_normal((1, Hq, D)), g.standard_normal((1, Hkv, D)), g.standard_normal((1, Hkv, D))
+    steps, dt = 0, 0.0
+    while dt < min_seconds and steps < 200:
+        t0 = time.perf_counter()
+        oracle.softmax_decode(qd, kn, vn, kc, vc, np.array([ctx]), rope_dims=R, base=base)
+        dt += time.perf_counter() - t0
+        steps += 1
+    dec = {"value": round(steps / dt, 3), "unit": "sequence-steps/s", "cores": _blas_threads(), "kind": "oracle",
+           "sample": f"{steps} decode steps of one sequence over {ctx} cached tokens, {Hq} / {Hkv} heads, "
+                     f"{dt:.2f} s, fp64 (the GPU step serves {wd.batch} sequences)"}
+    return {"prefill": pre, "decode": dec}
+
+
 def run_decode(la, torch, nsteps, warmup=5, norm_gate=False, slots=0):
     """Batched decode steps (norm_gate: lt_decode_norm_gate with bf16 gate and
     bf16 y, the same algorithmic bytes as the plain step with fp32 o; slots > 0:
@@ -609,6 +662,10 @@ def main():
         smx = run_softmax(la, torch, 5, 1, 100)
         log(f"[bench] softmax prefill {smx['prefill']['call_ms_mean']:.3f} ms, decode "
             f"{smx['decode']['ms_per_step_median'] * 1e3:.1f} us")
+        if not args.no_cpu:
+            log("[bench] softmax oracle on the host")
+            sb = run_softmax_cpu_baseline(la, torch)
+            smx["prefill"]["cpu_baseline"], smx["decode"]["cpu_baseline"] = sb["prefill"], sb["decode"]
     cpu = None
     if not args.no_cpu:
         log(f"[bench] cpu oracle on {args.cpu_tokens} tokens")
