@@ -173,6 +173,8 @@ __global__ __launch_bounds__(NT, 4) void piece_state_kernel(PrefillArgs a, Segme
 }
 
 // ---------------------------------------------------------------------------
+constexpr int kRankUnits = 64;
+
 template <typename OutT, bool NG>
 __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, float *ws) {
     __shared__ __attribute__((aligned(16))) __bf16 Qs[C * D];
@@ -185,9 +187,29 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
     const int segments = sp.segments;
     const long long seg_len = sp.seg_len;
     const int g = blockIdx.x % segments;
-    const int uh = blockIdx.x / segments;
-    const int h = uh % a.heads, n = uh / a.heads;
+    const int slot = blockIdx.x / segments;
+    const int h = slot % a.heads;
     const int tid = threadIdx.x, lane = tid & 63;
+    // Packed batches of up to kRankUnits sequences run their longest sequences
+    // first: unit slot r takes the sequence of rank r by length (descending,
+    // ties by index), so the long whole-sequence workgroups do not start last
+    // and leave the end of the launch to a few CUs.
+    int n = slot / a.heads;
+    if (a.cu_seqlens && a.units <= kRankUnits) {
+        __shared__ long long lens[kRankUnits];
+        __shared__ int by_rank[kRankUnits];
+        if (tid < a.units) lens[tid] = sequence_of(a, tid).len;
+        __syncthreads();
+        if (tid < a.units) {
+            const long long li = lens[tid];
+            int r = 0;
+            for (int j = 0; j < a.units; ++j) r += lens[j] > li || (lens[j] == li && j < tid);
+            by_rank[r] = tid;
+        }
+        __syncthreads();
+        n = by_rank[n];
+    }
+    const int uh = n * a.heads + h;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int qh = w >> 2, cq = w & 3, r32 = lane & 31, hf = lane >> 5;
 
