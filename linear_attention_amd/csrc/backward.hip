@@ -207,6 +207,7 @@ __global__ __launch_bounds__(NT, 4) void rev_piece_kernel(BackwardArgs a, Segmen
     const uint16_t *qg = static_cast<const uint16_t *>(a.q) + (seq + h) * (long long)D;
     const uint16_t *gg = static_cast<const uint16_t *>(a.dout) + (seq + h) * (long long)D;
     const float s2 = a.slopes[h] * LOG2E;
+    if (fix_head(s2, sp.seg_len, sp.fix_osz)) return;  // local-start segments: no pre-pass
     float *u = sp.unit(ws, uh);
 
     f32x16 R[2];
@@ -297,8 +298,13 @@ __global__ __launch_bounds__(NT) void bwd_kv_kernel(BackwardArgs a, Segmented sp
     auto sidx = [&](int db, int v) {
         return (64 * qh + 32 * db + 8 * (v >> 2) + 4 * hf + (v & 3)) * D + 32 * cq + r32;
     };
-    const float *r_in = sp.segments > 1 ? sp.start_state(sp.unit(ws, uh), g)
-                                        : (a.d_state_out ? a.d_state_out + (size_t)uh * D * D : nullptr);
+    // local-start segments: segment 0 (the sequence end) starts from dS, the
+    // others from zero (the correction pass adds their carried-in term)
+    const bool fix = sp.segments > 1 && fix_head(s2, sp.seg_len, sp.fix_osz);
+    const float *r_in = sp.segments > 1 && !fix
+                            ? sp.start_state(sp.unit(ws, uh), g)
+                            : ((sp.segments == 1 || g == 0) && a.d_state_out ? a.d_state_out + (size_t)uh * D * D
+                                                                              : nullptr);
     if (r_in) {
 #pragma unroll
         for (int db = 0; db < 2; ++db)
@@ -424,12 +430,180 @@ __global__ __launch_bounds__(NT) void bwd_kv_kernel(BackwardArgs a, Segmented sp
             step(p, head_len, std::false_type{}, st0);
     }
 
-    if (a.d_state_in && g == sp.segments - 1) {  // the segment holding token 0
+    if (fix) {  // end carry of this local-start segment, for the chain
+        float *dst = sp.start_state(sp.unit(ws, uh), g);
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) dst[sidx(db, v)] = R[db][v];
+    } else if (a.d_state_in && g == sp.segments - 1) {  // the segment holding token 0
         float *dst = a.d_state_in + (size_t)uh * D * D;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
             for (int v = 0; v < 16; ++v) dst[sidx(db, v)] = R[db][v];
+    }
+}
+
+// Reverse pass on local-start segments. Mirrored segment g >= 1 started from a
+// zero carry instead of R_in(g) (boundary slot B_g after the chain), so token t
+// of it, n = seg_hi - 1 - t tokens before its right end, misses e^{-s n} R_in in
+// its gradient of S_t:
+//   dv_t += e^{-s n} k_t R_in,    dk_t += e^{-s n} v_t R_in^T,
+// added here for n <= kFixExp / s2 (smaller terms are below fp32 resolution),
+// in 64-token chunks counted from the right end, kRevFixParts workgroups per
+// (unit, head, segment). The products are the forward correction's (the carry,
+// or its transpose, as a bf16 S^T tile on MFMA).
+constexpr int kRevFixParts = 12;
+
+// Rows a thread adds to (loaded ahead of the products): fp32 rows (t/32) + 16j,
+// 4 columns at 4(t%32); bf16 rows (t/16) + 32j, 8 columns at 8(t%16). Rows
+// below rlo read row rlo and are not stored.
+struct RowsFrom {
+    uint4 y[4];
+    __device__ void load(const float *out, long long ts, int rlo, int tid) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = (tid >> 5) + 16 * j;
+            y[j] = *reinterpret_cast<const uint4 *>(out + (row > rlo ? row : rlo) * ts + 4 * (tid & 31));
+        }
+    }
+    __device__ void load(const __bf16 *out, long long ts, int rlo, int tid) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int row = (tid >> 4) + 32 * j;
+            y[j] = *reinterpret_cast<const uint4 *>(out + (row > rlo ? row : rlo) * ts + 8 * (tid & 15));
+        }
+    }
+    __device__ void add_store(float *out, long long ts, const float *Os, int rlo, int tid) const {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = (tid >> 5) + 16 * j, col = 4 * (tid & 31);
+            const float4 x = *reinterpret_cast<const float4 *>(Os + ooff(row, col));
+            if (row >= rlo)
+                *reinterpret_cast<float4 *>(out + row * ts + col) =
+                    make_float4(__uint_as_float(y[j].x) + x.x, __uint_as_float(y[j].y) + x.y,
+                                __uint_as_float(y[j].z) + x.z, __uint_as_float(y[j].w) + x.w);
+        }
+    }
+    __device__ void add_store(__bf16 *out, long long ts, const float *Os, int rlo, int tid) const {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int row = (tid >> 4) + 32 * j, col = 8 * (tid & 15);
+            const float4 x0 = *reinterpret_cast<const float4 *>(Os + ooff(row, col));
+            const float4 x1 = *reinterpret_cast<const float4 *>(Os + ooff(row, col + 4));
+            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            const uint32_t wv[4] = {y[j].x, y[j].y, y[j].z, y[j].w};
+            uint32_t r[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const __bf16 lo = static_cast<__bf16>(__uint_as_float(wv[i] << 16) + xs[2 * i]);
+                const __bf16 hi = static_cast<__bf16>(__uint_as_float(wv[i] & 0xffff0000u) + xs[2 * i + 1]);
+                uint16_t ulo, uhi;
+                __builtin_memcpy(&ulo, &lo, 2);
+                __builtin_memcpy(&uhi, &hi, 2);
+                r[i] = (uint32_t)ulo | ((uint32_t)uhi << 16);
+            }
+            if (row >= rlo) *reinterpret_cast<uint4 *>(out + row * ts + col) = make_uint4(r[0], r[1], r[2], r[3]);
+        }
+    }
+};
+
+template <typename OutT>
+__global__ __launch_bounds__(NT) void rev_fix_kernel(BackwardArgs a, Segmented sp, float *ws) {
+    __shared__ __attribute__((aligned(16))) __bf16 Rt[D * D];   // R_in^T: operand of the dv term
+    __shared__ __attribute__((aligned(16))) __bf16 Rn[D * D];   // R_in: operand of the dk term
+    __shared__ __attribute__((aligned(16))) __bf16 Kt[C * D];
+    __shared__ __attribute__((aligned(16))) __bf16 Vt[C * D];
+    __shared__ __attribute__((aligned(16))) float Os[C * D];
+
+    const int part = blockIdx.x % kRevFixParts;
+    const int gi = blockIdx.x / kRevFixParts;
+    const int g = 1 + gi % (sp.segments - 1);
+    const int uh = gi / (sp.segments - 1);
+    const int h = uh % a.heads, n = uh / a.heads;
+    const float s2 = a.slopes[h] * LOG2E;
+    if (!fix_head(s2, sp.seg_len, sp.fix_osz)) return;
+    const long long L = a.seqlen;
+    const long long seg_hi = L - g * sp.seg_len;
+    const long long seg_lo = seg_hi - sp.seg_len > 0 && g + 1 < sp.segments ? seg_hi - sp.seg_len : 0;
+    const long long len = seg_hi - seg_lo;
+    const long long fl = fix_len(s2, sp.seg_len) + 1;  // n = 0 .. fix_len
+    const long long T = fl < len ? fl : len;
+    const long long nch = (T + C - 1) / C;
+    if (part >= nch) return;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qh = w >> 2, cq = w & 3, r32 = lane & 31, hf = lane >> 5;
+    {
+        const float *ri = sp.partial(sp.unit(ws, uh), g);
+        f32x16 S[2];
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                S[db][v] = ri[(64 * qh + 32 * db + 8 * (v >> 2) + 4 * hf + (v & 3)) * D + 32 * cq + r32];
+        write_state_t(Rt, S, qh, cq, lane);
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)  // the transpose: element (r, c) of R_in^T is R_in[c][r]
+                S[db][v] = ri[(32 * cq + r32) * D + 64 * qh + 32 * db + 8 * (v >> 2) + 4 * hf + (v & 3)];
+        write_state_t(Rn, S, qh, cq, lane);
+    }
+    const int ts = a.heads * D;
+    const long long row0 = ((long long)n * L) * a.heads + h;  // token 0 of this (sequence, head)
+    const uint16_t *kg = static_cast<const uint16_t *>(a.k) + row0 * D;
+    const uint16_t *vg = static_cast<const uint16_t *>(a.v) + row0 * D;
+    OutT *dkg = static_cast<OutT *>(a.dk) + row0 * D;
+    OutT *dvg = static_cast<OutT *>(a.dv) + row0 * D;
+    const int seg = tid & 15;
+    for (long long c = part; c < nch; c += kRevFixParts) {
+        // chunk rows r = 0..63 are tokens tlo + r; those below seg_hi - T are not
+        // corrected (their loads read row rlo and they are not stored)
+        const long long tlo = seg_hi - C * (c + 1);
+        const int rlo = (int)(seg_hi - T - tlo > 0 ? seg_hi - T - tlo : 0);
+        OutT *dvc = dvg + tlo * (long long)ts, *dkc = dkg + tlo * (long long)ts;
+        uint4 kx[2], vx[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = (tid >> 4) + 32 * i;
+            const long long off = (tlo + (r > rlo ? r : rlo)) * (long long)ts + 8 * seg;
+            kx[i] = stream_load16(kg + off);
+            vx[i] = stream_load16(vg + off);
+        }
+        RowsFrom dvr, dkr;
+        dvr.load(dvc, ts, rlo, tid);
+        dkr.load(dkc, ts, rlo, tid);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = (tid >> 4) + 32 * i;
+            *reinterpret_cast<uint4 *>(Kt + L128::off(r, 8 * seg)) = keep_if(r >= rlo, kx[i]);
+            *reinterpret_cast<uint4 *>(Vt + L128::off(r, 8 * seg)) = keep_if(r >= rlo, vx[i]);
+        }
+        __syncthreads();  // K, V tiles (and the carry tiles) visible; Os free
+        const float f = fast_exp2(-s2 * (float)(seg_hi - 1 - (tlo + 32 * qh + r32)));
+        f32x16 o;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[v] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            o = mma(ld_op<L128>(Rt, 32 * cq, 16 * ks, lane), ld_op<L128>(Kt, 32 * qh, 16 * ks, lane), o);
+        o *= f;
+        stage_out(Os, o, qh, cq, lane);
+        __syncthreads();  // dv rows staged
+        dvr.add_store(dvc, ts, Os, rlo, tid);
+        __syncthreads();  // Os read
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[v] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            o = mma(ld_op<L128>(Rn, 32 * cq, 16 * ks, lane), ld_op<L128>(Vt, 32 * qh, 16 * ks, lane), o);
+        o *= f;
+        stage_out(Os, o, qh, cq, lane);
+        __syncthreads();  // dk rows staged; every read of the K and V tiles done
+        dkr.add_store(dkc, ts, Os, rlo, tid);
     }
 }
 
@@ -439,7 +613,11 @@ hipError_t launch(const BackwardArgs &a, const PrefillPlan &p, void *workspace, 
     const long long uh = (long long)a.units * a.heads;
     float *ws = static_cast<float *>(workspace);
     const bool seg = p.segments > 1 && p.value_slices == 1;
-    const Segmented sp = seg ? Segmented{p.segments, p.pieces, p.seg_len, p.piece_len}
+    // heads may take local-start segments when the correction (k, v read, dk, dv
+    // read and written: 512 + 512 sizeof(OutT) B per token) costs less than the
+    // reverse pre-pass (q, dO re-read: 512 B per token)
+    const int fix_osz = seg ? 1 + 2 * (int)sizeof(OutT) : 0;
+    const Segmented sp = seg ? Segmented{p.segments, p.pieces, p.seg_len, p.piece_len, fix_osz}
                              : Segmented{1, 0, a.seqlen, 0};
     if (seg) {
         hipLaunchKernelGGL(rev_piece_kernel, dim3((unsigned)(uh * p.pieces)), dim3(NT), 0, stream, a,
@@ -453,6 +631,15 @@ hipError_t launch(const BackwardArgs &a, const PrefillPlan &p, void *workspace, 
     }
     hipLaunchKernelGGL((bwd_kv_kernel<OutT>), dim3((unsigned)(uh * sp.segments)), dim3(NT), 0, stream,
                        a, sp, ws);
+    if (!fix_osz) return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fix_combine_kernel, dim3((unsigned)(uh * kCombineSlices)), dim3(kCombineThreads), 0, stream,
+                       a.slopes, a.heads, a.seqlen, a.d_state_in, sp, ws);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((rev_fix_kernel<OutT>), dim3((unsigned)(uh * (sp.segments - 1) * kRevFixParts)), dim3(NT), 0,
+                       stream, a, sp, ws);
     return hipGetLastError();
 }
 

@@ -447,7 +447,7 @@ LT_API lt_status lt_prefill_backward(const void *q, const void *k, const void *v
                              batch, heads};
     // the reverse pass splits long sequences like the forward when the
     // workspace allows (the dq pass above has finished with it by then)
-    lt::PrefillPlan p = lt::plan_prefill(batch, seqlen, heads, LT_BF16, false);
+    lt::PrefillPlan p = lt::plan_prefill(batch, seqlen, heads, LT_BF16, false, kPrepassWide);
     if (p.value_slices != 1 || (p.workspace > 0 && (!workspace || workspace_bytes < p.workspace))) {
         p = lt::PrefillPlan{};
         p.seg_len = seqlen;

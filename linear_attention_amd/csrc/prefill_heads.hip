@@ -625,30 +625,6 @@ __global__ __launch_bounds__(NT) void slice_kernel(PrefillArgs a) {
     }
 }
 
-// ---------------------------------------------------------------------------
-// Local-start segments (heads with fix_head): after the main kernel, the true
-// start state of every segment g >= 1 (into boundary slot B_g) and the final
-// state, from the end states E_g the main kernel left in slots S_g (segment 0
-// started from S_0, the others from zero):
-//   S_in(1) = E_0,   S_in(g+1) = e^{-s len_g} S_in(g) + E_g,
-//   S_final = e^{-s len_{G-1}} S_in(G-1) + E_{G-1}.
-__global__ __launch_bounds__(kCombineThreads) void fix_combine_kernel(PrefillArgs a, Segmented sp, float *ws) {
-    const int uh = blockIdx.x / kCombineSlices;
-    const int e = 4 * ((blockIdx.x % kCombineSlices) * kCombineThreads + threadIdx.x);
-    const float s2 = a.slopes[uh % a.heads] * LOG2E;
-    if (!fix_head(s2, sp.seg_len, sp.fix_osz)) return;
-    float *u = sp.unit(ws, uh);
-    float4 acc = *reinterpret_cast<const float4 *>(sp.start_state(u, 0) + e);
-    for (int g = 1; g < sp.segments; ++g) {
-        *reinterpret_cast<float4 *>(sp.partial(u, g) + e) = acc;
-        const long long rest = a.seqlen - (long long)g * sp.seg_len;
-        const float f = fast_exp2(-s2 * (float)(rest < sp.seg_len ? rest : sp.seg_len));
-        const float4 p = *reinterpret_cast<const float4 *>(sp.start_state(u, g) + e);
-        acc = make_float4(f * acc.x + p.x, f * acc.y + p.y, f * acc.z + p.z, f * acc.w + p.w);
-    }
-    if (a.state_out) *reinterpret_cast<float4 *>(a.state_out + (size_t)uh * D * D + e) = acc;
-}
-
 // o[t] += e^{-s(t+1)} q[t] S_in(g) for the first fix_len tokens t of segment g
 // (g >= 1), 64-token chunks; kFixParts workgroups per (unit, head, segment)
 // take every kFixParts-th chunk. The product is the main kernel's inter-block
@@ -813,7 +789,7 @@ hipError_t launch(const PrefillArgs &a, const PrefillPlan &p, void *workspace, h
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(fix_combine_kernel, dim3((unsigned)(uh * kCombineSlices)), dim3(kCombineThreads), 0, stream,
-                       a, sp, ws);
+                       a.slopes, a.heads, a.seqlen, a.state_out, sp, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((fix_kernel<OutT>), dim3((unsigned)(uh * (p.segments - 1) * kFixParts)), dim3(NT), 0, stream,
