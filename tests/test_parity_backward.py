@@ -97,3 +97,34 @@ def test_backward_long_sequence_without_workspace(la):
     """No workspace: one workgroup per (sequence, head) in both passes."""
     errs = backward_case(la, 1, 9000, 2, 1901, with_state=True, workspace="none")
     assert max(errs.values()) <= TOL_BF16, errs
+
+
+@pytest.mark.parametrize("grad_dtype", ["f32", "bf16"])
+def test_backward_segmented_slope_mix(la, grad_dtype):
+    """Segmented backward over heads on both routes of both passes: short-memory
+    heads (slopes 0.2, 1, 30) on local-start segments with the carried-in terms
+    added afterwards (30: only the last token of each reverse segment), the
+    others (0, 1e-6, 0.02) on the pre-passes; carried-in state and final-state
+    gradient."""
+    import torch
+
+    L, H = 9000, 6
+    sl = np.array([0.0, 1e-6, 0.02, 0.2, 1.0, 30.0], np.float32)
+    print(f"[case] backward segmented slope mix L={L} slopes={list(sl)} grad={grad_dtype}", flush=True)
+    q, k, v = workloads.qkv_host(2501, (1, L, H, 128), "bf16")
+    do = workloads.gate_host(2502, (1, L, H, 128), "bf16")
+    s0 = workloads.state_host(2503, (1, H, 128, 128))
+    ds = workloads.state_host(2504, (1, H, 128, 128))
+    gd = torch.float32 if grad_dtype == "f32" else torch.bfloat16
+    dq, dk, dv, dsi = la.lt_prefill_backward(
+        to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16"), to_device(do, "bf16"),
+        torch.from_numpy(sl).cuda(), 256, torch.from_numpy(s0).cuda(), torch.from_numpy(ds).cuda(), grad_dtype=gd)
+    torch.cuda.synchronize()
+    rq, rk, rv, rs = oracle.backward_batch(q, k, v, do, sl, s0=s0, ds=ds)
+    errs = {}
+    for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        gh = to_host_f32(g)
+        errs[name] = max(rel_l2(gh[0, :, h], r[0, :, h]) for h in range(H))
+    errs["ds0"] = max_rel_states(to_host_f32(dsi), rs)
+    print(f"[result] {errs}", flush=True)
+    assert max(errs.values()) <= TOL_BF16, errs
