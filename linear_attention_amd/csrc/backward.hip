@@ -613,9 +613,9 @@ hipError_t launch(const BackwardArgs &a, const PrefillPlan &p, void *workspace, 
     const long long uh = (long long)a.units * a.heads;
     float *ws = static_cast<float *>(workspace);
     const bool seg = p.segments > 1 && p.value_slices == 1;
-    // heads may take local-start segments when the correction (k, v read, dk, dv
-    // read and written: 512 + 512 sizeof(OutT) B per token) costs less than the
-    // reverse pre-pass (q, dO re-read: 512 B per token)
+    // heads may take local-start segments (fix_head's rule) with the correction's
+    // traffic at k, v read, dk, dv read and written: 512 + 512 sizeof(OutT) B per
+    // token, against the reverse pre-pass's q, dO re-read, 512 B per token
     const int fix_osz = seg ? 1 + 2 * (int)sizeof(OutT) : 0;
     const Segmented sp = seg ? Segmented{p.segments, p.pieces, p.seg_len, p.piece_len, fix_osz}
                              : Segmented{1, 0, a.seqlen, 0};

@@ -288,17 +288,25 @@ __device__ __forceinline__ SeqRange sequence_of(const PrefillArgs &a, int n) {
 // t + 1 > kFixExp / s2: a correction pass adds the term to the first
 // fix_len = min(segment, kFixExp / s2) tokens and leaves the rest (2^-32 of the
 // term's own scale is below fp32 resolution of the output). A head takes this
-// route when re-reading q and o for fix_len tokens costs less HBM traffic than
-// the pre-pass re-read of the whole segment's k and v:
-//   fix_len (256 + 256 osz) <= 512 seg_len    (osz: bytes per output element;
-// q read once, o read and written).
+// route when its decay cuts the term off inside the segment and re-reading q
+// and o for fix_len tokens costs at most twice the HBM traffic of the pre-pass
+// re-read of the whole segment's k and v:
+//   fix_len < seg_len  and  fix_len (256 + 256 osz) <= 2 * 512 seg_len
+// (osz: bytes per output element; q read once, o read and written). The factor
+// 2 is measured: the pre-pass of the few heads that still need it runs far
+// below the bandwidth the correction pass reaches, and the pre-pass and combine
+// launches are dependent steps ahead of the main kernel (M1 layer, 64 heads,
+// 32,768 tokens: with factor 1, 57 heads correct and 7 take the pre-pass,
+// 0.574 ms; with factor 2 all 64 correct, 0.557 ms).
 constexpr float kFixExp = 32.f;
 __device__ __forceinline__ long long fix_len(float s2, long long seg_len) {
     const float t = kFixExp / s2;
     return t >= (float)seg_len ? seg_len : (long long)t;
 }
 __device__ __forceinline__ bool fix_head(float s2, long long seg_len, int osz) {
-    return osz > 0 && s2 > 0.f && fix_len(s2, seg_len) * (1 + osz) <= 2 * seg_len;
+    if (osz <= 0 || !(s2 > 0.f)) return false;
+    const long long n = fix_len(s2, seg_len);
+    return n < seg_len && n * (1 + osz) <= 4 * seg_len;
 }
 
 struct Segmented {

@@ -387,15 +387,16 @@ def test_decode_batches_with_strided_order(la, B):
 
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_prefill_segmented_slope_mix(la, out_dtype):
-    """Segmented plan over heads whose decay sends them down both routes: heads
-    with a short memory start every segment from zero and get the carried-in
-    term added to their first tokens afterwards (slopes 0.2, 1, 30; 30 needs no
-    correction at all), heads with a long one (0, 1e-6, 0.02) take the pre-pass;
-    with a carried-in state updated in place."""
+    """Segmented plan (4 segments of 2,304 tokens) over heads whose decay sends
+    them down both routes: heads with a short memory start every segment from
+    zero and get the carried-in term added to their first tokens afterwards
+    (slopes 0.02, 0.2, 1, 30: 1,109 corrected tokens down to none at all), heads
+    with a long one (0, 1e-6, 0.005: 4,436 tokens, past the segment) take the
+    pre-pass; with a carried-in state updated in place."""
     import torch
 
-    L, H = 9000, 6
-    sl = np.array([0.0, 1e-6, 0.02, 0.2, 1.0, 30.0], np.float32)
+    L, H = 9000, 7
+    sl = np.array([0.0, 1e-6, 0.005, 0.02, 0.2, 1.0, 30.0], np.float32)
     print(f"[case] segmented slope mix L={L} slopes={list(sl)} out={out_dtype}", flush=True)
     assert la.lt_prefill_workspace_bytes(1, L, H) > 0
     q, k, v = workloads.qkv_host(2301, (1, L, H, 128), "bf16")
