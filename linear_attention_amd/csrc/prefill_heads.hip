@@ -626,42 +626,73 @@ __global__ __launch_bounds__(NT) void slice_kernel(PrefillArgs a) {
 }
 
 // o[t] += e^{-s(t+1)} q[t] S_in(g) for the first fix_len tokens t of segment g
-// (g >= 1), 64-token chunks; kFixParts workgroups per (unit, head, segment)
-// take every kFixParts-th chunk. The product is the main kernel's inter-block
-// one (S^T in bf16 on MFMA, Q from an LDS tile).
-constexpr int kFixParts = 12;
+// (g >= 1), in 64-token chunks. The chunks of all (unit, head, segment) pairs
+// are numbered in pair order and cut into equal contiguous ranges, one per
+// workgroup (the pairs' chunk counts differ with the decay by up to two orders
+// of magnitude); consecutive ranges go to workgroups on one XCD, so the few
+// workgroups that share a pair read its end states through one L2. A workgroup
+// forms S_in(g) from the end states E_0..E_{g-1} the main pass left
+// (S_in(1) = E_0, S_in(j+1) = e^{-s len_j} S_in(j) + E_j) and loads the next
+// chunk's q and o rows before the current chunk's product, which is the main
+// kernel's inter-block one (S^T in bf16 on MFMA, Q from an LDS tile). The first
+// `nfinal` workgroups instead write the final state of each local-start head,
+// e^{-s len_{G-1}} S_in(G-1) + E_{G-1}, kFinalSlices workgroups per head.
+constexpr int kFixWorkgroups = 512;                // two per CU; a multiple of 8 (XCDs)
+constexpr int kFixMaxPairs = 256;                  // segmented plans have fewer (unit, head, g >= 1) pairs
+constexpr int kFinalSlices = D * D / (4 * NT);     // 4 state elements per thread
+
+// A 64-bit value that is the same in every lane, kept in scalar registers.
+__device__ __forceinline__ long long uniform64(long long x) {
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)x);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)((unsigned long long)x >> 32));
+    return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
+__device__ __forceinline__ long long seg_len_at(const Segmented &sp, long long seqlen, int g) {
+    const long long rest = seqlen - (long long)g * sp.seg_len;
+    return rest < sp.seg_len ? rest : sp.seg_len;
+}
 
 // The rows of o a thread adds to (loaded before the product, so their latency
 // overlaps it): fp32 rows (t/32) + 16j, 4 columns at 4(t%32); bf16 rows
 // (t/16) + 32j, 8 columns at 8(t%16). Rows >= m read row m-1 and are not stored.
-struct OutRows {
+// Offsets from the chunk's first row fit in 32 bits (64 rows). Sized by the
+// output type, so that a copy moves only loaded registers.
+template <typename OutT>
+struct OutRows;
+template <>
+struct OutRows<float> {
     uint4 y[4];
-    __device__ void load(const float *out, long long ts, int m, int tid) {
+    __device__ void load(const float *out, int ts, int m, int tid) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int row = (tid >> 5) + 16 * j;
-            y[j] = *reinterpret_cast<const uint4 *>(out + (row < m ? row : m - 1) * ts + 4 * (tid & 31));
+            y[j] = *reinterpret_cast<const uint4 *>(out + (unsigned)((row < m ? row : m - 1) * ts + 4 * (tid & 31)));
         }
     }
-    __device__ void load(const __bf16 *out, long long ts, int m, int tid) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int row = (tid >> 4) + 32 * j;
-            y[j] = *reinterpret_cast<const uint4 *>(out + (row < m ? row : m - 1) * ts + 8 * (tid & 15));
-        }
-    }
-    __device__ void add_store(float *out, long long ts, const float *Os, int m, int tid) const {
+    __device__ void add_store(float *out, int ts, const float *Os, int m, int tid) const {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int row = (tid >> 5) + 16 * j, col = 4 * (tid & 31);
             const float4 x = *reinterpret_cast<const float4 *>(Os + ooff(row, col));
             if (row < m)
-                *reinterpret_cast<float4 *>(out + row * ts + col) =
+                *reinterpret_cast<float4 *>(out + (unsigned)(row * ts + col)) =
                     make_float4(__uint_as_float(y[j].x) + x.x, __uint_as_float(y[j].y) + x.y,
                                 __uint_as_float(y[j].z) + x.z, __uint_as_float(y[j].w) + x.w);
         }
     }
-    __device__ void add_store(__bf16 *out, long long ts, const float *Os, int m, int tid) const {
+};
+template <>
+struct OutRows<__bf16> {
+    uint4 y[2];
+    __device__ void load(const __bf16 *out, int ts, int m, int tid) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int row = (tid >> 4) + 32 * j;
+            y[j] = *reinterpret_cast<const uint4 *>(out + (unsigned)((row < m ? row : m - 1) * ts + 8 * (tid & 15)));
+        }
+    }
+    __device__ void add_store(__bf16 *out, int ts, const float *Os, int m, int tid) const {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int row = (tid >> 4) + 32 * j, col = 8 * (tid & 15);
@@ -684,73 +715,188 @@ struct OutRows {
     }
 };
 
+// One chunk of the correction: rows [t0, t0 + m) of segment g of pair `pair`.
 template <typename OutT>
-__global__ __launch_bounds__(NT) void fix_kernel(PrefillArgs a, Segmented sp, float *ws) {
+struct FixChunk {
+    const uint16_t *q;
+    OutT *o;
+    long long t0;
+    int m, pair, uh, g;
+    float s2;
+};
+
+template <typename OutT>
+__device__ __forceinline__ FixChunk<OutT> fix_chunk(const PrefillArgs &a, const Segmented &sp,
+                                                    const long long *first, long long j, int &p) {
+    while (first[p + 1] <= j) ++p;
+    p = __builtin_amdgcn_readfirstlane(p);  // the same for every lane
+    FixChunk<OutT> x;
+    const int gs = sp.segments - 1;
+    x.pair = p;
+    x.uh = p / gs;
+    x.g = 1 + p % gs;
+    const int h = x.uh % a.heads, n = x.uh / a.heads;
+    x.s2 = a.slopes[h] * LOG2E;
+    const long long len = seg_len_at(sp, a.seqlen, x.g), fl = fix_len(x.s2, sp.seg_len);
+    const long long T = fl < len ? fl : len;
+    x.t0 = uniform64((j - first[p]) * C);
+    x.m = (int)(T - x.t0 < C ? T - x.t0 : C);
+    const long long row = (long long)n * a.seqlen + (long long)x.g * sp.seg_len + x.t0;
+    const long long off = (row * a.heads + h) * (long long)D;
+    x.q = static_cast<const uint16_t *>(a.q) + off;
+    x.o = static_cast<OutT *>(a.o) + off;
+    return x;
+}
+
+// Two workgroups per CU: 128 registers per lane, and the Q tile shares its
+// LDS with the staged output (66 KB per workgroup).
+template <typename OutT>
+__global__ __launch_bounds__(NT, 4) void fix_kernel(PrefillArgs a, Segmented sp, float *ws, int nfinal) {
     __shared__ __attribute__((aligned(16))) __bf16 Sts[D * D];
-    __shared__ __attribute__((aligned(16))) __bf16 Qs[C * D];
     __shared__ __attribute__((aligned(16))) float Os[C * D];
+    __shared__ long long first[kFixMaxPairs + 1];  // first chunk number of each pair
+    __bf16 *const Qs = reinterpret_cast<__bf16 *>(Os);
 
-    const int part = blockIdx.x % kFixParts;
-    const int gi = blockIdx.x / kFixParts;
-    const int g = 1 + gi % (sp.segments - 1);
-    const int uh = gi / (sp.segments - 1);
-    const int h = uh % a.heads, n = uh / a.heads;
-    const float s2 = a.slopes[h] * LOG2E;
-    if (!fix_head(s2, sp.seg_len, sp.fix_osz)) return;
-    const long long seg0 = (long long)g * sp.seg_len;
-    const long long len = a.seqlen - seg0 < sp.seg_len ? a.seqlen - seg0 : sp.seg_len;
-    const long long T = fix_len(s2, sp.seg_len) < len ? fix_len(s2, sp.seg_len) : len;
-    const long long nch = (T + C - 1) / C;
-    if (part >= nch) return;
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int qh = w >> 2, cq = w & 3, r32 = lane & 31, hf = lane >> 5;
-    {
-        const float *si = sp.partial(sp.unit(ws, uh), g);
-        f32x16 S[2];
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                S[db][v] = si[(64 * qh + 32 * db + 8 * (v >> 2) + 4 * hf + (v & 3)) * D + 32 * cq + r32];
-        write_state_t(Sts, S, qh, cq, lane);
+    const int tid = threadIdx.x;
+    if ((int)blockIdx.x < nfinal) {  // final state of a local-start head
+        const int uh = blockIdx.x / kFinalSlices;
+        const float s2 = a.slopes[uh % a.heads] * LOG2E;
+        if (!fix_head(s2, sp.seg_len, sp.fix_osz)) return;
+        const int e = 4 * ((blockIdx.x % kFinalSlices) * NT + tid);
+        float *u = sp.unit(ws, uh);
+        float4 acc = *reinterpret_cast<const float4 *>(sp.start_state(u, 0) + e);
+        for (int g = 1; g < sp.segments; ++g) {
+            const float f = fast_exp2(-s2 * (float)seg_len_at(sp, a.seqlen, g));
+            const float4 x = *reinterpret_cast<const float4 *>(sp.start_state(u, g) + e);
+            acc = make_float4(f * acc.x + x.x, f * acc.y + x.y, f * acc.z + x.z, f * acc.w + x.w);
+        }
+        *reinterpret_cast<float4 *>(a.state_out + (size_t)uh * D * D + e) = acc;
+        return;
     }
-    const int ts = a.heads * D;
-    const long long base = (((long long)n * a.seqlen + seg0) * a.heads + h) * (long long)D;
-    const uint16_t *qg = static_cast<const uint16_t *>(a.q) + base;
-    OutT *og = static_cast<OutT *>(a.o) + base;
-    const int seg = tid & 15;
-    for (long long c = part; c < nch; c += kFixParts) {
-        const int m = (int)(T - c * C < C ? T - c * C : C);
-        // q rows of this chunk (rows past m read row m-1 and are zeroed); the
-        // previous chunk's reads of Qs and Os ended before its last barrier
-        // for the MFMA reads, and before this chunk's first barrier for Os
-        OutT *oc = og + c * C * (long long)ts;
-        uint4 qx[2];
+
+    // chunks per pair (0 unless the head takes local starts), then their
+    // prefix sums (inclusive scan over the first kFixMaxPairs threads)
+    const int gs = sp.segments - 1;
+    const int pairs = a.units * a.heads * gs;
+    long long x = 0;
+    if (tid < pairs) {
+        const int g = 1 + tid % gs;
+        const float s2 = a.slopes[(tid / gs) % a.heads] * LOG2E;
+        if (fix_head(s2, sp.seg_len, sp.fix_osz)) {
+            const long long len = seg_len_at(sp, a.seqlen, g), fl = fix_len(s2, sp.seg_len);
+            x = ((fl < len ? fl : len) + C - 1) / C;
+        }
+    }
+    for (int off = 1; off < kFixMaxPairs; off <<= 1) {
+        if (tid < kFixMaxPairs) first[tid + 1] = x;
+        __syncthreads();
+        if (tid < kFixMaxPairs && tid >= off) x += first[tid + 1 - off];
+        __syncthreads();
+    }
+    if (tid < kFixMaxPairs) first[tid + 1] = x;
+    if (tid == 0) first[0] = 0;
+    __syncthreads();
+
+    // this workgroup's range: workgroups on one XCD (blockIdx % 8; nfinal and
+    // the grid's remainder are multiples of 8) take consecutive ranges
+    const long long total = uniform64(first[pairs]);
+    const int nwg = gridDim.x - nfinal;
+    const int r = (int)(blockIdx.x % 8) * (nwg / 8) + (int)(blockIdx.x - nfinal) / 8;
+    const long long j0 = total * r / nwg, j1 = total * (r + 1) / nwg;
+    if (j0 >= j1) return;
+
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qh = w >> 2, cq = w & 3;
+    const int ts = a.heads * D;  // 32-bit row offsets within a chunk (64 rows)
+    auto load_q = [&](const FixChunk<OutT> &c, uint4 (&qx)[2], int th) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int t = (tid >> 4) + 32 * i;
-            qx[i] = stream_load16(qg + (c * C + (t < m ? t : m - 1)) * (long long)ts + 8 * seg);
+            const int t = (th >> 4) + 32 * i;
+            qx[i] = stream_load16(c.q + (unsigned)((t < c.m ? t : c.m - 1) * ts + 8 * (th & 15)));
         }
-        OutRows rows;
-        rows.load(oc, ts, m, tid);
+    };
+    int p = 0;
+    FixChunk<OutT> cur = fix_chunk<OutT>(a, sp, first, j0, p);
+    uint4 qa[2];
+    OutRows<OutT> ra;
+    load_q(cur, qa, tid);
+    ra.load(cur.o, ts, cur.m, tid);
+    int loaded = -1;
+    for (long long j = j0; j < j1; ++j) {
+        if (j > j0) __syncthreads();  // the previous chunk's reads of Os (= Qs) done
+        // Lane-dependent offsets are recomputed from an opaque copy of the
+        // thread index every chunk: hoisted out of the loop they would be
+        // spilled, and a spill reload waits for every load in flight,
+        // including the next chunk's.
+        int tl = tid;
+        asm volatile("" : "+v"(tl));
+        const int ln = tl & 63;
+        // the next chunk's loads go out before anything waits for this one's
+        FixChunk<OutT> nxt = cur;
+        uint4 qb[2] = {qa[0], qa[1]};
+        OutRows<OutT> rb = ra;
+        if (j + 1 < j1) {
+            nxt = fix_chunk<OutT>(a, sp, first, j + 1, p);
+            load_q(nxt, qb, tl);
+            rb.load(nxt.o, ts, nxt.m, tl);
+        }
+        if (cur.pair != loaded) {
+            // S_in(g) of this pair as bf16 S^T: the thread with value column
+            // c and key quad kq forms S_in[4(kq + 4i) + r + 64 half][c], i < 4,
+            // r < 4, half < 2 (the previous chunk's reads of Sts ended before
+            // its second barrier)
+            const int c = tl & (D - 1), kq = tl >> 7;
+            float *u = sp.unit(ws, cur.uh);
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {  // 16 elements at a time (registers)
+                float acc[4][4];
+                {
+                    const float *e = sp.start_state(u, 0) + (4 * kq + 64 * half) * D + c;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[i][r] = e[(16 * i + r) * D];
+                }
+                for (int g = 1; g < cur.g; ++g) {
+                    const float f = fast_exp2(-cur.s2 * (float)seg_len_at(sp, a.seqlen, g));
+                    const float *e = sp.start_state(u, g) + (4 * kq + 64 * half) * D + c;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[i][r] = f * acc[i][r] + e[(16 * i + r) * D];
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    bf16x4 x;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) x[r] = static_cast<__bf16>(acc[i][r]);
+                    *reinterpret_cast<bf16x4 *>(Sts + L128::off(c, 4 * (kq + 4 * i) + 64 * half)) = x;
+                }
+            }
+            loaded = cur.pair;
+        }
+        // this chunk's q rows into the tile (rows past m zeroed)
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int t = (tid >> 4) + 32 * i;
-            *reinterpret_cast<uint4 *>(Qs + L128::off(t, 8 * seg)) = keep_if(t < m, qx[i]);
+            const int t = (tl >> 4) + 32 * i;
+            *reinterpret_cast<uint4 *>(Qs + L128::off(t, 8 * (tl & 15))) = keep_if(t < cur.m, qa[i]);
         }
-        __syncthreads();  // Q tile (and S^T) visible; Os free
+        __syncthreads();  // Q tile and S^T visible
         f32x16 o;
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[v] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks)
-            o = mma(ld_op<L128>(Sts, 32 * cq, 16 * ks, lane), ld_op<L128>(Qs, 32 * qh, 16 * ks, lane), o);
-        o *= fast_exp2(-s2 * (float)(c * C + 32 * qh + r32 + 1));
-        stage_out(Os, o, qh, cq, lane);
-        __syncthreads();  // Os visible; every read of Qs done
-        rows.add_store(oc, ts, Os, m, tid);
+            o = mma(ld_op<L128>(Sts, 32 * cq, 16 * ks, ln), ld_op<L128>(Qs, 32 * qh, 16 * ks, ln), o);
+        o *= fast_exp2(-cur.s2 * (float)(cur.t0 + 32 * qh + (ln & 31) + 1));
+        __syncthreads();  // every read of Qs and Sts done
+        stage_out(Os, o, qh, cq, ln);
+        __syncthreads();  // Os visible
+        ra.add_store(cur.o, ts, Os, cur.m, tl);
+        cur = nxt;
+        qa[0] = qb[0];
+        qa[1] = qb[1];
+        ra = rb;
     }
 }
 
@@ -788,12 +934,10 @@ hipError_t launch(const PrefillArgs &a, const PrefillPlan &p, void *workspace, h
     if (!fix_osz) return hipGetLastError();
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fix_combine_kernel, dim3((unsigned)(uh * kCombineSlices)), dim3(kCombineThreads), 0, stream,
-                       a.slopes, a.heads, a.seqlen, a.state_out, sp, ws);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((fix_kernel<OutT>), dim3((unsigned)(uh * (p.segments - 1) * kFixParts)), dim3(NT), 0, stream,
-                       a, sp, ws);
+    if (uh * (p.segments - 1) > kFixMaxPairs) return hipErrorInvalidValue;  // not a segmented plan
+    const int nfinal = a.state_out ? (int)(uh * kFinalSlices) : 0;
+    hipLaunchKernelGGL((fix_kernel<OutT>), dim3((unsigned)(nfinal + kFixWorkgroups)), dim3(NT), 0, stream, a, sp,
+                       ws, nfinal);
     return hipGetLastError();
 }
 

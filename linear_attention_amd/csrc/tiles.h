@@ -386,33 +386,5 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float *s
     }
 }
 
-// Local-start segments (heads with fix_head), after the main pass: the true
-// start state of every segment g >= 1 (into boundary slot B_g) and the final
-// state, from the end states E_g the main pass left in slots S_g (segment 0
-// started from the carried-in state, the others from zero):
-//   S_in(1) = E_0,   S_in(g+1) = e^{-s len_g} S_in(g) + E_g,
-//   final   = e^{-s len_{G-1}} S_in(G-1) + E_{G-1},
-// len_g = min(seg_len, seqlen - g seg_len). The backward's reverse pass uses it
-// on its mirrored segments (counted from the sequence end), whose lengths
-// follow the same formula, with the carry in place of the state.
-__global__ __launch_bounds__(kCombineThreads) void fix_combine_kernel(const float *slopes, int heads,
-                                                                       long long seqlen, float *final_out,
-                                                                       Segmented sp, float *ws) {
-    const int uh = blockIdx.x / kCombineSlices;
-    const int e = 4 * ((blockIdx.x % kCombineSlices) * kCombineThreads + threadIdx.x);
-    const float s2 = slopes[uh % heads] * LOG2E;
-    if (!fix_head(s2, sp.seg_len, sp.fix_osz)) return;
-    float *u = sp.unit(ws, uh);
-    float4 acc = *reinterpret_cast<const float4 *>(sp.start_state(u, 0) + e);
-    for (int g = 1; g < sp.segments; ++g) {
-        *reinterpret_cast<float4 *>(sp.partial(u, g) + e) = acc;
-        const long long rest = seqlen - (long long)g * sp.seg_len;
-        const float f = fast_exp2(-s2 * (float)(rest < sp.seg_len ? rest : sp.seg_len));
-        const float4 p = *reinterpret_cast<const float4 *>(sp.start_state(u, g) + e);
-        acc = make_float4(f * acc.x + p.x, f * acc.y + p.y, f * acc.z + p.z, f * acc.w + p.w);
-    }
-    if (final_out) *reinterpret_cast<float4 *>(final_out + (size_t)uh * D * D + e) = acc;
-}
-
 }  // namespace
 }  // namespace lt
