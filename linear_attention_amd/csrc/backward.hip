@@ -322,12 +322,6 @@ __global__ __launch_bounds__(NT) void bwd_kv_kernel(BackwardArgs a, Segmented sp
     const bool scorer = w < 6;
     const int blk = w % 3;
     const int sI = blk == 2 ? 1 : 0, sJ = blk == 0 ? 0 : 1;  // rows i in 32sI.., columns i' in 32sJ..
-    float dscore[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int diff = (32 * sJ + r32) - (32 * sI + 8 * (v >> 2) + 4 * hf + (v & 3));
-        dscore[v] = diff >= 0 ? fast_exp2(-s2 * (float)diff) : 0.f;
-    }
 
     // Sub-blocks are anchored at the end of the sequence: step p < nfull covers
     // tokens [len - 64(p+1), len - 64p); a short first block [0, len mod 64),
@@ -368,6 +362,18 @@ __global__ __launch_bounds__(NT) void bwd_kv_kernel(BackwardArgs a, Segmented sp
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks)
                 sc = mma(ld_op<LT>(X, 32 * sI, 16 * ks, lane), ld_op<LT>(Y, 32 * sJ, 16 * ks, lane), sc);
+            // decay of C[i][i'], e^{-s(i' - i)} for i' >= i, recomputed every step
+            // from an opaque copy of the lane: kept across the loop these 16
+            // values were spilled, and each reload waited for every load in
+            // flight, the prefetch of the sub-blocks ahead included
+            int lo = lane;
+            asm volatile("" : "+v"(lo));
+            float dscore[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int diff = (32 * sJ + (lo & 31)) - (32 * sI + 8 * (v >> 2) + 4 * (lo >> 5) + (v & 3));
+                dscore[v] = diff >= 0 ? fast_exp2(-s2 * (float)diff) : 0.f;
+            }
 #pragma unroll
             for (int gv = 0; gv < 4; ++gv) {
                 bf16x4 pv;
