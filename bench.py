@@ -139,7 +139,7 @@ def run_prefill(la, torch, steps, warmup):
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "bytes_per_launch": bytes_alg,
                      "kernel": "lt_prefill call: piece_state_kernel + combine_kernel + head_kernel<float> "
-                               "+ fix_combine_kernel + fix_kernel<float>"},
+                               "+ fix_kernel<float>"},
     }
 
 
