@@ -95,7 +95,7 @@ inline void clear_pending_error() { (void)hipGetLastError(); }
 
 // prepass_wgs: pre-pass workgroups to aim for (sets the piece length).
 PrefillPlan plan_prefill(long long units, long long seqlen, int heads, lt_dtype in_dtype,
-                         bool varlen, long long prepass_wgs = 512);
+                         bool varlen, long long prepass_wgs);
 
 // Backward of a fixed-length bf16 prefill (gradients of
 // l = sum dout . o + <d_state_out, S_final>): dk, dv and d_state_in from one

@@ -50,14 +50,10 @@ lt_status map_hip(hipError_t e) {
 constexpr long long kTargetWorkgroups = 256;
 // Shortest segment worth a workgroup of its own.
 constexpr long long kMinSegment = 2048;
-// Pre-pass workgroups to aim for: two per CU is what its registers allow, so
-// the whole pre-pass grid is resident at once.
-constexpr long long kPrepassWorkgroups = 512;
-// Pre-pass workgroups when heads may take local-start segments (every call but
-// the norm-gate ones): the heads with a short memory skip the pre-pass, and the
-// few that remain (7 of 64 in the M1 layer's slope schedule) get more, shorter
-// pieces.
-// Measured on the M1 layer: 512 -> 661 us, 1024 -> 643 us, 2048 -> 608 us.
+// Pre-pass workgroups to aim for. Heads with a short memory take local-start
+// segments and skip the pre-pass, so the few that remain get more, shorter
+// pieces (measured on the M1 layer when 7 of its 64 heads took the pre-pass:
+// 512 -> 661 us, 1024 -> 643 us, 2048 -> 608 us per call).
 constexpr long long kPrepassWide = 2048;
 // Shortest pre-pass piece.
 constexpr long long kMinPiece = 512;
@@ -70,7 +66,7 @@ lt_status launch(const lt::PrefillArgs &a, int in_dtype, int out_dtype, bool var
     const bool whole_rows = a.ng.gate || a.state_in_t;  // epilogue or transposed S_0
     lt::PrefillPlan p = lt::plan_prefill(a.units, varlen ? a.total_tokens : a.seqlen, a.heads,
                                          (lt_dtype)in_dtype, varlen,
-                                         a.ng.gate ? kPrepassWorkgroups : kPrepassWide);
+                                         kPrepassWide);
     // Without the workspace the segmented plan needs, split value columns instead;
     // the norm-gate epilogue needs whole output rows, so it keeps one workgroup
     // per (sequence, head) rather than value slices.
@@ -200,11 +196,7 @@ LT_API size_t lt_prefill_workspace_bytes(int batch, long long seqlen, int heads,
     if (batch <= 0 || seqlen <= 0 || heads <= 0 || heads > LT_MAX_HEADS ||
         head_dim != lt::kHeadDim || !dtype_ok(in_dtype))
         return 0;
-    // enough for either pre-pass granularity (the norm-gate entry points use
-    // the coarser one)
-    const size_t a = lt::plan_prefill(batch, seqlen, heads, in_dtype, false, kPrepassWide).workspace;
-    const size_t b = lt::plan_prefill(batch, seqlen, heads, in_dtype, false, kPrepassWorkgroups).workspace;
-    return a > b ? a : b;
+    return lt::plan_prefill(batch, seqlen, heads, in_dtype, false, kPrepassWide).workspace;
 }
 
 LT_API const char *lt_status_string(int status) {

@@ -72,10 +72,11 @@ __device__ __forceinline__ void row_sumsq(float *rss, const f32x16 &o, int qh, i
     if (lane < 32) rss[(32 * qh + lane) * 4 + cq] = ss;
 }
 
+// raw: store o itself (every factor replaced by 1, by a select).
 template <bool FULL, typename OutT>
 __device__ __forceinline__ void store_rows_norm_gate(OutT *out, long long ts, const float *Os,
                                                      const float *rss, int m, int tid,
-                                                     const uint2 (&gr)[4], float4 w, float eps) {
+                                                     const uint2 (&gr)[4], float4 w, float eps, bool raw) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int row = (tid >> 5) + 16 * j, col = 4 * (tid & 31);
@@ -84,8 +85,9 @@ __device__ __forceinline__ void store_rows_norm_gate(OutT *out, long long ts, co
         const float inv = __builtin_amdgcn_rsqf((p.x + p.y + p.z + p.w) * (1.f / D) + eps);
         const float g0 = __uint_as_float(gr[j].x << 16), g1 = __uint_as_float(gr[j].x & 0xffff0000u);
         const float g2 = __uint_as_float(gr[j].y << 16), g3 = __uint_as_float(gr[j].y & 0xffff0000u);
-        const float4 y = make_float4(x.x * inv * w.x * sigmoid(g0), x.y * inv * w.y * sigmoid(g1),
-                                     x.z * inv * w.z * sigmoid(g2), x.w * inv * w.w * sigmoid(g3));
+        const float f0 = raw ? 1.f : inv * w.x * sigmoid(g0), f1 = raw ? 1.f : inv * w.y * sigmoid(g1);
+        const float f2 = raw ? 1.f : inv * w.z * sigmoid(g2), f3 = raw ? 1.f : inv * w.w * sigmoid(g3);
+        const float4 y = make_float4(x.x * f0, x.y * f1, x.z * f2, x.w * f3);
         if (FULL || row < m) put4(out + row * ts + col, y);
     }
 }
@@ -306,6 +308,11 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
     // writes of the next. The output tile reuses the S^T buffer that the
     // inter-block product just finished reading (it is rewritten only after the
     // next barrier B).
+    // norm-gate on a local-start segment g >= 1: the sub-blocks of its first
+    // raw_rows rows store the raw output to y (the epilogue's scale replaced
+    // by 1, a select rather than a second store path), which the correction
+    // pass finishes
+    const long long raw_rows = NG && fix && g > 0 ? ng_fix_rows(s2, seg_len, len) : 0;
     auto step = [&](long long c, int m, auto full, Stage<true> &st) {
         constexpr bool FULL = decltype(full)::value;
         st.template store<FULL>(Qs, Ks, Vs, Vds, m, s2, tid);
@@ -364,7 +371,8 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
         __syncthreads();  // (D)
         if constexpr (NG)
             store_rows_norm_gate<FULL>(og + c * C * (long long)ts, ts, Os, Rss, m, tid, gr,
-                                       *reinterpret_cast<const float4 *>(Wn + 4 * (tid & 31)), a.ng.eps);
+                                       *reinterpret_cast<const float4 *>(Wn + 4 * (tid & 31)), a.ng.eps,
+                                       c * C < raw_rows);
         else
             store_rows<FULL>(og + c * C * (long long)ts, ts, Os, m, tid);
         cur ^= 1;
@@ -718,14 +726,26 @@ struct OutRows<__bf16> {
 // One chunk of the correction: rows [t0, t0 + m) of segment g of pair `pair`.
 template <typename OutT>
 struct FixChunk {
-    const uint16_t *q;
+    const uint16_t *q, *gate;
     OutT *o;
     long long t0;
-    int m, pair, uh, g;
+    int m, pair, uh, g, h;
     float s2;
 };
 
-template <typename OutT>
+// Rows a correction pass treats in segment g of a local-start head (the chunk
+// count and the chunk contents must agree on it).
+template <bool NG>
+__device__ __forceinline__ long long fix_rows(float s2, long long seg_len, long long len) {
+    if constexpr (NG) {
+        return ng_fix_rows(s2, seg_len, len);
+    } else {
+        const long long fl = fix_len(s2, seg_len);
+        return fl < len ? fl : len;
+    }
+}
+
+template <typename OutT, bool NG>
 __device__ __forceinline__ FixChunk<OutT> fix_chunk(const PrefillArgs &a, const Segmented &sp,
                                                     const long long *first, long long j, int &p) {
     while (first[p + 1] <= j) ++p;
@@ -736,21 +756,67 @@ __device__ __forceinline__ FixChunk<OutT> fix_chunk(const PrefillArgs &a, const 
     x.uh = p / gs;
     x.g = 1 + p % gs;
     const int h = x.uh % a.heads, n = x.uh / a.heads;
+    x.h = h;
     x.s2 = a.slopes[h] * LOG2E;
-    const long long len = seg_len_at(sp, a.seqlen, x.g), fl = fix_len(x.s2, sp.seg_len);
-    const long long T = fl < len ? fl : len;
+    const long long T = fix_rows<NG>(x.s2, sp.seg_len, seg_len_at(sp, a.seqlen, x.g));
     x.t0 = uniform64((j - first[p]) * C);
     x.m = (int)(T - x.t0 < C ? T - x.t0 : C);
     const long long row = (long long)n * a.seqlen + (long long)x.g * sp.seg_len + x.t0;
     const long long off = (row * a.heads + h) * (long long)D;
     x.q = static_cast<const uint16_t *>(a.q) + off;
+    x.gate = NG ? static_cast<const uint16_t *>(a.ng.gate) + off : nullptr;
     x.o = static_cast<OutT *>(a.o) + off;
     return x;
 }
 
+// Norm-gate correction rows: the raw output the main pass left in y, and the
+// gate, for rows (tid/32) + 16j, columns 4(tid%32)..+3 (the epilogue's layout).
+// finish() adds the staged correction, normalises each row (its 32 lanes
+// reduce the sum of squares), gates, and stores y.
+template <typename OutT>
+struct NgRows {
+    using Raw = typename std::conditional<sizeof(OutT) == 4, uint4, uint2>::type;
+    Raw y[4];
+    uint2 gt[4];
+    __device__ void load(const OutT *out, const uint16_t *gate, int ts, int m, int tid) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = (tid >> 5) + 16 * j;
+            const unsigned off = (unsigned)((row < m ? row : m - 1) * ts + 4 * (tid & 31));
+            y[j] = *reinterpret_cast<const Raw *>(out + off);
+            gt[j] = stream_load8(gate + off);
+        }
+    }
+    __device__ static float4 raw4(const uint4 &x) {
+        return make_float4(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w));
+    }
+    __device__ static float4 raw4(const uint2 &x) {
+        return make_float4(__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u),
+                           __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u));
+    }
+    __device__ void finish(OutT *out, int ts, const float *Os, int m, int tid, float4 w, float eps) const {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = (tid >> 5) + 16 * j, col = 4 * (tid & 31);
+            const float4 x = *reinterpret_cast<const float4 *>(Os + ooff(row, col));
+            const float4 r = raw4(y[j]);
+            const float4 o = make_float4(r.x + x.x, r.y + x.y, r.z + x.z, r.w + x.w);
+            float ss = o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
+#pragma unroll
+            for (int k = 16; k >= 1; k >>= 1) ss += __shfl_xor(ss, k);
+            const float inv = __builtin_amdgcn_rsqf(ss * (1.f / D) + eps);
+            const float g0 = __uint_as_float(gt[j].x << 16), g1 = __uint_as_float(gt[j].x & 0xffff0000u);
+            const float g2 = __uint_as_float(gt[j].y << 16), g3 = __uint_as_float(gt[j].y & 0xffff0000u);
+            const float4 yv = make_float4(o.x * inv * w.x * sigmoid(g0), o.y * inv * w.y * sigmoid(g1),
+                                          o.z * inv * w.z * sigmoid(g2), o.w * inv * w.w * sigmoid(g3));
+            if (row < m) put4(out + (unsigned)(row * ts + col), yv);
+        }
+    }
+};
+
 // Two workgroups per CU: 128 registers per lane, and the Q tile shares its
 // LDS with the staged output (66 KB per workgroup).
-template <typename OutT>
+template <typename OutT, bool NG>
 __global__ __launch_bounds__(NT, 4) void fix_kernel(PrefillArgs a, Segmented sp, float *ws, int nfinal) {
     __shared__ __attribute__((aligned(16))) __bf16 Sts[D * D];
     __shared__ __attribute__((aligned(16))) float Os[C * D];
@@ -782,10 +848,7 @@ __global__ __launch_bounds__(NT, 4) void fix_kernel(PrefillArgs a, Segmented sp,
     if (tid < pairs) {
         const int g = 1 + tid % gs;
         const float s2 = a.slopes[(tid / gs) % a.heads] * LOG2E;
-        if (fix_head(s2, sp.seg_len, sp.fix_osz)) {
-            const long long len = seg_len_at(sp, a.seqlen, g), fl = fix_len(s2, sp.seg_len);
-            x = ((fl < len ? fl : len) + C - 1) / C;
-        }
+        if (fix_head(s2, sp.seg_len, sp.fix_osz)) x = (fix_rows<NG>(s2, sp.seg_len, seg_len_at(sp, a.seqlen, g)) + C - 1) / C;
     }
     for (int off = 1; off < kFixMaxPairs; off <<= 1) {
         if (tid < kFixMaxPairs) first[tid + 1] = x;
@@ -815,12 +878,19 @@ __global__ __launch_bounds__(NT, 4) void fix_kernel(PrefillArgs a, Segmented sp,
             qx[i] = stream_load16(c.q + (unsigned)((t < c.m ? t : c.m - 1) * ts + 8 * (th & 15)));
         }
     };
+    using Rows = typename std::conditional<NG, NgRows<OutT>, OutRows<OutT>>::type;
+    auto load_rows = [&](Rows &r, const FixChunk<OutT> &c, int th) {
+        if constexpr (NG)
+            r.load(c.o, c.gate, ts, c.m, th);
+        else
+            r.load(c.o, ts, c.m, th);
+    };
     int p = 0;
-    FixChunk<OutT> cur = fix_chunk<OutT>(a, sp, first, j0, p);
+    FixChunk<OutT> cur = fix_chunk<OutT, NG>(a, sp, first, j0, p);
     uint4 qa[2];
-    OutRows<OutT> ra;
+    Rows ra;
     load_q(cur, qa, tid);
-    ra.load(cur.o, ts, cur.m, tid);
+    load_rows(ra, cur, tid);
     int loaded = -1;
     for (long long j = j0; j < j1; ++j) {
         if (j > j0) __syncthreads();  // the previous chunk's reads of Os (= Qs) done
@@ -834,11 +904,11 @@ __global__ __launch_bounds__(NT, 4) void fix_kernel(PrefillArgs a, Segmented sp,
         // the next chunk's loads go out before anything waits for this one's
         FixChunk<OutT> nxt = cur;
         uint4 qb[2] = {qa[0], qa[1]};
-        OutRows<OutT> rb = ra;
+        Rows rb = ra;
         if (j + 1 < j1) {
-            nxt = fix_chunk<OutT>(a, sp, first, j + 1, p);
+            nxt = fix_chunk<OutT, NG>(a, sp, first, j + 1, p);
             load_q(nxt, qb, tl);
-            rb.load(nxt.o, ts, nxt.m, tl);
+            load_rows(rb, nxt, tl);
         }
         if (cur.pair != loaded) {
             // S_in(g) of this pair as bf16 S^T: the thread with value column
@@ -892,7 +962,11 @@ __global__ __launch_bounds__(NT, 4) void fix_kernel(PrefillArgs a, Segmented sp,
         __syncthreads();  // every read of Qs and Sts done
         stage_out(Os, o, qh, cq, ln);
         __syncthreads();  // Os visible
-        ra.add_store(cur.o, ts, Os, cur.m, tl);
+        if constexpr (NG)
+            ra.finish(cur.o, ts, Os, cur.m, tl,
+                      *reinterpret_cast<const float4 *>(a.ng.norm_weight + cur.h * D + 4 * (tl & 31)), a.ng.eps);
+        else
+            ra.add_store(cur.o, ts, Os, cur.m, tl);
         cur = nxt;
         qa[0] = qb[0];
         qa[1] = qb[1];
@@ -911,9 +985,11 @@ hipError_t launch(const PrefillArgs &a, const PrefillPlan &p, void *workspace, h
         return hipGetLastError();
     }
     float *ws = static_cast<float *>(workspace);
-    // heads may take local-start segments unless the epilogue needs the whole
-    // output (norm-gate)
-    const int fix_osz = p.segments > 1 && !a.ng.gate ? (int)sizeof(OutT) : 0;
+    // heads may take local-start segments; the correction's extra traffic per
+    // token is, in units of 256 B, 1 + sizeof(OutT): q read and the output row
+    // read and written (with the norm-gate epilogue the gate is read by the
+    // correction pass instead of the main pass)
+    const int fix_osz = p.segments > 1 ? (int)sizeof(OutT) : 0;
     const Segmented sp{p.segments, p.pieces, p.seg_len, p.piece_len, fix_osz};
     if (p.segments > 1) {
         hipLaunchKernelGGL(piece_state_kernel, dim3((unsigned)(uh * p.pieces)), dim3(NT), 0, stream,
@@ -936,8 +1012,12 @@ hipError_t launch(const PrefillArgs &a, const PrefillPlan &p, void *workspace, h
     if (e != hipSuccess) return e;
     if (uh * (p.segments - 1) > kFixMaxPairs) return hipErrorInvalidValue;  // not a segmented plan
     const int nfinal = a.state_out ? (int)(uh * kFinalSlices) : 0;
-    hipLaunchKernelGGL((fix_kernel<OutT>), dim3((unsigned)(nfinal + kFixWorkgroups)), dim3(NT), 0, stream, a, sp,
-                       ws, nfinal);
+    if (a.ng.gate)
+        hipLaunchKernelGGL((fix_kernel<OutT, true>), dim3((unsigned)(nfinal + kFixWorkgroups)), dim3(NT), 0, stream,
+                           a, sp, ws, nfinal);
+    else
+        hipLaunchKernelGGL((fix_kernel<OutT, false>), dim3((unsigned)(nfinal + kFixWorkgroups)), dim3(NT), 0, stream,
+                           a, sp, ws, nfinal);
     return hipGetLastError();
 }
 

@@ -303,6 +303,14 @@ __device__ __forceinline__ long long fix_len(float s2, long long seg_len) {
     const float t = kFixExp / s2;
     return t >= (float)seg_len ? seg_len : (long long)t;
 }
+// With the norm-gate epilogue the main pass leaves the raw output of a
+// segment's first rows in y (in y's type) and the correction pass finishes them
+// (adds the carried-in term, normalises, gates): fix_len rounded up to whole
+// pairs of 64-token sub-blocks, at most the segment's length.
+__device__ __forceinline__ long long ng_fix_rows(float s2, long long seg_len, long long len) {
+    const long long r = (fix_len(s2, seg_len) + 127) / 128 * 128;
+    return r < len ? r : len;
+}
 __device__ __forceinline__ bool fix_head(float s2, long long seg_len, int osz) {
     if (osz <= 0 || !(s2 > 0.f)) return false;
     const long long n = fix_len(s2, seg_len);

@@ -180,10 +180,11 @@ def test_decode_norm_gate_bf16_output(la):
 
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_prefill_norm_gate_segmented_slope_mix(la, out_dtype):
-    """Norm-gate prefill of the segmented plan over a slope mix (0, 1e-6, 0.02,
-    0.2, 1, 30): the epilogue needs each row's whole output, so every head takes
-    the pre-pass route whatever its decay, including those that take local
-    starts in a plain prefill. Carried-in state updated in place."""
+    """Norm-gate prefill of the segmented plan over heads on both routes: the
+    short-memory heads (0.02, 0.2, 1, 30) start every segment from zero, leave
+    the raw output of their first rows in y, and the correction pass adds the
+    carried-in term, normalises and gates those rows; 0 and 1e-6 take the
+    pre-pass. Carried-in state updated in place."""
     import torch
 
     L, H = 9000, 6
