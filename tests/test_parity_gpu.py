@@ -412,3 +412,24 @@ def test_prefill_segmented_slope_mix(la, out_dtype):
     es = max_rel_states(to_host_f32(st), s_ref)
     print(f"[result] o {eo:.3e} state {es:.3e}", flush=True)
     assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)
+
+
+def test_prefill_segmented_local_starts_no_final_state(la):
+    """Segmented plan over local-start heads with no final state requested
+    (the correction pass writes no state) and a carried-in state."""
+    import torch
+
+    L, H = 9000, 4
+    sl = np.array([0.02, 0.2, 1.0, 30.0], np.float32)
+    print(f"[case] segmented local starts, no state_out, L={L} slopes={list(sl)}", flush=True)
+    q, k, v = workloads.qkv_host(2311, (1, L, H, 128), "bf16")
+    s0 = workloads.state_host(2312, (1, H, 128, 128))
+    o, st = la.lt_prefill(*(to_device(x, "bf16") for x in (q, k, v)), torch.from_numpy(sl).cuda(), 256,
+                          torch.from_numpy(s0).cuda(), want_state=False)
+    torch.cuda.synchronize()
+    assert st is None
+    o_ref, _ = oracle.recurrence_batch(q, k, v, sl, s0=s0)
+    og = to_host_f32(o)
+    eo = max(rel_l2(og[0, :, h], o_ref[0, :, h]) for h in range(H))
+    print(f"[result] o {eo:.3e}", flush=True)
+    assert eo <= TOL_BF16, eo

@@ -207,3 +207,29 @@ def test_prefill_norm_gate_segmented_slope_mix(la, out_dtype):
     es = max_rel_states(to_host_f32(st), s_ref)
     print(f"[result] y {ey:.3e} state {es:.3e}", flush=True)
     assert ey <= TOL_BF16 and es <= TOL_BF16, (ey, es)
+
+
+def test_prefill_norm_gate_segmented_no_final_state(la):
+    """Segmented norm-gate prefill over local-start heads with no final state
+    requested: the correction pass still finishes every parked row."""
+    import torch
+
+    L, H = 9000, 4
+    sl = np.array([0.02, 0.2, 1.0, 30.0], np.float32)
+    print(f"[case] norm-gate segmented, no state_out, L={L} slopes={list(sl)}", flush=True)
+    q, k, v = workloads.qkv_host(2411, (1, L, H, 128), "bf16")
+    gate = workloads.gate_host(2412, (1, L, H, 128), "bf16")
+    w = workloads.norm_weight_host(2413, H)
+    s0 = workloads.state_host(2414, (1, H, 128, 128))
+    y, st = la.lt_prefill_norm_gate(to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16"),
+                                    torch.from_numpy(sl).cuda(), to_device(gate, "bf16"),
+                                    torch.from_numpy(w).cuda(), EPS, 256, torch.from_numpy(s0).cuda(),
+                                    want_state=False, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert st is None
+    o_ref, _ = oracle.recurrence_batch(q, k, v, sl, s0=s0)
+    y_ref = oracle.norm_gate(o_ref, gate, w, EPS)
+    yg = to_host_f32(y)
+    ey = max(rel_l2(yg[0, :, h], y_ref[0, :, h]) for h in range(H))
+    print(f"[result] y {ey:.3e}", flush=True)
+    assert ey <= TOL_BF16, ey
