@@ -139,7 +139,7 @@ def run_prefill(la, torch, steps, warmup):
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "bytes_per_launch": bytes_alg,
                      "kernel": "lt_prefill call: piece_state_kernel + combine_kernel + head_kernel<float> "
-                               "+ fix_kernel<float>"},
+                               "+ fix_kernel<float, false>"},
     }
 
 
@@ -548,7 +548,7 @@ def traffic_from(copy_dir, fetch_dir, write_dir, copy_bytes):
     # calls: the norm-gate call and the backward's dq pass plan their pre-pass
     # differently)
     kernels = [k for k in kf if any(n in k for n in ("head_kernel<float, false>", "piece_state_kernel",
-                                                      "combine_kernel", "fix_kernel<float>"))]
+                                                      "combine_kernel", "fix_kernel<float, false>"))]
     import numpy as np
 
     fetch = sum(float(np.median(kf[k])) for k in kernels) * 1024 * f_scale
