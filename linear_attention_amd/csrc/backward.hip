@@ -191,23 +191,28 @@ __global__ __launch_bounds__(NT, 4) void rev_piece_kernel(BackwardArgs a, Segmen
     __shared__ __attribute__((aligned(16))) __bf16 Qds[C * D];
     __shared__ __attribute__((aligned(16))) __bf16 Gs[C * D];
 
-    const int j = blockIdx.x % sp.pieces;
-    const int uh = blockIdx.x / sp.pieces;
+    // groups of kgr pieces, numbered as in the forward pre-pass
+    const int kgr = prepass_group(a.slopes, a.heads, a.units, sp);
+    const int gph = (sp.pieces + kgr - 1) / kgr;
+    if ((int)blockIdx.x >= a.units * a.heads * gph) return;
+    const int j = (blockIdx.x % gph) * kgr;
+    const int uh = blockIdx.x / gph;
     const int h = uh % a.heads, n = uh / a.heads;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int qh = w >> 2, cq = w & 3, r32 = lane & 31, hf = lane >> 5;
 
+    const float s2 = a.slopes[h] * LOG2E;
+    if (fix_head(s2, sp.seg_len, sp.fix_osz)) return;  // local-start segments: no pre-pass
+    const int jl = j + kgr - 1 < sp.pieces - 1 ? j + kgr - 1 : sp.pieces - 1;
     // mirrored range [t0, t1) = real tokens [L - t1, L - t0)
     const long long L = a.seqlen;
     const long long t0 = j * sp.piece_len;
-    const long long t1 = t0 + sp.piece_len < sp.covered() ? t0 + sp.piece_len : sp.covered();
+    const long long t1 = t0 + kgr * sp.piece_len < sp.covered() ? t0 + kgr * sp.piece_len : sp.covered();
     const int ts = a.heads * D;
     const long long seq = (long long)n * L * a.heads;
     const uint16_t *qg = static_cast<const uint16_t *>(a.q) + (seq + h) * (long long)D;
     const uint16_t *gg = static_cast<const uint16_t *>(a.dout) + (seq + h) * (long long)D;
-    const float s2 = a.slopes[h] * LOG2E;
-    if (fix_head(s2, sp.seg_len, sp.fix_osz)) return;  // local-start segments: no pre-pass
     float *u = sp.unit(ws, uh);
 
     f32x16 R[2];
@@ -253,9 +258,9 @@ __global__ __launch_bounds__(NT, 4) void rev_piece_kernel(BackwardArgs a, Segmen
     const long long b = gb * sp.seg_len;
     const long long cb = b < t1 ? (b - t0) / C : nch;
     run(0, cb);
-    store_state(b < t1 ? sp.partial_slot(gb) : j);
+    store_state(b < t1 ? sp.partial_slot(gb) : jl);
     run(cb, nch);
-    store_state(j);
+    store_state(jl);
 }
 
 template <typename OutT>

@@ -50,10 +50,12 @@ lt_status map_hip(hipError_t e) {
 constexpr long long kTargetWorkgroups = 256;
 // Shortest segment worth a workgroup of its own.
 constexpr long long kMinSegment = 2048;
-// Pre-pass workgroups to aim for. Heads with a short memory take local-start
-// segments and skip the pre-pass, so the few that remain get more, shorter
-// pieces (measured on the M1 layer when 7 of its 64 heads took the pre-pass:
-// 512 -> 661 us, 1024 -> 643 us, 2048 -> 608 us per call).
+// Pre-pass pieces to plan for (the pieces cover the first G-1 segments of
+// every head; heads on local-start segments skip them, and when many heads do
+// take the pre-pass the kernels merge consecutive pieces into groups so that
+// about 512 workgroups work). Fine pieces suit the case of few pre-pass heads
+// (measured on the M1 layer when 7 of its 64 heads took it: 512 -> 661 us,
+// 1024 -> 643 us, 2048 -> 608 us per call).
 constexpr long long kPrepassWide = 2048;
 // Shortest pre-pass piece.
 constexpr long long kMinPiece = 512;

@@ -93,28 +93,37 @@ __device__ __forceinline__ void store_rows_norm_gate(OutT *out, long long ts, co
 }
 
 // Pre-pass: workgroup (unit, head, piece j) runs the state update over the
-// piece's full 64-token sub-blocks without outputs, writing P_j and, if a
-// segment boundary falls strictly inside the piece, B_g on the way.
+// full 64-token sub-blocks of its group of pieces without outputs, writing its
+// state and, if a segment boundary falls strictly inside the group, B_g on the
+// way.
 __global__ __launch_bounds__(NT, 4) void piece_state_kernel(PrefillArgs a, Segmented sp, float *ws) {
     __shared__ __attribute__((aligned(16))) __bf16 Ks[C * D];
     __shared__ __attribute__((aligned(16))) __bf16 Vds[C * D];
 
-    const int j = blockIdx.x % sp.pieces;
-    const int uh = blockIdx.x / sp.pieces;
+    // workgroup b takes group b % gph of (unit, head) b / gph, gph groups of
+    // kgr pieces per head; the working workgroups are the first U * gph, which
+    // the hardware spreads over all XCDs. The group's state goes to the slot
+    // of its last piece.
+    const int kgr = prepass_group(a.slopes, a.heads, a.units, sp);
+    const int gph = (sp.pieces + kgr - 1) / kgr;
+    if ((int)blockIdx.x >= a.units * a.heads * gph) return;
+    const int j = (blockIdx.x % gph) * kgr;
+    const int uh = blockIdx.x / gph;
     const int h = uh % a.heads, n = uh / a.heads;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int qh = w >> 2, cq = w & 3, r32 = lane & 31, hf = lane >> 5;
 
+    const float s2 = a.slopes[h] * LOG2E;
+    if (fix_head(s2, sp.seg_len, sp.fix_osz)) return;  // local-start segments: no pre-pass
+    const int jl = j + kgr - 1 < sp.pieces - 1 ? j + kgr - 1 : sp.pieces - 1;
     const long long t0 = j * sp.piece_len;
-    const long long t1 = t0 + sp.piece_len < sp.covered() ? t0 + sp.piece_len : sp.covered();
+    const long long t1 = t0 + kgr * sp.piece_len < sp.covered() ? t0 + kgr * sp.piece_len : sp.covered();
     const SeqRange sr = sequence_of(a, n);
     const int ts = a.heads * D;
     const long long base = ((sr.start + t0) * a.heads + h) * (long long)D;
     const uint16_t *kg = static_cast<const uint16_t *>(a.k) + base;
     const uint16_t *vg = static_cast<const uint16_t *>(a.v) + base;
-    const float s2 = a.slopes[h] * LOG2E;
-    if (fix_head(s2, sp.seg_len, sp.fix_osz)) return;  // local-start segments: no pre-pass
     float *u = sp.unit(ws, uh);
 
     f32x16 S[2];
@@ -169,9 +178,9 @@ __global__ __launch_bounds__(NT, 4) void piece_state_kernel(PrefillArgs a, Segme
     const long long b = gb * sp.seg_len;
     const long long cb = b < t1 ? (b - t0) / C : nch;
     run(0, cb);
-    store_state(b < t1 ? sp.partial_slot(gb) : j);
+    store_state(b < t1 ? sp.partial_slot(gb) : jl);
     run(cb, nch);
-    store_state(j);
+    store_state(jl);
 }
 
 // ---------------------------------------------------------------------------

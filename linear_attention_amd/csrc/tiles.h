@@ -332,12 +332,31 @@ struct Segmented {
     __device__ float *start_state(float *u, int g) const { return slot(u, pieces + segments - 1 + g); }
 };
 
+// Pre-pass grouping. The plan cuts the first G-1 segments of every head into
+// many short pieces, which is right when few heads take the pre-pass; when
+// many do, a workgroup takes k consecutive pieces of a head (writing one state,
+// in the slot of the group's last piece), so that about kPrepassActive
+// workgroups work and the combine walks fewer, larger states. Every kernel
+// derives k from the slopes with this function (a workgroup-wide count, one
+// head per thread: segmented plans have fewer than 256 heads; every thread of
+// the workgroup must call it). A group never exceeds one segment, so it holds
+// at most one segment boundary strictly inside.
+constexpr int kPrepassActive = 512;
+__device__ inline int prepass_group(const float *slopes, int heads, int units, const Segmented &sp) {
+    const int t = threadIdx.x;
+    const int npre = __syncthreads_count(t < heads && !fix_head(slopes[t] * LOG2E, sp.seg_len, sp.fix_osz));
+    long long k = ((long long)units * npre * sp.pieces + kPrepassActive - 1) / kPrepassActive;
+    const long long kmax = sp.seg_len / sp.piece_len;
+    if (k > kmax) k = kmax;
+    return k < 1 ? 1 : (int)k;
+}
+
 // Combine pass: the state at every segment start, S_0 being the first state
 // (the carried-in state, or zero). Workgroup (unit, head, 1024-element slice) walks the pieces
-// in order with 4 elements per thread:
+// (groups of pieces, above) in order with 4 elements per thread:
 //   acc <- e^{-s len_j} acc + P_j,
-// and at each boundary b_g: S_g = acc if b_g ends piece j, or
-// e^{-s(b_g - start_j)} acc + B_g if it falls inside piece j.
+// and at each boundary b_g: S_g = acc if b_g ends group j, or
+// e^{-s(b_g - start_j)} acc + B_g if it falls inside group j.
 constexpr int kCombineThreads = 256;
 constexpr int kCombineSlices = D * D / (4 * kCombineThreads);
 
@@ -363,20 +382,23 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float *s
     }
     *reinterpret_cast<float4 *>(sp.start_state(u, 0) + e) = acc;
     const long long covered = sp.covered();
-    // the piece states are independent loads: issue a batch of them ahead of
+    const int kg = prepass_group(slopes, heads, (int)(gridDim.x / kCombineSlices) / heads, sp);
+    const int groups = (sp.pieces + kg - 1) / kg;
+    auto last_piece = [&](int j) { return (j + 1) * kg - 1 < sp.pieces - 1 ? (j + 1) * kg - 1 : sp.pieces - 1; };
+    // the group states are independent loads: issue a batch of them ahead of
     // the sequential accumulation (this kernel never writes piece slots)
     constexpr int kBatch = 8;
-    for (int j0 = 0; j0 < sp.pieces; j0 += kBatch) {
+    for (int j0 = 0; j0 < groups; j0 += kBatch) {
         float4 pj[kBatch];
 #pragma unroll
         for (int i = 0; i < kBatch; ++i)
-            if (j0 + i < sp.pieces) pj[i] = *reinterpret_cast<const float4 *>(sp.piece_state(u, j0 + i) + e);
+            if (j0 + i < groups) pj[i] = *reinterpret_cast<const float4 *>(sp.piece_state(u, last_piece(j0 + i)) + e);
 #pragma unroll
         for (int i = 0; i < kBatch; ++i) {
             const int j = j0 + i;
-            if (j >= sp.pieces) break;
-            const long long t0 = j * sp.piece_len;
-            const long long t1 = t0 + sp.piece_len < covered ? t0 + sp.piece_len : covered;
+            if (j >= groups) break;
+            const long long t0 = (long long)j * kg * sp.piece_len;
+            const long long t1 = t0 + kg * sp.piece_len < covered ? t0 + kg * sp.piece_len : covered;
             const int gb = (int)(t0 / sp.seg_len) + 1;
             const long long b = gb * sp.seg_len;
             if (b < t1) {

@@ -130,3 +130,34 @@ def test_backward_segmented_slope_mix(la, grad_dtype):
     errs["ds0"] = max_rel_states(to_host_f32(dsi), rs)
     print(f"[result] {errs}", flush=True)
     assert max(errs.values()) <= TOL_BF16, errs
+
+
+def test_backward_prepass_groups(la):
+    """Backward with every head on both pre-passes (64 heads, slopes scaled by
+    1e-4; 20480 tokens: 30 pieces merged into groups of 4, the last of 2):
+    sampled heads against the oracle, with carried state and final-state
+    gradient."""
+    import torch
+
+    L, H = 20480, 64
+    sl = (workloads.slopes(H) * np.float32(1e-4)).astype(np.float32)
+    print(f"[case] backward pre-pass groups L={L} H={H}", flush=True)
+    q, k, v = workloads.qkv_host(2521, (1, L, H, 128), "bf16")
+    do = workloads.gate_host(2522, (1, L, H, 128), "bf16")
+    s0 = workloads.state_host(2523, (1, H, 128, 128))
+    ds = workloads.state_host(2524, (1, H, 128, 128))
+    dq, dk, dv, dsi = la.lt_prefill_backward(
+        to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16"), to_device(do, "bf16"),
+        torch.from_numpy(sl).cuda(), 256, torch.from_numpy(s0).cuda(), torch.from_numpy(ds).cuda())
+    torch.cuda.synchronize()
+    hs = [0, 5, 33, 63]
+    sub = lambda x: np.ascontiguousarray(x[:, :, hs])
+    rq, rk, rv, rs = oracle.backward_batch(sub(q), sub(k), sub(v), sub(do), np.ascontiguousarray(sl[hs]),
+                                           s0=np.ascontiguousarray(s0[:, hs]), ds=np.ascontiguousarray(ds[:, hs]))
+    errs = {}
+    for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        gh = to_host_f32(g)[:, :, hs]
+        errs[name] = max(rel_l2(gh[0, :, i], r[0, :, i]) for i in range(len(hs)))
+    errs["ds0"] = max_rel_states(to_host_f32(dsi)[:, hs], rs)
+    print(f"[result] {errs}", flush=True)
+    assert max(errs.values()) <= TOL_BF16, errs

@@ -433,3 +433,31 @@ def test_prefill_segmented_local_starts_no_final_state(la):
     eo = max(rel_l2(og[0, :, h], o_ref[0, :, h]) for h in range(H))
     print(f"[result] o {eo:.3e}", flush=True)
     assert eo <= TOL_BF16, eo
+
+
+@pytest.mark.parametrize("L", [16384, 20480])
+def test_prefill_prepass_groups(la, L):
+    """Many heads on the pre-pass (64 heads, slopes scaled by 1e-4, so no head
+    takes local starts): the kernels merge consecutive pre-pass pieces into
+    groups (L = 16384: 24 pieces of 512 in 8 groups of 3, boundaries inside
+    groups; L = 20480: 30 pieces in groups of 4, the last group of 2, a group
+    ending on a boundary). Carried-in state updated in place; sampled heads
+    against the oracle."""
+    import torch
+
+    H = 64
+    sl = (workloads.slopes(H) * np.float32(1e-4)).astype(np.float32)
+    print(f"[case] pre-pass groups L={L} H={H} slopes x1e-4", flush=True)
+    q, k, v = workloads.qkv_host(2321 + L, (1, L, H, 128), "bf16")
+    s0 = workloads.state_host(2322 + L, (1, H, 128, 128))
+    st = torch.from_numpy(s0).cuda()
+    o, _ = la.lt_prefill(*(to_device(x, "bf16") for x in (q, k, v)), torch.from_numpy(sl).cuda(), 256,
+                         st, state_out=st)
+    torch.cuda.synchronize()
+    hs = [0, 1, 17, 40, 63]
+    o_ref, s_ref = oracle.recurrence_batch(q, k, v, sl, s0=s0, heads=hs)
+    og = to_host_f32(o)[:, :, hs]
+    eo = max(rel_l2(og[0, :, i], o_ref[0, :, i]) for i in range(len(hs)))
+    es = max_rel_states(to_host_f32(st)[:, hs], s_ref)
+    print(f"[result] o {eo:.3e} state {es:.3e}", flush=True)
+    assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)
