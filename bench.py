@@ -94,7 +94,10 @@ def committed_traffic(bytes_alg):
     return t.get("traffic_bytes_per_launch")
 
 
-def run_prefill(la, torch, steps, warmup):
+def run_prefill(la, torch, steps, warmup, slope_scale=1.0):
+    """lt_prefill on the M1 layer. slope_scale multiplies every head's slope
+    (smaller slopes: longer memories, so more heads take the pre-pass instead
+    of local-start segments); 1 is the benchmark line."""
     import numpy as np
 
     import workloads
@@ -102,7 +105,7 @@ def run_prefill(la, torch, steps, warmup):
     w = workloads.M1_LAYER
     shape = (w.batch, w.seqlen, w.heads, w.head_dim)
     q, k, v = workloads.qkv_device(w.seed, shape, "bf16")
-    slopes = torch.from_numpy(workloads.slopes(w.heads)).cuda()
+    slopes = torch.from_numpy((workloads.slopes(w.heads) * np.float32(slope_scale)).astype(np.float32)).cuda()
     o = torch.empty(shape, device="cuda", dtype=torch.float32)
     st = torch.empty((w.batch, w.heads, D, D), device="cuda", dtype=torch.float32)
     stream = torch.cuda.current_stream()
@@ -634,6 +637,13 @@ def main():
     log("[bench] prefill m1_layer L=32768 H=64 d=128 block=256")
     w, dev_inputs, pre = run_prefill(la, torch, args.steps, args.warmup)
     log(f"[bench] prefill {pre['kernel_ms_mean']:.3f} ms/launch")
+    scaled = {}
+    for f in (0.1, 1e-5):
+        _, _, r = run_prefill(la, torch, 10, 2, slope_scale=f)
+        scaled[f"x{f:g}"] = {"kernel_ms_mean": round(r["kernel_ms_mean"], 5),
+                             "tokens_per_s": round(1e3 * w.batch * w.seqlen / r["kernel_ms_mean"], 1),
+                             "roofline_frac": r["roofline"]["frac"]}
+        log(f"[bench] prefill, slopes x{f:g}: {r['kernel_ms_mean']:.3f} ms/launch")
     dec = None
     if not args.no_decode:
         log(f"[bench] decode batch=256 H=64, {args.decode_steps} steps")
@@ -689,6 +699,9 @@ def main():
                    "out_dtype": "f32", "state_out": "f32"},
         "roofline": pre["roofline"],
         "kernel_ms_mean": round(pre["kernel_ms_mean"], 5),
+        # the same call with every slope scaled down (x0.1: 25 of the 64 heads
+        # take the pre-pass; x1e-5: all of them)
+        "prefill_slopes_scaled": scaled,
         "decode": dec,
         "norm_gate": ng,
         "backward": bwd,
