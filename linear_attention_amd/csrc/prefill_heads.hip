@@ -30,6 +30,11 @@
 //    contributed by fixed pieces of every segment but the last (the same state
 //    update without outputs) into a workspace; segment g starts from
 //    e^{-s*start_g} S_0 plus each piece's state decayed to start_g.
+//  * Heads whose decay ends their memory within a segment skip the pre-pass:
+//    their segments start from a zero state, and a correction pass adds the
+//    missed carried-in term e^{-s(t+1)} q_t S_in to each segment's first
+//    tokens (with the norm-gate epilogue the main kernel leaves those rows raw
+//    in y and the correction pass also normalises and gates them).
 //  * Outputs go through LDS and leave as whole rows (full 512-byte fp32 rows
 //    stream far better than the 32-byte pieces of the accumulator layout).
 //  * Shared building blocks (layouts, operand loads, staging, state update)
