@@ -161,3 +161,31 @@ def test_backward_prepass_groups(la):
     errs["ds0"] = max_rel_states(to_host_f32(dsi)[:, hs], rs)
     print(f"[result] {errs}", flush=True)
     assert max(errs.values()) <= TOL_BF16, errs
+
+
+def test_backward_segmented_batch_slope_mix(la):
+    """Segmented backward with several sequences (2 x 9000 tokens, 4 heads) over
+    heads on both routes of both passes, with carried state and final-state
+    gradient."""
+    import torch
+
+    B, L, H = 2, 9000, 4
+    sl = np.array([0.0, 0.01, 0.3, 4.0], np.float32)
+    print(f"[case] backward segmented batch={B} L={L} slopes={list(sl)}", flush=True)
+    q, k, v = workloads.qkv_host(2531, (B, L, H, 128), "bf16")
+    do = workloads.gate_host(2532, (B, L, H, 128), "bf16")
+    s0 = workloads.state_host(2533, (B, H, 128, 128))
+    ds = workloads.state_host(2534, (B, H, 128, 128))
+    assert la.lt_prefill_workspace_bytes(B, L, H) > 0
+    dq, dk, dv, dsi = la.lt_prefill_backward(
+        to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16"), to_device(do, "bf16"),
+        torch.from_numpy(sl).cuda(), 256, torch.from_numpy(s0).cuda(), torch.from_numpy(ds).cuda())
+    torch.cuda.synchronize()
+    rq, rk, rv, rs = oracle.backward_batch(q, k, v, do, sl, s0=s0, ds=ds)
+    errs = {}
+    for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        gh = to_host_f32(g)
+        errs[name] = max(rel_l2(gh[b, :, h], r[b, :, h]) for b in range(B) for h in range(H))
+    errs["ds0"] = max_rel_states(to_host_f32(dsi), rs)
+    print(f"[result] {errs}", flush=True)
+    assert max(errs.values()) <= TOL_BF16, errs

@@ -461,3 +461,26 @@ def test_prefill_prepass_groups(la, L):
     es = max_rel_states(to_host_f32(st)[:, hs], s_ref)
     print(f"[result] o {eo:.3e} state {es:.3e}", flush=True)
     assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)
+
+
+def test_prefill_segmented_batch_slope_mix(la):
+    """Segmented plan with several sequences (3 x 9000 tokens, 5 heads: 15
+    pairs, 5 segments each) over heads on both routes (pre-pass: 0, 1e-6;
+    local starts: 0.02, 0.3, 4), carried-in states, bf16 output."""
+    import torch
+
+    B, L, H = 3, 9000, 5
+    sl = np.array([0.0, 1e-6, 0.02, 0.3, 4.0], np.float32)
+    print(f"[case] segmented batch={B} L={L} slopes={list(sl)}", flush=True)
+    assert la.lt_prefill_workspace_bytes(B, L, H) > 0
+    q, k, v = workloads.qkv_host(2331, (B, L, H, 128), "bf16")
+    s0 = workloads.state_host(2332, (B, H, 128, 128))
+    o, st = la.lt_prefill(*(to_device(x, "bf16") for x in (q, k, v)), torch.from_numpy(sl).cuda(), 256,
+                          torch.from_numpy(s0).cuda(), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.recurrence_batch(q, k, v, sl, s0=s0)
+    og = to_host_f32(o)
+    eo = max(rel_l2(og[b, :, h], o_ref[b, :, h]) for b in range(B) for h in range(H))
+    es = max_rel_states(to_host_f32(st), s_ref)
+    print(f"[result] o {eo:.3e} state {es:.3e}", flush=True)
+    assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)
