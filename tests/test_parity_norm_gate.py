@@ -233,3 +233,28 @@ def test_prefill_norm_gate_segmented_no_final_state(la):
     ey = max(rel_l2(yg[0, :, h], y_ref[0, :, h]) for h in range(H))
     print(f"[result] y {ey:.3e}", flush=True)
     assert ey <= TOL_BF16, ey
+
+
+def test_prefill_norm_gate_segmented_batch(la):
+    """Segmented norm-gate prefill with several sequences (3 x 9000 tokens, 4
+    heads on both routes), carried-in states, fp32 y."""
+    import torch
+
+    B, L, H = 3, 9000, 4
+    sl = np.array([1e-6, 0.02, 0.3, 4.0], np.float32)
+    print(f"[case] norm-gate segmented batch={B} L={L} slopes={list(sl)}", flush=True)
+    q, k, v = workloads.qkv_host(2421, (B, L, H, 128), "bf16")
+    gate = workloads.gate_host(2422, (B, L, H, 128), "bf16")
+    w = workloads.norm_weight_host(2423, H)
+    s0 = workloads.state_host(2424, (B, H, 128, 128))
+    y, st = la.lt_prefill_norm_gate(to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16"),
+                                    torch.from_numpy(sl).cuda(), to_device(gate, "bf16"),
+                                    torch.from_numpy(w).cuda(), EPS, 256, torch.from_numpy(s0).cuda())
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.recurrence_batch(q, k, v, sl, s0=s0)
+    y_ref = oracle.norm_gate(o_ref, gate, w, EPS)
+    yg = to_host_f32(y)
+    ey = max(rel_l2(yg[b, :, h], y_ref[b, :, h]) for b in range(B) for h in range(H))
+    es = max_rel_states(to_host_f32(st), s_ref)
+    print(f"[result] y {ey:.3e} state {es:.3e}", flush=True)
+    assert ey <= TOL_BF16 and es <= TOL_BF16, (ey, es)
