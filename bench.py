@@ -601,6 +601,8 @@ def main():
     ap.add_argument("--no-norm-gate", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-softmax", action="store_true")
+    ap.add_argument("--no-slopes-scaled", action="store_true",
+                    help="skip the prefill runs with scaled-down slopes")
     ap.add_argument("--norm-gate-decode-steps", type=int, default=200)
     ap.add_argument("--workload", default="m1_layer",
                     choices=["m1_layer", "long_1m", "varlen", "tiny_f32"])
@@ -638,7 +640,7 @@ def main():
     w, dev_inputs, pre = run_prefill(la, torch, args.steps, args.warmup)
     log(f"[bench] prefill {pre['kernel_ms_mean']:.3f} ms/launch")
     scaled = {}
-    for f in (0.1, 1e-5):
+    for f in (() if args.no_slopes_scaled else (0.1, 1e-5)):
         _, _, r = run_prefill(la, torch, 10, 2, slope_scale=f)
         scaled[f"x{f:g}"] = {"kernel_ms_mean": round(r["kernel_ms_mean"], 5),
                              "tokens_per_s": round(1e3 * w.batch * w.seqlen / r["kernel_ms_mean"], 1),
