@@ -19,7 +19,8 @@
  * state does not depend on B: the block form is an exact re-association of the
  * per-token recurrence S <- e^{-s_h} S + k^T v, o = q S (the token sees its own
  * key). The kernels may leave out a carried-state term once its decay factor
- * e^{-s t} is below 2^-32 (far below fp32 resolution of the output).
+ * e^{-s t} is below 2^-24 (the unit roundoff of fp32, and far below the bf16
+ * rounding of the products' operands).
  * lt_prefill, lt_prefill_varlen and lt_decode write the raw sum; the
  * *_norm_gate variants also apply the normalisation and gate that follow the
  * sum in the §03 data-flow figure before anything is stored.

@@ -461,7 +461,8 @@ __global__ __launch_bounds__(NT) void bwd_kv_kernel(BackwardArgs a, Segmented sp
 // of it, n = seg_hi - 1 - t tokens before its right end, misses e^{-s n} R_in in
 // its gradient of S_t:
 //   dv_t += e^{-s n} k_t R_in,    dk_t += e^{-s n} v_t R_in^T,
-// added here for n <= kFixExp / s2 (smaller terms are below fp32 resolution),
+// added here for n <= kFixExp / s2 (past that the factor is below the fp32
+// unit roundoff, 2^-24),
 // in 64-token chunks counted from the right end, kRevFixParts workgroups per
 // (unit, head, segment). The products are the forward correction's (the carry,
 // or its transpose, as a bf16 S^T tile on MFMA).

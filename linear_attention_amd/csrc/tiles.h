@@ -286,8 +286,10 @@ __device__ __forceinline__ SeqRange sequence_of(const PrefillArgs &a, int n) {
 // its true start state S_in misses, at its token t (t = 0, 1, ...), the term
 // e^{-s(t+1)} q_t S_in. With s2 = s log2(e) that factor is below 2^-kFixExp once
 // t + 1 > kFixExp / s2: a correction pass adds the term to the first
-// fix_len = min(segment, kFixExp / s2) tokens and leaves the rest (2^-32 of the
-// term's own scale is below fp32 resolution of the output). A head takes this
+// fix_len = min(segment, kFixExp / s2) tokens and leaves the rest: past them
+// the term is below 2^-24 of its own scale at the segment start, the unit
+// roundoff of fp32 (and 2^15 times below the rounding of the bf16 operands
+// every product of the path already carries). A head takes this
 // route when its decay cuts the term off inside the segment and re-reading q
 // and o for fix_len tokens costs at most twice the HBM traffic of the pre-pass
 // re-read of the whole segment's k and v:
@@ -296,9 +298,9 @@ __device__ __forceinline__ SeqRange sequence_of(const PrefillArgs &a, int n) {
 // 2 is measured: the pre-pass of the few heads that still need it runs far
 // below the bandwidth the correction pass reaches, and the pre-pass and combine
 // launches are dependent steps ahead of the main kernel (M1 layer, 64 heads,
-// 32,768 tokens: with factor 1, 57 heads correct and 7 take the pre-pass,
-// 0.574 ms; with factor 2 all 64 correct, 0.557 ms).
-constexpr float kFixExp = 32.f;
+// 32,768 tokens, with a 2^-32 cutoff: with factor 1, 57 heads correct and 7
+// take the pre-pass, 0.574 ms; with factor 2 all 64 correct, 0.557 ms).
+constexpr float kFixExp = 24.f;
 __device__ __forceinline__ long long fix_len(float s2, long long seg_len) {
     const float t = kFixExp / s2;
     return t >= (float)seg_len ? seg_len : (long long)t;

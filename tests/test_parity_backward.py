@@ -102,12 +102,10 @@ def test_backward_long_sequence_without_workspace(la):
 @pytest.mark.parametrize("grad_dtype", ["f32", "bf16"])
 def test_backward_segmented_slope_mix(la, grad_dtype):
     """Segmented backward over heads on both routes of both passes: short-memory
-    heads (slopes 0.2, 1, 30) on local-start segments with the carried-in terms
-    added afterwards (30: only the last token of each reverse segment), 0 and
-    1e-6 on the pre-passes, 0.02 (1,109 corrected tokens of 2,304) local in the
-    dq pass and, by the correction's cost, on the reverse pre-pass with fp32
-    gradients and local with bf16 ones; carried-in state and final-state
-    gradient."""
+    heads (slopes 0.02, 0.2, 1, 30) on local-start segments with the carried-in
+    terms added afterwards (0.02: 831 corrected tokens of 2,304; 30: only the
+    last token of each reverse segment), 0 and 1e-6 on the pre-passes; carried-in
+    state and final-state gradient."""
     import torch
 
     L, H = 9000, 6

@@ -390,8 +390,8 @@ def test_prefill_segmented_slope_mix(la, out_dtype):
     """Segmented plan (4 segments of 2,304 tokens) over heads whose decay sends
     them down both routes: heads with a short memory start every segment from
     zero and get the carried-in term added to their first tokens afterwards
-    (slopes 0.02, 0.2, 1, 30: 1,109 corrected tokens down to none at all), heads
-    with a long one (0, 1e-6, 0.005: 4,436 tokens, past the segment) take the
+    (slopes 0.02, 0.2, 1, 30: 831 corrected tokens down to none at all), heads
+    with a long one (0, 1e-6, 0.005: 3,327 tokens, past the segment) take the
     pre-pass; with a carried-in state updated in place."""
     import torch
 
