@@ -339,14 +339,19 @@ struct Segmented {
 // many do, a workgroup takes k consecutive pieces of a head (writing one state,
 // in the slot of the group's last piece), so that about kPrepassActive
 // workgroups work and the combine walks fewer, larger states. Every kernel
-// derives k from the slopes with this function (a workgroup-wide count, one
-// head per thread: segmented plans have fewer than 256 heads; every thread of
-// the workgroup must call it). A group never exceeds one segment, so it holds
-// at most one segment boundary strictly inside.
+// derives k from the slopes with this function (each wave counts the heads on
+// the pre-pass itself, 64 at a time by ballot, so no barrier is needed). A
+// group never exceeds one segment, so it holds at most one segment boundary
+// strictly inside.
 constexpr int kPrepassActive = 512;
 __device__ inline int prepass_group(const float *slopes, int heads, int units, const Segmented &sp) {
-    const int t = threadIdx.x;
-    const int npre = __syncthreads_count(t < heads && !fix_head(slopes[t] * LOG2E, sp.seg_len, sp.fix_osz));
+    const int lane = threadIdx.x & 63;
+    int npre = 0;
+    for (int h0 = 0; h0 < heads; h0 += 64) {
+        const int h = h0 + lane;
+        npre += __popcll(__ballot(h < heads && !fix_head(slopes[h < heads ? h : 0] * LOG2E, sp.seg_len, sp.fix_osz)));
+    }
+    npre = __builtin_amdgcn_readfirstlane(npre);
     long long k = ((long long)units * npre * sp.pieces + kPrepassActive - 1) / kPrepassActive;
     const long long kmax = sp.seg_len / sp.piece_len;
     if (k > kmax) k = kmax;
