@@ -119,7 +119,9 @@ LT_API lt_status lt_prefill(const void *q, const void *k, const void *v, lt_dtyp
  * the GPU with one workgroup per sequence and head; holds one fp32 d x d state
  * per sequence, head and sequence piece). Returns 0 when no workspace helps or
  * the arguments are invalid. lt_prefill given a NULL or smaller workspace still
- * computes the same result, with one workgroup per (sequence, head).
+ * computes the same result, with four workgroups per (sequence, head), one per
+ * 32 value columns (the norm-gate variants, which need whole output rows, with
+ * one workgroup per (sequence, head)).
  */
 LT_API size_t lt_prefill_workspace_bytes(int batch, long long seqlen, int heads, int head_dim,
                                          lt_dtype in_dtype);
