@@ -457,48 +457,59 @@ __global__ __launch_bounds__(NT) void bwd_kv_kernel(BackwardArgs a, Segmented sp
 }
 
 // Reverse pass on local-start segments. Mirrored segment g >= 1 started from a
-// zero carry instead of R_in(g) (boundary slot B_g after the chain), so token t
-// of it, n = seg_hi - 1 - t tokens before its right end, misses e^{-s n} R_in in
-// its gradient of S_t:
+// zero carry instead of R_in(g), so token t of it, n = seg_hi - 1 - t tokens
+// before its right end, misses e^{-s n} R_in in its gradient of S_t:
 //   dv_t += e^{-s n} k_t R_in,    dk_t += e^{-s n} v_t R_in^T,
 // added here for n <= kFixExp / s2 (past that the factor is below the fp32
-// unit roundoff, 2^-24),
-// in 64-token chunks counted from the right end, kRevFixParts workgroups per
-// (unit, head, segment). The products are the forward correction's (the carry,
-// or its transpose, as a bf16 S^T tile on MFMA).
-constexpr int kRevFixParts = 12;
+// unit roundoff, 2^-24), in 64-token chunks counted from the right end. As in
+// the forward correction, the chunks of all (unit, head, segment) pairs are
+// numbered in pair order and cut into equal contiguous ranges, consecutive
+// ranges on one XCD; a workgroup forms R_in(g) itself from the end carries E_j
+// the main pass left (R_in(1) = E_0, R_in(j+1) = e^{-s len_j} R_in(j) + E_j)
+// and loads the next chunk's rows before the current chunk's products, which
+// take R_in^T (bf16, LDS) as the operand of the dv term and, through the
+// transposing read, R_in for the dk term. The first `nfinal` workgroups write
+// d_state_in, the final carry, of each local-start head.
+constexpr int kRevFixWorkgroups = 256;  // one per CU (98 KB of LDS); a multiple of 8 (XCDs)
 
 // Rows a thread adds to (loaded ahead of the products): fp32 rows (t/32) + 16j,
-// 4 columns at 4(t%32); bf16 rows (t/16) + 32j, 8 columns at 8(t%16). Rows
-// below rlo read row rlo and are not stored.
-struct RowsFrom {
+// 4 columns at 4(t%32); bf16 rows (t/16) + 32j, 8 columns at 8(t%16). `out`
+// points at chunk row rlo; rows below rlo read that row and are not stored.
+template <typename OutT>
+struct RowsFrom;
+template <>
+struct RowsFrom<float> {
     uint4 y[4];
-    __device__ void load(const float *out, long long ts, int rlo, int tid) {
+    __device__ void load(const float *out, int ts, int rlo, int tid) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int row = (tid >> 5) + 16 * j;
-            y[j] = *reinterpret_cast<const uint4 *>(out + (row > rlo ? row : rlo) * ts + 4 * (tid & 31));
+            y[j] = *reinterpret_cast<const uint4 *>(out + (unsigned)((row > rlo ? row - rlo : 0) * ts + 4 * (tid & 31)));
         }
     }
-    __device__ void load(const __bf16 *out, long long ts, int rlo, int tid) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int row = (tid >> 4) + 32 * j;
-            y[j] = *reinterpret_cast<const uint4 *>(out + (row > rlo ? row : rlo) * ts + 8 * (tid & 15));
-        }
-    }
-    __device__ void add_store(float *out, long long ts, const float *Os, int rlo, int tid) const {
+    __device__ void add_store(float *out, int ts, const float *Os, int rlo, int tid) const {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int row = (tid >> 5) + 16 * j, col = 4 * (tid & 31);
             const float4 x = *reinterpret_cast<const float4 *>(Os + ooff(row, col));
             if (row >= rlo)
-                *reinterpret_cast<float4 *>(out + row * ts + col) =
+                *reinterpret_cast<float4 *>(out + (unsigned)((row - rlo) * ts + col)) =
                     make_float4(__uint_as_float(y[j].x) + x.x, __uint_as_float(y[j].y) + x.y,
                                 __uint_as_float(y[j].z) + x.z, __uint_as_float(y[j].w) + x.w);
         }
     }
-    __device__ void add_store(__bf16 *out, long long ts, const float *Os, int rlo, int tid) const {
+};
+template <>
+struct RowsFrom<__bf16> {
+    uint4 y[2];
+    __device__ void load(const __bf16 *out, int ts, int rlo, int tid) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int row = (tid >> 4) + 32 * j;
+            y[j] = *reinterpret_cast<const uint4 *>(out + (unsigned)((row > rlo ? row - rlo : 0) * ts + 8 * (tid & 15)));
+        }
+    }
+    __device__ void add_store(__bf16 *out, int ts, const float *Os, int rlo, int tid) const {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int row = (tid >> 4) + 32 * j, col = 8 * (tid & 15);
@@ -516,135 +527,192 @@ struct RowsFrom {
                 __builtin_memcpy(&uhi, &hi, 2);
                 r[i] = (uint32_t)ulo | ((uint32_t)uhi << 16);
             }
-            if (row >= rlo) *reinterpret_cast<uint4 *>(out + row * ts + col) = make_uint4(r[0], r[1], r[2], r[3]);
+            if (row >= rlo)
+                *reinterpret_cast<uint4 *>(out + (unsigned)((row - rlo) * ts + col)) = make_uint4(r[0], r[1], r[2], r[3]);
         }
     }
 };
 
 template <typename OutT>
-__global__ __launch_bounds__(NT) void rev_fix_kernel(BackwardArgs a, Segmented sp, float *ws) {
-    __shared__ __attribute__((aligned(16))) __bf16 Rt[D * D];   // R_in^T: operand of the dv term
-    __shared__ __attribute__((aligned(16))) __bf16 Rn[D * D];   // R_in: operand of the dk term
+__global__ __launch_bounds__(NT) void rev_fix_kernel(BackwardArgs a, Segmented sp, float *ws, int nfinal) {
+    __shared__ __attribute__((aligned(16))) __bf16 Rt[D * D];  // R_in^T
     __shared__ __attribute__((aligned(16))) __bf16 Kt[C * D];
     __shared__ __attribute__((aligned(16))) __bf16 Vt[C * D];
     __shared__ __attribute__((aligned(16))) float Os[C * D];
+    __shared__ long long first[kFixMaxPairs + 1];  // first chunk number of each pair
 
-    const int part = blockIdx.x % kRevFixParts;
-    const int gi = blockIdx.x / kRevFixParts;
-    const int g = 1 + gi % (sp.segments - 1);
-    const int uh = gi / (sp.segments - 1);
-    const int h = uh % a.heads, n = uh / a.heads;
-    const float s2 = a.slopes[h] * LOG2E;
-    if (!fix_head(s2, sp.seg_len, sp.fix_osz)) return;
+    const int tid = threadIdx.x;
     const long long L = a.seqlen;
-    const long long seg_hi = L - g * sp.seg_len;
-    const long long seg_lo = seg_hi - sp.seg_len > 0 && g + 1 < sp.segments ? seg_hi - sp.seg_len : 0;
-    const long long len = seg_hi - seg_lo;
-    const long long fl = fix_len(s2, sp.seg_len) + 1;  // n = 0 .. fix_len
-    const long long T = fl < len ? fl : len;
-    const long long nch = (T + C - 1) / C;
-    if (part >= nch) return;
+    if ((int)blockIdx.x < nfinal) {  // d_state_in of a local-start head
+        const int uh = blockIdx.x / kFinalSlices;
+        const float s2 = a.slopes[uh % a.heads] * LOG2E;
+        if (!fix_head(s2, sp.seg_len, sp.fix_osz)) return;
+        const int e = 4 * ((blockIdx.x % kFinalSlices) * NT + tid);
+        float *u = sp.unit(ws, uh);
+        float4 acc = *reinterpret_cast<const float4 *>(sp.start_state(u, 0) + e);
+        for (int g = 1; g < sp.segments; ++g) {
+            const float f = fast_exp2(-s2 * (float)seg_len_at(sp, L, g));
+            const float4 x = *reinterpret_cast<const float4 *>(sp.start_state(u, g) + e);
+            acc = make_float4(f * acc.x + x.x, f * acc.y + x.y, f * acc.z + x.z, f * acc.w + x.w);
+        }
+        *reinterpret_cast<float4 *>(a.d_state_in + (size_t)uh * D * D + e) = acc;
+        return;
+    }
 
-    const int tid = threadIdx.x, lane = tid & 63;
+    // chunks per pair, then their prefix sums
+    const int gs = sp.segments - 1;
+    const int pairs = a.units * a.heads * gs;
+    auto rows_of = [&](float s2, int g) {
+        const long long len = seg_len_at(sp, L, g), fl = fix_len(s2, sp.seg_len) + 1;  // n = 0 .. fix_len
+        return fl < len ? fl : len;
+    };
+    long long x = 0;
+    if (tid < pairs) {
+        const float s2 = a.slopes[(tid / gs) % a.heads] * LOG2E;
+        if (fix_head(s2, sp.seg_len, sp.fix_osz)) x = (rows_of(s2, 1 + tid % gs) + C - 1) / C;
+    }
+    for (int off = 1; off < kFixMaxPairs; off <<= 1) {
+        if (tid < kFixMaxPairs) first[tid + 1] = x;
+        __syncthreads();
+        if (tid < kFixMaxPairs && tid >= off) x += first[tid + 1 - off];
+        __syncthreads();
+    }
+    if (tid < kFixMaxPairs) first[tid + 1] = x;
+    if (tid == 0) first[0] = 0;
+    __syncthreads();
+
+    const long long total = uniform64(first[pairs]);
+    const int nwg = gridDim.x - nfinal;
+    const int r = (int)(blockIdx.x % 8) * (nwg / 8) + (int)(blockIdx.x - nfinal) / 8;
+    const long long j0 = total * r / nwg, j1 = total * (r + 1) / nwg;
+    if (j0 >= j1) return;
+
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int qh = w >> 2, cq = w & 3, r32 = lane & 31, hf = lane >> 5;
-    {
-        const float *ri = sp.partial(sp.unit(ws, uh), g);
-        f32x16 S[2];
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                S[db][v] = ri[(64 * qh + 32 * db + 8 * (v >> 2) + 4 * hf + (v & 3)) * D + 32 * cq + r32];
-        write_state_t(Rt, S, qh, cq, lane);
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)  // the transpose: element (r, c) of R_in^T is R_in[c][r]
-                S[db][v] = ri[(32 * cq + r32) * D + 64 * qh + 32 * db + 8 * (v >> 2) + 4 * hf + (v & 3)];
-        write_state_t(Rn, S, qh, cq, lane);
-    }
+    const int qh = w >> 2, cq = w & 3;
     const int ts = a.heads * D;
-    const long long row0 = ((long long)n * L) * a.heads + h;  // token 0 of this (sequence, head)
-    const uint16_t *kg = static_cast<const uint16_t *>(a.k) + row0 * D;
-    const uint16_t *vg = static_cast<const uint16_t *>(a.v) + row0 * D;
-    OutT *dkg = static_cast<OutT *>(a.dk) + row0 * D;
-    OutT *dvg = static_cast<OutT *>(a.dv) + row0 * D;
-    const int seg = tid & 15;
-    for (long long c = part; c < nch; c += kRevFixParts) {
-        // chunk rows r = 0..63 are tokens tlo + r; those below seg_hi - T are not
-        // corrected (their loads read row rlo and they are not stored)
-        const long long tlo = seg_hi - C * (c + 1);
-        const int rlo = (int)(seg_hi - T - tlo > 0 ? seg_hi - T - tlo : 0);
-        OutT *dvc = dvg + tlo * (long long)ts, *dkc = dkg + tlo * (long long)ts;
+    struct Chunk {
+        const uint16_t *k, *v;
+        OutT *dk, *dv;
+        long long seg_hi, tlo;
+        int rlo, pair, uh, g;
+        float s2;
+    };
+    int p = 0;
+    auto chunk_at = [&](long long j) {
+        while (first[p + 1] <= j) ++p;
+        p = __builtin_amdgcn_readfirstlane(p);
+        Chunk c;
+        c.pair = p;
+        c.uh = p / gs;
+        c.g = 1 + p % gs;
+        const int h = c.uh % a.heads, n = c.uh / a.heads;
+        c.s2 = a.slopes[h] * LOG2E;
+        const long long T = rows_of(c.s2, c.g);
+        c.seg_hi = L - (long long)c.g * sp.seg_len;
+        const long long ci = uniform64(j - first[p]);
+        c.tlo = c.seg_hi - C * (ci + 1);
+        c.rlo = (int)(c.seg_hi - T - c.tlo > 0 ? c.seg_hi - T - c.tlo : 0);
+        // rows below rlo are never touched: the base is the chunk's first
+        // corrected row, and row offsets are taken relative to it
+        const long long off = (((long long)n * L + c.tlo + c.rlo) * a.heads + h) * (long long)D;
+        c.k = static_cast<const uint16_t *>(a.k) + off;
+        c.v = static_cast<const uint16_t *>(a.v) + off;
+        c.dk = static_cast<OutT *>(a.dk) + off;
+        c.dv = static_cast<OutT *>(a.dv) + off;
+        return c;
+    };
+    // loads of a chunk: k, v rows and the dv, dk rows (row r of the chunk at
+    // offset (r - rlo) from the base; rows below rlo read row rlo)
+    struct Loads {
         uint4 kx[2], vx[2];
+        RowsFrom<OutT> dvr, dkr;
+    };
+    auto load = [&](const Chunk &c, Loads &l, int th) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int r = (tid >> 4) + 32 * i;
-            const long long off = (tlo + (r > rlo ? r : rlo)) * (long long)ts + 8 * seg;
-            kx[i] = stream_load16(kg + off);
-            vx[i] = stream_load16(vg + off);
+            const int rr = (th >> 4) + 32 * i;
+            const unsigned o = (unsigned)((rr > c.rlo ? rr - c.rlo : 0) * ts + 8 * (th & 15));
+            l.kx[i] = stream_load16(c.k + o);
+            l.vx[i] = stream_load16(c.v + o);
         }
-        RowsFrom dvr, dkr;
-        dvr.load(dvc, ts, rlo, tid);
-        dkr.load(dkc, ts, rlo, tid);
+        l.dvr.load(c.dv, ts, c.rlo, th);
+        l.dkr.load(c.dk, ts, c.rlo, th);
+    };
+    Chunk cur = chunk_at(j0);
+    Loads la;
+    load(cur, la, tid);
+    int loaded = -1;
+    for (long long j = j0; j < j1; ++j) {
+        if (j > j0) __syncthreads();  // the previous chunk's reads of Kt, Vt, Os done
+        int tl = tid;
+        asm volatile("" : "+v"(tl));  // lane offsets recomputed per chunk (not spilled)
+        const int ln = tl & 63;
+        Chunk nxt = cur;
+        Loads lb = la;
+        if (j + 1 < j1) {
+            nxt = chunk_at(j + 1);
+            load(nxt, lb, tl);
+        }
+        if (cur.pair != loaded) {  // R_in(g)^T as bf16 (the last reads of Rt ended before a barrier)
+            const int c = tl & (D - 1), kq = tl >> 7;
+            float *u = sp.unit(ws, cur.uh);
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                float acc[4][4];
+                {
+                    const float *e = sp.start_state(u, 0) + (4 * kq + 64 * half) * D + c;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) acc[i][rr] = e[(16 * i + rr) * D];
+                }
+                for (int g = 1; g < cur.g; ++g) {
+                    const float f = fast_exp2(-cur.s2 * (float)seg_len_at(sp, L, g));
+                    const float *e = sp.start_state(u, g) + (4 * kq + 64 * half) * D + c;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) acc[i][rr] = f * acc[i][rr] + e[(16 * i + rr) * D];
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    bf16x4 y;
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) y[rr] = static_cast<__bf16>(acc[i][rr]);
+                    *reinterpret_cast<bf16x4 *>(Rt + L128::off(c, 4 * (kq + 4 * i) + 64 * half)) = y;
+                }
+            }
+            loaded = cur.pair;
+        }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int r = (tid >> 4) + 32 * i;
-            *reinterpret_cast<uint4 *>(Kt + L128::off(r, 8 * seg)) = keep_if(r >= rlo, kx[i]);
-            *reinterpret_cast<uint4 *>(Vt + L128::off(r, 8 * seg)) = keep_if(r >= rlo, vx[i]);
+            const int rr = (tl >> 4) + 32 * i;
+            *reinterpret_cast<uint4 *>(Kt + L128::off(rr, 8 * (tl & 15))) = keep_if(rr >= cur.rlo, la.kx[i]);
+            *reinterpret_cast<uint4 *>(Vt + L128::off(rr, 8 * (tl & 15))) = keep_if(rr >= cur.rlo, la.vx[i]);
         }
-        __syncthreads();  // K, V tiles (and the carry tiles) visible; Os free
-        const float f = fast_exp2(-s2 * (float)(seg_hi - 1 - (tlo + 32 * qh + r32)));
-        f32x16 o;
+        __syncthreads();  // K, V tiles and R_in^T visible
+        f32x16 odv, odk;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) o[v] = 0.f;
+        for (int v = 0; v < 16; ++v) odv[v] = odk[v] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks)
-            o = mma(ld_op<L128>(Rt, 32 * cq, 16 * ks, lane), ld_op<L128>(Kt, 32 * qh, 16 * ks, lane), o);
-        o *= f;
-        stage_out(Os, o, qh, cq, lane);
+            odv = mma(ld_op<L128>(Rt, 32 * cq, 16 * ks, ln), ld_op<L128>(Kt, 32 * qh, 16 * ks, ln), odv);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            odk = mma(ld_op_t<L128>(Rt, 32 * cq, 16 * ks, ln), ld_op<L128>(Vt, 32 * qh, 16 * ks, ln), odk);
+        const float f = fast_exp2(-cur.s2 * (float)(cur.seg_hi - 1 - (cur.tlo + 32 * qh + (ln & 31))));
+        odv *= f;
+        odk *= f;
+        stage_out(Os, odv, qh, cq, ln);
         __syncthreads();  // dv rows staged
-        dvr.add_store(dvc, ts, Os, rlo, tid);
+        la.dvr.add_store(cur.dv, ts, Os, cur.rlo, tl);
         __syncthreads();  // Os read
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[v] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-            o = mma(ld_op<L128>(Rn, 32 * cq, 16 * ks, lane), ld_op<L128>(Vt, 32 * qh, 16 * ks, lane), o);
-        o *= f;
-        stage_out(Os, o, qh, cq, lane);
-        __syncthreads();  // dk rows staged; every read of the K and V tiles done
-        dkr.add_store(dkc, ts, Os, rlo, tid);
+        stage_out(Os, odk, qh, cq, ln);
+        __syncthreads();  // dk rows staged
+        la.dkr.add_store(cur.dk, ts, Os, cur.rlo, tl);
+        cur = nxt;
+        la = lb;
     }
-}
-
-// Local-start segments of the reverse pass (heads with fix_head), after its
-// main pass: the true carried-in term of every mirrored segment g >= 1 (into
-// boundary slot B_g) and the final carry, from the end carries E_g the main
-// pass left in slots S_g (segment 0 started from dS_final, the others from
-// zero):
-//   R_in(1) = E_0,   R_in(g+1) = e^{-s len_g} R_in(g) + E_g,
-//   final   = e^{-s len_{G-1}} R_in(G-1) + E_{G-1},
-// len_g = min(seg_len, seqlen - g seg_len) (mirrored segments are counted from
-// the sequence end).
-__global__ __launch_bounds__(kCombineThreads) void fix_combine_kernel(const float *slopes, int heads,
-                                                                       long long seqlen, float *final_out,
-                                                                       Segmented sp, float *ws) {
-    const int uh = blockIdx.x / kCombineSlices;
-    const int e = 4 * ((blockIdx.x % kCombineSlices) * kCombineThreads + threadIdx.x);
-    const float s2 = slopes[uh % heads] * LOG2E;
-    if (!fix_head(s2, sp.seg_len, sp.fix_osz)) return;
-    float *u = sp.unit(ws, uh);
-    float4 acc = *reinterpret_cast<const float4 *>(sp.start_state(u, 0) + e);
-    for (int g = 1; g < sp.segments; ++g) {
-        *reinterpret_cast<float4 *>(sp.partial(u, g) + e) = acc;
-        const long long rest = seqlen - (long long)g * sp.seg_len;
-        const float f = fast_exp2(-s2 * (float)(rest < sp.seg_len ? rest : sp.seg_len));
-        const float4 p = *reinterpret_cast<const float4 *>(sp.start_state(u, g) + e);
-        acc = make_float4(f * acc.x + p.x, f * acc.y + p.y, f * acc.z + p.z, f * acc.w + p.w);
-    }
-    if (final_out) *reinterpret_cast<float4 *>(final_out + (size_t)uh * D * D + e) = acc;
 }
 
 template <typename OutT>
@@ -674,12 +742,10 @@ hipError_t launch(const BackwardArgs &a, const PrefillPlan &p, void *workspace, 
     if (!fix_osz) return hipGetLastError();
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fix_combine_kernel, dim3((unsigned)(uh * kCombineSlices)), dim3(kCombineThreads), 0, stream,
-                       a.slopes, a.heads, a.seqlen, a.d_state_in, sp, ws);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((rev_fix_kernel<OutT>), dim3((unsigned)(uh * (sp.segments - 1) * kRevFixParts)), dim3(NT), 0,
-                       stream, a, sp, ws);
+    if (uh * (sp.segments - 1) > kFixMaxPairs) return hipErrorInvalidValue;  // not a segmented plan
+    const int nfinal = a.d_state_in ? (int)(uh * kFinalSlices) : 0;
+    hipLaunchKernelGGL((rev_fix_kernel<OutT>), dim3((unsigned)(nfinal + kRevFixWorkgroups)), dim3(NT), 0, stream,
+                       a, sp, ws, nfinal);
     return hipGetLastError();
 }
 

@@ -660,20 +660,7 @@ __global__ __launch_bounds__(NT) void slice_kernel(PrefillArgs a) {
 // `nfinal` workgroups instead write the final state of each local-start head,
 // e^{-s len_{G-1}} S_in(G-1) + E_{G-1}, kFinalSlices workgroups per head.
 constexpr int kFixWorkgroups = 512;                // two per CU; a multiple of 8 (XCDs)
-constexpr int kFixMaxPairs = 256;                  // segmented plans have fewer (unit, head, g >= 1) pairs
-constexpr int kFinalSlices = D * D / (4 * NT);     // 4 state elements per thread
 
-// A 64-bit value that is the same in every lane, kept in scalar registers.
-__device__ __forceinline__ long long uniform64(long long x) {
-    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)x);
-    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)((unsigned long long)x >> 32));
-    return (long long)(((unsigned long long)hi << 32) | lo);
-}
-
-__device__ __forceinline__ long long seg_len_at(const Segmented &sp, long long seqlen, int g) {
-    const long long rest = seqlen - (long long)g * sp.seg_len;
-    return rest < sp.seg_len ? rest : sp.seg_len;
-}
 
 // The rows of o a thread adds to (loaded before the product, so their latency
 // overlaps it): fp32 rows (t/32) + 16j, 4 columns at 4(t%32); bf16 rows

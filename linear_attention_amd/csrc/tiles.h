@@ -334,6 +334,23 @@ struct Segmented {
     __device__ float *start_state(float *u, int g) const { return slot(u, pieces + segments - 1 + g); }
 };
 
+// Correction passes: (unit, head, segment g >= 1) pairs of a segmented plan
+// (fewer than 256), and the final-state slices (4 elements per thread).
+constexpr int kFixMaxPairs = 256;                  // segmented plans have fewer (unit, head, g >= 1) pairs
+constexpr int kFinalSlices = D * D / (4 * NT);     // 4 state elements per thread
+
+// A 64-bit value that is the same in every lane, kept in scalar registers.
+__device__ __forceinline__ long long uniform64(long long x) {
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)x);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)((unsigned long long)x >> 32));
+    return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
+__device__ __forceinline__ long long seg_len_at(const Segmented &sp, long long seqlen, int g) {
+    const long long rest = seqlen - (long long)g * sp.seg_len;
+    return rest < sp.seg_len ? rest : sp.seg_len;
+}
+
 // Pre-pass grouping. The plan cuts the first G-1 segments of every head into
 // many short pieces, which is right when few heads take the pre-pass; when
 // many do, a workgroup takes k consecutive pieces of a head (writing one state,
