@@ -187,7 +187,7 @@ def run_prefill_norm_gate(la, torch, steps, warmup):
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "bytes_per_launch": nbytes,
                          "kernel": "lt_prefill_norm_gate call: piece_state_kernel + combine_kernel "
-                                   "+ head_kernel<bf16, norm-gate>"}}
+                                   "+ head_kernel<bf16, norm-gate> + fix_kernel<bf16, true>"}}
 
 
 def run_backward(la, torch, steps, warmup, batch, seqlen):
@@ -231,7 +231,8 @@ def run_backward(la, torch, steps, warmup, batch, seqlen):
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "bytes_per_launch": nbytes,
-                         "kernel": "lt_prefill_backward call: dq forward pass + bwd_kv_kernel"}}
+                         "kernel": "lt_prefill_backward call: dq forward pass + rev_piece_kernel "
+                                   "+ combine_kernel + bwd_kv_kernel + rev_fix_kernel"}}
 
 
 MFMA_BF16_PEAK_TFS = 2500.0
