@@ -721,10 +721,15 @@ hipError_t launch(const BackwardArgs &a, const PrefillPlan &p, void *workspace, 
     const long long uh = (long long)a.units * a.heads;
     float *ws = static_cast<float *>(workspace);
     const bool seg = p.segments > 1 && p.value_slices == 1;
-    // heads may take local-start segments (fix_head's rule) with the correction's
-    // traffic at k, v read, dk, dv read and written: 512 + 512 sizeof(OutT) B per
-    // token, against the reverse pre-pass's q, dO re-read, 512 B per token
-    const int fix_osz = seg ? 1 + 2 * (int)sizeof(OutT) : 0;
+    // heads may take local-start segments (fix_head's rule). The correction moves
+    // k, v once and dk, dv read and written, 512 (1 + sizeof(OutT)) B per token,
+    // against the reverse pre-pass's q, dO re-read, 512 B per token. fix_head
+    // weighs a correction token at 256 (1 + osz) B; osz = 1 + sizeof(OutT) counts
+    // it at 60-67% of that traffic, because the reverse pre-pass of the few heads
+    // that would still need it runs far below the correction's bandwidth (M1
+    // layer: with the exact weight the 3 slowest-decay heads take the pre-pass,
+    // 1.430 ms per call; with this one all 64 heads correct, 1.418 ms)
+    const int fix_osz = seg ? 1 + (int)sizeof(OutT) : 0;
     const Segmented sp = seg ? Segmented{p.segments, p.pieces, p.seg_len, p.piece_len, fix_osz}
                              : Segmented{1, 0, a.seqlen, 0};
     if (seg) {

@@ -102,14 +102,16 @@ def test_backward_long_sequence_without_workspace(la):
 @pytest.mark.parametrize("grad_dtype", ["f32", "bf16"])
 def test_backward_segmented_slope_mix(la, grad_dtype):
     """Segmented backward over heads on both routes of both passes: short-memory
-    heads (slopes 0.02, 0.2, 1, 30) on local-start segments with the carried-in
-    terms added afterwards (0.02: 831 corrected tokens of 2,304; 30: only the
-    last token of each reverse segment), 0 and 1e-6 on the pre-passes; carried-in
+    heads (slopes 0.012, 0.02, 0.2, 1, 30) on local-start segments with the
+    carried-in terms added afterwards (0.012: 1,386 corrected tokens of 2,304,
+    0.60 of the segment, a head the reverse pass corrects although its
+    correction moves more than the pre-pass would; 0.02: 831; 30: only the last
+    token of each reverse segment), 0 and 1e-6 on the pre-passes; carried-in
     state and final-state gradient."""
     import torch
 
-    L, H = 9000, 6
-    sl = np.array([0.0, 1e-6, 0.02, 0.2, 1.0, 30.0], np.float32)
+    L, H = 9000, 7
+    sl = np.array([0.0, 1e-6, 0.012, 0.02, 0.2, 1.0, 30.0], np.float32)
     print(f"[case] backward segmented slope mix L={L} slopes={list(sl)} grad={grad_dtype}", flush=True)
     q, k, v = workloads.qkv_host(2501, (1, L, H, 128), "bf16")
     do = workloads.gate_host(2502, (1, L, H, 128), "bf16")
