@@ -43,17 +43,20 @@ __device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 struct L128 {  // [rows][128] bf16
+    static constexpr int kPitch = 128;
     __device__ static int off(int row, int col) {
         return row * 128 + ((((col >> 3) ^ swz(row)) << 3) | (col & 7));
     }
 };
 struct LP {  // P tile [64][64] bf16: 8 chunks per 128-byte row, two rows per bank line
+    static constexpr int kPitch = PW;
     __device__ static int off(int row, int col) {
         return row * PW + ((((col >> 3) ^ ((row >> 1) & 7)) << 3) | (col & 7));
     }
 };
 template <int PITCH>
 struct LPad {  // narrow tiles: plain padded rows
+    static constexpr int kPitch = PITCH;
     __device__ static int off(int row, int col) { return row * PITCH + col; }
 };
 
@@ -71,9 +74,15 @@ __device__ __forceinline__ bf16x8 ld_op(const __bf16 *t, int row0, int k0, int l
 template <class L>
 __device__ __forceinline__ bf16x8 ld_op_t(const __bf16 *t, int c0, int k0, int lane) {
     const int li = lane & 15, grp = lane >> 4;
-    const int row = k0 + 8 * (grp >> 1) + (li >> 2), col = c0 + 16 * (grp & 1) + 4 * (li & 3);
-    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(t + L::off(row, col)));
-    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(t + L::off(row + 4, col)));
+    // k0 (a multiple of 16 at every call) enters as a whole number of rows:
+    // each layout's row swizzle repeats every 16 rows, so k0 * kPitch is a plain
+    // offset, which the compiler folds into the read's immediate field instead
+    // of holding one address register per k0 (15 fewer in the main prefill
+    // loop; the norm-gate variant's spill reloads left its loop)
+    const int r = 8 * (grp >> 1) + (li >> 2), col = c0 + 16 * (grp & 1) + 4 * (li & 3);
+    const __bf16 *p = t + k0 * L::kPitch;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p + L::off(r, col)));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p + L::off(r + 4, col)));
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
