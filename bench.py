@@ -6,7 +6,7 @@ L = 32768 tokens, 64 heads x 128, block 256, bf16 Q/K/V, fp32 O and fp32 final
 state (the block form of MiniMax Signal Lab · M1, §03, on the layer shape of
 §02/§04). Inputs are seeded synthetic tensors already resident in HBM.
 
-Prints ONE JSON line. Besides the driver's fields it carries:
+Prints ONE JSON line. Besides the standard fields (metric, value, unit, steps, config ...) it carries:
   roofline      prefill kernel: algorithmic bytes per launch / mean launch
                 duration (HIP events on the launch stream) against 8 TB/s HBM;
                 ``traffic`` from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE

@@ -36,7 +36,7 @@ Three independent formulations of the same operator, all in fp64:
     is normalised and gated (RMS normalisation per (token, head), a weight per
     (head, feature), a logistic-sigmoid gate; the pages name neither form).
 
-Readings of points the pages leave open (each is listed in the design doc):
+Readings of points the pages leave open:
 positions inside a block are 1-indexed, ``d_q[i] = e^{-s i}``,
 ``d_k[j] = e^{-s (m - j)}``, the state decays by ``e^{-s m}`` per block of
 ``m`` tokens, ``D`` includes the diagonal, ``⊙`` with a length-``m`` vector
