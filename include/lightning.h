@@ -184,8 +184,9 @@ LT_API lt_status lt_decode(const void *q, const void *k, const void *v, lt_dtype
  *   dq, dk, dv     [batch, seqlen, heads, head_dim], grad_dtype (LT_F32 or
  *                  LT_BF16).
  *   d_state_in     [batch, heads, head_dim, head_dim] fp32, or NULL to skip.
- *   block, workspace: as lt_prefill (the workspace serves the dq pass; query
- *                  it with lt_prefill_workspace_bytes).
+ *   block, workspace: as lt_prefill (the workspace serves the dq pass and
+ *                  then the reverse pass, one after the other on `stream`;
+ *                  query its size with lt_prefill_workspace_bytes).
  *   No output may overlap an input or another output (LT_ERR_ALIAS).
  *   Errors: LT_ERR_NULL, LT_ERR_SHAPE, LT_ERR_BLOCK, LT_ERR_DTYPE,
  *   LT_ERR_ALIAS, LT_ERR_HIP.
