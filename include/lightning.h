@@ -86,6 +86,11 @@ LT_API const char *lt_status_string(int status);
 /* Library ABI version: major * 10000 + minor * 100 + patch. */
 LT_API int lt_version(void);
 
+/* Build identity: a hash of the sources the library was compiled from (16 hex
+ * digits; "unknown" when built without one). Static storage; never NULL. Runs
+ * no HIP call, so it can be read on a machine without a GPU. */
+LT_API const char *lt_build_id(void);
+
 /*
  * lt_prefill - block-wise prefill of `batch` sequences of equal length.
  *

@@ -20,7 +20,7 @@ LT_F32, LT_BF16 = 0, 1
 LT_MAX_BLOCK = 65536
 HEAD_DIM = 128
 
-EXPORTS = ("lt_status_string", "lt_version", "lt_prefill", "lt_prefill_workspace_bytes",
+EXPORTS = ("lt_status_string", "lt_version", "lt_build_id", "lt_prefill", "lt_prefill_workspace_bytes",
            "lt_prefill_varlen", "lt_decode", "lt_prefill_norm_gate", "lt_prefill_varlen_norm_gate",
            "lt_decode_norm_gate", "lt_decode_slots", "lt_prefill_backward", "lt_softmax_prefill",
            "lt_softmax_decode", "lt_softmax_decode_workspace_bytes")
@@ -52,6 +52,8 @@ def _load() -> ctypes.CDLL:
     lib.lt_status_string.restype = ctypes.c_char_p
     lib.lt_version.argtypes = []
     lib.lt_version.restype = _i
+    lib.lt_build_id.argtypes = []
+    lib.lt_build_id.restype = ctypes.c_char_p
     lib.lt_prefill.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp,
                                _i, _ll, _i, _i, _i, _vp, ctypes.c_size_t, _vp]
     lib.lt_prefill.restype = _i

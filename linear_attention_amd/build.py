@@ -6,7 +6,9 @@ calls :func:`build` as well.
 
 from __future__ import annotations
 
+import hashlib
 import os
+import re
 import subprocess
 import sys
 import tempfile
@@ -37,6 +39,39 @@ HIPCC_FLAGS = [
 EXTRA_FLAGS = {"softmax.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
+def source_hash() -> str:
+    """sha256 (first 16 hex digits) over every file of csrc/ and include/ (names
+    and contents, sorted by name) and the compile flags: the build identity the
+    library reports through lt_build_id()."""
+    h = hashlib.sha256()
+    for d in (CSRC, INCLUDE):
+        for name in sorted(os.listdir(d)):
+            path = os.path.join(d, name)
+            if os.path.isfile(path):
+                h.update(os.path.relpath(path, ROOT).encode() + b"\0")
+                with open(path, "rb") as f:
+                    h.update(f.read())
+    h.update(repr((HIPCC_FLAGS[:-4], sorted(EXTRA_FLAGS.items()))).encode())
+    return h.hexdigest()[:16]
+
+
+def built_id(path: str = LIB):
+    """The build identity a built library carries, or None when it has none
+    (missing file or no tag). Read from the file's bytes: loading the library
+    here would keep this version mapped in the process even after a rebuild
+    replaces the file."""
+    if not os.path.exists(path):
+        return None
+    with open(path, "rb") as f:
+        m = re.search(rb"LT_BUILD_ID=([0-9a-f]{16}|unknown)\0", f.read())
+    return m.group(1).decode() if m else None
+
+
+def library_is_current() -> bool:
+    """True when liblightning.so exists and was built from the current sources."""
+    return built_id() == source_hash()
+
+
 def hipcc() -> str:
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     cand = os.path.join(rocm, "bin", "hipcc")
@@ -59,9 +94,11 @@ def build(verbose: bool = False) -> str:
     with tempfile.TemporaryDirectory(prefix="lt_build_") as work:
         objs = [os.path.join(work, s + ".o") for s in SOURCES]
 
+        build_id = ["-DLT_BUILD_ID=\"%s\"" % source_hash()]
+
         def compile_one(i):
             src = SOURCES[i]
-            _run([hipcc()] + HIPCC_FLAGS + EXTRA_FLAGS.get(src, []) +
+            _run([hipcc()] + HIPCC_FLAGS + EXTRA_FLAGS.get(src, []) + build_id +
                  ["-c", os.path.join(CSRC, src), "-o", objs[i]], verbose, src)
 
         with ThreadPoolExecutor(max_workers=min(len(SOURCES), 6)) as ex:

@@ -217,6 +217,15 @@ LT_API const char *lt_status_string(int status) {
 
 LT_API int lt_version(void) { return 10100; }
 
+// The build passes the hash of the sources it compiled; a build by other means
+// reports "unknown". The tag keeps a fixed prefix so the identity can also be
+// read from the library file without loading it.
+#ifndef LT_BUILD_ID
+#define LT_BUILD_ID "unknown"
+#endif
+static const char kBuildTag[] = "LT_BUILD_ID=" LT_BUILD_ID;
+LT_API const char *lt_build_id(void) { return kBuildTag + sizeof("LT_BUILD_ID=") - 1; }
+
 }  // extern "C"
 
 namespace {

@@ -55,6 +55,15 @@ def test_status_strings():
     assert la.lib.lt_version() == 10100
 
 
+def test_build_id_matches_the_sources():
+    """The library reports the hash of the csrc/ and include/ files it was built
+    from (the test fixture rebuilds it when they differ)."""
+    from linear_attention_amd import build as b
+
+    assert la.lib.lt_build_id().decode() == b.source_hash()
+    assert b.library_is_current()
+
+
 def prefill(**kw):
     args = dict(q=A, k=A + 100 * MB, v=A + 200 * MB, in_dtype=la.LT_BF16, slopes=A + 300 * MB,
                 o=A + 400 * MB, out_dtype=la.LT_F32, state_in=None, state_out=A + 900 * MB,

@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 import workloads
-from parity_util import TOL_BF16, ensure_built, max_rel_states, rel_l2, to_device, to_host_f32
+from parity_util import TOL_BF16, ensure_built, max_rel_states, parity_err, to_device, to_host_f32
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +45,7 @@ def backward_case(la, batch, L, H, seed, with_state=False, grad_dtype="f32", wor
     errs = {}
     for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
         gh = to_host_f32(g)
-        errs[name] = max(rel_l2(gh[b, :, h], r[b, :, h]) for b in range(batch) for h in range(H))
+        errs[name] = max(parity_err(gh[b, :, h], r[b, :, h]) for b in range(batch) for h in range(H))
     errs["ds0"] = max_rel_states(to_host_f32(dsi), rs)
     print(f"[result] {errs}", flush=True)
     return errs
@@ -126,7 +126,7 @@ def test_backward_segmented_slope_mix(la, grad_dtype):
     errs = {}
     for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
         gh = to_host_f32(g)
-        errs[name] = max(rel_l2(gh[0, :, h], r[0, :, h]) for h in range(H))
+        errs[name] = max(parity_err(gh[0, :, h], r[0, :, h]) for h in range(H))
     errs["ds0"] = max_rel_states(to_host_f32(dsi), rs)
     print(f"[result] {errs}", flush=True)
     assert max(errs.values()) <= TOL_BF16, errs
@@ -157,7 +157,7 @@ def test_backward_prepass_groups(la):
     errs = {}
     for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
         gh = to_host_f32(g)[:, :, hs]
-        errs[name] = max(rel_l2(gh[0, :, i], r[0, :, i]) for i in range(len(hs)))
+        errs[name] = max(parity_err(gh[0, :, i], r[0, :, i]) for i in range(len(hs)))
     errs["ds0"] = max_rel_states(to_host_f32(dsi)[:, hs], rs)
     print(f"[result] {errs}", flush=True)
     assert max(errs.values()) <= TOL_BF16, errs
@@ -185,7 +185,7 @@ def test_backward_segmented_batch_slope_mix(la):
     errs = {}
     for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
         gh = to_host_f32(g)
-        errs[name] = max(rel_l2(gh[b, :, h], r[b, :, h]) for b in range(B) for h in range(H))
+        errs[name] = max(parity_err(gh[b, :, h], r[b, :, h]) for b in range(B) for h in range(H))
     errs["ds0"] = max_rel_states(to_host_f32(dsi), rs)
     print(f"[result] {errs}", flush=True)
     assert max(errs.values()) <= TOL_BF16, errs

@@ -3,7 +3,9 @@
 Small and medium shapes that span several 64-token sub-blocks, ragged tails,
 empty inputs, carried-in states, in-place state updates, both input dtypes and
 both output dtypes. Tolerance: relative L2 per (sequence, head) of O and of
-the final state, <= 1e-5 for fp32 inputs and <= 1e-2 for bf16 inputs.
+the final state, <= 1e-5 for fp32 inputs and <= 1e-2 for bf16 inputs, and
+every row (token, or key row of a state) within 5x that of the slice's RMS row
+norm (parity_util.parity_err).
 """
 
 import numpy as np
@@ -12,7 +14,7 @@ import pytest
 import oracle
 import workloads
 from parity_util import (TOL_BF16, TOL_F32, ensure_built, max_rel_per_head, max_rel_states,
-                         rel_l2, to_device, to_host_f32)
+                         parity_err, segment_boundary_err, to_device, to_host_f32)
 
 pytestmark = pytest.mark.gpu
 
@@ -51,6 +53,11 @@ def run_prefill_case(la, batch, L, H, dtype, seed, block=256, with_s0=False, out
     cu = np.arange(batch + 1) * L
     eo = max_rel_per_head(o_g.reshape(batch * L, H, 128), o_ref.reshape(batch * L, H, 128), cu)
     es = max_rel_states(s_g, s_ref)
+    if L > 0 and dtype == "bf16":  # the rows next to the plan's switches, on their own
+        eb = max(segment_boundary_err(o_g[b, :, h], o_ref[b, :, h], batch, L, H, sl[h])
+                 for b in range(batch) for h in range(H))
+        print(f"[result] o {eo:.3e} state {es:.3e} segment-boundary rows {eb:.3e}", flush=True)
+        eo = max(eo, eb)
     return eo, es
 
 
@@ -87,11 +94,11 @@ def test_prefill_tiny_f32_config(la):
     o_ref, s_ref = oracle.recurrence_batch(q, k, v, sl)
     for h in range(w.heads):
         ob, sb = oracle.brute_force(q[0, :, h], k[0, :, h], v[0, :, h], sl[h])
-        assert rel_l2(o_ref[0, :, h], ob) < 1e-12
-        assert rel_l2(o_g[0, :, h], ob) <= TOL_F32
-        assert rel_l2(o_g[0, :, h], o_ref[0, :, h]) <= TOL_F32
-        assert rel_l2(s_g[0, h], sb) <= TOL_F32
-        assert rel_l2(s_g[0, h], s_ref[0, h]) <= TOL_F32
+        assert parity_err(o_ref[0, :, h], ob) < 1e-12
+        assert parity_err(o_g[0, :, h], ob) <= TOL_F32
+        assert parity_err(o_g[0, :, h], o_ref[0, :, h]) <= TOL_F32
+        assert parity_err(s_g[0, h], sb) <= TOL_F32
+        assert parity_err(s_g[0, h], s_ref[0, h]) <= TOL_F32
 
 
 @pytest.mark.parametrize("block", [1, 16, 64, 100, 256, 4096])
@@ -119,8 +126,8 @@ def test_prefill_extreme_slopes(la):
     o_g, s_g = to_host_f32(o), to_host_f32(st)
     assert np.isfinite(o_g).all() and np.isfinite(s_g).all()
     for h in range(H):
-        assert rel_l2(o_g[0, :, h], o_ref[0, :, h]) <= TOL_BF16, h
-        assert rel_l2(s_g[0, h], s_ref[0, h]) <= TOL_BF16, h
+        assert parity_err(o_g[0, :, h], o_ref[0, :, h]) <= TOL_BF16, h
+        assert parity_err(s_g[0, h], s_ref[0, h]) <= TOL_BF16, h
 
 
 def test_prefill_state_in_place(la):
@@ -219,7 +226,7 @@ def test_decode_steps_continue_prefill(la, dtype):
         og = to_host_f32(outs[i])
         for b in range(B):
             for h in range(H):
-                assert rel_l2(og[b, h], o_ref[b, t, h]) <= tol(dtype), (t, b, h)
+                assert parity_err(og[b, h], o_ref[b, t, h]) <= tol(dtype), (t, b, h)
     assert max_rel_states(to_host_f32(st), s_ref) <= tol(dtype)
 
 
@@ -239,9 +246,9 @@ def test_decode_single_step_exact_inputs(la):
     og, sg = to_host_f32(o), to_host_f32(st)
     for b in range(B):
         for h in range(H):
-            assert rel_l2(og[b, h], o_ref[b, h]) <= TOL_BF16
+            assert parity_err(og[b, h], o_ref[b, h]) <= TOL_BF16
             # fp32 state update: a few ulps
-            assert rel_l2(sg[b, h], s_ref[b, h]) <= 1e-6
+            assert parity_err(sg[b, h], s_ref[b, h]) <= 1e-6
 
 
 def test_prefill_is_deterministic(la):
@@ -380,7 +387,7 @@ def test_decode_batches_with_strided_order(la, B):
     torch.cuda.synchronize()
     o_ref, s_ref = oracle.decode(q, k, v, sl, s0)
     og = to_host_f32(o)
-    eo = max(rel_l2(og[b, h], o_ref[b, h]) for b in range(B) for h in range(H))
+    eo = max(parity_err(og[b, h], o_ref[b, h]) for b in range(B) for h in range(H))
     es = max_rel_states(to_host_f32(state), s_ref)
     assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)
 
@@ -408,10 +415,11 @@ def test_prefill_segmented_slope_mix(la, out_dtype):
     torch.cuda.synchronize()
     o_ref, s_ref = oracle.recurrence_batch(q, k, v, sl, s0=s0)
     o_g = to_host_f32(o)
-    eo = max(rel_l2(o_g[0, :, h], o_ref[0, :, h]) for h in range(H))
+    eo = max(parity_err(o_g[0, :, h], o_ref[0, :, h]) for h in range(H))
     es = max_rel_states(to_host_f32(st), s_ref)
-    print(f"[result] o {eo:.3e} state {es:.3e}", flush=True)
-    assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)
+    eb = max(segment_boundary_err(o_g[0, :, h], o_ref[0, :, h], 1, L, H, sl[h]) for h in range(H))
+    print(f"[result] o {eo:.3e} state {es:.3e} segment-boundary rows {eb:.3e}", flush=True)
+    assert eo <= TOL_BF16 and es <= TOL_BF16 and eb <= TOL_BF16, (eo, es, eb)
 
 
 def test_prefill_segmented_local_starts_no_final_state(la):
@@ -430,7 +438,7 @@ def test_prefill_segmented_local_starts_no_final_state(la):
     assert st is None
     o_ref, _ = oracle.recurrence_batch(q, k, v, sl, s0=s0)
     og = to_host_f32(o)
-    eo = max(rel_l2(og[0, :, h], o_ref[0, :, h]) for h in range(H))
+    eo = max(parity_err(og[0, :, h], o_ref[0, :, h]) for h in range(H))
     print(f"[result] o {eo:.3e}", flush=True)
     assert eo <= TOL_BF16, eo
 
@@ -457,7 +465,7 @@ def test_prefill_prepass_groups(la, L):
     hs = [0, 1, 17, 40, 63]
     o_ref, s_ref = oracle.recurrence_batch(q, k, v, sl, s0=s0, heads=hs)
     og = to_host_f32(o)[:, :, hs]
-    eo = max(rel_l2(og[0, :, i], o_ref[0, :, i]) for i in range(len(hs)))
+    eo = max(parity_err(og[0, :, i], o_ref[0, :, i]) for i in range(len(hs)))
     es = max_rel_states(to_host_f32(st)[:, hs], s_ref)
     print(f"[result] o {eo:.3e} state {es:.3e}", flush=True)
     assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)
@@ -480,7 +488,7 @@ def test_prefill_segmented_batch_slope_mix(la):
     torch.cuda.synchronize()
     o_ref, s_ref = oracle.recurrence_batch(q, k, v, sl, s0=s0)
     og = to_host_f32(o)
-    eo = max(rel_l2(og[b, :, h], o_ref[b, :, h]) for b in range(B) for h in range(H))
+    eo = max(parity_err(og[b, :, h], o_ref[b, :, h]) for b in range(B) for h in range(H))
     es = max_rel_states(to_host_f32(st), s_ref)
     print(f"[result] o {eo:.3e} state {es:.3e}", flush=True)
     assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)

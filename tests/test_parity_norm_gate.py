@@ -10,7 +10,7 @@ import pytest
 import oracle
 import workloads
 from parity_util import (TOL_BF16, TOL_F32, ensure_built, max_rel_per_head, max_rel_states,
-                         rel_l2, to_device, to_host_f32)
+                         parity_err, to_device, to_host_f32)
 
 pytestmark = pytest.mark.gpu
 EPS = workloads.NORM_EPS
@@ -98,7 +98,7 @@ def test_prefill_norm_gate_in_place_state(la):
     torch.cuda.synchronize()
     o_ref, s_ref = oracle.recurrence_batch(q, k, v, sl, s0=s0)
     y_ref = oracle.norm_gate(o_ref, gate, w, EPS)
-    ey = max(rel_l2(to_host_f32(y)[0, :, h], y_ref[0, :, h]) for h in range(H))
+    ey = max(parity_err(to_host_f32(y)[0, :, h], y_ref[0, :, h]) for h in range(H))
     es = max_rel_states(to_host_f32(st), s_ref)
     assert ey <= TOL_BF16 and es <= TOL_BF16, (ey, es)
 
@@ -152,7 +152,7 @@ def test_decode_norm_gate_steps(la, dtype):
         o_ref, st_ref = oracle.decode(q, k, v, sl, st_ref)
         y_ref = oracle.norm_gate(o_ref, gate, w, EPS)
         yg = to_host_f32(y)
-        worst = max(worst, max(rel_l2(yg[b, h], y_ref[b, h]) for b in range(B) for h in range(H)))
+        worst = max(worst, max(parity_err(yg[b, h], y_ref[b, h]) for b in range(B) for h in range(H)))
     es = max_rel_states(to_host_f32(state), st_ref)
     print(f"[result] y {worst:.3e} state {es:.3e}", flush=True)
     assert worst <= tol and es <= tol
@@ -175,7 +175,7 @@ def test_decode_norm_gate_bf16_output(la):
     o_ref, _ = oracle.decode(q, k, v, sl, s0)
     y_ref = oracle.norm_gate(o_ref, gate, w, EPS)
     yg = to_host_f32(y)
-    assert max(rel_l2(yg[b, h], y_ref[b, h]) for b in range(B) for h in range(H)) <= TOL_BF16
+    assert max(parity_err(yg[b, h], y_ref[b, h]) for b in range(B) for h in range(H)) <= TOL_BF16
 
 
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
@@ -203,7 +203,7 @@ def test_prefill_norm_gate_segmented_slope_mix(la, out_dtype):
     o_ref, s_ref = oracle.recurrence_batch(q, k, v, sl, s0=s0)
     y_ref = oracle.norm_gate(o_ref, gate, w, EPS)
     yg = to_host_f32(y)
-    ey = max(rel_l2(yg[0, :, h], y_ref[0, :, h]) for h in range(H))
+    ey = max(parity_err(yg[0, :, h], y_ref[0, :, h]) for h in range(H))
     es = max_rel_states(to_host_f32(st), s_ref)
     print(f"[result] y {ey:.3e} state {es:.3e}", flush=True)
     assert ey <= TOL_BF16 and es <= TOL_BF16, (ey, es)
@@ -230,7 +230,7 @@ def test_prefill_norm_gate_segmented_no_final_state(la):
     o_ref, _ = oracle.recurrence_batch(q, k, v, sl, s0=s0)
     y_ref = oracle.norm_gate(o_ref, gate, w, EPS)
     yg = to_host_f32(y)
-    ey = max(rel_l2(yg[0, :, h], y_ref[0, :, h]) for h in range(H))
+    ey = max(parity_err(yg[0, :, h], y_ref[0, :, h]) for h in range(H))
     print(f"[result] y {ey:.3e}", flush=True)
     assert ey <= TOL_BF16, ey
 
@@ -254,7 +254,7 @@ def test_prefill_norm_gate_segmented_batch(la):
     o_ref, s_ref = oracle.recurrence_batch(q, k, v, sl, s0=s0)
     y_ref = oracle.norm_gate(o_ref, gate, w, EPS)
     yg = to_host_f32(y)
-    ey = max(rel_l2(yg[b, :, h], y_ref[b, :, h]) for b in range(B) for h in range(H))
+    ey = max(parity_err(yg[b, :, h], y_ref[b, :, h]) for b in range(B) for h in range(H))
     es = max_rel_states(to_host_f32(st), s_ref)
     print(f"[result] y {ey:.3e} state {es:.3e}", flush=True)
     assert ey <= TOL_BF16 and es <= TOL_BF16, (ey, es)

@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import workloads
-from parity_util import TOL_BF16, TOL_F32, ensure_built, rel_l2, to_device, to_host_f32
+from parity_util import TOL_BF16, TOL_F32, ensure_built, parity_err, to_device, to_host_f32
 
 pytestmark = pytest.mark.gpu
 
@@ -49,11 +49,11 @@ def test_decode_slots_small_pool(la, dtype):
         o_ref, ref = oracle.decode_slots(q, k, v, sl, ref, ids)
         og = to_host_f32(o)
         assert np.all(og[1] == 0.0) and np.all(og[5] == 0.0), "padding rows must be zero"
-        worst = max(worst, max(rel_l2(og[b, h], o_ref[b, h]) for b in (0, 2, 3, 4) for h in range(H)))
+        worst = max(worst, max(parity_err(og[b, h], o_ref[b, h]) for b in (0, 2, 3, 4) for h in range(H)))
     pg = to_host_f32(pool)
     for s in (1, 2, 4, 5, 6, 8):  # never addressed
         assert np.array_equal(pg[s], pool0[s]), f"slot {s} changed"
-    es = max(rel_l2(pg[s, h], ref[s, h]) for s in (0, 3, 7, 9) for h in range(H))
+    es = max(parity_err(pg[s, h], ref[s, h]) for s in (0, 3, 7, 9) for h in range(H))
     print(f"[result] o {worst:.3e} pool {es:.3e}", flush=True)
     assert worst <= tol and es <= tol
 
@@ -93,8 +93,8 @@ def test_decode_slots_full_batch(la):
             x = [to_host_f32(qkv[j, b:b + 1]) for j in range(3)]
             o_ref, st = oracle.decode(x[0], x[1], x[2], sl, refs[b][None])
             refs[b] = st[0]
-            worst = max(worst, max(rel_l2(og[b, h], o_ref[0, h]) for h in range(H)))
-    es = max(rel_l2(to_host_f32(pool[int(ids[b])])[h], refs[b][h]) for b in refs for h in range(H))
+            worst = max(worst, max(parity_err(og[b, h], o_ref[0, h]) for h in range(H)))
+    es = max(parity_err(to_host_f32(pool[int(ids[b])])[h], refs[b][h]) for b in refs for h in range(H))
     for s in untouched:
         assert np.array_equal(to_host_f32(pool[s]), pool0_sampled[s])
     print(f"[result] o {worst:.3e} pool {es:.3e}", flush=True)

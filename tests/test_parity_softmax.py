@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import workloads
-from parity_util import TOL_BF16, ensure_built, rel_l2, to_device, to_host_f32
+from parity_util import TOL_BF16, ensure_built, parity_err, to_device, to_host_f32
 
 pytestmark = pytest.mark.gpu
 
@@ -42,8 +42,8 @@ def _run(la, seed, B, L, Hq, Hkv, R, out, pos0=0, std=1.0, base=10000.0, scale=N
     o_ref = oracle.softmax_attention(q, k, v, rope_dims=R, base=base, scale=scale, pos0=pos0)
     kr_ref = oracle.rope(k, pos0 + np.arange(L), R, base)
     og, kg = to_host_f32(o), to_host_f32(kr)
-    worst = max(rel_l2(og[b, :, h], o_ref[b, :, h]) for b in range(B) for h in range(Hq))
-    wk = max(rel_l2(kg[b, :, g], kr_ref[b, :, g]) for b in range(B) for g in range(Hkv))
+    worst = max(parity_err(og[b, :, h], o_ref[b, :, h]) for b in range(B) for h in range(Hq))
+    wk = max(parity_err(kg[b, :, g], kr_ref[b, :, g]) for b in range(B) for g in range(Hkv))
     print(f"[result] o {worst:.3e} k_rope {wk:.3e}", flush=True)
     assert worst <= TOL_BF16, worst
     assert wk <= TOL_ROPE, wk
@@ -106,8 +106,8 @@ def test_softmax_prefill_m1_layer_sampled(la):
     qh, kh, vh = to_host_f32(q), to_host_f32(k), to_host_f32(v)
     ref = oracle.softmax_attention_rows(qh, kh, vh, rows, rope_dims=R, base=base)
     og = to_host_f32(o)[:, rows]
-    worst = max(rel_l2(og[0, i, h], ref[0, i, h]) for i in range(len(rows)) for h in range(Hq))
+    worst = max(parity_err(og[0, i, h], ref[0, i, h]) for i in range(len(rows)) for h in range(Hq))
     kref = oracle.rope(kh[:, rows], np.array(rows), R, base)
-    wk = max(rel_l2(to_host_f32(kr)[0, rows][:, g], kref[0, :, g]) for g in range(Hkv))
+    wk = max(parity_err(to_host_f32(kr)[0, rows][:, g], kref[0, :, g]) for g in range(Hkv))
     print(f"[result] o {worst:.3e} k_rope {wk:.3e}", flush=True)
     assert worst <= TOL_BF16 and wk <= TOL_ROPE

@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import workloads
-from parity_util import TOL_BF16, ensure_built, rel_l2, to_device, to_host_f32
+from parity_util import TOL_BF16, ensure_built, parity_err, to_device, to_host_f32
 
 pytestmark = pytest.mark.gpu
 
@@ -56,11 +56,11 @@ def _check(la, seed, B, cap, Hq, Hkv, lengths, R=64, out="f32", split=True, base
             assert np.all(og[b] == 0), f"padding row {b} not zero"
             assert np.array_equal(kg[b], kc[b]) and np.array_equal(vg[b], vc[b]), f"padding row {b} touched the cache"
             continue
-        worst = max(worst, max(rel_l2(og[b, h], o_ref[b, h]) for h in range(Hq)))
+        worst = max(worst, max(parity_err(og[b, h], o_ref[b, h]) for h in range(Hq)))
         others = np.arange(cap) != n
         assert np.array_equal(kg[b, others], kc[b, others]) and np.array_equal(vg[b, others], vc[b, others])
         assert np.array_equal(vg[b, n], vn[b])
-        assert rel_l2(kg[b, n], kc_ref[b, n]) <= TOL_ROPE
+        assert parity_err(kg[b, n], kc_ref[b, n]) <= TOL_ROPE
     print(f"[result] o {worst:.3e}", flush=True)
     assert worst <= TOL_BF16, worst
 
@@ -103,8 +103,8 @@ def test_softmax_decode_after_prefill(la):
     torch.cuda.synchronize()
     ref = oracle.softmax_attention(q, k, v)[:, L]
     og, of = to_host_f32(o), to_host_f32(o_full)[:, L]
-    e1 = max(rel_l2(og[b, h], ref[b, h]) for b in range(B) for h in range(Hq))
-    e2 = max(rel_l2(og[b, h], of[b, h]) for b in range(B) for h in range(Hq))
+    e1 = max(parity_err(og[b, h], ref[b, h]) for b in range(B) for h in range(Hq))
+    e2 = max(parity_err(og[b, h], of[b, h]) for b in range(B) for h in range(Hq))
     print(f"[result] vs oracle {e1:.3e} vs prefill row {e2:.3e}", flush=True)
     assert e1 <= TOL_BF16 and e2 <= TOL_BF16
     assert torch.equal(kc[:, L], kr_full[:, L])  # same rope rows from both paths
@@ -135,8 +135,8 @@ def test_softmax_decode_m1_layer(la):
     ref, kref, _ = oracle.softmax_decode(to_host_f32(q)[sel], to_host_f32(kn)[sel], to_host_f32(vn)[sel], kc0, vc0,
                                          lengths[sel], rope_dims=wl.extra["rope_dims"], base=wl.extra["rope_base"])
     og = to_host_f32(o)[sel]
-    worst = max(rel_l2(og[i, h], ref[i, h]) for i in range(len(sel)) for h in range(Hq))
+    worst = max(parity_err(og[i, h], ref[i, h]) for i in range(len(sel)) for h in range(Hq))
     kg = to_host_f32(kc[sel])
-    wk = max(rel_l2(kg[i, lengths[s]], kref[i, lengths[s]]) for i, s in enumerate(sel))
+    wk = max(parity_err(kg[i, lengths[s]], kref[i, lengths[s]]) for i, s in enumerate(sel))
     print(f"[result] o {worst:.3e} appended k {wk:.3e}", flush=True)
     assert worst <= TOL_BF16 and wk <= TOL_ROPE

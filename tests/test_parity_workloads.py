@@ -12,7 +12,9 @@ configuration the benchmark times.
   * Varlen prefill: 16 sequences of 1024..65536 tokens with N(0, 0.01) carried-in
     states; every final state, and outputs on sampled heads.
 
-Relative L2 per (sequence, head) <= 1e-2 (bf16 inputs).
+Relative L2 per (sequence, head) <= 1e-2 (bf16 inputs), and every output row
+within 5e-2 of the head's RMS row norm (parity_util.parity_err); the rows next
+to the segmented plan's switches are also reported on their own.
 """
 
 import numpy as np
@@ -20,7 +22,7 @@ import pytest
 
 import oracle
 import workloads
-from parity_util import TOL_BF16, ensure_built, rel_l2, to_host_f32
+from parity_util import TOL_BF16, ensure_built, parity_err, segment_boundary_err, to_host_f32
 
 pytestmark = pytest.mark.gpu
 
@@ -56,10 +58,13 @@ def test_m1_layer_all_heads(la):
     hq, hk, hv = (to_host_f32(x) for x in (q, k, v))
     o_ref, s_ref = oracle.recurrence_batch(hq, hk, hv, sl)
     o_g, s_g = to_host_f32(o), to_host_f32(st)
-    worst_o = max(rel_l2(o_g[0, :, h], o_ref[0, :, h]) for h in range(w.heads))
-    worst_s = max(rel_l2(s_g[0, h], s_ref[0, h]) for h in range(w.heads))
-    print(f"[result] worst rel L2: o {worst_o:.3e} state {worst_s:.3e}", flush=True)
-    assert worst_o <= TOL_BF16 and worst_s <= TOL_BF16
+    worst_o = max(parity_err(o_g[0, :, h], o_ref[0, :, h]) for h in range(w.heads))
+    worst_s = max(parity_err(s_g[0, h], s_ref[0, h]) for h in range(w.heads))
+    worst_b = max(segment_boundary_err(o_g[0, :, h], o_ref[0, :, h], 1, w.seqlen, w.heads, sl[h])
+                  for h in range(w.heads))
+    print(f"[result] worst parity err: o {worst_o:.3e} state {worst_s:.3e} "
+          f"segment-boundary rows {worst_b:.3e}", flush=True)
+    assert worst_o <= TOL_BF16 and worst_s <= TOL_BF16 and worst_b <= TOL_BF16
 
 
 def test_m1_layer_norm_gate_all_heads(la):
@@ -81,8 +86,8 @@ def test_m1_layer_norm_gate_all_heads(la):
     o_ref, s_ref = oracle.recurrence_batch(hq, hk, hv, sl)
     y_ref = oracle.norm_gate(o_ref, to_host_f32(gate), nw, workloads.NORM_EPS)
     y_g, s_g = to_host_f32(y), to_host_f32(st)
-    worst_y = max(rel_l2(y_g[0, :, h], y_ref[0, :, h]) for h in range(w.heads))
-    worst_s = max(rel_l2(s_g[0, h], s_ref[0, h]) for h in range(w.heads))
+    worst_y = max(parity_err(y_g[0, :, h], y_ref[0, :, h]) for h in range(w.heads))
+    worst_s = max(parity_err(s_g[0, h], s_ref[0, h]) for h in range(w.heads))
     print(f"[result] worst rel L2: y {worst_y:.3e} state {worst_s:.3e}", flush=True)
     assert worst_y <= TOL_BF16 and worst_s <= TOL_BF16
 
@@ -107,9 +112,9 @@ def test_m1_layer_backward_all_heads(la):
     worst = {}
     for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
         gh = to_host_f32(g)
-        worst[name] = max(rel_l2(gh[0, :, h], r[0, :, h]) for h in range(w.heads))
+        worst[name] = max(parity_err(gh[0, :, h], r[0, :, h]) for h in range(w.heads))
     sg = to_host_f32(dsi)
-    worst["ds0"] = max(rel_l2(sg[0, h], rs[0, h]) for h in range(w.heads))
+    worst["ds0"] = max(parity_err(sg[0, h], rs[0, h]) for h in range(w.heads))
     print(f"[result] worst rel L2 {worst}", flush=True)
     assert max(worst.values()) <= TOL_BF16
 
@@ -131,10 +136,13 @@ def test_long_context_1m_sampled_heads(la):
     o_ref, s_ref = oracle.recurrence_batch(hq, hk, hv, sl[hs])
     s_g = to_host_f32(st)
     for j, h in enumerate(hs):
-        eo = rel_l2(head_slice(o, h), o_ref[0, :, j])
-        es = rel_l2(s_g[0, h], s_ref[0, j])
-        print(f"[result] head {h}: o {eo:.3e} state {es:.3e}", flush=True)
-        assert eo <= TOL_BF16 and es <= TOL_BF16
+        og = head_slice(o, h)
+        eo = parity_err(og, o_ref[0, :, j])
+        es = parity_err(s_g[0, h], s_ref[0, j])
+        eb = segment_boundary_err(og, o_ref[0, :, j], 1, w.seqlen, w.heads, sl[h])
+        print(f"[result] head {h}: o {eo:.3e} state {es:.3e} segment-boundary rows {eb:.3e}",
+              flush=True)
+        assert eo <= TOL_BF16 and es <= TOL_BF16 and eb <= TOL_BF16
 
 
 def _history_states(seed, seqs, H, d, history):
@@ -183,11 +191,11 @@ def test_batched_decode_1000_steps_sampled_sequences(la):
     worst_o = 0.0
     for j in range(len(seqs)):
         for h in range(H):
-            worst_o = max(worst_o, rel_l2(og[:, j, h], o_ref[j, :, h]))
+            worst_o = max(worst_o, parity_err(og[:, j, h], o_ref[j, :, h]))
     sg = to_host_f32(state[seqs])
-    worst_s = max(rel_l2(sg[j, h], s_ref[j, h]) for j in range(len(seqs)) for h in range(H))
+    worst_s = max(parity_err(sg[j, h], s_ref[j, h]) for j in range(len(seqs)) for h in range(H))
     # per-step check on the worst (sequence, head) as well
-    step_worst = max(rel_l2(og[t, j, h], o_ref[j, t, h]) for t in (0, steps // 2, steps - 1)
+    step_worst = max(parity_err(og[t, j, h], o_ref[j, t, h]) for t in (0, steps // 2, steps - 1)
                      for j in range(len(seqs)) for h in range(H))
     print(f"[result] o {worst_o:.3e} (single steps {step_worst:.3e}) state {worst_s:.3e}",
           flush=True)
@@ -214,9 +222,9 @@ def test_batched_decode_all_units_short(la):
     h = to_host_f32(qkv).transpose(1, 2, 0, 3, 4)  # [3, B, steps, H, d]
     o_ref, s_ref = oracle.recurrence_batch(h[0], h[1], h[2], workloads.slopes(H), s0=s0)
     sg = to_host_f32(state)
-    worst_s = max(rel_l2(sg[b, hh], s_ref[b, hh]) for b in range(B) for hh in range(H))
+    worst_s = max(parity_err(sg[b, hh], s_ref[b, hh]) for b in range(B) for hh in range(H))
     og = np.stack([to_host_f32(x) for x in outs], axis=1)  # [B, steps, H, d]
-    worst_o = max(rel_l2(og[b, :, hh], o_ref[b, :, hh]) for b in range(B) for hh in range(H))
+    worst_o = max(parity_err(og[b, :, hh], o_ref[b, :, hh]) for b in range(B) for hh in range(H))
     print(f"[result] o {worst_o:.3e} state {worst_s:.3e}", flush=True)
     assert worst_o <= TOL_BF16 and worst_s <= TOL_BF16
 
@@ -244,7 +252,7 @@ def test_varlen_carried_state(la):
         kh = to_host_f32(k[:, h0:h0 + 8].contiguous())
         vh = to_host_f32(v[:, h0:h0 + 8].contiguous())
         _, s_ref = oracle.recurrence_packed(kh, kh, vh, sl[hs], cu, s0=s0h[:, hs], want_o=False)
-        worst_s = max(worst_s, max(rel_l2(sg[n, h0 + j], s_ref[n, j])
+        worst_s = max(worst_s, max(parity_err(sg[n, h0 + j], s_ref[n, j])
                                    for n in range(len(lens)) for j in range(8)))
     # outputs on sampled heads
     hs = SAMPLED_HEADS
@@ -257,6 +265,6 @@ def test_varlen_carried_state(la):
     for n in range(len(lens)):
         a, b = int(cu[n]), int(cu[n + 1])
         for j in range(len(hs)):
-            worst_o = max(worst_o, rel_l2(og[a:b, j], o_ref[a:b, j]))
+            worst_o = max(worst_o, parity_err(og[a:b, j], o_ref[a:b, j]))
     print(f"[result] o {worst_o:.3e} state {worst_s:.3e}", flush=True)
     assert worst_o <= TOL_BF16 and worst_s <= TOL_BF16
