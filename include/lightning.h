@@ -18,9 +18,9 @@
  * "⊙" with a length-B vector scales token rows. The value of O and of the final
  * state does not depend on B: the block form is an exact re-association of the
  * per-token recurrence S <- e^{-s_h} S + k^T v, o = q S (the token sees its own
- * key). The kernels may leave out a carried-state term once its decay factor
- * e^{-s t} is below 2^-24 (the unit roundoff of fp32, and far below the bf16
- * rounding of the products' operands).
+ * key). The kernels may leave out a finite carried-state term once its decay
+ * factor e^{-s t} is below 2^-24 (the unit roundoff of fp32, and far below the
+ * bf16 rounding of the products' operands).
  * lt_prefill, lt_prefill_varlen and lt_decode write the raw sum; the
  * *_norm_gate variants also apply the normalisation and gate that follow the
  * sum in the §03 data-flow figure before anything is stored.
@@ -36,7 +36,20 @@
  *  - State tensors are FP32 [units, heads, head_dim (key index), head_dim
  *    (value index)]: S[r][c] multiplies key component r into value column c.
  *  - Slopes are FP32 [heads], s_h >= 0 (0 = no decay). Their values are read on
- *    the device and are not validated; NaN/Inf anywhere propagate to outputs.
+ *    the device and are not validated.
+ *  - Non-finite values. A NaN or Inf in any input (q, k, v, a carried-in
+ *    state, a slope) makes non-finite every output that the exact operator
+ *    makes non-finite, on every launch plan (NaN or Inf: which of the two may
+ *    differ from the exact result). The cutoff of carried-state terms below
+ *    2^-24 is never applied to a carried-in state that holds a NaN or Inf.
+ *    Outputs the exact operator leaves finite stay finite and within rounding,
+ *    with one exception: a NaN or Inf in v at token t can also make NaN, in the
+ *    value columns it holds, the outputs of the earlier tokens of t's 64-token
+ *    block (blocks counted from the sequence start): masked entries of the
+ *    in-block product are zeros multiplied on the matrix cores, and 0 * Inf is
+ *    NaN there. (The backward: non-finite gradients wherever the exact
+ *    derivative is non-finite; a non-finite input can also make NaN the other
+ *    gradients of its 64-token block, counted from either end.)
  *  - Arguments are validated on the host before any launch. A failed check
  *    returns its status and enqueues nothing. A failed launch returns
  *    LT_ERR_HIP. No C++ exception crosses this interface.
@@ -239,7 +252,10 @@ LT_API lt_status lt_decode_slots(const void *q, const void *k, const void *v, lt
  *   norm_weight  [heads, head_dim] fp32.
  *   eps          finite, >= 0; otherwise LT_ERR_VALUE. With eps = 0 a zero
  *                output row gives NaN, as the formula does.
- *   y            takes the place of o (same shape, out_dtype).
+ *   y            takes the place of o (same shape, out_dtype). A row whose
+ *                sum o holds a NaN or Inf gives a row of y holding a NaN (the
+ *                norm of an infinite row is infinite: its infinite columns
+ *                come out NaN and the others 0, or the whole row NaN).
  *
  * Every other argument, the state handling and the workspace are those of
  * lt_prefill / lt_prefill_varlen / lt_decode. The prefill variants take bf16

@@ -377,13 +377,13 @@ __global__ __launch_bounds__(NT) void bwd_kv_kernel(BackwardArgs a, Segmented sp
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int diff = (32 * sJ + (lo & 31)) - (32 * sI + 8 * (v >> 2) + 4 * (lo >> 5) + (v & 3));
-                dscore[v] = diff >= 0 ? fast_exp2(-s2 * (float)diff) : 0.f;
+                dscore[v] = masked_decay(diff, s2);
             }
 #pragma unroll
             for (int gv = 0; gv < 4; ++gv) {
                 bf16x4 pv;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) pv[r] = static_cast<__bf16>(sc[4 * gv + r] * dscore[4 * gv + r]);
+                for (int r = 0; r < 4; ++r) pv[r] = static_cast<__bf16>(mask_mul(sc[4 * gv + r], dscore[4 * gv + r]));
                 *reinterpret_cast<bf16x4 *>(T + LS::off(32 * sJ + r32, 32 * sI + 8 * gv + 4 * hf)) = pv;
             }
         }
@@ -442,11 +442,13 @@ __global__ __launch_bounds__(NT) void bwd_kv_kernel(BackwardArgs a, Segmented sp
     }
 
     if (fix) {  // end carry of this local-start segment, for the chain
-        float *dst = sp.start_state(sp.unit(ws, uh), g);
+        float *u = sp.unit(ws, uh);
+        float *dst = sp.start_state(u, g);
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
             for (int v = 0; v < 16; ++v) dst[sidx(db, v)] = R[db][v];
+        if (g + 1 < sp.segments) flag_end_state(end_flags(sp, u, g), R, w, lane);
     } else if (a.d_state_in && g == sp.segments - 1) {  // the segment holding token 0
         float *dst = a.d_state_in + (size_t)uh * D * D;
 #pragma unroll
@@ -540,6 +542,7 @@ __global__ __launch_bounds__(NT) void rev_fix_kernel(BackwardArgs a, Segmented s
     __shared__ __attribute__((aligned(16))) __bf16 Vt[C * D];
     __shared__ __attribute__((aligned(16))) float Os[C * D];
     __shared__ long long first[kFixMaxPairs + 1];  // first chunk number of each pair
+    __shared__ long long prows[kFixMaxPairs];       // rows corrected in each pair
 
     const int tid = threadIdx.x;
     const long long L = a.seqlen;
@@ -559,17 +562,21 @@ __global__ __launch_bounds__(NT) void rev_fix_kernel(BackwardArgs a, Segmented s
         return;
     }
 
-    // chunks per pair, then their prefix sums
+    // rows and chunks per pair (the whole segment when its carried-in carry is
+    // non-finite), then the chunks' prefix sums
     const int gs = sp.segments - 1;
     const int pairs = a.units * a.heads * gs;
-    auto rows_of = [&](float s2, int g) {
-        const long long len = seg_len_at(sp, L, g), fl = fix_len(s2, sp.seg_len) + 1;  // n = 0 .. fix_len
-        return fl < len ? fl : len;
-    };
     long long x = 0;
     if (tid < pairs) {
-        const float s2 = a.slopes[(tid / gs) % a.heads] * LOG2E;
-        if (fix_head(s2, sp.seg_len, sp.fix_osz)) x = (rows_of(s2, 1 + tid % gs) + C - 1) / C;
+        const int g = 1 + tid % gs, uh = tid / gs;
+        const float s2 = a.slopes[uh % a.heads] * LOG2E;
+        long long rows = 0;
+        if (fix_head(s2, sp.seg_len, sp.fix_osz)) {
+            const long long len = seg_len_at(sp, L, g), fl = fix_len(s2, sp.seg_len) + 1;  // n = 0 .. fix_len
+            rows = start_poisoned(sp, sp.unit(ws, uh), g) || fl > len ? len : fl;
+        }
+        prows[tid] = rows;
+        x = (rows + C - 1) / C;
     }
     for (int off = 1; off < kFixMaxPairs; off <<= 1) {
         if (tid < kFixMaxPairs) first[tid + 1] = x;
@@ -607,7 +614,7 @@ __global__ __launch_bounds__(NT) void rev_fix_kernel(BackwardArgs a, Segmented s
         c.g = 1 + p % gs;
         const int h = c.uh % a.heads, n = c.uh / a.heads;
         c.s2 = a.slopes[h] * LOG2E;
-        const long long T = rows_of(c.s2, c.g);
+        const long long T = uniform64(prows[p]);
         c.seg_hi = L - (long long)c.g * sp.seg_len;
         const long long ci = uniform64(j - first[p]);
         c.tlo = c.seg_hi - C * (ci + 1);

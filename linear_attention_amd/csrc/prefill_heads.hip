@@ -293,7 +293,7 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
         const int diff = (32 * qb + r32) - (32 * kb + 8 * (v >> 2) + 4 * hf + (v & 3));
-        dscore[v] = diff >= 0 ? fast_exp2(-s2 * (float)diff) : 0.f;
+        dscore[v] = masked_decay(diff, s2);
     }
 
     // Two register stages: sub-block c is staged in st[c % 2] and its loads are
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
             for (int gv = 0; gv < 4; ++gv) {
                 bf16x4 p;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) p[r] = static_cast<__bf16>(sc[4 * gv + r] * dscore[4 * gv + r]);
+                for (int r = 0; r < 4; ++r) p[r] = static_cast<__bf16>(mask_mul(sc[4 * gv + r], dscore[4 * gv + r]));
                 *reinterpret_cast<bf16x4 *>(Ps + LP::off(32 * qb + r32, 32 * kb + 8 * gv + 4 * hf)) = p;
             }
         }
@@ -409,11 +409,13 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
     }
 
     if (fix) {  // end state of this local-start segment, for the correction pass
-        float *dst = sp.start_state(sp.unit(ws, uh), g);
+        float *u = sp.unit(ws, uh);
+        float *dst = sp.start_state(u, g);
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
             for (int v = 0; v < 16; ++v) dst[sidx(db, v)] = S[db][v];
+        if (g + 1 < segments) flag_end_state(end_flags(sp, u, g), S, w, lane);
     } else if (a.state_out && g == segments - 1) {
         const long long sb = (long long)uh * D * D;
 #pragma unroll
@@ -559,7 +561,7 @@ __global__ __launch_bounds__(NT) void slice_kernel(PrefillArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
         const int diff = (32 * qb + r32) - (32 * kb + 8 * (v >> 2) + 4 * hf + (v & 3));
-        dscore[v] = diff >= 0 ? fast_exp2(-s2 * (float)diff) : 0.f;
+        dscore[v] = masked_decay(diff, s2);
     }
 
     SliceStage st0, st1;
@@ -596,7 +598,7 @@ __global__ __launch_bounds__(NT) void slice_kernel(PrefillArgs a) {
             for (int gv = 0; gv < 4; ++gv) {
                 bf16x4 p;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) p[r] = static_cast<__bf16>(sc[4 * gv + r] * dscore[4 * gv + r]);
+                for (int r = 0; r < 4; ++r) p[r] = static_cast<__bf16>(mask_mul(sc[4 * gv + r], dscore[4 * gv + r]));
                 *reinterpret_cast<bf16x4 *>(Ps + LP::off(32 * qb + r32, 32 * kb + 8 * gv + 4 * hf)) = p;
             }
         }
@@ -752,7 +754,8 @@ __device__ __forceinline__ long long fix_rows(float s2, long long seg_len, long 
 
 template <typename OutT, bool NG>
 __device__ __forceinline__ FixChunk<OutT> fix_chunk(const PrefillArgs &a, const Segmented &sp,
-                                                    const long long *first, long long j, int &p) {
+                                                    const long long *first, const long long *prows,
+                                                    long long j, int &p) {
     while (first[p + 1] <= j) ++p;
     p = __builtin_amdgcn_readfirstlane(p);  // the same for every lane
     FixChunk<OutT> x;
@@ -763,7 +766,7 @@ __device__ __forceinline__ FixChunk<OutT> fix_chunk(const PrefillArgs &a, const 
     const int h = x.uh % a.heads, n = x.uh / a.heads;
     x.h = h;
     x.s2 = a.slopes[h] * LOG2E;
-    const long long T = fix_rows<NG>(x.s2, sp.seg_len, seg_len_at(sp, a.seqlen, x.g));
+    const long long T = uniform64(prows[p]);
     x.t0 = uniform64((j - first[p]) * C);
     x.m = (int)(T - x.t0 < C ? T - x.t0 : C);
     const long long row = (long long)n * a.seqlen + (long long)x.g * sp.seg_len + x.t0;
@@ -826,6 +829,7 @@ __global__ __launch_bounds__(NT, 4) void fix_kernel(PrefillArgs a, Segmented sp,
     __shared__ __attribute__((aligned(16))) __bf16 Sts[D * D];
     __shared__ __attribute__((aligned(16))) float Os[C * D];
     __shared__ long long first[kFixMaxPairs + 1];  // first chunk number of each pair
+    __shared__ long long prows[kFixMaxPairs];       // rows corrected in each pair
     __bf16 *const Qs = reinterpret_cast<__bf16 *>(Os);
 
     const int tid = threadIdx.x;
@@ -845,15 +849,22 @@ __global__ __launch_bounds__(NT, 4) void fix_kernel(PrefillArgs a, Segmented sp,
         return;
     }
 
-    // chunks per pair (0 unless the head takes local starts), then their
+    // rows and chunks per pair (none unless the head takes local starts; the
+    // whole segment when its carried-in state is non-finite), then the chunks'
     // prefix sums (inclusive scan over the first kFixMaxPairs threads)
     const int gs = sp.segments - 1;
     const int pairs = a.units * a.heads * gs;
     long long x = 0;
     if (tid < pairs) {
-        const int g = 1 + tid % gs;
-        const float s2 = a.slopes[(tid / gs) % a.heads] * LOG2E;
-        if (fix_head(s2, sp.seg_len, sp.fix_osz)) x = (fix_rows<NG>(s2, sp.seg_len, seg_len_at(sp, a.seqlen, g)) + C - 1) / C;
+        const int g = 1 + tid % gs, uh = tid / gs;
+        const float s2 = a.slopes[uh % a.heads] * LOG2E;
+        long long rows = 0;
+        if (fix_head(s2, sp.seg_len, sp.fix_osz)) {
+            const long long len = seg_len_at(sp, a.seqlen, g);
+            rows = start_poisoned(sp, sp.unit(ws, uh), g) ? len : fix_rows<NG>(s2, sp.seg_len, len);
+        }
+        prows[tid] = rows;
+        x = (rows + C - 1) / C;
     }
     for (int off = 1; off < kFixMaxPairs; off <<= 1) {
         if (tid < kFixMaxPairs) first[tid + 1] = x;
@@ -891,7 +902,7 @@ __global__ __launch_bounds__(NT, 4) void fix_kernel(PrefillArgs a, Segmented sp,
             r.load(c.o, ts, c.m, th);
     };
     int p = 0;
-    FixChunk<OutT> cur = fix_chunk<OutT, NG>(a, sp, first, j0, p);
+    FixChunk<OutT> cur = fix_chunk<OutT, NG>(a, sp, first, prows, j0, p);
     uint4 qa[2];
     Rows ra;
     load_q(cur, qa, tid);
@@ -911,7 +922,7 @@ __global__ __launch_bounds__(NT, 4) void fix_kernel(PrefillArgs a, Segmented sp,
         uint4 qb[2] = {qa[0], qa[1]};
         Rows rb = ra;
         if (j + 1 < j1) {
-            nxt = fix_chunk<OutT, NG>(a, sp, first, j + 1, p);
+            nxt = fix_chunk<OutT, NG>(a, sp, first, prows, j + 1, p);
             load_q(nxt, qb, tl);
             load_rows(rb, nxt, tl);
         }

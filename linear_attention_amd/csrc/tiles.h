@@ -28,6 +28,19 @@ static_assert(D == 128 && C == 64, "tile shapes are fixed below");
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Masked, decayed scores. A score of key j for query i is multiplied by
+// D_ij = e^{-s(i-j)} for i >= j and is 0 for i < j. The product uses the
+// legacy multiply (v_mul_legacy_f32: 0 times anything, NaN and Inf included,
+// is 0), so a NaN or Inf score from a non-finite q or k never reaches a query
+// that cannot see that key, while every visible entry keeps a factor of at
+// least 2^-126 (a decay that underflows contributes below 1e-38 instead of
+// 0), through which a NaN or Inf still propagates as in the exact operator.
+__device__ __forceinline__ float masked_decay(int diff, float s2) {
+    return diff >= 0 ? fmaxf(fast_exp2(-s2 * (float)diff), 0x1p-126f) : 0.f;
+}
+extern "C" __device__ float lt_fmul_legacy(float, float) __asm("llvm.amdgcn.fmul.legacy");
+__device__ __forceinline__ float mask_mul(float score, float decay) { return lt_fmul_legacy(score, decay); }
+
 __device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -342,6 +355,42 @@ struct Segmented {
     __device__ float *partial(float *u, int g) const { return slot(u, partial_slot(g)); }
     __device__ float *start_state(float *u, int g) const { return slot(u, pieces + segments - 1 + g); }
 };
+
+// Non-finite carried-in states. The correction's cutoff is sound only for a
+// finite S_in: e^{-s(t+1)} q_t S_in is then below 2^-24 of its scale past
+// fix_len tokens, but a NaN or Inf in S_in reaches every later token of the
+// exact operator. So the main pass flags each local-start segment whose end
+// state E_g holds a NaN or Inf, and the correction pass treats the whole of
+// segment g as "first tokens" when any of E_0 .. E_{g-1} is flagged (S_in(g)
+// is then non-finite). The flags of E_g (g <= segments - 2) sit in the slot
+// of the partial state B_{g+1}, which heads on local starts never use: one int
+// per wave of the segment's workgroup.
+__device__ __forceinline__ bool nonfinite(float x) {
+    return (__float_as_uint(x) & 0x7f800000u) == 0x7f800000u;
+}
+__device__ __forceinline__ int *end_flags(const Segmented &sp, float *u, int g) {
+    return reinterpret_cast<int *>(sp.partial(u, g + 1));
+}
+// Wave w's flag of its accumulator blocks of E_g.
+__device__ __forceinline__ void flag_end_state(int *flags, const f32x16 (&S)[2], int w, int lane) {
+    bool bad = false;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) bad |= nonfinite(S[db][v]);
+    const bool any = __ballot(bad) != 0;
+    if (lane == 0) flags[w] = any ? 1 : 0;
+}
+// S_in(g) non-finite: some E_j, j < g, flagged.
+__device__ __forceinline__ bool start_poisoned(const Segmented &sp, float *u, int g) {
+    int bad = 0;
+    for (int j = 0; j < g; ++j) {
+        const int *f = end_flags(sp, u, j);
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w) bad |= f[w];
+    }
+    return bad != 0;
+}
 
 // Correction passes: (unit, head, segment g >= 1) pairs of a segmented plan
 // (fewer than 256), and the final-state slices (4 elements per thread).

@@ -849,3 +849,38 @@ def test_softmax_rows_match_full_form():
     full = oracle.softmax_attention(q, k, v, rope_dims=R, base=500.0, scale=0.3, pos0=77)
     part = oracle.softmax_attention_rows(q, k, v, rows, rope_dims=R, base=500.0, scale=0.3, pos0=77)
     assert rel(part, full[:, rows]) < 1e-13
+
+
+def test_recurrence_propagates_non_finite_inputs():
+    """The exact operator's non-finite pattern (reading 14: NaN and Inf
+    propagate), pinned by what the recurrence S <- e^{-s} S + k^T v, o = q S
+    implies: a NaN in feature r of k_j makes row r of every later state NaN, so
+    every output from token j on is NaN and every earlier one finite; an Inf in
+    column c of v_j makes column c of every later state infinite, so column c of
+    every output from token j on is non-finite and nothing else is; a NaN in q_i
+    touches output i only; a NaN at (r, c) of S_0 column c of every output."""
+    L, d, s = 40, 16, 0.3
+    g = np.random.default_rng(77)
+    base = [g.standard_normal((L, d)).astype(np.float32) for _ in range(3)]
+
+    def run(q=None, k=None, v=None, s0=None):
+        x = [b.copy() for b in base]
+        for i, (arr, spot) in enumerate(((x[0], q), (x[1], k), (x[2], v))):
+            if spot:
+                arr[spot[0], spot[1]] = spot[2]
+        o, S = oracle.recurrence(x[0], x[1], x[2], s, s0=s0)
+        return ~np.isfinite(o), ~np.isfinite(S)
+
+    bad, sbad = run(k=(10, 3, np.nan))
+    assert not bad[:10].any() and bad[10:].all()
+    assert sbad[3].all() and not np.delete(sbad, 3, axis=0).any()
+    bad, sbad = run(v=(25, 5, np.inf))
+    assert not bad[:25].any() and bad[25:, 5].all() and not np.delete(bad, 5, axis=1).any()
+    assert sbad[:, 5].all() and not np.delete(sbad, 5, axis=1).any()
+    bad, _ = run(q=(7, 0, np.nan))
+    assert bad[7].all() and not np.delete(bad, 7, axis=0).any()
+    s0 = np.zeros((d, d))
+    s0[2, 9] = np.nan
+    bad, sbad = run(s0=s0)
+    assert bad[:, 9].all() and not np.delete(bad, 9, axis=1).any()
+    assert sbad[2, 9] and sbad.sum() == 1
