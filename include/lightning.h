@@ -83,7 +83,8 @@ typedef enum {
     LT_ERR_DTYPE = 4,     /* unsupported dtype code */
     LT_ERR_ALIAS = 5,     /* an output overlaps another buffer */
     LT_ERR_HIP = 6,       /* the HIP runtime reported an error at launch */
-    LT_ERR_VALUE = 7      /* a scalar argument is out of range (eps of the norm-gate variants) */
+    LT_ERR_VALUE = 7,     /* a scalar argument is out of range (eps of the norm-gate variants) */
+    LT_ERR_SCRATCH = 8    /* the call needs more scratch than lt_prefill_noalloc holds */
 } lt_status;
 
 typedef enum { LT_F32 = 0, LT_BF16 = 1 } lt_dtype;
@@ -136,13 +137,41 @@ LT_API lt_status lt_prefill(const void *q, const void *k, const void *v, lt_dtyp
  * sequences across workgroups (used when batch * heads is too small to occupy
  * the GPU with one workgroup per sequence and head; holds one fp32 d x d state
  * per sequence, head and sequence piece). Returns 0 when no workspace helps or
- * the arguments are invalid. lt_prefill given a NULL or smaller workspace still
- * computes the same result, with four workgroups per (sequence, head), one per
- * 32 value columns (the norm-gate variants, which need whole output rows, with
- * one workgroup per (sequence, head)).
+ * the arguments are invalid. Given a smaller workspace, lt_prefill splits the
+ * sequences into longer pre-pass pieces whose states fit it (the coarsest split
+ * needs at most 63.75 MiB); given NULL or less than that, it still computes the
+ * same result, with four workgroups per (sequence, head), one per 32 value
+ * columns (the norm-gate variants, which need whole output rows, with one
+ * workgroup per (sequence, head)).
  */
 LT_API size_t lt_prefill_workspace_bytes(int batch, long long seqlen, int heads, int head_dim,
                                          lt_dtype in_dtype);
+
+/*
+ * lt_prefill_noalloc - lt_prefill for callers that cannot allocate device
+ * memory at call time: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. Same arguments, result and errors as
+ * lt_prefill, without the workspace pair: the split of long sequences across
+ * workgroups takes its states from a 64 MiB scratch array that the library
+ * holds in each GPU's memory from the first call on that GPU (the device of
+ * `stream`) until the process ends. No call allocates or frees memory.
+ *   - The planner takes the finest pre-pass pieces whose states fit the
+ *     scratch; every shape lt_prefill accepts fits (the coarsest plan of any
+ *     of them needs at most 63.75 MiB). A plan that did not fit would return
+ *     LT_ERR_SCRATCH and enqueue nothing.
+ *   - Every call on one GPU uses that GPU's one scratch array. Calls whose
+ *     work overlaps on one GPU (other streams, other threads, or graph
+ *     replays running at the same time) race on it and give wrong results;
+ *     calls ordered on one stream do not. Nothing in the scratch needs to be
+ *     zero on entry, and it keeps the last call's contents.
+ *   Errors: those of lt_prefill, LT_ERR_SCRATCH, and LT_ERR_HIP when the
+ *   scratch address cannot be looked up.
+ */
+LT_API lt_status lt_prefill_noalloc(const void *q, const void *k, const void *v, lt_dtype in_dtype,
+                                    const float *slopes, void *o, lt_dtype out_dtype,
+                                    const float *state_in, float *state_out,
+                                    int batch, long long seqlen, int heads, int head_dim, int block,
+                                    void *stream);
 
 /*
  * lt_prefill_varlen - prefill of `num_seqs` packed sequences of different

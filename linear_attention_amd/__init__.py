@@ -4,7 +4,9 @@ The operator (MiniMax Signal Lab · M1, §03 Lightning Attention) is causal
 linear attention with a per-head exponential decay, evaluated block by block
 with a fixed d x d fp32 state per head, plus its one-token decode step.
 
-``lt_prefill``, ``lt_prefill_workspace_bytes``, ``lt_prefill_varlen``,
+``lt_prefill``, ``lt_prefill_noalloc`` (the same with the library's static
+scratch, for callers that cannot allocate), ``lt_prefill_workspace_bytes``,
+``lt_prefill_varlen``,
 ``lt_decode``, ``lt_decode_slots`` (decode over a state pool),
 ``lt_prefill_backward`` (gradients of a prefill) and the ``*_norm_gate``
 variants (the operator followed by the
@@ -19,12 +21,12 @@ ImportError there, and there is no fallback path.
 """
 
 _NATIVE_NAMES = (
-    "lt_prefill", "lt_prefill_workspace_bytes", "lt_prefill_varlen", "lt_decode",
+    "lt_prefill", "lt_prefill_noalloc", "lt_prefill_workspace_bytes", "lt_prefill_varlen", "lt_decode",
     "lt_prefill_norm_gate", "lt_prefill_varlen_norm_gate", "lt_decode_norm_gate", "lt_decode_slots",
     "lt_prefill_backward", "lt_softmax_prefill", "lt_softmax_decode", "lt_softmax_decode_workspace_bytes",
     "LightningError", "lib", "status_string", "EXPORTS", "LIB_PATH", "HEAD_DIM", "LT_OK",
     "LT_ERR_NULL", "LT_ERR_SHAPE", "LT_ERR_BLOCK", "LT_ERR_DTYPE", "LT_ERR_ALIAS", "LT_ERR_HIP",
-    "LT_ERR_VALUE",
+    "LT_ERR_VALUE", "LT_ERR_SCRATCH",
     "LT_F32", "LT_BF16", "LT_MAX_BLOCK",
 )
 

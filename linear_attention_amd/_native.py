@@ -15,12 +15,14 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "liblightning.so")
 
-LT_OK, LT_ERR_NULL, LT_ERR_SHAPE, LT_ERR_BLOCK, LT_ERR_DTYPE, LT_ERR_ALIAS, LT_ERR_HIP, LT_ERR_VALUE = range(8)
+(LT_OK, LT_ERR_NULL, LT_ERR_SHAPE, LT_ERR_BLOCK, LT_ERR_DTYPE, LT_ERR_ALIAS, LT_ERR_HIP, LT_ERR_VALUE,
+ LT_ERR_SCRATCH) = range(9)
 LT_F32, LT_BF16 = 0, 1
 LT_MAX_BLOCK = 65536
 HEAD_DIM = 128
 
-EXPORTS = ("lt_status_string", "lt_version", "lt_build_id", "lt_prefill", "lt_prefill_workspace_bytes",
+EXPORTS = ("lt_status_string", "lt_version", "lt_build_id", "lt_prefill", "lt_prefill_noalloc",
+           "lt_prefill_workspace_bytes",
            "lt_prefill_varlen", "lt_decode", "lt_prefill_norm_gate", "lt_prefill_varlen_norm_gate",
            "lt_decode_norm_gate", "lt_decode_slots", "lt_prefill_backward", "lt_softmax_prefill",
            "lt_softmax_decode", "lt_softmax_decode_workspace_bytes")
@@ -57,6 +59,9 @@ def _load() -> ctypes.CDLL:
     lib.lt_prefill.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp,
                                _i, _ll, _i, _i, _i, _vp, ctypes.c_size_t, _vp]
     lib.lt_prefill.restype = _i
+    lib.lt_prefill_noalloc.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp,
+                                       _i, _ll, _i, _i, _i, _vp]
+    lib.lt_prefill_noalloc.restype = _i
     lib.lt_prefill_workspace_bytes.argtypes = [_i, _ll, _i, _i, _i]
     lib.lt_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.lt_prefill_varlen.argtypes = [_vp, _vp, _vp, _i, _vp, _i, _ll, _vp, _vp, _i,
@@ -173,6 +178,33 @@ def lt_prefill(q, k, v, slopes, block, state_in=None, *, o=None, state_out=None,
                         batch, L, H, d, int(block), _dev_ptr(workspace, "workspace"), ws_bytes,
                         _stream(stream, q.device))
     _check(st, "lt_prefill")
+    return o, state_out
+
+
+def lt_prefill_noalloc(q, k, v, slopes, block, state_in=None, *, o=None, state_out=None,
+                       want_state=True, out_dtype=None, stream=None):
+    """lt_prefill without a workspace argument: the library's static scratch
+    (64 MiB per GPU, held from the first call on a GPU until the process ends)
+    serves the split of long sequences. Calls whose work overlaps on one GPU
+    race on that scratch. Same arguments and result as lt_prefill otherwise.
+    """
+    torch = _torch()
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [batch, L, H, d] shape")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    batch, L, H, d = q.shape
+    out_dtype = out_dtype or torch.float32
+    if o is None:
+        o = torch.empty((batch, L, H, d), device=q.device, dtype=out_dtype)
+    if state_out is None and want_state:
+        state_out = torch.empty((batch, H, d, d), device=q.device, dtype=torch.float32)
+    st = lib.lt_prefill_noalloc(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
+                                _dtype_code(q.dtype), _dev_ptr(slopes, "slopes"), _dev_ptr(o, "o"),
+                                _dtype_code(o.dtype), _dev_ptr(state_in, "state_in"),
+                                _dev_ptr(state_out, "state_out"), batch, L, H, d, int(block),
+                                _stream(stream, q.device))
+    _check(st, "lt_prefill_noalloc")
     return o, state_out
 
 

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblightning.so")
 
 SOURCES = ["prefill_heads.hip", "prefill_slices.hip", "decode.hip", "backward.hip", "softmax.hip",
-           "lightning_api.cpp"]
+           "noalloc.hip", "lightning_api.cpp"]
 
 HIPCC_FLAGS = [
     "-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC",
@@ -101,7 +101,7 @@ def build(verbose: bool = False) -> str:
             _run([hipcc()] + HIPCC_FLAGS + EXTRA_FLAGS.get(src, []) + build_id +
                  ["-c", os.path.join(CSRC, src), "-o", objs[i]], verbose, src)
 
-        with ThreadPoolExecutor(max_workers=min(len(SOURCES), 6)) as ex:
+        with ThreadPoolExecutor(max_workers=min(len(SOURCES), 7)) as ex:
             list(ex.map(compile_one, range(len(SOURCES))))
         _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose,
              "liblightning.so")

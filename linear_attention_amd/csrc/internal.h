@@ -81,6 +81,9 @@ struct PrefillPlan {
     long long piece_len = 0;
     size_t workspace = 0;  // bytes: per (unit, head), prefill_states(...) fp32 d x d states
     int value_slices = 1;  // 1 = whole head per workgroup, 4 = value-slice workgroups
+    // A segmented plan was wanted but even its coarsest pre-pass pieces need
+    // more workspace than allowed (this plan is then the one without segments).
+    bool workspace_short = false;
 };
 
 // fp32 d x d states per (unit, head) in the workspace of a segmented plan:
@@ -94,8 +97,17 @@ constexpr long long prefill_states(int segments, int pieces) { return pieces + 2
 inline void clear_pending_error() { (void)hipGetLastError(); }
 
 // prepass_wgs: pre-pass workgroups to aim for (sets the piece length).
+// max_workspace: bytes the plan may use; when the preferred pieces need more,
+// the pieces are made longer (fewer states) until they fit. Without any fit the
+// plan has no segments (value slices; whole heads for the caller to choose) and
+// workspace_short set.
 PrefillPlan plan_prefill(long long units, long long seqlen, int heads, lt_dtype in_dtype,
-                         bool varlen, long long prepass_wgs);
+                         bool varlen, long long prepass_wgs, size_t max_workspace);
+
+// The no-allocation entry point's scratch: the device address of this device's
+// copy of a fixed static array, looked up once per device (hipGetSymbolAddress
+// with the stream's device current) and kept until the process ends.
+hipError_t noalloc_scratch(hipStream_t stream, void **ptr, size_t *bytes);
 
 // Backward of a fixed-length bf16 prefill (gradients of
 // l = sum dout . o + <d_state_out, S_final>): dk, dv and d_state_in from one

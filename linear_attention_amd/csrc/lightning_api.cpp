@@ -2,6 +2,7 @@
 // stream. Every check runs before any HIP call, so the error paths need no GPU.
 #include <cstdint>
 #include <cstdio>
+#include <cstddef>
 #include <numeric>
 
 #include "internal.h"
@@ -60,23 +61,24 @@ constexpr long long kPrepassWide = 2048;
 // Shortest pre-pass piece.
 constexpr long long kMinPiece = 512;
 
+// need_ws: fail with LT_ERR_SCRATCH instead of running without segments when a
+// segmented plan does not fit the workspace (the no-allocation entry point).
 lt_status launch(const lt::PrefillArgs &a, int in_dtype, int out_dtype, bool varlen,
-                 void *workspace, size_t workspace_bytes, void *stream) {
+                 void *workspace, size_t workspace_bytes, void *stream, bool need_ws = false) {
     const hipStream_t st = static_cast<hipStream_t>(stream);
     if (in_dtype != LT_BF16)
         return map_hip(lt::launch_prefill_slices(a, (lt_dtype)in_dtype, (lt_dtype)out_dtype, st));
     const bool whole_rows = a.ng.gate || a.state_in_t;  // epilogue or transposed S_0
     lt::PrefillPlan p = lt::plan_prefill(a.units, varlen ? a.total_tokens : a.seqlen, a.heads,
-                                         (lt_dtype)in_dtype, varlen,
-                                         kPrepassWide);
-    // Without the workspace the segmented plan needs, split value columns instead;
-    // the norm-gate epilogue needs whole output rows, so it keeps one workgroup
-    // per (sequence, head) rather than value slices.
-    const bool no_ws = p.workspace > 0 && (!workspace || workspace_bytes < p.workspace);
-    if (no_ws || (whole_rows && p.value_slices != 1)) {
+                                         (lt_dtype)in_dtype, varlen, kPrepassWide,
+                                         workspace ? workspace_bytes : 0);
+    if (p.workspace_short && need_ws) return LT_ERR_SCRATCH;
+    // Without a workspace for any segmented plan, value columns are split
+    // instead; the norm-gate epilogue needs whole output rows, so it keeps one
+    // workgroup per (sequence, head) rather than value slices.
+    if (whole_rows && p.value_slices != 1) {
         p = lt::PrefillPlan{};
         p.seg_len = varlen ? a.total_tokens : a.seqlen;
-        if (!whole_rows) p.value_slices = lt::kValueSlices;
     }
     return map_hip(lt::launch_prefill_heads(a, p, workspace, (lt_dtype)out_dtype, st));
 }
@@ -149,7 +151,7 @@ lt_status check_norm_gate(const void *gate, long long gate_bytes, const float *n
 namespace lt {
 
 PrefillPlan plan_prefill(long long units, long long seqlen, int heads, lt_dtype in_dtype,
-                         bool varlen, long long prepass_wgs) {
+                         bool varlen, long long prepass_wgs, size_t max_workspace) {
     // bf16 plans, by the number of (sequence, head) pairs uh:
     //   uh >= 256: one whole-head workgroup per pair;
     //   long fixed-length sequences: whole heads cut into segments, with the
@@ -179,13 +181,30 @@ PrefillPlan plan_prefill(long long units, long long seqlen, int heads, lt_dtype 
     piece = (piece + 127) / 128 * 128;
     if (piece < kMinPiece) piece = kMinPiece;
     if (piece > seg) piece = seg;
+    constexpr size_t kStateBytes = (size_t)kHeadDim * kHeadDim * sizeof(float);
+    auto bytes = [&](long long pieces) {
+        return (size_t)uh * (size_t)prefill_states((int)g, (int)pieces) * kStateBytes;
+    };
+    long long pieces = (covered + piece - 1) / piece;
+    if (bytes(pieces) > max_workspace) {
+        // longer pieces: as many states as fit (at least one piece per segment
+        // boundary, i.e. pieces of a whole segment)
+        const long long fit = (long long)(max_workspace / kStateBytes / (size_t)uh) - (2 * g - 1);
+        if (fit < g - 1) {
+            p.workspace_short = true;
+            return p;
+        }
+        piece = (covered + fit - 1) / fit;
+        piece = (piece + 127) / 128 * 128;
+        if (piece > seg) piece = seg;
+        pieces = (covered + piece - 1) / piece;
+    }
     p.value_slices = 1;
     p.segments = (int)g;
     p.seg_len = seg;
     p.piece_len = piece;
-    p.pieces = (int)((covered + piece - 1) / piece);
-    p.workspace = (size_t)uh * (size_t)prefill_states(p.segments, p.pieces) * kHeadDim * kHeadDim *
-                  sizeof(float);
+    p.pieces = (int)pieces;
+    p.workspace = bytes(pieces);
     return p;
 }
 
@@ -198,7 +217,7 @@ LT_API size_t lt_prefill_workspace_bytes(int batch, long long seqlen, int heads,
     if (batch <= 0 || seqlen <= 0 || heads <= 0 || heads > LT_MAX_HEADS ||
         head_dim != lt::kHeadDim || !dtype_ok(in_dtype))
         return 0;
-    return lt::plan_prefill(batch, seqlen, heads, in_dtype, false, kPrepassWide).workspace;
+    return lt::plan_prefill(batch, seqlen, heads, in_dtype, false, kPrepassWide, SIZE_MAX).workspace;
 }
 
 LT_API const char *lt_status_string(int status) {
@@ -211,6 +230,8 @@ LT_API const char *lt_status_string(int status) {
         case LT_ERR_ALIAS: return "LT_ERR_ALIAS: an output overlaps another buffer";
         case LT_ERR_HIP: return "LT_ERR_HIP: HIP runtime error at launch";
         case LT_ERR_VALUE: return "LT_ERR_VALUE: a scalar argument is out of range";
+        case LT_ERR_SCRATCH:
+            return "LT_ERR_SCRATCH: the call needs more scratch than the no-allocation entry point holds";
         default: return "unknown lt_status";
     }
 }
@@ -234,7 +255,7 @@ lt_status prefill_impl(const void *q, const void *k, const void *v, lt_dtype in_
                        const float *slopes, void *o, lt_dtype out_dtype, const float *state_in,
                        float *state_out, int batch, long long seqlen, int heads, int head_dim,
                        int block, void *workspace, size_t workspace_bytes, void *stream,
-                       const lt::NormGate *ng) {
+                       const lt::NormGate *ng, bool use_scratch = false) {
     if (batch < 0 || seqlen < 0) return LT_ERR_SHAPE;
     long long tokens;
     if (__builtin_mul_overflow((long long)batch, seqlen, &tokens)) return LT_ERR_SHAPE;
@@ -265,7 +286,12 @@ lt_status prefill_impl(const void *q, const void *k, const void *v, lt_dtype in_
     lt::PrefillArgs a{q, k, v, slopes, o, state_in, state_out, nullptr, seqlen, tokens,
                       batch, heads};
     if (ng) a.ng = *ng;
-    return launch(a, in_dtype, out_dtype, false, workspace, workspace_bytes, stream);
+    if (use_scratch) {  // the library's static scratch in place of a workspace
+        const hipError_t e =
+            lt::noalloc_scratch(static_cast<hipStream_t>(stream), &workspace, &workspace_bytes);
+        if (e != hipSuccess) return map_hip(e);
+    }
+    return launch(a, in_dtype, out_dtype, false, workspace, workspace_bytes, stream, use_scratch);
 }
 
 lt_status varlen_impl(const void *q, const void *k, const void *v, lt_dtype in_dtype,
@@ -360,6 +386,15 @@ LT_API lt_status lt_prefill(const void *q, const void *k, const void *v, lt_dtyp
                         heads, head_dim, block, workspace, workspace_bytes, stream, nullptr);
 }
 
+LT_API lt_status lt_prefill_noalloc(const void *q, const void *k, const void *v,
+                                    lt_dtype in_dtype, const float *slopes, void *o,
+                                    lt_dtype out_dtype, const float *state_in, float *state_out,
+                                    int batch, long long seqlen, int heads, int head_dim, int block,
+                                    void *stream) {
+    return prefill_impl(q, k, v, in_dtype, slopes, o, out_dtype, state_in, state_out, batch, seqlen,
+                        heads, head_dim, block, nullptr, 0, stream, nullptr, true);
+}
+
 LT_API lt_status lt_prefill_norm_gate(const void *q, const void *k, const void *v,
                                       lt_dtype in_dtype, const float *slopes, const void *gate,
                                       const float *norm_weight, float eps, void *y,
@@ -450,8 +485,9 @@ LT_API lt_status lt_prefill_backward(const void *q, const void *k, const void *v
                              batch, heads};
     // the reverse pass splits long sequences like the forward when the
     // workspace allows (the dq pass above has finished with it by then)
-    lt::PrefillPlan p = lt::plan_prefill(batch, seqlen, heads, LT_BF16, false, kPrepassWide);
-    if (p.value_slices != 1 || (p.workspace > 0 && (!workspace || workspace_bytes < p.workspace))) {
+    lt::PrefillPlan p = lt::plan_prefill(batch, seqlen, heads, LT_BF16, false, kPrepassWide,
+                                         workspace ? workspace_bytes : 0);
+    if (p.value_slices != 1) {
         p = lt::PrefillPlan{};
         p.seg_len = seqlen;
     }

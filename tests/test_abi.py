@@ -47,7 +47,7 @@ def test_only_the_abi_is_exported():
 
 def test_status_strings():
     names = ["LT_OK", "LT_ERR_NULL", "LT_ERR_SHAPE", "LT_ERR_BLOCK", "LT_ERR_DTYPE",
-             "LT_ERR_ALIAS", "LT_ERR_HIP", "LT_ERR_VALUE"]
+             "LT_ERR_ALIAS", "LT_ERR_HIP", "LT_ERR_VALUE", "LT_ERR_SCRATCH"]
     for code, name in enumerate(names):
         assert la.status_string(code).startswith(name)
         assert getattr(la, name) == code
@@ -71,6 +71,33 @@ def prefill(**kw):
                 workspace_bytes=0, stream=None)
     args.update(kw)
     return la.lib.lt_prefill(*args.values())
+
+
+def prefill_noalloc(**kw):
+    args = dict(q=A, k=A + 100 * MB, v=A + 200 * MB, in_dtype=la.LT_BF16, slopes=A + 300 * MB,
+                o=A + 400 * MB, out_dtype=la.LT_F32, state_in=None, state_out=A + 900 * MB,
+                batch=1, seqlen=64, heads=2, head_dim=128, block=64, stream=None)
+    args.update(kw)
+    return la.lib.lt_prefill_noalloc(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), la.LT_ERR_NULL),
+    (dict(slopes=None), la.LT_ERR_NULL),
+    (dict(head_dim=64), la.LT_ERR_SHAPE),
+    (dict(batch=-1), la.LT_ERR_SHAPE),
+    (dict(seqlen=1 << 50, heads=64), la.LT_ERR_SHAPE),
+    (dict(block=0), la.LT_ERR_BLOCK),
+    (dict(in_dtype=7), la.LT_ERR_DTYPE),
+    (dict(o=A + 16384), la.LT_ERR_ALIAS),
+    (dict(state_out=A + 400 * MB), la.LT_ERR_ALIAS),
+    (dict(batch=0), la.LT_OK),                     # documented no-ops, before any HIP call
+    (dict(seqlen=0, state_out=None), la.LT_OK),
+])
+def test_prefill_noalloc_checks_arguments_before_any_hip_call(kw, code):
+    """The no-allocation entry point runs lt_prefill's host checks before it
+    looks up its scratch (its first HIP call)."""
+    assert prefill_noalloc(**kw) == code
 
 
 def varlen(**kw):

@@ -1,0 +1,129 @@
+"""lt_prefill_noalloc (the no-allocation entry point) against lt_prefill, through
+the C ABI, on two calls in a row: an M1-layer-sized call whose every head takes
+the pre-pass (so its states fill the static scratch), then a smaller call whose
+heads take both routes, which must not see the first call's scratch contents.
+
+Bar: the benchmark spec's tolerance per (sequence, head) with every row held to
+parity_util's row bound; where lt_prefill is given a workspace of the scratch's
+size the two run the same plan and must agree bit for bit.
+"""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from parity_util import TOL_BF16, ensure_built, max_rel_states, parity_err, to_device, to_host_f32
+
+pytestmark = pytest.mark.gpu
+
+SCRATCH_BYTES = 64 << 20
+
+
+@pytest.fixture(scope="module")
+def la():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm device")
+    ensure_built()
+    import linear_attention_amd
+
+    return linear_attention_amd
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def c_noalloc(la, q, k, v, slopes, o, s_in, s_out):
+    import torch
+
+    b, L, H, d = q.shape
+    st = la.lib.lt_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), la.LT_BF16, _ptr(slopes), _ptr(o),
+                                   la.LT_F32, _ptr(s_in), _ptr(s_out), b, L, H, d, 256,
+                                   ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == la.LT_OK, la.status_string(st)
+
+
+def c_prefill(la, q, k, v, slopes, o, s_in, s_out, ws):
+    import torch
+
+    b, L, H, d = q.shape
+    nbytes = 0 if ws is None else ws.numel()
+    st = la.lib.lt_prefill(_ptr(q), _ptr(k), _ptr(v), la.LT_BF16, _ptr(slopes), _ptr(o), la.LT_F32,
+                           _ptr(s_in), _ptr(s_out), b, L, H, d, 256, _ptr(ws), nbytes,
+                           ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == la.LT_OK, la.status_string(st)
+
+
+def test_noalloc_two_calls_match_lt_prefill(la):
+    import torch
+
+    # call 1: M1 layer shape, slopes x 1e-5 (every head takes the pre-pass, so
+    # the scratch holds the coarser pieces' states), carried-in state
+    w = workloads.M1_LAYER
+    shape = (1, w.seqlen, w.heads, 128)
+    print(f"[case] noalloc call 1 {shape} slopes x1e-5", flush=True)
+    q, k, v = workloads.qkv_device(w.seed, shape, "bf16")
+    sl_h = (workloads.slopes(w.heads) * np.float32(1e-5)).astype(np.float32)
+    sl = torch.from_numpy(sl_h).cuda()
+    s0 = workloads.state_device(w.seed + 5, (1, w.heads, 128, 128), std=0.1)
+    o_na = torch.empty(shape, device="cuda", dtype=torch.float32)
+    s_na = torch.empty((1, w.heads, 128, 128), device="cuda", dtype=torch.float32)
+    c_noalloc(la, q, k, v, sl, o_na, s0, s_na)
+    # lt_prefill with a workspace of the scratch's size (the same plan) and with
+    # the full workspace it asks for (finer pre-pass pieces)
+    ws_same = torch.empty(SCRATCH_BYTES, device="cuda", dtype=torch.uint8)
+    o_same, s_same = torch.empty_like(o_na), torch.empty_like(s_na)
+    c_prefill(la, q, k, v, sl, o_same, s0, s_same, ws_same)
+    full = la.lt_prefill_workspace_bytes(*shape[:3])
+    assert full > SCRATCH_BYTES
+    ws_full = torch.empty(full, device="cuda", dtype=torch.uint8)
+    o_full, s_full = torch.empty_like(o_na), torch.empty_like(s_na)
+    c_prefill(la, q, k, v, sl, o_full, s0, s_full, ws_full)
+    torch.cuda.synchronize()
+    assert torch.equal(o_na, o_same) and torch.equal(s_na, s_same)
+    og, of = to_host_f32(o_na)[0], to_host_f32(o_full)[0]
+    eo = max(parity_err(og[:, h], of[:, h]) for h in range(w.heads))
+    es = max_rel_states(to_host_f32(s_na), to_host_f32(s_full))
+    # and the oracle on sampled heads
+    hs = [0, 31, 63]
+    hq, hk, hv = (to_host_f32(x[0][:, hs].contiguous())[None] for x in (q, k, v))
+    o_ref, s_ref = oracle.recurrence_batch(hq, hk, hv, sl_h[hs], s0=to_host_f32(s0)[:, hs])
+    er = max(parity_err(og[:, h], o_ref[0, :, j]) for j, h in enumerate(hs))
+    er = max(er, max_rel_states(to_host_f32(s_na)[:, hs], s_ref))
+    print(f"[result] call 1: vs lt_prefill (full workspace) o {eo:.3e} state {es:.3e}; "
+          f"vs oracle {er:.3e}", flush=True)
+    assert eo <= TOL_BF16 and es <= TOL_BF16 and er <= TOL_BF16
+    del q, k, v, o_na, o_same, o_full, ws_full
+
+    # call 2: smaller, heads on both routes (pre-pass and local starts), the
+    # carried-in state updated in place
+    L, H = 9000, 7
+    sl2_h = np.array([0.0, 1e-6, 0.005, 0.02, 0.2, 1.0, 30.0], np.float32)
+    print(f"[case] noalloc call 2 (1, {L}, {H}) slopes {list(sl2_h)}", flush=True)
+    qh, kh, vh = workloads.qkv_host(2401, (1, L, H, 128), "bf16")
+    s0h = workloads.state_host(2402, (1, H, 128, 128))
+    q2, k2, v2 = (to_device(x, "bf16") for x in (qh, kh, vh))
+    sl2 = torch.from_numpy(sl2_h).cuda()
+    st_na = torch.from_numpy(s0h).cuda()
+    o2 = torch.empty((1, L, H, 128), device="cuda", dtype=torch.float32)
+    c_noalloc(la, q2, k2, v2, sl2, o2, st_na, st_na)
+    st_ref = torch.from_numpy(s0h).cuda()
+    o2r = torch.empty_like(o2)
+    ws2 = torch.empty(la.lt_prefill_workspace_bytes(1, L, H), device="cuda", dtype=torch.uint8)
+    c_prefill(la, q2, k2, v2, sl2, o2r, st_ref, st_ref, ws2)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.recurrence_batch(qh, kh, vh, sl2_h, s0=s0h)
+    g2, r2 = to_host_f32(o2)[0], to_host_f32(o2r)[0]
+    e_api = max(parity_err(g2[:, h], r2[:, h]) for h in range(H))
+    e_orc = max(parity_err(g2[:, h], o_ref[0, :, h]) for h in range(H))
+    e_st = max(max_rel_states(to_host_f32(st_na), to_host_f32(st_ref)),
+               max_rel_states(to_host_f32(st_na), s_ref))
+    print(f"[result] call 2: vs lt_prefill {e_api:.3e}, vs oracle {e_orc:.3e}, state {e_st:.3e}",
+          flush=True)
+    assert torch.equal(o2, o2r) and torch.equal(st_na, st_ref)
+    assert e_api <= TOL_BF16 and e_orc <= TOL_BF16 and e_st <= TOL_BF16
