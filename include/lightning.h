@@ -175,7 +175,10 @@ LT_API lt_status lt_prefill_noalloc(const void *q, const void *k, const void *v,
 
 /*
  * lt_prefill_varlen - prefill of `num_seqs` packed sequences of different
- * lengths, each with its own carried-in state (chunked prefill / resume).
+ * lengths, each with its own carried-in state: chunked prefill, or resuming a
+ * sequence whose state was kept (the §03 block form carries the state from one
+ * block to the next, so a later call that starts from it continues the same
+ * sequence; §04: that state is all a sequence keeps, whatever its length).
  *
  *   q, k, v     [total_tokens, heads, head_dim], in_dtype; sequence n owns rows
  *               cu_seqlens[n] .. cu_seqlens[n+1]-1.
@@ -184,16 +187,36 @@ LT_API lt_status lt_prefill_noalloc(const void *q, const void *k, const void *v,
  *               host; the kernels clamp every boundary into [0, total_tokens],
  *               so malformed boundaries give wrong results, never stray memory
  *               accesses.
+ *   max_seqlen  length of the longest sequence, 0 <= max_seqlen <= total_tokens
+ *               (0: not known, taken as total_tokens). With few (sequence,
+ *               head) pairs, sequences are split across workgroups like
+ *               lt_prefill's, on segments cut from max_seqlen; a value below
+ *               the longest real length gives wrong results for the longer
+ *               sequences (never memory accesses outside the tensors).
  *   slopes, o, state_in, state_out, block: as lt_prefill, with state tensors
  *               [num_seqs, heads, head_dim, head_dim]. Blocks restart at each
  *               sequence start; zero-length sequences pass their state through.
- *   Errors: as lt_prefill.
+ *   workspace   as lt_prefill's, sized by lt_prefill_varlen_workspace_bytes
+ *               (NULL or smaller: the same result from an unsplit plan or
+ *               coarser pieces).
+ *   Errors: as lt_prefill (LT_ERR_SHAPE also for max_seqlen outside
+ *   [0, total_tokens] or total_tokens >= 2^31).
  */
 LT_API lt_status lt_prefill_varlen(const void *q, const void *k, const void *v, lt_dtype in_dtype,
                                    const int *cu_seqlens, int num_seqs, long long total_tokens,
-                                   const float *slopes, void *o, lt_dtype out_dtype,
-                                   const float *state_in, float *state_out,
-                                   int heads, int head_dim, int block, void *stream);
+                                   long long max_seqlen, const float *slopes, void *o,
+                                   lt_dtype out_dtype, const float *state_in, float *state_out,
+                                   int heads, int head_dim, int block, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
+/*
+ * lt_prefill_varlen_workspace_bytes - the workspace lt_prefill_varlen (and its
+ * norm-gate variant) uses to split the sequences of a packed batch whose
+ * longest sequence has max_seqlen tokens (0 when no workspace helps or the
+ * arguments are invalid).
+ */
+LT_API size_t lt_prefill_varlen_workspace_bytes(int num_seqs, long long max_seqlen, int heads,
+                                                int head_dim, lt_dtype in_dtype);
 
 /*
  * lt_decode - one decode step for `batch` sequences: each reads and writes its
@@ -303,10 +326,11 @@ LT_API lt_status lt_prefill_norm_gate(const void *q, const void *k, const void *
 LT_API lt_status lt_prefill_varlen_norm_gate(const void *q, const void *k, const void *v,
                                              lt_dtype in_dtype, const int *cu_seqlens,
                                              int num_seqs, long long total_tokens,
-                                             const float *slopes, const void *gate,
-                                             const float *norm_weight, float eps, void *y,
-                                             lt_dtype out_dtype, const float *state_in,
+                                             long long max_seqlen, const float *slopes,
+                                             const void *gate, const float *norm_weight, float eps,
+                                             void *y, lt_dtype out_dtype, const float *state_in,
                                              float *state_out, int heads, int head_dim, int block,
+                                             void *workspace, size_t workspace_bytes,
                                              void *stream);
 
 LT_API lt_status lt_decode_norm_gate(const void *q, const void *k, const void *v,

@@ -21,7 +21,8 @@ ImportError there, and there is no fallback path.
 """
 
 _NATIVE_NAMES = (
-    "lt_prefill", "lt_prefill_noalloc", "lt_prefill_workspace_bytes", "lt_prefill_varlen", "lt_decode",
+    "lt_prefill", "lt_prefill_noalloc", "lt_prefill_workspace_bytes", "lt_prefill_varlen",
+    "lt_prefill_varlen_workspace_bytes", "lt_decode",
     "lt_prefill_norm_gate", "lt_prefill_varlen_norm_gate", "lt_decode_norm_gate", "lt_decode_slots",
     "lt_prefill_backward", "lt_softmax_prefill", "lt_softmax_decode", "lt_softmax_decode_workspace_bytes",
     "LightningError", "lib", "status_string", "EXPORTS", "LIB_PATH", "HEAD_DIM", "LT_OK",

@@ -22,8 +22,8 @@ LT_MAX_BLOCK = 65536
 HEAD_DIM = 128
 
 EXPORTS = ("lt_status_string", "lt_version", "lt_build_id", "lt_prefill", "lt_prefill_noalloc",
-           "lt_prefill_workspace_bytes",
-           "lt_prefill_varlen", "lt_decode", "lt_prefill_norm_gate", "lt_prefill_varlen_norm_gate",
+           "lt_prefill_workspace_bytes", "lt_prefill_varlen", "lt_prefill_varlen_workspace_bytes",
+           "lt_decode", "lt_prefill_norm_gate", "lt_prefill_varlen_norm_gate",
            "lt_decode_norm_gate", "lt_decode_slots", "lt_prefill_backward", "lt_softmax_prefill",
            "lt_softmax_decode", "lt_softmax_decode_workspace_bytes")
 
@@ -64,16 +64,19 @@ def _load() -> ctypes.CDLL:
     lib.lt_prefill_noalloc.restype = _i
     lib.lt_prefill_workspace_bytes.argtypes = [_i, _ll, _i, _i, _i]
     lib.lt_prefill_workspace_bytes.restype = ctypes.c_size_t
-    lib.lt_prefill_varlen.argtypes = [_vp, _vp, _vp, _i, _vp, _i, _ll, _vp, _vp, _i,
-                                      _vp, _vp, _i, _i, _i, _vp]
+    lib.lt_prefill_varlen.argtypes = [_vp, _vp, _vp, _i, _vp, _i, _ll, _ll, _vp, _vp, _i,
+                                      _vp, _vp, _i, _i, _i, _vp, ctypes.c_size_t, _vp]
     lib.lt_prefill_varlen.restype = _i
+    lib.lt_prefill_varlen_workspace_bytes.argtypes = [_i, _ll, _i, _i, _i]
+    lib.lt_prefill_varlen_workspace_bytes.restype = ctypes.c_size_t
     lib.lt_decode.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _vp]
     lib.lt_decode.restype = _i
     lib.lt_prefill_norm_gate.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _f, _vp, _i, _vp, _vp,
                                          _i, _ll, _i, _i, _i, _vp, ctypes.c_size_t, _vp]
     lib.lt_prefill_norm_gate.restype = _i
-    lib.lt_prefill_varlen_norm_gate.argtypes = [_vp, _vp, _vp, _i, _vp, _i, _ll, _vp, _vp, _vp, _f,
-                                                _vp, _i, _vp, _vp, _i, _i, _i, _vp]
+    lib.lt_prefill_varlen_norm_gate.argtypes = [_vp, _vp, _vp, _i, _vp, _i, _ll, _ll, _vp, _vp, _vp, _f,
+                                                _vp, _i, _vp, _vp, _i, _i, _i, _vp, ctypes.c_size_t,
+                                                _vp]
     lib.lt_prefill_varlen_norm_gate.restype = _i
     lib.lt_decode_norm_gate.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _f, _vp, _i, _i, _i,
                                         _i, _vp]
@@ -124,14 +127,43 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t}; Lightning kernels take float32 or bfloat16")
 
 
-def _dev_ptr(t, name):
-    if t is None:
-        return None
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
-    return t.data_ptr()
+class _Args:
+    """The tensor arguments of one call. ``ptrs()`` checks every shape, dtype and
+    layout, then every device, before any raw pointer reaches the library:
+    a wrong-sized or wrongly typed buffer would otherwise be read or written
+    out of bounds on the device (the C ABI sees only pointers and sizes)."""
+
+    def __init__(self, device):
+        self.device = device
+        self.items = []
+
+    def add(self, t, name, shape=None, dtypes=None):
+        self.items.append((t, name, None if shape is None else tuple(int(x) for x in shape), dtypes))
+        return self
+
+    def ptrs(self):
+        for t, name, shape, dtypes in self.items:
+            if t is None:
+                continue
+            if shape is not None and tuple(t.shape) != shape:
+                raise ValueError(f"{name} must have shape {shape}, got {tuple(t.shape)}")
+            if dtypes is not None and t.dtype not in dtypes:
+                names = " or ".join(str(d) for d in dtypes)
+                raise TypeError(f"{name} must be {names}, got {t.dtype}")
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+        for t, name, _, _ in self.items:
+            if t is None:
+                continue
+            if not t.is_cuda:
+                raise ValueError(f"{name} must be a device tensor")
+            if t.device != self.device:
+                raise ValueError(f"{name} is on {t.device}, the call's inputs on {self.device}")
+        return [None if t is None else t.data_ptr() for t, _, _, _ in self.items]
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def _stream(stream, device):
@@ -141,9 +173,55 @@ def _stream(stream, device):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _io_dtypes():
+    torch = _torch()
+    return (torch.float32, torch.bfloat16)
+
+
+def _out(t, shape, out_dtype, like, name):
+    """The caller's output tensor (whose dtype must agree with out_dtype when both
+    are given), or a new one of out_dtype (default float32)."""
+    torch = _torch()
+    if t is not None:
+        if out_dtype is not None and t.dtype != out_dtype:
+            raise TypeError(f"{name} is {t.dtype} but out_dtype is {out_dtype}")
+        return t
+    return torch.empty(shape, device=like.device, dtype=out_dtype or torch.float32)
+
+
+def _qkv(q, k, v, ndim, what):
+    if q.dim() != ndim or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError(f"q, k, v must share one {what} shape")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if q.dtype not in _io_dtypes():
+        raise TypeError(f"q, k, v must be float32 or bfloat16, got {q.dtype}")
+
+
 def lt_prefill_workspace_bytes(batch, seqlen, heads, head_dim=HEAD_DIM, in_dtype=LT_BF16) -> int:
     return int(lib.lt_prefill_workspace_bytes(int(batch), int(seqlen), int(heads), int(head_dim),
                                               int(in_dtype)))
+
+
+def lt_prefill_varlen_workspace_bytes(num_seqs, max_seqlen, heads, head_dim=HEAD_DIM, in_dtype=LT_BF16) -> int:
+    return int(lib.lt_prefill_varlen_workspace_bytes(int(num_seqs), int(max_seqlen), int(heads),
+                                                     int(head_dim), int(in_dtype)))
+
+
+def _prefill_args(q, k, v, slopes, o, state_in, state_out, extra=()):
+    """Checked pointers of a fixed-length prefill's tensors (q, k, v, slopes, o,
+    state_in, state_out, then `extra` (tensor, name, shape, dtypes) entries)."""
+    torch = _torch()
+    batch, L, H, d = q.shape
+    a = _Args(q.device)
+    a.add(q, "q", dtypes=_io_dtypes()).add(k, "k").add(v, "v")
+    a.add(slopes, "slopes", (H,), (torch.float32,))
+    a.add(o, "o", (batch, L, H, d), _io_dtypes())
+    a.add(state_in, "state_in", (batch, H, d, d), (torch.float32,))
+    a.add(state_out, "state_out", (batch, H, d, d), (torch.float32,))
+    for e in extra:
+        a.add(*e)
+    return a.ptrs()
 
 
 def lt_prefill(q, k, v, slopes, block, state_in=None, *, o=None, state_out=None,
@@ -153,29 +231,22 @@ def lt_prefill(q, k, v, slopes, block, state_in=None, *, o=None, state_out=None,
     Returns (o [batch, L, H, 128], state_out [batch, H, 128, 128] fp32 or None).
     ``state_out`` may be given (it may be ``state_in`` itself for an in-place
     update); otherwise one is allocated when ``want_state``. ``workspace`` is a
-    uint8 device tensor of at least ``lt_prefill_workspace_bytes`` bytes; one
-    is allocated when it is None and the plan wants one.
+    device tensor of at least ``lt_prefill_workspace_bytes`` bytes; one is
+    allocated when it is None and the plan wants one.
     """
     torch = _torch()
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must share one [batch, L, H, d] shape")
-    if k.dtype != q.dtype or v.dtype != q.dtype:
-        raise TypeError("q, k, v must share one dtype")
+    _qkv(q, k, v, 4, "[batch, L, H, d]")
     batch, L, H, d = q.shape
-    out_dtype = out_dtype or torch.float32
-    if o is None:
-        o = torch.empty((batch, L, H, d), device=q.device, dtype=out_dtype)
+    o = _out(o, (batch, L, H, d), out_dtype, q, "o")
     if state_out is None and want_state:
         state_out = torch.empty((batch, H, d, d), device=q.device, dtype=torch.float32)
     if workspace is None:
         nbytes = lt_prefill_workspace_bytes(batch, L, H, d, _dtype_code(q.dtype))
         if nbytes:
             workspace = torch.empty(nbytes, device=q.device, dtype=torch.uint8)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.lt_prefill(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dtype_code(q.dtype),
-                        _dev_ptr(slopes, "slopes"), _dev_ptr(o, "o"), _dtype_code(o.dtype),
-                        _dev_ptr(state_in, "state_in"), _dev_ptr(state_out, "state_out"),
-                        batch, L, H, d, int(block), _dev_ptr(workspace, "workspace"), ws_bytes,
+    p = _prefill_args(q, k, v, slopes, o, state_in, state_out, [(workspace, "workspace")])
+    st = lib.lt_prefill(p[0], p[1], p[2], _dtype_code(q.dtype), p[3], p[4], _dtype_code(o.dtype),
+                        p[5], p[6], batch, L, H, d, int(block), p[7], _nbytes(workspace),
                         _stream(stream, q.device))
     _check(st, "lt_prefill")
     return o, state_out
@@ -189,50 +260,83 @@ def lt_prefill_noalloc(q, k, v, slopes, block, state_in=None, *, o=None, state_o
     race on that scratch. Same arguments and result as lt_prefill otherwise.
     """
     torch = _torch()
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must share one [batch, L, H, d] shape")
-    if k.dtype != q.dtype or v.dtype != q.dtype:
-        raise TypeError("q, k, v must share one dtype")
+    _qkv(q, k, v, 4, "[batch, L, H, d]")
     batch, L, H, d = q.shape
-    out_dtype = out_dtype or torch.float32
-    if o is None:
-        o = torch.empty((batch, L, H, d), device=q.device, dtype=out_dtype)
+    o = _out(o, (batch, L, H, d), out_dtype, q, "o")
     if state_out is None and want_state:
         state_out = torch.empty((batch, H, d, d), device=q.device, dtype=torch.float32)
-    st = lib.lt_prefill_noalloc(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
-                                _dtype_code(q.dtype), _dev_ptr(slopes, "slopes"), _dev_ptr(o, "o"),
-                                _dtype_code(o.dtype), _dev_ptr(state_in, "state_in"),
-                                _dev_ptr(state_out, "state_out"), batch, L, H, d, int(block),
-                                _stream(stream, q.device))
+    p = _prefill_args(q, k, v, slopes, o, state_in, state_out)
+    st = lib.lt_prefill_noalloc(p[0], p[1], p[2], _dtype_code(q.dtype), p[3], p[4], _dtype_code(o.dtype),
+                                p[5], p[6], batch, L, H, d, int(block), _stream(stream, q.device))
     _check(st, "lt_prefill_noalloc")
     return o, state_out
 
 
-def lt_prefill_varlen(q, k, v, cu_seqlens, slopes, block, state_in=None, *, o=None,
-                      state_out=None, want_state=True, out_dtype=None, stream=None):
-    """Packed variable-length prefill. q, k, v: [T, H, 128]; cu_seqlens: int32 [n+1] on device.
-
-    Returns (o [T, H, 128], state_out [n, H, 128, 128] fp32 or None).
-    """
+def _varlen_args(q, k, v, cu_seqlens, slopes, o, state_in, state_out, extra=()):
     torch = _torch()
-    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must share one [T, H, d] shape")
-    if cu_seqlens.dtype != torch.int32:
-        raise TypeError("cu_seqlens must be int32")
     T, H, d = q.shape
     n = cu_seqlens.numel() - 1
-    out_dtype = out_dtype or torch.float32
-    if o is None:
-        o = torch.empty((T, H, d), device=q.device, dtype=out_dtype)
+    a = _Args(q.device)
+    a.add(q, "q", dtypes=_io_dtypes()).add(k, "k").add(v, "v")
+    a.add(cu_seqlens, "cu_seqlens", (n + 1,), (torch.int32,))
+    a.add(slopes, "slopes", (H,), (torch.float32,))
+    a.add(o, "o", (T, H, d), _io_dtypes())
+    a.add(state_in, "state_in", (n, H, d, d), (torch.float32,))
+    a.add(state_out, "state_out", (n, H, d, d), (torch.float32,))
+    for e in extra:
+        a.add(*e)
+    return a.ptrs()
+
+
+def _varlen_common(q, k, v, cu_seqlens, max_seqlen, want_state, state_out, workspace):
+    torch = _torch()
+    _qkv(q, k, v, 3, "[T, H, d]")
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D tensor of num_seqs + 1 entries")
+    T, H, d = q.shape
+    n = cu_seqlens.numel() - 1
+    if max_seqlen is None:
+        max_seqlen = T  # an upper bound (the split is then cut on it)
     if state_out is None and want_state:
         state_out = torch.empty((n, H, d, d), device=q.device, dtype=torch.float32)
-    st = lib.lt_prefill_varlen(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
-                               _dtype_code(q.dtype), _dev_ptr(cu_seqlens, "cu_seqlens"), n, T,
-                               _dev_ptr(slopes, "slopes"), _dev_ptr(o, "o"), _dtype_code(o.dtype),
-                               _dev_ptr(state_in, "state_in"), _dev_ptr(state_out, "state_out"),
-                               H, d, int(block), _stream(stream, q.device))
+    if workspace is None:
+        nbytes = lt_prefill_varlen_workspace_bytes(n, max_seqlen, H, d, _dtype_code(q.dtype))
+        if nbytes:
+            workspace = torch.empty(nbytes, device=q.device, dtype=torch.uint8)
+    return T, H, d, n, int(max_seqlen), state_out, workspace
+
+
+def lt_prefill_varlen(q, k, v, cu_seqlens, slopes, block, state_in=None, *, max_seqlen=None, o=None,
+                      state_out=None, want_state=True, out_dtype=None, workspace=None, stream=None):
+    """Packed variable-length prefill. q, k, v: [T, H, 128]; cu_seqlens: int32 [n+1] on device.
+
+    max_seqlen: the longest sequence's length (None: T, an upper bound). A
+    workspace of lt_prefill_varlen_workspace_bytes bytes is allocated when none
+    is given and the plan wants one.
+    Returns (o [T, H, 128], state_out [n, H, 128, 128] fp32 or None).
+    """
+    T, H, d, n, mx, state_out, workspace = _varlen_common(q, k, v, cu_seqlens, max_seqlen, want_state,
+                                                          state_out, workspace)
+    o = _out(o, (T, H, d), out_dtype, q, "o")
+    p = _varlen_args(q, k, v, cu_seqlens, slopes, o, state_in, state_out, [(workspace, "workspace")])
+    st = lib.lt_prefill_varlen(p[0], p[1], p[2], _dtype_code(q.dtype), p[3], n, T, mx, p[4], p[5],
+                               _dtype_code(o.dtype), p[6], p[7], H, d, int(block), p[8],
+                               _nbytes(workspace), _stream(stream, q.device))
     _check(st, "lt_prefill_varlen")
     return o, state_out
+
+
+def _decode_args(q, k, v, slopes, state, o, state_shape, state_name="state", extra=()):
+    torch = _torch()
+    batch, H, d = q.shape
+    a = _Args(q.device)
+    a.add(q, "q", dtypes=_io_dtypes()).add(k, "k").add(v, "v")
+    a.add(slopes, "slopes", (H,), (torch.float32,))
+    a.add(state, state_name, state_shape, (torch.float32,))
+    a.add(o, "o", (batch, H, d), _io_dtypes())
+    for e in extra:
+        a.add(*e)
+    return a.ptrs()
 
 
 def lt_decode(q, k, v, slopes, state, *, o=None, out_dtype=None, stream=None):
@@ -240,28 +344,20 @@ def lt_decode(q, k, v, slopes, state, *, o=None, out_dtype=None, stream=None):
 
     Returns o [batch, H, 128].
     """
-    torch = _torch()
-    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must share one [batch, H, d] shape")
+    _qkv(q, k, v, 3, "[batch, H, d]")
     batch, H, d = q.shape
-    if state.dtype != torch.float32 or tuple(state.shape) != (batch, H, d, d):
-        raise ValueError("state must be float32 [batch, H, d, d]")
-    out_dtype = out_dtype or torch.float32
-    if o is None:
-        o = torch.empty((batch, H, d), device=q.device, dtype=out_dtype)
-    st = lib.lt_decode(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dtype_code(q.dtype),
-                       _dev_ptr(slopes, "slopes"), _dev_ptr(state, "state"), _dev_ptr(o, "o"),
-                       _dtype_code(o.dtype), batch, H, d, _stream(stream, q.device))
+    o = _out(o, (batch, H, d), out_dtype, q, "o")
+    p = _decode_args(q, k, v, slopes, state, o, (batch, H, d, d))
+    st = lib.lt_decode(p[0], p[1], p[2], _dtype_code(q.dtype), p[3], p[4], p[5], _dtype_code(o.dtype),
+                       batch, H, d, _stream(stream, q.device))
     _check(st, "lt_decode")
     return o
 
 
-def _check_gate(gate, like, norm_weight, heads):
+def _gate_entries(gate, norm_weight, like, H):
     torch = _torch()
-    if tuple(gate.shape) != tuple(like.shape) or gate.dtype != like.dtype:
-        raise ValueError("gate must have the shape and dtype of q")
-    if norm_weight.dtype != torch.float32 or tuple(norm_weight.shape) != (heads, HEAD_DIM):
-        raise ValueError("norm_weight must be float32 [heads, 128]")
+    return [(gate, "gate", tuple(like.shape), (like.dtype,)),
+            (norm_weight, "norm_weight", (H, HEAD_DIM), (torch.float32,))]
 
 
 def lt_prefill_norm_gate(q, k, v, slopes, gate, norm_weight, eps, block, state_in=None, *, y=None,
@@ -273,60 +369,41 @@ def lt_prefill_norm_gate(q, k, v, slopes, gate, norm_weight, eps, block, state_i
     Returns (y [batch, L, H, 128], state_out or None); other arguments as lt_prefill.
     """
     torch = _torch()
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must share one [batch, L, H, d] shape")
-    if k.dtype != q.dtype or v.dtype != q.dtype:
-        raise TypeError("q, k, v must share one dtype")
+    _qkv(q, k, v, 4, "[batch, L, H, d]")
     batch, L, H, d = q.shape
-    _check_gate(gate, q, norm_weight, H)
-    out_dtype = out_dtype or torch.float32
-    if y is None:
-        y = torch.empty((batch, L, H, d), device=q.device, dtype=out_dtype)
+    y = _out(y, (batch, L, H, d), out_dtype, q, "y")
     if state_out is None and want_state:
         state_out = torch.empty((batch, H, d, d), device=q.device, dtype=torch.float32)
     if workspace is None:
         nbytes = lt_prefill_workspace_bytes(batch, L, H, d, _dtype_code(q.dtype))
         if nbytes:
             workspace = torch.empty(nbytes, device=q.device, dtype=torch.uint8)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.lt_prefill_norm_gate(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
-                                  _dtype_code(q.dtype), _dev_ptr(slopes, "slopes"),
-                                  _dev_ptr(gate, "gate"), _dev_ptr(norm_weight, "norm_weight"),
-                                  float(eps), _dev_ptr(y, "y"), _dtype_code(y.dtype),
-                                  _dev_ptr(state_in, "state_in"), _dev_ptr(state_out, "state_out"),
-                                  batch, L, H, d, int(block), _dev_ptr(workspace, "workspace"),
-                                  ws_bytes, _stream(stream, q.device))
+    p = _prefill_args(q, k, v, slopes, y, state_in, state_out,
+                      _gate_entries(gate, norm_weight, q, H) + [(workspace, "workspace")])
+    st = lib.lt_prefill_norm_gate(p[0], p[1], p[2], _dtype_code(q.dtype), p[3], p[7], p[8], float(eps), p[4],
+                                  _dtype_code(y.dtype), p[5], p[6], batch, L, H, d, int(block), p[9],
+                                  _nbytes(workspace), _stream(stream, q.device))
     _check(st, "lt_prefill_norm_gate")
     return y, state_out
 
 
 def lt_prefill_varlen_norm_gate(q, k, v, cu_seqlens, slopes, gate, norm_weight, eps, block,
-                                state_in=None, *, y=None, state_out=None, want_state=True,
-                                out_dtype=None, stream=None):
+                                state_in=None, *, max_seqlen=None, y=None, state_out=None,
+                                want_state=True, out_dtype=None, workspace=None, stream=None):
     """Packed variable-length prefill followed by the norm-gate epilogue.
     q, k, v, gate: bf16 [T, H, 128]; other arguments as lt_prefill_varlen.
 
     Returns (y [T, H, 128], state_out [n, H, 128, 128] or None).
     """
-    torch = _torch()
-    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must share one [T, H, d] shape")
-    if cu_seqlens.dtype != torch.int32:
-        raise TypeError("cu_seqlens must be int32")
-    T, H, d = q.shape
-    _check_gate(gate, q, norm_weight, H)
-    n = cu_seqlens.numel() - 1
-    out_dtype = out_dtype or torch.float32
-    if y is None:
-        y = torch.empty((T, H, d), device=q.device, dtype=out_dtype)
-    if state_out is None and want_state:
-        state_out = torch.empty((n, H, d, d), device=q.device, dtype=torch.float32)
+    T, H, d, n, mx, state_out, workspace = _varlen_common(q, k, v, cu_seqlens, max_seqlen, want_state,
+                                                          state_out, workspace)
+    y = _out(y, (T, H, d), out_dtype, q, "y")
+    p = _varlen_args(q, k, v, cu_seqlens, slopes, y, state_in, state_out,
+                     _gate_entries(gate, norm_weight, q, H) + [(workspace, "workspace")])
     st = lib.lt_prefill_varlen_norm_gate(
-        _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dtype_code(q.dtype),
-        _dev_ptr(cu_seqlens, "cu_seqlens"), n, T, _dev_ptr(slopes, "slopes"),
-        _dev_ptr(gate, "gate"), _dev_ptr(norm_weight, "norm_weight"), float(eps),
-        _dev_ptr(y, "y"), _dtype_code(y.dtype), _dev_ptr(state_in, "state_in"),
-        _dev_ptr(state_out, "state_out"), H, d, int(block), _stream(stream, q.device))
+        p[0], p[1], p[2], _dtype_code(q.dtype), p[3], n, T, mx, p[4], p[8], p[9], float(eps), p[5],
+        _dtype_code(y.dtype), p[6], p[7], H, d, int(block), p[10], _nbytes(workspace),
+        _stream(stream, q.device))
     _check(st, "lt_prefill_varlen_norm_gate")
     return y, state_out
 
@@ -336,21 +413,14 @@ def lt_decode_norm_gate(q, k, v, slopes, state, gate, norm_weight, eps, *, y=Non
     """One decode step followed by the norm-gate epilogue. q, k, v, gate: [batch, H, 128];
     state: [batch, H, 128, 128] fp32, updated in place. Returns y [batch, H, 128].
     """
-    torch = _torch()
-    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must share one [batch, H, d] shape")
+    _qkv(q, k, v, 3, "[batch, H, d]")
     batch, H, d = q.shape
-    _check_gate(gate, q, norm_weight, H)
-    if state.dtype != torch.float32 or tuple(state.shape) != (batch, H, d, d):
-        raise ValueError("state must be float32 [batch, H, d, d]")
-    out_dtype = out_dtype or torch.float32
-    if y is None:
-        y = torch.empty((batch, H, d), device=q.device, dtype=out_dtype)
-    st = lib.lt_decode_norm_gate(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
-                                 _dtype_code(q.dtype), _dev_ptr(slopes, "slopes"),
-                                 _dev_ptr(state, "state"), _dev_ptr(gate, "gate"),
-                                 _dev_ptr(norm_weight, "norm_weight"), float(eps), _dev_ptr(y, "y"),
-                                 _dtype_code(y.dtype), batch, H, d, _stream(stream, q.device))
+    y = _out(y, (batch, H, d), out_dtype, q, "y")
+    p = _decode_args(q, k, v, slopes, state, y, (batch, H, d, d),
+                     extra=_gate_entries(gate, norm_weight, q, H))
+    st = lib.lt_decode_norm_gate(p[0], p[1], p[2], _dtype_code(q.dtype), p[3], p[4], p[6], p[7],
+                                 float(eps), p[5], _dtype_code(y.dtype), batch, H, d,
+                                 _stream(stream, q.device))
     _check(st, "lt_decode_norm_gate")
     return y
 
@@ -361,19 +431,15 @@ def lt_decode_slots(q, k, v, slopes, state_pool, slot_ids, *, o=None, out_dtype=
     device (out-of-range ids are padding rows with zero output). Returns o [batch, H, 128].
     """
     torch = _torch()
-    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must share one [batch, H, d] shape")
+    _qkv(q, k, v, 3, "[batch, H, d]")
     batch, H, d = q.shape
-    if state_pool.dtype != torch.float32 or state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H, d, d):
-        raise ValueError("state_pool must be float32 [num_slots, H, d, d]")
-    if slot_ids.dtype != torch.int32 or tuple(slot_ids.shape) != (batch,):
-        raise ValueError("slot_ids must be int32 [batch]")
-    out_dtype = out_dtype or torch.float32
-    if o is None:
-        o = torch.empty((batch, H, d), device=q.device, dtype=out_dtype)
-    st = lib.lt_decode_slots(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dtype_code(q.dtype),
-                             _dev_ptr(slopes, "slopes"), _dev_ptr(state_pool, "state_pool"),
-                             int(state_pool.shape[0]), _dev_ptr(slot_ids, "slot_ids"), _dev_ptr(o, "o"),
+    if state_pool.dim() != 4:
+        raise ValueError("state_pool must be [num_slots, H, d, d]")
+    slots = int(state_pool.shape[0])
+    o = _out(o, (batch, H, d), out_dtype, q, "o")
+    p = _decode_args(q, k, v, slopes, state_pool, o, (slots, H, d, d), "state_pool",
+                     [(slot_ids, "slot_ids", (batch,), (torch.int32,))])
+    st = lib.lt_decode_slots(p[0], p[1], p[2], _dtype_code(q.dtype), p[3], p[4], slots, p[6], p[5],
                              _dtype_code(o.dtype), batch, H, d, _stream(stream, q.device))
     _check(st, "lt_decode_slots")
     return o
@@ -384,8 +450,9 @@ def lt_prefill_backward(q, k, v, dout, slopes, block, state_in=None, d_state_out
                         workspace=None, stream=None):
     """Gradients of sum(dout * o) + <d_state_out, S_final> for a fixed-length prefill.
     q, k, v, dout: bf16 [batch, L, H, 128]; state_in, d_state_out: fp32 [batch, H, 128, 128]
-    or None. Returns (dq, dk, dv [batch, L, H, 128] in grad_dtype (default fp32),
-    d_state_in [batch, H, 128, 128] fp32 or None).
+    or None. Returns (dq, dk, dv [batch, L, H, 128] in grad_dtype (default fp32, or the
+    dtype of the given gradient tensors, which must agree), d_state_in [batch, H, 128, 128]
+    fp32 or None).
     """
     torch = _torch()
     if q.dim() != 4 or any(x.shape != q.shape for x in (k, v, dout)):
@@ -393,7 +460,11 @@ def lt_prefill_backward(q, k, v, dout, slopes, block, state_in=None, d_state_out
     if any(x.dtype != q.dtype for x in (k, v, dout)):
         raise TypeError("q, k, v, dout must share one dtype")
     batch, L, H, d = q.shape
-    grad_dtype = grad_dtype or torch.float32
+    given = [g.dtype for g in (dq, dk, dv) if g is not None]
+    if grad_dtype is None:
+        grad_dtype = given[0] if given else torch.float32
+    if any(g != grad_dtype for g in given):
+        raise TypeError(f"dq, dk and dv must all be {grad_dtype}")
     mk = lambda: torch.empty((batch, L, H, d), device=q.device, dtype=grad_dtype)
     dq = mk() if dq is None else dq
     dk = mk() if dk is None else dk
@@ -404,14 +475,19 @@ def lt_prefill_backward(q, k, v, dout, slopes, block, state_in=None, d_state_out
         nbytes = lt_prefill_workspace_bytes(batch, L, H, d, _dtype_code(q.dtype))
         if nbytes:
             workspace = torch.empty(nbytes, device=q.device, dtype=torch.uint8)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.lt_prefill_backward(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"),
-                                 _dev_ptr(dout, "dout"), _dtype_code(q.dtype),
-                                 _dev_ptr(slopes, "slopes"), _dev_ptr(state_in, "state_in"),
-                                 _dev_ptr(d_state_out, "d_state_out"), _dev_ptr(dq, "dq"),
-                                 _dev_ptr(dk, "dk"), _dev_ptr(dv, "dv"), _dtype_code(dq.dtype),
-                                 _dev_ptr(d_state_in, "d_state_in"), batch, L, H, d, int(block),
-                                 _dev_ptr(workspace, "workspace"), ws_bytes, _stream(stream, q.device))
+    sh, st_sh = (batch, L, H, d), (batch, H, d, d)
+    a = _Args(q.device)
+    a.add(q, "q", dtypes=(torch.bfloat16,)).add(k, "k").add(v, "v").add(dout, "dout")
+    a.add(slopes, "slopes", (H,), (torch.float32,))
+    a.add(state_in, "state_in", st_sh, (torch.float32,))
+    a.add(d_state_out, "d_state_out", st_sh, (torch.float32,))
+    a.add(dq, "dq", sh, (grad_dtype,)).add(dk, "dk", sh, (grad_dtype,)).add(dv, "dv", sh, (grad_dtype,))
+    a.add(d_state_in, "d_state_in", st_sh, (torch.float32,))
+    a.add(workspace, "workspace")
+    p = a.ptrs()
+    st = lib.lt_prefill_backward(p[0], p[1], p[2], p[3], _dtype_code(q.dtype), p[4], p[5], p[6], p[7],
+                                 p[8], p[9], _dtype_code(grad_dtype), p[10], batch, L, H, d, int(block),
+                                 p[11], _nbytes(workspace), _stream(stream, q.device))
     _check(st, "lt_prefill_backward")
     return dq, dk, dv, d_state_in
 
@@ -425,18 +501,16 @@ def lt_softmax_prefill(q, k, v, *, rope_dims=64, rope_base=10000.0, scale=None, 
     torch = _torch()
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]:
         raise ValueError("q must be [batch, L, Hq, d] and k, v [batch, L, Hkv, d]")
-    if any(x.dtype != torch.bfloat16 for x in (q, k, v)):
-        raise TypeError("q, k, v must be bfloat16")
     batch, L, Hq, d = q.shape
     Hkv = k.shape[2]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    out_dtype = out_dtype or torch.float32
-    if o is None:
-        o = torch.empty((batch, L, Hq, d), device=q.device, dtype=out_dtype)
+    o = _out(o, (batch, L, Hq, d), out_dtype, q, "o")
     if k_rope is None:
         k_rope = torch.empty_like(k)
-    st = lib.lt_softmax_prefill(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dev_ptr(o, "o"),
-                                _dtype_code(o.dtype), _dev_ptr(k_rope, "k_rope"), batch, L, Hq, Hkv, d,
+    bf = (torch.bfloat16,)
+    p = (_Args(q.device).add(q, "q", dtypes=bf).add(k, "k", dtypes=bf).add(v, "v", dtypes=bf)
+         .add(o, "o", (batch, L, Hq, d), _io_dtypes()).add(k_rope, "k_rope", tuple(k.shape), bf).ptrs())
+    st = lib.lt_softmax_prefill(p[0], p[1], p[2], p[3], _dtype_code(o.dtype), p[4], batch, L, Hq, Hkv, d,
                                 int(rope_dims), float(rope_base), scale, int(pos0), _stream(stream, q.device))
     _check(st, "lt_softmax_prefill")
     return o, k_rope
@@ -462,23 +536,19 @@ def lt_softmax_decode(q, k_new, v_new, k_cache, v_cache, lengths, *, rope_dims=6
     if k_cache.dim() != 4 or v_cache.shape != k_cache.shape or k_cache.shape[0] != batch or \
             tuple(k_cache.shape[2:]) != (Hkv, d):
         raise ValueError("caches must be [batch, capacity, Hkv, d]")
-    if any(x.dtype != torch.bfloat16 for x in (q, k_new, v_new, k_cache, v_cache)):
-        raise TypeError("q, k_new, v_new and the caches must be bfloat16")
-    if lengths.dtype != torch.int32 or tuple(lengths.shape) != (batch,):
-        raise ValueError("lengths must be int32 [batch]")
     cap = k_cache.shape[1]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    out_dtype = out_dtype or torch.float32
-    if o is None:
-        o = torch.empty((batch, Hq, d), device=q.device, dtype=out_dtype)
+    o = _out(o, (batch, Hq, d), out_dtype, q, "o")
     if workspace is None:
         nb = lt_softmax_decode_workspace_bytes(batch, cap, Hq, Hkv, d)
         workspace = torch.empty(max(nb, 1), device=q.device, dtype=torch.uint8) if nb else None
-    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib.lt_softmax_decode(_dev_ptr(q, "q"), _dev_ptr(k_new, "k_new"), _dev_ptr(v_new, "v_new"),
-                               _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
-                               _dev_ptr(lengths, "lengths"), _dev_ptr(o, "o"), _dtype_code(o.dtype), batch,
-                               cap, Hq, Hkv, d, int(rope_dims), float(rope_base), scale,
-                               _dev_ptr(workspace, "workspace"), wbytes, _stream(stream, q.device))
+    bf = (torch.bfloat16,)
+    p = (_Args(q.device).add(q, "q", dtypes=bf).add(k_new, "k_new", dtypes=bf).add(v_new, "v_new", dtypes=bf)
+         .add(k_cache, "k_cache", dtypes=bf).add(v_cache, "v_cache", dtypes=bf)
+         .add(lengths, "lengths", (batch,), (torch.int32,)).add(o, "o", (batch, Hq, d), _io_dtypes())
+         .add(workspace, "workspace").ptrs())
+    st = lib.lt_softmax_decode(p[0], p[1], p[2], p[3], p[4], p[5], p[6], _dtype_code(o.dtype), batch,
+                               cap, Hq, Hkv, d, int(rope_dims), float(rope_base), scale, p[7],
+                               _nbytes(workspace), _stream(stream, q.device))
     _check(st, "lt_softmax_decode")
     return o

@@ -208,7 +208,8 @@ __global__ __launch_bounds__(NT, 4) void rev_piece_kernel(BackwardArgs a, Segmen
     // mirrored range [t0, t1) = real tokens [L - t1, L - t0)
     const long long L = a.seqlen;
     const long long t0 = j * sp.piece_len;
-    const long long t1 = t0 + kgr * sp.piece_len < sp.covered() ? t0 + kgr * sp.piece_len : sp.covered();
+    const long long covered = sp.covered(L);
+    const long long t1 = t0 + kgr * sp.piece_len < covered ? t0 + kgr * sp.piece_len : covered;
     const int ts = a.heads * D;
     const long long seq = (long long)n * L * a.heads;
     const uint16_t *qg = static_cast<const uint16_t *>(a.q) + (seq + h) * (long long)D;
@@ -745,7 +746,8 @@ hipError_t launch(const BackwardArgs &a, const PrefillPlan &p, void *workspace, 
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(uh * kCombineSlices)), dim3(kCombineThreads),
-                           0, stream, a.slopes, a.heads, a.d_state_out, false, sp, ws);
+                           0, stream, a.slopes, a.heads, a.d_state_out, false, sp,
+                           SeqLens{nullptr, (long long)a.units * a.seqlen, a.seqlen}, ws);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

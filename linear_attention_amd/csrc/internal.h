@@ -10,7 +10,8 @@ namespace lt {
 
 // One prefill launch: `units` independent sequences x `heads` heads.
 // Fixed-length batches leave cu_seqlens NULL and use seqlen; packed batches
-// pass cu_seqlens (device int32, units + 1 entries) and total_tokens.
+// pass cu_seqlens (device int32, units + 1 entries), total_tokens, and in
+// seqlen the length of their longest sequence (the plan's upper bound).
 // Optional epilogue after O = O_intra + O_inter: with gate != nullptr the
 // kernels write y = o / sqrt(mean_d(o^2) + eps) * norm_weight[h] * sigmoid(g)
 // per (token, head) instead of o; gate has o's shape in the input dtype,

@@ -69,17 +69,17 @@ lt_status launch(const lt::PrefillArgs &a, int in_dtype, int out_dtype, bool var
     if (in_dtype != LT_BF16)
         return map_hip(lt::launch_prefill_slices(a, (lt_dtype)in_dtype, (lt_dtype)out_dtype, st));
     const bool whole_rows = a.ng.gate || a.state_in_t;  // epilogue or transposed S_0
-    lt::PrefillPlan p = lt::plan_prefill(a.units, varlen ? a.total_tokens : a.seqlen, a.heads,
-                                         (lt_dtype)in_dtype, varlen, kPrepassWide,
-                                         workspace ? workspace_bytes : 0);
+    // packed batches plan on their longest sequence (a.seqlen = max_seqlen)
+    lt::PrefillPlan p = lt::plan_prefill(a.units, a.seqlen, a.heads, (lt_dtype)in_dtype, varlen,
+                                         kPrepassWide, workspace ? workspace_bytes : 0);
     if (p.workspace_short && need_ws) return LT_ERR_SCRATCH;
     // Without a workspace for any segmented plan, value columns are split
     // instead; the norm-gate epilogue needs whole output rows, so it keeps one
     // workgroup per (sequence, head) rather than value slices.
-    if (whole_rows && p.value_slices != 1) {
-        p = lt::PrefillPlan{};
-        p.seg_len = varlen ? a.total_tokens : a.seqlen;
-    }
+    if (whole_rows && p.value_slices != 1) p = lt::PrefillPlan{};
+    // one segment covers any sequence of the call (for packed batches whatever
+    // the lengths on the device are)
+    if (p.segments == 1) p.seg_len = varlen ? a.total_tokens : a.seqlen;
     return map_hip(lt::launch_prefill_heads(a, p, workspace, (lt_dtype)out_dtype, st));
 }
 
@@ -154,18 +154,19 @@ PrefillPlan plan_prefill(long long units, long long seqlen, int heads, lt_dtype 
                          bool varlen, long long prepass_wgs, size_t max_workspace) {
     // bf16 plans, by the number of (sequence, head) pairs uh:
     //   uh >= 256: one whole-head workgroup per pair;
-    //   long fixed-length sequences: whole heads cut into segments, with the
-    //     pre-pass and combine pass (its extra k, v reads cost less than
-    //     re-reading q, k per value slice, which measured 4.05 TB/s memory-only
-    //     against 5.2 TB/s);
-    //   otherwise (varlen, short sequences): four value-slice workgroups per pair.
+    //   long sequences: whole heads cut into segments, with the pre-pass and
+    //     combine pass (its extra k, v reads cost less than re-reading q, k per
+    //     value slice, which measured 4.05 TB/s memory-only against 5.2 TB/s);
+    //     packed batches cut on their longest sequence (seqlen = max_seqlen),
+    //     each sequence using the segments its own length needs;
+    //   otherwise (short sequences): four value-slice workgroups per pair.
+    (void)varlen;
     PrefillPlan p;
     p.seg_len = seqlen;
     if (in_dtype != LT_BF16 || units <= 0 || heads <= 0) return p;
     const long long uh = units * heads;
     if (uh >= kTargetWorkgroups) return p;
     p.value_slices = kValueSlices;
-    if (varlen) return p;
     long long g = (kTargetWorkgroups + uh - 1) / uh;
     if (g > seqlen / kMinSegment) g = seqlen / kMinSegment;
     if (g < 2) return p;
@@ -220,6 +221,14 @@ LT_API size_t lt_prefill_workspace_bytes(int batch, long long seqlen, int heads,
     return lt::plan_prefill(batch, seqlen, heads, in_dtype, false, kPrepassWide, SIZE_MAX).workspace;
 }
 
+LT_API size_t lt_prefill_varlen_workspace_bytes(int num_seqs, long long max_seqlen, int heads,
+                                                int head_dim, lt_dtype in_dtype) {
+    if (num_seqs <= 0 || max_seqlen <= 0 || heads <= 0 || heads > LT_MAX_HEADS ||
+        head_dim != lt::kHeadDim || !dtype_ok(in_dtype))
+        return 0;
+    return lt::plan_prefill(num_seqs, max_seqlen, heads, in_dtype, true, kPrepassWide, SIZE_MAX).workspace;
+}
+
 LT_API const char *lt_status_string(int status) {
     switch (status) {
         case LT_OK: return "LT_OK";
@@ -236,7 +245,7 @@ LT_API const char *lt_status_string(int status) {
     }
 }
 
-LT_API int lt_version(void) { return 10100; }
+LT_API int lt_version(void) { return 20000; }
 
 // The build passes the hash of the sources it compiled; a build by other means
 // reports "unknown". The tag keeps a fixed prefix so the identity can also be
@@ -296,11 +305,14 @@ lt_status prefill_impl(const void *q, const void *k, const void *v, lt_dtype in_
 
 lt_status varlen_impl(const void *q, const void *k, const void *v, lt_dtype in_dtype,
                       const int *cu_seqlens, int num_seqs, long long total_tokens,
-                      const float *slopes, void *o, lt_dtype out_dtype, const float *state_in,
-                      float *state_out, int heads, int head_dim, int block, void *stream,
+                      long long max_seqlen, const float *slopes, void *o, lt_dtype out_dtype,
+                      const float *state_in, float *state_out, int heads, int head_dim, int block,
+                      void *workspace, size_t workspace_bytes, void *stream,
                       const lt::NormGate *ng) {
     if (num_seqs < 0 || total_tokens < 0) return LT_ERR_SHAPE;
     if (total_tokens > 0x7fffffffLL) return LT_ERR_SHAPE;  // int32 sequence boundaries
+    if (max_seqlen < 0 || max_seqlen > total_tokens) return LT_ERR_SHAPE;
+    if (max_seqlen == 0) max_seqlen = total_tokens;  // unknown: no sequence is longer
     lt_status st = check_prefill(q, k, v, in_dtype, slopes, o, out_dtype, state_in, state_out,
                                  num_seqs, total_tokens, heads, head_dim, block);
     if (st != LT_OK) return st;
@@ -314,17 +326,29 @@ lt_status varlen_impl(const void *q, const void *k, const void *v, lt_dtype in_d
     }
     if (num_seqs == 0 || heads == 0) return LT_OK;
     if (!cu_seqlens) return LT_ERR_NULL;
-    if (overlaps(range_of(cu_seqlens, (long long)(num_seqs + 1) * 4),
-                 range_of(o, total_tokens * heads * head_dim * dtype_size(out_dtype))) ||
-        (state_out && overlaps(range_of(cu_seqlens, (long long)(num_seqs + 1) * 4),
-                               range_of(state_out, (long long)num_seqs * heads * head_dim *
-                                                       head_dim * 4))))
+    const long long in_b = total_tokens * heads * head_dim * dtype_size(in_dtype);
+    const long long out_b = total_tokens * heads * head_dim * dtype_size(out_dtype);
+    const long long st_b = (long long)num_seqs * heads * head_dim * head_dim * 4;
+    const Range rcu = range_of(cu_seqlens, (long long)(num_seqs + 1) * 4);
+    if (overlaps(rcu, range_of(o, out_b)) || (state_out && overlaps(rcu, range_of(state_out, st_b))))
         return LT_ERR_ALIAS;
+    if (workspace && workspace_bytes > 0) {
+        const Range rw = range_of(workspace, (long long)workspace_bytes);
+        if (overlaps(rw, range_of(q, in_b)) || overlaps(rw, range_of(k, in_b)) ||
+            overlaps(rw, range_of(v, in_b)) || overlaps(rw, range_of(slopes, heads * 4LL)) ||
+            overlaps(rw, range_of(o, out_b)) || overlaps(rw, rcu) ||
+            (state_in && overlaps(rw, range_of(state_in, st_b))) ||
+            (state_out && overlaps(rw, range_of(state_out, st_b))) ||
+            (ng && (overlaps(rw, range_of(ng->gate, in_b)) ||
+                    overlaps(rw, range_of(ng->norm_weight, (long long)heads * head_dim * 4)))))
+            return LT_ERR_ALIAS;
+    }
     if (total_tokens == 0 && !state_out) return LT_OK;
-    lt::PrefillArgs a{q, k, v, slopes, o, state_in, state_out, cu_seqlens, 0, total_tokens,
+    // seqlen carries the longest sequence's length (the plan's upper bound)
+    lt::PrefillArgs a{q, k, v, slopes, o, state_in, state_out, cu_seqlens, max_seqlen, total_tokens,
                       num_seqs, heads};
     if (ng) a.ng = *ng;
-    return launch(a, in_dtype, out_dtype, true, nullptr, 0, stream);
+    return launch(a, in_dtype, out_dtype, true, workspace, workspace_bytes, stream);
 }
 
 // Decode. With slot_ids, `state` is a pool of num_slots entries of
@@ -409,24 +433,28 @@ LT_API lt_status lt_prefill_norm_gate(const void *q, const void *k, const void *
 
 LT_API lt_status lt_prefill_varlen(const void *q, const void *k, const void *v, lt_dtype in_dtype,
                                    const int *cu_seqlens, int num_seqs, long long total_tokens,
-                                   const float *slopes, void *o, lt_dtype out_dtype,
-                                   const float *state_in, float *state_out,
-                                   int heads, int head_dim, int block, void *stream) {
-    return varlen_impl(q, k, v, in_dtype, cu_seqlens, num_seqs, total_tokens, slopes, o, out_dtype,
-                       state_in, state_out, heads, head_dim, block, stream, nullptr);
+                                   long long max_seqlen, const float *slopes, void *o,
+                                   lt_dtype out_dtype, const float *state_in, float *state_out,
+                                   int heads, int head_dim, int block, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+    return varlen_impl(q, k, v, in_dtype, cu_seqlens, num_seqs, total_tokens, max_seqlen, slopes, o,
+                       out_dtype, state_in, state_out, heads, head_dim, block, workspace,
+                       workspace_bytes, stream, nullptr);
 }
 
 LT_API lt_status lt_prefill_varlen_norm_gate(const void *q, const void *k, const void *v,
                                              lt_dtype in_dtype, const int *cu_seqlens,
                                              int num_seqs, long long total_tokens,
-                                             const float *slopes, const void *gate,
-                                             const float *norm_weight, float eps, void *y,
-                                             lt_dtype out_dtype, const float *state_in,
+                                             long long max_seqlen, const float *slopes,
+                                             const void *gate, const float *norm_weight, float eps,
+                                             void *y, lt_dtype out_dtype, const float *state_in,
                                              float *state_out, int heads, int head_dim, int block,
+                                             void *workspace, size_t workspace_bytes,
                                              void *stream) {
     const lt::NormGate ng{gate, norm_weight, eps};
-    return varlen_impl(q, k, v, in_dtype, cu_seqlens, num_seqs, total_tokens, slopes, y, out_dtype,
-                       state_in, state_out, heads, head_dim, block, stream, &ng);
+    return varlen_impl(q, k, v, in_dtype, cu_seqlens, num_seqs, total_tokens, max_seqlen, slopes, y,
+                       out_dtype, state_in, state_out, heads, head_dim, block, workspace,
+                       workspace_bytes, stream, &ng);
 }
 
 LT_API lt_status lt_decode(const void *q, const void *k, const void *v, lt_dtype in_dtype,

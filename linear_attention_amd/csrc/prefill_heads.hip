@@ -122,9 +122,11 @@ __global__ __launch_bounds__(NT, 4) void piece_state_kernel(PrefillArgs a, Segme
     const float s2 = a.slopes[h] * LOG2E;
     if (fix_head(s2, sp.seg_len, sp.fix_osz)) return;  // local-start segments: no pre-pass
     const int jl = j + kgr - 1 < sp.pieces - 1 ? j + kgr - 1 : sp.pieces - 1;
-    const long long t0 = j * sp.piece_len;
-    const long long t1 = t0 + kgr * sp.piece_len < sp.covered() ? t0 + kgr * sp.piece_len : sp.covered();
     const SeqRange sr = sequence_of(a, n);
+    const long long covered = sp.covered(sr.len);
+    const long long t0 = j * sp.piece_len;
+    if (t0 >= covered) return;  // past this sequence's pre-pass tokens
+    const long long t1 = t0 + kgr * sp.piece_len < covered ? t0 + kgr * sp.piece_len : covered;
     const int ts = a.heads * D;
     const long long base = ((sr.start + t0) * a.heads + h) * (long long)D;
     const uint16_t *kg = static_cast<const uint16_t *>(a.k) + base;
@@ -230,6 +232,8 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
     const int qh = w >> 2, cq = w & 3, r32 = lane & 31, hf = lane >> 5;
 
     const SeqRange sr = sequence_of(a, n);
+    const int gused = sp.used(sr.len);  // segments this sequence has
+    if (g >= gused) return;
     const long long seg0 = (long long)g * seg_len;
     long long len = sr.len - seg0;
     len = len < 0 ? 0 : (len > seg_len ? seg_len : len);
@@ -416,7 +420,7 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
 #pragma unroll
             for (int v = 0; v < 16; ++v) dst[sidx(db, v)] = S[db][v];
         if (g + 1 < segments) flag_end_state(end_flags(sp, u, g), S, w, lane);
-    } else if (a.state_out && g == segments - 1) {
+    } else if (a.state_out && g == gused - 1) {
         const long long sb = (long long)uh * D * D;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
@@ -769,7 +773,7 @@ __device__ __forceinline__ FixChunk<OutT> fix_chunk(const PrefillArgs &a, const 
     const long long T = uniform64(prows[p]);
     x.t0 = uniform64((j - first[p]) * C);
     x.m = (int)(T - x.t0 < C ? T - x.t0 : C);
-    const long long row = (long long)n * a.seqlen + (long long)x.g * sp.seg_len + x.t0;
+    const long long row = uniform64(sequence_of(a, n).start) + (long long)x.g * sp.seg_len + x.t0;
     const long long off = (row * a.heads + h) * (long long)D;
     x.q = static_cast<const uint16_t *>(a.q) + off;
     x.gate = NG ? static_cast<const uint16_t *>(a.ng.gate) + off : nullptr;
@@ -839,9 +843,10 @@ __global__ __launch_bounds__(NT, 4) void fix_kernel(PrefillArgs a, Segmented sp,
         if (!fix_head(s2, sp.seg_len, sp.fix_osz)) return;
         const int e = 4 * ((blockIdx.x % kFinalSlices) * NT + tid);
         float *u = sp.unit(ws, uh);
+        const long long len = sequence_of(a, uh / a.heads).len;
         float4 acc = *reinterpret_cast<const float4 *>(sp.start_state(u, 0) + e);
-        for (int g = 1; g < sp.segments; ++g) {
-            const float f = fast_exp2(-s2 * (float)seg_len_at(sp, a.seqlen, g));
+        for (int g = 1; g < sp.used(len); ++g) {
+            const float f = fast_exp2(-s2 * (float)seg_len_at(sp, len, g));
             const float4 x = *reinterpret_cast<const float4 *>(sp.start_state(u, g) + e);
             acc = make_float4(f * acc.x + x.x, f * acc.y + x.y, f * acc.z + x.z, f * acc.w + x.w);
         }
@@ -859,10 +864,9 @@ __global__ __launch_bounds__(NT, 4) void fix_kernel(PrefillArgs a, Segmented sp,
         const int g = 1 + tid % gs, uh = tid / gs;
         const float s2 = a.slopes[uh % a.heads] * LOG2E;
         long long rows = 0;
-        if (fix_head(s2, sp.seg_len, sp.fix_osz)) {
-            const long long len = seg_len_at(sp, a.seqlen, g);
+        const long long len = seg_len_at(sp, sequence_of(a, uh / a.heads).len, g);
+        if (len > 0 && fix_head(s2, sp.seg_len, sp.fix_osz))
             rows = start_poisoned(sp, sp.unit(ws, uh), g) ? len : fix_rows<NG>(s2, sp.seg_len, len);
-        }
         prows[tid] = rows;
         x = (rows + C - 1) / C;
     }
@@ -943,8 +947,8 @@ __global__ __launch_bounds__(NT, 4) void fix_kernel(PrefillArgs a, Segmented sp,
 #pragma unroll
                         for (int r = 0; r < 4; ++r) acc[i][r] = e[(16 * i + r) * D];
                 }
-                for (int g = 1; g < cur.g; ++g) {
-                    const float f = fast_exp2(-cur.s2 * (float)seg_len_at(sp, a.seqlen, g));
+                for (int g = 1; g < cur.g; ++g) {  // segments before cur.g are whole
+                    const float f = fast_exp2(-cur.s2 * (float)sp.seg_len);
                     const float *e = sp.start_state(u, g) + (4 * kq + 64 * half) * D + c;
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
@@ -1013,7 +1017,8 @@ hipError_t launch(const PrefillArgs &a, const PrefillPlan &p, void *workspace, h
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(uh * kCombineSlices)), dim3(kCombineThreads),
-                           0, stream, a.slopes, a.heads, a.state_in, a.state_in_t, sp, ws);
+                           0, stream, a.slopes, a.heads, a.state_in, a.state_in_t, sp,
+                           SeqLens{a.cu_seqlens, a.total_tokens, a.seqlen}, ws);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

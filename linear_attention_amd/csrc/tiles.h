@@ -341,11 +341,34 @@ __device__ __forceinline__ bool fix_head(float s2, long long seg_len, int osz) {
     return n < seg_len && n * (1 + osz) <= 4 * seg_len;
 }
 
+// Lengths of the sequences of a launch: packed (cu_seqlens, every boundary
+// clamped into [0, total]) or all of one length.
+struct SeqLens {
+    const int *cu;
+    long long total, seqlen;
+    __device__ long long len(int n) const {
+        if (!cu) return seqlen;
+        long long lo = cu[n], hi = cu[n + 1];
+        lo = lo < 0 ? 0 : (lo > total ? total : lo);
+        hi = hi < lo ? lo : (hi > total ? total : hi);
+        return hi - lo;
+    }
+};
+
+// The plan is cut on the longest sequence (packed batches: the caller's
+// max_seqlen); a sequence of `len` tokens uses its first used(len) segments
+// (at least one, which also carries a zero-length sequence's state), and its
+// pre-pass pieces cover the first covered(len) of its tokens. Workgroups of the
+// other segments and pieces exit at once.
 struct Segmented {
     int segments, pieces;
     long long seg_len, piece_len;
     int fix_osz = 0;  // output element size when heads may take local-start segments, else 0
-    __device__ long long covered() const { return (segments - 1) * seg_len; }
+    __device__ int used(long long len) const {
+        const long long g = (len + seg_len - 1) / seg_len;
+        return g < 1 ? 1 : (g > segments ? segments : (int)g);
+    }
+    __device__ long long covered(long long len) const { return (long long)(used(len) - 1) * seg_len; }
     __device__ float *unit(float *ws, int uh) const {
         return ws + (size_t)uh * (size_t)(pieces + 2 * segments - 1) * D * D;
     }
@@ -404,9 +427,10 @@ __device__ __forceinline__ long long uniform64(long long x) {
     return (long long)(((unsigned long long)hi << 32) | lo);
 }
 
+// Tokens of segment g of a sequence of `seqlen` tokens (0 past its end).
 __device__ __forceinline__ long long seg_len_at(const Segmented &sp, long long seqlen, int g) {
     const long long rest = seqlen - (long long)g * sp.seg_len;
-    return rest < sp.seg_len ? rest : sp.seg_len;
+    return rest < 0 ? 0 : (rest < sp.seg_len ? rest : sp.seg_len);
 }
 
 // Pre-pass grouping. The plan cuts the first G-1 segments of every head into
@@ -445,7 +469,7 @@ constexpr int kCombineSlices = D * D / (4 * kCombineThreads);
 // s0: [units, heads, d, d] first state (null: zero); s0_t: given transposed.
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float *slopes, int heads,
                                                                    const float *s0, bool s0_t,
-                                                                   Segmented sp, float *ws) {
+                                                                   Segmented sp, SeqLens sl, float *ws) {
     const int uh = blockIdx.x / kCombineSlices;
     const int e = 4 * ((blockIdx.x % kCombineSlices) * kCombineThreads + threadIdx.x);
     const int h = uh % heads;
@@ -463,9 +487,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float *s
         }
     }
     *reinterpret_cast<float4 *>(sp.start_state(u, 0) + e) = acc;
-    const long long covered = sp.covered();
+    const long long covered = sp.covered(sl.len(uh / heads));
     const int kg = prepass_group(slopes, heads, (int)(gridDim.x / kCombineSlices) / heads, sp);
-    const int groups = (sp.pieces + kg - 1) / kg;
+    const int groups = (int)((covered + kg * sp.piece_len - 1) / (kg * sp.piece_len));
     auto last_piece = [&](int j) { return (j + 1) * kg - 1 < sp.pieces - 1 ? (j + 1) * kg - 1 : sp.pieces - 1; };
     // the group states are independent loads: issue a batch of them ahead of
     // the sequential accumulation (this kernel never writes piece slots)

@@ -52,7 +52,7 @@ def test_status_strings():
         assert la.status_string(code).startswith(name)
         assert getattr(la, name) == code
     assert la.status_string(99) == "unknown lt_status"
-    assert la.lib.lt_version() == 10100
+    assert la.lib.lt_version() == 20000
 
 
 def test_build_id_matches_the_sources():
@@ -102,9 +102,9 @@ def test_prefill_noalloc_checks_arguments_before_any_hip_call(kw, code):
 
 def varlen(**kw):
     args = dict(q=A, k=A + 100 * MB, v=A + 200 * MB, in_dtype=la.LT_BF16,
-                cu=A + 290 * MB, num_seqs=2, total=64, slopes=A + 300 * MB, o=A + 400 * MB,
-                out_dtype=la.LT_F32, state_in=None, state_out=A + 900 * MB, heads=2,
-                head_dim=128, block=64, stream=None)
+                cu=A + 290 * MB, num_seqs=2, total=64, max_seqlen=40, slopes=A + 300 * MB,
+                o=A + 400 * MB, out_dtype=la.LT_F32, state_in=None, state_out=A + 900 * MB, heads=2,
+                head_dim=128, block=64, workspace=None, workspace_bytes=0, stream=None)
     args.update(kw)
     return la.lib.lt_prefill_varlen(*args.values())
 
@@ -192,7 +192,24 @@ def test_varlen_checks():
     assert varlen(block=0) == la.LT_ERR_BLOCK
     assert varlen(cu=A + 400 * MB) == la.LT_ERR_ALIAS            # cu_seqlens inside o
     assert varlen(num_seqs=0) == la.LT_OK
-    assert varlen(total=0, state_out=None, q=None, k=None, v=None, o=None) == la.LT_OK
+    assert varlen(total=0, max_seqlen=0, state_out=None, q=None, k=None, v=None, o=None) == la.LT_OK
+    assert varlen(max_seqlen=-1) == la.LT_ERR_SHAPE
+    assert varlen(max_seqlen=65) == la.LT_ERR_SHAPE               # longer than all tokens
+    assert varlen(workspace=A + 100, workspace_bytes=4096) == la.LT_ERR_ALIAS   # inside q
+    assert varlen(workspace=A + 290 * MB, workspace_bytes=4096) == la.LT_ERR_ALIAS  # on cu_seqlens
+
+
+def test_varlen_workspace_query():
+    ws = la.lt_prefill_varlen_workspace_bytes
+    st = 128 * 128 * 4
+    # 2 sequences x 64 heads, longest 131072 tokens: 2 segments of 65536, the
+    # first covered by 16 pre-pass pieces of 4096 (2048 pre-pass workgroups)
+    assert ws(2, 131072, 64) == 2 * 64 * (16 + 2 * 2 - 1) * st
+    # the fixed-length plan of the same longest length
+    assert ws(2, 131072, 64) == la.lt_prefill_workspace_bytes(2, 131072, 64)
+    assert ws(16, 65536, 64) == 0          # 1024 (sequence, head) pairs: no split
+    assert ws(2, 3000, 64) == 0            # too short to split
+    assert ws(0, 100, 64) == 0 and ws(2, 0, 64) == 0 and ws(2, 100, 64, 96) == 0
 
 
 @pytest.mark.parametrize("field", ["q", "k", "v", "slopes", "state", "o"])
@@ -225,9 +242,10 @@ def prefill_ng(**kw):
 
 def varlen_ng(**kw):
     args = dict(q=A, k=A + 100 * MB, v=A + 200 * MB, in_dtype=la.LT_BF16, cu=A + 290 * MB,
-                num_seqs=2, total=64, slopes=A + 300 * MB, gate=A + 310 * MB, weight=A + 350 * MB,
-                eps=1e-6, y=A + 400 * MB, out_dtype=la.LT_F32, state_in=None,
-                state_out=A + 900 * MB, heads=2, head_dim=128, block=64, stream=None)
+                num_seqs=2, total=64, max_seqlen=64, slopes=A + 300 * MB, gate=A + 310 * MB,
+                weight=A + 350 * MB, eps=1e-6, y=A + 400 * MB, out_dtype=la.LT_F32, state_in=None,
+                state_out=A + 900 * MB, heads=2, head_dim=128, block=64, workspace=None,
+                workspace_bytes=0, stream=None)
     args.update(kw)
     return la.lib.lt_prefill_varlen_norm_gate(*args.values())
 
@@ -281,7 +299,7 @@ def test_norm_gate_noops_need_no_gpu():
     assert prefill_ng(batch=0) == la.LT_OK
     assert prefill_ng(heads=0) == la.LT_OK
     assert prefill_ng(seqlen=0, state_out=None, gate=None, weight=None) == la.LT_OK
-    assert varlen_ng(num_seqs=0, total=0) == la.LT_OK
+    assert varlen_ng(num_seqs=0, total=0, max_seqlen=0) == la.LT_OK
     assert decode_ng(batch=0, gate=None, weight=None) == la.LT_OK
 
 

@@ -1,0 +1,117 @@
+"""GPU parity of packed (varlen) prefill whose long sequences are split across
+workgroups: the plan is cut on the longest sequence (max_seqlen) and every
+sequence uses the segments its own length needs, with the pre-pass and the
+carried-state correction stopping at its end.
+
+Tolerance: relative L2 per (sequence, head) <= 1e-2 with every row within the
+row bound (parity_util.parity_err), outputs and final states.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from parity_util import (TOL_BF16, ensure_built, max_rel_per_head, max_rel_states, parity_err,
+                         to_device, to_host_f32)
+
+pytestmark = pytest.mark.gpu
+
+# heads 0-2 on the pre-pass (their memory outlasts a segment), 3-6 on
+# local-start segments with a carried-state correction
+MIX = np.array([0.0, 1e-6, 0.005, 0.02, 0.2, 1.0, 30.0], np.float32)
+
+
+@pytest.fixture(scope="module")
+def la():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm device")
+    ensure_built()
+    import linear_attention_amd
+
+    return linear_attention_amd
+
+
+@pytest.mark.parametrize("lens,max_given,out_dtype", [
+    ([9000, 0, 5000, 1, 12000], True, "f32"),     # 5 segments of 2432: 4, 1, 3, 1, 5 used
+    ([9000, 0, 5000, 1, 12000], False, "bf16"),   # plan cut on all 26001 tokens instead
+    ([4097, 8191, 64, 8192], True, "f32"),        # segment-edge lengths
+])
+def test_varlen_segmented_both_routes(la, lens, max_given, out_dtype):
+    import torch
+
+    H = len(MIX)
+    cu = workloads.cu_seqlens(lens)
+    T, n = int(cu[-1]), len(lens)
+    mx = max(lens) if max_given else None
+    assert la.lt_prefill_varlen_workspace_bytes(n, max(lens), H) > 0
+    print(f"[case] varlen segmented lens={lens} max_seqlen={mx} out={out_dtype}", flush=True)
+    q, k, v = workloads.qkv_host(6101 + T, (T, H, 128), "bf16")
+    s0 = workloads.state_host(6102 + T, (n, H, 128, 128))
+    st = torch.from_numpy(s0).cuda()
+    od = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    o, _ = la.lt_prefill_varlen(*(to_device(x, "bf16") for x in (q, k, v)), torch.from_numpy(cu).cuda(),
+                                torch.from_numpy(MIX).cuda(), 256, st, max_seqlen=mx, state_out=st,
+                                out_dtype=od)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.recurrence_packed(q, k, v, MIX, cu, s0=s0)
+    eo = max_rel_per_head(to_host_f32(o), o_ref, cu)
+    es = max_rel_states(to_host_f32(st), s_ref)
+    print(f"[result] o {eo:.3e} state {es:.3e}", flush=True)
+    assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)
+
+
+def test_varlen_segmented_norm_gate(la):
+    import torch
+
+    lens = [9000, 0, 5000, 1, 12000]
+    H = len(MIX)
+    cu = workloads.cu_seqlens(lens)
+    T, n = int(cu[-1]), len(lens)
+    print(f"[case] varlen segmented norm-gate lens={lens}", flush=True)
+    q, k, v = workloads.qkv_host(6201, (T, H, 128), "bf16")
+    gate = workloads.gate_host(6202, (T, H, 128))
+    nw = workloads.norm_weight_host(6203, H)
+    s0 = workloads.state_host(6204, (n, H, 128, 128))
+    y, st = la.lt_prefill_varlen_norm_gate(*(to_device(x, "bf16") for x in (q, k, v)),
+                                           torch.from_numpy(cu).cuda(), torch.from_numpy(MIX).cuda(),
+                                           to_device(gate, "bf16"), torch.from_numpy(nw).cuda(),
+                                           workloads.NORM_EPS, 256, torch.from_numpy(s0).cuda(),
+                                           max_seqlen=max(lens), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.recurrence_packed(q, k, v, MIX, cu, s0=s0)
+    y_ref = oracle.norm_gate(o_ref, gate, nw, workloads.NORM_EPS)
+    ey = max_rel_per_head(to_host_f32(y), y_ref, cu)
+    es = max_rel_states(to_host_f32(st), s_ref)
+    print(f"[result] y {ey:.3e} state {es:.3e}", flush=True)
+    assert ey <= TOL_BF16 and es <= TOL_BF16, (ey, es)
+
+
+def test_varlen_two_long_sequences_match_fixed_length(la):
+    """2 x 131072 tokens x 64 heads with carried states: the packed call plans
+    like lt_prefill on the same [2, 131072] batch (2 segments per sequence), so
+    the two agree bit for bit; sampled heads against the oracle."""
+    import torch
+
+    L, H, nseq = 131072, 64, 2
+    print(f"[case] varlen 2 x {L} x {H} heads vs lt_prefill", flush=True)
+    q, k, v = workloads.qkv_device(6301, (nseq, L, H, 128), "bf16")
+    s0 = workloads.state_device(6302, (nseq, H, 128, 128), std=0.1)
+    sl = workloads.slopes(H)
+    slt = torch.from_numpy(sl).cuda()
+    o_fix, s_fix = la.lt_prefill(q, k, v, slt, 256, s0)
+    cu = torch.tensor([0, L, 2 * L], dtype=torch.int32, device="cuda")
+    flat = lambda x: x.view(nseq * L, H, 128)
+    o_var, s_var = la.lt_prefill_varlen(flat(q), flat(k), flat(v), cu, slt, 256, s0, max_seqlen=L)
+    torch.cuda.synchronize()
+    assert torch.equal(o_var, flat(o_fix)) and torch.equal(s_var, s_fix)
+    hs = [0, 63]
+    hq, hk, hv = (to_host_f32(flat(x)[:, hs].contiguous()) for x in (q, k, v))
+    o_ref, s_ref = oracle.recurrence_packed(hq, hk, hv, sl[hs], [0, L, 2 * L], s0=to_host_f32(s0)[:, hs])
+    og = to_host_f32(o_var[:, hs].contiguous())
+    eo = max(parity_err(og[a:b, j], o_ref[a:b, j]) for a, b in ((0, L), (L, 2 * L)) for j in range(2))
+    es = max_rel_states(to_host_f32(s_var)[:, hs], s_ref)
+    print(f"[result] o {eo:.3e} state {es:.3e}", flush=True)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
