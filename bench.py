@@ -237,7 +237,7 @@ def run_m1_prefill(la, torch, steps, warmup, slope_scale=1.0):
     res = {"tokens_per_s": tokens * steps / wall, "ms_per_step": wall * 1e3 / steps, "kernel_ms_mean": ms,
            "kernel_ms_median": med,
            "roofline": hbm_roofline(nbytes, ms, "lt_prefill call: piece_state_kernel + combine_kernel + "
-                                    "head_kernel<float> + fix_kernel<float, false>",
+                                    "head_kernel<float> + finish_kernel<float, false>",
                                     committed_traffic("m1_layer") if slope_scale == 1.0 else None)}
     return w, (q, k, v, slopes), res
 
@@ -265,7 +265,7 @@ def run_norm_gate(la, torch, steps, warmup):
     return {"workload": w.name + " + norm_gate", "gate_dtype": "bf16", "out_dtype": "bf16",
             "tokens_per_s": round(tokens / (ms / 1e3), 1), "kernel_ms_mean": round(ms, 5),
             "roofline": hbm_roofline(nbytes, ms, "lt_prefill_norm_gate call: piece_state_kernel + "
-                                     "combine_kernel + head_kernel<bf16, norm-gate> + fix_kernel<bf16, true>")}
+                                     "combine_kernel + head_kernel<bf16, norm-gate> + finish_kernel<bf16, true>")}
 
 
 def run_backward(la, torch, steps, warmup, batch, seqlen):

@@ -203,7 +203,7 @@ __global__ __launch_bounds__(NT, 4) void rev_piece_kernel(BackwardArgs a, Segmen
     const int qh = w >> 2, cq = w & 3, r32 = lane & 31, hf = lane >> 5;
 
     const float s2 = a.slopes[h] * LOG2E;
-    if (fix_head(s2, sp.seg_len, sp.fix_osz)) return;  // local-start segments: no pre-pass
+    if (!takes_prepass(sp, s2)) return;  // local-start segments: no pre-pass
     const int jl = j + kgr - 1 < sp.pieces - 1 ? j + kgr - 1 : sp.pieces - 1;
     // mirrored range [t0, t1) = real tokens [L - t1, L - t0)
     const long long L = a.seqlen;

@@ -30,11 +30,13 @@
 //    contributed by fixed pieces of every segment but the last (the same state
 //    update without outputs) into a workspace; segment g starts from
 //    e^{-s*start_g} S_0 plus each piece's state decayed to start_g.
-//  * Heads whose decay ends their memory within a segment skip the pre-pass:
-//    their segments start from a zero state, and a correction pass adds the
-//    missed carried-in term e^{-s(t+1)} q_t S_in to each segment's first
-//    tokens (with the norm-gate epilogue the main kernel leaves those rows raw
-//    in y and the correction pass also normalises and gates them).
+//  * Heads whose decay ends their memory well within a segment (below 2^-24
+//    after W tokens, W < the segment length) skip the pre-pass. Their tokens
+//    are cut into ranges of equal cost, one per remaining workgroup, and a
+//    range that starts at token t0 > 0 first rebuilds its carried-in state
+//    from the W tokens before t0 by state-only steps. A small finishing pass
+//    restores the NaN and Inf that the exact operator carries past a range's
+//    end (a warm-up window cannot see them).
 //  * Outputs go through LDS and leave as whole rows (full 512-byte fp32 rows
 //    stream far better than the 32-byte pieces of the accumulator layout).
 //  * Shared building blocks (layouts, operand loads, staging, state update)
@@ -77,11 +79,10 @@ __device__ __forceinline__ void row_sumsq(float *rss, const f32x16 &o, int qh, i
     if (lane < 32) rss[(32 * qh + lane) * 4 + cq] = ss;
 }
 
-// raw: store o itself (every factor replaced by 1, by a select).
 template <bool FULL, typename OutT>
 __device__ __forceinline__ void store_rows_norm_gate(OutT *out, long long ts, const float *Os,
                                                      const float *rss, int m, int tid,
-                                                     const uint2 (&gr)[4], float4 w, float eps, bool raw) {
+                                                     const uint2 (&gr)[4], float4 w, float eps) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int row = (tid >> 5) + 16 * j, col = 4 * (tid & 31);
@@ -90,8 +91,8 @@ __device__ __forceinline__ void store_rows_norm_gate(OutT *out, long long ts, co
         const float inv = __builtin_amdgcn_rsqf((p.x + p.y + p.z + p.w) * (1.f / D) + eps);
         const float g0 = __uint_as_float(gr[j].x << 16), g1 = __uint_as_float(gr[j].x & 0xffff0000u);
         const float g2 = __uint_as_float(gr[j].y << 16), g3 = __uint_as_float(gr[j].y & 0xffff0000u);
-        const float f0 = raw ? 1.f : inv * w.x * sigmoid(g0), f1 = raw ? 1.f : inv * w.y * sigmoid(g1);
-        const float f2 = raw ? 1.f : inv * w.z * sigmoid(g2), f3 = raw ? 1.f : inv * w.w * sigmoid(g3);
+        const float f0 = inv * w.x * sigmoid(g0), f1 = inv * w.y * sigmoid(g1);
+        const float f2 = inv * w.z * sigmoid(g2), f3 = inv * w.w * sigmoid(g3);
         const float4 y = make_float4(x.x * f0, x.y * f1, x.z * f2, x.w * f3);
         if (FULL || row < m) put4(out + row * ts + col, y);
     }
@@ -120,7 +121,7 @@ __global__ __launch_bounds__(NT, 4) void piece_state_kernel(PrefillArgs a, Segme
     const int qh = w >> 2, cq = w & 3, r32 = lane & 31, hf = lane >> 5;
 
     const float s2 = a.slopes[h] * LOG2E;
-    if (fix_head(s2, sp.seg_len, sp.fix_osz)) return;  // local-start segments: no pre-pass
+    if (!takes_prepass(sp, s2)) return;  // warm-up segments: no pre-pass
     const int jl = j + kgr - 1 < sp.pieces - 1 ? j + kgr - 1 : sp.pieces - 1;
     const SeqRange sr = sequence_of(a, n);
     const long long covered = sp.covered(sr.len);
@@ -190,8 +191,224 @@ __global__ __launch_bounds__(NT, 4) void piece_state_kernel(PrefillArgs a, Segme
     store_state(jl);
 }
 
+
 // ---------------------------------------------------------------------------
 constexpr int kRankUnits = 64;
+// Segmented plans have fewer than 256 (sequence, head) pairs.
+constexpr int kMaxPairs = 256;
+
+// Warm-up cost of a token against an output token: its k and v rows (2 x 256 B)
+// against q, k, v, the output row and, with the norm-gate epilogue, the gate row.
+template <typename OutT, bool NG>
+__device__ constexpr double warm_cost() {
+    return 512.0 / (768.0 + 128.0 * sizeof(OutT) + (NG ? 256.0 : 0.0));
+}
+
+// The heads of a segmented plan split by route (each wave computes the same
+// lists: 64 heads at a time by ballot, in head order).
+struct Routes {
+    int npre, nwarm;
+};
+__device__ inline Routes split_heads(const float *slopes, int heads, const Segmented &sp, short *pre,
+                                     short *warm, bool write) {
+    const int lane = threadIdx.x & 63;
+    Routes r{0, 0};
+    for (int h0 = 0; h0 < heads; h0 += 64) {
+        const int h = h0 + lane;
+        const bool in = h < heads;
+        const bool p = in && takes_prepass(sp, slopes[in ? h : 0] * LOG2E);
+        const unsigned long long bp = __ballot(p), bw = __ballot(in && !p);
+        if (write) {
+            const int below = lane ? __popcll(bp & (~0ull >> (64 - lane))) : 0;
+            const int belw = lane ? __popcll(bw & (~0ull >> (64 - lane))) : 0;
+            if (p) pre[r.npre + below] = (short)h;
+            if (in && !p) warm[r.nwarm + belw] = (short)h;
+        }
+        r.npre += __popcll(bp);
+        r.nwarm += __popcll(bw);
+    }
+    return r;
+}
+
+// Work of a workgroup of a segmented plan. The (unit, head) pairs of heads on
+// the pre-pass route take `segments` workgroups each, one per segment: the
+// first npre * units * segments workgroups, pair i of them (i / segments) the
+// i-th such pair in (unit, head) order. The tokens of the other pairs (the
+// warm-up route, see warm_len) are cut into ranges of equal cost over the
+// remaining workgroups, one range each; a range may end in one pair and go on
+// in the next. An output token costs 1 and a warm-up token warm_cost(); pair j
+// (the j-th warm pair in (unit, head) order) costs
+//     C_j = len_j + warm_cost * min(W_j, len_j) * len_j / T0,
+// its length plus the warm-ups of the about len_j / T0 cuts inside it (T0: the
+// warm tokens per workgroup), spread evenly over its tokens; that balances the
+// workgroups to first order. A workgroup's range is [r T, (r+1) T) of the
+// prefix sums of C (T = sum C / workgroups), mapped onto each pair's tokens
+// linearly and cut at whole 64-token sub-blocks, so neighbours agree on every
+// cut. Ranges ending inside a pair leave a flag (and, when non-finite, their
+// end state) in the slots of their home pair, the (r / segments)-th warm pair,
+// which the finishing pass reads.
+struct WarmCut {
+    const double *cpre;  // [nwarm pairs + 1] prefix sums of C
+    double T;
+    __device__ long long cut(int j, double c, long long len) const {
+        const double a = cpre[j], b = cpre[j + 1];
+        if (c <= a) return 0;
+        if (c >= b) return len;
+        long long x = (long long)((c - a) / (b - a) * (double)len) / 64 * 64;
+        return x < 0 ? 0 : (x > len ? len : x);
+    }
+};
+
+// Segmented plans launch fewer than two workgroups per CU.
+constexpr int kMaxWarmWgs = 512;
+// Home slots of warm workgroup r (r counted from the first warm workgroup):
+// its flag {pair + 1 if its end state is non-finite else 0, cut} at ints
+// 2 (r % segments) of slot `segments` of its home pair, and that end state in
+// slot r % segments. Slot segments + 1 of a warm pair holds its final state
+// on in-place calls.
+__device__ __forceinline__ float *warm_home(float *ws, const Segmented &sp, const short *heads_warm, int nwarm,
+                                            int heads, int r) {
+    const int iw = r / sp.segments;
+    return sp.unit(ws, (iw / nwarm) * heads + heads_warm[iw % nwarm]);
+}
+__device__ __forceinline__ int *warm_flag(float *ws, const Segmented &sp, const short *heads_warm, int nwarm,
+                                          int heads, int r) {
+    return reinterpret_cast<int *>(Segmented::slot(warm_home(ws, sp, heads_warm, nwarm, heads, r), sp.segments)) +
+           2 * (r % sp.segments);
+}
+__device__ __forceinline__ float *warm_end_state(float *ws, const Segmented &sp, const short *heads_warm, int nwarm,
+                                                 int heads, int r) {
+    return Segmented::slot(warm_home(ws, sp, heads_warm, nwarm, heads, r), r % sp.segments);
+}
+
+// A workgroup's current piece, as thread 0 lays it out for the others: rows
+// of the piece's first token (k and v: of its warm-up's first token; row
+// stride ts elements), its length, the carried-in state and where the end
+// state goes.
+struct Piece {
+    const uint16_t *q, *k, *v, *gate;
+    void *o;
+    const float *nw;    // the head's normalisation weights (norm-gate epilogue)
+    const float *s_in;  // carried-in state (nullptr: zero)
+    float *dst;         // end state destination
+    int *flag;          // end == 2: the range's flag
+    long long len, warm;  // tokens of the piece; warm-up tokens before it (whole sub-blocks)
+    float s2, eps;
+    int ts;
+    int uh;      // -1: no more pieces
+    int s_in_t;  // s_in transposed
+    int cut;     // end == 2: the token the range ends at
+    int end;     // 0 nothing, 1 the end state to dst, 2 to dst and flagged if non-finite
+};
+// Warm-route bookkeeping of a workgroup.
+struct PlanState {
+    double T;   // cost per workgroup
+    int rl;     // this workgroup's range, counted from the first warm workgroup
+    int next;   // the next pair to visit (pw: none)
+    int npre, nwarm, pw;
+    int last;   // the last workgroup (takes every pair left)
+};
+
+template <typename OutT>
+__device__ void piece_rows(Piece &p, const PrefillArgs &a, int n, int h, long long t0, long long t1,
+                           long long t0w) {
+    const long long start = sequence_of(a, n).start;
+    const long long r0 = ((start + t0) * a.heads + h) * (long long)D, rw = ((start + t0w) * a.heads + h) * (long long)D;
+    p.q = static_cast<const uint16_t *>(a.q) + r0;
+    p.k = static_cast<const uint16_t *>(a.k) + rw;
+    p.v = static_cast<const uint16_t *>(a.v) + rw;
+    p.o = static_cast<OutT *>(a.o) + r0;
+    p.gate = a.ng.gate ? static_cast<const uint16_t *>(a.ng.gate) + r0 : nullptr;
+    p.nw = a.ng.norm_weight ? a.ng.norm_weight + h * D : nullptr;
+    p.len = t1 - t0;
+    p.warm = t0 - t0w;
+    p.s2 = a.slopes[h] * LOG2E;
+    p.eps = a.ng.eps;
+    p.ts = a.heads * D;
+    p.uh = n * a.heads + h;
+}
+
+// The next piece of this workgroup (thread 0; the arguments are LDS copies,
+// so that none of them stays in registers through a piece).
+template <typename OutT>
+__device__ Piece next_piece(const PrefillArgs &a, const Segmented &sp, float *ws, int mode, int k,
+                            PlanState &ps, const short *heads_pre, const short *heads_warm, const double *cpre,
+                            const int *by_rank) {
+    const SeqLens lens{a.cu_seqlens, a.total_tokens, a.seqlen};
+    Piece p{};
+    p.uh = -1;
+    if (mode == 0) {  // the whole sequence of one pair
+        if (k > 0) return p;
+        int n = blockIdx.x / a.heads;
+        const int h = blockIdx.x % a.heads;
+        if (a.cu_seqlens && a.units <= kRankUnits) n = by_rank[n];
+        piece_rows<OutT>(p, a, n, h, 0, lens.len(n), 0);
+        const size_t sb = (size_t)p.uh * D * D;
+        p.s_in = a.state_in ? a.state_in + sb : nullptr;
+        p.s_in_t = a.state_in_t;
+        p.dst = a.state_out ? a.state_out + sb : nullptr;
+        p.end = p.dst ? 1 : 0;
+        return p;
+    }
+    if (mode == 1) {  // one segment of a pre-pass pair
+        if (k > 0) return p;
+        const int i = blockIdx.x / sp.segments, g = blockIdx.x % sp.segments;
+        const int n = i / ps.npre, h = heads_pre[i % ps.npre];
+        const long long len = lens.len(n);
+        if (g >= sp.used(len)) return p;
+        const long long t0 = (long long)g * sp.seg_len;
+        piece_rows<OutT>(p, a, n, h, t0, t0 + seg_len_at(sp, len, g), t0);
+        p.s_in = sp.start_state(sp.unit(ws, p.uh), g);  // the combine pass wrote it (S_0 for g = 0)
+        p.dst = a.state_out && g == sp.used(len) - 1 ? a.state_out + (size_t)p.uh * D * D : nullptr;
+        p.end = p.dst ? 1 : 0;
+        return p;
+    }
+    const WarmCut wc{cpre, ps.T};
+    const double c0 = (double)ps.rl * ps.T, c1 = (double)(ps.rl + 1) * ps.T;
+    while (ps.next < ps.pw) {
+        const int j = ps.next;
+        const int n = j / ps.nwarm, h = heads_warm[j % ps.nwarm];
+        const long long len = lens.len(n);
+        const long long t0 = wc.cut(j, c0, len);
+        const long long t1 = ps.last ? len : wc.cut(j, c1, len);
+        ps.next = ps.last || cpre[j + 1] < c1 ? j + 1 : ps.pw;  // the range goes on into the next pair
+        if (t1 <= t0) continue;
+        const long long wl = warm_len(a.slopes[h] * LOG2E);
+        const long long t0w = t0 > wl ? t0 - wl : 0;
+        piece_rows<OutT>(p, a, n, h, t0, t1, t0w);
+        const size_t sb = (size_t)p.uh * D * D;
+        if (t0w == 0 && a.state_in) {  // the warm-up reaches the sequence start: exact
+            p.s_in = a.state_in + sb;
+            p.s_in_t = a.state_in_t;
+        }
+        if (t1 < len) {
+            p.dst = warm_end_state(ws, sp, heads_warm, ps.nwarm, a.heads, ps.rl);
+            p.flag = warm_flag(ws, sp, heads_warm, ps.nwarm, a.heads, ps.rl);
+            p.cut = (int)t1;
+            p.end = 2;
+        } else if (a.state_out) {
+            p.dst = a.state_in == a.state_out ? Segmented::slot(sp.unit(ws, p.uh), sp.segments + 1)
+                                              : a.state_out + sb;
+            p.end = 1;
+        }
+        return p;
+    }
+    return p;
+}
+
+// x, opaque to the optimiser: nothing computed from it moves out of the loop
+// that computes it.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+template <typename T>
+__device__ __forceinline__ T *uniform_ptr(T *p) {
+    return reinterpret_cast<T *>(uniform64((long long)reinterpret_cast<uintptr_t>(p)));
+}
+__device__ __forceinline__ float uniformf(float x) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
 
 template <typename OutT, bool NG>
 __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, float *ws) {
@@ -201,231 +418,354 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
     __shared__ __attribute__((aligned(16))) __bf16 Vds[C * D];
     __shared__ __attribute__((aligned(16))) __bf16 Sts[2][D * D];
     __shared__ __attribute__((aligned(16))) __bf16 Ps[C * PW];
-
-    const int segments = sp.segments;
-    const long long seg_len = sp.seg_len;
-    const int g = blockIdx.x % segments;
-    const int slot = blockIdx.x / segments;
-    const int h = slot % a.heads;
-    const int tid = threadIdx.x, lane = tid & 63;
-    // Packed batches of up to kRankUnits sequences run their longest sequences
-    // first: unit slot r takes the sequence of rank r by length (descending,
-    // ties by index), so the long whole-sequence workgroups do not start last
-    // and leave the end of the launch to a few CUs.
-    int n = slot / a.heads;
-    if (a.cu_seqlens && a.units <= kRankUnits) {
-        __shared__ long long lens[kRankUnits];
-        __shared__ int by_rank[kRankUnits];
-        if (tid < a.units) lens[tid] = sequence_of(a, tid).len;
-        __syncthreads();
-        if (tid < a.units) {
-            const long long li = lens[tid];
-            int r = 0;
-            for (int j = 0; j < a.units; ++j) r += lens[j] > li || (lens[j] == li && j < tid);
-            by_rank[r] = tid;
-        }
-        __syncthreads();
-        n = by_rank[n];
-    }
-    const int uh = n * a.heads + h;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int qh = w >> 2, cq = w & 3, r32 = lane & 31, hf = lane >> 5;
-
-    const SeqRange sr = sequence_of(a, n);
-    const int gused = sp.used(sr.len);  // segments this sequence has
-    if (g >= gused) return;
-    const long long seg0 = (long long)g * seg_len;
-    long long len = sr.len - seg0;
-    len = len < 0 ? 0 : (len > seg_len ? seg_len : len);
-    const int ts = a.heads * D;
-    const long long base = ((sr.start + seg0) * a.heads + h) * (long long)D;
-    const uint16_t *qg = static_cast<const uint16_t *>(a.q) + base;
-    const uint16_t *kg = static_cast<const uint16_t *>(a.k) + base;
-    const uint16_t *vg = static_cast<const uint16_t *>(a.v) + base;
-    OutT *og = static_cast<OutT *>(a.o) + base;
-    const float s2 = a.slopes[h] * LOG2E;
-    // epilogue: gate rows of this (sequence, head) and the head's normalisation
-    // weights, kept in LDS (read after the first barrier B)
     __shared__ __attribute__((aligned(16))) float Wn[NG ? D : 1];
     __shared__ __attribute__((aligned(16))) float Rss[NG ? C * 4 : 1];  // per-row partial sums of o^2
-    const uint16_t *gg = NG ? static_cast<const uint16_t *>(a.ng.gate) + base : nullptr;
-    if (NG && tid < D / 4)
-        *reinterpret_cast<float4 *>(Wn + 4 * tid) = *reinterpret_cast<const float4 *>(a.ng.norm_weight + h * D + 4 * tid);
+    __shared__ double cpre[kMaxPairs + 1];
+    __shared__ short heads_pre[kMaxPairs], heads_warm[kMaxPairs];
+    __shared__ int by_rank[kRankUnits];
+    __shared__ long long rlen[kRankUnits];
+    __shared__ PlanState ps;
+    __shared__ Piece pc;
+    __shared__ int any_bad;
+    __shared__ __attribute__((aligned(16))) unsigned char args_lds[sizeof(PrefillArgs)];
+    __shared__ __attribute__((aligned(16))) unsigned char sp_lds[sizeof(Segmented)];
+    __shared__ float *ws_lds;
 
-    // ---- carried-in state of this segment (the combine pass wrote it for
-    // segmented plans; on local-start segments segment 0 reads S_0 itself and
-    // the final state is written by a later kernel; either way an in-place
-    // state update never races with this read)
-    f32x16 S[2];
-    auto sidx = [&](int db, int v) {
-        return (64 * qh + 32 * db + 8 * (v >> 2) + 4 * hf + (v & 3)) * D + 32 * cq + r32;
-    };
-    // local-start segments: segment 0 starts from S_0, the others from zero
-    // (the correction pass adds their carried-in term afterwards)
-    const bool fix = segments > 1 && fix_head(s2, seg_len, sp.fix_osz);
-    const float *s_in = segments > 1 && !fix
-                            ? sp.start_state(sp.unit(ws, uh), g)
-                            : ((segments == 1 || g == 0) && a.state_in ? a.state_in + (size_t)uh * D * D : nullptr);
-    if (s_in && (segments == 1 || fix) && a.state_in_t) {
-        // S_0 given transposed: element (r, c) at c * D + r
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int r = 64 * qh + 32 * db + 8 * (v >> 2) + 4 * hf + (v & 3), c = 32 * cq + r32;
-                S[db][v] = s_in[c * D + r];
-            }
-    } else if (s_in) {
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) S[db][v] = s_in[sidx(db, v)];
-    } else {
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) S[db][v] = 0.f;
-    }
-    write_state_t(Sts[0], S, qh, cq, lane);
-
-    // loop-invariant decay factors
-    const int qpos = 32 * qh + r32;                       // query row of this lane's outputs
-    const float dq = fast_exp2(-s2 * (float)(qpos + 1));  // d_q for that row
-    const bool scorer = w < 3;                            // waves 0..2 own one score block each
-    const int qb = w == 0 ? 0 : 1, kb = w == 2 ? 1 : 0;   // (query block, key block)
-    float dscore[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int diff = (32 * qb + r32) - (32 * kb + 8 * (v >> 2) + 4 * hf + (v & 3));
-        dscore[v] = masked_decay(diff, s2);
+    const int segments = sp.segments;
+    // thread indices of the set-up (each piece recomputes its own, below)
+    const int t0id = threadIdx.x, lane0 = t0id & 63;
+    const int w = __builtin_amdgcn_readfirstlane(t0id >> 6);
+    const SeqLens lens{a.cu_seqlens, a.total_tokens, a.seqlen};
+    if (t0id == 0) {
+        *reinterpret_cast<PrefillArgs *>(args_lds) = a;
+        *reinterpret_cast<Segmented *>(sp_lds) = sp;
+        ws_lds = ws;
     }
 
-    // Two register stages: sub-block c is staged in st[c % 2] and its loads are
-    // issued two sub-blocks ahead, so about 96 KiB of loads are in flight per CU.
-    Stage<true> st0, st1;
-    const long long nfull = len / C;
-    const int tail = (int)(len - nfull * C);
-    const long long nchunks = nfull + (tail > 0);
-    auto chunk_len = [&](long long c) { return c < nfull ? C : tail; };
-    auto prefetch = [&](Stage<true> &st, long long c) {
-        // past the end, re-read the last sub-block (ignored) to keep the count fixed
-        const long long cn = c < nchunks ? c : nchunks - 1;
-        const long long off = cn * C * (long long)ts;
-        st.load(qg + off, kg + off, vg + off, ts, chunk_len(cn), tid);
-    };
-    if (nchunks > 0) {
-        prefetch(st0, 0);
-        prefetch(st1, 1);
-    }
-
-    int cur = 0;
-    // Per sub-block: (B) tiles visible -> scores, inter-block product, state
-    // update -> (C) P visible -> intra-block product, output block to LDS ->
-    // (D) output tile visible and every read of this sub-block's tiles done ->
-    // full-row output stores. Barrier D of one sub-block also guards the tile
-    // writes of the next. The output tile reuses the S^T buffer that the
-    // inter-block product just finished reading (it is rewritten only after the
-    // next barrier B).
-    // norm-gate on a local-start segment g >= 1: the sub-blocks of its first
-    // raw_rows rows store the raw output to y (the epilogue's scale replaced
-    // by 1, a select rather than a second store path), which the correction
-    // pass finishes
-    const long long raw_rows = NG && fix && g > 0 ? ng_fix_rows(s2, seg_len, len) : 0;
-    auto step = [&](long long c, int m, auto full, Stage<true> &st) {
-        constexpr bool FULL = decltype(full)::value;
-        // gate rows of this sub-block, consumed by the epilogue at its end. They
-        // are issued ahead of the prefetch two sub-blocks out: loads complete in
-        // order, so the epilogue's wait for them then leaves that prefetch in
-        // flight (issued after it, the wait drained it: 0.63 -> 0.61 ms per
-        // norm-gate call on the M1 layer)
-        uint2 gr[4];
-        if constexpr (NG) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = (tid >> 5) + 16 * j;
-                const int rr = FULL || row < m ? row : m - 1;
-                gr[j] = stream_load8(gg + (c * C + rr) * (long long)ts + 4 * (tid & 31));
+    // ---- this workgroup's work: pieces (pair uh, tokens [t0, t1)), each
+    // starting from the pre-pass's start state, S_0, zero, and a warm-up
+    int mode;  // 0: one pair, whole (no segments); 1: one pre-pass segment; 2: warm ranges
+    if (segments == 1) {
+        mode = 0;
+        // Packed batches of up to kRankUnits sequences run their longest
+        // sequences first: unit slot r takes the sequence of rank r by length
+        // (descending, ties by index), so the long whole-sequence workgroups do
+        // not start last and leave the end of the launch to a few CUs.
+        if (a.cu_seqlens && a.units <= kRankUnits) {
+            if (t0id < a.units) rlen[t0id] = lens.len(t0id);
+            __syncthreads();
+            if (t0id < a.units) {
+                const long long li = rlen[t0id];
+                int r = 0;
+                for (int j = 0; j < a.units; ++j) r += rlen[j] > li || (rlen[j] == li && j < t0id);
+                by_rank[r] = t0id;
             }
         }
-        st.template store<FULL>(Qs, Ks, Vs, Vds, m, s2, tid);
-        if (FULL) prefetch(st, c + 2);
-        __syncthreads();  // (B) tiles and S^T of the previous sub-block are visible
-        if (scorer) {
-            // scores^T block: keys 32kb.., queries 32qb.. ; masked, decayed, to LDS as P
-            f32x16 sc;
+    } else {
+        const Routes rt = split_heads(a.slopes, a.heads, sp, heads_pre, heads_warm, w == 0);
+        __syncthreads();  // wave 0's head lists are visible
+        const long long pre_wgs = (long long)a.units * rt.npre * segments;
+        mode = (long long)blockIdx.x < pre_wgs ? 1 : 2;
+        const int pw = a.units * rt.nwarm;  // warm pairs
+        if (mode == 2 && w == 0) {
+            const double nwg = (double)pw * segments;
+            // lane l: warm pairs 4l .. 4l+3 (pw < 256)
+            double L[4], Wt[4], sum = 0.0;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) sc[v] = 0.f;
+            for (int i = 0; i < 4; ++i) {
+                const int j = 4 * lane0 + i;
+                L[i] = 0.0;
+                Wt[i] = 0.0;
+                if (j < pw) {
+                    const int h = heads_warm[j % rt.nwarm];
+                    L[i] = (double)lens.len(j / rt.nwarm);
+                    Wt[i] = (double)warm_len(a.slopes[h] * LOG2E);
+                }
+                sum += L[i];
+            }
+            for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+            const double t0 = sum / nwg;  // warm tokens per workgroup
+            double c[4], run = 0.0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const double wl = Wt[i] < L[i] ? Wt[i] : L[i];
+                c[i] = L[i] > 0.0 ? L[i] + warm_cost<OutT, NG>() * wl * (L[i] / t0) : 0.0;
+                run += c[i];
+            }
+            double incl = run;  // inclusive scan of the lanes' sums
+            for (int o = 1; o < 64; o <<= 1) {
+                const double y = __shfl_up(incl, o);
+                if (lane0 >= o) incl += y;
+            }
+            double acc = incl - run;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int j = 4 * lane0 + i;
+                if (j < pw) cpre[j] = acc;
+                acc += c[i];
+            }
+            if (lane0 == 63) cpre[pw] = incl;
+        }
+        __syncthreads();  // cpre is visible
+        if (t0id == 0) {
+            ps.npre = rt.npre;
+            ps.nwarm = rt.nwarm;
+            ps.pw = pw;
+            if (mode == 2) {
+                const int rl = (int)((long long)blockIdx.x - pre_wgs);
+                ps.rl = rl;
+                ps.T = cpre[pw] / ((double)pw * segments);
+                ps.last = rl + 1 == pw * segments;
+                // the first warm pair this range reaches: the first j with cpre[j + 1] > rl T
+                const double c0 = (double)rl * ps.T;
+                int lo = 0, hi = pw;
+                while (lo < hi) {
+                    const int mid = (lo + hi) / 2;
+                    if (cpre[mid + 1] > c0) hi = mid; else lo = mid + 1;
+                }
+                ps.next = lo;
+                // no flag until a range ends inside a pair
+                int *flag = warm_flag(ws, sp, heads_warm, rt.nwarm, a.heads, rl);
+                flag[0] = 0;
+                flag[1] = 0;
+            }
+        }
+    }
+
+    // ---- the pieces
+    f32x16 S[2];
+    for (int k = 0;; ++k) {
+        // The thread index is made opaque once per piece, so that the compiler
+        // computes the lane-dependent addresses (the swizzled LDS operand
+        // offsets, the state elements' offsets) in each piece instead of once
+        // before this loop, where they would stay in registers through every
+        // piece's warm-up and set-up as well and spill.
+        const int tid = opaque((int)threadIdx.x), lane = tid & 63;
+        const int qh = w >> 2, cq = w & 3, r32 = lane & 31, hf = lane >> 5;
+        auto sbase = [&]() { return (64 * qh + 4 * hf) * D + 32 * cq + r32; };
+        auto sidx = [&](int base, int db, int v) { return base + (32 * db + 8 * (v >> 2) + (v & 3)) * D; };
+        __syncthreads();  // the previous piece is done with the tiles, S^T and pc
+        if (tid == 0)
+            pc = next_piece<OutT>(*reinterpret_cast<const PrefillArgs *>(args_lds),
+                                  *reinterpret_cast<const Segmented *>(sp_lds), ws_lds, mode, k, ps, heads_pre,
+                                  heads_warm, cpre, by_rank);
+        __syncthreads();
+        const int uh = __builtin_amdgcn_readfirstlane(pc.uh);
+        if (uh < 0) break;
+        const int ts = __builtin_amdgcn_readfirstlane(pc.ts);
+        const float s2 = uniformf(pc.s2);
+        const float *s_in = uniform_ptr(pc.s_in);
+        const bool s_in_t = __builtin_amdgcn_readfirstlane(pc.s_in_t) != 0;
+        // carried-in state
+        if (s_in && s_in_t) {
+            // S_0 given transposed: element (r, c) at c * D + r
+            const int tb = (32 * cq + r32) * D + 64 * qh + 4 * hf;
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) S[db][v] = s_in[tb + 32 * db + 8 * (v >> 2) + (v & 3)];
+        } else if (s_in) {
+            const int sb = sbase();
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) S[db][v] = s_in[sidx(sb, db, v)];
+        } else {
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) S[db][v] = 0.f;
+        }
+
+        // warm-up: state-only steps over [t0w, t0) (whole sub-blocks)
+        const long long warm = uniform64(pc.warm);
+        const uint16_t *kw = uniform_ptr(pc.k), *vw = uniform_ptr(pc.v);
+        if (warm > 0) {
+            const long long nw = warm / C;
+            const float bdw = fast_exp2(-s2 * (float)C);
+            Stage<false> w0, w1;
+            auto wpre = [&](Stage<false> &st, long long c) {
+                const long long off = (c < nw ? c : nw - 1) * C * (long long)ts;
+                st.load(nullptr, kw + off, vw + off, ts, C, tid);
+            };
+            auto wstep = [&](long long c, Stage<false> &st) {
+                __builtin_amdgcn_sched_barrier(0);
+                __syncthreads();
+                st.template store<true>(nullptr, Ks, nullptr, Vds, C, s2, tid);
+                wpre(st, c + 2);
+                __syncthreads();
+                state_update(S, Ks, Vds, bdw, qh, cq, lane);
+            };
+            wpre(w0, 0);
+            wpre(w1, 1);
+            long long c = 0;
+            for (; c + 1 < nw; c += 2) {
+                wstep(c, w0);
+                wstep(c + 1, w1);
+            }
+            if (c < nw) wstep(c, w0);
+            __syncthreads();  // the last warm-up reads of Ks, Vds are done
+        }
+        write_state_t(Sts[0], S, qh, cq, lane);
+
+        const long long len = uniform64(pc.len);
+        const uint16_t *qg = uniform_ptr(pc.q);
+        const uint16_t *kg = kw + warm * ts, *vg = vw + warm * ts;
+        OutT *og = static_cast<OutT *>(uniform_ptr(pc.o));
+        // epilogue: gate rows of this piece and the head's normalisation
+        // weights, kept in LDS (read after the first barrier B)
+        const uint16_t *gg = NG ? uniform_ptr(pc.gate) : nullptr;
+        const float eps = NG ? uniformf(pc.eps) : 0.f;
+        if (NG && tid < D / 4)
+            *reinterpret_cast<float4 *>(Wn + 4 * tid) = *reinterpret_cast<const float4 *>(uniform_ptr(pc.nw) + 4 * tid);
+
+        // loop-invariant decay factors
+        const int qpos = 32 * qh + r32;                       // query row of this lane's outputs
+        const float dq = fast_exp2(-s2 * (float)(qpos + 1));  // d_q for that row
+        const bool scorer = w < 3;                            // waves 0..2 own one score block each
+        const int qb = w == 0 ? 0 : 1, kb = w == 2 ? 1 : 0;   // (query block, key block)
+        float dscore[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int diff = (32 * qb + r32) - (32 * kb + 8 * (v >> 2) + 4 * hf + (v & 3));
+            dscore[v] = masked_decay(diff, s2);
+        }
+
+        // Two register stages: sub-block c is staged in st[c % 2] and its loads
+        // are issued two sub-blocks ahead, so about 96 KiB of loads are in flight
+        // per CU.
+        Stage<true> st0, st1;
+        const long long nfull = len / C;
+        const int tail = (int)(len - nfull * C);
+        const long long nchunks = nfull + (tail > 0);
+        auto chunk_len = [&](long long c) { return c < nfull ? C : tail; };
+        auto prefetch = [&](Stage<true> &st, long long c) {
+            // past the end, re-read the last sub-block (ignored) to keep the count fixed
+            const long long cn = c < nchunks ? c : nchunks - 1;
+            const long long off = cn * C * (long long)ts;
+            st.load(qg + off, kg + off, vg + off, ts, chunk_len(cn), tid);
+        };
+        if (nchunks > 0) {
+            prefetch(st0, 0);
+            prefetch(st1, 1);
+        }
+
+        int cur = 0;
+        // Per sub-block: (B) tiles visible -> scores, inter-block product, state
+        // update -> (C) P visible -> intra-block product, output block to LDS ->
+        // (D) output tile visible and every read of this sub-block's tiles done
+        // -> full-row output stores. Barrier D of one sub-block also guards the
+        // tile writes of the next. The output tile reuses the S^T buffer that
+        // the inter-block product just finished reading (it is rewritten only
+        // after the next barrier B).
+        auto step = [&](long long c, int m, auto full, Stage<true> &st) {
+            constexpr bool FULL = decltype(full)::value;
+            // gate rows of this sub-block, consumed by the epilogue at its end.
+            // They are issued ahead of the prefetch two sub-blocks out: loads
+            // complete in order, so the epilogue's wait for them then leaves
+            // that prefetch in flight (issued after it, the wait drained it:
+            // 0.63 -> 0.61 ms per norm-gate call on the M1 layer)
+            uint2 gr[4];
+            if constexpr (NG) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int row = (tid >> 5) + 16 * j;
+                    const int rr = FULL || row < m ? row : m - 1;
+                    gr[j] = stream_load8(gg + (c * C + rr) * (long long)ts + 4 * (tid & 31));
+                }
+            }
+            st.template store<FULL>(Qs, Ks, Vs, Vds, m, s2, tid);
+            if (FULL) prefetch(st, c + 2);
+            __syncthreads();  // (B) tiles and S^T of the previous sub-block are visible
+            if (scorer) {
+                // scores^T block: keys 32kb.., queries 32qb.. ; masked, decayed, to LDS as P
+                f32x16 sc;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) sc[v] = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks)
+                    sc = mma(ld_op<L128>(Ks, 32 * kb, 16 * ks, lane), ld_op<L128>(Qs, 32 * qb, 16 * ks, lane), sc);
+#pragma unroll
+                for (int gv = 0; gv < 4; ++gv) {
+                    bf16x4 p;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) p[r] = static_cast<__bf16>(mask_mul(sc[4 * gv + r], dscore[4 * gv + r]));
+                    *reinterpret_cast<bf16x4 *>(Ps + LP::off(32 * qb + r32, 32 * kb + 8 * gv + 4 * hf)) = p;
+                }
+            }
+
+            // inter-block part: O^T = S^T (Q ⊙ d_q)^T
+            f32x16 o;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[v] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks)
-                sc = mma(ld_op<L128>(Ks, 32 * kb, 16 * ks, lane), ld_op<L128>(Qs, 32 * qb, 16 * ks, lane), sc);
+                o = mma(ld_op<L128>(Sts[cur], 32 * cq, 16 * ks, lane), ld_op<L128>(Qs, 32 * qh, 16 * ks, lane), o);
+            o *= dq;
+
+            // state: S = e^{-s m} S + K^T (V ⊙ d_k), then S^T (bf16) for the next sub-block
+            state_update(S, Ks, Vds, fast_exp2(-s2 * (float)m), qh, cq, lane);
+            write_state_t(Sts[cur ^ 1], S, qh, cq, lane);
+            __syncthreads();  // (C) P is visible
+
+            // intra-block part: O^T += V^T P^T over the causal key range
 #pragma unroll
-            for (int gv = 0; gv < 4; ++gv) {
-                bf16x4 p;
+            for (int ks = 0; ks < C / 16; ++ks) {
+                if (ks >= 2 * (qh + 1)) break;
+                o = mma(ld_op_t<L128>(Vs, 32 * cq, 16 * ks, lane), ld_op<LP>(Ps, 32 * qh, 16 * ks, lane), o);
+            }
+            float *Os = reinterpret_cast<float *>(Sts[cur]);
+            stage_out(Os, o, qh, cq, lane);
+            if constexpr (NG) row_sumsq(Rss, o, qh, cq, lane);
+            __syncthreads();  // (D)
+            if constexpr (NG)
+                store_rows_norm_gate<FULL>(og + c * C * (long long)ts, ts, Os, Rss, m, tid, gr,
+                                           *reinterpret_cast<const float4 *>(Wn + 4 * (tid & 31)), eps);
+            else
+                store_rows<FULL>(og + c * C * (long long)ts, ts, Os, m, tid);
+            cur ^= 1;
+        };
+        long long c = 0;
+        for (; c + 1 < nfull; c += 2) {
+            step(c, C, std::true_type{}, st0);
+            step(c + 1, C, std::true_type{}, st1);
+        }
+        if (c < nfull) step(c, C, std::true_type{}, st0);
+        if (tail > 0) {  // sub-block nfull is staged in st[nfull % 2]
+            if (nfull & 1)
+                step(nfull, tail, std::false_type{}, st1);
+            else
+                step(nfull, tail, std::false_type{}, st0);
+        }
+
+        // the end state (pc is unchanged until the next piece)
+        const int end = __builtin_amdgcn_readfirstlane(pc.end);
+        bool keep = end == 1;
+        if (end == 2) {  // a warm range ending inside its pair: kept and flagged only if non-finite
+            bool bad = false;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) p[r] = static_cast<__bf16>(mask_mul(sc[4 * gv + r], dscore[4 * gv + r]));
-                *reinterpret_cast<bf16x4 *>(Ps + LP::off(32 * qb + r32, 32 * kb + 8 * gv + 4 * hf)) = p;
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) bad |= nonfinite(S[db][v]);
+            if (tid == 0) any_bad = 0;
+            __syncthreads();
+            if (__ballot(bad) != 0 && lane == 0) atomicOr(&any_bad, 1);
+            __syncthreads();
+            keep = any_bad != 0;
+        }
+        if (keep) {
+            float *dst = uniform_ptr(pc.dst);
+            const int sb = sbase();
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) dst[sidx(sb, db, v)] = S[db][v];
+            if (end == 2 && tid == 0) {  // after the state, so that it is not held through the flag's writes
+                int *flag = pc.flag;
+                flag[0] = uh + 1;
+                flag[1] = pc.cut;
             }
         }
-
-        // inter-block part: O^T = S^T (Q ⊙ d_q)^T
-        f32x16 o;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[v] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-            o = mma(ld_op<L128>(Sts[cur], 32 * cq, 16 * ks, lane), ld_op<L128>(Qs, 32 * qh, 16 * ks, lane), o);
-        o *= dq;
-
-        // state: S = e^{-s m} S + K^T (V ⊙ d_k), then S^T (bf16) for the next sub-block
-        state_update(S, Ks, Vds, fast_exp2(-s2 * (float)m), qh, cq, lane);
-        write_state_t(Sts[cur ^ 1], S, qh, cq, lane);
-        __syncthreads();  // (C) P is visible
-
-        // intra-block part: O^T += V^T P^T over the causal key range
-#pragma unroll
-        for (int ks = 0; ks < C / 16; ++ks) {
-            if (ks >= 2 * (qh + 1)) break;
-            o = mma(ld_op_t<L128>(Vs, 32 * cq, 16 * ks, lane), ld_op<LP>(Ps, 32 * qh, 16 * ks, lane), o);
-        }
-        float *Os = reinterpret_cast<float *>(Sts[cur]);
-        stage_out(Os, o, qh, cq, lane);
-        if constexpr (NG) row_sumsq(Rss, o, qh, cq, lane);
-        __syncthreads();  // (D)
-        if constexpr (NG)
-            store_rows_norm_gate<FULL>(og + c * C * (long long)ts, ts, Os, Rss, m, tid, gr,
-                                       *reinterpret_cast<const float4 *>(Wn + 4 * (tid & 31)), a.ng.eps,
-                                       c * C < raw_rows);
-        else
-            store_rows<FULL>(og + c * C * (long long)ts, ts, Os, m, tid);
-        cur ^= 1;
-    };
-    long long c = 0;
-    for (; c + 1 < nfull; c += 2) {
-        step(c, C, std::true_type{}, st0);
-        step(c + 1, C, std::true_type{}, st1);
-    }
-    if (c < nfull) step(c, C, std::true_type{}, st0);
-    if (tail > 0) {  // sub-block nfull is staged in st[nfull % 2]
-        if (nfull & 1)
-            step(nfull, tail, std::false_type{}, st1);
-        else
-            step(nfull, tail, std::false_type{}, st0);
-    }
-
-    if (fix) {  // end state of this local-start segment, for the correction pass
-        float *u = sp.unit(ws, uh);
-        float *dst = sp.start_state(u, g);
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) dst[sidx(db, v)] = S[db][v];
-        if (g + 1 < segments) flag_end_state(end_flags(sp, u, g), S, w, lane);
-    } else if (a.state_out && g == gused - 1) {
-        const long long sb = (long long)uh * D * D;
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) a.state_out[sb + sidx(db, v)] = S[db][v];
     }
 }
 
@@ -657,340 +997,120 @@ __global__ __launch_bounds__(NT) void slice_kernel(PrefillArgs a) {
     }
 }
 
-// o[t] += e^{-s(t+1)} q[t] S_in(g) for the first fix_len tokens t of segment g
-// (g >= 1), in 64-token chunks. The chunks of all (unit, head, segment) pairs
-// are numbered in pair order and cut into equal contiguous ranges, one per
-// workgroup (the pairs' chunk counts differ with the decay by up to two orders
-// of magnitude); consecutive ranges go to workgroups on one XCD, so the few
-// workgroups that share a pair read its end states through one L2. A workgroup
-// forms S_in(g) from the end states E_0..E_{g-1} the main pass left
-// (S_in(1) = E_0, S_in(j+1) = e^{-s len_j} S_in(j) + E_j) and loads the next
-// chunk's q and o rows before the current chunk's product, which is the main
-// kernel's inter-block one (S^T in bf16 on MFMA, Q from an LDS tile). The first
-// `nfinal` workgroups instead write the final state of each local-start head,
-// e^{-s len_{G-1}} S_in(G-1) + E_{G-1}, kFinalSlices workgroups per head.
-constexpr int kFixWorkgroups = 512;                // two per CU; a multiple of 8 (XCDs)
+// ---------------------------------------------------------------------------
+// Finishing pass of the warm-up route: one workgroup per (unit, head) pair;
+// pairs on the pre-pass route exit at once. A range that ends inside its pair
+// built its carried-in state from a finite window of tokens, so it cannot see
+// a NaN or Inf from before that window, which the exact operator carries
+// forward: it stays in the state entries it reached, and every later output
+// column of those entries is non-finite. Each such range flagged its
+// non-finite end state E (cut c) in its home slots; this pass puts NaN in rows
+// [c, len) of the pair in every column where E has one (whole rows with the
+// norm-gate epilogue, whose normalisation spreads it over the row) and in each
+// final-state entry where some E has one. It also writes the final state of
+// empty sequences (S_0, or zero) and, for in-place calls (state_out ==
+// state_in), copies the final state that the main pass left in the workspace:
+// writing it there directly could race with the reads of S_0 by the pair's
+// other ranges.
+__device__ __forceinline__ void poison(float *p) { *p = __builtin_nanf(""); }
+__device__ __forceinline__ void poison(__bf16 *p) { *reinterpret_cast<uint16_t *>(p) = 0x7fc0; }
 
-
-// The rows of o a thread adds to (loaded before the product, so their latency
-// overlaps it): fp32 rows (t/32) + 16j, 4 columns at 4(t%32); bf16 rows
-// (t/16) + 32j, 8 columns at 8(t%16). Rows >= m read row m-1 and are not stored.
-// Offsets from the chunk's first row fit in 32 bits (64 rows). Sized by the
-// output type, so that a copy moves only loaded registers.
-template <typename OutT>
-struct OutRows;
-template <>
-struct OutRows<float> {
-    uint4 y[4];
-    __device__ void load(const float *out, int ts, int m, int tid) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = (tid >> 5) + 16 * j;
-            y[j] = *reinterpret_cast<const uint4 *>(out + (unsigned)((row < m ? row : m - 1) * ts + 4 * (tid & 31)));
-        }
-    }
-    __device__ void add_store(float *out, int ts, const float *Os, int m, int tid) const {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = (tid >> 5) + 16 * j, col = 4 * (tid & 31);
-            const float4 x = *reinterpret_cast<const float4 *>(Os + ooff(row, col));
-            if (row < m)
-                *reinterpret_cast<float4 *>(out + (unsigned)(row * ts + col)) =
-                    make_float4(__uint_as_float(y[j].x) + x.x, __uint_as_float(y[j].y) + x.y,
-                                __uint_as_float(y[j].z) + x.z, __uint_as_float(y[j].w) + x.w);
-        }
-    }
-};
-template <>
-struct OutRows<__bf16> {
-    uint4 y[2];
-    __device__ void load(const __bf16 *out, int ts, int m, int tid) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int row = (tid >> 4) + 32 * j;
-            y[j] = *reinterpret_cast<const uint4 *>(out + (unsigned)((row < m ? row : m - 1) * ts + 8 * (tid & 15)));
-        }
-    }
-    __device__ void add_store(__bf16 *out, int ts, const float *Os, int m, int tid) const {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int row = (tid >> 4) + 32 * j, col = 8 * (tid & 15);
-            const float4 x0 = *reinterpret_cast<const float4 *>(Os + ooff(row, col));
-            const float4 x1 = *reinterpret_cast<const float4 *>(Os + ooff(row, col + 4));
-            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-            const uint32_t w[4] = {y[j].x, y[j].y, y[j].z, y[j].w};
-            uint32_t r[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const __bf16 lo = static_cast<__bf16>(__uint_as_float(w[i] << 16) + xs[2 * i]);
-                const __bf16 hi = static_cast<__bf16>(__uint_as_float(w[i] & 0xffff0000u) + xs[2 * i + 1]);
-                uint16_t ulo, uhi;
-                __builtin_memcpy(&ulo, &lo, 2);
-                __builtin_memcpy(&uhi, &hi, 2);
-                r[i] = (uint32_t)ulo | ((uint32_t)uhi << 16);
-            }
-            if (row < m) *reinterpret_cast<uint4 *>(out + row * ts + col) = make_uint4(r[0], r[1], r[2], r[3]);
-        }
-    }
-};
-
-// One chunk of the correction: rows [t0, t0 + m) of segment g of pair `pair`.
-template <typename OutT>
-struct FixChunk {
-    const uint16_t *q, *gate;
-    OutT *o;
-    long long t0;
-    int m, pair, uh, g, h;
-    float s2;
-};
-
-// Rows a correction pass treats in segment g of a local-start head (the chunk
-// count and the chunk contents must agree on it).
-template <bool NG>
-__device__ __forceinline__ long long fix_rows(float s2, long long seg_len, long long len) {
-    if constexpr (NG) {
-        return ng_fix_rows(s2, seg_len, len);
-    } else {
-        const long long fl = fix_len(s2, seg_len);
-        return fl < len ? fl : len;
-    }
-}
+// float4 elements of a d x d state per thread of a workgroup
+constexpr int kStateF4 = D * D / (4 * NT);
+static_assert(kStateF4 * 4 * NT == D * D && 4 * kStateF4 <= 64, "state elements per thread");
 
 template <typename OutT, bool NG>
-__device__ __forceinline__ FixChunk<OutT> fix_chunk(const PrefillArgs &a, const Segmented &sp,
-                                                    const long long *first, const long long *prows,
-                                                    long long j, int &p) {
-    while (first[p + 1] <= j) ++p;
-    p = __builtin_amdgcn_readfirstlane(p);  // the same for every lane
-    FixChunk<OutT> x;
-    const int gs = sp.segments - 1;
-    x.pair = p;
-    x.uh = p / gs;
-    x.g = 1 + p % gs;
-    const int h = x.uh % a.heads, n = x.uh / a.heads;
-    x.h = h;
-    x.s2 = a.slopes[h] * LOG2E;
-    const long long T = uniform64(prows[p]);
-    x.t0 = uniform64((j - first[p]) * C);
-    x.m = (int)(T - x.t0 < C ? T - x.t0 : C);
-    const long long row = uniform64(sequence_of(a, n).start) + (long long)x.g * sp.seg_len + x.t0;
-    const long long off = (row * a.heads + h) * (long long)D;
-    x.q = static_cast<const uint16_t *>(a.q) + off;
-    x.gate = NG ? static_cast<const uint16_t *>(a.ng.gate) + off : nullptr;
-    x.o = static_cast<OutT *>(a.o) + off;
-    return x;
-}
-
-// Norm-gate correction rows: the raw output the main pass left in y, and the
-// gate, for rows (tid/32) + 16j, columns 4(tid%32)..+3 (the epilogue's layout).
-// finish() adds the staged correction, normalises each row (its 32 lanes
-// reduce the sum of squares), gates, and stores y.
-template <typename OutT>
-struct NgRows {
-    using Raw = typename std::conditional<sizeof(OutT) == 4, uint4, uint2>::type;
-    Raw y[4];
-    uint2 gt[4];
-    __device__ void load(const OutT *out, const uint16_t *gate, int ts, int m, int tid) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = (tid >> 5) + 16 * j;
-            const unsigned off = (unsigned)((row < m ? row : m - 1) * ts + 4 * (tid & 31));
-            y[j] = *reinterpret_cast<const Raw *>(out + off);
-            gt[j] = stream_load8(gate + off);
-        }
-    }
-    __device__ static float4 raw4(const uint4 &x) {
-        return make_float4(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w));
-    }
-    __device__ static float4 raw4(const uint2 &x) {
-        return make_float4(__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u),
-                           __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u));
-    }
-    __device__ void finish(OutT *out, int ts, const float *Os, int m, int tid, float4 w, float eps) const {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = (tid >> 5) + 16 * j, col = 4 * (tid & 31);
-            const float4 x = *reinterpret_cast<const float4 *>(Os + ooff(row, col));
-            const float4 r = raw4(y[j]);
-            const float4 o = make_float4(r.x + x.x, r.y + x.y, r.z + x.z, r.w + x.w);
-            float ss = o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
-#pragma unroll
-            for (int k = 16; k >= 1; k >>= 1) ss += __shfl_xor(ss, k);
-            const float inv = __builtin_amdgcn_rsqf(ss * (1.f / D) + eps);
-            const float g0 = __uint_as_float(gt[j].x << 16), g1 = __uint_as_float(gt[j].x & 0xffff0000u);
-            const float g2 = __uint_as_float(gt[j].y << 16), g3 = __uint_as_float(gt[j].y & 0xffff0000u);
-            const float4 yv = make_float4(o.x * inv * w.x * sigmoid(g0), o.y * inv * w.y * sigmoid(g1),
-                                          o.z * inv * w.z * sigmoid(g2), o.w * inv * w.w * sigmoid(g3));
-            if (row < m) put4(out + (unsigned)(row * ts + col), yv);
-        }
-    }
-};
-
-// Two workgroups per CU: 128 registers per lane, and the Q tile shares its
-// LDS with the staged output (66 KB per workgroup).
-template <typename OutT, bool NG>
-__global__ __launch_bounds__(NT, 4) void fix_kernel(PrefillArgs a, Segmented sp, float *ws, int nfinal) {
-    __shared__ __attribute__((aligned(16))) __bf16 Sts[D * D];
-    __shared__ __attribute__((aligned(16))) float Os[C * D];
-    __shared__ long long first[kFixMaxPairs + 1];  // first chunk number of each pair
-    __shared__ long long prows[kFixMaxPairs];       // rows corrected in each pair
-    __bf16 *const Qs = reinterpret_cast<__bf16 *>(Os);
-
+__global__ __launch_bounds__(NT) void finish_kernel(PrefillArgs a, Segmented sp, float *ws) {
+    __shared__ short heads_pre[kMaxPairs], heads_warm[kMaxPairs];
+    __shared__ int flagged[kMaxWarmWgs], cutv[kMaxWarmWgs], order[kMaxWarmWgs];
+    __shared__ int nflag;
+    __shared__ unsigned colbad[D / 32];
     const int tid = threadIdx.x;
-    if ((int)blockIdx.x < nfinal) {  // final state of a local-start head
-        const int uh = blockIdx.x / kFinalSlices;
-        const float s2 = a.slopes[uh % a.heads] * LOG2E;
-        if (!fix_head(s2, sp.seg_len, sp.fix_osz)) return;
-        const int e = 4 * ((blockIdx.x % kFinalSlices) * NT + tid);
-        float *u = sp.unit(ws, uh);
-        const long long len = sequence_of(a, uh / a.heads).len;
-        float4 acc = *reinterpret_cast<const float4 *>(sp.start_state(u, 0) + e);
-        for (int g = 1; g < sp.used(len); ++g) {
-            const float f = fast_exp2(-s2 * (float)seg_len_at(sp, len, g));
-            const float4 x = *reinterpret_cast<const float4 *>(sp.start_state(u, g) + e);
-            acc = make_float4(f * acc.x + x.x, f * acc.y + x.y, f * acc.z + x.z, f * acc.w + x.w);
-        }
-        *reinterpret_cast<float4 *>(a.state_out + (size_t)uh * D * D + e) = acc;
+    const int uh = blockIdx.x, h = uh % a.heads, n = uh / a.heads;
+    if (takes_prepass(sp, a.slopes[h] * LOG2E)) return;
+    const Routes rt = split_heads(a.slopes, a.heads, sp, heads_pre, heads_warm, tid < 64);
+    if (tid == 0) nflag = 0;
+    if (tid < D / 32) colbad[tid] = 0;
+    __syncthreads();
+    const long long len = SeqLens{a.cu_seqlens, a.total_tokens, a.seqlen}.len(n);
+    const size_t sb = (size_t)uh * D * D;
+    if (len == 0) {  // no range covers the pair: the final state is S_0
+        if (a.state_out && a.state_out != a.state_in)
+            for (int i = tid; i < D * D; i += NT) {
+                float x = 0.f;
+                if (a.state_in) x = a.state_in_t ? a.state_in[sb + (i % D) * D + i / D] : a.state_in[sb + i];
+                a.state_out[sb + i] = x;
+            }
         return;
     }
-
-    // rows and chunks per pair (none unless the head takes local starts; the
-    // whole segment when its carried-in state is non-finite), then the chunks'
-    // prefix sums (inclusive scan over the first kFixMaxPairs threads)
-    const int gs = sp.segments - 1;
-    const int pairs = a.units * a.heads * gs;
-    long long x = 0;
-    if (tid < pairs) {
-        const int g = 1 + tid % gs, uh = tid / gs;
-        const float s2 = a.slopes[uh % a.heads] * LOG2E;
-        long long rows = 0;
-        const long long len = seg_len_at(sp, sequence_of(a, uh / a.heads).len, g);
-        if (len > 0 && fix_head(s2, sp.seg_len, sp.fix_osz))
-            rows = start_poisoned(sp, sp.unit(ws, uh), g) ? len : fix_rows<NG>(s2, sp.seg_len, len);
-        prows[tid] = rows;
-        x = (rows + C - 1) / C;
+    const int nwg = a.units * rt.nwarm * sp.segments;
+    for (int r = tid; r < nwg; r += NT) {
+        const int *f = warm_flag(ws, sp, heads_warm, rt.nwarm, a.heads, r);
+        if (f[0] == uh + 1) {
+            const int i = atomicAdd(&nflag, 1);
+            flagged[i] = r;
+            cutv[i] = f[1];
+        }
     }
-    for (int off = 1; off < kFixMaxPairs; off <<= 1) {
-        if (tid < kFixMaxPairs) first[tid + 1] = x;
-        __syncthreads();
-        if (tid < kFixMaxPairs && tid >= off) x += first[tid + 1 - off];
-        __syncthreads();
-    }
-    if (tid < kFixMaxPairs) first[tid + 1] = x;
-    if (tid == 0) first[0] = 0;
     __syncthreads();
-
-    // this workgroup's range: workgroups on one XCD (blockIdx % 8; nfinal and
-    // the grid's remainder are multiples of 8) take consecutive ranges
-    const long long total = uniform64(first[pairs]);
-    const int nwg = gridDim.x - nfinal;
-    const int r = (int)(blockIdx.x % 8) * (nwg / 8) + (int)(blockIdx.x - nfinal) / 8;
-    const long long j0 = total * r / nwg, j1 = total * (r + 1) / nwg;
-    if (j0 >= j1) return;
-
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int qh = w >> 2, cq = w & 3;
-    const int ts = a.heads * D;  // 32-bit row offsets within a chunk (64 rows)
-    auto load_q = [&](const FixChunk<OutT> &c, uint4 (&qx)[2], int th) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int t = (th >> 4) + 32 * i;
-            qx[i] = stream_load16(c.q + (unsigned)((t < c.m ? t : c.m - 1) * ts + 8 * (th & 15)));
+    const int cnt = nflag;
+    // this thread's state elements: float4 tid + NT j (j < kStateF4), all in
+    // columns 4 (tid % 32) .. + 3 (NT j float4 are a whole number of rows)
+    unsigned long long bad = 0;
+    if (cnt > 0) {
+        for (int i = tid; i < cnt; i += NT) {  // order the flagged ranges by cut
+            int rank = 0;
+            for (int j = 0; j < cnt; ++j) rank += cutv[j] < cutv[i] || (cutv[j] == cutv[i] && j < i);
+            order[rank] = i;
         }
-    };
-    using Rows = typename std::conditional<NG, NgRows<OutT>, OutRows<OutT>>::type;
-    auto load_rows = [&](Rows &r, const FixChunk<OutT> &c, int th) {
-        if constexpr (NG)
-            r.load(c.o, c.gate, ts, c.m, th);
-        else
-            r.load(c.o, ts, c.m, th);
-    };
-    int p = 0;
-    FixChunk<OutT> cur = fix_chunk<OutT, NG>(a, sp, first, prows, j0, p);
-    uint4 qa[2];
-    Rows ra;
-    load_q(cur, qa, tid);
-    load_rows(ra, cur, tid);
-    int loaded = -1;
-    for (long long j = j0; j < j1; ++j) {
-        if (j > j0) __syncthreads();  // the previous chunk's reads of Os (= Qs) done
-        // Lane-dependent offsets are recomputed from an opaque copy of the
-        // thread index every chunk: hoisted out of the loop they would be
-        // spilled, and a spill reload waits for every load in flight,
-        // including the next chunk's.
-        int tl = tid;
-        asm volatile("" : "+v"(tl));
-        const int ln = tl & 63;
-        // the next chunk's loads go out before anything waits for this one's
-        FixChunk<OutT> nxt = cur;
-        uint4 qb[2] = {qa[0], qa[1]};
-        Rows rb = ra;
-        if (j + 1 < j1) {
-            nxt = fix_chunk<OutT, NG>(a, sp, first, prows, j + 1, p);
-            load_q(nxt, qb, tl);
-            load_rows(rb, nxt, tl);
-        }
-        if (cur.pair != loaded) {
-            // S_in(g) of this pair as bf16 S^T: the thread with value column
-            // c and key quad kq forms S_in[4(kq + 4i) + r + 64 half][c], i < 4,
-            // r < 4, half < 2 (the previous chunk's reads of Sts ended before
-            // its second barrier)
-            const int c = tl & (D - 1), kq = tl >> 7;
-            float *u = sp.unit(ws, cur.uh);
+        __syncthreads();
+        const SeqRange sr = sequence_of(a, n);
+        OutT *o = static_cast<OutT *>(a.o);
+        const int col = 4 * (tid & 31);
+        for (int k = 0; k < cnt; ++k) {
+            const int i = order[k];
+            const float4 *e = reinterpret_cast<const float4 *>(warm_end_state(ws, sp, heads_warm, rt.nwarm,
+                                                                              a.heads, flagged[i]));
+            unsigned cb = 0;
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {  // 16 elements at a time (registers)
-                float acc[4][4];
-                {
-                    const float *e = sp.start_state(u, 0) + (4 * kq + 64 * half) * D + c;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) acc[i][r] = e[(16 * i + r) * D];
-                }
-                for (int g = 1; g < cur.g; ++g) {  // segments before cur.g are whole
-                    const float f = fast_exp2(-cur.s2 * (float)sp.seg_len);
-                    const float *e = sp.start_state(u, g) + (4 * kq + 64 * half) * D + c;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) acc[i][r] = f * acc[i][r] + e[(16 * i + r) * D];
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    bf16x4 x;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) x[r] = static_cast<__bf16>(acc[i][r]);
-                    *reinterpret_cast<bf16x4 *>(Sts + L128::off(c, 4 * (kq + 4 * i) + 64 * half)) = x;
-                }
+            for (int j = 0; j < kStateF4; ++j) {
+                const float4 x = e[tid + NT * j];
+                const unsigned b = (unsigned)nonfinite(x.x) | (unsigned)nonfinite(x.y) << 1 |
+                                   (unsigned)nonfinite(x.z) << 2 | (unsigned)nonfinite(x.w) << 3;
+                bad |= (unsigned long long)b << (4 * j);
+                cb |= b;
             }
-            loaded = cur.pair;
+            if (cb) atomicOr(&colbad[(tid & 31) >> 3], cb << (4 * (tid & 7)));
+            __syncthreads();
+            // rows [c0, c1): NaN in every column flagged so far (32 threads per row,
+            // NT / 32 rows at a time)
+            const long long c0 = cutv[i], c1 = k + 1 < cnt ? cutv[order[k + 1]] : len;
+            const unsigned m4 = NG ? 0xfu : (colbad[col >> 5] >> (col & 31)) & 0xfu;
+            if (m4)
+                for (long long t = c0 + (tid >> 5); t < c1; t += NT / 32) {
+                    OutT *row = o + ((sr.start + t) * a.heads + h) * (long long)D + col;
+#pragma unroll
+                    for (int x = 0; x < 4; ++x)
+                        if (m4 >> x & 1) poison(row + x);
+                }
+            __syncthreads();  // every read of colbad for these rows is done
         }
-        // this chunk's q rows into the tile (rows past m zeroed)
+    }
+    const bool in_place = a.state_in && a.state_in == a.state_out;
+    if (a.state_out && (in_place || bad)) {
+        const float4 *src = reinterpret_cast<const float4 *>(in_place ? Segmented::slot(sp.unit(ws, uh), sp.segments + 1)
+                                                                      : a.state_out + sb);
+        float4 *dst = reinterpret_cast<float4 *>(a.state_out + sb);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int t = (tl >> 4) + 32 * i;
-            *reinterpret_cast<uint4 *>(Qs + L128::off(t, 8 * (tl & 15))) = keep_if(t < cur.m, qa[i]);
+        for (int j = 0; j < kStateF4; ++j) {
+            float4 x = src[tid + NT * j];
+            const unsigned b = (unsigned)(bad >> (4 * j)) & 0xfu;
+            if (b & 1) x.x = __builtin_nanf("");
+            if (b & 2) x.y = __builtin_nanf("");
+            if (b & 4) x.z = __builtin_nanf("");
+            if (b & 8) x.w = __builtin_nanf("");
+            dst[tid + NT * j] = x;
         }
-        __syncthreads();  // Q tile and S^T visible
-        f32x16 o;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[v] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-            o = mma(ld_op<L128>(Sts, 32 * cq, 16 * ks, ln), ld_op<L128>(Qs, 32 * qh, 16 * ks, ln), o);
-        o *= fast_exp2(-cur.s2 * (float)(cur.t0 + 32 * qh + (ln & 31) + 1));
-        __syncthreads();  // every read of Qs and Sts done
-        stage_out(Os, o, qh, cq, ln);
-        __syncthreads();  // Os visible
-        if constexpr (NG)
-            ra.finish(cur.o, ts, Os, cur.m, tl,
-                      *reinterpret_cast<const float4 *>(a.ng.norm_weight + cur.h * D + 4 * (tl & 31)), a.ng.eps);
-        else
-            ra.add_store(cur.o, ts, Os, cur.m, tl);
-        cur = nxt;
-        qa[0] = qb[0];
-        qa[1] = qb[1];
-        ra = rb;
     }
 }
 
@@ -1005,13 +1125,11 @@ hipError_t launch(const PrefillArgs &a, const PrefillPlan &p, void *workspace, h
         return hipGetLastError();
     }
     float *ws = static_cast<float *>(workspace);
-    // heads may take local-start segments; the correction's extra traffic per
-    // token is, in units of 256 B, 1 + sizeof(OutT): q read and the output row
-    // read and written (with the norm-gate epilogue the gate is read by the
-    // correction pass instead of the main pass)
-    const int fix_osz = p.segments > 1 ? (int)sizeof(OutT) : 0;
-    const Segmented sp{p.segments, p.pieces, p.seg_len, p.piece_len, fix_osz};
+    Segmented sp{p.segments, p.pieces, p.seg_len, p.piece_len};
+    sp.warm = true;
     if (p.segments > 1) {
+        // the kernels' per-plan tables hold every pair and workgroup of a segmented plan
+        if (uh >= kMaxPairs || uh * p.segments > kMaxWarmWgs) return hipErrorInvalidValue;
         hipLaunchKernelGGL(piece_state_kernel, dim3((unsigned)(uh * p.pieces)), dim3(NT), 0, stream,
                            a, sp, ws);
         hipError_t e = hipGetLastError();
@@ -1022,23 +1140,17 @@ hipError_t launch(const PrefillArgs &a, const PrefillPlan &p, void *workspace, h
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    const dim3 grid((unsigned)(uh * p.segments));
     if (a.ng.gate)
-        hipLaunchKernelGGL((head_kernel<OutT, true>), dim3((unsigned)(uh * p.segments)), dim3(NT), 0,
-                           stream, a, sp, ws);
+        hipLaunchKernelGGL((head_kernel<OutT, true>), grid, dim3(NT), 0, stream, a, sp, ws);
     else
-        hipLaunchKernelGGL((head_kernel<OutT, false>), dim3((unsigned)(uh * p.segments)), dim3(NT), 0,
-                           stream, a, sp, ws);
-    if (!fix_osz) return hipGetLastError();
+        hipLaunchKernelGGL((head_kernel<OutT, false>), grid, dim3(NT), 0, stream, a, sp, ws);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (uh * (p.segments - 1) > kFixMaxPairs) return hipErrorInvalidValue;  // not a segmented plan
-    const int nfinal = a.state_out ? (int)(uh * kFinalSlices) : 0;
+    if (e != hipSuccess || p.segments == 1) return e;
     if (a.ng.gate)
-        hipLaunchKernelGGL((fix_kernel<OutT, true>), dim3((unsigned)(nfinal + kFixWorkgroups)), dim3(NT), 0, stream,
-                           a, sp, ws, nfinal);
+        hipLaunchKernelGGL((finish_kernel<OutT, true>), dim3((unsigned)uh), dim3(NT), 0, stream, a, sp, ws);
     else
-        hipLaunchKernelGGL((fix_kernel<OutT, false>), dim3((unsigned)(nfinal + kFixWorkgroups)), dim3(NT), 0, stream,
-                           a, sp, ws, nfinal);
+        hipLaunchKernelGGL((finish_kernel<OutT, false>), dim3((unsigned)uh), dim3(NT), 0, stream, a, sp, ws);
     return hipGetLastError();
 }
 

@@ -302,10 +302,12 @@ __device__ __forceinline__ SeqRange sequence_of(const PrefillArgs &a, int n) {
 //   [B_1 .. B_{segments-1}]     for a boundary inside a piece: the state of that
 //                               piece's tokens before the boundary
 //   [S_0 .. S_{segments-1}]     state at the start of each segment
+// (pairs on the forward's warm-up route use slots 0 .. segments + 1 of theirs
+// instead: end states and flags of warm ranges, and an in-place final state).
 // A state of tokens [t0, t1) from zero is sum_t e^{-s(t1-1-t)} k_t^T v_t, and
 // states compose as S(t2) = e^{-s(t2-t1)} S(t1) + state of [t1, t2).
-// Local-start segments. A segment that starts from a zero state instead of
-// its true start state S_in misses, at its token t (t = 0, 1, ...), the term
+// Local-start segments (the reverse pass of the backward). A segment that
+// starts from a zero state instead of its true start state S_in misses, at its token t (t = 0, 1, ...), the term
 // e^{-s(t+1)} q_t S_in. With s2 = s log2(e) that factor is below 2^-kFixExp once
 // t + 1 > kFixExp / s2: a correction pass adds the term to the first
 // fix_len = min(segment, kFixExp / s2) tokens and leaves the rest: past them
@@ -327,18 +329,24 @@ __device__ __forceinline__ long long fix_len(float s2, long long seg_len) {
     const float t = kFixExp / s2;
     return t >= (float)seg_len ? seg_len : (long long)t;
 }
-// With the norm-gate epilogue the main pass leaves the raw output of a
-// segment's first rows in y (in y's type) and the correction pass finishes them
-// (adds the carried-in term, normalises, gates): fix_len rounded up to whole
-// pairs of 64-token sub-blocks, at most the segment's length.
-__device__ __forceinline__ long long ng_fix_rows(float s2, long long seg_len, long long len) {
-    const long long r = (fix_len(s2, seg_len) + 127) / 128 * 128;
-    return r < len ? r : len;
-}
 __device__ __forceinline__ bool fix_head(float s2, long long seg_len, int osz) {
     if (osz <= 0 || !(s2 > 0.f)) return false;
     const long long n = fix_len(s2, seg_len);
     return n < seg_len && n * (1 + osz) <= 4 * seg_len;
+}
+
+// Warm-up segments (the forward). A range of a sequence that starts at token
+// t0 > 0 computes its carried-in state from the last W tokens before t0 (from a
+// zero state; from S_0 when the sequence starts within them), by state-only
+// steps: the terms older than W tokens are below 2^-kFixExp of their scale, as
+// with the correction above, but no output needs a second pass. W is rounded up
+// to whole 64-token sub-blocks; a head whose W is shorter than a segment takes
+// this route, the others the pre-pass.
+__device__ __forceinline__ long long warm_len(float s2) {
+    if (!(s2 > 0.f)) return 1LL << 62;  // no decay (or NaN): never forgets
+    const float t = kFixExp / s2;
+    if (!(t < 1.0e15f)) return 1LL << 62;
+    return ((long long)t + 64) / 64 * 64;
 }
 
 // Lengths of the sequences of a launch: packed (cu_seqlens, every boundary
@@ -363,7 +371,8 @@ struct SeqLens {
 struct Segmented {
     int segments, pieces;
     long long seg_len, piece_len;
-    int fix_osz = 0;  // output element size when heads may take local-start segments, else 0
+    int fix_osz = 0;    // local-start segments with a correction pass (the backward): output element size
+    bool warm = false;  // warm-up segments (the forward): see warm_len
     __device__ int used(long long len) const {
         const long long g = (len + seg_len - 1) / seg_len;
         return g < 1 ? 1 : (g > segments ? segments : (int)g);
@@ -379,10 +388,10 @@ struct Segmented {
     __device__ float *start_state(float *u, int g) const { return slot(u, pieces + segments - 1 + g); }
 };
 
-// Non-finite carried-in states. The correction's cutoff is sound only for a
-// finite S_in: e^{-s(t+1)} q_t S_in is then below 2^-24 of its scale past
-// fix_len tokens, but a NaN or Inf in S_in reaches every later token of the
-// exact operator. So the main pass flags each local-start segment whose end
+// Non-finite carried-in states (local-start segments). The correction's cutoff
+// is sound only for a finite S_in: e^{-s(t+1)} q_t S_in is then below 2^-24 of
+// its scale past fix_len tokens, but a NaN or Inf in S_in reaches every later
+// token of the exact operator. So the main pass flags each local-start segment whose end
 // state E_g holds a NaN or Inf, and the correction pass treats the whole of
 // segment g as "first tokens" when any of E_0 .. E_{g-1} is flagged (S_in(g)
 // is then non-finite). The flags of E_g (g <= segments - 2) sit in the slot
@@ -427,6 +436,14 @@ __device__ __forceinline__ long long uniform64(long long x) {
     return (long long)(((unsigned long long)hi << 32) | lo);
 }
 
+// Heads whose segments start from states the pre-pass and combine compute; the
+// others take local-start segments (the backward) or warm-up segments (the
+// forward).
+__device__ __forceinline__ bool takes_prepass(const Segmented &sp, float s2) {
+    if (sp.warm) return !(warm_len(s2) < sp.seg_len);
+    return !fix_head(s2, sp.seg_len, sp.fix_osz);
+}
+
 // Tokens of segment g of a sequence of `seqlen` tokens (0 past its end).
 __device__ __forceinline__ long long seg_len_at(const Segmented &sp, long long seqlen, int g) {
     const long long rest = seqlen - (long long)g * sp.seg_len;
@@ -448,7 +465,7 @@ __device__ inline int prepass_group(const float *slopes, int heads, int units, c
     int npre = 0;
     for (int h0 = 0; h0 < heads; h0 += 64) {
         const int h = h0 + lane;
-        npre += __popcll(__ballot(h < heads && !fix_head(slopes[h < heads ? h : 0] * LOG2E, sp.seg_len, sp.fix_osz)));
+        npre += __popcll(__ballot(h < heads && takes_prepass(sp, slopes[h < heads ? h : 0] * LOG2E)));
     }
     npre = __builtin_amdgcn_readfirstlane(npre);
     long long k = ((long long)units * npre * sp.pieces + kPrepassActive - 1) / kPrepassActive;
@@ -474,7 +491,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float *s
     const int e = 4 * ((blockIdx.x % kCombineSlices) * kCombineThreads + threadIdx.x);
     const int h = uh % heads;
     const float s2 = slopes[h] * LOG2E;
-    if (fix_head(s2, sp.seg_len, sp.fix_osz)) return;  // local-start segments: no pre-pass states
+    if (!takes_prepass(sp, s2)) return;  // local-start or warm-up segments: no pre-pass states
     float *u = sp.unit(ws, uh);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (s0) {

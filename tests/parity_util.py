@@ -16,9 +16,9 @@ Every GPU-vs-oracle comparison goes through :func:`parity_err`, which holds a
 bound alone cannot see a few wrong rows in a long sequence: at L = 32768 one
 entirely wrong row adds only sqrt(1/32768) ~ 0.0055 to it. The row bound
 catches such a row (its ratio is ~1, against 5e-2 for bf16), including the
-rows where a segmented plan could go wrong (segment starts, the end of a
-carried-state correction, sub-block edges, the last token), since every row
-of every compared slice is checked.
+rows where a segmented plan could go wrong (segment starts, the cuts between
+warm-up ranges, sub-block edges, the last token), since every row of every
+compared slice is checked.
 
 ROW_FACTOR = 5: with bf16 inputs the per-row error of a correct kernel is the
 rounding of its bf16 operands (the scores and the state, 2^-9 relative),
@@ -146,17 +146,17 @@ def plan_segments(batch, L, heads):
 
 def boundary_rows(L, seg_len, segments, slope):
     """Rows (token indices) next to every place a segmented plan switches: segment
-    starts +-2, the end of the carried-state correction +-1 (for heads that take
-    local starts), every 64-token sub-block edge +-1, and the last token."""
+    starts +-2 (heads on the pre-pass), every 64-token sub-block edge +-1 (the
+    cuts between the warm-up ranges of the other heads fall on such edges), and
+    the last token. ``slope`` is kept for the callers; the rows do not depend
+    on it."""
+    del slope
     rows = {0, L - 1}
     for c in range(0, L, 64):
         rows.update((c - 1, c))
     for g in range(segments):
         s0 = g * seg_len
         rows.update(range(s0 - 2, s0 + 3))
-        if g > 0 and slope > 0:
-            fix = min(seg_len, int(np.float32(24.0) / (np.float32(slope) * np.float32(LOG2E))))
-            rows.update(range(s0 + fix - 1, s0 + fix + 2))
     return sorted(r for r in rows if 0 <= r < L)
 
 

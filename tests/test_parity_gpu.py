@@ -422,14 +422,15 @@ def test_prefill_segmented_slope_mix(la, out_dtype):
     assert eo <= TOL_BF16 and es <= TOL_BF16 and eb <= TOL_BF16, (eo, es, eb)
 
 
-def test_prefill_segmented_local_starts_no_final_state(la):
-    """Segmented plan over local-start heads with no final state requested
-    (the correction pass writes no state) and a carried-in state."""
+def test_prefill_segmented_warm_ranges_no_final_state(la):
+    """Segmented plan over warm-up heads only, with no final state requested
+    and a carried-in state (read by the ranges whose warm-up reaches the
+    sequence start)."""
     import torch
 
     L, H = 9000, 4
     sl = np.array([0.02, 0.2, 1.0, 30.0], np.float32)
-    print(f"[case] segmented local starts, no state_out, L={L} slopes={list(sl)}", flush=True)
+    print(f"[case] segmented warm ranges, no state_out, L={L} slopes={list(sl)}", flush=True)
     q, k, v = workloads.qkv_host(2311, (1, L, H, 128), "bf16")
     s0 = workloads.state_host(2312, (1, H, 128, 128))
     o, st = la.lt_prefill(*(to_device(x, "bf16") for x in (q, k, v)), torch.from_numpy(sl).cuda(), 256,

@@ -2,8 +2,11 @@
 
 The contract (include/lightning.h): every output that the exact operator makes
 non-finite is non-finite (NaN or Inf) on the GPU, whatever plan the call takes
-(including local-start segments, whose carried-state correction is widened to
-the whole segment when that state is non-finite), and every other output is
+(including warm-up ranges, which rebuild their carried-in state from a window
+of earlier tokens and so cannot see a NaN or Inf from before it: a finishing
+pass puts it back from the flagged end states of the earlier ranges), and the
+carried-in state of the backward's local-start segments, whose correction is
+widened to the whole segment when that state is non-finite; every other output is
 finite and within the parity bound, except outputs of earlier tokens of the
 same 64-token block (counted from the sequence start) as a non-finite v: the
 masked entries of the in-block product are zeros multiplied on the matrix
@@ -88,18 +91,18 @@ def check_states(g, r, what):
 
 
 # Slope mix of the segmented slope-mix test: heads 0-2 take the pre-pass (their
-# memory outlasts a 2304-token segment), 3-6 local-start segments (correction of
-# 831, 83, 16 and 0 tokens).
+# memory outlasts a 2304-token segment), 3-6 warm-up ranges (warm-ups of 832,
+# 128, 64 and 64 tokens; the ranges are about 2,250 tokens long).
 MIX = np.array([0.0, 1e-6, 0.005, 0.02, 0.2, 1.0, 30.0], np.float32)
 # (tensor, head, token, feature, value): segment 0 is [0, 2304), 1 [2304, 4608),
 # 2 [4608, 6912), 3 [6912, 9000).
 MIX_SPOTS = [
-    ("k", 3, 1000, 5, np.nan),     # local-start head, segment 0: poisons the later segments
-    ("v", 5, 1500, 17, np.inf),    # local-start head, one value column, mid block
+    ("k", 3, 1000, 5, np.nan),     # warm-up head: poisons the later ranges, whose warm-ups miss it
+    ("v", 5, 1500, 17, np.inf),    # warm-up head, one value column, mid block
     ("k", 1, 700, 9, np.nan),      # pre-pass head
     ("v", 2, 2000, 3, -np.inf),    # pre-pass head, one column
     ("q", 6, 5000, 1, np.nan),     # one output row only
-    ("k", 4, 4000, 0, -np.inf),    # local-start head, segment 1: poisons segments 2, 3
+    ("k", 4, 4000, 0, -np.inf),    # warm-up head: poisons the later ranges
     ("q", 0, 8000, 2, np.inf),     # one output row only
 ]
 

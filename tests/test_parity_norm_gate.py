@@ -181,10 +181,10 @@ def test_decode_norm_gate_bf16_output(la):
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_prefill_norm_gate_segmented_slope_mix(la, out_dtype):
     """Norm-gate prefill of the segmented plan over heads on both routes: the
-    short-memory heads (0.02, 0.2, 1, 30) start every segment from zero, leave
-    the raw output of their first rows in y, and the correction pass adds the
-    carried-in term, normalises and gates those rows; 0 and 1e-6 take the
-    pre-pass. Carried-in state updated in place."""
+    short-memory heads (0.02, 0.2, 1, 30) take warm-up ranges (each range
+    rebuilds its carried-in state from the tokens just before it), 0 and 1e-6
+    the pre-pass. Carried-in state updated in place, so the warm-up heads'
+    final states go through the workspace."""
     import torch
 
     L, H = 9000, 6
@@ -210,8 +210,8 @@ def test_prefill_norm_gate_segmented_slope_mix(la, out_dtype):
 
 
 def test_prefill_norm_gate_segmented_no_final_state(la):
-    """Segmented norm-gate prefill over local-start heads with no final state
-    requested: the correction pass still finishes every parked row."""
+    """Segmented norm-gate prefill over warm-up heads only, with no final state
+    requested."""
     import torch
 
     L, H = 9000, 4

@@ -1,7 +1,8 @@
 """GPU parity of packed (varlen) prefill whose long sequences are split across
 workgroups: the plan is cut on the longest sequence (max_seqlen) and every
-sequence uses the segments its own length needs, with the pre-pass and the
-carried-state correction stopping at its end.
+sequence uses the segments its own length needs: the pre-pass stops at its
+end, and the warm-up ranges of the other heads are cut over the tokens of all
+sequences by cost.
 
 Tolerance: relative L2 per (sequence, head) <= 1e-2 with every row within the
 row bound (parity_util.parity_err), outputs and final states.
@@ -18,7 +19,7 @@ from parity_util import (TOL_BF16, ensure_built, max_rel_per_head, max_rel_state
 pytestmark = pytest.mark.gpu
 
 # heads 0-2 on the pre-pass (their memory outlasts a segment), 3-6 on
-# local-start segments with a carried-state correction
+# warm-up ranges
 MIX = np.array([0.0, 1e-6, 0.005, 0.02, 0.2, 1.0, 30.0], np.float32)
 
 
