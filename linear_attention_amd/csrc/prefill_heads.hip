@@ -197,11 +197,15 @@ constexpr int kRankUnits = 64;
 // Segmented plans have fewer than 256 (sequence, head) pairs.
 constexpr int kMaxPairs = 256;
 
-// Warm-up cost of a token against an output token: its k and v rows (2 x 256 B)
-// against q, k, v, the output row and, with the norm-gate epilogue, the gate row.
+// Warm-up cost of a token against an output token. By bytes a warm-up token
+// moves its k and v rows (2 x 256 B) against q, k, v, the output row and, with
+// the norm-gate epilogue, the gate row of an output token; the warm-up's steps
+// (two barriers per 64-token sub-block, no output stores to overlap) run below
+// the streaming rate, by the factor measured on the M1 layer (24-27 ns per
+// warm-up token against 53 ns per output token with fp32 outputs).
 template <typename OutT, bool NG>
 __device__ constexpr double warm_cost() {
-    return 512.0 / (768.0 + 128.0 * sizeof(OutT) + (NG ? 256.0 : 0.0));
+    return 1.25 * 512.0 / (768.0 + 128.0 * sizeof(OutT) + (NG ? 256.0 : 0.0));
 }
 
 // The heads of a segmented plan split by route (each wave computes the same
@@ -233,20 +237,37 @@ __device__ inline Routes split_heads(const float *slopes, int heads, const Segme
 // Work of a workgroup of a segmented plan. The (unit, head) pairs of heads on
 // the pre-pass route take `segments` workgroups each, one per segment: the
 // first npre * units * segments workgroups, pair i of them (i / segments) the
-// i-th such pair in (unit, head) order. The tokens of the other pairs (the
-// warm-up route, see warm_len) are cut into ranges of equal cost over the
-// remaining workgroups, one range each; a range may end in one pair and go on
-// in the next. An output token costs 1 and a warm-up token warm_cost(); pair j
-// (the j-th warm pair in (unit, head) order) costs
-//     C_j = len_j + warm_cost * min(W_j, len_j) * len_j / T0,
-// its length plus the warm-ups of the about len_j / T0 cuts inside it (T0: the
-// warm tokens per workgroup), spread evenly over its tokens; that balances the
-// workgroups to first order. A workgroup's range is [r T, (r+1) T) of the
-// prefix sums of C (T = sum C / workgroups), mapped onto each pair's tokens
-// linearly and cut at whole 64-token sub-blocks, so neighbours agree on every
-// cut. Ranges ending inside a pair leave a flag (and, when non-finite, their
-// end state) in the slots of their home pair, the (r / segments)-th warm pair,
-// which the finishing pass reads.
+// i-th such pair in (unit, head) order. The other pairs (the warm-up route, see
+// warm_len) share the remaining workgroups in two phases.
+//  * Fine chunks: about kFineFrac of the warm-up route's tokens, taken from the
+//    end of the pairs whose warm-up is at most kFineWarm tokens, nf chunks of
+//    kFineChunk tokens from each such pair that is long enough (at most half
+//    its tokens). A workgroup that has finished its range takes the next
+//    chunk from a counter; chunk c is chunk c / Q of the (c % Q)-th of the Q
+//    such pairs, so the chunks in flight at any time spread over the heads
+//    (the rows of one head sit at the same offset of every token's row, and
+//    many workgroups on a few heads stream far slower). Which chunk a
+//    workgroup gets depends on timing, but where the chunks are cut does not,
+//    so the result does not either; the chunks absorb the differences in speed
+//    between workgroups that a static split cannot foresee (on the M1 layer
+//    one head in four streams about 15% slower than the others, the same
+//    heads on every call).
+//  * Ranges: the rest of each pair's tokens ("bulk") is cut into ranges of
+//    equal cost, one per workgroup; a range may end in one pair and go on in
+//    the next. An output token costs 1 and a warm-up token warm_cost(); pair j
+//    (the j-th warm pair in (unit, head) order, with B_j bulk tokens) costs
+//        C_j = B_j + warm_cost * min(W_j, B_j) * B_j / T0,
+//    its bulk plus the warm-ups of the about B_j / T0 cuts inside it (T0: the
+//    bulk tokens per workgroup), spread evenly over its tokens; that balances
+//    the ranges to first order. A workgroup's range is [r T, (r+1) T) of the
+//    prefix sums of C (T = sum C / workgroups), mapped onto each pair's tokens
+//    linearly and cut at whole 64-token sub-blocks, so neighbours agree on
+//    every cut.
+// A piece that ends inside its pair with a NaN or Inf in its end state records
+// them in the pair's records (warm_records), from which the finishing pass
+// restores them in the later tokens.
+constexpr double kFineFrac = 0.15;
+constexpr long long kFineWarm = 128, kFineChunk = 512;
 struct WarmCut {
     const double *cpre;  // [nwarm pairs + 1] prefix sums of C
     double T;
@@ -259,28 +280,6 @@ struct WarmCut {
     }
 };
 
-// Segmented plans launch fewer than two workgroups per CU.
-constexpr int kMaxWarmWgs = 512;
-// Home slots of warm workgroup r (r counted from the first warm workgroup):
-// its flag {pair + 1 if its end state is non-finite else 0, cut} at ints
-// 2 (r % segments) of slot `segments` of its home pair, and that end state in
-// slot r % segments. Slot segments + 1 of a warm pair holds its final state
-// on in-place calls.
-__device__ __forceinline__ float *warm_home(float *ws, const Segmented &sp, const short *heads_warm, int nwarm,
-                                            int heads, int r) {
-    const int iw = r / sp.segments;
-    return sp.unit(ws, (iw / nwarm) * heads + heads_warm[iw % nwarm]);
-}
-__device__ __forceinline__ int *warm_flag(float *ws, const Segmented &sp, const short *heads_warm, int nwarm,
-                                          int heads, int r) {
-    return reinterpret_cast<int *>(Segmented::slot(warm_home(ws, sp, heads_warm, nwarm, heads, r), sp.segments)) +
-           2 * (r % sp.segments);
-}
-__device__ __forceinline__ float *warm_end_state(float *ws, const Segmented &sp, const short *heads_warm, int nwarm,
-                                                 int heads, int r) {
-    return Segmented::slot(warm_home(ws, sp, heads_warm, nwarm, heads, r), r % sp.segments);
-}
-
 // A workgroup's current piece, as thread 0 lays it out for the others: rows
 // of the piece's first token (k and v: of its warm-up's first token; row
 // stride ts elements), its length, the carried-in state and where the end
@@ -290,23 +289,26 @@ struct Piece {
     void *o;
     const float *nw;    // the head's normalisation weights (norm-gate epilogue)
     const float *s_in;  // carried-in state (nullptr: zero)
-    float *dst;         // end state destination
-    int *flag;          // end == 2: the range's flag
+    float *dst;         // end == 1: the final state's destination
+    int *rec;           // end == 2: the pair's records
     long long len, warm;  // tokens of the piece; warm-up tokens before it (whole sub-blocks)
     float s2, eps;
     int ts;
     int uh;      // -1: no more pieces
     int s_in_t;  // s_in transposed
-    int cut;     // end == 2: the token the range ends at
-    int end;     // 0 nothing, 1 the end state to dst, 2 to dst and flagged if non-finite
+    int cut;     // end == 2: the token the piece ends at
+    int end;     // 0 nothing, 1 the final state to dst, 2 records if the end state is non-finite
 };
 // Warm-route bookkeeping of a workgroup.
 struct PlanState {
     double T;   // cost per workgroup
     int rl;     // this workgroup's range, counted from the first warm workgroup
-    int next;   // the next pair to visit (pw: none)
+    int next;   // the next pair of its range to visit (pw: none)
     int npre, nwarm, pw;
     int last;   // the last workgroup (takes every pair left)
+    int nfine;     // fine chunks in all (nq pairs x nf chunks)
+    int nq, nf;
+    int *counter;  // the fine-chunk counter
 };
 
 template <typename OutT>
@@ -328,12 +330,35 @@ __device__ void piece_rows(Piece &p, const PrefillArgs &a, int n, int h, long lo
     p.uh = n * a.heads + h;
 }
 
+// A warm-route piece of pair (n, h): tokens [t0, t1) of a sequence of len.
+template <typename OutT>
+__device__ void warm_piece(Piece &p, const PrefillArgs &a, const Segmented &sp, float *ws, int n, int h,
+                           long long t0, long long t1, long long len) {
+    const long long wl = warm_len(a.slopes[h] * LOG2E);
+    const long long t0w = t0 > wl ? t0 - wl : 0;
+    piece_rows<OutT>(p, a, n, h, t0, t1, t0w);
+    const size_t sb = (size_t)p.uh * D * D;
+    if (t0w == 0 && a.state_in) {  // the warm-up reaches the sequence start: exact
+        p.s_in = a.state_in + sb;
+        p.s_in_t = a.state_in_t;
+    }
+    if (t1 < len) {
+        p.rec = warm_records(sp, ws, p.uh);
+        p.cut = (int)t1;
+        p.end = 2;
+    } else if (a.state_out) {
+        // on in-place calls other pieces of the pair may still read S_0
+        p.dst = a.state_in == a.state_out ? Segmented::slot(sp.unit(ws, p.uh), 1) : a.state_out + sb;
+        p.end = 1;
+    }
+}
+
 // The next piece of this workgroup (thread 0; the arguments are LDS copies,
 // so that none of them stays in registers through a piece).
 template <typename OutT>
 __device__ Piece next_piece(const PrefillArgs &a, const Segmented &sp, float *ws, int mode, int k,
                             PlanState &ps, const short *heads_pre, const short *heads_warm, const double *cpre,
-                            const int *by_rank) {
+                            const long long *bulk, const short *qlist, const int *by_rank) {
     const SeqLens lens{a.cu_seqlens, a.total_tokens, a.seqlen};
     Piece p{};
     p.uh = -1;
@@ -363,35 +388,33 @@ __device__ Piece next_piece(const PrefillArgs &a, const Segmented &sp, float *ws
         p.end = p.dst ? 1 : 0;
         return p;
     }
+    // this workgroup's range of bulk tokens
     const WarmCut wc{cpre, ps.T};
     const double c0 = (double)ps.rl * ps.T, c1 = (double)(ps.rl + 1) * ps.T;
     while (ps.next < ps.pw) {
         const int j = ps.next;
         const int n = j / ps.nwarm, h = heads_warm[j % ps.nwarm];
-        const long long len = lens.len(n);
-        const long long t0 = wc.cut(j, c0, len);
-        const long long t1 = ps.last ? len : wc.cut(j, c1, len);
+        const long long b = bulk[j];
+        const long long t0 = wc.cut(j, c0, b);
+        const long long t1 = ps.last ? b : wc.cut(j, c1, b);
         ps.next = ps.last || cpre[j + 1] < c1 ? j + 1 : ps.pw;  // the range goes on into the next pair
         if (t1 <= t0) continue;
-        const long long wl = warm_len(a.slopes[h] * LOG2E);
-        const long long t0w = t0 > wl ? t0 - wl : 0;
-        piece_rows<OutT>(p, a, n, h, t0, t1, t0w);
-        const size_t sb = (size_t)p.uh * D * D;
-        if (t0w == 0 && a.state_in) {  // the warm-up reaches the sequence start: exact
-            p.s_in = a.state_in + sb;
-            p.s_in_t = a.state_in_t;
-        }
-        if (t1 < len) {
-            p.dst = warm_end_state(ws, sp, heads_warm, ps.nwarm, a.heads, ps.rl);
-            p.flag = warm_flag(ws, sp, heads_warm, ps.nwarm, a.heads, ps.rl);
-            p.cut = (int)t1;
-            p.end = 2;
-        } else if (a.state_out) {
-            p.dst = a.state_in == a.state_out ? Segmented::slot(sp.unit(ws, p.uh), sp.segments + 1)
-                                              : a.state_out + sb;
-            p.end = 1;
-        }
+        warm_piece<OutT>(p, a, sp, ws, n, h, t0, t1, lens.len(n));
         return p;
+    }
+    // then fine chunks, while any are left
+    if (ps.nfine > 0) {
+        const int c = atomicAdd(ps.counter, 1);
+        if (c >= ps.nfine) {
+            ps.nfine = 0;
+            return p;
+        }
+        const int j = qlist[c % ps.nq], i = c / ps.nq;
+        const int n = j / ps.nwarm, h = heads_warm[j % ps.nwarm];
+        const long long len = lens.len(n);
+        const long long t0 = bulk[j] + (long long)i * kFineChunk;
+        const long long t1 = i + 1 == ps.nf ? len : t0 + kFineChunk;
+        warm_piece<OutT>(p, a, sp, ws, n, h, t0, t1, len);
     }
     return p;
 }
@@ -421,12 +444,14 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
     __shared__ __attribute__((aligned(16))) float Wn[NG ? D : 1];
     __shared__ __attribute__((aligned(16))) float Rss[NG ? C * 4 : 1];  // per-row partial sums of o^2
     __shared__ double cpre[kMaxPairs + 1];
+    __shared__ long long bulk[kMaxPairs];
+    __shared__ short qlist[kMaxPairs];  // pairs that give fine chunks
+    __shared__ int fq[2];               // their count, chunks per pair
     __shared__ short heads_pre[kMaxPairs], heads_warm[kMaxPairs];
     __shared__ int by_rank[kRankUnits];
     __shared__ long long rlen[kRankUnits];
     __shared__ PlanState ps;
     __shared__ Piece pc;
-    __shared__ int any_bad;
     __shared__ __attribute__((aligned(16))) unsigned char args_lds[sizeof(PrefillArgs)];
     __shared__ __attribute__((aligned(16))) unsigned char sp_lds[sizeof(Segmented)];
     __shared__ float *ws_lds;
@@ -468,45 +493,78 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
         mode = (long long)blockIdx.x < pre_wgs ? 1 : 2;
         const int pw = a.units * rt.nwarm;  // warm pairs
         if (mode == 2 && w == 0) {
-            const double nwg = (double)pw * segments;
             // lane l: warm pairs 4l .. 4l+3 (pw < 256)
-            double L[4], Wt[4], sum = 0.0;
+            const double nwg = (double)pw * segments;
+            long long L[4], Wt[4], nf[4];
+            double lsum = 0.0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int j = 4 * lane0 + i;
-                L[i] = 0.0;
-                Wt[i] = 0.0;
+                L[i] = 0;
+                Wt[i] = 0;
                 if (j < pw) {
-                    const int h = heads_warm[j % rt.nwarm];
-                    L[i] = (double)lens.len(j / rt.nwarm);
-                    Wt[i] = (double)warm_len(a.slopes[h] * LOG2E);
+                    L[i] = lens.len(j / rt.nwarm);
+                    Wt[i] = warm_len(a.slopes[heads_warm[j % rt.nwarm]] * LOG2E);
                 }
-                sum += L[i];
+                lsum += (double)L[i];
             }
-            for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
-            const double t0 = sum / nwg;  // warm tokens per workgroup
+            for (int o = 32; o >= 1; o >>= 1) lsum += __shfl_xor(lsum, o);
+            // fine chunks: kFineFrac of all warm tokens, nf from each pair that
+            // qualifies (at first count) and holds at least 2 nf chunks
+            int nq0 = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) nq0 += Wt[i] <= kFineWarm && L[i] >= 2 * kFineChunk;
+            for (int o = 32; o >= 1; o >>= 1) nq0 += __shfl_xor(nq0, o);
+            const long long nfw = nq0 > 0 ? (long long)(kFineFrac * lsum / ((double)nq0 * (double)kFineChunk)) : 0;
+            double bsum = 0.0;
+            int nrun = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool q = nfw > 0 && Wt[i] <= kFineWarm && L[i] >= 2 * nfw * kFineChunk;
+                nf[i] = q ? nfw : 0;
+                // bulk: the tokens before the first fine chunk (a multiple of 64)
+                const long long b = q ? (L[i] - nfw * kFineChunk) / 64 * 64 : L[i];
+                const int j = 4 * lane0 + i;
+                if (j < pw) bulk[j] = b;
+                L[i] = b;
+                bsum += (double)b;
+                nrun += q;
+            }
+            for (int o = 32; o >= 1; o >>= 1) bsum += __shfl_xor(bsum, o);
+            const double t0 = bsum / nwg;  // bulk tokens per workgroup
             double c[4], run = 0.0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const double wl = Wt[i] < L[i] ? Wt[i] : L[i];
-                c[i] = L[i] > 0.0 ? L[i] + warm_cost<OutT, NG>() * wl * (L[i] / t0) : 0.0;
+                const double bl = (double)L[i], wl = Wt[i] < L[i] ? (double)Wt[i] : bl;
+                c[i] = L[i] > 0 ? bl + warm_cost<OutT, NG>() * wl * (bl / t0) : 0.0;
                 run += c[i];
             }
-            double incl = run;  // inclusive scan of the lanes' sums
+            double incl = run;  // inclusive scans of the lanes' sums
+            int fincl = nrun;
             for (int o = 1; o < 64; o <<= 1) {
                 const double y = __shfl_up(incl, o);
-                if (lane0 >= o) incl += y;
+                const int fy = __shfl_up(fincl, o);
+                if (lane0 >= o) {
+                    incl += y;
+                    fincl += fy;
+                }
             }
             double acc = incl - run;
+            int facc = fincl - nrun;  // qualifying pairs before this lane's
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int j = 4 * lane0 + i;
                 if (j < pw) cpre[j] = acc;
+                if (nf[i] > 0) qlist[facc++] = (short)j;
                 acc += c[i];
             }
-            if (lane0 == 63) cpre[pw] = incl;
+            if (lane0 == 63) {
+                cpre[pw] = incl;
+                fq[0] = fincl;
+                fq[1] = (int)nfw;
+            }
         }
-        __syncthreads();  // cpre is visible
+        __syncthreads();  // cpre, bulk, qlist and fq are visible
         if (t0id == 0) {
             ps.npre = rt.npre;
             ps.nwarm = rt.nwarm;
@@ -524,10 +582,10 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
                     if (cpre[mid + 1] > c0) hi = mid; else lo = mid + 1;
                 }
                 ps.next = lo;
-                // no flag until a range ends inside a pair
-                int *flag = warm_flag(ws, sp, heads_warm, rt.nwarm, a.heads, rl);
-                flag[0] = 0;
-                flag[1] = 0;
+                ps.nq = fq[0];
+                ps.nf = fq[1];
+                ps.nfine = ps.nq * ps.nf;
+                ps.counter = warm_records(sp, ws, heads_warm[0]) + kFineCounter;  // in the first warm pair's records
             }
         }
     }
@@ -548,7 +606,7 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
         if (tid == 0)
             pc = next_piece<OutT>(*reinterpret_cast<const PrefillArgs *>(args_lds),
                                   *reinterpret_cast<const Segmented *>(sp_lds), ws_lds, mode, k, ps, heads_pre,
-                                  heads_warm, cpre, by_rank);
+                                  heads_warm, cpre, bulk, qlist, by_rank);
         __syncthreads();
         const int uh = __builtin_amdgcn_readfirstlane(pc.uh);
         if (uh < 0) break;
@@ -740,30 +798,31 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
 
         // the end state (pc is unchanged until the next piece)
         const int end = __builtin_amdgcn_readfirstlane(pc.end);
-        bool keep = end == 1;
-        if (end == 2) {  // a warm range ending inside its pair: kept and flagged only if non-finite
-            bool bad = false;
-#pragma unroll
-            for (int db = 0; db < 2; ++db)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) bad |= nonfinite(S[db][v]);
-            if (tid == 0) any_bad = 0;
-            __syncthreads();
-            if (__ballot(bad) != 0 && lane == 0) atomicOr(&any_bad, 1);
-            __syncthreads();
-            keep = any_bad != 0;
-        }
-        if (keep) {
+        if (end == 1) {  // the final state
             float *dst = uniform_ptr(pc.dst);
             const int sb = sbase();
 #pragma unroll
             for (int db = 0; db < 2; ++db)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) dst[sidx(sb, db, v)] = S[db][v];
-            if (end == 2 && tid == 0) {  // after the state, so that it is not held through the flag's writes
-                int *flag = pc.flag;
-                flag[0] = uh + 1;
-                flag[1] = pc.cut;
+        } else if (end == 2) {  // a warm piece ending inside its pair: record a NaN or Inf
+            bool bad = false;
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) bad |= nonfinite(S[db][v]);
+            if (bad) {  // rare: every entry of this thread's state blocks is in column 32 cq + r32
+                int *rec = pc.rec;
+                const int sb = sbase();
+#pragma unroll
+                for (int db = 0; db < 2; ++db)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        if (nonfinite(S[db][v])) {
+                            const int e = sidx(sb, db, v);
+                            atomicOr(reinterpret_cast<unsigned *>(rec + kRecEntBad) + (e >> 5), 1u << (e & 31));
+                        }
+                atomicMin(rec + kRecColCut + 32 * cq + r32, pc.cut);
             }
         }
     }
@@ -999,42 +1058,36 @@ __global__ __launch_bounds__(NT) void slice_kernel(PrefillArgs a) {
 
 // ---------------------------------------------------------------------------
 // Finishing pass of the warm-up route: one workgroup per (unit, head) pair;
-// pairs on the pre-pass route exit at once. A range that ends inside its pair
-// built its carried-in state from a finite window of tokens, so it cannot see
+// pairs on the pre-pass route exit at once. A piece that starts inside its pair
+// builds its carried-in state from a window of earlier tokens, so it cannot see
 // a NaN or Inf from before that window, which the exact operator carries
-// forward: it stays in the state entries it reached, and every later output
-// column of those entries is non-finite. Each such range flagged its
-// non-finite end state E (cut c) in its home slots; this pass puts NaN in rows
-// [c, len) of the pair in every column where E has one (whole rows with the
-// norm-gate epilogue, whose normalisation spreads it over the row) and in each
-// final-state entry where some E has one. It also writes the final state of
-// empty sequences (S_0, or zero) and, for in-place calls (state_out ==
-// state_in), copies the final state that the main pass left in the workspace:
-// writing it there directly could race with the reads of S_0 by the pair's
-// other ranges.
+// forward: it stays in the state entries it reached, and every later output in
+// the value columns of those entries is non-finite. The pieces that ended
+// inside the pair recorded where their end states held one (warm_records);
+// this pass puts NaN in every output of column c from the earliest such end in
+// that column on (in whole rows with the norm-gate epilogue, whose
+// normalisation spreads it over the row) and in each final-state entry that
+// was non-finite at some such end. It also writes the final state of empty
+// sequences (S_0, or zero) and, for in-place calls (state_out == state_in),
+// copies the final state that the main pass left in the workspace: writing it
+// there directly could race with the reads of S_0 by the pair's other pieces.
 __device__ __forceinline__ void poison(float *p) { *p = __builtin_nanf(""); }
 __device__ __forceinline__ void poison(__bf16 *p) { *reinterpret_cast<uint16_t *>(p) = 0x7fc0; }
 
 // float4 elements of a d x d state per thread of a workgroup
 constexpr int kStateF4 = D * D / (4 * NT);
-static_assert(kStateF4 * 4 * NT == D * D && 4 * kStateF4 <= 64, "state elements per thread");
+static_assert(kStateF4 * 4 * NT == D * D, "state elements per thread");
 
 template <typename OutT, bool NG>
 __global__ __launch_bounds__(NT) void finish_kernel(PrefillArgs a, Segmented sp, float *ws) {
-    __shared__ short heads_pre[kMaxPairs], heads_warm[kMaxPairs];
-    __shared__ int flagged[kMaxWarmWgs], cutv[kMaxWarmWgs], order[kMaxWarmWgs];
-    __shared__ int nflag;
-    __shared__ unsigned colbad[D / 32];
+    __shared__ int colcut[D];
+    __shared__ int mincut;
     const int tid = threadIdx.x;
     const int uh = blockIdx.x, h = uh % a.heads, n = uh / a.heads;
     if (takes_prepass(sp, a.slopes[h] * LOG2E)) return;
-    const Routes rt = split_heads(a.slopes, a.heads, sp, heads_pre, heads_warm, tid < 64);
-    if (tid == 0) nflag = 0;
-    if (tid < D / 32) colbad[tid] = 0;
-    __syncthreads();
     const long long len = SeqLens{a.cu_seqlens, a.total_tokens, a.seqlen}.len(n);
     const size_t sb = (size_t)uh * D * D;
-    if (len == 0) {  // no range covers the pair: the final state is S_0
+    if (len == 0) {  // no piece covers the pair: the final state is S_0
         if (a.state_out && a.state_out != a.state_in)
             for (int i = tid; i < D * D; i += NT) {
                 float x = 0.f;
@@ -1043,73 +1096,48 @@ __global__ __launch_bounds__(NT) void finish_kernel(PrefillArgs a, Segmented sp,
             }
         return;
     }
-    const int nwg = a.units * rt.nwarm * sp.segments;
-    for (int r = tid; r < nwg; r += NT) {
-        const int *f = warm_flag(ws, sp, heads_warm, rt.nwarm, a.heads, r);
-        if (f[0] == uh + 1) {
-            const int i = atomicAdd(&nflag, 1);
-            flagged[i] = r;
-            cutv[i] = f[1];
-        }
+    const int *rec = warm_records(sp, ws, uh);
+    if (tid == 0) mincut = kNoCut;
+    __syncthreads();
+    if (tid < D) {
+        colcut[tid] = rec[kRecColCut + tid];
+        atomicMin(&mincut, colcut[tid]);
     }
     __syncthreads();
-    const int cnt = nflag;
-    // this thread's state elements: float4 tid + NT j (j < kStateF4), all in
-    // columns 4 (tid % 32) .. + 3 (NT j float4 are a whole number of rows)
-    unsigned long long bad = 0;
-    if (cnt > 0) {
-        for (int i = tid; i < cnt; i += NT) {  // order the flagged ranges by cut
-            int rank = 0;
-            for (int j = 0; j < cnt; ++j) rank += cutv[j] < cutv[i] || (cutv[j] == cutv[i] && j < i);
-            order[rank] = i;
-        }
-        __syncthreads();
-        const SeqRange sr = sequence_of(a, n);
-        OutT *o = static_cast<OutT *>(a.o);
+    const int first = mincut;
+    if (first != kNoCut) {
+        // rows t >= colcut[c] in column c; 32 threads per row (4 columns each),
+        // NT / 32 rows at a time
         const int col = 4 * (tid & 31);
-        for (int k = 0; k < cnt; ++k) {
-            const int i = order[k];
-            const float4 *e = reinterpret_cast<const float4 *>(warm_end_state(ws, sp, heads_warm, rt.nwarm,
-                                                                              a.heads, flagged[i]));
-            unsigned cb = 0;
+        const long long base = sequence_of(a, n).start;
+        OutT *o = static_cast<OutT *>(a.o);
+        int cut4[4];
 #pragma unroll
-            for (int j = 0; j < kStateF4; ++j) {
-                const float4 x = e[tid + NT * j];
-                const unsigned b = (unsigned)nonfinite(x.x) | (unsigned)nonfinite(x.y) << 1 |
-                                   (unsigned)nonfinite(x.z) << 2 | (unsigned)nonfinite(x.w) << 3;
-                bad |= (unsigned long long)b << (4 * j);
-                cb |= b;
-            }
-            if (cb) atomicOr(&colbad[(tid & 31) >> 3], cb << (4 * (tid & 7)));
-            __syncthreads();
-            // rows [c0, c1): NaN in every column flagged so far (32 threads per row,
-            // NT / 32 rows at a time)
-            const long long c0 = cutv[i], c1 = k + 1 < cnt ? cutv[order[k + 1]] : len;
-            const unsigned m4 = NG ? 0xfu : (colbad[col >> 5] >> (col & 31)) & 0xfu;
-            if (m4)
-                for (long long t = c0 + (tid >> 5); t < c1; t += NT / 32) {
-                    OutT *row = o + ((sr.start + t) * a.heads + h) * (long long)D + col;
+        for (int x = 0; x < 4; ++x) cut4[x] = NG ? first : colcut[col + x];
+        for (long long t = first + (tid >> 5); t < len; t += NT / 32) {
+            OutT *row = o + ((base + t) * a.heads + h) * (long long)D + col;
 #pragma unroll
-                    for (int x = 0; x < 4; ++x)
-                        if (m4 >> x & 1) poison(row + x);
-                }
-            __syncthreads();  // every read of colbad for these rows is done
+            for (int x = 0; x < 4; ++x)
+                if (t >= cut4[x]) poison(row + x);
         }
     }
     const bool in_place = a.state_in && a.state_in == a.state_out;
-    if (a.state_out && (in_place || bad)) {
-        const float4 *src = reinterpret_cast<const float4 *>(in_place ? Segmented::slot(sp.unit(ws, uh), sp.segments + 1)
+    if (a.state_out && (in_place || first != kNoCut)) {
+        // this thread's state elements: float4 tid + NT j (j < kStateF4)
+        const unsigned *bad = reinterpret_cast<const unsigned *>(rec + kRecEntBad);
+        const float4 *src = reinterpret_cast<const float4 *>(in_place ? Segmented::slot(sp.unit(ws, uh), 1)
                                                                       : a.state_out + sb);
         float4 *dst = reinterpret_cast<float4 *>(a.state_out + sb);
 #pragma unroll
         for (int j = 0; j < kStateF4; ++j) {
-            float4 x = src[tid + NT * j];
-            const unsigned b = (unsigned)(bad >> (4 * j)) & 0xfu;
+            const int f = tid + NT * j;
+            float4 x = src[f];
+            const unsigned b = first != kNoCut ? (bad[f >> 3] >> (4 * (f & 7))) & 0xfu : 0u;  // entries 4f .. 4f+3
             if (b & 1) x.x = __builtin_nanf("");
             if (b & 2) x.y = __builtin_nanf("");
             if (b & 4) x.z = __builtin_nanf("");
             if (b & 8) x.w = __builtin_nanf("");
-            dst[tid + NT * j] = x;
+            dst[f] = x;
         }
     }
 }
@@ -1129,7 +1157,7 @@ hipError_t launch(const PrefillArgs &a, const PrefillPlan &p, void *workspace, h
     sp.warm = true;
     if (p.segments > 1) {
         // the kernels' per-plan tables hold every pair and workgroup of a segmented plan
-        if (uh >= kMaxPairs || uh * p.segments > kMaxWarmWgs) return hipErrorInvalidValue;
+        if (uh >= kMaxPairs) return hipErrorInvalidValue;
         hipLaunchKernelGGL(piece_state_kernel, dim3((unsigned)(uh * p.pieces)), dim3(NT), 0, stream,
                            a, sp, ws);
         hipError_t e = hipGetLastError();

@@ -444,6 +444,22 @@ __device__ __forceinline__ bool takes_prepass(const Segmented &sp, float s2) {
     return !fix_head(s2, sp.seg_len, sp.fix_osz);
 }
 
+// Warm-up route records, in slot 0 of each warm pair's workspace unit, reset by
+// the combine pass before the main kernel runs:
+//   ints [0, D)           per value column c, the earliest token t at which a
+//                         range ending at t left a non-finite end state with a
+//                         NaN or Inf in column c (kNoCut: none);
+//   ints [D, D + D*D/32)  one bit per state entry: non-finite in some such end
+//                         state;
+//   int kFineCounter      (first warm pair only) the next fine chunk to hand out.
+// Slot 1 holds the pair's final state on in-place calls.
+constexpr int kRecColCut = 0, kRecEntBad = D, kRecInts = D + D * D / 32, kFineCounter = 1024;
+constexpr int kNoCut = 0x7fffffff;
+static_assert(kRecInts <= kFineCounter, "warm records");
+__device__ __forceinline__ int *warm_records(const Segmented &sp, float *ws, int uh) {
+    return reinterpret_cast<int *>(Segmented::slot(sp.unit(ws, uh), 0));
+}
+
 // Tokens of segment g of a sequence of `seqlen` tokens (0 past its end).
 __device__ __forceinline__ long long seg_len_at(const Segmented &sp, long long seqlen, int g) {
     const long long rest = seqlen - (long long)g * sp.seg_len;
@@ -491,7 +507,14 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float *s
     const int e = 4 * ((blockIdx.x % kCombineSlices) * kCombineThreads + threadIdx.x);
     const int h = uh % heads;
     const float s2 = slopes[h] * LOG2E;
-    if (!takes_prepass(sp, s2)) return;  // local-start or warm-up segments: no pre-pass states
+    if (!takes_prepass(sp, s2)) {  // local-start or warm-up segments: no pre-pass states
+        if (sp.warm && blockIdx.x % kCombineSlices == 0) {  // reset the warm-up route's records
+            int *rec = warm_records(sp, ws, uh);
+            for (int i = threadIdx.x; i < kRecInts; i += kCombineThreads) rec[i] = i < kRecEntBad ? kNoCut : 0;
+            if (threadIdx.x == 0) rec[kFineCounter] = 0;
+        }
+        return;
+    }
     float *u = sp.unit(ws, uh);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (s0) {
