@@ -98,6 +98,35 @@ __device__ __forceinline__ void store_rows_norm_gate(OutT *out, long long ts, co
     }
 }
 
+// Segmented plans have fewer than 256 (sequence, head) pairs.
+constexpr int kMaxPairs = 256;
+
+// The heads of a segmented plan split by route (each wave computes the same
+// lists: 64 heads at a time by ballot, in head order).
+struct Routes {
+    int npre, nwarm;
+};
+__device__ inline Routes split_heads(const float *slopes, int heads, const Segmented &sp, short *pre,
+                                     short *warm, bool write) {
+    const int lane = threadIdx.x & 63;
+    Routes r{0, 0};
+    for (int h0 = 0; h0 < heads; h0 += 64) {
+        const int h = h0 + lane;
+        const bool in = h < heads;
+        const bool p = in && takes_prepass(sp, slopes[in ? h : 0] * LOG2E);
+        const unsigned long long bp = __ballot(p), bw = __ballot(in && !p);
+        if (write) {
+            const int below = lane ? __popcll(bp & (~0ull >> (64 - lane))) : 0;
+            const int belw = lane ? __popcll(bw & (~0ull >> (64 - lane))) : 0;
+            if (p) pre[r.npre + below] = (short)h;
+            if (in && !p) warm[r.nwarm + belw] = (short)h;
+        }
+        r.npre += __popcll(bp);
+        r.nwarm += __popcll(bw);
+    }
+    return r;
+}
+
 // Pre-pass: workgroup (unit, head, piece j) runs the state update over the
 // full 64-token sub-blocks of its group of pieces without outputs, writing its
 // state and, if a segment boundary falls strictly inside the group, B_g on the
@@ -105,23 +134,28 @@ __device__ __forceinline__ void store_rows_norm_gate(OutT *out, long long ts, co
 __global__ __launch_bounds__(NT, 4) void piece_state_kernel(PrefillArgs a, Segmented sp, float *ws) {
     __shared__ __attribute__((aligned(16))) __bf16 Ks[C * D];
     __shared__ __attribute__((aligned(16))) __bf16 Vds[C * D];
+    __shared__ short heads_pre[kMaxPairs], heads_warm[kMaxPairs];
 
-    // workgroup b takes group b % gph of (unit, head) b / gph, gph groups of
-    // kgr pieces per head; the working workgroups are the first U * gph, which
-    // the hardware spreads over all XCDs. The group's state goes to the slot
-    // of its last piece.
-    const int kgr = prepass_group(a.slopes, a.heads, a.units, sp);
-    const int gph = (sp.pieces + kgr - 1) / kgr;
-    if ((int)blockIdx.x >= a.units * a.heads * gph) return;
-    const int j = (blockIdx.x % gph) * kgr;
-    const int uh = blockIdx.x / gph;
-    const int h = uh % a.heads, n = uh / a.heads;
+    // workgroup b takes group b % gph of the (b / gph)-th pre-pass pair (in
+    // (unit, head) order), gph groups of kgr pieces per pair; the working
+    // workgroups are the first units * npre * gph (at most kPrepassActive +
+    // units * heads: the launch is sized for that), which the hardware spreads
+    // over all XCDs. The group's state goes to the slot of its last piece.
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const Routes rt = split_heads(a.slopes, a.heads, sp, heads_pre, heads_warm, w == 0);
+    if (rt.npre == 0) return;  // every head on warm-up segments: no pre-pass
+    const int kgr = prepass_group_of(rt.npre, a.units, sp);
+    const int gph = (sp.pieces + kgr - 1) / kgr;
+    if ((int)blockIdx.x >= a.units * rt.npre * gph) return;
+    __syncthreads();  // wave 0's head lists are visible
+    const int j = (blockIdx.x % gph) * kgr;
+    const int i = blockIdx.x / gph;
+    const int n = i / rt.npre, h = heads_pre[i % rt.npre];
+    const int uh = n * a.heads + h;
     const int qh = w >> 2, cq = w & 3, r32 = lane & 31, hf = lane >> 5;
 
     const float s2 = a.slopes[h] * LOG2E;
-    if (!takes_prepass(sp, s2)) return;  // warm-up segments: no pre-pass
     const int jl = j + kgr - 1 < sp.pieces - 1 ? j + kgr - 1 : sp.pieces - 1;
     const SeqRange sr = sequence_of(a, n);
     const long long covered = sp.covered(sr.len);
@@ -194,8 +228,6 @@ __global__ __launch_bounds__(NT, 4) void piece_state_kernel(PrefillArgs a, Segme
 
 // ---------------------------------------------------------------------------
 constexpr int kRankUnits = 64;
-// Segmented plans have fewer than 256 (sequence, head) pairs.
-constexpr int kMaxPairs = 256;
 
 // Warm-up cost of a token against an output token. By bytes a warm-up token
 // moves its k and v rows (2 x 256 B) against q, k, v, the output row and, with
@@ -206,32 +238,6 @@ constexpr int kMaxPairs = 256;
 template <typename OutT, bool NG>
 __device__ constexpr double warm_cost() {
     return 1.25 * 512.0 / (768.0 + 128.0 * sizeof(OutT) + (NG ? 256.0 : 0.0));
-}
-
-// The heads of a segmented plan split by route (each wave computes the same
-// lists: 64 heads at a time by ballot, in head order).
-struct Routes {
-    int npre, nwarm;
-};
-__device__ inline Routes split_heads(const float *slopes, int heads, const Segmented &sp, short *pre,
-                                     short *warm, bool write) {
-    const int lane = threadIdx.x & 63;
-    Routes r{0, 0};
-    for (int h0 = 0; h0 < heads; h0 += 64) {
-        const int h = h0 + lane;
-        const bool in = h < heads;
-        const bool p = in && takes_prepass(sp, slopes[in ? h : 0] * LOG2E);
-        const unsigned long long bp = __ballot(p), bw = __ballot(in && !p);
-        if (write) {
-            const int below = lane ? __popcll(bp & (~0ull >> (64 - lane))) : 0;
-            const int belw = lane ? __popcll(bw & (~0ull >> (64 - lane))) : 0;
-            if (p) pre[r.npre + below] = (short)h;
-            if (in && !p) warm[r.nwarm + belw] = (short)h;
-        }
-        r.npre += __popcll(bp);
-        r.nwarm += __popcll(bw);
-    }
-    return r;
 }
 
 // Work of a workgroup of a segmented plan. The (unit, head) pairs of heads on
@@ -1158,8 +1164,9 @@ hipError_t launch(const PrefillArgs &a, const PrefillPlan &p, void *workspace, h
     if (p.segments > 1) {
         // the kernels' per-plan tables hold every pair and workgroup of a segmented plan
         if (uh >= kMaxPairs) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(piece_state_kernel, dim3((unsigned)(uh * p.pieces)), dim3(NT), 0, stream,
-                           a, sp, ws);
+        // working pre-pass workgroups: at most kPrepassActive + uh (see piece_state_kernel)
+        const long long pre = uh * p.pieces < kPrepassActive + uh ? uh * p.pieces : kPrepassActive + uh;
+        hipLaunchKernelGGL(piece_state_kernel, dim3((unsigned)pre), dim3(NT), 0, stream, a, sp, ws);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(uh * kCombineSlices)), dim3(kCombineThreads),

@@ -476,6 +476,12 @@ __device__ __forceinline__ long long seg_len_at(const Segmented &sp, long long s
 // group never exceeds one segment, so it holds at most one segment boundary
 // strictly inside.
 constexpr int kPrepassActive = 512;
+__device__ inline int prepass_group_of(int npre, int units, const Segmented &sp) {
+    long long k = ((long long)units * npre * sp.pieces + kPrepassActive - 1) / kPrepassActive;
+    const long long kmax = sp.seg_len / sp.piece_len;
+    if (k > kmax) k = kmax;
+    return k < 1 ? 1 : (int)k;
+}
 __device__ inline int prepass_group(const float *slopes, int heads, int units, const Segmented &sp) {
     const int lane = threadIdx.x & 63;
     int npre = 0;
@@ -483,11 +489,7 @@ __device__ inline int prepass_group(const float *slopes, int heads, int units, c
         const int h = h0 + lane;
         npre += __popcll(__ballot(h < heads && takes_prepass(sp, slopes[h < heads ? h : 0] * LOG2E)));
     }
-    npre = __builtin_amdgcn_readfirstlane(npre);
-    long long k = ((long long)units * npre * sp.pieces + kPrepassActive - 1) / kPrepassActive;
-    const long long kmax = sp.seg_len / sp.piece_len;
-    if (k > kmax) k = kmax;
-    return k < 1 ? 1 : (int)k;
+    return prepass_group_of(__builtin_amdgcn_readfirstlane(npre), units, sp);
 }
 
 // Combine pass: the state at every segment start, S_0 being the first state
