@@ -28,7 +28,8 @@
  * Conventions shared by every entry point
  *  - Every pointer argument except `stream` is a DEVICE pointer (HBM). The
  *    caller owns every buffer; the library allocates nothing, keeps no global
- *    state, and never synchronises.
+ *    state (lt_prefill_noalloc aside, whose static device scratch is described
+ *    there), and never synchronises.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *    the call returns before it runs.
  *  - Layouts are dense and row-major with head_dim innermost. Element offsets
