@@ -131,7 +131,7 @@ __device__ inline Routes split_heads(const float *slopes, int heads, const Segme
 // full 64-token sub-blocks of its group of pieces without outputs, writing its
 // state and, if a segment boundary falls strictly inside the group, B_g on the
 // way.
-__global__ __launch_bounds__(NT, 4) void piece_state_kernel(PrefillArgs a, Segmented sp, float *ws) {
+__global__ __launch_bounds__(NT, 2) void piece_state_kernel(PrefillArgs a, Segmented sp, float *ws) {
     __shared__ __attribute__((aligned(16))) __bf16 Ks[C * D];
     __shared__ __attribute__((aligned(16))) __bf16 Vds[C * D];
     __shared__ short heads_pre[kMaxPairs], heads_warm[kMaxPairs];
