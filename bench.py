@@ -750,7 +750,12 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # Untimed calls before each timed workload. A burst of back-to-back prefill
+    # calls starts slow and settles after about 30 calls (M1 layer: calls 3-15 of
+    # a burst take 0.57-0.64 ms, calls 30-60 0.531-0.54 ms, every call 0.535 ms
+    # with the GPU idle for a millisecond before it); the timed calls measure the
+    # settled rate.
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--cpu-tokens", type=int, default=32768)
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
@@ -802,7 +807,7 @@ def main():
     log(f"[bench] prefill {pre['kernel_ms_mean']:.3f} ms/call")
     scaled = {}
     for f in (() if args.no_slopes_scaled else (0.1, 1e-5)):
-        _, _, r = run_m1_prefill(la, torch, 10, 2, slope_scale=f)
+        _, _, r = run_m1_prefill(la, torch, 10, 20, slope_scale=f)
         scaled[f"x{f:g}"] = {"kernel_ms_mean": round(r["kernel_ms_mean"], 5),
                              "tokens_per_s": round(1e3 * w.batch * w.seqlen / r["kernel_ms_mean"], 1),
                              "roofline_frac": r["roofline"]["frac"]}
@@ -830,7 +835,7 @@ def main():
         configs["varlen"] = run_varlen(la, torch, 10, 2, not args.no_cpu, cpu_s)
         log(f"[bench] varlen {configs['varlen']['call_ms_mean']:.3f} ms/call")
         log("[bench] varlen prefill, 2 x 131072 tokens")
-        configs["varlen_2x131072"] = run_varlen_2x(la, torch, 10, 2, not args.no_cpu, cpu_s / 2)
+        configs["varlen_2x131072"] = run_varlen_2x(la, torch, 10, 4, not args.no_cpu, cpu_s / 2)
         log(f"[bench] varlen 2x131072 {configs['varlen_2x131072']['call_ms_mean']:.3f} ms/call "
             f"(lt_prefill {configs['varlen_2x131072']['lt_prefill_same_shape_ms_mean']:.3f})")
     dec = None
@@ -857,7 +862,7 @@ def main():
         bwd = {}
         for b_, l_ in ((1, 32768), (4, 8192)):
             log(f"[bench] backward batch={b_} L={l_} H=64")
-            bwd[f"b{b_}_L{l_}"] = run_backward(la, torch, 10, 2, b_, l_)
+            bwd[f"b{b_}_L{l_}"] = run_backward(la, torch, 10, 10, b_, l_)
             log(f"[bench] backward {bwd[f'b{b_}_L{l_}']['kernel_ms_mean']:.3f} ms/call")
         if not args.no_cpu:
             bwd["cpu_baseline"] = backward_cpu_baseline(cpu_s / 2)
