@@ -267,13 +267,14 @@ __device__ constexpr double warm_cost() {
 //    bulk tokens per workgroup), spread evenly over its tokens; that balances
 //    the ranges to first order. A workgroup's range is [r T, (r+1) T) of the
 //    prefix sums of C (T = sum C / workgroups), mapped onto each pair's tokens
-//    linearly and cut at whole 64-token sub-blocks, so neighbours agree on
-//    every cut.
+//    linearly and cut at multiples of 128 tokens, so neighbours agree on every
+//    cut and every warm-up is an even number of 64-token sub-blocks.
 // A piece that ends inside its pair with a NaN or Inf in its end state records
 // them in the pair's records (warm_records), from which the finishing pass
 // restores them in the later tokens.
 constexpr double kFineFrac = 0.15;
 constexpr long long kFineWarm = 128, kFineChunk = 512;
+static_assert(kFineChunk % 128 == 0, "pieces start at multiples of 128 tokens");
 struct WarmCut {
     const double *cpre;  // [nwarm pairs + 1] prefix sums of C
     double T;
@@ -281,7 +282,7 @@ struct WarmCut {
         const double a = cpre[j], b = cpre[j + 1];
         if (c <= a) return 0;
         if (c >= b) return len;
-        long long x = (long long)((c - a) / (b - a) * (double)len) / 64 * 64;
+        long long x = (long long)((c - a) / (b - a) * (double)len) / 128 * 128;
         return x < 0 ? 0 : (x > len ? len : x);
     }
 };
@@ -528,8 +529,8 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
             for (int i = 0; i < 4; ++i) {
                 const bool q = nfw > 0 && Wt[i] <= kFineWarm && L[i] >= 2 * nfw * kFineChunk;
                 nf[i] = q ? nfw : 0;
-                // bulk: the tokens before the first fine chunk (a multiple of 64)
-                const long long b = q ? (L[i] - nfw * kFineChunk) / 64 * 64 : L[i];
+                // bulk: the tokens before the first fine chunk (a multiple of 128)
+                const long long b = q ? (L[i] - nfw * kFineChunk) / 128 * 128 : L[i];
                 const int j = 4 * lane0 + i;
                 if (j < pw) bulk[j] = b;
                 L[i] = b;
@@ -641,37 +642,10 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
                 for (int v = 0; v < 16; ++v) S[db][v] = 0.f;
         }
 
-        // warm-up: state-only steps over [t0w, t0) (whole sub-blocks)
+        // this piece's rows: a warm-up over [t0w, t0) (whole sub-blocks, an
+        // even number), then its tokens
         const long long warm = uniform64(pc.warm);
         const uint16_t *kw = uniform_ptr(pc.k), *vw = uniform_ptr(pc.v);
-        if (warm > 0) {
-            const long long nw = warm / C;
-            const float bdw = fast_exp2(-s2 * (float)C);
-            Stage<false> w0, w1;
-            auto wpre = [&](Stage<false> &st, long long c) {
-                const long long off = (c < nw ? c : nw - 1) * C * (long long)ts;
-                st.load(nullptr, kw + off, vw + off, ts, C, tid);
-            };
-            auto wstep = [&](long long c, Stage<false> &st) {
-                __builtin_amdgcn_sched_barrier(0);
-                __syncthreads();
-                st.template store<true>(nullptr, Ks, nullptr, Vds, C, s2, tid);
-                wpre(st, c + 2);
-                __syncthreads();
-                state_update(S, Ks, Vds, bdw, qh, cq, lane);
-            };
-            wpre(w0, 0);
-            wpre(w1, 1);
-            long long c = 0;
-            for (; c + 1 < nw; c += 2) {
-                wstep(c, w0);
-                wstep(c + 1, w1);
-            }
-            if (c < nw) wstep(c, w0);
-            __syncthreads();  // the last warm-up reads of Ks, Vds are done
-        }
-        write_state_t(Sts[0], S, qh, cq, lane);
-
         const long long len = uniform64(pc.len);
         const uint16_t *qg = uniform_ptr(pc.q);
         const uint16_t *kg = kw + warm * ts, *vg = vw + warm * ts;
@@ -683,6 +657,59 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
         if (NG && tid < D / 4)
             *reinterpret_cast<float4 *>(Wn + 4 * tid) = *reinterpret_cast<const float4 *>(uniform_ptr(pc.nw) + 4 * tid);
 
+        // Two register stages: sub-block c is staged in st[c % 2] and its loads
+        // are issued two sub-blocks ahead, so about 96 KiB of loads are in flight
+        // per CU.
+        Stage<true> st0, st1;
+        const long long nfull = len / C;
+        const int tail = (int)(len - nfull * C);
+        const long long nchunks = nfull + (tail > 0);
+        auto chunk_len = [&](long long c) { return c < nfull ? C : tail; };
+        auto prefetch = [&](Stage<true> &st, long long c) {
+            // Past the end the same loads read one row of the last sub-block again
+            // (row stride 0; ignored): the count of loads stays fixed, so the
+            // compiler's waits stay exact, and almost nothing leaves HBM (a
+            // re-read of whole sub-blocks cost about 3% of the call's traffic).
+            const bool in = c < nchunks;
+            const long long cn = in ? c : nchunks - 1;
+            const long long off = cn * C * (long long)ts;
+            st.load(qg + off, kg + off, vg + off, in ? ts : 0, in ? chunk_len(cn) : C, tid);
+        };
+        if (warm > 0) {  // state-only steps, with their own two stages
+            // even: pieces start at multiples of 128 tokens and warm_len is one
+            const long long nw = warm / C;
+            const float bdw = fast_exp2(-s2 * (float)C);
+            Stage<false> w0, w1;
+            auto wpre = [&](Stage<false> &st, long long c) {
+                const long long off = c * C * (long long)ts;
+                st.load(nullptr, kw + off, vw + off, ts, C, tid);
+            };
+            auto wstep = [&](Stage<false> &st, auto &&issue) {
+                __builtin_amdgcn_sched_barrier(0);
+                __syncthreads();
+                st.template store<true>(nullptr, Ks, nullptr, Vds, C, s2, tid);
+                issue();
+                __syncthreads();
+                state_update(S, Ks, Vds, bdw, qh, cq, lane);
+            };
+            wpre(w0, 0);
+            wpre(w1, 1);
+            long long c = 0;
+            for (; c + 2 < nw; c += 2) {
+                wstep(w0, [&] { wpre(w0, c + 2); });
+                wstep(w1, [&] { wpre(w1, c + 3); });
+            }
+            // the last two warm-up steps issue the first two token sub-blocks'
+            // loads (the same two loads, in the same order, as without a warm-up)
+            wstep(w0, [&] { prefetch(st0, 0); });
+            wstep(w1, [&] { prefetch(st1, 1); });
+            __syncthreads();  // the last warm-up reads of Ks, Vds are done
+        } else if (nchunks > 0) {
+            prefetch(st0, 0);
+            prefetch(st1, 1);
+        }
+        write_state_t(Sts[0], S, qh, cq, lane);
+
         // loop-invariant decay factors
         const int qpos = 32 * qh + r32;                       // query row of this lane's outputs
         const float dq = fast_exp2(-s2 * (float)(qpos + 1));  // d_q for that row
@@ -693,25 +720,6 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
         for (int v = 0; v < 16; ++v) {
             const int diff = (32 * qb + r32) - (32 * kb + 8 * (v >> 2) + 4 * hf + (v & 3));
             dscore[v] = masked_decay(diff, s2);
-        }
-
-        // Two register stages: sub-block c is staged in st[c % 2] and its loads
-        // are issued two sub-blocks ahead, so about 96 KiB of loads are in flight
-        // per CU.
-        Stage<true> st0, st1;
-        const long long nfull = len / C;
-        const int tail = (int)(len - nfull * C);
-        const long long nchunks = nfull + (tail > 0);
-        auto chunk_len = [&](long long c) { return c < nfull ? C : tail; };
-        auto prefetch = [&](Stage<true> &st, long long c) {
-            // past the end, re-read the last sub-block (ignored) to keep the count fixed
-            const long long cn = c < nchunks ? c : nchunks - 1;
-            const long long off = cn * C * (long long)ts;
-            st.load(qg + off, kg + off, vg + off, ts, chunk_len(cn), tid);
-        };
-        if (nchunks > 0) {
-            prefetch(st0, 0);
-            prefetch(st1, 1);
         }
 
         int cur = 0;

@@ -340,13 +340,15 @@ __device__ __forceinline__ bool fix_head(float s2, long long seg_len, int osz) {
 // zero state; from S_0 when the sequence starts within them), by state-only
 // steps: the terms older than W tokens are below 2^-kFixExp of their scale, as
 // with the correction above, but no output needs a second pass. W is rounded up
-// to whole 64-token sub-blocks; a head whose W is shorter than a segment takes
-// this route, the others the pre-pass.
+// to whole pairs of 64-token sub-blocks (with pieces starting at multiples of
+// 128 tokens every warm-up is then an even number of sub-blocks, which the main
+// kernel's warm-up steps rely on); a head whose W is shorter than a segment
+// takes this route, the others the pre-pass.
 __device__ __forceinline__ long long warm_len(float s2) {
     if (!(s2 > 0.f)) return 1LL << 62;  // no decay (or NaN): never forgets
     const float t = kFixExp / s2;
     if (!(t < 1.0e15f)) return 1LL << 62;
-    return ((long long)t + 64) / 64 * 64;
+    return ((long long)t + 128) / 128 * 128;
 }
 
 // Lengths of the sequences of a launch: packed (cu_seqlens, every boundary
