@@ -187,7 +187,7 @@ struct RevStage {
     }
 };
 
-__global__ __launch_bounds__(NT, 4) void rev_piece_kernel(BackwardArgs a, Segmented sp, float *ws) {
+__global__ __launch_bounds__(NT, 2) void rev_piece_kernel(BackwardArgs a, Segmented sp, float *ws) {
     __shared__ __attribute__((aligned(16))) __bf16 Qds[C * D];
     __shared__ __attribute__((aligned(16))) __bf16 Gs[C * D];
 
@@ -236,9 +236,12 @@ __global__ __launch_bounds__(NT, 4) void rev_piece_kernel(BackwardArgs a, Segmen
     const float bd = fast_exp2(-s2 * (float)C);
     RevStage st0, st1;
     auto prefetch = [&](RevStage &st, long long k) {
-        const long long kk = k < nch ? k : nch - 1;
+        // past the piece one row is read again (row stride 0; ignored), so the
+        // count of loads stays fixed without a whole sub-block of traffic
+        const bool in = k < nch;
+        const long long kk = in ? k : nch - 1;
         const long long off = (L - t0 - C * (kk + 1)) * (long long)ts;
-        st.load(qg + off, gg + off, ts, tid);
+        st.load(qg + off, gg + off, in ? ts : 0, tid);
     };
     auto step = [&](long long k, RevStage &st) {
         __syncthreads();
@@ -340,9 +343,12 @@ __global__ __launch_bounds__(NT) void bwd_kv_kernel(BackwardArgs a, Segmented sp
     // sub-block of step p is staged in st[p % 2], loaded two steps ahead
     BwdStage st0, st1;
     auto prefetch = [&](BwdStage &st, long long p) {
-        const long long pp = p < nsteps ? p : nsteps - 1;  // past the start: reload (ignored)
+        // past the start one row is read again (row stride 0; ignored), so the
+        // count of loads stays fixed without a whole sub-block of traffic
+        const bool in = p < nsteps;
+        const long long pp = in ? p : nsteps - 1;
         const long long off = step_start(pp) * (long long)ts;
-        st.load(qg + off, kg + off, vg + off, gg + off, ts, step_len(pp), tid);
+        st.load(qg + off, kg + off, vg + off, gg + off, in ? ts : 0, in ? step_len(pp) : C, tid);
     };
     if (nsteps > 0) {
         prefetch(st0, 0);

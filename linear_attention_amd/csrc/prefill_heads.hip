@@ -190,8 +190,11 @@ __global__ __launch_bounds__(NT, 2) void piece_state_kernel(PrefillArgs a, Segme
     const long long nch = (t1 - t0) / C;  // even, >= 2: all full sub-blocks
     const float bd = fast_exp2(-s2 * (float)C);
     auto prefetch = [&](Stage<false> &st, long long c) {
-        const long long off = (c < nch ? c : nch - 1) * C * (long long)ts;
-        st.load(nullptr, kg + off, vg + off, ts, C, tid);
+        // past the end one row is read again (row stride 0; ignored), so the
+        // count of loads stays fixed without a whole sub-block of traffic
+        const bool in = c < nch;
+        const long long off = (in ? c : nch - 1) * C * (long long)ts;
+        st.load(nullptr, kg + off, vg + off, in ? ts : 0, C, tid);
     };
     auto step = [&](long long c, Stage<false> &st) {
         // Nothing of this sub-block may be scheduled into the previous one:
@@ -987,9 +990,11 @@ __global__ __launch_bounds__(NT) void slice_kernel(PrefillArgs a) {
     const long long nchunks = nfull + (tail > 0);
     auto chunk_len = [&](long long c) { return c < nfull ? C : tail; };
     auto prefetch = [&](SliceStage &st, long long c) {
-        const long long cn = c < nchunks ? c : nchunks - 1;
+        // past the end one row is read again (row stride 0; ignored)
+        const bool in = c < nchunks;
+        const long long cn = in ? c : nchunks - 1;
         const long long off = cn * C * (long long)ts;
-        st.load(qg + off, kg + off, vg + off, ts, chunk_len(cn), tid);
+        st.load(qg + off, kg + off, vg + off, in ? ts : 0, in ? chunk_len(cn) : C, tid);
     };
     if (nchunks > 0) {
         prefetch(st0, 0);
