@@ -276,7 +276,7 @@ __device__ constexpr double warm_cost() {
 // them in the pair's records (warm_records), from which the finishing pass
 // restores them in the later tokens.
 constexpr double kFineFrac = 0.15;
-constexpr long long kFineWarm = 128, kFineChunk = 512;
+constexpr long long kFineWarm = 128, kFineChunk = 768;
 static_assert(kFineChunk % 128 == 0, "pieces start at multiples of 128 tokens");
 struct WarmCut {
     const double *cpre;  // [nwarm pairs + 1] prefix sums of C
@@ -521,11 +521,23 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
             for (int o = 32; o >= 1; o >>= 1) lsum += __shfl_xor(lsum, o);
             // fine chunks: kFineFrac of all warm tokens, nf from each pair that
             // qualifies (at first count) and holds at least 2 nf chunks
+            // (capped at half the longest such pair, so that a large fraction
+            // does not leave every pair out)
             int nq0 = 0;
+            long long lmax = 0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) nq0 += Wt[i] <= kFineWarm && L[i] >= 2 * kFineChunk;
-            for (int o = 32; o >= 1; o >>= 1) nq0 += __shfl_xor(nq0, o);
-            const long long nfw = nq0 > 0 ? (long long)(kFineFrac * lsum / ((double)nq0 * (double)kFineChunk)) : 0;
+            for (int i = 0; i < 4; ++i)
+                if (Wt[i] <= kFineWarm && L[i] >= 2 * kFineChunk) {
+                    ++nq0;
+                    lmax = L[i] > lmax ? L[i] : lmax;
+                }
+            for (int o = 32; o >= 1; o >>= 1) {
+                nq0 += __shfl_xor(nq0, o);
+                const long long y = __shfl_xor(lmax, o);
+                lmax = y > lmax ? y : lmax;
+            }
+            long long nfw = nq0 > 0 ? (long long)(kFineFrac * lsum / ((double)nq0 * (double)kFineChunk)) : 0;
+            if (nfw > lmax / (2 * kFineChunk)) nfw = lmax / (2 * kFineChunk);
             double bsum = 0.0;
             int nrun = 0;
 #pragma unroll
