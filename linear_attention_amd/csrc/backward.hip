@@ -155,13 +155,18 @@ struct BwdStage {
 // ---------------------------------------------------------------------------
 // Long sequences with few (sequence, head) pairs are split as in the forward,
 // in mirrored token order (position t' = L - 1 - t): segment g covers real
-// tokens [L - (g+1) seg_len, L - g seg_len) (the last one starts at 0), and the
-// first (segments-1) segments from the end are cut into pre-pass pieces. In
+// tokens [L - (g+1) seg_len, L - g seg_len) (the last one starts at 0). In
 // these coordinates the carry R composes exactly like the forward state, with
-// dS in place of S_0, so the forward's combine kernel gives every segment its
-// starting carry. A piece's contribution, from zero at its real end p1 back to
-// its real start p0, is sum_i e^{-s(i - p0 + 1)} q_i^T dO_i: the carry update
-// over the piece's sub-blocks walked backward.
+// dS in place of S_0, so the forward's two routes carry over:
+//  * pre-pass heads: the first (segments-1) segments from the end are cut into
+//    pieces; a piece's contribution, from zero at its real end p1 back to its
+//    real start p0, is sum_i e^{-s(i - p0 + 1)} q_i^T dO_i (the carry update
+//    over the piece's sub-blocks walked backward), and the forward's combine
+//    kernel gives every segment its starting carry;
+//  * the other heads: warm-up ranges balanced by cost, then fine chunks (the
+//    forward's plan, tiles.h), each rebuilding its starting carry by carry-only
+//    steps over the q, dO rows of the W tokens after its real end (from zero;
+//    from dS when the window reaches the end of the sequence).
 struct RevStage {
     uint4 q[2], g[2];
 
@@ -174,13 +179,14 @@ struct RevStage {
             g[i] = stream_load16(gg + row);
         }
     }
-    // Q ⊙ d_q (d_q[t] = e^{-s(t+1)}) and dO, full sub-blocks only
+    // Q ⊙ d_q (d_q[t] = e^{-s(t+1)}) and dO in layout Lay, full sub-blocks only
+    template <typename Lay>
     __device__ void store(__bf16 *Qds, __bf16 *Gs, float s2, int tid) {
         const int seg = tid & 15;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int t = (tid >> 4) + 32 * i;
-            const int off = L128::off(t, 8 * seg);
+            const int off = Lay::off(t, 8 * seg);
             *reinterpret_cast<uint4 *>(Qds + off) = scale_bf16x8(q[i], fast_exp2(-s2 * (float)(t + 1)));
             *reinterpret_cast<uint4 *>(Gs + off) = g[i];
         }
@@ -190,25 +196,32 @@ struct RevStage {
 __global__ __launch_bounds__(NT, 2) void rev_piece_kernel(BackwardArgs a, Segmented sp, float *ws) {
     __shared__ __attribute__((aligned(16))) __bf16 Qds[C * D];
     __shared__ __attribute__((aligned(16))) __bf16 Gs[C * D];
+    __shared__ short heads_pre[kMaxPairs], heads_warm[kMaxPairs];
 
-    // groups of kgr pieces, numbered as in the forward pre-pass
-    const int kgr = prepass_group(a.slopes, a.heads, a.units, sp);
-    const int gph = (sp.pieces + kgr - 1) / kgr;
-    if ((int)blockIdx.x >= a.units * a.heads * gph) return;
-    const int j = (blockIdx.x % gph) * kgr;
-    const int uh = blockIdx.x / gph;
-    const int h = uh % a.heads, n = uh / a.heads;
+    // groups of kgr pieces, numbered as in the forward pre-pass: workgroup b
+    // takes group b % gph of the (b / gph)-th pre-pass pair (the launch is
+    // sized for at most kPrepassActive + units * heads working workgroups)
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const Routes rt = split_heads(a.slopes, a.heads, sp, heads_pre, heads_warm, w == 0);
+    if (rt.npre == 0) return;  // every head on warm-up ranges
+    const int kgr = prepass_group_of(rt.npre, a.units, sp);
+    const int gph = (sp.pieces + kgr - 1) / kgr;
+    if ((int)blockIdx.x >= a.units * rt.npre * gph) return;
+    __syncthreads();  // wave 0's head lists are visible
+    const int j = (blockIdx.x % gph) * kgr;
+    const int i = blockIdx.x / gph;
+    const int n = i / rt.npre, h = heads_pre[i % rt.npre];
+    const int uh = n * a.heads + h;
     const int qh = w >> 2, cq = w & 3, r32 = lane & 31, hf = lane >> 5;
 
     const float s2 = a.slopes[h] * LOG2E;
-    if (!takes_prepass(sp, s2)) return;  // local-start segments: no pre-pass
     const int jl = j + kgr - 1 < sp.pieces - 1 ? j + kgr - 1 : sp.pieces - 1;
     // mirrored range [t0, t1) = real tokens [L - t1, L - t0)
     const long long L = a.seqlen;
     const long long t0 = j * sp.piece_len;
     const long long covered = sp.covered(L);
+    if (t0 >= covered) return;
     const long long t1 = t0 + kgr * sp.piece_len < covered ? t0 + kgr * sp.piece_len : covered;
     const int ts = a.heads * D;
     const long long seq = (long long)n * L * a.heads;
@@ -245,7 +258,7 @@ __global__ __launch_bounds__(NT, 2) void rev_piece_kernel(BackwardArgs a, Segmen
     };
     auto step = [&](long long k, RevStage &st) {
         __syncthreads();
-        st.store(Qds, Gs, s2, tid);
+        st.store<L128>(Qds, Gs, s2, tid);
         prefetch(st, k + 2);
         __syncthreads();
         state_update(R, Qds, Gs, bd, qh, cq, lane);
@@ -267,6 +280,82 @@ __global__ __launch_bounds__(NT, 2) void rev_piece_kernel(BackwardArgs a, Segmen
     store_state(jl);
 }
 
+// Warm-up cost of a token against an output token of the reverse pass. By
+// bytes a warm-up token moves its q and dO rows (2 x 256 B) against the q, k,
+// v, dO rows and the dk, dv rows of an output token; the warm-up's steps run
+// below the streaming rate by the forward's factor.
+template <typename OutT>
+__device__ constexpr double bwd_warm_cost() {
+    return 1.25 * 512.0 / (1024.0 + 256.0 * sizeof(OutT));
+}
+
+// A workgroup's current piece (thread 0 lays it out for the others): rows of
+// the piece's first real token, the warm-up's rows (those of the real token
+// just past the piece), its length, the carried-in carry and where the end
+// carry goes.
+struct BwdPiece {
+    const uint16_t *q, *k, *v, *g;
+    void *dk, *dv;
+    const uint16_t *qw, *gw;
+    const float *r_in;    // carried-in carry (nullptr: zero)
+    float *dst;           // end == 1: d_state_in
+    int *rec;             // end == 2: the pair's records
+    long long len, warm;  // tokens of the piece; warm-up tokens (whole sub-blocks)
+    float s2;
+    int ts;
+    int uh;   // -1: no more pieces
+    int cut;  // end == 2: the mirrored token the piece ends at
+    int end;  // 0 nothing, 1 d_state_in, 2 records if the end carry is non-finite
+};
+
+template <typename OutT>
+__device__ BwdPiece next_bwd_piece(const BackwardArgs &a, const Segmented &sp, float *ws, int mode, int k,
+                                   PlanState &ps, const short *heads_pre, const short *heads_warm,
+                                   const double *cpre, const long long *bulk, const short *qlist) {
+    const long long L = a.seqlen;
+    const PieceRange r = next_range(SeqLens{nullptr, (long long)a.units * L, L}, a.heads, sp, mode, k, ps,
+                                    heads_pre, heads_warm, cpre, bulk, qlist, nullptr);
+    BwdPiece p{};
+    p.uh = -1;
+    if (r.n < 0) return p;
+    p.uh = r.n * a.heads + r.h;
+    p.ts = a.heads * D;
+    p.s2 = a.slopes[r.h] * LOG2E;
+    // mirrored [t0, t1) = real [L - t1, L - t0)
+    const long long row0 = (((long long)r.n * L + (L - r.t1)) * a.heads + r.h) * (long long)D;
+    const long long roww = (((long long)r.n * L + (L - r.t0)) * a.heads + r.h) * (long long)D;
+    p.q = static_cast<const uint16_t *>(a.q) + row0;
+    p.k = static_cast<const uint16_t *>(a.k) + row0;
+    p.v = static_cast<const uint16_t *>(a.v) + row0;
+    p.g = static_cast<const uint16_t *>(a.dout) + row0;
+    p.dk = static_cast<OutT *>(a.dk) + row0;
+    p.dv = static_cast<OutT *>(a.dv) + row0;
+    p.qw = static_cast<const uint16_t *>(a.q) + roww;
+    p.gw = static_cast<const uint16_t *>(a.dout) + roww;
+    p.len = r.t1 - r.t0;
+    const size_t sb = (size_t)p.uh * D * D;
+    const float *ds = a.d_state_out ? a.d_state_out + sb : nullptr;
+    if (r.kind == 0) {
+        p.r_in = ds;
+    } else if (r.kind == 1) {
+        p.r_in = sp.start_state(sp.unit(ws, p.uh), r.g);  // the combine pass wrote it (dS for g = 0)
+    } else {
+        const long long wl = warm_len(p.s2);
+        const long long t0w = r.t0 > wl ? r.t0 - wl : 0;
+        p.warm = r.t0 - t0w;
+        if (t0w == 0) p.r_in = ds;  // the warm-up starts at the end of the sequence: exact
+    }
+    if (r.kind == 2 && r.t1 < L) {
+        p.rec = warm_records(sp, ws, p.uh);
+        p.cut = (int)r.t1;
+        p.end = 2;
+    } else if (r.t1 >= L && a.d_state_in) {
+        p.dst = a.d_state_in + sb;
+        p.end = 1;
+    }
+    return p;
+}
+
 template <typename OutT>
 __global__ __launch_bounds__(NT) void bwd_kv_kernel(BackwardArgs a, Segmented sp, float *ws) {
     __shared__ __attribute__((aligned(16))) __bf16 Qs[C * PT];
@@ -278,454 +367,337 @@ __global__ __launch_bounds__(NT) void bwd_kv_kernel(BackwardArgs a, Segmented sp
     __shared__ __attribute__((aligned(16))) __bf16 Bts[C * PS];     // B^T: [i'][i]
     static_assert(sizeof(float) * C * PO <= sizeof(__bf16) * D * PT, "dV staging fits R^T");
     static_assert(sizeof(float) * C * PO <= 2 * sizeof(__bf16) * C * PT, "dK staging fits K, V");
+    __shared__ double cpre[kMaxPairs + 1];
+    __shared__ long long bulk[kMaxPairs];
+    __shared__ short qlist[kMaxPairs];  // pairs that give fine chunks
+    __shared__ int fq[2];               // their count, chunks per pair
+    __shared__ short heads_pre[kMaxPairs], heads_warm[kMaxPairs];
+    __shared__ PlanState ps;
+    __shared__ BwdPiece pc;
+    __shared__ __attribute__((aligned(16))) unsigned char args_lds[sizeof(BackwardArgs)];
+    __shared__ __attribute__((aligned(16))) unsigned char sp_lds[sizeof(Segmented)];
+    __shared__ float *ws_lds;
     __bf16 *Ks = KVs[0], *Vs = KVs[1];
 
-    const int g = blockIdx.x % sp.segments;  // mirrored segment (0 = the end of the sequence)
-    const int uh = blockIdx.x / sp.segments;
-    const int h = uh % a.heads, n = uh / a.heads;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int qh = w >> 2, cq = w & 3, r32 = lane & 31, hf = lane >> 5;
+    const int segments = sp.segments;
+    // thread indices of the set-up (each piece recomputes its own, below)
+    const int t0id = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(t0id >> 6);
+    if (t0id == 0) {
+        *reinterpret_cast<BackwardArgs *>(args_lds) = a;
+        *reinterpret_cast<Segmented *>(sp_lds) = sp;
+        ws_lds = ws;
+    }
 
-    // real tokens [seg_lo, seg_hi) of this segment
-    const long long L = a.seqlen;
-    const long long seg_hi = L - g * sp.seg_len;
-    const long long seg_lo = seg_hi - sp.seg_len > 0 && g + 1 < sp.segments ? seg_hi - sp.seg_len : 0;
-    const long long len = seg_hi - seg_lo;
-    const int ts = a.heads * D;
-    const long long base = (((long long)n * L + seg_lo) * a.heads + h) * (long long)D;
-    const uint16_t *qg = static_cast<const uint16_t *>(a.q) + base;
-    const uint16_t *kg = static_cast<const uint16_t *>(a.k) + base;
-    const uint16_t *vg = static_cast<const uint16_t *>(a.v) + base;
-    const uint16_t *gg = static_cast<const uint16_t *>(a.dout) + base;
-    OutT *dkg = static_cast<OutT *>(a.dk) + base;
-    OutT *dvg = static_cast<OutT *>(a.dv) + base;
-    const float s2 = a.slopes[h] * LOG2E;
+    // ---- this workgroup's work: pieces (pair uh, mirrored tokens [t0, t1)),
+    // each starting from the combine pass's start carry, dS, zero, and a warm-up
+    int mode = 0;  // 0: one pair, whole (no segments); 1: one pre-pass segment; 2: warm ranges
+    if (segments > 1) {
+        const Routes rt = split_heads(a.slopes, a.heads, sp, heads_pre, heads_warm, w == 0);
+        __syncthreads();  // wave 0's head lists are visible
+        const long long pre_wgs = (long long)a.units * rt.npre * segments;
+        mode = (long long)blockIdx.x < pre_wgs ? 1 : 2;
+        const int pw = a.units * rt.nwarm;  // warm pairs
+        if (mode == 2 && w == 0)
+            warm_plan(SeqLens{nullptr, (long long)a.units * a.seqlen, a.seqlen}, a.slopes, heads_warm, rt.nwarm,
+                      pw, (double)pw * segments, bwd_warm_cost<OutT>(), cpre, bulk, qlist, fq);
+        __syncthreads();  // cpre, bulk, qlist and fq are visible
+        if (t0id == 0) {
+            ps.npre = rt.npre;
+            ps.nwarm = rt.nwarm;
+            ps.pw = pw;
+            if (mode == 2)
+                warm_plan_state(ps, cpre, fq, pw, segments, (int)((long long)blockIdx.x - pre_wgs),
+                                warm_records(sp, ws, heads_warm[0]) + kFineCounter);  // in the first warm pair's records
+        }
+    }
 
-    // ---- carry from the right of the sequence: dS (or zero)
+    // ---- the pieces
     f32x16 R[2];
-    auto sidx = [&](int db, int v) {
-        return (64 * qh + 32 * db + 8 * (v >> 2) + 4 * hf + (v & 3)) * D + 32 * cq + r32;
-    };
-    // local-start segments: segment 0 (the sequence end) starts from dS, the
-    // others from zero (the correction pass adds their carried-in term)
-    const bool fix = sp.segments > 1 && fix_head(s2, sp.seg_len, sp.fix_osz);
-    const float *r_in = sp.segments > 1 && !fix
-                            ? sp.start_state(sp.unit(ws, uh), g)
-                            : ((sp.segments == 1 || g == 0) && a.d_state_out ? a.d_state_out + (size_t)uh * D * D
-                                                                              : nullptr);
-    if (r_in) {
+    for (int k = 0;; ++k) {
+        // the thread index is made opaque once per piece (lane-dependent
+        // addresses are recomputed in each piece instead of staying in
+        // registers through every piece's warm-up and set-up)
+        const int tid = opaque((int)threadIdx.x), lane = tid & 63;
+        const int qh = w >> 2, cq = w & 3, r32 = lane & 31, hf = lane >> 5;
+        auto sidx = [&](int db, int v) {
+            return (64 * qh + 32 * db + 8 * (v >> 2) + 4 * hf + (v & 3)) * D + 32 * cq + r32;
+        };
+        __syncthreads();  // the previous piece is done with the tiles, R^T and pc
+        if (tid == 0)
+            pc = next_bwd_piece<OutT>(*reinterpret_cast<const BackwardArgs *>(args_lds),
+                                      *reinterpret_cast<const Segmented *>(sp_lds), ws_lds, mode, k, ps, heads_pre,
+                                      heads_warm, cpre, bulk, qlist);
+        __syncthreads();
+        const int uh = __builtin_amdgcn_readfirstlane(pc.uh);
+        if (uh < 0) break;
+        const int ts = __builtin_amdgcn_readfirstlane(pc.ts);
+        const float s2 = uniformf(pc.s2);
+        const float *r_in = uniform_ptr(pc.r_in);
+        if (r_in) {
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
+            for (int db = 0; db < 2; ++db)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) R[db][v] = r_in[sidx(db, v)];
-    } else {
+                for (int v = 0; v < 16; ++v) R[db][v] = r_in[sidx(db, v)];
+        } else {
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
+            for (int db = 0; db < 2; ++db)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) R[db][v] = 0.f;
-    }
-    write_rt(Rts, R, qh, cq, lane);
+                for (int v = 0; v < 16; ++v) R[db][v] = 0.f;
+        }
+        const long long len = uniform64(pc.len), warm = uniform64(pc.warm);
+        const uint16_t *qg = uniform_ptr(pc.q), *kg = uniform_ptr(pc.k), *vg = uniform_ptr(pc.v);
+        const uint16_t *gg = uniform_ptr(pc.g);
+        OutT *dkg = static_cast<OutT *>(uniform_ptr(pc.dk));
+        OutT *dvg = static_cast<OutT *>(uniform_ptr(pc.dv));
 
-    // score blocks: waves 0..2 A, waves 3..5 B; block (I, I') in {(0,0), (0,1), (1,1)}
-    const bool scorer = w < 6;
-    const int blk = w % 3;
-    const int sI = blk == 2 ? 1 : 0, sJ = blk == 0 ? 0 : 1;  // rows i in 32sI.., columns i' in 32sJ..
+        // score blocks: waves 0..2 A, waves 3..5 B; block (I, I') in {(0,0), (0,1), (1,1)}
+        const bool scorer = w < 6;
+        const int blk = w % 3;
+        const int sI = blk == 2 ? 1 : 0, sJ = blk == 0 ? 0 : 1;  // rows i in 32sI.., columns i' in 32sJ..
 
-    // Sub-blocks are anchored at the end of the sequence: step p < nfull covers
-    // tokens [len - 64(p+1), len - 64p); a short first block [0, len mod 64),
-    // if any, is the last step (the block form holds for any partition).
-    const long long nfull = len / C;
-    const int head_len = (int)(len - nfull * C);
-    const long long nsteps = nfull + (head_len > 0);
-    auto step_start = [&](long long p) { return p < nfull ? len - C * (p + 1) : 0; };
-    auto step_len = [&](long long p) { return p < nfull ? C : head_len; };
-    // sub-block of step p is staged in st[p % 2], loaded two steps ahead
-    BwdStage st0, st1;
-    auto prefetch = [&](BwdStage &st, long long p) {
-        // past the start one row is read again (row stride 0; ignored), so the
-        // count of loads stays fixed without a whole sub-block of traffic
-        const bool in = p < nsteps;
-        const long long pp = in ? p : nsteps - 1;
-        const long long off = step_start(pp) * (long long)ts;
-        st.load(qg + off, kg + off, vg + off, gg + off, in ? ts : 0, in ? step_len(pp) : C, tid);
-    };
-    if (nsteps > 0) {
-        prefetch(st0, 0);
-        prefetch(st1, 1);
-    }
-
-    auto step = [&](long long p, int m, auto full, BwdStage &st) {
-        constexpr bool FULL = decltype(full)::value;
-        const long long t0 = step_start(p);
-        st.template store<FULL>(Qs, Ks, Vs, Gs, Qds, m, s2, tid);
-        prefetch(st, p + 2);
-        __syncthreads();  // (B) tiles and R^T visible
-
-        if (scorer) {
-            // A^T or B^T block: C[i][i'] = x_i . y_i' masked to i' >= i and decayed,
-            // stored as [i'][i]
-            const __bf16 *X = w < 3 ? Ks : Vs;
-            const __bf16 *Y = w < 3 ? Qs : Gs;
-            __bf16 *T = w < 3 ? Ats : Bts;
-            f32x16 sc;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) sc[v] = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks)
-                sc = mma(ld_op<LT>(X, 32 * sI, 16 * ks, lane), ld_op<LT>(Y, 32 * sJ, 16 * ks, lane), sc);
-            // decay of C[i][i'], e^{-s(i' - i)} for i' >= i, recomputed every step
-            // from an opaque copy of the lane: kept across the loop these 16
-            // values were spilled, and each reload waited for every load in
-            // flight, the prefetch of the sub-blocks ahead included
-            int lo = lane;
-            asm volatile("" : "+v"(lo));
-            float dscore[16];
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int diff = (32 * sJ + (lo & 31)) - (32 * sI + 8 * (v >> 2) + 4 * (lo >> 5) + (v & 3));
-                dscore[v] = masked_decay(diff, s2);
+        // Sub-blocks are anchored at the real end of the piece: step p < nfull
+        // covers tokens [len - 64(p+1), len - 64p); a short first block
+        // [0, len mod 64), if any, is the last step (only the piece that holds
+        // token 0 has one; the block form holds for any partition).
+        const long long nfull = len / C;
+        const int head_len = (int)(len - nfull * C);
+        const long long nsteps = nfull + (head_len > 0);
+        auto step_start = [&](long long p) { return p < nfull ? len - C * (p + 1) : 0; };
+        auto step_len = [&](long long p) { return p < nfull ? C : head_len; };
+        // sub-block of step p is staged in st[p % 2], loaded two steps ahead
+        BwdStage st0, st1;
+        auto prefetch = [&](BwdStage &st, long long p) {
+            // past the start one row is read again (row stride 0; ignored), so the
+            // count of loads stays fixed without a whole sub-block of traffic
+            const bool in = p < nsteps;
+            const long long pp = in ? p : nsteps - 1;
+            const long long off = step_start(pp) * (long long)ts;
+            st.load(qg + off, kg + off, vg + off, gg + off, in ? ts : 0, in ? step_len(pp) : C, tid);
+        };
+        if (warm > 0) {
+            // carry-only steps over the warm-up rows, from the last of them
+            // down (an even number of whole sub-blocks), with their own stages
+            const uint16_t *qw = uniform_ptr(pc.qw), *gw = uniform_ptr(pc.gw);
+            const long long nw = warm / C;
+            const float bdw = fast_exp2(-s2 * (float)C);
+            RevStage w0, w1;
+            auto wpre = [&](RevStage &st, long long c) {
+                const long long off = (warm - C * (c + 1)) * (long long)ts;
+                st.load(qw + off, gw + off, ts, tid);
+            };
+            auto wstep = [&](RevStage &st, auto &&issue) {
+                __builtin_amdgcn_sched_barrier(0);
+                __syncthreads();
+                st.store<LT>(Qds, Gs, s2, tid);
+                issue();
+                __syncthreads();
+                carry_update(R, Qds, Gs, bdw, qh, cq, lane);
+            };
+            wpre(w0, 0);
+            wpre(w1, 1);
+            long long c = 0;
+            for (; c + 2 < nw; c += 2) {
+                wstep(w0, [&] { wpre(w0, c + 2); });
+                wstep(w1, [&] { wpre(w1, c + 3); });
             }
-#pragma unroll
-            for (int gv = 0; gv < 4; ++gv) {
-                bf16x4 pv;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) pv[r] = static_cast<__bf16>(mask_mul(sc[4 * gv + r], dscore[4 * gv + r]));
-                *reinterpret_cast<bf16x4 *>(T + LS::off(32 * sJ + r32, 32 * sI + 8 * gv + 4 * hf)) = pv;
-            }
+            // the last two warm-up steps issue the first two sub-blocks' loads
+            wstep(w0, [&] { prefetch(st0, 0); });
+            wstep(w1, [&] { prefetch(st1, 1); });
+            __syncthreads();  // the last warm-up reads of Qds, Gs are done
+        } else if (nsteps > 0) {
+            prefetch(st0, 0);
+            prefetch(st1, 1);
         }
-
-        // inter products, scaled per token i = 32 qh + r32 by d_r[i] = e^{-s(m-1-i)}
-        f32x16 dv, dk;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) dv[v] = dk[v] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-            dv = mma(ld_op<LT>(Rts, 32 * cq, 16 * ks, lane), ld_op<LT>(Ks, 32 * qh, 16 * ks, lane), dv);
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-            dk = mma(ld_op_t<LT>(Rts, 32 * cq, 16 * ks, lane), ld_op<LT>(Vs, 32 * qh, 16 * ks, lane), dk);
-        const int ti = 32 * qh + r32;
-        const float dr = ti < m ? fast_exp2(-s2 * (float)(m - 1 - ti)) : 0.f;
-        dv *= dr;
-        dk *= dr;
-
-        // R <- e^{-s m} R + (Q ⊙ d_q)^T dO
-        carry_update(R, Qds, Gs, fast_exp2(-s2 * (float)m), qh, cq, lane);
-        __syncthreads();  // (C) A^T, B^T visible; reads of R^T, K, V, Q ⊙ d_q done
-
-        // intra products over i' >= 32 qh
-#pragma unroll
-        for (int ks = 0; ks < C / 16; ++ks) {
-            if (ks < 2 * qh) continue;
-            dv = mma(ld_op_t<LT>(Gs, 32 * cq, 16 * ks, lane), ld_op_t<LS>(Ats, 32 * qh, 16 * ks, lane), dv);
-        }
-#pragma unroll
-        for (int ks = 0; ks < C / 16; ++ks) {
-            if (ks < 2 * qh) continue;
-            dk = mma(ld_op_t<LT>(Qs, 32 * cq, 16 * ks, lane), ld_op_t<LS>(Bts, 32 * qh, 16 * ks, lane), dk);
-        }
-        float *dVs = reinterpret_cast<float *>(Rts);
-        float *dKs = reinterpret_cast<float *>(KVs[0]);
-        stage_rows(dVs, dv, qh, cq, lane);
-        stage_rows(dKs, dk, qh, cq, lane);
-        __syncthreads();  // (D) dV, dK staged
-        put_rows<FULL>(dvg + t0 * (long long)ts, ts, dVs, m, tid);
-        put_rows<FULL>(dkg + t0 * (long long)ts, ts, dKs, m, tid);
-        __syncthreads();  // (E) staging read; R^T and the next tiles may be written
         write_rt(Rts, R, qh, cq, lane);
-    };
-    long long p = 0;
-    for (; p + 1 < nfull; p += 2) {
-        step(p, C, std::true_type{}, st0);
-        step(p + 1, C, std::true_type{}, st1);
-    }
-    if (p < nfull) step(p++, C, std::true_type{}, st0);
-    if (head_len > 0) {  // staged in st[nfull % 2]
-        if (nfull & 1)
-            step(p, head_len, std::false_type{}, st1);
-        else
-            step(p, head_len, std::false_type{}, st0);
-    }
 
-    if (fix) {  // end carry of this local-start segment, for the chain
-        float *u = sp.unit(ws, uh);
-        float *dst = sp.start_state(u, g);
+        auto step = [&](long long p, int m, auto full, BwdStage &st) {
+            constexpr bool FULL = decltype(full)::value;
+            const long long t0 = step_start(p);
+            st.template store<FULL>(Qs, Ks, Vs, Gs, Qds, m, s2, tid);
+            prefetch(st, p + 2);
+            __syncthreads();  // (B) tiles and R^T visible
+
+            if (scorer) {
+                // A^T or B^T block: C[i][i'] = x_i . y_i' masked to i' >= i and decayed,
+                // stored as [i'][i]
+                const __bf16 *X = w < 3 ? Ks : Vs;
+                const __bf16 *Y = w < 3 ? Qs : Gs;
+                __bf16 *T = w < 3 ? Ats : Bts;
+                f32x16 sc;
+    #pragma unroll
+                for (int v = 0; v < 16; ++v) sc[v] = 0.f;
+    #pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks)
+                    sc = mma(ld_op<LT>(X, 32 * sI, 16 * ks, lane), ld_op<LT>(Y, 32 * sJ, 16 * ks, lane), sc);
+                // decay of C[i][i'], e^{-s(i' - i)} for i' >= i, recomputed every step
+                // from an opaque copy of the lane: kept across the loop these 16
+                // values were spilled, and each reload waited for every load in
+                // flight, the prefetch of the sub-blocks ahead included
+                int lo = lane;
+                asm volatile("" : "+v"(lo));
+                float dscore[16];
+    #pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int diff = (32 * sJ + (lo & 31)) - (32 * sI + 8 * (v >> 2) + 4 * (lo >> 5) + (v & 3));
+                    dscore[v] = masked_decay(diff, s2);
+                }
+    #pragma unroll
+                for (int gv = 0; gv < 4; ++gv) {
+                    bf16x4 pv;
+    #pragma unroll
+                    for (int r = 0; r < 4; ++r) pv[r] = static_cast<__bf16>(mask_mul(sc[4 * gv + r], dscore[4 * gv + r]));
+                    *reinterpret_cast<bf16x4 *>(T + LS::off(32 * sJ + r32, 32 * sI + 8 * gv + 4 * hf)) = pv;
+                }
+            }
+
+            // inter products, scaled per token i = 32 qh + r32 by d_r[i] = e^{-s(m-1-i)}
+            f32x16 dv, dk;
+    #pragma unroll
+            for (int v = 0; v < 16; ++v) dv[v] = dk[v] = 0.f;
+    #pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks)
+                dv = mma(ld_op<LT>(Rts, 32 * cq, 16 * ks, lane), ld_op<LT>(Ks, 32 * qh, 16 * ks, lane), dv);
+    #pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks)
+                dk = mma(ld_op_t<LT>(Rts, 32 * cq, 16 * ks, lane), ld_op<LT>(Vs, 32 * qh, 16 * ks, lane), dk);
+            const int ti = 32 * qh + r32;
+            const float dr = ti < m ? fast_exp2(-s2 * (float)(m - 1 - ti)) : 0.f;
+            dv *= dr;
+            dk *= dr;
+
+            // R <- e^{-s m} R + (Q ⊙ d_q)^T dO
+            carry_update(R, Qds, Gs, fast_exp2(-s2 * (float)m), qh, cq, lane);
+            __syncthreads();  // (C) A^T, B^T visible; reads of R^T, K, V, Q ⊙ d_q done
+
+            // intra products over i' >= 32 qh
+    #pragma unroll
+            for (int ks = 0; ks < C / 16; ++ks) {
+                if (ks < 2 * qh) continue;
+                dv = mma(ld_op_t<LT>(Gs, 32 * cq, 16 * ks, lane), ld_op_t<LS>(Ats, 32 * qh, 16 * ks, lane), dv);
+            }
+    #pragma unroll
+            for (int ks = 0; ks < C / 16; ++ks) {
+                if (ks < 2 * qh) continue;
+                dk = mma(ld_op_t<LT>(Qs, 32 * cq, 16 * ks, lane), ld_op_t<LS>(Bts, 32 * qh, 16 * ks, lane), dk);
+            }
+            float *dVs = reinterpret_cast<float *>(Rts);
+            float *dKs = reinterpret_cast<float *>(KVs[0]);
+            stage_rows(dVs, dv, qh, cq, lane);
+            stage_rows(dKs, dk, qh, cq, lane);
+            __syncthreads();  // (D) dV, dK staged
+            put_rows<FULL>(dvg + t0 * (long long)ts, ts, dVs, m, tid);
+            put_rows<FULL>(dkg + t0 * (long long)ts, ts, dKs, m, tid);
+            __syncthreads();  // (E) staging read; R^T and the next tiles may be written
+            write_rt(Rts, R, qh, cq, lane);
+        };
+        long long p = 0;
+        for (; p + 1 < nfull; p += 2) {
+            step(p, C, std::true_type{}, st0);
+            step(p + 1, C, std::true_type{}, st1);
+        }
+        if (p < nfull) step(p++, C, std::true_type{}, st0);
+        if (head_len > 0) {  // staged in st[nfull % 2]
+            if (nfull & 1)
+                step(p, head_len, std::false_type{}, st1);
+            else
+                step(p, head_len, std::false_type{}, st0);
+        }
+
+        // the end carry (pc is unchanged until the next piece)
+        const int end = __builtin_amdgcn_readfirstlane(pc.end);
+        if (end == 1) {  // the piece holds token 0: d_state_in
+            float *dst = uniform_ptr(pc.dst);
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
+            for (int db = 0; db < 2; ++db)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) dst[sidx(db, v)] = R[db][v];
-        if (g + 1 < sp.segments) flag_end_state(end_flags(sp, u, g), R, w, lane);
-    } else if (a.d_state_in && g == sp.segments - 1) {  // the segment holding token 0
-        float *dst = a.d_state_in + (size_t)uh * D * D;
+                for (int v = 0; v < 16; ++v) dst[sidx(db, v)] = R[db][v];
+        } else if (end == 2) {  // a warm piece ending inside its pair: record a NaN or Inf
+            bool bad = false;
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
+            for (int db = 0; db < 2; ++db)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) dst[sidx(db, v)] = R[db][v];
+                for (int v = 0; v < 16; ++v) bad |= nonfinite(R[db][v]);
+            if (bad) {  // rare: entry (r, c) of R poisons dk column r and dv column c
+                int *rec = pc.rec;
+                const int cut = pc.cut;
+#pragma unroll
+                for (int db = 0; db < 2; ++db)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        if (nonfinite(R[db][v])) {
+                            const int e = sidx(db, v);
+                            atomicOr(reinterpret_cast<unsigned *>(rec + kRecEntBad) + (e >> 5), 1u << (e & 31));
+                            atomicMin(rec + kRecRowCut + e / D, cut);
+                        }
+                atomicMin(rec + kRecColCut + 32 * cq + r32, cut);  // every entry of this thread is in that column
+            }
+        }
     }
 }
 
-// Reverse pass on local-start segments. Mirrored segment g >= 1 started from a
-// zero carry instead of R_in(g), so token t of it, n = seg_hi - 1 - t tokens
-// before its right end, misses e^{-s n} R_in in its gradient of S_t:
-//   dv_t += e^{-s n} k_t R_in,    dk_t += e^{-s n} v_t R_in^T,
-// added here for n <= kFixExp / s2 (past that the factor is below the fp32
-// unit roundoff, 2^-24), in 64-token chunks counted from the right end. As in
-// the forward correction, the chunks of all (unit, head, segment) pairs are
-// numbered in pair order and cut into equal contiguous ranges, consecutive
-// ranges on one XCD; a workgroup forms R_in(g) itself from the end carries E_j
-// the main pass left (R_in(1) = E_0, R_in(j+1) = e^{-s len_j} R_in(j) + E_j)
-// and loads the next chunk's rows before the current chunk's products, which
-// take R_in^T (bf16, LDS) as the operand of the dv term and, through the
-// transposing read, R_in for the dk term. The first `nfinal` workgroups write
-// d_state_in, the final carry, of each local-start head.
-constexpr int kRevFixWorkgroups = 256;  // one per CU (98 KB of LDS); a multiple of 8 (XCDs)
-
-// Rows a thread adds to (loaded ahead of the products): fp32 rows (t/32) + 16j,
-// 4 columns at 4(t%32); bf16 rows (t/16) + 32j, 8 columns at 8(t%16). `out`
-// points at chunk row rlo; rows below rlo read that row and are not stored.
+// Finishing pass of the reverse pass's warm-up route: one workgroup per (unit,
+// head) pair; pairs on the pre-pass route exit at once. A piece that starts
+// inside its pair builds its carry from a window of the tokens after it, so it
+// cannot see a NaN or Inf from beyond that window. In exact arithmetic an entry
+// (r, c) of the carry that is non-finite at some token stays non-finite at
+// every earlier token, and with it dk column r and dv column c of those tokens
+// and entry (r, c) of d_state_in. The pieces that ended inside the pair
+// recorded where their end carries held one (mirrored token t, per row and per
+// column, and the entries); this pass puts NaN in dk column r of every real
+// token below L - (earliest t of row r), likewise in dv by column, and in each
+// flagged entry of d_state_in (the piece holding token 0 has written it).
 template <typename OutT>
-struct RowsFrom;
-template <>
-struct RowsFrom<float> {
-    uint4 y[4];
-    __device__ void load(const float *out, int ts, int rlo, int tid) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = (tid >> 5) + 16 * j;
-            y[j] = *reinterpret_cast<const uint4 *>(out + (unsigned)((row > rlo ? row - rlo : 0) * ts + 4 * (tid & 31)));
-        }
-    }
-    __device__ void add_store(float *out, int ts, const float *Os, int rlo, int tid) const {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = (tid >> 5) + 16 * j, col = 4 * (tid & 31);
-            const float4 x = *reinterpret_cast<const float4 *>(Os + ooff(row, col));
-            if (row >= rlo)
-                *reinterpret_cast<float4 *>(out + (unsigned)((row - rlo) * ts + col)) =
-                    make_float4(__uint_as_float(y[j].x) + x.x, __uint_as_float(y[j].y) + x.y,
-                                __uint_as_float(y[j].z) + x.z, __uint_as_float(y[j].w) + x.w);
-        }
-    }
-};
-template <>
-struct RowsFrom<__bf16> {
-    uint4 y[2];
-    __device__ void load(const __bf16 *out, int ts, int rlo, int tid) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int row = (tid >> 4) + 32 * j;
-            y[j] = *reinterpret_cast<const uint4 *>(out + (unsigned)((row > rlo ? row - rlo : 0) * ts + 8 * (tid & 15)));
-        }
-    }
-    __device__ void add_store(__bf16 *out, int ts, const float *Os, int rlo, int tid) const {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int row = (tid >> 4) + 32 * j, col = 8 * (tid & 15);
-            const float4 x0 = *reinterpret_cast<const float4 *>(Os + ooff(row, col));
-            const float4 x1 = *reinterpret_cast<const float4 *>(Os + ooff(row, col + 4));
-            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-            const uint32_t wv[4] = {y[j].x, y[j].y, y[j].z, y[j].w};
-            uint32_t r[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const __bf16 lo = static_cast<__bf16>(__uint_as_float(wv[i] << 16) + xs[2 * i]);
-                const __bf16 hi = static_cast<__bf16>(__uint_as_float(wv[i] & 0xffff0000u) + xs[2 * i + 1]);
-                uint16_t ulo, uhi;
-                __builtin_memcpy(&ulo, &lo, 2);
-                __builtin_memcpy(&uhi, &hi, 2);
-                r[i] = (uint32_t)ulo | ((uint32_t)uhi << 16);
-            }
-            if (row >= rlo)
-                *reinterpret_cast<uint4 *>(out + (unsigned)((row - rlo) * ts + col)) = make_uint4(r[0], r[1], r[2], r[3]);
-        }
-    }
-};
-
-template <typename OutT>
-__global__ __launch_bounds__(NT) void rev_fix_kernel(BackwardArgs a, Segmented sp, float *ws, int nfinal) {
-    __shared__ __attribute__((aligned(16))) __bf16 Rt[D * D];  // R_in^T
-    __shared__ __attribute__((aligned(16))) __bf16 Kt[C * D];
-    __shared__ __attribute__((aligned(16))) __bf16 Vt[C * D];
-    __shared__ __attribute__((aligned(16))) float Os[C * D];
-    __shared__ long long first[kFixMaxPairs + 1];  // first chunk number of each pair
-    __shared__ long long prows[kFixMaxPairs];       // rows corrected in each pair
-
+__global__ __launch_bounds__(NT) void bwd_finish_kernel(BackwardArgs a, Segmented sp, float *ws) {
+    __shared__ int cuts[2 * D];  // [0, D): dv column c; [D, 2D): dk column r
+    __shared__ int mincut;
     const int tid = threadIdx.x;
-    const long long L = a.seqlen;
-    if ((int)blockIdx.x < nfinal) {  // d_state_in of a local-start head
-        const int uh = blockIdx.x / kFinalSlices;
-        const float s2 = a.slopes[uh % a.heads] * LOG2E;
-        if (!fix_head(s2, sp.seg_len, sp.fix_osz)) return;
-        const int e = 4 * ((blockIdx.x % kFinalSlices) * NT + tid);
-        float *u = sp.unit(ws, uh);
-        float4 acc = *reinterpret_cast<const float4 *>(sp.start_state(u, 0) + e);
-        for (int g = 1; g < sp.segments; ++g) {
-            const float f = fast_exp2(-s2 * (float)seg_len_at(sp, L, g));
-            const float4 x = *reinterpret_cast<const float4 *>(sp.start_state(u, g) + e);
-            acc = make_float4(f * acc.x + x.x, f * acc.y + x.y, f * acc.z + x.z, f * acc.w + x.w);
-        }
-        *reinterpret_cast<float4 *>(a.d_state_in + (size_t)uh * D * D + e) = acc;
-        return;
-    }
-
-    // rows and chunks per pair (the whole segment when its carried-in carry is
-    // non-finite), then the chunks' prefix sums
-    const int gs = sp.segments - 1;
-    const int pairs = a.units * a.heads * gs;
-    long long x = 0;
-    if (tid < pairs) {
-        const int g = 1 + tid % gs, uh = tid / gs;
-        const float s2 = a.slopes[uh % a.heads] * LOG2E;
-        long long rows = 0;
-        if (fix_head(s2, sp.seg_len, sp.fix_osz)) {
-            const long long len = seg_len_at(sp, L, g), fl = fix_len(s2, sp.seg_len) + 1;  // n = 0 .. fix_len
-            rows = start_poisoned(sp, sp.unit(ws, uh), g) || fl > len ? len : fl;
-        }
-        prows[tid] = rows;
-        x = (rows + C - 1) / C;
-    }
-    for (int off = 1; off < kFixMaxPairs; off <<= 1) {
-        if (tid < kFixMaxPairs) first[tid + 1] = x;
-        __syncthreads();
-        if (tid < kFixMaxPairs && tid >= off) x += first[tid + 1 - off];
-        __syncthreads();
-    }
-    if (tid < kFixMaxPairs) first[tid + 1] = x;
-    if (tid == 0) first[0] = 0;
+    const int uh = blockIdx.x, h = uh % a.heads, n = uh / a.heads;
+    if (takes_prepass(sp, a.slopes[h] * LOG2E)) return;
+    const int *rec = warm_records(sp, ws, uh);
+    if (tid == 0) mincut = kNoCut;
     __syncthreads();
-
-    const long long total = uniform64(first[pairs]);
-    const int nwg = gridDim.x - nfinal;
-    const int r = (int)(blockIdx.x % 8) * (nwg / 8) + (int)(blockIdx.x - nfinal) / 8;
-    const long long j0 = total * r / nwg, j1 = total * (r + 1) / nwg;
-    if (j0 >= j1) return;
-
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int qh = w >> 2, cq = w & 3;
-    const int ts = a.heads * D;
-    struct Chunk {
-        const uint16_t *k, *v;
-        OutT *dk, *dv;
-        long long seg_hi, tlo;
-        int rlo, pair, uh, g;
-        float s2;
-    };
-    int p = 0;
-    auto chunk_at = [&](long long j) {
-        while (first[p + 1] <= j) ++p;
-        p = __builtin_amdgcn_readfirstlane(p);
-        Chunk c;
-        c.pair = p;
-        c.uh = p / gs;
-        c.g = 1 + p % gs;
-        const int h = c.uh % a.heads, n = c.uh / a.heads;
-        c.s2 = a.slopes[h] * LOG2E;
-        const long long T = uniform64(prows[p]);
-        c.seg_hi = L - (long long)c.g * sp.seg_len;
-        const long long ci = uniform64(j - first[p]);
-        c.tlo = c.seg_hi - C * (ci + 1);
-        c.rlo = (int)(c.seg_hi - T - c.tlo > 0 ? c.seg_hi - T - c.tlo : 0);
-        // rows below rlo are never touched: the base is the chunk's first
-        // corrected row, and row offsets are taken relative to it
-        const long long off = (((long long)n * L + c.tlo + c.rlo) * a.heads + h) * (long long)D;
-        c.k = static_cast<const uint16_t *>(a.k) + off;
-        c.v = static_cast<const uint16_t *>(a.v) + off;
-        c.dk = static_cast<OutT *>(a.dk) + off;
-        c.dv = static_cast<OutT *>(a.dv) + off;
-        return c;
-    };
-    // loads of a chunk: k, v rows and the dv, dk rows (row r of the chunk at
-    // offset (r - rlo) from the base; rows below rlo read row rlo)
-    struct Loads {
-        uint4 kx[2], vx[2];
-        RowsFrom<OutT> dvr, dkr;
-    };
-    auto load = [&](const Chunk &c, Loads &l, int th) {
+    if (tid < 2 * D) {
+        cuts[tid] = rec[tid < D ? kRecColCut + tid : kRecRowCut + (tid - D)];
+        atomicMin(&mincut, cuts[tid]);
+    }
+    __syncthreads();
+    const int first = mincut;
+    if (first == kNoCut) return;
+    const long long L = a.seqlen;
+    // real rows t < L - cut; 32 threads per row (4 columns each), NT / 32 rows at a time
+    const int col = 4 * (tid & 31);
+    long long vtop[4], ktop[4];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int rr = (th >> 4) + 32 * i;
-            const unsigned o = (unsigned)((rr > c.rlo ? rr - c.rlo : 0) * ts + 8 * (th & 15));
-            l.kx[i] = stream_load16(c.k + o);
-            l.vx[i] = stream_load16(c.v + o);
+    for (int x = 0; x < 4; ++x) {
+        vtop[x] = L - cuts[col + x];
+        ktop[x] = L - cuts[D + col + x];
+    }
+    OutT *dk = static_cast<OutT *>(a.dk), *dv = static_cast<OutT *>(a.dv);
+    for (long long t = tid >> 5; t < L - first; t += NT / 32) {
+        const long long off = (((long long)n * L + t) * a.heads + h) * (long long)D + col;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            if (t < ktop[x]) poison(dk + off + x);
+            if (t < vtop[x]) poison(dv + off + x);
         }
-        l.dvr.load(c.dv, ts, c.rlo, th);
-        l.dkr.load(c.dk, ts, c.rlo, th);
-    };
-    Chunk cur = chunk_at(j0);
-    Loads la;
-    load(cur, la, tid);
-    int loaded = -1;
-    for (long long j = j0; j < j1; ++j) {
-        if (j > j0) __syncthreads();  // the previous chunk's reads of Kt, Vt, Os done
-        int tl = tid;
-        asm volatile("" : "+v"(tl));  // lane offsets recomputed per chunk (not spilled)
-        const int ln = tl & 63;
-        Chunk nxt = cur;
-        Loads lb = la;
-        if (j + 1 < j1) {
-            nxt = chunk_at(j + 1);
-            load(nxt, lb, tl);
-        }
-        if (cur.pair != loaded) {  // R_in(g)^T as bf16 (the last reads of Rt ended before a barrier)
-            const int c = tl & (D - 1), kq = tl >> 7;
-            float *u = sp.unit(ws, cur.uh);
+    }
+    if (a.d_state_in) {
+        const unsigned *bad = reinterpret_cast<const unsigned *>(rec + kRecEntBad);
+        float4 *dst = reinterpret_cast<float4 *>(a.d_state_in + (size_t)uh * D * D);
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                float acc[4][4];
-                {
-                    const float *e = sp.start_state(u, 0) + (4 * kq + 64 * half) * D + c;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int rr = 0; rr < 4; ++rr) acc[i][rr] = e[(16 * i + rr) * D];
-                }
-                for (int g = 1; g < cur.g; ++g) {
-                    const float f = fast_exp2(-cur.s2 * (float)seg_len_at(sp, L, g));
-                    const float *e = sp.start_state(u, g) + (4 * kq + 64 * half) * D + c;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int rr = 0; rr < 4; ++rr) acc[i][rr] = f * acc[i][rr] + e[(16 * i + rr) * D];
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    bf16x4 y;
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) y[rr] = static_cast<__bf16>(acc[i][rr]);
-                    *reinterpret_cast<bf16x4 *>(Rt + L128::off(c, 4 * (kq + 4 * i) + 64 * half)) = y;
-                }
+        for (int j = 0; j < kStateF4; ++j) {
+            const int f = tid + NT * j;
+            const unsigned b = (bad[f >> 3] >> (4 * (f & 7))) & 0xfu;  // entries 4f .. 4f+3
+            if (b) {
+                float4 x = dst[f];
+                if (b & 1) x.x = __builtin_nanf("");
+                if (b & 2) x.y = __builtin_nanf("");
+                if (b & 4) x.z = __builtin_nanf("");
+                if (b & 8) x.w = __builtin_nanf("");
+                dst[f] = x;
             }
-            loaded = cur.pair;
         }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int rr = (tl >> 4) + 32 * i;
-            *reinterpret_cast<uint4 *>(Kt + L128::off(rr, 8 * (tl & 15))) = keep_if(rr >= cur.rlo, la.kx[i]);
-            *reinterpret_cast<uint4 *>(Vt + L128::off(rr, 8 * (tl & 15))) = keep_if(rr >= cur.rlo, la.vx[i]);
-        }
-        __syncthreads();  // K, V tiles and R_in^T visible
-        f32x16 odv, odk;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) odv[v] = odk[v] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-            odv = mma(ld_op<L128>(Rt, 32 * cq, 16 * ks, ln), ld_op<L128>(Kt, 32 * qh, 16 * ks, ln), odv);
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-            odk = mma(ld_op_t<L128>(Rt, 32 * cq, 16 * ks, ln), ld_op<L128>(Vt, 32 * qh, 16 * ks, ln), odk);
-        const float f = fast_exp2(-cur.s2 * (float)(cur.seg_hi - 1 - (cur.tlo + 32 * qh + (ln & 31))));
-        odv *= f;
-        odk *= f;
-        stage_out(Os, odv, qh, cq, ln);
-        __syncthreads();  // dv rows staged
-        la.dvr.add_store(cur.dv, ts, Os, cur.rlo, tl);
-        __syncthreads();  // Os read
-        stage_out(Os, odk, qh, cq, ln);
-        __syncthreads();  // dk rows staged
-        la.dkr.add_store(cur.dk, ts, Os, cur.rlo, tl);
-        cur = nxt;
-        la = lb;
     }
 }
 
@@ -735,20 +707,13 @@ hipError_t launch(const BackwardArgs &a, const PrefillPlan &p, void *workspace, 
     const long long uh = (long long)a.units * a.heads;
     float *ws = static_cast<float *>(workspace);
     const bool seg = p.segments > 1 && p.value_slices == 1;
-    // heads may take local-start segments (fix_head's rule). The correction moves
-    // k, v once and dk, dv read and written, 512 (1 + sizeof(OutT)) B per token,
-    // against the reverse pre-pass's q, dO re-read, 512 B per token. fix_head
-    // weighs a correction token at 256 (1 + osz) B; osz = 1 + sizeof(OutT) counts
-    // it at 60-67% of that traffic, because the reverse pre-pass of the few heads
-    // that would still need it runs far below the correction's bandwidth (M1
-    // layer: with the exact weight the 3 slowest-decay heads take the pre-pass,
-    // 1.430 ms per call; with this one all 64 heads correct, 1.418 ms)
-    const int fix_osz = seg ? 1 + (int)sizeof(OutT) : 0;
-    const Segmented sp = seg ? Segmented{p.segments, p.pieces, p.seg_len, p.piece_len, fix_osz}
-                             : Segmented{1, 0, a.seqlen, 0};
+    const Segmented sp = seg ? Segmented{p.segments, p.pieces, p.seg_len, p.piece_len} : Segmented{1, 0, a.seqlen, 0};
     if (seg) {
-        hipLaunchKernelGGL(rev_piece_kernel, dim3((unsigned)(uh * p.pieces)), dim3(NT), 0, stream, a,
-                           sp, ws);
+        // the kernels' per-plan tables hold every pair and workgroup of a segmented plan
+        if (uh >= kMaxPairs) return hipErrorInvalidValue;
+        // working pre-pass workgroups: at most kPrepassActive + uh (see rev_piece_kernel)
+        const long long pre = uh * p.pieces < kPrepassActive + uh ? uh * p.pieces : kPrepassActive + uh;
+        hipLaunchKernelGGL(rev_piece_kernel, dim3((unsigned)pre), dim3(NT), 0, stream, a, sp, ws);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(uh * kCombineSlices)), dim3(kCombineThreads),
@@ -759,13 +724,9 @@ hipError_t launch(const BackwardArgs &a, const PrefillPlan &p, void *workspace, 
     }
     hipLaunchKernelGGL((bwd_kv_kernel<OutT>), dim3((unsigned)(uh * sp.segments)), dim3(NT), 0, stream,
                        a, sp, ws);
-    if (!fix_osz) return hipGetLastError();
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (uh * (sp.segments - 1) > kFixMaxPairs) return hipErrorInvalidValue;  // not a segmented plan
-    const int nfinal = a.d_state_in ? (int)(uh * kFinalSlices) : 0;
-    hipLaunchKernelGGL((rev_fix_kernel<OutT>), dim3((unsigned)(nfinal + kRevFixWorkgroups)), dim3(NT), 0, stream,
-                       a, sp, ws, nfinal);
+    if (e != hipSuccess || !seg) return e;
+    hipLaunchKernelGGL((bwd_finish_kernel<OutT>), dim3((unsigned)uh), dim3(NT), 0, stream, a, sp, ws);
     return hipGetLastError();
 }
 

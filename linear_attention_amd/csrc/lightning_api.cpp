@@ -52,9 +52,8 @@ constexpr long long kTargetWorkgroups = 256;
 // Shortest segment worth a workgroup of its own.
 constexpr long long kMinSegment = 2048;
 // Pre-pass pieces to plan for (the pieces cover the first G-1 segments of
-// every head; heads on warm-up ranges (local-start segments in the backward's
-// reverse pass) skip them, and when many heads do
-// take the pre-pass the kernels merge consecutive pieces into groups so that
+// every head; heads on warm-up ranges skip them, and when many heads do take
+// the pre-pass the kernels merge consecutive pieces into groups so that
 // about 512 workgroups work). Fine pieces suit the case of few pre-pass heads
 // (measured on the M1 layer when 7 of its 64 heads took it: 512 -> 661 us,
 // 1024 -> 643 us, 2048 -> 608 us per call).

@@ -98,35 +98,6 @@ __device__ __forceinline__ void store_rows_norm_gate(OutT *out, long long ts, co
     }
 }
 
-// Segmented plans have fewer than 256 (sequence, head) pairs.
-constexpr int kMaxPairs = 256;
-
-// The heads of a segmented plan split by route (each wave computes the same
-// lists: 64 heads at a time by ballot, in head order).
-struct Routes {
-    int npre, nwarm;
-};
-__device__ inline Routes split_heads(const float *slopes, int heads, const Segmented &sp, short *pre,
-                                     short *warm, bool write) {
-    const int lane = threadIdx.x & 63;
-    Routes r{0, 0};
-    for (int h0 = 0; h0 < heads; h0 += 64) {
-        const int h = h0 + lane;
-        const bool in = h < heads;
-        const bool p = in && takes_prepass(sp, slopes[in ? h : 0] * LOG2E);
-        const unsigned long long bp = __ballot(p), bw = __ballot(in && !p);
-        if (write) {
-            const int below = lane ? __popcll(bp & (~0ull >> (64 - lane))) : 0;
-            const int belw = lane ? __popcll(bw & (~0ull >> (64 - lane))) : 0;
-            if (p) pre[r.npre + below] = (short)h;
-            if (in && !p) warm[r.nwarm + belw] = (short)h;
-        }
-        r.npre += __popcll(bp);
-        r.nwarm += __popcll(bw);
-    }
-    return r;
-}
-
 // Pre-pass: workgroup (unit, head, piece j) runs the state update over the
 // full 64-token sub-blocks of its group of pieces without outputs, writing its
 // state and, if a segment boundary falls strictly inside the group, B_g on the
@@ -243,53 +214,6 @@ __device__ constexpr double warm_cost() {
     return 1.25 * 512.0 / (768.0 + 128.0 * sizeof(OutT) + (NG ? 256.0 : 0.0));
 }
 
-// Work of a workgroup of a segmented plan. The (unit, head) pairs of heads on
-// the pre-pass route take `segments` workgroups each, one per segment: the
-// first npre * units * segments workgroups, pair i of them (i / segments) the
-// i-th such pair in (unit, head) order. The other pairs (the warm-up route, see
-// warm_len) share the remaining workgroups in two phases.
-//  * Fine chunks: about kFineFrac of the warm-up route's tokens, taken from the
-//    end of the pairs whose warm-up is at most kFineWarm tokens, nf chunks of
-//    kFineChunk tokens from each such pair that is long enough (at most half
-//    its tokens). A workgroup that has finished its range takes the next
-//    chunk from a counter; chunk c is chunk c / Q of the (c % Q)-th of the Q
-//    such pairs, so the chunks in flight at any time spread over the heads
-//    (the rows of one head sit at the same offset of every token's row, and
-//    many workgroups on a few heads stream far slower). Which chunk a
-//    workgroup gets depends on timing, but where the chunks are cut does not,
-//    so the result does not either; the chunks absorb the differences in speed
-//    between workgroups that a static split cannot foresee (on the M1 layer
-//    one head in four streams about 15% slower than the others, the same
-//    heads on every call).
-//  * Ranges: the rest of each pair's tokens ("bulk") is cut into ranges of
-//    equal cost, one per workgroup; a range may end in one pair and go on in
-//    the next. An output token costs 1 and a warm-up token warm_cost(); pair j
-//    (the j-th warm pair in (unit, head) order, with B_j bulk tokens) costs
-//        C_j = B_j + warm_cost * min(W_j, B_j) * B_j / T0,
-//    its bulk plus the warm-ups of the about B_j / T0 cuts inside it (T0: the
-//    bulk tokens per workgroup), spread evenly over its tokens; that balances
-//    the ranges to first order. A workgroup's range is [r T, (r+1) T) of the
-//    prefix sums of C (T = sum C / workgroups), mapped onto each pair's tokens
-//    linearly and cut at multiples of 128 tokens, so neighbours agree on every
-//    cut and every warm-up is an even number of 64-token sub-blocks.
-// A piece that ends inside its pair with a NaN or Inf in its end state records
-// them in the pair's records (warm_records), from which the finishing pass
-// restores them in the later tokens.
-constexpr double kFineFrac = 0.15;
-constexpr long long kFineWarm = 128, kFineChunk = 768;
-static_assert(kFineChunk % 128 == 0, "pieces start at multiples of 128 tokens");
-struct WarmCut {
-    const double *cpre;  // [nwarm pairs + 1] prefix sums of C
-    double T;
-    __device__ long long cut(int j, double c, long long len) const {
-        const double a = cpre[j], b = cpre[j + 1];
-        if (c <= a) return 0;
-        if (c >= b) return len;
-        long long x = (long long)((c - a) / (b - a) * (double)len) / 128 * 128;
-        return x < 0 ? 0 : (x > len ? len : x);
-    }
-};
-
 // A workgroup's current piece, as thread 0 lays it out for the others: rows
 // of the piece's first token (k and v: of its warm-up's first token; row
 // stride ts elements), its length, the carried-in state and where the end
@@ -309,18 +233,6 @@ struct Piece {
     int cut;     // end == 2: the token the piece ends at
     int end;     // 0 nothing, 1 the final state to dst, 2 records if the end state is non-finite
 };
-// Warm-route bookkeeping of a workgroup.
-struct PlanState {
-    double T;   // cost per workgroup
-    int rl;     // this workgroup's range, counted from the first warm workgroup
-    int next;   // the next pair of its range to visit (pw: none)
-    int npre, nwarm, pw;
-    int last;   // the last workgroup (takes every pair left)
-    int nfine;     // fine chunks in all (nq pairs x nf chunks)
-    int nq, nf;
-    int *counter;  // the fine-chunk counter
-};
-
 template <typename OutT>
 __device__ void piece_rows(Piece &p, const PrefillArgs &a, int n, int h, long long t0, long long t1,
                            long long t0w) {
@@ -369,78 +281,28 @@ template <typename OutT>
 __device__ Piece next_piece(const PrefillArgs &a, const Segmented &sp, float *ws, int mode, int k,
                             PlanState &ps, const short *heads_pre, const short *heads_warm, const double *cpre,
                             const long long *bulk, const short *qlist, const int *by_rank) {
-    const SeqLens lens{a.cu_seqlens, a.total_tokens, a.seqlen};
+    const PieceRange r = next_range(SeqLens{a.cu_seqlens, a.total_tokens, a.seqlen}, a.heads, sp, mode, k, ps,
+                                    heads_pre, heads_warm, cpre, bulk, qlist,
+                                    a.cu_seqlens && a.units <= kRankUnits ? by_rank : nullptr);
     Piece p{};
     p.uh = -1;
-    if (mode == 0) {  // the whole sequence of one pair
-        if (k > 0) return p;
-        int n = blockIdx.x / a.heads;
-        const int h = blockIdx.x % a.heads;
-        if (a.cu_seqlens && a.units <= kRankUnits) n = by_rank[n];
-        piece_rows<OutT>(p, a, n, h, 0, lens.len(n), 0);
+    if (r.n < 0) return p;
+    if (r.kind == 0) {  // the whole sequence of one pair
+        piece_rows<OutT>(p, a, r.n, r.h, 0, r.len, 0);
         const size_t sb = (size_t)p.uh * D * D;
         p.s_in = a.state_in ? a.state_in + sb : nullptr;
         p.s_in_t = a.state_in_t;
         p.dst = a.state_out ? a.state_out + sb : nullptr;
         p.end = p.dst ? 1 : 0;
-        return p;
-    }
-    if (mode == 1) {  // one segment of a pre-pass pair
-        if (k > 0) return p;
-        const int i = blockIdx.x / sp.segments, g = blockIdx.x % sp.segments;
-        const int n = i / ps.npre, h = heads_pre[i % ps.npre];
-        const long long len = lens.len(n);
-        if (g >= sp.used(len)) return p;
-        const long long t0 = (long long)g * sp.seg_len;
-        piece_rows<OutT>(p, a, n, h, t0, t0 + seg_len_at(sp, len, g), t0);
-        p.s_in = sp.start_state(sp.unit(ws, p.uh), g);  // the combine pass wrote it (S_0 for g = 0)
-        p.dst = a.state_out && g == sp.used(len) - 1 ? a.state_out + (size_t)p.uh * D * D : nullptr;
+    } else if (r.kind == 1) {  // one segment of a pre-pass pair
+        piece_rows<OutT>(p, a, r.n, r.h, r.t0, r.t1, r.t0);
+        p.s_in = sp.start_state(sp.unit(ws, p.uh), r.g);  // the combine pass wrote it (S_0 for g = 0)
+        p.dst = a.state_out && r.g == sp.used(r.len) - 1 ? a.state_out + (size_t)p.uh * D * D : nullptr;
         p.end = p.dst ? 1 : 0;
-        return p;
-    }
-    // this workgroup's range of bulk tokens
-    const WarmCut wc{cpre, ps.T};
-    const double c0 = (double)ps.rl * ps.T, c1 = (double)(ps.rl + 1) * ps.T;
-    while (ps.next < ps.pw) {
-        const int j = ps.next;
-        const int n = j / ps.nwarm, h = heads_warm[j % ps.nwarm];
-        const long long b = bulk[j];
-        const long long t0 = wc.cut(j, c0, b);
-        const long long t1 = ps.last ? b : wc.cut(j, c1, b);
-        ps.next = ps.last || cpre[j + 1] < c1 ? j + 1 : ps.pw;  // the range goes on into the next pair
-        if (t1 <= t0) continue;
-        warm_piece<OutT>(p, a, sp, ws, n, h, t0, t1, lens.len(n));
-        return p;
-    }
-    // then fine chunks, while any are left
-    if (ps.nfine > 0) {
-        const int c = atomicAdd(ps.counter, 1);
-        if (c >= ps.nfine) {
-            ps.nfine = 0;
-            return p;
-        }
-        const int j = qlist[c % ps.nq], i = c / ps.nq;
-        const int n = j / ps.nwarm, h = heads_warm[j % ps.nwarm];
-        const long long len = lens.len(n);
-        const long long t0 = bulk[j] + (long long)i * kFineChunk;
-        const long long t1 = i + 1 == ps.nf ? len : t0 + kFineChunk;
-        warm_piece<OutT>(p, a, sp, ws, n, h, t0, t1, len);
+    } else {
+        warm_piece<OutT>(p, a, sp, ws, r.n, r.h, r.t0, r.t1, r.len);
     }
     return p;
-}
-
-// x, opaque to the optimiser: nothing computed from it moves out of the loop
-// that computes it.
-__device__ __forceinline__ int opaque(int x) {
-    asm volatile("" : "+v"(x));
-    return x;
-}
-template <typename T>
-__device__ __forceinline__ T *uniform_ptr(T *p) {
-    return reinterpret_cast<T *>(uniform64((long long)reinterpret_cast<uintptr_t>(p)));
-}
-__device__ __forceinline__ float uniformf(float x) {
-    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
 }
 
 template <typename OutT, bool NG>
@@ -502,113 +364,17 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
         const long long pre_wgs = (long long)a.units * rt.npre * segments;
         mode = (long long)blockIdx.x < pre_wgs ? 1 : 2;
         const int pw = a.units * rt.nwarm;  // warm pairs
-        if (mode == 2 && w == 0) {
-            // lane l: warm pairs 4l .. 4l+3 (pw < 256)
-            const double nwg = (double)pw * segments;
-            long long L[4], Wt[4], nf[4];
-            double lsum = 0.0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int j = 4 * lane0 + i;
-                L[i] = 0;
-                Wt[i] = 0;
-                if (j < pw) {
-                    L[i] = lens.len(j / rt.nwarm);
-                    Wt[i] = warm_len(a.slopes[heads_warm[j % rt.nwarm]] * LOG2E);
-                }
-                lsum += (double)L[i];
-            }
-            for (int o = 32; o >= 1; o >>= 1) lsum += __shfl_xor(lsum, o);
-            // fine chunks: kFineFrac of all warm tokens, nf from each pair that
-            // qualifies (at first count) and holds at least 2 nf chunks
-            // (capped at half the longest such pair, so that a large fraction
-            // does not leave every pair out)
-            int nq0 = 0;
-            long long lmax = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (Wt[i] <= kFineWarm && L[i] >= 2 * kFineChunk) {
-                    ++nq0;
-                    lmax = L[i] > lmax ? L[i] : lmax;
-                }
-            for (int o = 32; o >= 1; o >>= 1) {
-                nq0 += __shfl_xor(nq0, o);
-                const long long y = __shfl_xor(lmax, o);
-                lmax = y > lmax ? y : lmax;
-            }
-            long long nfw = nq0 > 0 ? (long long)(kFineFrac * lsum / ((double)nq0 * (double)kFineChunk)) : 0;
-            if (nfw > lmax / (2 * kFineChunk)) nfw = lmax / (2 * kFineChunk);
-            double bsum = 0.0;
-            int nrun = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool q = nfw > 0 && Wt[i] <= kFineWarm && L[i] >= 2 * nfw * kFineChunk;
-                nf[i] = q ? nfw : 0;
-                // bulk: the tokens before the first fine chunk (a multiple of 128)
-                const long long b = q ? (L[i] - nfw * kFineChunk) / 128 * 128 : L[i];
-                const int j = 4 * lane0 + i;
-                if (j < pw) bulk[j] = b;
-                L[i] = b;
-                bsum += (double)b;
-                nrun += q;
-            }
-            for (int o = 32; o >= 1; o >>= 1) bsum += __shfl_xor(bsum, o);
-            const double t0 = bsum / nwg;  // bulk tokens per workgroup
-            double c[4], run = 0.0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const double bl = (double)L[i], wl = Wt[i] < L[i] ? (double)Wt[i] : bl;
-                c[i] = L[i] > 0 ? bl + warm_cost<OutT, NG>() * wl * (bl / t0) : 0.0;
-                run += c[i];
-            }
-            double incl = run;  // inclusive scans of the lanes' sums
-            int fincl = nrun;
-            for (int o = 1; o < 64; o <<= 1) {
-                const double y = __shfl_up(incl, o);
-                const int fy = __shfl_up(fincl, o);
-                if (lane0 >= o) {
-                    incl += y;
-                    fincl += fy;
-                }
-            }
-            double acc = incl - run;
-            int facc = fincl - nrun;  // qualifying pairs before this lane's
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int j = 4 * lane0 + i;
-                if (j < pw) cpre[j] = acc;
-                if (nf[i] > 0) qlist[facc++] = (short)j;
-                acc += c[i];
-            }
-            if (lane0 == 63) {
-                cpre[pw] = incl;
-                fq[0] = fincl;
-                fq[1] = (int)nfw;
-            }
-        }
+        if (mode == 2 && w == 0)
+            warm_plan(lens, a.slopes, heads_warm, rt.nwarm, pw, (double)pw * segments, warm_cost<OutT, NG>(), cpre,
+                      bulk, qlist, fq);
         __syncthreads();  // cpre, bulk, qlist and fq are visible
         if (t0id == 0) {
             ps.npre = rt.npre;
             ps.nwarm = rt.nwarm;
             ps.pw = pw;
-            if (mode == 2) {
-                const int rl = (int)((long long)blockIdx.x - pre_wgs);
-                ps.rl = rl;
-                ps.T = cpre[pw] / ((double)pw * segments);
-                ps.last = rl + 1 == pw * segments;
-                // the first warm pair this range reaches: the first j with cpre[j + 1] > rl T
-                const double c0 = (double)rl * ps.T;
-                int lo = 0, hi = pw;
-                while (lo < hi) {
-                    const int mid = (lo + hi) / 2;
-                    if (cpre[mid + 1] > c0) hi = mid; else lo = mid + 1;
-                }
-                ps.next = lo;
-                ps.nq = fq[0];
-                ps.nf = fq[1];
-                ps.nfine = ps.nq * ps.nf;
-                ps.counter = warm_records(sp, ws, heads_warm[0]) + kFineCounter;  // in the first warm pair's records
-            }
+            if (mode == 2)
+                warm_plan_state(ps, cpre, fq, pw, segments, (int)((long long)blockIdx.x - pre_wgs),
+                                warm_records(sp, ws, heads_warm[0]) + kFineCounter);  // in the first warm pair's records
         }
     }
 
@@ -1102,12 +868,6 @@ __global__ __launch_bounds__(NT) void slice_kernel(PrefillArgs a) {
 // sequences (S_0, or zero) and, for in-place calls (state_out == state_in),
 // copies the final state that the main pass left in the workspace: writing it
 // there directly could race with the reads of S_0 by the pair's other pieces.
-__device__ __forceinline__ void poison(float *p) { *p = __builtin_nanf(""); }
-__device__ __forceinline__ void poison(__bf16 *p) { *reinterpret_cast<uint16_t *>(p) = 0x7fc0; }
-
-// float4 elements of a d x d state per thread of a workgroup
-constexpr int kStateF4 = D * D / (4 * NT);
-static_assert(kStateF4 * 4 * NT == D * D, "state elements per thread");
 
 template <typename OutT, bool NG>
 __global__ __launch_bounds__(NT) void finish_kernel(PrefillArgs a, Segmented sp, float *ws) {
@@ -1184,8 +944,7 @@ hipError_t launch(const PrefillArgs &a, const PrefillPlan &p, void *workspace, h
         return hipGetLastError();
     }
     float *ws = static_cast<float *>(workspace);
-    Segmented sp{p.segments, p.pieces, p.seg_len, p.piece_len};
-    sp.warm = true;
+    const Segmented sp{p.segments, p.pieces, p.seg_len, p.piece_len};
     if (p.segments > 1) {
         // the kernels' per-plan tables hold every pair and workgroup of a segmented plan
         if (uh >= kMaxPairs) return hipErrorInvalidValue;

@@ -302,48 +302,24 @@ __device__ __forceinline__ SeqRange sequence_of(const PrefillArgs &a, int n) {
 //   [B_1 .. B_{segments-1}]     for a boundary inside a piece: the state of that
 //                               piece's tokens before the boundary
 //   [S_0 .. S_{segments-1}]     state at the start of each segment
-// (pairs on the forward's warm-up route use slots 0 .. segments + 1 of theirs
-// instead: end states and flags of warm ranges, and an in-place final state).
+// (pairs on the warm-up route use slots 0 and 1 of theirs instead: the records
+// of their ranges' non-finite end states, and an in-place final state).
 // A state of tokens [t0, t1) from zero is sum_t e^{-s(t1-1-t)} k_t^T v_t, and
 // states compose as S(t2) = e^{-s(t2-t1)} S(t1) + state of [t1, t2).
-// Local-start segments (the reverse pass of the backward). A segment that
-// starts from a zero state instead of its true start state S_in misses, at its token t (t = 0, 1, ...), the term
-// e^{-s(t+1)} q_t S_in. With s2 = s log2(e) that factor is below 2^-kFixExp once
-// t + 1 > kFixExp / s2: a correction pass adds the term to the first
-// fix_len = min(segment, kFixExp / s2) tokens and leaves the rest: past them
-// the term is below 2^-24 of its own scale at the segment start, the unit
-// roundoff of fp32 (and 2^15 times below the rounding of the bf16 operands
-// every product of the path already carries). A head takes this
-// route when its decay cuts the term off inside the segment and re-reading q
-// and o for fix_len tokens costs at most twice the HBM traffic of the pre-pass
-// re-read of the whole segment's k and v:
-//   fix_len < seg_len  and  fix_len (256 + 256 osz) <= 2 * 512 seg_len
-// (osz: bytes per output element; q read once, o read and written). The factor
-// 2 is measured: the pre-pass of the few heads that still need it runs far
-// below the bandwidth the correction pass reaches, and the pre-pass and combine
-// launches are dependent steps ahead of the main kernel (M1 layer, 64 heads,
-// 32,768 tokens, with a 2^-32 cutoff: with factor 1, 57 heads correct and 7
-// take the pre-pass, 0.574 ms; with factor 2 all 64 correct, 0.557 ms).
+// Warm-up ranges. A range of a sequence that starts at token t0 > 0 computes
+// its carried-in state from the last W tokens before t0 (from a zero state;
+// from S_0 when the sequence starts within them), by state-only steps. A term
+// of the state t tokens old carries the factor e^{-s t}, below 2^-kFixExp of
+// its own scale once t > kFixExp / s2 (s2 = s log2 e): with W past that, what
+// the window leaves out is under 2^-24 of its scale, the unit roundoff of fp32
+// (and 2^15 times below the rounding of the bf16 operands every product of the
+// path already carries). W is rounded up to whole pairs of 64-token sub-blocks
+// (with pieces starting at multiples of 128 tokens every warm-up is then an
+// even number of sub-blocks, which the main kernels' warm-up steps rely on); a
+// head whose W is shorter than a segment takes this route, the others the
+// pre-pass. The backward's reverse pass does the same in mirrored token order
+// (its carry composes like the forward state; see backward.hip).
 constexpr float kFixExp = 24.f;
-__device__ __forceinline__ long long fix_len(float s2, long long seg_len) {
-    const float t = kFixExp / s2;
-    return t >= (float)seg_len ? seg_len : (long long)t;
-}
-__device__ __forceinline__ bool fix_head(float s2, long long seg_len, int osz) {
-    if (osz <= 0 || !(s2 > 0.f)) return false;
-    const long long n = fix_len(s2, seg_len);
-    return n < seg_len && n * (1 + osz) <= 4 * seg_len;
-}
-
-// Warm-up segments (the forward). A range of a sequence that starts at token
-// t0 > 0 computes its carried-in state from the last W tokens before t0 (from a
-// zero state; from S_0 when the sequence starts within them), by state-only
-// steps: the terms older than W tokens are below 2^-kFixExp of their scale, as
-// with the correction above, but no output needs a second pass. W is rounded up
-// to whole pairs of 64-token sub-blocks (with pieces starting at multiples of
-// 128 tokens every warm-up is then an even number of sub-blocks, which the main
-// kernel's warm-up steps rely on); a head whose W is shorter than a segment
-// takes this route, the others the pre-pass.
 __device__ __forceinline__ long long warm_len(float s2) {
     if (!(s2 > 0.f)) return 1LL << 62;  // no decay (or NaN): never forgets
     const float t = kFixExp / s2;
@@ -373,8 +349,6 @@ struct SeqLens {
 struct Segmented {
     int segments, pieces;
     long long seg_len, piece_len;
-    int fix_osz = 0;    // local-start segments with a correction pass (the backward): output element size
-    bool warm = false;  // warm-up segments (the forward): see warm_len
     __device__ int used(long long len) const {
         const long long g = (len + seg_len - 1) / seg_len;
         return g < 1 ? 1 : (g > segments ? segments : (int)g);
@@ -390,46 +364,9 @@ struct Segmented {
     __device__ float *start_state(float *u, int g) const { return slot(u, pieces + segments - 1 + g); }
 };
 
-// Non-finite carried-in states (local-start segments). The correction's cutoff
-// is sound only for a finite S_in: e^{-s(t+1)} q_t S_in is then below 2^-24 of
-// its scale past fix_len tokens, but a NaN or Inf in S_in reaches every later
-// token of the exact operator. So the main pass flags each local-start segment whose end
-// state E_g holds a NaN or Inf, and the correction pass treats the whole of
-// segment g as "first tokens" when any of E_0 .. E_{g-1} is flagged (S_in(g)
-// is then non-finite). The flags of E_g (g <= segments - 2) sit in the slot
-// of the partial state B_{g+1}, which heads on local starts never use: one int
-// per wave of the segment's workgroup.
 __device__ __forceinline__ bool nonfinite(float x) {
     return (__float_as_uint(x) & 0x7f800000u) == 0x7f800000u;
 }
-__device__ __forceinline__ int *end_flags(const Segmented &sp, float *u, int g) {
-    return reinterpret_cast<int *>(sp.partial(u, g + 1));
-}
-// Wave w's flag of its accumulator blocks of E_g.
-__device__ __forceinline__ void flag_end_state(int *flags, const f32x16 (&S)[2], int w, int lane) {
-    bool bad = false;
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) bad |= nonfinite(S[db][v]);
-    const bool any = __ballot(bad) != 0;
-    if (lane == 0) flags[w] = any ? 1 : 0;
-}
-// S_in(g) non-finite: some E_j, j < g, flagged.
-__device__ __forceinline__ bool start_poisoned(const Segmented &sp, float *u, int g) {
-    int bad = 0;
-    for (int j = 0; j < g; ++j) {
-        const int *f = end_flags(sp, u, j);
-#pragma unroll
-        for (int w = 0; w < NT / 64; ++w) bad |= f[w];
-    }
-    return bad != 0;
-}
-
-// Correction passes: (unit, head, segment g >= 1) pairs of a segmented plan
-// (fewer than 256), and the final-state slices (4 elements per thread).
-constexpr int kFixMaxPairs = 256;                  // segmented plans have fewer (unit, head, g >= 1) pairs
-constexpr int kFinalSlices = D * D / (4 * NT);     // 4 state elements per thread
 
 // A 64-bit value that is the same in every lane, kept in scalar registers.
 __device__ __forceinline__ long long uniform64(long long x) {
@@ -437,35 +374,333 @@ __device__ __forceinline__ long long uniform64(long long x) {
     const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)((unsigned long long)x >> 32));
     return (long long)(((unsigned long long)hi << 32) | lo);
 }
+// The same for a pointer and a float.
+template <typename T>
+__device__ __forceinline__ T *uniform_ptr(T *p) {
+    return reinterpret_cast<T *>(uniform64((long long)reinterpret_cast<uintptr_t>(p)));
+}
+__device__ __forceinline__ float uniformf(float x) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+// x, opaque to the optimiser: nothing computed from it moves out of the loop
+// that computes it.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
 
 // Heads whose segments start from states the pre-pass and combine compute; the
-// others take local-start segments (the backward) or warm-up segments (the
-// forward).
+// others take warm-up ranges.
 __device__ __forceinline__ bool takes_prepass(const Segmented &sp, float s2) {
-    if (sp.warm) return !(warm_len(s2) < sp.seg_len);
-    return !fix_head(s2, sp.seg_len, sp.fix_osz);
+    return !(warm_len(s2) < sp.seg_len);
 }
 
 // Warm-up route records, in slot 0 of each warm pair's workspace unit, reset by
-// the combine pass before the main kernel runs:
-//   ints [0, D)           per value column c, the earliest token t at which a
-//                         range ending at t left a non-finite end state with a
-//                         NaN or Inf in column c (kNoCut: none);
-//   ints [D, D + D*D/32)  one bit per state entry: non-finite in some such end
-//                         state;
-//   int kFineCounter      (first warm pair only) the next fine chunk to hand out.
-// Slot 1 holds the pair's final state on in-place calls.
-constexpr int kRecColCut = 0, kRecEntBad = D, kRecInts = D + D * D / 32, kFineCounter = 1024;
+// the combine pass before the main kernel runs. A range that ends at token t
+// inside its pair and leaves a NaN or Inf in entry (r, c) of its end state
+// (forward: S; backward: the carry R, t counted in mirrored order) records
+//   ints [0, D)            per column c, the earliest such t (kNoCut: none);
+//   ints [D, D + D*D/32)   one bit per state entry: non-finite in some such end
+//                          state;
+//   ints [kRecRowCut, +D)  per row r, the earliest such t (backward only);
+//   int kFineCounter       (first warm pair only) the next fine chunk to hand out.
+// Slot 1 holds the pair's final state on in-place forward calls.
+constexpr int kRecColCut = 0, kRecEntBad = D, kRecRowCut = D + D * D / 32, kRecInts = 2 * D + D * D / 32;
+constexpr int kFineCounter = 1024;
 constexpr int kNoCut = 0x7fffffff;
 static_assert(kRecInts <= kFineCounter, "warm records");
 __device__ __forceinline__ int *warm_records(const Segmented &sp, float *ws, int uh) {
     return reinterpret_cast<int *>(Segmented::slot(sp.unit(ws, uh), 0));
+}
+// The finishing passes' NaN, and the float4 elements of a d x d state per
+// thread of a workgroup.
+__device__ __forceinline__ void poison(float *p) { *p = __builtin_nanf(""); }
+__device__ __forceinline__ void poison(__bf16 *p) { *reinterpret_cast<uint16_t *>(p) = 0x7fc0; }
+constexpr int kStateF4 = D * D / (4 * NT);
+static_assert(kStateF4 * 4 * NT == D * D, "state elements per thread");
+
+// Segmented plans have fewer than 256 (sequence, head) pairs.
+constexpr int kMaxPairs = 256;
+
+// The heads of a segmented plan split by route (each wave computes the same
+// lists: 64 heads at a time by ballot, in head order).
+struct Routes {
+    int npre, nwarm;
+};
+__device__ inline Routes split_heads(const float *slopes, int heads, const Segmented &sp, short *pre,
+                                     short *warm, bool write) {
+    const int lane = threadIdx.x & 63;
+    Routes r{0, 0};
+    for (int h0 = 0; h0 < heads; h0 += 64) {
+        const int h = h0 + lane;
+        const bool in = h < heads;
+        const bool p = in && takes_prepass(sp, slopes[in ? h : 0] * LOG2E);
+        const unsigned long long bp = __ballot(p), bw = __ballot(in && !p);
+        if (write) {
+            const int below = lane ? __popcll(bp & (~0ull >> (64 - lane))) : 0;
+            const int belw = lane ? __popcll(bw & (~0ull >> (64 - lane))) : 0;
+            if (p) pre[r.npre + below] = (short)h;
+            if (in && !p) warm[r.nwarm + belw] = (short)h;
+        }
+        r.npre += __popcll(bp);
+        r.nwarm += __popcll(bw);
+    }
+    return r;
+}
+
+// Work of a workgroup of a segmented plan. The (unit, head) pairs of heads on
+// the pre-pass route take `segments` workgroups each, one per segment: the
+// first npre * units * segments workgroups, pair i of them (i / segments) the
+// i-th such pair in (unit, head) order. The other pairs (the warm-up route, see
+// warm_len) share the remaining workgroups in two phases.
+//  * Fine chunks: about kFineFrac of the warm-up route's tokens, taken from the
+//    end of the pairs whose warm-up is at most kFineWarm tokens, nf chunks of
+//    kFineChunk tokens from each such pair that is long enough (at most half
+//    its tokens). A workgroup that has finished its range takes the next
+//    chunk from a counter; chunk c is chunk c / Q of the (c % Q)-th of the Q
+//    such pairs, so the chunks in flight at any time spread over the heads
+//    (the rows of one head sit at the same offset of every token's row, and
+//    many workgroups on a few heads stream far slower). Which chunk a
+//    workgroup gets depends on timing, but where the chunks are cut does not,
+//    so the result does not either; the chunks absorb the differences in speed
+//    between workgroups that a static split cannot foresee (on the M1 layer
+//    one head in four streams about 15% slower than the others, the same
+//    heads on every call).
+//  * Ranges: the rest of each pair's tokens ("bulk") is cut into ranges of
+//    equal cost, one per workgroup; a range may end in one pair and go on in
+//    the next. An output token costs 1 and a warm-up token warm_cost(); pair j
+//    (the j-th warm pair in (unit, head) order, with B_j bulk tokens) costs
+//        C_j = B_j + warm_cost * min(W_j, B_j) * B_j / T0,
+//    its bulk plus the warm-ups of the about B_j / T0 cuts inside it (T0: the
+//    bulk tokens per workgroup), spread evenly over its tokens; that balances
+//    the ranges to first order. A workgroup's range is [r T, (r+1) T) of the
+//    prefix sums of C (T = sum C / workgroups), mapped onto each pair's tokens
+//    linearly and cut at multiples of 128 tokens, so neighbours agree on every
+//    cut and every warm-up is an even number of 64-token sub-blocks.
+// A piece that ends inside its pair with a NaN or Inf in its end state records
+// them in the pair's records (warm_records), from which the finishing pass
+// restores them in the later tokens.
+constexpr double kFineFrac = 0.15;
+constexpr long long kFineWarm = 128, kFineChunk = 768;
+static_assert(kFineChunk % 128 == 0, "pieces start at multiples of 128 tokens");
+struct WarmCut {
+    const double *cpre;  // [nwarm pairs + 1] prefix sums of C
+    double T;
+    __device__ long long cut(int j, double c, long long len) const {
+        const double a = cpre[j], b = cpre[j + 1];
+        if (c <= a) return 0;
+        if (c >= b) return len;
+        long long x = (long long)((c - a) / (b - a) * (double)len) / 128 * 128;
+        return x < 0 ? 0 : (x > len ? len : x);
+    }
+};
+
+// Warm-route bookkeeping of a workgroup.
+struct PlanState {
+    double T;   // cost per workgroup
+    int rl;     // this workgroup's range, counted from the first warm workgroup
+    int next;   // the next pair of its range to visit (pw: none)
+    int npre, nwarm, pw;
+    int last;   // the last workgroup (takes every pair left)
+    int nfine;     // fine chunks in all (nq pairs x nf chunks)
+    int nq, nf;
+    int *counter;  // the fine-chunk counter
+};
+
+// Wave 0 of a workgroup computes the warm-up route's plan into LDS: cpre (the
+// prefix sums of the ranges' costs, see WarmCut), bulk (each pair's bulk
+// tokens), qlist and fq (the pairs that give fine chunks, their count and the
+// chunks per pair). Warm pair j (j < pw < 256) is head heads_warm[j % nwarm] of
+// unit j / nwarm; nwg workgroups share the ranges; a warm-up token costs wcost
+// output tokens. Lane l takes pairs 4l .. 4l+3. Every workgroup computes the
+// same plan (the same fp64 operations on the same inputs).
+__device__ inline void warm_plan(const SeqLens &lens, const float *slopes, const short *heads_warm, int nwarm, int pw,
+                                 double nwg, double wcost, double *cpre, long long *bulk, short *qlist, int *fq) {
+    const int lane0 = threadIdx.x & 63;
+    long long L[4], Wt[4], nf[4];
+    double lsum = 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = 4 * lane0 + i;
+        L[i] = 0;
+        Wt[i] = 0;
+        if (j < pw) {
+            L[i] = lens.len(j / nwarm);
+            Wt[i] = warm_len(slopes[heads_warm[j % nwarm]] * LOG2E);
+        }
+        lsum += (double)L[i];
+    }
+    for (int o = 32; o >= 1; o >>= 1) lsum += __shfl_xor(lsum, o);
+    // fine chunks: kFineFrac of all warm tokens, nf from each pair that
+    // qualifies (at first count) and holds at least 2 nf chunks
+    // (capped at half the longest such pair, so that a large fraction
+    // does not leave every pair out)
+    int nq0 = 0;
+    long long lmax = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (Wt[i] <= kFineWarm && L[i] >= 2 * kFineChunk) {
+            ++nq0;
+            lmax = L[i] > lmax ? L[i] : lmax;
+        }
+    for (int o = 32; o >= 1; o >>= 1) {
+        nq0 += __shfl_xor(nq0, o);
+        const long long y = __shfl_xor(lmax, o);
+        lmax = y > lmax ? y : lmax;
+    }
+    long long nfw = nq0 > 0 ? (long long)(kFineFrac * lsum / ((double)nq0 * (double)kFineChunk)) : 0;
+    if (nfw > lmax / (2 * kFineChunk)) nfw = lmax / (2 * kFineChunk);
+    double bsum = 0.0;
+    int nrun = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bool q = nfw > 0 && Wt[i] <= kFineWarm && L[i] >= 2 * nfw * kFineChunk;
+        nf[i] = q ? nfw : 0;
+        // bulk: the tokens before the first fine chunk (a multiple of 128)
+        const long long b = q ? (L[i] - nfw * kFineChunk) / 128 * 128 : L[i];
+        const int j = 4 * lane0 + i;
+        if (j < pw) bulk[j] = b;
+        L[i] = b;
+        bsum += (double)b;
+        nrun += q;
+    }
+    for (int o = 32; o >= 1; o >>= 1) bsum += __shfl_xor(bsum, o);
+    const double t0 = bsum / nwg;  // bulk tokens per workgroup
+    double c[4], run = 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const double bl = (double)L[i], wl = Wt[i] < L[i] ? (double)Wt[i] : bl;
+        c[i] = L[i] > 0 ? bl + wcost * wl * (bl / t0) : 0.0;
+        run += c[i];
+    }
+    double incl = run;  // inclusive scans of the lanes' sums
+    int fincl = nrun;
+    for (int o = 1; o < 64; o <<= 1) {
+        const double y = __shfl_up(incl, o);
+        const int fy = __shfl_up(fincl, o);
+        if (lane0 >= o) {
+            incl += y;
+            fincl += fy;
+        }
+    }
+    double acc = incl - run;
+    int facc = fincl - nrun;  // qualifying pairs before this lane's
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = 4 * lane0 + i;
+        if (j < pw) cpre[j] = acc;
+        if (nf[i] > 0) qlist[facc++] = (short)j;
+        acc += c[i];
+    }
+    if (lane0 == 63) {
+        cpre[pw] = incl;
+        fq[0] = fincl;
+        fq[1] = (int)nfw;
+    }
+}
+
+// Thread 0: the bookkeeping of warm workgroup rl (counted from the first warm
+// workgroup) of nwg = pw * segments, from the plan above; `counter` is the
+// fine-chunk counter.
+__device__ inline void warm_plan_state(PlanState &ps, const double *cpre, const int *fq, int pw, int segments, int rl,
+                                       int *counter) {
+    ps.rl = rl;
+    ps.T = cpre[pw] / ((double)pw * segments);
+    ps.last = rl + 1 == pw * segments;
+    // the first warm pair this range reaches: the first j with cpre[j + 1] > rl T
+    const double c0 = (double)rl * ps.T;
+    int lo = 0, hi = pw;
+    while (lo < hi) {
+        const int mid = (lo + hi) / 2;
+        if (cpre[mid + 1] > c0) hi = mid; else lo = mid + 1;
+    }
+    ps.next = lo;
+    ps.nq = fq[0];
+    ps.nf = fq[1];
+    ps.nfine = ps.nq * ps.nf;
+    ps.counter = counter;
 }
 
 // Tokens of segment g of a sequence of `seqlen` tokens (0 past its end).
 __device__ __forceinline__ long long seg_len_at(const Segmented &sp, long long seqlen, int g) {
     const long long rest = seqlen - (long long)g * sp.seg_len;
     return rest < 0 ? 0 : (rest < sp.seg_len ? rest : sp.seg_len);
+}
+
+// A workgroup's next piece: tokens [t0, t1) of pair (sequence n, head h), of a
+// sequence of len tokens (the backward counts them in mirrored order).
+struct PieceRange {
+    int n, h;  // n < 0: no more pieces
+    int kind;  // 0 the whole pair (no segments), 1 segment g of a pre-pass pair, 2 a warm-route piece
+    int g;
+    long long t0, t1, len;
+};
+// Thread 0 walks its workgroup's plan: mode 0 (no segments; by_rank, if given,
+// maps workgroup slots to sequences), 1 (a pre-pass pair's segment) or 2 (its
+// range of bulk tokens, then fine chunks while any are left); k counts the
+// pieces taken so far.
+__device__ inline PieceRange next_range(const SeqLens &lens, int heads, const Segmented &sp, int mode, int k,
+                                        PlanState &ps, const short *heads_pre, const short *heads_warm,
+                                        const double *cpre, const long long *bulk, const short *qlist,
+                                        const int *by_rank) {
+    PieceRange r{-1, 0, 0, 0, 0, 0, 0};
+    if (mode == 0) {
+        if (k > 0) return r;
+        r.n = blockIdx.x / heads;
+        if (by_rank) r.n = by_rank[r.n];
+        r.h = blockIdx.x % heads;
+        r.len = r.t1 = lens.len(r.n);
+        return r;
+    }
+    if (mode == 1) {
+        if (k > 0) return r;
+        const int i = blockIdx.x / sp.segments, g = blockIdx.x % sp.segments;
+        const int n = i / ps.npre;
+        const long long len = lens.len(n);
+        if (g >= sp.used(len)) return r;
+        r.n = n;
+        r.h = heads_pre[i % ps.npre];
+        r.kind = 1;
+        r.g = g;
+        r.len = len;
+        r.t0 = (long long)g * sp.seg_len;
+        r.t1 = r.t0 + seg_len_at(sp, len, g);
+        return r;
+    }
+    // this workgroup's range of bulk tokens
+    const WarmCut wc{cpre, ps.T};
+    const double c0 = (double)ps.rl * ps.T, c1 = (double)(ps.rl + 1) * ps.T;
+    while (ps.next < ps.pw) {
+        const int j = ps.next;
+        const long long b = bulk[j];
+        const long long t0 = wc.cut(j, c0, b);
+        const long long t1 = ps.last ? b : wc.cut(j, c1, b);
+        ps.next = ps.last || cpre[j + 1] < c1 ? j + 1 : ps.pw;  // the range goes on into the next pair
+        if (t1 <= t0) continue;
+        r.n = j / ps.nwarm;
+        r.h = heads_warm[j % ps.nwarm];
+        r.kind = 2;
+        r.len = lens.len(r.n);
+        r.t0 = t0;
+        r.t1 = t1;
+        return r;
+    }
+    // then fine chunks, while any are left
+    if (ps.nfine > 0) {
+        const int c = atomicAdd(ps.counter, 1);
+        if (c >= ps.nfine) {
+            ps.nfine = 0;
+            return r;
+        }
+        const int j = qlist[c % ps.nq], i = c / ps.nq;
+        r.n = j / ps.nwarm;
+        r.h = heads_warm[j % ps.nwarm];
+        r.kind = 2;
+        r.len = lens.len(r.n);
+        r.t0 = bulk[j] + (long long)i * kFineChunk;
+        r.t1 = i + 1 == ps.nf ? r.len : r.t0 + kFineChunk;
+    }
+    return r;
 }
 
 // Pre-pass grouping. The plan cuts the first G-1 segments of every head into
@@ -511,10 +746,11 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float *s
     const int e = 4 * ((blockIdx.x % kCombineSlices) * kCombineThreads + threadIdx.x);
     const int h = uh % heads;
     const float s2 = slopes[h] * LOG2E;
-    if (!takes_prepass(sp, s2)) {  // local-start or warm-up segments: no pre-pass states
-        if (sp.warm && blockIdx.x % kCombineSlices == 0) {  // reset the warm-up route's records
+    if (!takes_prepass(sp, s2)) {  // warm-up ranges: no pre-pass states
+        if (blockIdx.x % kCombineSlices == 0) {  // reset the warm-up route's records
             int *rec = warm_records(sp, ws, uh);
-            for (int i = threadIdx.x; i < kRecInts; i += kCombineThreads) rec[i] = i < kRecEntBad ? kNoCut : 0;
+            for (int i = threadIdx.x; i < kRecInts; i += kCombineThreads)
+                rec[i] = i < kRecEntBad || i >= kRecRowCut ? kNoCut : 0;
             if (threadIdx.x == 0) rec[kFineCounter] = 0;
         }
         return;

@@ -122,9 +122,11 @@ def max_rel_states(s_gpu, s_ref):
 # of lt_prefill (batch-1 style calls with fewer than 256 (sequence, head) pairs
 # and at least 4096 tokens per sequence): G = ceil(256 / (batch * heads))
 # segments, at most L / 2048, of seg = ceil(L / G) tokens rounded up to a
-# multiple of 128. A head with slope s whose carried-in term dies inside a
-# segment starts segments g >= 1 from zero and gets that term added to its
-# first fix_len = min(seg, floor(24 / (s log2 e))) tokens afterwards.
+# multiple of 128. A head with slope s whose warm-up W = 128 * floor((floor(24 /
+# (s log2 e)) + 128) / 128) is shorter than a segment takes warm-up ranges
+# (cut at multiples of 128 tokens, each rebuilding its carried-in state from
+# the W tokens before it); the others take the pre-pass. The backward's reverse
+# pass does the same counted from the end of the sequence.
 
 LOG2E = 1.4426950408889634
 

@@ -102,12 +102,11 @@ def test_backward_long_sequence_without_workspace(la):
 @pytest.mark.parametrize("grad_dtype", ["f32", "bf16"])
 def test_backward_segmented_slope_mix(la, grad_dtype):
     """Segmented backward over heads on both routes of both passes: short-memory
-    heads (slopes 0.012, 0.02, 0.2, 1, 30) on local-start segments with the
-    carried-in terms added afterwards (0.012: 1,386 corrected tokens of 2,304,
-    0.60 of the segment, a head the reverse pass corrects although its
-    correction moves more than the pre-pass would; 0.02: 831; 30: only the last
-    token of each reverse segment), 0 and 1e-6 on the pre-passes; carried-in
-    state and final-state gradient."""
+    heads (slopes 0.012, 0.02, 0.2, 1, 30) on warm-up ranges (warm-ups of 1,408,
+    896 and 128 tokens, against 2,304-token segments; the reverse pass's ranges
+    and fine chunks are cut from the end of the sequence, so its last piece
+    holds the ragged first 9000 mod 64 tokens), 0 and 1e-6 on the pre-passes;
+    carried-in state and final-state gradient."""
     import torch
 
     L, H = 9000, 7

@@ -447,7 +447,7 @@ def test_prefill_segmented_warm_ranges_no_final_state(la):
 @pytest.mark.parametrize("L", [16384, 20480])
 def test_prefill_prepass_groups(la, L):
     """Many heads on the pre-pass (64 heads, slopes scaled by 1e-4, so no head
-    takes local starts): the kernels merge consecutive pre-pass pieces into
+    takes warm-up ranges): the kernels merge consecutive pre-pass pieces into
     groups (L = 16384: 24 pieces of 512 in 8 groups of 3, boundaries inside
     groups; L = 20480: 30 pieces in groups of 4, the last group of 2, a group
     ending on a boundary). Carried-in state updated in place; sampled heads
@@ -475,7 +475,7 @@ def test_prefill_prepass_groups(la, L):
 def test_prefill_segmented_batch_slope_mix(la):
     """Segmented plan with several sequences (3 x 9000 tokens, 5 heads: 15
     pairs, 5 segments each) over heads on both routes (pre-pass: 0, 1e-6;
-    local starts: 0.02, 0.3, 4), carried-in states, bf16 output."""
+    warm-up ranges: 0.02, 0.3, 4), carried-in states, bf16 output."""
     import torch
 
     B, L, H = 3, 9000, 5

@@ -4,9 +4,9 @@ The contract (include/lightning.h): every output that the exact operator makes
 non-finite is non-finite (NaN or Inf) on the GPU, whatever plan the call takes
 (including warm-up ranges, which rebuild their carried-in state from a window
 of earlier tokens and so cannot see a NaN or Inf from before it: a finishing
-pass puts it back from the flagged end states of the earlier ranges), and the
-carried-in state of the backward's local-start segments, whose correction is
-widened to the whole segment when that state is non-finite; every other output is
+pass puts it back from the flagged end states of the earlier ranges; the
+backward's reverse pass does the same with its carry, in mirrored token
+order); every other output is
 finite and within the parity bound, except outputs of earlier tokens of the
 same 64-token block (counted from the sequence start) as a non-finite v: the
 masked entries of the in-block product are zeros multiplied on the matrix
@@ -212,18 +212,19 @@ def test_nonfinite_norm_gate_segmented(la):
 
 def test_nonfinite_backward_segmented(la):
     """lt_prefill_backward on the segmented slope mix with a NaN in q near the
-    end of the sequence (the reverse pass's first mirrored segment, whose end
-    carry then reaches every earlier token of local-start heads through the
-    widened correction) and an Inf in dout."""
+    end of the sequence (in the reverse pass's first ranges: the carry entries
+    it reaches stay non-finite at every earlier token, past the warm-up windows
+    of the later ranges, which the finishing pass covers from the records) and
+    an Inf in dout."""
     import torch
 
     L, H = 9000, 7
     print(f"[case] non-finite inputs, backward segmented L={L}", flush=True)
     q, k, v = workloads.qkv_host(5501, (1, L, H, 128), "bf16")
     do = workloads.gate_host(5502, (1, L, H, 128))
-    q[0, 8500, 4, 3] = np.nan        # local-start head (s = 0.2), mirrored segment 0
+    q[0, 8500, 4, 3] = np.nan        # warm-up head (s = 0.2), near the end of the sequence
     q[0, 8200, 1, 0] = np.nan        # pre-pass head
-    do[0, 7000, 5, 9] = np.inf       # local-start head (s = 1)
+    do[0, 7000, 5, 9] = np.inf       # warm-up head (s = 1)
     ds = workloads.state_host(5503, (1, H, 128, 128))
     dq, dk, dv, dsi = la.lt_prefill_backward(*(to_device(x, "bf16") for x in (q, k, v, do)),
                                              torch.from_numpy(MIX).cuda(), 256, None,

@@ -100,7 +100,7 @@ def test_noalloc_two_calls_match_lt_prefill(la):
     assert eo <= TOL_BF16 and es <= TOL_BF16 and er <= TOL_BF16
     del q, k, v, o_na, o_same, o_full, ws_full
 
-    # call 2: smaller, heads on both routes (pre-pass and local starts), the
+    # call 2: smaller, heads on both routes (pre-pass and warm-up ranges), the
     # carried-in state updated in place
     L, H = 9000, 7
     sl2_h = np.array([0.0, 1e-6, 0.005, 0.02, 0.2, 1.0, 30.0], np.float32)
