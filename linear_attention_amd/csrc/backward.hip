@@ -25,9 +25,8 @@
 //    (K, V ⊙ d_k);
 //  * sub-blocks are anchored at the end of the sequence (a short block, if
 //    any, comes last and covers the first tokens);
-//  * long sequences with few (sequence, head) pairs are cut into segments
-//    counted from the end, with a reverse pre-pass and the forward's combine
-//    kernel (see rev_piece_kernel);
+//  * long sequences with few (sequence, head) pairs are split like the
+//    forward's, counted from the end (see rev_piece_kernel);
 //  * dV and dK are staged through LDS (in the R^T buffer and the K, V tiles,
 //    free by then) and leave as whole rows; four barriers per sub-block.
 #include <hip/hip_runtime.h>
@@ -161,8 +160,8 @@ struct BwdStage {
 //  * pre-pass heads: the first (segments-1) segments from the end are cut into
 //    pieces; a piece's contribution, from zero at its real end p1 back to its
 //    real start p0, is sum_i e^{-s(i - p0 + 1)} q_i^T dO_i (the carry update
-//    over the piece's sub-blocks walked backward), and the forward's combine
-//    kernel gives every segment its starting carry;
+//    over the piece's sub-blocks walked backward), and each segment's
+//    workgroup combines its starting carry from them (combine_start);
 //  * the other heads: warm-up ranges balanced by cost, then fine chunks (the
 //    forward's plan, tiles.h), each rebuilding its starting carry by carry-only
 //    steps over the q, dO rows of the W tokens after its real end (from zero;
@@ -197,6 +196,11 @@ __global__ __launch_bounds__(NT, 2) void rev_piece_kernel(BackwardArgs a, Segmen
     __shared__ __attribute__((aligned(16))) __bf16 Qds[C * D];
     __shared__ __attribute__((aligned(16))) __bf16 Gs[C * D];
     __shared__ short heads_pre[kMaxPairs], heads_warm[kMaxPairs];
+
+    // workgroup b < units * heads first resets the records of pair b if that
+    // pair takes warm-up ranges
+    if ((int)blockIdx.x < a.units * a.heads && !takes_prepass(sp, a.slopes[blockIdx.x % a.heads] * LOG2E))
+        reset_records(warm_records(sp, ws, blockIdx.x), NT);
 
     // groups of kgr pieces, numbered as in the forward pre-pass: workgroup b
     // takes group b % gph of the (b / gph)-th pre-pass pair (the launch is
@@ -300,12 +304,16 @@ struct BwdPiece {
     const float *r_in;    // carried-in carry (nullptr: zero)
     float *dst;           // end == 1: d_state_in
     int *rec;             // end == 2: the pair's records
+    float *u;             // comb_g > 0: the pair's workspace unit
+    long long covered;    // comb_g > 0: the pair's pre-pass tokens
     long long len, warm;  // tokens of the piece; warm-up tokens (whole sub-blocks)
     float s2;
     int ts;
     int uh;   // -1: no more pieces
     int cut;  // end == 2: the mirrored token the piece ends at
     int end;  // 0 nothing, 1 d_state_in, 2 records if the end carry is non-finite
+    int comb_g;  // > 0: mirrored segment comb_g of a pre-pass pair, whose start carry the piece combines
+    int kg;      // comb_g > 0: pre-pass pieces per group
 };
 
 template <typename OutT>
@@ -337,8 +345,12 @@ __device__ BwdPiece next_bwd_piece(const BackwardArgs &a, const Segmented &sp, f
     const float *ds = a.d_state_out ? a.d_state_out + sb : nullptr;
     if (r.kind == 0) {
         p.r_in = ds;
-    } else if (r.kind == 1) {
-        p.r_in = sp.start_state(sp.unit(ws, p.uh), r.g);  // the combine pass wrote it (dS for g = 0)
+    } else if (r.kind == 1) {  // dS, then the combine of the pieces after the segment
+        p.r_in = ds;
+        p.u = sp.unit(ws, p.uh);
+        p.comb_g = r.g;
+        p.kg = prepass_group_of(ps.npre, a.units, sp);
+        p.covered = sp.covered(L);
     } else {
         const long long wl = warm_len(p.s2);
         const long long t0w = r.t0 > wl ? r.t0 - wl : 0;
@@ -390,7 +402,8 @@ __global__ __launch_bounds__(NT) void bwd_kv_kernel(BackwardArgs a, Segmented sp
     }
 
     // ---- this workgroup's work: pieces (pair uh, mirrored tokens [t0, t1)),
-    // each starting from the combine pass's start carry, dS, zero, and a warm-up
+    // each starting from dS (combined with the pre-pass's carries of the later
+    // tokens on the pre-pass route), zero, and a warm-up
     int mode = 0;  // 0: one pair, whole (no segments); 1: one pre-pass segment; 2: warm ranges
     if (segments > 1) {
         const Routes rt = split_heads(a.slopes, a.heads, sp, heads_pre, heads_warm, w == 0);
@@ -445,6 +458,10 @@ __global__ __launch_bounds__(NT) void bwd_kv_kernel(BackwardArgs a, Segmented sp
 #pragma unroll
                 for (int v = 0; v < 16; ++v) R[db][v] = 0.f;
         }
+        const int comb_g = __builtin_amdgcn_readfirstlane(pc.comb_g);
+        if (comb_g > 0)
+            combine_start(R, *reinterpret_cast<const Segmented *>(sp_lds), uniform_ptr(pc.u), comb_g,
+                          __builtin_amdgcn_readfirstlane(pc.kg), uniform64(pc.covered), s2, qh, cq, lane);
         const long long len = uniform64(pc.len), warm = uniform64(pc.warm);
         const uint16_t *qg = uniform_ptr(pc.q), *kg = uniform_ptr(pc.k), *vg = uniform_ptr(pc.v);
         const uint16_t *gg = uniform_ptr(pc.g);
@@ -715,11 +732,6 @@ hipError_t launch(const BackwardArgs &a, const PrefillPlan &p, void *workspace, 
         const long long pre = uh * p.pieces < kPrepassActive + uh ? uh * p.pieces : kPrepassActive + uh;
         hipLaunchKernelGGL(rev_piece_kernel, dim3((unsigned)pre), dim3(NT), 0, stream, a, sp, ws);
         hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(uh * kCombineSlices)), dim3(kCombineThreads),
-                           0, stream, a.slopes, a.heads, a.d_state_out, false, sp,
-                           SeqLens{nullptr, (long long)a.units * a.seqlen, a.seqlen}, ws);
-        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL((bwd_kv_kernel<OutT>), dim3((unsigned)(uh * sp.segments)), dim3(NT), 0, stream,

@@ -90,7 +90,7 @@ struct PrefillPlan {
 // fp32 d x d states per (unit, head) in the workspace of a segmented plan:
 // one per piece, one partial state per segment boundary, one carried-in state
 // per segment.
-constexpr long long prefill_states(int segments, int pieces) { return pieces + 2LL * segments - 1; }
+constexpr long long prefill_states(int segments, int pieces) { return pieces + (long long)segments; }
 
 // HIP keeps the last error of any runtime call until it is read. Launchers
 // clear it first, so the check after a launch reports that launch only and not

@@ -154,8 +154,8 @@ PrefillPlan plan_prefill(long long units, long long seqlen, int heads, lt_dtype 
                          bool varlen, long long prepass_wgs, size_t max_workspace) {
     // bf16 plans, by the number of (sequence, head) pairs uh:
     //   uh >= 256: one whole-head workgroup per pair;
-    //   long sequences: whole heads cut into segments, with the pre-pass and
-    //     combine pass (its extra k, v reads cost less than re-reading q, k per
+    //   long sequences: whole heads cut into segments, with the pre-pass (its
+    //     extra k, v reads cost less than re-reading q, k per
     //     value slice, which measured 4.05 TB/s memory-only against 5.2 TB/s);
     //     packed batches cut on their longest sequence (seqlen = max_seqlen),
     //     each sequence using the segments its own length needs;
@@ -190,7 +190,7 @@ PrefillPlan plan_prefill(long long units, long long seqlen, int heads, lt_dtype 
     if (bytes(pieces) > max_workspace) {
         // longer pieces: as many states as fit (at least one piece per segment
         // boundary, i.e. pieces of a whole segment)
-        const long long fit = (long long)(max_workspace / kStateBytes / (size_t)uh) - (2 * g - 1);
+        const long long fit = (long long)(max_workspace / kStateBytes / (size_t)uh) - g;
         if (fit < g - 1) {
             p.workspace_short = true;
             return p;

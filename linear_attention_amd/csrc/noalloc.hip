@@ -17,9 +17,9 @@
 namespace {
 
 // 64 MiB. The coarsest segmented plan (one pre-pass piece per segment) holds
-// 3G - 2 states of 64 KiB per (sequence, head) pair, with at most
-// G = ceil(256 / u) segments for u < 256 pairs; u (3 ceil(256 / u) - 2) peaks
-// at u = 255 (1,020 states, 63.75 MiB), so every accepted call fits and the
+// 2G - 1 states of 64 KiB per (sequence, head) pair, with at most
+// G = ceil(256 / u) segments for u < 256 pairs; u (2 ceil(256 / u) - 1) peaks
+// at u = 255 (765 states, 47.8 MiB), so every accepted call fits and the
 // planner takes the finest pieces that do.
 constexpr size_t kScratchBytes = size_t(64) << 20;
 

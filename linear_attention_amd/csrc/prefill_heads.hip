@@ -101,11 +101,15 @@ __device__ __forceinline__ void store_rows_norm_gate(OutT *out, long long ts, co
 // Pre-pass: workgroup (unit, head, piece j) runs the state update over the
 // full 64-token sub-blocks of its group of pieces without outputs, writing its
 // state and, if a segment boundary falls strictly inside the group, B_g on the
-// way.
+// way. Workgroup b < units * heads first resets the records of pair b if that
+// pair takes warm-up ranges.
 __global__ __launch_bounds__(NT, 2) void piece_state_kernel(PrefillArgs a, Segmented sp, float *ws) {
     __shared__ __attribute__((aligned(16))) __bf16 Ks[C * D];
     __shared__ __attribute__((aligned(16))) __bf16 Vds[C * D];
     __shared__ short heads_pre[kMaxPairs], heads_warm[kMaxPairs];
+
+    if ((int)blockIdx.x < a.units * a.heads && !takes_prepass(sp, a.slopes[blockIdx.x % a.heads] * LOG2E))
+        reset_records(warm_records(sp, ws, blockIdx.x), NT);
 
     // workgroup b takes group b % gph of the (b / gph)-th pre-pass pair (in
     // (unit, head) order), gph groups of kgr pieces per pair; the working
@@ -225,6 +229,8 @@ struct Piece {
     const float *s_in;  // carried-in state (nullptr: zero)
     float *dst;         // end == 1: the final state's destination
     int *rec;           // end == 2: the pair's records
+    float *u;           // comb_g > 0: the pair's workspace unit
+    long long covered;  // comb_g > 0: the pair's pre-pass tokens
     long long len, warm;  // tokens of the piece; warm-up tokens before it (whole sub-blocks)
     float s2, eps;
     int ts;
@@ -232,6 +238,8 @@ struct Piece {
     int s_in_t;  // s_in transposed
     int cut;     // end == 2: the token the piece ends at
     int end;     // 0 nothing, 1 the final state to dst, 2 records if the end state is non-finite
+    int comb_g;  // > 0: segment comb_g of a pre-pass pair, whose start state the piece combines
+    int kg;      // comb_g > 0: pre-pass pieces per group
 };
 template <typename OutT>
 __device__ void piece_rows(Piece &p, const PrefillArgs &a, int n, int h, long long t0, long long t1,
@@ -270,7 +278,7 @@ __device__ void warm_piece(Piece &p, const PrefillArgs &a, const Segmented &sp, 
         p.end = 2;
     } else if (a.state_out) {
         // on in-place calls other pieces of the pair may still read S_0
-        p.dst = a.state_in == a.state_out ? Segmented::slot(sp.unit(ws, p.uh), 1) : a.state_out + sb;
+        p.dst = a.state_in == a.state_out ? sp.final_state(sp.unit(ws, p.uh)) : a.state_out + sb;
         p.end = 1;
     }
 }
@@ -294,11 +302,21 @@ __device__ Piece next_piece(const PrefillArgs &a, const Segmented &sp, float *ws
         p.s_in_t = a.state_in_t;
         p.dst = a.state_out ? a.state_out + sb : nullptr;
         p.end = p.dst ? 1 : 0;
-    } else if (r.kind == 1) {  // one segment of a pre-pass pair
+    } else if (r.kind == 1) {  // one segment of a pre-pass pair: S_0, then the combine of the pieces before it
         piece_rows<OutT>(p, a, r.n, r.h, r.t0, r.t1, r.t0);
-        p.s_in = sp.start_state(sp.unit(ws, p.uh), r.g);  // the combine pass wrote it (S_0 for g = 0)
-        p.dst = a.state_out && r.g == sp.used(r.len) - 1 ? a.state_out + (size_t)p.uh * D * D : nullptr;
-        p.end = p.dst ? 1 : 0;
+        const size_t sb = (size_t)p.uh * D * D;
+        float *u = sp.unit(ws, p.uh);
+        p.s_in = a.state_in ? a.state_in + sb : nullptr;
+        p.s_in_t = a.state_in_t;
+        p.u = u;
+        p.comb_g = r.g;
+        p.kg = prepass_group_of(ps.npre, a.units, sp);
+        p.covered = sp.covered(r.len);
+        if (a.state_out && r.g == sp.used(r.len) - 1) {
+            // on in-place calls the pair's other segments may still read S_0
+            p.dst = a.state_in == a.state_out ? sp.final_state(u) : a.state_out + sb;
+            p.end = 1;
+        }
     } else {
         warm_piece<OutT>(p, a, sp, ws, r.n, r.h, r.t0, r.t1, r.len);
     }
@@ -340,7 +358,8 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
     }
 
     // ---- this workgroup's work: pieces (pair uh, tokens [t0, t1)), each
-    // starting from the pre-pass's start state, S_0, zero, and a warm-up
+    // starting from S_0 (combined with the pre-pass's states of the earlier
+    // tokens on the pre-pass route), zero, and a warm-up
     int mode;  // 0: one pair, whole (no segments); 1: one pre-pass segment; 2: warm ranges
     if (segments == 1) {
         mode = 0;
@@ -422,6 +441,10 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
 #pragma unroll
                 for (int v = 0; v < 16; ++v) S[db][v] = 0.f;
         }
+        const int comb_g = __builtin_amdgcn_readfirstlane(pc.comb_g);
+        if (comb_g > 0)
+            combine_start(S, *reinterpret_cast<const Segmented *>(sp_lds), uniform_ptr(pc.u), comb_g,
+                          __builtin_amdgcn_readfirstlane(pc.kg), uniform64(pc.covered), s2, qh, cq, lane);
 
         // this piece's rows: a warm-up over [t0w, t0) (whole sub-blocks, an
         // even number), then its tokens
@@ -875,9 +898,18 @@ __global__ __launch_bounds__(NT) void finish_kernel(PrefillArgs a, Segmented sp,
     __shared__ int mincut;
     const int tid = threadIdx.x;
     const int uh = blockIdx.x, h = uh % a.heads, n = uh / a.heads;
-    if (takes_prepass(sp, a.slopes[h] * LOG2E)) return;
     const long long len = SeqLens{a.cu_seqlens, a.total_tokens, a.seqlen}.len(n);
     const size_t sb = (size_t)uh * D * D;
+    const bool in_place = a.state_in && a.state_in == a.state_out;
+    if (takes_prepass(sp, a.slopes[h] * LOG2E)) {  // the pre-pass route: only an in-place final state
+        if (in_place) {
+            const float4 *src = reinterpret_cast<const float4 *>(sp.final_state(sp.unit(ws, uh)));
+            float4 *dst = reinterpret_cast<float4 *>(a.state_out + sb);
+#pragma unroll
+            for (int j = 0; j < kStateF4; ++j) dst[threadIdx.x + NT * j] = src[threadIdx.x + NT * j];
+        }
+        return;
+    }
     if (len == 0) {  // no piece covers the pair: the final state is S_0
         if (a.state_out && a.state_out != a.state_in)
             for (int i = tid; i < D * D; i += NT) {
@@ -912,11 +944,10 @@ __global__ __launch_bounds__(NT) void finish_kernel(PrefillArgs a, Segmented sp,
                 if (t >= cut4[x]) poison(row + x);
         }
     }
-    const bool in_place = a.state_in && a.state_in == a.state_out;
     if (a.state_out && (in_place || first != kNoCut)) {
         // this thread's state elements: float4 tid + NT j (j < kStateF4)
         const unsigned *bad = reinterpret_cast<const unsigned *>(rec + kRecEntBad);
-        const float4 *src = reinterpret_cast<const float4 *>(in_place ? Segmented::slot(sp.unit(ws, uh), 1)
+        const float4 *src = reinterpret_cast<const float4 *>(in_place ? sp.final_state(sp.unit(ws, uh))
                                                                       : a.state_out + sb);
         float4 *dst = reinterpret_cast<float4 *>(a.state_out + sb);
 #pragma unroll
@@ -952,11 +983,6 @@ hipError_t launch(const PrefillArgs &a, const PrefillPlan &p, void *workspace, h
         const long long pre = uh * p.pieces < kPrepassActive + uh ? uh * p.pieces : kPrepassActive + uh;
         hipLaunchKernelGGL(piece_state_kernel, dim3((unsigned)pre), dim3(NT), 0, stream, a, sp, ws);
         hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(uh * kCombineSlices)), dim3(kCombineThreads),
-                           0, stream, a.slopes, a.heads, a.state_in, a.state_in_t, sp,
-                           SeqLens{a.cu_seqlens, a.total_tokens, a.seqlen}, ws);
-        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const dim3 grid((unsigned)(uh * p.segments));

@@ -108,16 +108,26 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// The streams live in device memory. Their accesses go through global-address-
+// space pointers: a generic pointer that the compiler cannot trace back to a
+// kernel argument (one read back from LDS, as the piece loops do) would get
+// flat loads and stores instead, and on this GPU a flat access counts against
+// the LDS wait counter too, so every wait for an LDS operand would also wait
+// for the sub-block prefetches in flight.
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(1))) T *global_view(T *p) {
+    return (__attribute__((address_space(1))) T *)p;
+}
 __device__ __forceinline__ uint4 stream_load16(const uint16_t *p) {
-    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    const u32x4 x = __builtin_nontemporal_load(global_view(reinterpret_cast<const u32x4 *>(p)));
     return make_uint4(x.x, x.y, x.z, x.w);
 }
 __device__ __forceinline__ uint2 stream_load8(const uint16_t *p) {
-    const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+    const u32x2 x = __builtin_nontemporal_load(global_view(reinterpret_cast<const u32x2 *>(p)));
     return make_uint2(x.x, x.y);
 }
 __device__ __forceinline__ void stream_store(float *p, float4 x) {
-    __builtin_nontemporal_store(f32x4{x.x, x.y, x.z, x.w}, reinterpret_cast<f32x4 *>(p));
+    __builtin_nontemporal_store(f32x4{x.x, x.y, x.z, x.w}, global_view(reinterpret_cast<f32x4 *>(p)));
 }
 template <class V>
 __device__ __forceinline__ void stream_store_bits(__bf16 *p, const V &x) {
@@ -125,11 +135,11 @@ __device__ __forceinline__ void stream_store_bits(__bf16 *p, const V &x) {
     if constexpr (sizeof(V) == 16) {
         u32x4 b;
         __builtin_memcpy(&b, &x, 16);
-        __builtin_nontemporal_store(b, reinterpret_cast<u32x4 *>(p));
+        __builtin_nontemporal_store(b, global_view(reinterpret_cast<u32x4 *>(p)));
     } else {
         u32x2 b;
         __builtin_memcpy(&b, &x, 8);
-        __builtin_nontemporal_store(b, reinterpret_cast<u32x2 *>(p));
+        __builtin_nontemporal_store(b, global_view(reinterpret_cast<u32x2 *>(p)));
     }
 }
 
@@ -301,9 +311,10 @@ __device__ __forceinline__ SeqRange sequence_of(const PrefillArgs &a, int n) {
 //   [P_0 .. P_{pieces-1}]       state of each piece's tokens from a zero state
 //   [B_1 .. B_{segments-1}]     for a boundary inside a piece: the state of that
 //                               piece's tokens before the boundary
-//   [S_0 .. S_{segments-1}]     state at the start of each segment
-// (pairs on the warm-up route use slots 0 and 1 of theirs instead: the records
-// of their ranges' non-finite end states, and an in-place final state).
+//   [F]                         the final state of an in-place call
+// (pairs on the warm-up route use slot 0 of theirs for the records of their
+// ranges' non-finite end states, and F). The workgroups of a segment combine
+// its start state from the P and B states themselves (combine_start).
 // A state of tokens [t0, t1) from zero is sum_t e^{-s(t1-1-t)} k_t^T v_t, and
 // states compose as S(t2) = e^{-s(t2-t1)} S(t1) + state of [t1, t2).
 // Warm-up ranges. A range of a sequence that starts at token t0 > 0 computes
@@ -355,13 +366,13 @@ struct Segmented {
     }
     __device__ long long covered(long long len) const { return (long long)(used(len) - 1) * seg_len; }
     __device__ float *unit(float *ws, int uh) const {
-        return ws + (size_t)uh * (size_t)(pieces + 2 * segments - 1) * D * D;
+        return ws + (size_t)uh * (size_t)(pieces + segments) * D * D;
     }
     __device__ static float *slot(float *u, long long i) { return u + (size_t)i * D * D; }
     __device__ float *piece_state(float *u, int j) const { return slot(u, j); }
     __device__ int partial_slot(int g) const { return pieces + g - 1; }
     __device__ float *partial(float *u, int g) const { return slot(u, partial_slot(g)); }
-    __device__ float *start_state(float *u, int g) const { return slot(u, pieces + segments - 1 + g); }
+    __device__ float *final_state(float *u) const { return slot(u, pieces + segments - 1); }
 };
 
 __device__ __forceinline__ bool nonfinite(float x) {
@@ -396,7 +407,7 @@ __device__ __forceinline__ bool takes_prepass(const Segmented &sp, float s2) {
 }
 
 // Warm-up route records, in slot 0 of each warm pair's workspace unit, reset by
-// the combine pass before the main kernel runs. A range that ends at token t
+// the pre-pass kernel (reset_records) before the main kernel runs. A range that ends at token t
 // inside its pair and leaves a NaN or Inf in entry (r, c) of its end state
 // (forward: S; backward: the carry R, t counted in mirrored order) records
 //   ints [0, D)            per column c, the earliest such t (kNoCut: none);
@@ -404,13 +415,17 @@ __device__ __forceinline__ bool takes_prepass(const Segmented &sp, float s2) {
 //                          state;
 //   ints [kRecRowCut, +D)  per row r, the earliest such t (backward only);
 //   int kFineCounter       (first warm pair only) the next fine chunk to hand out.
-// Slot 1 holds the pair's final state on in-place forward calls.
 constexpr int kRecColCut = 0, kRecEntBad = D, kRecRowCut = D + D * D / 32, kRecInts = 2 * D + D * D / 32;
 constexpr int kFineCounter = 1024;
 constexpr int kNoCut = 0x7fffffff;
 static_assert(kRecInts <= kFineCounter, "warm records");
 __device__ __forceinline__ int *warm_records(const Segmented &sp, float *ws, int uh) {
     return reinterpret_cast<int *>(Segmented::slot(sp.unit(ws, uh), 0));
+}
+// Every thread of a workgroup of nt threads.
+__device__ inline void reset_records(int *rec, int nt) {
+    for (int i = threadIdx.x; i < kRecInts; i += nt) rec[i] = i < kRecEntBad || i >= kRecRowCut ? kNoCut : 0;
+    if (threadIdx.x == 0) rec[kFineCounter] = 0;
 }
 // The finishing passes' NaN, and the float4 elements of a d x d state per
 // thread of a workgroup.
@@ -729,75 +744,50 @@ __device__ inline int prepass_group(const float *slopes, int heads, int units, c
     return prepass_group_of(__builtin_amdgcn_readfirstlane(npre), units, sp);
 }
 
-// Combine pass: the state at every segment start, S_0 being the first state
-// (the carried-in state, or zero). Workgroup (unit, head, 1024-element slice) walks the pieces
-// (groups of pieces, above) in order with 4 elements per thread:
-//   acc <- e^{-s len_j} acc + P_j,
-// and at each boundary b_g: S_g = acc if b_g ends group j, or
-// e^{-s(b_g - start_j)} acc + B_g if it falls inside group j.
-constexpr int kCombineThreads = 256;
-constexpr int kCombineSlices = D * D / (4 * kCombineThreads);
-
-// s0: [units, heads, d, d] first state (null: zero); s0_t: given transposed.
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float *slopes, int heads,
-                                                                   const float *s0, bool s0_t,
-                                                                   Segmented sp, SeqLens sl, float *ws) {
-    const int uh = blockIdx.x / kCombineSlices;
-    const int e = 4 * ((blockIdx.x % kCombineSlices) * kCombineThreads + threadIdx.x);
-    const int h = uh % heads;
-    const float s2 = slopes[h] * LOG2E;
-    if (!takes_prepass(sp, s2)) {  // warm-up ranges: no pre-pass states
-        if (blockIdx.x % kCombineSlices == 0) {  // reset the warm-up route's records
-            int *rec = warm_records(sp, ws, uh);
-            for (int i = threadIdx.x; i < kRecInts; i += kCombineThreads)
-                rec[i] = i < kRecEntBad || i >= kRecRowCut ? kNoCut : 0;
-            if (threadIdx.x == 0) rec[kFineCounter] = 0;
-        }
-        return;
-    }
-    float *u = sp.unit(ws, uh);
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (s0) {
-        const float *si = s0 + (size_t)uh * D * D;
-        if (s0_t) {  // element (r, c) at c * D + r
-            const int r = e / D, c = e % D;
-            acc = make_float4(si[c * D + r], si[(c + 1) * D + r], si[(c + 2) * D + r], si[(c + 3) * D + r]);
-        } else {
-            acc = *reinterpret_cast<const float4 *>(si + e);
-        }
-    }
-    *reinterpret_cast<float4 *>(sp.start_state(u, 0) + e) = acc;
-    const long long covered = sp.covered(sl.len(uh / heads));
-    const int kg = prepass_group(slopes, heads, (int)(gridDim.x / kCombineSlices) / heads, sp);
-    const int groups = (int)((covered + kg * sp.piece_len - 1) / (kg * sp.piece_len));
-    auto last_piece = [&](int j) { return (j + 1) * kg - 1 < sp.pieces - 1 ? (j + 1) * kg - 1 : sp.pieces - 1; };
-    // the group states are independent loads: issue a batch of them ahead of
-    // the sequential accumulation (this kernel never writes piece slots)
-    constexpr int kBatch = 8;
-    for (int j0 = 0; j0 < groups; j0 += kBatch) {
-        float4 pj[kBatch];
+// Start state of segment g >= 1 of a pair on the pre-pass route, in each
+// thread's accumulator blocks S (wave w: rows 64(w/4).., columns 32(w%4)..;
+// entry (db, v) at row 64(w/4) + 32db + 8(v/4) + 4(lane/32) + v%4, column
+// 32(w%4) + lane%32, as the pre-pass stores its states), which hold the first
+// state S_0 on entry: the pre-pass group states (kg pieces each; the last group
+// ends at `covered`) combined in order,
+//   S <- e^{-s len_j} S + P_j,
+// over the groups that end at or before b = g seg_len, then, if b falls inside
+// the next group j, S <- e^{-s(b - start_j)} S + B_g. A group never exceeds one
+// segment, so the group holding b is the one whose partial state is B_g. The
+// states are loaded kCombineBatch at a time ahead of their updates (more keep
+// too many registers live in the main kernels, which then spill).
+constexpr int kCombineBatch = 2;
+__device__ inline void combine_start(f32x16 (&S)[2], const Segmented &sp, float *u, int g, int kg,
+                                     long long covered, float s2, int qh, int cq, int lane) {
+    const long long b = (long long)g * sp.seg_len, glen = (long long)kg * sp.piece_len;
+    const int nfull = (int)(b / glen);                  // groups 0 .. nfull-1 end at or before b
+    const int n = nfull + ((long long)nfull * glen < b);  // and the part of group nfull before b
+    const int base = (64 * qh + 4 * (lane >> 5)) * D + 32 * cq + (lane & 31);
+    auto src = [&](int j) {
+        // group nfull ends at covered = b on the last segment (a whole group),
+        // else b is strictly inside it (its partial state B_g)
+        const int lp = (j + 1) * kg - 1 < sp.pieces - 1 ? (j + 1) * kg - 1 : sp.pieces - 1;
+        return j < nfull || covered <= b ? sp.piece_state(u, lp) : sp.partial(u, g);
+    };
+    for (int j0 = 0; j0 < n; j0 += kCombineBatch) {
+        float x[kCombineBatch][32];
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i)
-            if (j0 + i < groups) pj[i] = *reinterpret_cast<const float4 *>(sp.piece_state(u, last_piece(j0 + i)) + e);
+        for (int i = 0; i < kCombineBatch; ++i) {
+            const float *p = src(j0 + i < n ? j0 + i : n - 1);
 #pragma unroll
-        for (int i = 0; i < kBatch; ++i) {
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) x[i][16 * db + v] = p[base + (32 * db + 8 * (v >> 2) + (v & 3)) * D];
+        }
+#pragma unroll
+        for (int i = 0; i < kCombineBatch; ++i) {
             const int j = j0 + i;
-            if (j >= groups) break;
-            const long long t0 = (long long)j * kg * sp.piece_len;
-            const long long t1 = t0 + kg * sp.piece_len < covered ? t0 + kg * sp.piece_len : covered;
-            const int gb = (int)(t0 / sp.seg_len) + 1;
-            const long long b = gb * sp.seg_len;
-            if (b < t1) {
-                const float f = fast_exp2(-s2 * (float)(b - t0));
-                const float4 p = *reinterpret_cast<const float4 *>(sp.partial(u, gb) + e);
-                *reinterpret_cast<float4 *>(sp.start_state(u, gb) + e) =
-                    make_float4(f * acc.x + p.x, f * acc.y + p.y, f * acc.z + p.z, f * acc.w + p.w);
-            }
-            const float f = fast_exp2(-s2 * (float)(t1 - t0));
-            const float4 p = pj[i];
-            acc = make_float4(f * acc.x + p.x, f * acc.y + p.y, f * acc.z + p.z, f * acc.w + p.w);
-            if (t1 % sp.seg_len == 0)
-                *reinterpret_cast<float4 *>(sp.start_state(u, (int)(t1 / sp.seg_len)) + e) = acc;
+            if (j >= n) break;
+            const float f = fast_exp2(-s2 * (float)(j < nfull ? glen : b - (long long)j * glen));
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) S[db][v] = f * S[db][v] + x[i][16 * db + v];
         }
     }
 }

@@ -156,18 +156,18 @@ def test_workspace_query():
     ws = la.lt_prefill_workspace_bytes
     st = 128 * 128 * 4  # one fp32 state
     # Segmented plan: per (sequence, head) one state per pre-pass piece, one
-    # partial state per segment boundary and one start state per segment; the
+    # partial state per segment boundary and one for an in-place final state; the
     # query covers the finer of the two pre-pass granularities (2048 pre-pass
     # workgroups for plain prefill, 512 for the norm-gate variants).
     # batch 1, 64 heads, 32K tokens: 4 segments of 8192; 24576 covered tokens
     # in 32 pieces of 768
-    assert ws(1, 32768, 64) == 64 * (32 + 2 * 4 - 1) * st
+    assert ws(1, 32768, 64) == 64 * (32 + 4) * st
     # batch 1, 8 heads, 32K tokens: 16 segments of 2048; 30720 covered tokens
     # in 60 pieces of 512 (the shortest piece) at either granularity
-    assert ws(1, 32768, 8) == 8 * (60 + 2 * 16 - 1) * st
+    assert ws(1, 32768, 8) == 8 * (60 + 16) * st
     # batch 1, 2 heads, 1M tokens: 128 segments of 8192; 127 * 8192 covered
     # tokens in 1016 pieces of 1024
-    assert ws(1, 1 << 20, 2) == 2 * (1016 + 2 * 128 - 1) * st
+    assert ws(1, 1 << 20, 2) == 2 * (1016 + 128) * st
     assert ws(1, 3000, 64) == 0           # short: value slices, no workspace
     assert ws(4, 32768, 64) == 0          # 256 (sequence, head) pairs already fill the GPU
     assert ws(1, 2048, 64) == 0           # too short to split
@@ -204,7 +204,7 @@ def test_varlen_workspace_query():
     st = 128 * 128 * 4
     # 2 sequences x 64 heads, longest 131072 tokens: 2 segments of 65536, the
     # first covered by 16 pre-pass pieces of 4096 (2048 pre-pass workgroups)
-    assert ws(2, 131072, 64) == 2 * 64 * (16 + 2 * 2 - 1) * st
+    assert ws(2, 131072, 64) == 2 * 64 * (16 + 2) * st
     # the fixed-length plan of the same longest length
     assert ws(2, 131072, 64) == la.lt_prefill_workspace_bytes(2, 131072, 64)
     assert ws(16, 65536, 64) == 0          # 1024 (sequence, head) pairs: no split
