@@ -33,6 +33,8 @@
 #include <stdint.h>
 
 #include <numeric>
+#include <type_traits>
+#include <utility>
 
 #include "internal.h"
 #include "tiles.h"
@@ -59,6 +61,16 @@ constexpr bf16x2 kOnes2 = {(__bf16)1.f, (__bf16)1.f};
 // Growth of a score over the running reference maximum (log2 units) that is
 // let pass before O and l are rescaled.
 constexpr float kStale = 8.f;
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
+template <int N, class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
 
 __device__ __forceinline__ float bf2f(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
 __device__ __forceinline__ uint16_t f2bf(float f) {
@@ -240,34 +252,38 @@ __global__ __launch_bounds__(FNT) void fa_prefill_kernel(SoftmaxArgs a, const ui
     const int ts = a.kv_heads * D;                             // token stride (elements)
     const long long kend = q0 + geo.qpw < L ? q0 + geo.qpw : L; // keys [0, kend)
     const int nkb = (int)((kend + SKB - 1) / SKB);
-    // staging: thread t holds block rows t/16 and t/16 + 32, features
+    // staging: thread t holds block rows t/16 + (FNT/16) i, features
     // 8(t%16)..; rows past the end repeat the last key (masked later)
+    constexpr int kSR = FNT / 16, kNR = SKB / kSR;  // rows per pass, passes
     const int srow = tid >> 4, scol = 8 * (tid & 15);
-    uint4 sk0, sk1, sv0, sv1;
-#define LT_FA_LOAD(KB)                                                                      \
-    {                                                                                       \
-        const long long k0_ = (long long)(KB) * SKB;                                        \
-        const uint16_t *kb_ = kg + k0_ * ts, *vb_ = vg + k0_ * ts;                          \
-        const int last_ = L - 1 - k0_ < SKB - 1 ? (int)(L - 1 - k0_) : SKB - 1;             \
-        const int o0_ = min(srow, last_) * ts + scol, o1_ = min(srow + 32, last_) * ts + scol; \
-        sk0 = *reinterpret_cast<const uint4 *>(kb_ + o0_);                                  \
-        sk1 = *reinterpret_cast<const uint4 *>(kb_ + o1_);                                  \
-        sv0 = *reinterpret_cast<const uint4 *>(vb_ + o0_);                                  \
-        sv1 = *reinterpret_cast<const uint4 *>(vb_ + o1_);                                  \
-    }
-    if (nkb > 0) LT_FA_LOAD(0)
-    for (int kb = 0; kb < nkb; ++kb) {
+    u32x4 skr[kNR], svr[kNR];  // native vectors: arrays of uint4 (a union type) stayed in scratch
+    // (indices fixed at compile time, so the staging stays in registers)
+    auto fa_load = [&](int kb) {
+        const long long k0 = (long long)kb * SKB;
+        const uint16_t *kb_ = kg + k0 * ts, *vb_ = vg + k0 * ts;
+        const int last = L - 1 - k0 < SKB - 1 ? (int)(L - 1 - k0) : SKB - 1;
+        static_for<kNR>([&](auto I) {
+            const int o = min(srow + kSR * (int)I, last) * ts + scol;
+            skr[I] = *reinterpret_cast<const u32x4 *>(kb_ + o);
+            svr[I] = *reinterpret_cast<const u32x4 *>(vb_ + o);
+        });
+    };
+    if (nkb > 0) fa_load(0);
+    // key block kb; MASKED: the block reaches the diagonal of some query of
+    // the wave or the end of the sequence
+    auto block = [&](int kb, auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
         // double-buffered tiles: buffer kb&1 was last read in block kb-2, which
         // every wave finished before the barrier of block kb-1
         __bf16 *Kb = Ks[kb & 1], *Vb = Vs[kb & 1];
-        *reinterpret_cast<uint4 *>(Kb + LK::off(srow, scol)) = sk0;
-        *reinterpret_cast<uint4 *>(Kb + LK::off(srow + 32, scol)) = sk1;
-        *reinterpret_cast<uint4 *>(Vb + LV::off(srow, scol)) = sv0;
-        *reinterpret_cast<uint4 *>(Vb + LV::off(srow + 32, scol)) = sv1;
-        if (kb + 1 < nkb) LT_FA_LOAD(kb + 1)
+        static_for<kNR>([&](auto I) {
+            *reinterpret_cast<u32x4 *>(Kb + LK::off(srow + kSR * (int)I, scol)) = skr[I];
+            *reinterpret_cast<u32x4 *>(Vb + LV::off(srow + kSR * (int)I, scol)) = svr[I];
+        });
+        if (kb + 1 < nkb) fa_load(kb + 1);
         __syncthreads();  // tiles visible
         const long long k0 = (long long)kb * SKB;
-        if (k0 > qlast) continue;  // every key of this block is after the wave's queries
+        if (k0 > qlast) return;  // every key of this block is after the wave's queries
 
         // S^T blocks: keys k0 + 32kk.., this lane's query column; the two
         // halves interleave and each step's K operands load one step ahead
@@ -291,9 +307,8 @@ __global__ __launch_bounds__(FNT) void fa_prefill_kernel(SoftmaxArgs a, const ui
                 ka1 = kn1;
             }
         }
-        // causal mask (and keys past the end) on blocks that reach the diagonal
-        // (a wave-uniform test); key 32kk + 8(v/4) + 4hf + v%4 of the block
-        if (k0 + SKB - 1 > qw0 || k0 + SKB > L) {
+        // causal mask (and keys past the end); key 32kk + 8(v/4) + 4hf + v%4 of the block
+        if constexpr (MASKED) {
             const int lim_q = (int)(qrow - k0);  // last key of this lane's query
             const int lim_l = (int)(L - 1 - k0 < SKB ? L - 1 - k0 : SKB);
             const int lim = lim_q < lim_l ? lim_q : lim_l;
@@ -352,9 +367,17 @@ __global__ __launch_bounds__(FNT) void fa_prefill_kernel(SoftmaxArgs a, const ui
                 for (int c = 0; c < 4; ++c) va[c] = vn[c];
             }
         }
-    }
-
-#undef LT_FA_LOAD
+    };
+    // Blocks that end at or before the first query of every wave and inside
+    // the sequence take no mask (done as selects, the mask was a third of the
+    // loop's vector instructions); the waves of a workgroup may differ in
+    // their first query, so the split is at the smallest.
+    const long long qmin = q0;  // first query of the workgroup
+    int nfree = (int)((qmin + 1) / SKB);  // blocks [0, nfree): keys <= q0 for every query
+    if ((long long)nfree * SKB > L) nfree = (int)(L / SKB);
+    if (nfree > nkb) nfree = nkb;
+    for (int kb = 0; kb < nfree; ++kb) block(kb, std::false_type{});
+    for (int kb = nfree; kb < nkb; ++kb) block(kb, std::true_type{});
 
     // ---- normalise and store this lane's query row (value dims 32c + 8gv + 4hf..)
     lsum += __shfl_xor(lsum, 32);
