@@ -236,8 +236,8 @@ def run_m1_prefill(la, torch, steps, warmup, slope_scale=1.0):
     nbytes = prefill_bytes(tokens, w.heads)
     res = {"tokens_per_s": tokens * steps / wall, "ms_per_step": wall * 1e3 / steps, "kernel_ms_mean": ms,
            "kernel_ms_median": med,
-           "roofline": hbm_roofline(nbytes, ms, "lt_prefill call: piece_state_kernel + combine_kernel + "
-                                    "head_kernel<float> + finish_kernel<float, false>",
+           "roofline": hbm_roofline(nbytes, ms, "lt_prefill call: piece_state_kernel + "
+                                    "head_kernel<float, false> + finish_kernel<float, false>",
                                     committed_traffic("m1_layer") if slope_scale == 1.0 else None)}
     return w, (q, k, v, slopes), res
 
@@ -265,7 +265,7 @@ def run_norm_gate(la, torch, steps, warmup):
     return {"workload": w.name + " + norm_gate", "gate_dtype": "bf16", "out_dtype": "bf16",
             "tokens_per_s": round(tokens / (ms / 1e3), 1), "kernel_ms_mean": round(ms, 5),
             "roofline": hbm_roofline(nbytes, ms, "lt_prefill_norm_gate call: piece_state_kernel + "
-                                     "combine_kernel + head_kernel<bf16, norm-gate> + finish_kernel<bf16, true>")}
+                                     "head_kernel<bf16, norm-gate> + finish_kernel<bf16, true>")}
 
 
 def run_backward(la, torch, steps, warmup, batch, seqlen):
@@ -293,7 +293,7 @@ def run_backward(la, torch, steps, warmup, batch, seqlen):
     return {"workload": f"backward [{batch}, {seqlen}, {H}, {D}] bf16 -> fp32 grads",
             "tokens_per_s": round(tokens / (ms / 1e3), 1), "kernel_ms_mean": round(ms, 5),
             "roofline": hbm_roofline(nbytes, ms, "lt_prefill_backward call: dq forward pass + rev_piece_kernel "
-                                     "+ combine_kernel + bwd_kv_kernel + bwd_finish_kernel", committed_traffic(name))}
+                                     "+ bwd_kv_kernel + bwd_finish_kernel", committed_traffic(name))}
 
 
 def backward_cpu_baseline(min_seconds):
