@@ -33,7 +33,7 @@ Prints ONE JSON line. Besides the standard fields (metric, value, unit, steps, c
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps N]
                        [--no-cpu] [--no-configs] [--no-decode] [--no-norm-gate]
-                       [--no-backward] [--no-softmax] [--no-slopes-scaled]
+                       [--no-backward] [--no-softmax] [--no-slopes-scaled] [--no-settle]
        python bench.py --only WORKLOAD --steps K --warmup W
                        (one workload alone, for profiler passes: m1_layer,
                         decode, backward, tiny_f32, long_1m, varlen, varlen_2x131072)
@@ -121,12 +121,38 @@ def committed_traffic(workload):
     return entry.get("traffic_bytes_per_call")
 
 
+_SETTLE = {"on": True, "x": None}
+
+
+def settle_gpu(torch):
+    """About 30 ms of bf16 matrix products (hipBLASLt, nothing of this library)
+    before a timed workload. After the GPU has been idle, the first tens of
+    milliseconds of back-to-back work run in a slower state: M1-layer prefill
+    calls 6-25 of a burst after 0.5 s idle took 0.561-0.566 ms against 0.500 ms
+    once settled, and 0.495 ms from the first call on after these products (or
+    after 20 GB of plain copies). The timed region is unchanged: exactly
+    `steps` calls after `warmup` untimed ones. --no-settle turns it off."""
+    if not _SETTLE["on"]:
+        return
+    if _SETTLE["x"] is None:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(7)
+        _SETTLE["x"] = torch.randn((8192, 8192), device="cuda", dtype=torch.bfloat16, generator=g)
+    x = _SETTLE["x"]
+    for _ in range(40):
+        y = x @ x
+    torch.cuda.synchronize()
+    del y
+
+
 def time_calls(torch, call, steps, warmup, stream):
     """Mean and median call time (ms) from HIP events recorded on `stream` around
-    each of `steps` calls after `warmup` untimed ones, and the wall time (s) of
-    the timed calls bracketed by device synchronisations."""
+    each of `steps` calls after `warmup` untimed ones (and settle_gpu before
+    them), and the wall time (s) of the timed calls bracketed by device
+    synchronisations."""
     import numpy as np
 
+    settle_gpu(torch)
     for _ in range(warmup):
         call()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -750,16 +776,15 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    # Untimed calls before each timed workload. A burst of back-to-back prefill
-    # calls starts slow and settles after about 30 calls (M1 layer: calls 3-15 of
-    # a burst take 0.57-0.64 ms, calls 30-60 0.531-0.54 ms, every call 0.535 ms
-    # with the GPU idle for a millisecond before it); the timed calls measure the
-    # settled rate.
+    # Untimed calls before each timed workload (after settle_gpu; without it a
+    # burst of back-to-back calls after idle starts slow for about 30 calls).
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--cpu-tokens", type=int, default=32768)
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-settle", action="store_true",
+                    help="time from an idle GPU (no settle_gpu before each workload)")
     ap.add_argument("--no-configs", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-norm-gate", action="store_true")
@@ -775,6 +800,7 @@ def main():
     ap.add_argument("--calls", type=int, default=0, help="calls of the profiled --only run (warm-ups included)")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     args = ap.parse_args()
+    _SETTLE["on"] = not args.no_settle
     if args.traffic_from:
         traffic_from(*args.traffic_from, args.copy_bytes, args.traffic_workload, args.calls)
         return
@@ -900,6 +926,9 @@ def main():
         "roofline": pre["roofline"],
         "kernel_ms_mean": round(pre["kernel_ms_mean"], 5),
         "kernel_ms_median": round(pre["kernel_ms_median"], 5),
+        # before each timed workload: 40 bf16 8192^3 matrix products (settle_gpu)
+        # bring the GPU out of its post-idle state; null with --no-settle
+        "gpu_settle": "40 x bf16 8192^3 matmul before warm-up" if _SETTLE["on"] else None,
         # the same call with every slope scaled down (x0.1: 25 of the 64 heads
         # take the pre-pass; x1e-5: all of them)
         "prefill_slopes_scaled": scaled,
