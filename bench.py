@@ -929,7 +929,7 @@ def main():
         # before each timed workload: 40 bf16 8192^3 matrix products (settle_gpu)
         # bring the GPU out of its post-idle state; null with --no-settle
         "gpu_settle": "40 x bf16 8192^3 matmul before warm-up" if _SETTLE["on"] else None,
-        # the same call with every slope scaled down (x0.1: 25 of the 64 heads
+        # the same call with every slope scaled down (x0.1: 15 of the 64 heads
         # take the pre-pass; x1e-5: all of them)
         "prefill_slopes_scaled": scaled,
         "configs": configs,

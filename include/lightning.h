@@ -19,8 +19,8 @@
  * state does not depend on B: the block form is an exact re-association of the
  * per-token recurrence S <- e^{-s_h} S + k^T v, o = q S (the token sees its own
  * key). The kernels may leave out a finite carried-state term once its decay
- * factor e^{-s t} is below 2^-24 (the unit roundoff of fp32, and far below the
- * bf16 rounding of the products' operands).
+ * factor e^{-s t} is below 2^-16 (2^7 below the bf16 rounding of the state as
+ * an operand of the products, the kernels' dominant rounding).
  * lt_prefill, lt_prefill_varlen and lt_decode write the raw sum; the
  * *_norm_gate variants also apply the normalisation and gate that follow the
  * sum in the §03 data-flow figure before anything is stored.
@@ -42,7 +42,7 @@
  *    state, a slope) makes non-finite every output that the exact operator
  *    makes non-finite, on every launch plan (NaN or Inf: which of the two may
  *    differ from the exact result). The cutoff of carried-state terms below
- *    2^-24 is never applied to a carried-in state that holds a NaN or Inf.
+ *    2^-16 is never applied to a carried-in state that holds a NaN or Inf.
  *    Outputs the exact operator leaves finite stay finite and within rounding,
  *    with one exception: a NaN or Inf in v at token t can also make NaN, in the
  *    value columns it holds, the outputs of the earlier tokens of t's 64-token

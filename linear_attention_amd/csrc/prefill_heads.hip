@@ -30,7 +30,7 @@
 //    contributed by fixed pieces of every segment but the last (the same state
 //    update without outputs) into a workspace; segment g starts from
 //    e^{-s*start_g} S_0 plus each piece's state decayed to start_g.
-//  * Heads whose decay ends their memory well within a segment (below 2^-24
+//  * Heads whose decay ends their memory well within a segment (below 2^-16
 //    after W tokens, W < the segment length) skip the pre-pass. Their tokens
 //    are cut into ranges of equal cost, one per remaining workgroup, and a
 //    range that starts at token t0 > 0 first rebuilds its carried-in state

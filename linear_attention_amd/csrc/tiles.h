@@ -322,15 +322,16 @@ __device__ __forceinline__ SeqRange sequence_of(const PrefillArgs &a, int n) {
 // from S_0 when the sequence starts within them), by state-only steps. A term
 // of the state t tokens old carries the factor e^{-s t}, below 2^-kFixExp of
 // its own scale once t > kFixExp / s2 (s2 = s log2 e): with W past that, what
-// the window leaves out is under 2^-24 of its scale, the unit roundoff of fp32
-// (and 2^15 times below the rounding of the bf16 operands every product of the
-// path already carries). W is rounded up to whole pairs of 64-token sub-blocks
+// the window leaves out is under 2^-16 of its scale, 2^7 below the bf16
+// rounding of the state operand of every inter-block product (the path's
+// dominant error; in o the window changes a row by at most about 1e-5 relative
+// on unit-variance inputs). W is rounded up to whole pairs of 64-token sub-blocks
 // (with pieces starting at multiples of 128 tokens every warm-up is then an
 // even number of sub-blocks, which the main kernels' warm-up steps rely on); a
 // head whose W is shorter than a segment takes this route, the others the
 // pre-pass. The backward's reverse pass does the same in mirrored token order
 // (its carry composes like the forward state; see backward.hip).
-constexpr float kFixExp = 24.f;
+constexpr float kFixExp = 16.f;
 __device__ __forceinline__ long long warm_len(float s2) {
     if (!(s2 > 0.f)) return 1LL << 62;  // no decay (or NaN): never forgets
     const float t = kFixExp / s2;

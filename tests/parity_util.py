@@ -122,7 +122,7 @@ def max_rel_states(s_gpu, s_ref):
 # of lt_prefill (batch-1 style calls with fewer than 256 (sequence, head) pairs
 # and at least 4096 tokens per sequence): G = ceil(256 / (batch * heads))
 # segments, at most L / 2048, of seg = ceil(L / G) tokens rounded up to a
-# multiple of 128. A head with slope s whose warm-up W = 128 * floor((floor(24 /
+# multiple of 128. A head with slope s whose warm-up W = 128 * floor((floor(16 /
 # (s log2 e)) + 128) / 128) is shorter than a segment takes warm-up ranges
 # (cut at multiples of 128 tokens, each rebuilding its carried-in state from
 # the W tokens before it); the others take the pre-pass. The backward's reverse

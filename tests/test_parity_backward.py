@@ -102,8 +102,8 @@ def test_backward_long_sequence_without_workspace(la):
 @pytest.mark.parametrize("grad_dtype", ["f32", "bf16"])
 def test_backward_segmented_slope_mix(la, grad_dtype):
     """Segmented backward over heads on both routes of both passes: short-memory
-    heads (slopes 0.012, 0.02, 0.2, 1, 30) on warm-up ranges (warm-ups of 1,408,
-    896 and 128 tokens, against 2,304-token segments; the reverse pass's ranges
+    heads (slopes 0.012, 0.02, 0.2, 1, 30) on warm-up ranges (warm-ups of 1,024,
+    640 and 128 tokens, against 2,304-token segments; the reverse pass's ranges
     and fine chunks are cut from the end of the sequence, so its last piece
     holds the ragged first 9000 mod 64 tokens), 0 and 1e-6 on the pre-passes;
     carried-in state and final-state gradient."""

@@ -91,8 +91,8 @@ def check_states(g, r, what):
 
 
 # Slope mix of the segmented slope-mix test: heads 0-2 take the pre-pass (their
-# memory outlasts a 2304-token segment), 3-6 warm-up ranges (warm-ups of 832,
-# 128, 64 and 64 tokens; the ranges are about 2,250 tokens long).
+# memory outlasts a 2304-token segment), 3-6 warm-up ranges (warm-ups of 640,
+# 128, 128 and 128 tokens; the ranges are about 2,250 tokens long).
 MIX = np.array([0.0, 1e-6, 0.005, 0.02, 0.2, 1.0, 30.0], np.float32)
 # (tensor, head, token, feature, value): segment 0 is [0, 2304), 1 [2304, 4608),
 # 2 [4608, 6912), 3 [6912, 9000).
