@@ -288,6 +288,10 @@ __global__ __launch_bounds__(NT, 2) void rev_piece_kernel(BackwardArgs a, Segmen
 // bytes a warm-up token moves its q and dO rows (2 x 256 B) against the q, k,
 // v, dO rows and the dk, dv rows of an output token; the warm-up's steps run
 // below the streaming rate by the forward's factor.
+// Tokens per fine chunk of the reverse pass.
+constexpr long long kBwdFineChunk = 768;
+static_assert(kBwdFineChunk % 128 == 0, "pieces start at multiples of 128 tokens");
+
 template <typename OutT>
 __device__ constexpr double bwd_warm_cost() {
     return 1.25 * 512.0 / (1024.0 + 256.0 * sizeof(OutT));
@@ -413,14 +417,14 @@ __global__ __launch_bounds__(NT) void bwd_kv_kernel(BackwardArgs a, Segmented sp
         const int pw = a.units * rt.nwarm;  // warm pairs
         if (mode == 2 && w == 0)
             warm_plan(SeqLens{nullptr, (long long)a.units * a.seqlen, a.seqlen}, a.slopes, heads_warm, rt.nwarm,
-                      pw, (double)pw * segments, bwd_warm_cost<OutT>(), cpre, bulk, qlist, fq);
+                      pw, (double)pw * segments, bwd_warm_cost<OutT>(), kBwdFineChunk, cpre, bulk, qlist, fq);
         __syncthreads();  // cpre, bulk, qlist and fq are visible
         if (t0id == 0) {
             ps.npre = rt.npre;
             ps.nwarm = rt.nwarm;
             ps.pw = pw;
             if (mode == 2)
-                warm_plan_state(ps, cpre, fq, pw, segments, (int)((long long)blockIdx.x - pre_wgs),
+                warm_plan_state(ps, cpre, fq, pw, segments, (int)((long long)blockIdx.x - pre_wgs), kBwdFineChunk,
                                 warm_records(sp, ws, heads_warm[0]) + kFineCounter);  // in the first warm pair's records
         }
     }

@@ -384,15 +384,15 @@ __global__ __launch_bounds__(NT) void head_kernel(PrefillArgs a, Segmented sp, f
         mode = (long long)blockIdx.x < pre_wgs ? 1 : 2;
         const int pw = a.units * rt.nwarm;  // warm pairs
         if (mode == 2 && w == 0)
-            warm_plan(lens, a.slopes, heads_warm, rt.nwarm, pw, (double)pw * segments, warm_cost<OutT, NG>(), cpre,
-                      bulk, qlist, fq);
+            warm_plan(lens, a.slopes, heads_warm, rt.nwarm, pw, (double)pw * segments, warm_cost<OutT, NG>(), kFineChunk,
+                      cpre, bulk, qlist, fq);
         __syncthreads();  // cpre, bulk, qlist and fq are visible
         if (t0id == 0) {
             ps.npre = rt.npre;
             ps.nwarm = rt.nwarm;
             ps.pw = pw;
             if (mode == 2)
-                warm_plan_state(ps, cpre, fq, pw, segments, (int)((long long)blockIdx.x - pre_wgs),
+                warm_plan_state(ps, cpre, fq, pw, segments, (int)((long long)blockIdx.x - pre_wgs), kFineChunk,
                                 warm_records(sp, ws, heads_warm[0]) + kFineCounter);  // in the first warm pair's records
         }
     }

@@ -471,7 +471,7 @@ __device__ inline Routes split_heads(const float *slopes, int heads, const Segme
 // warm_len) share the remaining workgroups in two phases.
 //  * Fine chunks: about kFineFrac of the warm-up route's tokens, taken from the
 //    end of the pairs whose warm-up is at most kFineWarm tokens, nf chunks of
-//    kFineChunk tokens from each such pair that is long enough (at most half
+//    kFineChunk tokens (the forward's; the backward's kernel passes its own) from each such pair that is long enough (at most half
 //    its tokens). A workgroup that has finished its range takes the next
 //    chunk from a counter; chunk c is chunk c / Q of the (c % Q)-th of the Q
 //    such pairs, so the chunks in flight at any time spread over the heads
@@ -520,7 +520,8 @@ struct PlanState {
     int last;   // the last workgroup (takes every pair left)
     int nfine;     // fine chunks in all (nq pairs x nf chunks)
     int nq, nf;
-    int *counter;  // the fine-chunk counter
+    long long chunk;  // tokens per fine chunk
+    int *counter;     // the fine-chunk counter
 };
 
 // Wave 0 of a workgroup computes the warm-up route's plan into LDS: cpre (the
@@ -528,10 +529,11 @@ struct PlanState {
 // tokens), qlist and fq (the pairs that give fine chunks, their count and the
 // chunks per pair). Warm pair j (j < pw < 256) is head heads_warm[j % nwarm] of
 // unit j / nwarm; nwg workgroups share the ranges; a warm-up token costs wcost
-// output tokens. Lane l takes pairs 4l .. 4l+3. Every workgroup computes the
+// output tokens; fine chunks hold `chunk` tokens (a multiple of 128). Lane l takes pairs 4l .. 4l+3. Every workgroup computes the
 // same plan (the same fp64 operations on the same inputs).
 __device__ inline void warm_plan(const SeqLens &lens, const float *slopes, const short *heads_warm, int nwarm, int pw,
-                                 double nwg, double wcost, double *cpre, long long *bulk, short *qlist, int *fq) {
+                                 double nwg, double wcost, long long chunk, double *cpre, long long *bulk, short *qlist,
+                                 int *fq) {
     const int lane0 = threadIdx.x & 63;
     long long L[4], Wt[4], nf[4];
     double lsum = 0.0;
@@ -555,7 +557,7 @@ __device__ inline void warm_plan(const SeqLens &lens, const float *slopes, const
     long long lmax = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        if (Wt[i] <= kFineWarm && L[i] >= 2 * kFineChunk) {
+        if (Wt[i] <= kFineWarm && L[i] >= 2 * chunk) {
             ++nq0;
             lmax = L[i] > lmax ? L[i] : lmax;
         }
@@ -564,16 +566,16 @@ __device__ inline void warm_plan(const SeqLens &lens, const float *slopes, const
         const long long y = __shfl_xor(lmax, o);
         lmax = y > lmax ? y : lmax;
     }
-    long long nfw = nq0 > 0 ? (long long)(kFineFrac * lsum / ((double)nq0 * (double)kFineChunk)) : 0;
-    if (nfw > lmax / (2 * kFineChunk)) nfw = lmax / (2 * kFineChunk);
+    long long nfw = nq0 > 0 ? (long long)(kFineFrac * lsum / ((double)nq0 * (double)chunk)) : 0;
+    if (nfw > lmax / (2 * chunk)) nfw = lmax / (2 * chunk);
     double bsum = 0.0;
     int nrun = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const bool q = nfw > 0 && Wt[i] <= kFineWarm && L[i] >= 2 * nfw * kFineChunk;
+        const bool q = nfw > 0 && Wt[i] <= kFineWarm && L[i] >= 2 * nfw * chunk;
         nf[i] = q ? nfw : 0;
         // bulk: the tokens before the first fine chunk (a multiple of 128)
-        const long long b = q ? (L[i] - nfw * kFineChunk) / 128 * 128 : L[i];
+        const long long b = q ? (L[i] - nfw * chunk) / 128 * 128 : L[i];
         const int j = 4 * lane0 + i;
         if (j < pw) bulk[j] = b;
         L[i] = b;
@@ -619,7 +621,8 @@ __device__ inline void warm_plan(const SeqLens &lens, const float *slopes, const
 // workgroup) of nwg = pw * segments, from the plan above; `counter` is the
 // fine-chunk counter.
 __device__ inline void warm_plan_state(PlanState &ps, const double *cpre, const int *fq, int pw, int segments, int rl,
-                                       int *counter) {
+                                       long long chunk, int *counter) {
+    ps.chunk = chunk;
     ps.rl = rl;
     ps.T = cpre[pw] / ((double)pw * segments);
     ps.last = rl + 1 == pw * segments;
@@ -713,8 +716,8 @@ __device__ inline PieceRange next_range(const SeqLens &lens, int heads, const Se
         r.h = heads_warm[j % ps.nwarm];
         r.kind = 2;
         r.len = lens.len(r.n);
-        r.t0 = bulk[j] + (long long)i * kFineChunk;
-        r.t1 = i + 1 == ps.nf ? r.len : r.t0 + kFineChunk;
+        r.t0 = bulk[j] + (long long)i * ps.chunk;
+        r.t1 = i + 1 == ps.nf ? r.len : r.t0 + ps.chunk;
     }
     return r;
 }
