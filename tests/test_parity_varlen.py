@@ -18,8 +18,10 @@ from parity_util import (TOL_BF16, ensure_built, max_rel_per_head, max_rel_state
 
 pytestmark = pytest.mark.gpu
 
-# heads 0-2 on the pre-pass (their memory outlasts a segment), 3-6 on
-# warm-up ranges
+# heads 0 and 1 on the pre-pass (their memory outlasts a segment), 3-6 on
+# warm-up ranges; head 2 (a 2,304-token warm-up) takes warm-up ranges against
+# the 2,432-token segments of the first two cases and the pre-pass against the
+# 2,048-token segments of the third
 MIX = np.array([0.0, 1e-6, 0.005, 0.02, 0.2, 1.0, 30.0], np.float32)
 
 
