@@ -70,9 +70,10 @@ constexpr int kValueSlices = 4;
 // (segments-1)*seg_len tokens are also cut into `pieces` pre-pass pieces of
 // `piece_len` tokens (the last may be shorter); the pre-pass computes the state
 // each piece contributes (and, for a piece that straddles a segment boundary,
-// the part before the boundary), a combine pass sums them into the state at
-// every segment start, and segment g starts from that. seg_len and piece_len
-// are multiples of 128 tokens (two 64-token sub-blocks).
+// the part before the boundary), and the workgroup of segment g sums those
+// before its start into its start state. Heads whose memory ends within a
+// segment skip the pre-pass and take warm-up ranges (tiles.h). seg_len and
+// piece_len are multiples of 128 tokens (two 64-token sub-blocks).
 // With value_slices == 4 the head is instead split into four 32-column value
 // slices (one workgroup each, no segments, no workspace).
 struct PrefillPlan {

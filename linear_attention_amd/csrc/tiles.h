@@ -401,7 +401,7 @@ __device__ __forceinline__ int opaque(int x) {
     return x;
 }
 
-// Heads whose segments start from states the pre-pass and combine compute; the
+// Heads whose segments start from states combined from the pre-pass's; the
 // others take warm-up ranges.
 __device__ __forceinline__ bool takes_prepass(const Segmented &sp, float s2) {
     return !(warm_len(s2) < sp.seg_len);
@@ -726,26 +726,16 @@ __device__ inline PieceRange next_range(const SeqLens &lens, int heads, const Se
 // many short pieces, which is right when few heads take the pre-pass; when
 // many do, a workgroup takes k consecutive pieces of a head (writing one state,
 // in the slot of the group's last piece), so that about kPrepassActive
-// workgroups work and the combine walks fewer, larger states. Every kernel
-// derives k from the slopes with this function (each wave counts the heads on
-// the pre-pass itself, 64 at a time by ballot, so no barrier is needed). A
-// group never exceeds one segment, so it holds at most one segment boundary
-// strictly inside.
+// workgroups work and the segments' combines walk fewer, larger states. Every
+// kernel derives k with this function from the count of pre-pass heads that
+// split_heads gives it. A group never exceeds one segment, so it holds at most
+// one segment boundary strictly inside.
 constexpr int kPrepassActive = 512;
 __device__ inline int prepass_group_of(int npre, int units, const Segmented &sp) {
     long long k = ((long long)units * npre * sp.pieces + kPrepassActive - 1) / kPrepassActive;
     const long long kmax = sp.seg_len / sp.piece_len;
     if (k > kmax) k = kmax;
     return k < 1 ? 1 : (int)k;
-}
-__device__ inline int prepass_group(const float *slopes, int heads, int units, const Segmented &sp) {
-    const int lane = threadIdx.x & 63;
-    int npre = 0;
-    for (int h0 = 0; h0 < heads; h0 += 64) {
-        const int h = h0 + lane;
-        npre += __popcll(__ballot(h < heads && takes_prepass(sp, slopes[h < heads ? h : 0] * LOG2E)));
-    }
-    return prepass_group_of(__builtin_amdgcn_readfirstlane(npre), units, sp);
 }
 
 // Start state of segment g >= 1 of a pair on the pre-pass route, in each
