@@ -107,6 +107,17 @@ LT_API int lt_version(void);
 LT_API const char *lt_build_id(void);
 
 /*
+ * lt_init - optional set-up on the calling thread's current device: loads the
+ * library's GPU code there (the HIP runtime otherwise loads a kernel source's
+ * code at the first launch of one of its kernels, a few milliseconds of host
+ * work inside that first call) and looks up the device address of
+ * lt_prefill_noalloc's scratch. Safe to call more than once and from several
+ * threads; each other entry point works without it.
+ *   Errors: LT_ERR_HIP (no device, or a load failed).
+ */
+LT_API lt_status lt_init(void);
+
+/*
  * lt_prefill - block-wise prefill of `batch` sequences of equal length.
  *
  *   q, k, v    [batch, seqlen, heads, head_dim], in_dtype.

@@ -4,6 +4,7 @@ The operator (MiniMax Signal Lab · M1, §03 Lightning Attention) is causal
 linear attention with a per-head exponential decay, evaluated block by block
 with a fixed d x d fp32 state per head, plus its one-token decode step.
 
+``lt_init`` (optional: loads the GPU code before the first call),
 ``lt_prefill``, ``lt_prefill_noalloc`` (the same with the library's static
 scratch, for callers that cannot allocate), ``lt_prefill_workspace_bytes``,
 ``lt_prefill_varlen``,
@@ -21,7 +22,7 @@ ImportError there, and there is no fallback path.
 """
 
 _NATIVE_NAMES = (
-    "lt_prefill", "lt_prefill_noalloc", "lt_prefill_workspace_bytes", "lt_prefill_varlen",
+    "lt_init", "lt_prefill", "lt_prefill_noalloc", "lt_prefill_workspace_bytes", "lt_prefill_varlen",
     "lt_prefill_varlen_workspace_bytes", "lt_decode",
     "lt_prefill_norm_gate", "lt_prefill_varlen_norm_gate", "lt_decode_norm_gate", "lt_decode_slots",
     "lt_prefill_backward", "lt_softmax_prefill", "lt_softmax_decode", "lt_softmax_decode_workspace_bytes",

@@ -21,7 +21,7 @@ LT_F32, LT_BF16 = 0, 1
 LT_MAX_BLOCK = 65536
 HEAD_DIM = 128
 
-EXPORTS = ("lt_status_string", "lt_version", "lt_build_id", "lt_prefill", "lt_prefill_noalloc",
+EXPORTS = ("lt_status_string", "lt_version", "lt_build_id", "lt_init", "lt_prefill", "lt_prefill_noalloc",
            "lt_prefill_workspace_bytes", "lt_prefill_varlen", "lt_prefill_varlen_workspace_bytes",
            "lt_decode", "lt_prefill_norm_gate", "lt_prefill_varlen_norm_gate",
            "lt_decode_norm_gate", "lt_decode_slots", "lt_prefill_backward", "lt_softmax_prefill",
@@ -56,6 +56,8 @@ def _load() -> ctypes.CDLL:
     lib.lt_version.restype = _i
     lib.lt_build_id.argtypes = []
     lib.lt_build_id.restype = ctypes.c_char_p
+    lib.lt_init.argtypes = []
+    lib.lt_init.restype = _i
     lib.lt_prefill.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp,
                                _i, _ll, _i, _i, _i, _vp, ctypes.c_size_t, _vp]
     lib.lt_prefill.restype = _i
@@ -107,6 +109,13 @@ def status_string(status: int) -> str:
 def _check(status: int, where: str) -> None:
     if status != LT_OK:
         raise LightningError(status, where)
+
+
+def lt_init() -> None:
+    """Optional set-up on the current device: loads the library's GPU code
+    (otherwise loaded inside the first call of each kernel source) and looks up
+    the no-allocation scratch. Raises LightningError without a device."""
+    _check(lib.lt_init(), "lt_init")
 
 
 # ---------------------------------------------------------------------------

@@ -748,6 +748,11 @@ hipError_t launch(const BackwardArgs &a, const PrefillPlan &p, void *workspace, 
 
 }  // namespace
 
+hipError_t load_backward_code() {
+    hipFuncAttributes attr;
+    return hipFuncGetAttributes(&attr, reinterpret_cast<const void *>(&bwd_kv_kernel<float>));
+}
+
 hipError_t launch_backward_kv(const BackwardArgs &a, const PrefillPlan &plan, void *workspace,
                               lt_dtype out_dtype, hipStream_t stream) {
     return out_dtype == LT_F32 ? launch<float>(a, plan, workspace, stream)

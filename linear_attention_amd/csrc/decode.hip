@@ -179,6 +179,11 @@ hipError_t launch(const DecodeArgs &a, hipStream_t stream) {
 
 }  // namespace
 
+hipError_t load_decode_code() {
+    hipFuncAttributes attr;
+    return hipFuncGetAttributes(&attr, reinterpret_cast<const void *>(&decode_kernel<uint16_t, float, false>));
+}
+
 hipError_t launch_decode(const DecodeArgs &a, lt_dtype in_dtype, lt_dtype out_dtype,
                          hipStream_t stream) {
     if (in_dtype == LT_BF16)

@@ -111,6 +111,15 @@ PrefillPlan plan_prefill(long long units, long long seqlen, int heads, lt_dtype 
 // with the stream's device current) and kept until the process ends.
 hipError_t noalloc_scratch(hipStream_t stream, void **ptr, size_t *bytes);
 
+// Each kernel source's code object, loaded on the current device (the HIP
+// runtime otherwise loads it at the first launch of one of its kernels): a
+// query of one of its kernels' attributes forces the load.
+hipError_t load_prefill_heads_code();
+hipError_t load_prefill_slices_code();
+hipError_t load_decode_code();
+hipError_t load_backward_code();
+hipError_t load_softmax_code();
+
 // Backward of a fixed-length bf16 prefill (gradients of
 // l = sum dout . o + <d_state_out, S_final>): dk, dv and d_state_in from one
 // reverse pass; dq is the forward operator on (dout, v, k) with S_0^T.

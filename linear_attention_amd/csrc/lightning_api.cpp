@@ -247,6 +247,16 @@ LT_API const char *lt_status_string(int status) {
 
 LT_API int lt_version(void) { return 20000; }
 
+LT_API lt_status lt_init(void) {
+    hipError_t (*const loads[])() = {lt::load_prefill_heads_code, lt::load_prefill_slices_code,
+                                     lt::load_decode_code, lt::load_backward_code, lt::load_softmax_code};
+    for (auto load : loads)
+        if (load() != hipSuccess) return LT_ERR_HIP;
+    void *scratch = nullptr;
+    size_t bytes = 0;
+    return lt::noalloc_scratch(nullptr, &scratch, &bytes) == hipSuccess ? LT_OK : LT_ERR_HIP;
+}
+
 // The build passes the hash of the sources it compiled; a build by other means
 // reports "unknown". The tag keeps a fixed prefix so the identity can also be
 // read from the library file without loading it.

@@ -1001,6 +1001,11 @@ hipError_t launch(const PrefillArgs &a, const PrefillPlan &p, void *workspace, h
 
 }  // namespace
 
+hipError_t load_prefill_heads_code() {
+    hipFuncAttributes attr;
+    return hipFuncGetAttributes(&attr, reinterpret_cast<const void *>(&head_kernel<float, false>));
+}
+
 hipError_t launch_prefill_heads(const PrefillArgs &a, const PrefillPlan &plan, void *workspace,
                                 lt_dtype out_dtype, hipStream_t stream) {
     return out_dtype == LT_F32 ? launch<float>(a, plan, workspace, stream)

@@ -501,6 +501,11 @@ hipError_t launch(const PrefillArgs &a, hipStream_t stream) {
 
 }  // namespace
 
+hipError_t load_prefill_slices_code() {
+    hipFuncAttributes attr;
+    return hipFuncGetAttributes(&attr, reinterpret_cast<const void *>(&prefill_kernel<__bf16, float>));
+}
+
 hipError_t launch_prefill_slices(const PrefillArgs &a, lt_dtype in_dtype, lt_dtype out_dtype,
                           hipStream_t stream) {
     if (in_dtype == LT_BF16)

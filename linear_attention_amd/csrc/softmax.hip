@@ -583,6 +583,11 @@ __global__ __launch_bounds__(D) void fd_combine_kernel(SoftmaxDecodeArgs a, int 
 
 }  // namespace
 
+hipError_t load_softmax_code() {
+    hipFuncAttributes attr;
+    return hipFuncGetAttributes(&attr, reinterpret_cast<const void *>(&fa_prefill_kernel<__bf16>));
+}
+
 hipError_t launch_softmax_prefill(const SoftmaxArgs &a, void *workspace, lt_dtype out_dtype,
                                   hipStream_t stream) {
     clear_pending_error();

@@ -28,6 +28,11 @@ hipError_t launch_prefill_heads(const PrefillArgs &, const PrefillPlan &, void *
     return hipErrorNoDevice;
 }
 hipError_t launch_decode(const DecodeArgs &, lt_dtype, lt_dtype, hipStream_t) { return hipErrorNoDevice; }
+hipError_t load_prefill_heads_code() { return hipErrorNoDevice; }
+hipError_t load_prefill_slices_code() { return hipErrorNoDevice; }
+hipError_t load_decode_code() { return hipErrorNoDevice; }
+hipError_t load_backward_code() { return hipErrorNoDevice; }
+hipError_t load_softmax_code() { return hipErrorNoDevice; }
 
 }  // namespace lt
 

@@ -55,6 +55,19 @@ def test_status_strings():
     assert la.lib.lt_version() == 20000
 
 
+def test_init_without_a_device():
+    """lt_init reports LT_ERR_HIP, without crashing, where no GPU is visible
+    (its loads and the scratch lookup are HIP calls; tests/test_parity_gpu.py
+    covers it on a GPU)."""
+    import torch
+
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible: covered by the GPU tests")
+    assert la.lib.lt_init() == la.LT_ERR_HIP
+    with pytest.raises(la.LightningError):
+        la.lt_init()
+
+
 def test_build_id_matches_the_sources():
     """The library reports the hash of the csrc/ and include/ files it was built
     from (the test fixture rebuilds it when they differ)."""

@@ -61,6 +61,16 @@ def run_prefill_case(la, batch, L, H, dtype, seed, block=256, with_s0=False, out
     return eo, es
 
 
+def test_init_loads_and_repeats(la):
+    """lt_init succeeds on the device, again on a second call, and a prefill
+    after it matches the oracle."""
+    print("[case] lt_init twice, then a 300-token prefill", flush=True)
+    assert la.lib.lt_init() == la.LT_OK
+    la.lt_init()
+    eo, es = run_prefill_case(la, 1, 300, 3, "bf16", 1203)
+    assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)
+
+
 @pytest.mark.parametrize("L", [1, 2, 63, 64, 65, 128, 200, 1000])
 def test_prefill_bf16_lengths(la, L):
     eo, es = run_prefill_case(la, 1, L, 4, "bf16", 100 + L)
