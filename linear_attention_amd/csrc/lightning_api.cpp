@@ -245,7 +245,7 @@ LT_API const char *lt_status_string(int status) {
     }
 }
 
-LT_API int lt_version(void) { return 20000; }
+LT_API int lt_version(void) { return 20100; }
 
 LT_API lt_status lt_init(void) {
     hipError_t (*const loads[])() = {lt::load_prefill_heads_code, lt::load_prefill_slices_code,

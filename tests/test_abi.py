@@ -52,7 +52,7 @@ def test_status_strings():
         assert la.status_string(code).startswith(name)
         assert getattr(la, name) == code
     assert la.status_string(99) == "unknown lt_status"
-    assert la.lib.lt_version() == 20000
+    assert la.lib.lt_version() == 20100
 
 
 def test_init_without_a_device():
