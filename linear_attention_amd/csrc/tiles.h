@@ -730,7 +730,10 @@ __device__ inline PieceRange next_range(const SeqLens &lens, int heads, const Se
 // kernel derives k with this function from the count of pre-pass heads that
 // split_heads gives it. A group never exceeds one segment, so it holds at most
 // one segment boundary strictly inside.
-constexpr int kPrepassActive = 512;
+// 256: the pre-pass kernel fits one workgroup per CU, so with 512 the second
+// half ran in a second round (M1 layer, slopes x1e-5: 0.659 -> 0.639 ms per
+// call at 256; x0.1: 0.613 -> 0.610 ms).
+constexpr int kPrepassActive = 256;
 __device__ inline int prepass_group_of(int npre, int units, const Segmented &sp) {
     long long k = ((long long)units * npre * sp.pieces + kPrepassActive - 1) / kPrepassActive;
     const long long kmax = sp.seg_len / sp.piece_len;
