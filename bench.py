@@ -149,21 +149,32 @@ def time_calls(torch, call, steps, warmup, stream):
     """Mean and median call time (ms) from HIP events recorded on `stream` around
     each of `steps` calls after `warmup` untimed ones (and settle_gpu before
     them), and the wall time (s) of the timed calls bracketed by device
-    synchronisations."""
+    synchronisations. Python's garbage collector is off from the warmups to the
+    end of the timed calls (as in the standard library's timeit), so that a
+    collection pass cannot stall the host between two launches."""
+    import gc
+
     import numpy as np
 
     settle_gpu(torch)
-    for _ in range(warmup):
-        call()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for a, b in ev:
-        a.record(stream)
-        call()
-        b.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    was_on = gc.isenabled()
+    gc.collect()
+    gc.disable()
+    try:
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for a, b in ev:
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    finally:
+        if was_on:
+            gc.enable()
     ms = np.array([a.elapsed_time(b) for a, b in ev])
     return float(ms.mean()), float(np.median(ms)), ms, wall
 
