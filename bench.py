@@ -149,19 +149,21 @@ def time_calls(torch, call, steps, warmup, stream):
     """Mean and median call time (ms) from HIP events recorded on `stream` around
     each of `steps` calls after `warmup` untimed ones (and settle_gpu before
     them), and the wall time (s) of the timed calls bracketed by device
-    synchronisations. Python's garbage collector is off from the warmups to the
-    end of the timed calls (as in the standard library's timeit), so that a
-    collection pass cannot stall the host between two launches."""
+    synchronisations. Python's garbage collector is off from the settling work
+    to the end of the timed calls (as in the standard library's timeit), so
+    that a collection pass cannot stall the host between two launches; the
+    collection before it runs ahead of settle_gpu, since an idle gap of tens
+    of milliseconds after it puts the GPU back into its slower state."""
     import gc
 
     import numpy as np
 
-    settle_gpu(torch)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     was_on = gc.isenabled()
     gc.collect()
     gc.disable()
     try:
+        settle_gpu(torch)
         for _ in range(warmup):
             call()
         torch.cuda.synchronize()
