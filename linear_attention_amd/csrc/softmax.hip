@@ -245,6 +245,9 @@ __global__ __launch_bounds__(FNT) void fa_prefill_kernel(SoftmaxArgs a, const ui
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[c][v] = 0.f;
     float mrun = 0.f, lsum = 0.f;  // lane's reference maximum (log2 units) and sum
+    f32x16 negm;                   // -mrun in every entry: where the score products start
+#pragma unroll
+    for (int v = 0; v < 16; ++v) negm[v] = 0.f;
 
     const long long kvh = (long long)b * L * a.kv_heads + g;  // row of token 0, K/V head g
     const uint16_t *kg = kr + kvh * D;
@@ -258,16 +261,36 @@ __global__ __launch_bounds__(FNT) void fa_prefill_kernel(SoftmaxArgs a, const ui
     const int srow = tid >> 4, scol = 8 * (tid & 15);
     u32x4 skr[kNR], svr[kNR];  // native vectors: arrays of uint4 (a union type) stayed in scratch
     // (indices fixed at compile time, so the staging stays in registers)
+    // Byte offsets of the staged rows from a block's first row, unsigned 32-bit:
+    // the block's base address is wave-uniform, so each load takes it from
+    // scalar registers and adds its offset with no vector address arithmetic.
+    const int nwhole = (int)(L / SKB);  // blocks [0, nwhole) lie inside the sequence
+    uint32_t soff[kNR];
+    static_for<kNR>([&](auto I) { soff[I] = (uint32_t)((srow + kSR * (int)I) * ts + scol) * 2u; });
     auto fa_load = [&](int kb) {
         const long long k0 = (long long)kb * SKB;
-        const uint16_t *kb_ = kg + k0 * ts, *vb_ = vg + k0 * ts;
-        const int last = L - 1 - k0 < SKB - 1 ? (int)(L - 1 - k0) : SKB - 1;
-        static_for<kNR>([&](auto I) {
-            const int o = min(srow + kSR * (int)I, last) * ts + scol;
-            skr[I] = *reinterpret_cast<const u32x4 *>(kb_ + o);
-            svr[I] = *reinterpret_cast<const u32x4 *>(vb_ + o);
-        });
+        const char *kb_ = reinterpret_cast<const char *>(kg + k0 * ts);
+        const char *vb_ = reinterpret_cast<const char *>(vg + k0 * ts);
+        if (kb < nwhole) {  // whole block (a 32-bit test, so it stays scalar)
+            static_for<kNR>([&](auto I) {
+                skr[I] = *reinterpret_cast<const u32x4 *>(kb_ + soff[I]);
+                svr[I] = *reinterpret_cast<const u32x4 *>(vb_ + soff[I]);
+            });
+        } else {
+            const int last = (int)(L - 1 - k0);
+            static_for<kNR>([&](auto I) {
+                const uint32_t o = (uint32_t)(min(srow + kSR * (int)I, last) * ts + scol) * 2u;
+                skr[I] = *reinterpret_cast<const u32x4 *>(kb_ + o);
+                svr[I] = *reinterpret_cast<const u32x4 *>(vb_ + o);
+            });
+        }
     };
+    int wk[kNR], wv[kNR];  // tile offsets (elements) of the staged rows
+    static_for<kNR>([&](auto I) {
+        wk[I] = LK::off(srow + kSR * (int)I, scol);
+        wv[I] = LV::off(srow + kSR * (int)I, scol);
+    });
+    const int kblast = (int)(qlast / SKB);  // the wave's last block with live keys
     if (nkb > 0) fa_load(0);
     // key block kb; MASKED: the block reaches the diagonal of some query of
     // the wave or the end of the sequence
@@ -277,21 +300,18 @@ __global__ __launch_bounds__(FNT) void fa_prefill_kernel(SoftmaxArgs a, const ui
         // every wave finished before the barrier of block kb-1
         __bf16 *Kb = Ks[kb & 1], *Vb = Vs[kb & 1];
         static_for<kNR>([&](auto I) {
-            *reinterpret_cast<u32x4 *>(Kb + LK::off(srow + kSR * (int)I, scol)) = skr[I];
-            *reinterpret_cast<u32x4 *>(Vb + LV::off(srow + kSR * (int)I, scol)) = svr[I];
+            *reinterpret_cast<u32x4 *>(Kb + wk[I]) = skr[I];
+            *reinterpret_cast<u32x4 *>(Vb + wv[I]) = svr[I];
         });
         if (kb + 1 < nkb) fa_load(kb + 1);
         __syncthreads();  // tiles visible
+        if (kb > kblast) return;  // every key of this block is after the wave's queries
         const long long k0 = (long long)kb * SKB;
-        if (k0 > qlast) return;  // every key of this block is after the wave's queries
 
         // S^T blocks: keys k0 + 32kk.., this lane's query column; the two
         // halves interleave and each step's K operands load one step ahead
+        // The products accumulate onto -m (negm), so sc holds s - m.
         f32x16 sc[2];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) sc[kk][v] = 0.f;
         {
             bf16x8 ka0 = ld_op<LK>(Kb, 0, 0, lane), ka1 = ld_op<LK>(Kb, 32, 0, lane);
 #pragma unroll
@@ -301,8 +321,8 @@ __global__ __launch_bounds__(FNT) void fa_prefill_kernel(SoftmaxArgs a, const ui
                     kn0 = ld_op<LK>(Kb, 0, 16 * (ks + 1), lane);
                     kn1 = ld_op<LK>(Kb, 32, 16 * (ks + 1), lane);
                 }
-                sc[0] = mma(ka0, qop[ks], sc[0]);
-                sc[1] = mma(ka1, qop[ks], sc[1]);
+                sc[0] = mma(ka0, qop[ks], ks == 0 ? negm : sc[0]);
+                sc[1] = mma(ka1, qop[ks], ks == 0 ? negm : sc[1]);
                 ka0 = kn0;
                 ka1 = kn1;
             }
@@ -323,20 +343,27 @@ __global__ __launch_bounds__(FNT) void fa_prefill_kernel(SoftmaxArgs a, const ui
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[kk][v]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));  // finite: key k0 is live for every lane
-        // The reference maximum m is the first block's maximum and afterwards
-        // moves only when a score exceeds it by more than kStale (log2 units):
-        // the probabilities stay below 2^kStale, and the rescale of O and l (a
-        // wave-uniform branch) is rare after the first blocks.
-        if (kb == 0) {
-            mrun = mx;
-        } else if (__builtin_amdgcn_ballot_w64(mx > mrun + kStale)) {
-            const float mnew = fmaxf(mx, mrun);
-            const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
-            mrun = mnew;
+        // The reference maximum m (log2 units) is the first block's maximum
+        // and afterwards moves only when a score exceeds it by more than
+        // kStale: the probabilities stay below 2^kStale, and the rescale of O
+        // and l (a wave-uniform branch) is rare after the first blocks. sc is
+        // relative to m, so only a move of m subtracts anything from it. The
+        // ballot sees every lane's own maximum; only a move needs the maximum
+        // of the query's two lanes.
+        if (kb == 0 || __builtin_amdgcn_ballot_w64(mx > kStale)) {
+            mx = fmaxf(mx, __shfl_xor(mx, 32));  // finite: key k0 is live for every lane
+            const float d = kb == 0 ? mx : fmaxf(mx, 0.f);  // the move of m
+            if (kb != 0) {  // block 0 sets m: O and l are still zero
+                const float alpha = __builtin_amdgcn_exp2f(-d);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) o[c] *= alpha;
-            lsum *= alpha;
+                for (int c = 0; c < 4; ++c) o[c] *= alpha;
+                lsum *= alpha;
+            }
+            mrun += d;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) sc[kk] -= d;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) negm[v] = -mrun;
         }
         // P^T operands: step j holds keys 16j + 4hf + 0..3, 16j + 8 + 4hf + 0..3;
         // l sums the bf16 probabilities that enter the product
@@ -345,7 +372,7 @@ __global__ __launch_bounds__(FNT) void fa_prefill_kernel(SoftmaxArgs a, const ui
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int v = 0; v < 16; ++v)
-                pb[2 * kk + v / 8][v % 8] = static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[kk][v] - mrun));
+                pb[2 * kk + v / 8][v % 8] = static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[kk][v]));
 #pragma unroll
         for (int j = 0; j < SKB / 16; ++j)
 #pragma unroll
