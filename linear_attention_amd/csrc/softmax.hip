@@ -17,10 +17,11 @@
 //    8 / hpw consecutive 32-query blocks, so each K/V tile staged in LDS feeds
 //    all eight waves (FaGeom below); a wave's 32 queries are held as MFMA
 //    operands in registers (rope applied, scaled by scale * log2(e)); per
-//    64-key block S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (a lane owns one
-//    query and 32 keys, so the running max and sum are lane-local plus one
-//    xor-32 shuffle); the probabilities stay in registers as the B operand of
-//    O^T += V^T P^T; blocks past a wave's last query are skipped; heavy (late)
+//    64-key block S^T = K Q^T on v_mfma_f32_32x32x16_bf16, accumulated onto
+//    the negated reference maximum (a lane owns one query and 32 keys, so the
+//    test for a move of the maximum and the sum are lane-local; a move takes
+//    one xor-32 shuffle); the probabilities stay in registers as the B operand
+//    of O^T += V^T P^T; blocks past a wave's last query are skipped; heavy (late)
 //    query blocks are launched first, and the workgroups of one
 //    (sequence, K/V head) run on one XCD.
 // Decode: rope_append_kernel writes rope(k_new), v_new into the KV cache; then
