@@ -94,12 +94,20 @@ __device__ __forceinline__ bf16x8 ld_vt(const __bf16 *t, int c0, int k0, int lan
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// sin and cos of position * base^(-2m/R): the angle is formed in fp64 as a
-// fraction of a turn and reduced to [0, 1) before the hardware sine and
+// Rotation rates of the R/2 feature pairs, base^(-2m/R) in turns (fp64),
+// into th[0 .. R/2) of the workgroup's LDS: one fp64 exp2 per thread at most,
+// instead of one per rotated element. The caller synchronises the workgroup
+// before reading the table.
+constexpr int kRopePairs = D / 2;
+__device__ __forceinline__ void rope_table(double *th, int R, double log2_base, int tid, int nthreads) {
+    for (int m = tid; m < R / 2; m += nthreads)
+        th[m] = exp2(-(2.0 * m / R) * log2_base) * 0.15915494309189535;
+}
+
+// sin and cos of position * rate (rate in turns): the angle is formed in fp64
+// as a fraction of a turn and reduced to [0, 1) before the hardware sine and
 // cosine (which take turns), so it stays exact at any position.
-__device__ __forceinline__ void rope_sincos(long long pos, int m, int R, double log2_base, float &s,
-                                            float &c) {
-    const double th = exp2(-(2.0 * m / R) * log2_base) * 0.15915494309189535;
+__device__ __forceinline__ void rope_sincos(long long pos, double th, float &s, float &c) {
     double t = (double)pos * th;
     t -= floor(t);
     s = __builtin_amdgcn_sinf((float)t);
@@ -110,7 +118,7 @@ __device__ __forceinline__ void rope_sincos(long long pos, int m, int R, double 
 // 8j..8j+7; a thread in the first half of the rotated span also writes the
 // partner features.
 __device__ __forceinline__ void rope_row(const uint16_t *x, uint16_t *y, long long pos, int R,
-                                         double log2_base, int j) {
+                                         const double *th, int j) {
     const int f0 = 8 * j;
     const int half = R / 2;
     if (f0 >= half && f0 < R) return;  // written by the partner thread
@@ -125,7 +133,7 @@ __device__ __forceinline__ void rope_row(const uint16_t *x, uint16_t *y, long lo
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         float s, c;
-        rope_sincos(pos, f0 + e, R, log2_base, s, c);
+        rope_sincos(pos, th[f0 + e], s, c);
         const float u = bf2f(a[e]), w = bf2f(b[e]);
         ra[e] = f2bf(u * c - w * s);
         rb[e] = f2bf(u * s + w * c);
@@ -138,7 +146,7 @@ __device__ __forceinline__ void rope_row(const uint16_t *x, uint16_t *y, long lo
 // holds features 16ks + 8hf + e, e = 0..7, after rope at position pos, times
 // qs (the score scale with log2(e) folded in, so softmax runs on exp2).
 __device__ __forceinline__ void load_q_operand(const uint16_t *qg, long long pos, int rope_dims,
-                                               double log2_base, float qs, int hf,
+                                               const double *th, float qs, int hf,
                                                bf16x8 (&qop)[D / 16]) {
     float x[D / 16][8];
 #pragma unroll
@@ -159,7 +167,7 @@ __device__ __forceinline__ void load_q_operand(const uint16_t *qg, long long pos
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     float s, c;
-                    rope_sincos(pos, 16 * ks + 8 * hf + e, rope_dims, log2_base, s, c);
+                    rope_sincos(pos, th[16 * ks + 8 * hf + e], s, c);
                     const float u = x[ks][e], v = x[ks + dd][e];
                     x[ks][e] = u * c - v * s;
                     x[ks + dd][e] = u * s + v * c;
@@ -173,12 +181,15 @@ __device__ __forceinline__ void load_q_operand(const uint16_t *qg, long long pos
 
 // rope of every k row: [B, L, Hkv, d] -> same shape. 16 threads per row.
 __global__ __launch_bounds__(SNT) void rope_rows_kernel(SoftmaxArgs a, uint16_t *kr) {
+    __shared__ double th[kRopePairs];
+    rope_table(th, a.rope_dims, a.log2_base, threadIdx.x, SNT);
+    __syncthreads();
     const long long row = (long long)blockIdx.x * (SNT / 16) + threadIdx.x / 16;
     const long long rows = (long long)a.batch * a.seqlen * a.kv_heads;
     if (row >= rows) return;
     const long long t = (row / a.kv_heads) % a.seqlen;
-    rope_row(static_cast<const uint16_t *>(a.k) + row * D, kr + row * D, a.pos0 + t, a.rope_dims,
-             a.log2_base, threadIdx.x % 16);
+    rope_row(static_cast<const uint16_t *>(a.k) + row * D, kr + row * D, a.pos0 + t, a.rope_dims, th,
+             threadIdx.x % 16);
 }
 
 template <typename OutT>
@@ -213,10 +224,13 @@ template <typename OutT>
 __global__ __launch_bounds__(FNT) void fa_prefill_kernel(SoftmaxArgs a, const uint16_t *kr, FaGeom geo) {
     __shared__ __attribute__((aligned(16))) __bf16 Ks[2][SKB * SPT];
     __shared__ __attribute__((aligned(16))) __bf16 Vs[2][SKB * SPV];
+    __shared__ double th[kRopePairs];
 
     const long long per_xcd = gridDim.x / 8;
     const long long u = (long long)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    if (u >= geo.real) return;  // padding workgroup
+    if (u >= geo.real) return;  // padding workgroup (the whole workgroup leaves)
+    rope_table(th, a.rope_dims, a.log2_base, threadIdx.x, FNT);
+    __syncthreads();
     const int G = a.q_heads / a.kv_heads;
     const int bg = (int)(u / geo.per_group), rem = (int)(u % geo.per_group);
     const int hsubs = G / geo.hpw;
@@ -237,7 +251,7 @@ __global__ __launch_bounds__(FNT) void fa_prefill_kernel(SoftmaxArgs a, const ui
     {
         const long long qr = qrow < L ? qrow : L - 1;
         load_q_operand(static_cast<const uint16_t *>(a.q) + ((b * L + qr) * a.q_heads + h) * (long long)D,
-                       a.pos0 + qr, a.rope_dims, a.log2_base, a.scale * 1.4426950408889634f, hf, qop);
+                       a.pos0 + qr, a.rope_dims, th, a.scale * 1.4426950408889634f, hf, qop);
     }
 
     f32x16 o[4];
@@ -430,6 +444,9 @@ constexpr int kDecodeRec = 132;  // floats per partial record: O[128], m, l, 2 p
 // rope(k_new) into the key cache and v_new into the value cache at each
 // sequence's position; 16 threads per (sequence, K/V head).
 __global__ __launch_bounds__(SNT) void rope_append_kernel(SoftmaxDecodeArgs a) {
+    __shared__ double th[kRopePairs];
+    rope_table(th, a.rope_dims, a.log2_base, threadIdx.x, SNT);
+    __syncthreads();
     const int row = blockIdx.x * (SNT / 16) + threadIdx.x / 16;
     if (row >= a.batch * a.kv_heads) return;
     const int b = row / a.kv_heads, g = row % a.kv_heads;
@@ -440,7 +457,7 @@ __global__ __launch_bounds__(SNT) void rope_append_kernel(SoftmaxDecodeArgs a) {
     *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.v_cache) + dst + 8 * j) =
         *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.v_new) + (long long)row * D + 8 * j);
     rope_row(static_cast<const uint16_t *>(a.k_new) + (long long)row * D,
-             static_cast<uint16_t *>(a.k_cache) + dst, n, a.rope_dims, a.log2_base, j);
+             static_cast<uint16_t *>(a.k_cache) + dst, n, a.rope_dims, th, j);
 }
 
 // One wave per (sequence b, K/V head g, key split s): keys
@@ -453,6 +470,9 @@ __global__ __launch_bounds__(SNT) void fd_kernel(SoftmaxDecodeArgs a, int splits
                                                  float *ws) {
     __shared__ __attribute__((aligned(16))) __bf16 Kw[4][DKB * SPT];
     __shared__ __attribute__((aligned(16))) __bf16 Vw[4][DKB * SPV];
+    __shared__ double th[kRopePairs];  // filled before any wave can leave
+    rope_table(th, a.rope_dims, a.log2_base, threadIdx.x, SNT);
+    __syncthreads();
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const long long unit = (long long)blockIdx.x * 4 + w;
@@ -481,7 +501,7 @@ __global__ __launch_bounds__(SNT) void fd_kernel(SoftmaxDecodeArgs a, int splits
 
     bf16x8 qop[D / 16];
     load_q_operand(static_cast<const uint16_t *>(a.q) + ((long long)b * a.q_heads + h) * D, n,
-                   a.rope_dims, a.log2_base, a.scale * 1.4426950408889634f, hf, qop);
+                   a.rope_dims, th, a.scale * 1.4426950408889634f, hf, qop);
     if (!col) {
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks)
