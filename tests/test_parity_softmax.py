@@ -111,3 +111,32 @@ def test_softmax_prefill_m1_layer_sampled(la):
     wk = max(parity_err(to_host_f32(kr)[0, rows][:, g], kref[0, :, g]) for g in range(Hkv))
     print(f"[result] o {worst:.3e} k_rope {wk:.3e}", flush=True)
     assert worst <= TOL_BF16 and wk <= TOL_ROPE
+
+
+def test_softmax_prefill_moving_maximum(la):
+    """Scores built so that the reference maximum moves many times: queries share
+    a direction u (on the features RoPE leaves alone), the first 64 keys point
+    against it (every query's first block has a strongly negative maximum,
+    about -24 in log2 units) and later keys along it with a weight rising over
+    the sequence (maxima up to about +36), so each query's maximum climbs by
+    much more than the stale-maximum allowance in several steps."""
+    import torch
+
+    B, L, Hq, Hkv, R = 1, 1000, 8, 2, 64
+    print(f"[case] softmax_prefill moving maximum L={L} Hq={Hq} Hkv={Hkv}", flush=True)
+    g = workloads.rng(2204)
+    u = np.zeros(128, np.float32)
+    u[R:] = 1.0
+    gam = np.where(np.arange(L) < 64, -2.0, -1.0 + 4.0 * np.arange(L) / L).astype(np.float32)
+    q = workloads.round_bf16(g.standard_normal((B, L, Hq, 128), dtype=np.float32) + np.float32(1.5) * u)
+    k = workloads.round_bf16(np.float32(0.5) * g.standard_normal((B, L, Hkv, 128), dtype=np.float32)
+                             + gam[None, :, None, None] * u)
+    v = workloads.round_bf16(g.standard_normal((B, L, Hkv, 128), dtype=np.float32))
+    o, _ = la.lt_softmax_prefill(to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16"),
+                                 rope_dims=R, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref = oracle.softmax_attention(q, k, v, rope_dims=R)
+    og = to_host_f32(o)
+    worst = max(parity_err(og[0, :, h], o_ref[0, :, h]) for h in range(Hq))
+    print(f"[result] o {worst:.3e}", flush=True)
+    assert worst <= TOL_BF16, worst
