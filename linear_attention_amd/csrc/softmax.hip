@@ -366,7 +366,9 @@ __global__ __launch_bounds__(FNT) void fa_prefill_kernel(SoftmaxArgs a, const ui
         // ballot sees every lane's own maximum; only a move needs the maximum
         // of the query's two lanes.
         if (kb == 0 || __builtin_amdgcn_ballot_w64(mx > kStale)) {
-            mx = fmaxf(mx, __shfl_xor(mx, 32));  // finite: key k0 is live for every lane
+            // finite in block 0, where key 0 is live for every query; later, a
+            // query with every key of the block masked has -inf and moves by 0
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
             const float d = kb == 0 ? mx : fmaxf(mx, 0.f);  // the move of m
             if (kb != 0) {  // block 0 sets m: O and l are still zero
                 const float alpha = __builtin_amdgcn_exp2f(-d);
