@@ -470,7 +470,8 @@ __device__ inline Routes split_heads(const float *slopes, int heads, const Segme
 // i-th such pair in (unit, head) order. The other pairs (the warm-up route, see
 // warm_len) share the remaining workgroups in two phases.
 //  * Fine chunks: about kFineFrac of the warm-up route's tokens, taken from the
-//    end of the pairs whose warm-up is at most kFineWarm tokens, nf chunks of
+//    end of the pairs whose warm-up is at most kFineWarm tokens (256 or 512
+//    when fewer than kFinePairs pairs qualify at 128), nf chunks of
 //    kFineChunk tokens (the forward's; the backward's kernel passes its own) from each such pair that is long enough (at most half
 //    its tokens). A workgroup that has finished its range takes the next
 //    chunk from a counter; chunk c is chunk c / Q of the (c % Q)-th of the Q
@@ -498,6 +499,7 @@ __device__ inline Routes split_heads(const float *slopes, int heads, const Segme
 // restores them in the later tokens.
 constexpr double kFineFrac = 0.15;
 constexpr long long kFineWarm = 128, kFineChunk = 768;
+constexpr int kFinePairs = 16;
 static_assert(kFineChunk % 128 == 0, "pieces start at multiples of 128 tokens");
 struct WarmCut {
     const double *cpre;  // [nwarm pairs + 1] prefix sums of C
@@ -553,11 +555,23 @@ __device__ inline void warm_plan(const SeqLens &lens, const float *slopes, const
     // qualifies (at first count) and holds at least 2 nf chunks
     // (capped at half the longest such pair, so that a large fraction
     // does not leave every pair out)
+    // The pairs' warm-up bound is kFineWarm, doubled (at most twice) while
+    // fewer than kFinePairs pairs would qualify: chunks from a few heads stream
+    // slowly (M1 layer with its slopes scaled by 0.1: one head of 64 qualifies).
+    long long fwarm = kFineWarm;
+    for (int step = 0; step < 2; ++step) {
+        int n = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) n += Wt[i] <= fwarm && L[i] >= 2 * chunk;
+        for (int o = 32; o >= 1; o >>= 1) n += __shfl_xor(n, o);
+        if (n >= kFinePairs) break;
+        fwarm *= 2;
+    }
     int nq0 = 0;
     long long lmax = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        if (Wt[i] <= kFineWarm && L[i] >= 2 * chunk) {
+        if (Wt[i] <= fwarm && L[i] >= 2 * chunk) {
             ++nq0;
             lmax = L[i] > lmax ? L[i] : lmax;
         }
@@ -572,7 +586,7 @@ __device__ inline void warm_plan(const SeqLens &lens, const float *slopes, const
     int nrun = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const bool q = nfw > 0 && Wt[i] <= kFineWarm && L[i] >= 2 * nfw * chunk;
+        const bool q = nfw > 0 && Wt[i] <= fwarm && L[i] >= 2 * nfw * chunk;
         nf[i] = q ? nfw : 0;
         // bulk: the tokens before the first fine chunk (a multiple of 128)
         const long long b = q ? (L[i] - nfw * chunk) / 128 * 128 : L[i];
